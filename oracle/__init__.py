@@ -1,0 +1,230 @@
+"""CPU fp64 oracle of the draft-tree verify path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its binding in ``tree_attention_verify_amd``) never imports, loads or calls
+it, and the two share no code.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, OpenMP over rows); this
+module only builds it with gcc and marshals numpy arrays through ctypes.
+Every function cites the page passage it follows in ``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (gcc -O2 -fopenmp)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+               "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class OrcRows(ctypes.Structure):
+    _fields_ = [
+        ("base", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("prefix_len", ctypes.c_void_p),
+        ("max_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("stride_page", ctypes.c_int64),
+        ("stride_token", ctypes.c_int64),
+        ("stride_head", ctypes.c_int64),
+        ("stride_batch", ctypes.c_int64),
+        ("n_heads", ctypes.c_int32),
+        ("row_bytes", ctypes.c_int32),
+    ]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = ctypes.CDLL(_LIB)
+        P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        L.orc_build_masks.argtypes = [P, I, I, P, P, P, P, P]
+        L.orc_shift_positions.argtypes = [P, P, I, I, I]
+        L.orc_tree_attention.argtypes = [P, P, P, I, I64, I64, I64, P, I, I, P, I,
+                                         P, I, I, I, I, I, I, D, P, I64, P, P]
+        L.orc_causal_attention.argtypes = [P, P, P, I, I, I, I, I, I, D, P, P]
+        L.orc_merge.argtypes = [P, P, I, I, I, P, P]
+        L.orc_verify_greedy.argtypes = [P, P, P, I, I, P, P, P]
+        L.orc_compact_rows.argtypes = [ctypes.POINTER(OrcRows), I, P, P, I, I]
+        for f in ("orc_build_masks", "orc_shift_positions", "orc_tree_attention",
+                  "orc_causal_attention", "orc_merge", "orc_verify_greedy",
+                  "orc_compact_rows"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return 0
+    if a.dtype == np.uint16:  # raw bf16 bit patterns
+        return 1
+    raise TypeError("oracle inputs are float32 or raw bf16 (uint16) arrays, got %s" % a.dtype)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError("oracle %s rejected its arguments" % name)
+
+
+def build_masks(parents, vc=None):
+    """parents int32 [B][N] -> dict(depth, masks uint64, positions, tree_error)."""
+    parents = _c(parents, np.int32)
+    B, N = parents.shape
+    depth = np.empty((B, N), np.int32)
+    masks = np.empty((B, N), np.uint64)
+    err = np.empty((B,), np.int32)
+    pos = None
+    if vc is not None:
+        vc = _c(vc, np.int32)
+        pos = np.empty((B, N), np.int32)
+    _check(lib().orc_build_masks(_p(parents), B, N, _p(vc), _p(depth), _p(masks),
+                                 _p(pos), _p(err)), "build_masks")
+    return {"depth": depth, "masks": masks, "positions": pos, "tree_error": err}
+
+
+def shift_positions(pos, depth, direction):
+    pos = np.array(pos, dtype=np.int32, copy=True, order="C")
+    depth = _c(depth, np.int32)
+    B, N = pos.shape
+    _check(lib().orc_shift_positions(_p(pos), _p(depth), B, N, int(direction)),
+           "shift_positions")
+    return pos
+
+
+def tree_attention(q, k_cache, v_cache, strides, page_table, page_size, prefix_len,
+                   masks, W, Hkv, prefix_window=0, sm_scale=0.0, rows=None):
+    """fp64 tree attention.
+
+    q: [B][R][Hq][D] float32 or uint16 (bf16 bits); k_cache/v_cache: flat pools
+    of the same dtype addressed with ``strides`` = (page, head, token) in
+    elements; page_table int32 [B][max_pages]; prefix_len int32 [B];
+    masks uint64 [B][R].  Returns (out float64, lse2 float64) of shape
+    [B][R][Hq][D] / [B][R][Hq], or [n][D] / [n] for a ``rows`` list of flat
+    row ids ((b*R + r)*Hq + h).
+    """
+    q = np.ascontiguousarray(q)
+    dt = _dtype_code(q)
+    k_cache = np.ascontiguousarray(k_cache)
+    v_cache = np.ascontiguousarray(v_cache)
+    assert k_cache.dtype == q.dtype and v_cache.dtype == q.dtype
+    B, R, Hq, D = q.shape
+    page_table = _c(page_table, np.int32)
+    prefix_len = _c(prefix_len, np.int32)
+    masks = _c(masks, np.uint64)
+    assert masks.shape == (B, R)
+    if rows is None:
+        out = np.empty((B, R, Hq, D), np.float64)
+        lse = np.empty((B, R, Hq), np.float64)
+        rp, nr = None, 0
+    else:
+        rows = _c(rows, np.int64)
+        out = np.empty((rows.size, D), np.float64)
+        lse = np.empty((rows.size,), np.float64)
+        rp, nr = rows, rows.size
+    sp, sh, st = (int(x) for x in strides)
+    _check(lib().orc_tree_attention(
+        _p(q), _p(k_cache), _p(v_cache), dt, sp, sh, st, _p(page_table),
+        page_table.shape[1], int(page_size), _p(prefix_len), int(prefix_window),
+        _p(masks), int(W), B, R, Hq, int(Hkv), D, float(sm_scale), _p(rp), nr,
+        _p(out), _p(lse)), "tree_attention")
+    return out, lse
+
+
+def causal_attention(q, k, v, sm_scale=0.0):
+    """q [n][Hq][D], k/v [L][Hkv][D] (float32 or bf16 bits) -> fp64 (out, lse2)."""
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    dt = _dtype_code(q)
+    n, Hq, D = q.shape
+    L, Hkv, _ = k.shape
+    out = np.empty((n, Hq, D), np.float64)
+    lse = np.empty((n, Hq), np.float64)
+    _check(lib().orc_causal_attention(_p(q), _p(k), _p(v), dt, n, L, Hq, Hkv, D,
+                                      float(sm_scale), _p(out), _p(lse)), "causal")
+    return out, lse
+
+
+def merge(o_parts, lse2_parts):
+    """o_parts [S][n][D], lse2_parts [S][n] (float64) -> merged (out, lse2)."""
+    o_parts = _c(o_parts, np.float64)
+    lse2_parts = _c(lse2_parts, np.float64)
+    S, n, D = o_parts.shape
+    out = np.empty((n, D), np.float64)
+    lse = np.empty((n,), np.float64)
+    _check(lib().orc_merge(_p(o_parts), _p(lse2_parts), S, n, D, _p(out), _p(lse)),
+           "merge")
+    return out, lse
+
+
+def verify_greedy(draft, target, parents):
+    draft = _c(draft, np.int32)
+    target = _c(target, np.int32)
+    parents = _c(parents, np.int32)
+    B, N = parents.shape
+    path = np.empty((B, N), np.int32)
+    alen = np.empty((B,), np.int32)
+    tok = np.empty((B, N), np.int32)
+    _check(lib().orc_verify_greedy(_p(draft), _p(target), _p(parents), B, N,
+                                   _p(path), _p(alen), _p(tok)), "verify_greedy")
+    return {"accepted_path": path, "accept_len": alen, "accepted_tokens": tok}
+
+
+def compact_rows(tables, accepted_path, accept_len):
+    """In-place compaction of host buffers.
+
+    tables: list of dicts with keys buf (writable numpy array, any dtype),
+    page_table (int32 [B][max_pages] or None), prefix_len (int32 [B] or None),
+    page_size, stride_page, stride_token, stride_head, stride_batch (bytes),
+    n_heads, row_bytes.
+    """
+    accepted_path = _c(accepted_path, np.int32)
+    accept_len = _c(accept_len, np.int32)
+    B, N = accepted_path.shape
+    arr = (OrcRows * len(tables))()
+    keep = []
+    for i, t in enumerate(tables):
+        buf = t["buf"]
+        assert buf.flags.c_contiguous and buf.flags.writeable
+        pt = t.get("page_table")
+        pl = t.get("prefix_len")
+        if pt is not None:
+            pt = _c(pt, np.int32)
+            pl = _c(pl, np.int32)
+            keep += [pt, pl]
+        arr[i] = OrcRows(buf.ctypes.data, _p(pt), _p(pl),
+                         0 if pt is None else pt.shape[1], int(t.get("page_size", 1)),
+                         int(t.get("stride_page", 0)), int(t["stride_token"]),
+                         int(t.get("stride_head", 0)), int(t.get("stride_batch", 0)),
+                         int(t.get("n_heads", 1)), int(t["row_bytes"]))
+    _check(lib().orc_compact_rows(arr, len(tables), _p(accepted_path), _p(accept_len),
+                                  B, N), "compact_rows")

@@ -1,0 +1,456 @@
+/*
+ * Plain CPU fp64 oracle for the draft-tree verify path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the tests, the package's smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no code, header, table or
+ * helper with the HIP library; every routine below is the plain definition
+ * of what the method computes, written out slowly and in the order the pages
+ * state it, with no blocking, fusion or reordering beyond that.
+ *
+ * Sources (page title, section):
+ *  [DTS]  "Draft-tree speculation" (tokenspeed design notes)
+ *  [ETA]  "EAGLE Tree Attention candidate layout, positions and visibility"
+ *         (SGLang EAGLE tree-verify analysis, Chinese)
+ *  [MEM]  "Medusa, EAGLE-1/2/3, MTP, and tree attention" (course chapter)
+ *  [DDT]  "From Greedy to Sampling: The Architecture of Choice in DDTree
+ *         Speculative Decoding"
+ *
+ * Floating point: every score, exponential, sum and output is fp64, on the
+ * exact input values (bf16 inputs are widened bit-exactly).  Parity of every
+ * routine here is pinned by tests against worked values printed on the
+ * pages, closed forms, brute force and a library attention routine; see the
+ * test module for the list.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_BAD 1
+
+/* ------------------------------------------------------------------ */
+/* element access                                                      */
+/* ------------------------------------------------------------------ */
+
+/* dtype codes of this file: 0 = fp32, 1 = bf16 (raw 16-bit patterns). */
+static double orc_load(const void *base, int dtype, int64_t idx)
+{
+    if (dtype == 0)
+        return (double)((const float *)base)[idx];
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* ------------------------------------------------------------------ */
+/* tree metadata                                                       */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Ancestor masks, depth and RoPE positions of every node.
+ *
+ * [ETA] section 1 (the visibility rule M(i,j)): row i sees key j of the
+ * window iff j == i or j is an ancestor of i.  The bit form follows
+ * [DTS] "One tree attention ...": one 64-bit ancestor mask per row, bit j
+ * standing for window node j.  The walk up the parent links is the one of
+ * [MEM]'s tiny numpy reference (climb while the ancestor is not -1).
+ * Depth counts the climbs; the position is the prefix length plus depth
+ * ([ETA] section 2, positions = seq_len + depth; [DTS] "Position follows
+ * depth, slot follows node index": node i sits at vc + depth[i]).
+ *
+ * A tree is valid when node 0 is the only root (parent -1) and every other
+ * node's parent is an earlier node ([ETA] section 1 puts the root first;
+ * [MEM] "Building the mask, for real": a missing parent is rejected, never
+ * treated as a root).  For an invalid request tree_error[b] = 1 + the first
+ * offending node, and its masks are 0, depth and positions -1.
+ */
+int orc_build_masks(const int32_t *parents, int B, int N, const int32_t *vc,
+                    int32_t *depth, uint64_t *masks, int32_t *positions,
+                    int32_t *tree_error)
+{
+    if (B < 0 || N < 1 || N > 64)
+        return ORC_BAD;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *par = parents + (int64_t)b * N;
+        int bad = -1;
+        for (int i = 0; i < N && bad < 0; ++i) {
+            if (i == 0 && par[0] != -1)
+                bad = 0;
+            if (i > 0 && (par[i] < 0 || par[i] >= i))
+                bad = i;
+        }
+        if (tree_error)
+            tree_error[b] = bad < 0 ? 0 : 1 + bad;
+        for (int i = 0; i < N; ++i) {
+            int64_t o = (int64_t)b * N + i;
+            if (bad >= 0) {
+                masks[o] = 0;
+                depth[o] = -1;
+                if (positions)
+                    positions[o] = -1;
+                continue;
+            }
+            uint64_t m = 0;
+            int climbs = 0;
+            int a = i;
+            while (a != -1) {
+                m |= (uint64_t)1 << a;
+                a = par[a];
+                if (a != -1)
+                    ++climbs;
+            }
+            masks[o] = m;
+            depth[o] = climbs;
+            if (positions)
+                positions[o] = (vc ? vc[b] : 0) + climbs;
+        }
+    }
+    return ORC_OK;
+}
+
+/*
+ * Position shifts of [DTS] "Position follows depth, slot follows node
+ * index": load_step moves window row i from vc + i to vc + depth[i]
+ * (direction +1); compact_rows moves it back (direction -1).
+ */
+int orc_shift_positions(int32_t *pos, const int32_t *depth, int B, int N,
+                        int direction)
+{
+    if (direction != 1 && direction != -1)
+        return ORC_BAD;
+    for (int b = 0; b < B; ++b)
+        for (int i = 0; i < N; ++i) {
+            int64_t o = (int64_t)b * N + i;
+            pos[o] += direction * (depth[o] - i);
+        }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* attention                                                           */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Softmax attention of one query row over an ordered list of keys, in fp64.
+ * s_t = scale * sum_d q[d] k_t[d];  m = max s;  Z = sum exp(s_t - m);
+ * o = sum exp(s_t - m) v_t / Z;  lse2 = (m + ln Z) / ln 2, the base-2
+ * log-sum-exp of the scores ([DTS] "One tree attention ...": both halves of
+ * the cascade carry a base-2 log-sum-exp).  No key: o = 0, lse2 = -inf.
+ * kofs/vofs hold the element offset of each key's row.
+ */
+static void orc_softmax_row(const void *qb, int64_t qofs, const void *kb,
+                            const void *vb, int dtype, const int64_t *kofs,
+                            int nk, int D, double scale, double *s,
+                            double *out, double *lse2)
+{
+    for (int d = 0; d < D; ++d)
+        out[d] = 0.0;
+    if (nk == 0) {
+        *lse2 = -INFINITY;
+        return;
+    }
+    double m = -INFINITY;
+    for (int t = 0; t < nk; ++t) {
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d)
+            acc += orc_load(qb, dtype, qofs + d) * orc_load(kb, dtype, kofs[t] + d);
+        s[t] = scale * acc;
+        if (s[t] > m)
+            m = s[t];
+    }
+    double Z = 0.0;
+    for (int t = 0; t < nk; ++t) {
+        double w = exp(s[t] - m);
+        Z += w;
+        for (int d = 0; d < D; ++d)
+            out[d] += w * orc_load(vb, dtype, kofs[t] + d);
+    }
+    for (int d = 0; d < D; ++d)
+        out[d] /= Z;
+    *lse2 = (m + log(Z)) / log(2.0);
+}
+
+/*
+ * Tree attention over a paged KV cache.
+ *
+ * Row r of request b, query head h, reads kv head h / (Hq / Hkv).  Its
+ * visible keys, in this order, are
+ *   - the committed prefix: logical positions t in [p_lo, P), where P =
+ *     prefix_len[b] and p_lo = max(0, P - prefix_window) when
+ *     prefix_window > 0, else 0 ([ETA] section 1: every row sees the
+ *     committed prefix; [DTS] "One tree attention ...": a sliding-window
+ *     draft layer sees the window frozen at the round's prefix end);
+ *   - then window node j, stored at logical position P + j, for j < W in
+ *     ascending order with bit j of masks[b*R + r] set ([DTS] "One tree
+ *     attention ...": the 64-bit ancestor mask covers the last W keys;
+ *     "Position follows depth, slot follows node index": the slot follows
+ *     the node index).
+ * Logical position t lives in physical page page_table[b*max_pages + t/ps]
+ * at slot t % ps; the element offset of (page, kv head g, slot) is
+ * page*stride_page + g*stride_head + slot*stride_token, channels contiguous.
+ * Keys that are not visible are never read.
+ *
+ * rows: optional list of flat row ids ((b*R + r)*Hq + h); out/lse2 then hold
+ * n_rows entries in list order.  With rows == NULL every row is computed and
+ * out is [B][R][Hq][D], lse2 [B][R][Hq].
+ * q is [B][R][Hq][D] contiguous.  sm_scale <= 0 means 1/sqrt(D).
+ */
+int orc_tree_attention(const void *q, const void *k_cache, const void *v_cache,
+                       int dtype, int64_t stride_page, int64_t stride_head,
+                       int64_t stride_token, const int32_t *page_table,
+                       int max_pages, int page_size, const int32_t *prefix_len,
+                       int prefix_window, const uint64_t *masks, int W, int B,
+                       int R, int Hq, int Hkv, int D, double sm_scale,
+                       const int64_t *rows, int64_t n_rows, double *out,
+                       double *lse2)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0 || W < 0 || W > 64 || page_size <= 0)
+        return ORC_BAD;
+    if (sm_scale <= 0.0)
+        sm_scale = 1.0 / sqrt((double)D);
+    int64_t total = rows ? n_rows : (int64_t)B * R * Hq;
+    int group = Hq / Hkv;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t n = 0; n < total; ++n) {
+        int64_t id = rows ? rows[n] : n;
+        int h = (int)(id % Hq);
+        int r = (int)((id / Hq) % R);
+        int b = (int)(id / ((int64_t)Hq * R));
+        int g = h / group;
+        int P = prefix_len[b];
+        int p_lo = prefix_window > 0 && P > prefix_window ? P - prefix_window : 0;
+        int nk_max = P - p_lo + W;
+        int64_t *kofs = (int64_t *)malloc(sizeof(int64_t) * (nk_max > 0 ? nk_max : 1));
+        double *s = (double *)malloc(sizeof(double) * (nk_max > 0 ? nk_max : 1));
+        int nk = 0;
+        uint64_t m = masks[(int64_t)b * R + r];
+        for (int t = p_lo; t < P + W; ++t) {
+            if (t >= P) {
+                int j = t - P;
+                if (!((m >> j) & 1))
+                    continue;
+            }
+            int lp = t / page_size;
+            if (lp >= max_pages) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            int64_t page = page_table[(int64_t)b * max_pages + lp];
+            kofs[nk++] = page * stride_page + (int64_t)g * stride_head +
+                         (int64_t)(t % page_size) * stride_token;
+        }
+        int64_t qofs = (((int64_t)b * R + r) * Hq + h) * D;
+        orc_softmax_row(q, qofs, k_cache, v_cache, dtype, kofs, nk, D, sm_scale,
+                        s, out + n * D, lse2 + n);
+        free(kofs);
+        free(s);
+    }
+    return bad ? ORC_BAD : ORC_OK;
+}
+
+/*
+ * Plain causal attention on contiguous keys: q is [n][Hq][D], k and v are
+ * [L][Hkv][D].  Query row i sits at position L - n + i and sees keys
+ * t <= L - n + i, in ascending order.  Used by the pins: a chain tree must
+ * equal this ([DTS] "The tree is a parameter of the chain path": a chain is
+ * the tree parent[i] = i - 1), and each tree row must equal the last row of
+ * this run on prefix + its own root-to-node path ([ETA] section 1,
+ * L(v) = Target(prefix + path(root -> v))).
+ */
+int orc_causal_attention(const void *q, const void *k, const void *v,
+                         int dtype, int n, int L, int Hq, int Hkv, int D,
+                         double sm_scale, double *out, double *lse2)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0 || n > L)
+        return ORC_BAD;
+    if (sm_scale <= 0.0)
+        sm_scale = 1.0 / sqrt((double)D);
+    int group = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t id = 0; id < (int64_t)n * Hq; ++id) {
+        int i = (int)(id / Hq), h = (int)(id % Hq), g = h / group;
+        int nk = L - n + i + 1;
+        int64_t *kofs = (int64_t *)malloc(sizeof(int64_t) * nk);
+        double *s = (double *)malloc(sizeof(double) * nk);
+        for (int t = 0; t < nk; ++t)
+            kofs[t] = ((int64_t)t * Hkv + g) * D;
+        orc_softmax_row(q, id * D, k, v, dtype, kofs, nk, D, sm_scale, s,
+                        out + id * D, lse2 + id);
+        free(kofs);
+        free(s);
+    }
+    return ORC_OK;
+}
+
+/*
+ * Merge of softmax states over disjoint key sets ([ETA] section 4, the
+ * cascade merge): with Z_k the unnormalised weight sum of part k (here
+ * Z_k = 2^lse2_k), O = sum_k Z_k O_k / sum_k Z_k and lse2 = log2 sum_k Z_k.
+ * Parts with lse2 = -inf (no key) carry no weight; if every part is empty the
+ * result is O = 0, lse2 = -inf.  o_parts is [S][n][D], lse2_parts [S][n].
+ */
+int orc_merge(const double *o_parts, const double *lse2_parts, int S, int n,
+              int D, double *out, double *lse2)
+{
+    for (int i = 0; i < n; ++i) {
+        double mx = -INFINITY;
+        for (int k = 0; k < S; ++k)
+            if (lse2_parts[(int64_t)k * n + i] > mx)
+                mx = lse2_parts[(int64_t)k * n + i];
+        for (int d = 0; d < D; ++d)
+            out[(int64_t)i * D + d] = 0.0;
+        if (mx == -INFINITY) {
+            lse2[i] = -INFINITY;
+            continue;
+        }
+        double Zsum = 0.0;
+        for (int k = 0; k < S; ++k) {
+            double l = lse2_parts[(int64_t)k * n + i];
+            if (l == -INFINITY)
+                continue;
+            double Z = exp2(l - mx); /* Z_k scaled by 2^-mx */
+            Zsum += Z;
+            for (int d = 0; d < D; ++d)
+                out[(int64_t)i * D + d] += Z * o_parts[((int64_t)k * n + i) * D + d];
+        }
+        for (int d = 0; d < D; ++d)
+            out[(int64_t)i * D + d] /= Zsum;
+        lse2[i] = mx + log2(Zsum);
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* greedy verify                                                       */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Greedy tree walk ([MEM] "Walking the accepted path"): start at the root;
+ * t = target_argmax[cur], the target's token at the current node; move to a
+ * child of cur whose draft token equals t; stop when none does.  When
+ * several children carry t, the lowest node index wins (the pages' walk
+ * scans children in order; [DTS] "Tree construction is deterministic"
+ * numbers the best child first).  accept_len counts the root ([ETA]
+ * section 2, accept_lens = num_correct_drafts + 1; [DDT]: the accepted
+ * count includes the root).  path is N wide and -1 padded; tokens[k] =
+ * target_argmax[path[k]] for k < accept_len (the last one is the bonus),
+ * -1 after.  The walk takes at most N nodes whatever the parent array holds.
+ */
+int orc_verify_greedy(const int32_t *draft, const int32_t *target,
+                      const int32_t *parents, int B, int N, int32_t *path,
+                      int32_t *accept_len, int32_t *tokens)
+{
+    if (N < 1 || N > 64)
+        return ORC_BAD;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *dr = draft + (int64_t)b * N;
+        const int32_t *tg = target + (int64_t)b * N;
+        const int32_t *par = parents + (int64_t)b * N;
+        int32_t *pb = path + (int64_t)b * N;
+        for (int k = 0; k < N; ++k)
+            pb[k] = -1;
+        int len = 0;
+        int cur = 0;
+        pb[len++] = cur;
+        while (len < N) {
+            int t = tg[cur];
+            int next = -1;
+            for (int c = 0; c < N; ++c)
+                if (par[c] == cur && dr[c] == t) {
+                    next = c;
+                    break;
+                }
+            if (next < 0)
+                break;
+            cur = next;
+            pb[len++] = cur;
+        }
+        accept_len[b] = len;
+        if (tokens)
+            for (int k = 0; k < N; ++k)
+                tokens[(int64_t)b * N + k] = k < len ? tg[pb[k]] : -1;
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* compaction                                                          */
+/* ------------------------------------------------------------------ */
+
+/*
+ * One row table of the compaction: a buffer with one row of n_heads
+ * segments of row_bytes bytes per (request, window slot).  Paged tables
+ * (page_table != NULL) put window slot i of request b at logical position
+ * prefix_len[b] + i, resolved through the page table; the byte offset of
+ * (page, head h, slot s) is page*stride_page + h*stride_head +
+ * s*stride_token.  Dense tables put it at b*stride_batch + i*stride_token
+ * + h*stride_head.  All strides are in bytes.
+ */
+typedef struct {
+    uint8_t *base;
+    const int32_t *page_table;
+    const int32_t *prefix_len;
+    int32_t max_pages, page_size;
+    int64_t stride_page, stride_token, stride_head, stride_batch;
+    int32_t n_heads, row_bytes;
+} orc_rows;
+
+static uint8_t *orc_row_addr(const orc_rows *t, int b, int slot, int h)
+{
+    if (t->page_table) {
+        int64_t lp = (int64_t)t->prefix_len[b] + slot;
+        int64_t page = t->page_table[(int64_t)b * t->max_pages + lp / t->page_size];
+        return t->base + page * t->stride_page + (int64_t)h * t->stride_head +
+               (lp % t->page_size) * t->stride_token;
+    }
+    return t->base + (int64_t)b * t->stride_batch + (int64_t)slot * t->stride_token +
+           (int64_t)h * t->stride_head;
+}
+
+/*
+ * Moves the accepted path to the window's leading slots, in every table:
+ * for i < accept_len[b], row i <- row accepted_path[b][i] ([DTS] "The tree
+ * is a parameter of the chain path": compact_window_rows copies words, so
+ * it does not depend on the dtype; [MEM] "Discarding the rejected branches'
+ * KV": slots of the accepted nodes move to the front of the block).  All
+ * source rows are read before any row is written; rows from accept_len on,
+ * other requests and other bytes are left as they are.
+ */
+int orc_compact_rows(const orc_rows *tables, int n_tables,
+                     const int32_t *accepted_path, const int32_t *accept_len,
+                     int B, int N)
+{
+    for (int ti = 0; ti < n_tables; ++ti) {
+        const orc_rows *t = &tables[ti];
+        int64_t seg = t->row_bytes;
+        uint8_t *snap = (uint8_t *)malloc((size_t)(N * t->n_heads * seg + 1));
+        for (int b = 0; b < B; ++b) {
+            int a = accept_len[b];
+            if (a < 0 || a > N) {
+                free(snap);
+                return ORC_BAD;
+            }
+            for (int i = 0; i < a; ++i) {
+                int src = accepted_path[(int64_t)b * N + i];
+                if (src < 0 || src >= N) {
+                    free(snap);
+                    return ORC_BAD;
+                }
+                for (int h = 0; h < t->n_heads; ++h)
+                    memcpy(snap + ((int64_t)i * t->n_heads + h) * seg,
+                           orc_row_addr(t, b, src, h), (size_t)seg);
+            }
+            for (int i = 0; i < a; ++i)
+                for (int h = 0; h < t->n_heads; ++h)
+                    memcpy(orc_row_addr(t, b, i, h),
+                           snap + ((int64_t)i * t->n_heads + h) * seg, (size_t)seg);
+        }
+        free(snap);
+    }
+    return ORC_OK;
+}

@@ -1,0 +1,559 @@
+"""Pins of the CPU fp64 oracle against what the pages and the mathematics fix.
+
+Nothing here runs the oracle against itself: every check compares it with a
+value printed on a page (tests/golden, cited there), a closed form, a brute
+force enumeration, an independent characterisation (boolean reachability),
+or a library routine (torch scaled_dot_product_attention in fp64 on the CPU
+with an explicit dense mask).  CPU only.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.golden import load
+from tree_attention_verify_amd import inputs as gen
+
+LOG2E = 1.0 / math.log(2.0)
+
+
+def as_bits(mask_row):
+    return sum(int(b) << j for j, b in enumerate(mask_row))
+
+
+def bits_of(m, W):
+    return [(int(m) >> j) & 1 for j in range(W)]
+
+
+# ---------------------------------------------------------------------------
+# masks, depth, positions
+# ---------------------------------------------------------------------------
+
+def test_worked_tree_masks():
+    g = load("worked_tree.txt")
+    r = oracle.build_masks(np.array([g["parents"]]), vc=np.array([0]))
+    want = [as_bits(g["visibility_row%d" % i]) for i in range(5)]
+    assert r["masks"][0].tolist() == want == [1, 3, 5, 11, 21]
+    assert r["depth"][0].tolist() == [0, 1, 1, 2, 2]
+    # C (row 3) sees root and A, never B
+    assert bits_of(r["masks"][0, 3], 5)[:3] == [1, 1, 0]
+    assert r["masks"][0, 2] != as_bits(g["causal_row2"])
+    assert r["tree_error"][0] == 0
+
+
+def test_positions_examples():
+    g = load("positions.txt")
+    # example 1: depth [0,1,1,2] comes from parents [-1,0,0,1]
+    r = oracle.build_masks(np.array([[-1, 0, 0, 1]]), vc=np.array(g["example1_prefix"]))
+    assert r["depth"][0].tolist() == g["example1_depth"]
+    assert r["positions"][0].tolist() == g["example1_positions"]
+    r = oracle.build_masks(np.array([g["example2_parents"]]), vc=np.array(g["example2_prefix"]))
+    assert r["positions"][0].tolist() == g["example2_positions"]
+
+
+def test_closure_example():
+    g = load("closure.txt")
+    r = oracle.build_masks(np.array([g["parents"]]))
+    assert bits_of(r["masks"][0, 2], 4) == g["mask_row2"]
+    # the selection {0, 2} renumbered: node 1 (old 2) has its parent (old 1)
+    # outside the set -> rejected, never treated as a root
+    sel = g["bad_selection"]
+    renum = {old: new for new, old in enumerate(sel)}
+    par = [-1] + [renum.get(g["parents"][old], 99) for old in sel[1:]]
+    r = oracle.build_masks(np.array([par]))
+    assert r["tree_error"][0] == 2
+    assert r["masks"][0].tolist() == [0, 0]
+    assert r["depth"][0].tolist() == [-1, -1]
+
+
+def test_suffix_lists_example():
+    g = load("suffix_lists.txt")
+    slots = g["candidate_slots"]
+    r = oracle.build_masks(np.array([[-1, 0, 0]]))
+    for i in range(3):
+        row = bits_of(r["masks"][0, i], 3)
+        assert row == g["mask_row%d" % i]
+        assert [slots[j] for j in range(3) if row[j]] == g["list_row%d" % i]
+
+
+@pytest.mark.parametrize("bad,err", [
+    ([0, 0, 1], 1),              # node 0 is not a root
+    ([-1, 1, 0], 2),             # self parent
+    ([-1, 0, 3, 1], 3),          # forward reference
+    ([-1, 0, 1, 1, 0, -1, 5], 6),  # a forest (second root)
+    ([-1, -7], 2),               # negative non-root parent
+])
+def test_bad_trees_rejected(bad, err):
+    r = oracle.build_masks(np.array([bad]), vc=np.array([3]))
+    assert r["tree_error"][0] == err
+    assert not r["masks"].any()
+    assert (r["depth"] == -1).all() and (r["positions"] == -1).all()
+
+
+def test_chain_masks():
+    for N in (1, 2, 8, 63, 64):
+        r = oracle.build_masks(gen.chain_tree(N)[None])
+        want = [(1 << (i + 1)) - 1 for i in range(N)]
+        assert [int(x) for x in r["masks"][0]] == want
+        assert r["depth"][0].tolist() == list(range(N))
+
+
+def _reach(par):
+    """Ancestor-or-self relation by boolean closure of the parent matrix."""
+    N = len(par)
+    A = np.eye(N, dtype=np.int64)
+    for i, p in enumerate(par):
+        if p >= 0:
+            A[i, p] = 1
+    R = A.copy()
+    for _ in range(7):
+        R = ((R @ R) > 0).astype(np.int64)
+    return R
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_tree_invariants(seed):
+    rng = np.random.default_rng(seed)
+    B, N = 16, 64
+    par = np.stack([gen.random_tree(rng, N, int(rng.integers(1, 10))) for _ in range(B)])
+    vc = rng.integers(0, 10000, B).astype(np.int32)
+    r = oracle.build_masks(par, vc=vc)
+    assert not r["tree_error"].any()
+    for b in range(B):
+        R = _reach(par[b])
+        for i in range(N):
+            m = int(r["masks"][b, i])
+            assert m & 1 and (m >> i) & 1
+            assert bin(m).count("1") == r["depth"][b, i] + 1
+            assert [(m >> j) & 1 for j in range(N)] == R[i].tolist()
+            if i:
+                p = par[b, i]
+                assert m == int(r["masks"][b, p]) | (1 << i)
+                assert r["depth"][b, i] == r["depth"][b, p] + 1
+            assert r["positions"][b, i] == vc[b] + r["depth"][b, i]
+
+
+def test_eagle_generator_trees_are_valid():
+    rng = np.random.default_rng(3)
+    for _ in range(4):
+        par = gen.eagle_tree(rng, 8, 6, 64)
+        r = oracle.build_masks(par[None])
+        assert r["tree_error"][0] == 0
+        assert r["depth"].max() <= 6
+
+
+# ---------------------------------------------------------------------------
+# position shifts
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(4))
+def test_shifts_cancel_and_load_step(seed):
+    rng = np.random.default_rng(seed)
+    B, N = 8, 32
+    par = np.stack([gen.random_tree(rng, N, 6) for _ in range(B)])
+    vc = rng.integers(0, 5000, B).astype(np.int32)
+    r = oracle.build_masks(par, vc=vc)
+    chain_pos = vc[:, None] + np.arange(N, dtype=np.int32)[None]
+    up = oracle.shift_positions(chain_pos, r["depth"], +1)
+    assert (up == r["positions"]).all()                        # load_step: vc + depth
+    assert (oracle.shift_positions(up, r["depth"], -1) == chain_pos).all()  # compact_rows
+    # cancel for any depth buffer, not only a tree's
+    anyd = rng.integers(-100, 100, (B, N)).astype(np.int32)
+    p0 = rng.integers(-1000, 1000, (B, N)).astype(np.int32)
+    assert (oracle.shift_positions(oracle.shift_positions(p0, anyd, 1), anyd, -1) == p0).all()
+
+
+def test_fresh_spec_is_the_chain():
+    N = 16
+    d = oracle.build_masks(gen.chain_tree(N)[None])["depth"]
+    p = np.arange(N, dtype=np.int32)[None] + 40
+    assert (oracle.shift_positions(p, d, 1) == p).all()
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def small_case(seed, tree="random", B=2, P=37, N=12, Hq=4, Hkv=2, D=16, ps=8,
+               dtype="bf16", layout="HND", prefix_window=0):
+    wl = gen.Workload("t", B, P, N, Hq, Hkv, D, dtype, ps, tree, depth_cap=4)
+    inp = gen.make_inputs(wl, seed, "cpu", layout=layout)
+    m = oracle.build_masks(inp.parents)["masks"]
+    return wl, inp, m
+
+
+def oracle_attn(inp, masks, prefix_window=0, rows=None):
+    wl = inp.wl
+    return oracle.tree_attention(gen.bf16_bits(inp.q), gen.bf16_bits(inp.k_cache),
+                                 gen.bf16_bits(inp.v_cache), inp.strides, inp.page_table,
+                                 wl.page_size, inp.prefix_len, masks, wl.W, wl.Hkv,
+                                 prefix_window=prefix_window, rows=rows)
+
+
+def logical_kv(inp):
+    """[B][T][Hkv][D] float64 logical K/V (every slot of every page, in order)."""
+    wl = inp.wl
+    k = inp.k_cache.double()
+    v = inp.v_cache.double()
+    if inp.layout == "NHD":
+        k = k.permute(0, 2, 1, 3)
+        v = v.permute(0, 2, 1, 3)
+    pt = torch.from_numpy(inp.page_table.astype(np.int64))
+    kk = k[pt].permute(0, 1, 3, 2, 4).reshape(wl.B, -1, wl.Hkv, wl.D)
+    vv = v[pt].permute(0, 1, 3, 2, 4).reshape(wl.B, -1, wl.Hkv, wl.D)
+    return kk, vv
+
+
+def sdpa_reference(inp, masks, prefix_window=0):
+    """torch SDPA in fp64 with a dense [R][T] boolean mask over logical keys."""
+    wl = inp.wl
+    kk, vv = logical_kv(inp)
+    T = kk.shape[1]
+    g = wl.Hq // wl.Hkv
+    outs, lses = [], []
+    for b in range(wl.B):
+        P = int(inp.prefix_len[b])
+        lo = max(0, P - prefix_window) if prefix_window > 0 else 0
+        dense = torch.zeros(wl.R, T, dtype=torch.bool)
+        dense[:, lo:P] = True
+        for r in range(wl.R):
+            for j in range(wl.W):
+                if (int(masks[b, r]) >> j) & 1:
+                    dense[r, P + j] = True
+        q = inp.q[b].double().permute(1, 0, 2)                       # [Hq][R][D]
+        k = kk[b].permute(1, 0, 2).repeat_interleave(g, 0)            # [Hq][T][D]
+        v = vv[b].permute(1, 0, 2).repeat_interleave(g, 0)
+        k = torch.where(dense.any(0)[None, :, None], k, 0.0)         # unseen NaN slots out
+        v = torch.where(dense.any(0)[None, :, None], v, 0.0)
+        o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=dense[None])
+        s = (q @ k.transpose(1, 2)) / math.sqrt(wl.D)
+        s = torch.where(dense[None], s, -math.inf)
+        outs.append(o.permute(1, 0, 2))
+        lses.append((torch.logsumexp(s, -1) * LOG2E).permute(1, 0))
+    return torch.stack(outs).numpy(), torch.stack(lses).numpy()
+
+
+@pytest.mark.parametrize("layout", ["HND", "NHD"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tree_attention_matches_sdpa(layout, dtype):
+    wl, inp, m = small_case(1, dtype=dtype, layout=layout)
+    o, l = oracle_attn(inp, m)
+    ro, rl = sdpa_reference(inp, m)
+    assert np.isfinite(o).all()
+    np.testing.assert_allclose(o, ro, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(l, rl, atol=1e-12, rtol=0)
+
+
+def test_ragged_prefix_and_window_matches_sdpa():
+    wl = gen.Workload("t", 3, 50, 10, 6, 2, 16, "bf16", 8, "random", depth_cap=3)
+    inp = gen.make_inputs(wl, 5, "cpu", prefix_lens=np.array([50, 0, 17]))
+    m = oracle.build_masks(inp.parents)["masks"]
+    for pw in (0, 9, 1000):
+        o, l = oracle_attn(inp, m, prefix_window=pw)
+        ro, rl = sdpa_reference(inp, m, prefix_window=pw)
+        np.testing.assert_allclose(o, ro, atol=1e-12, rtol=0)
+        np.testing.assert_allclose(l, rl, atol=1e-12, rtol=0)
+
+
+def test_path_equivalence_bit_exact():
+    """Every tree row equals causal attention on prefix + its root-to-node path."""
+    wl, inp, m = small_case(2, N=16)
+    o, l = oracle_attn(inp, m)
+    kk = gen.bf16_bits(inp.k_cache)
+    vv = gen.bf16_bits(inp.v_cache)
+    ps = wl.page_size
+    sp, sh, st = inp.strides
+    for b in range(wl.B):
+        P = int(inp.prefix_len[b])
+        for r in range(wl.R):
+            path = [j for j in range(wl.W) if (int(m[b, r]) >> j) & 1]
+            keys = list(range(P)) + [P + j for j in path]
+            K = np.empty((len(keys), wl.Hkv, wl.D), kk.dtype)
+            V = np.empty_like(K)
+            for n, t in enumerate(keys):
+                pg = inp.page_table[b, t // ps]
+                for g in range(wl.Hkv):
+                    off = pg * sp + g * sh + (t % ps) * st
+                    K[n, g] = kk.reshape(-1)[off:off + wl.D]
+                    V[n, g] = vv.reshape(-1)[off:off + wl.D]
+            q = gen.bf16_bits(inp.q)[b, r][None]
+            co, cl = oracle.causal_attention(q, K, V)
+            assert np.array_equal(co[0], o[b, r]) and np.array_equal(cl[0], l[b, r])
+
+
+def test_chain_equals_causal_bit_exact():
+    wl, inp, m = small_case(3, tree="chain", N=8, P=29)
+    o, l = oracle_attn(inp, m)
+    kk, vv = logical_kv(inp)
+    for b in range(wl.B):
+        L = wl.P + wl.N
+        K = gen.bf16_bits(kk[b, :L].to(torch.bfloat16))
+        V = gen.bf16_bits(vv[b, :L].to(torch.bfloat16))
+        co, cl = oracle.causal_attention(gen.bf16_bits(inp.q)[b], K, V)
+        assert np.array_equal(co, o[b]) and np.array_equal(cl, l[b])
+
+
+def test_causal_matches_sdpa():
+    rng = np.random.default_rng(0)
+    n, L, Hq, Hkv, D = 5, 23, 4, 2, 8
+    q = rng.standard_normal((n, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+    o, l = oracle.causal_attention(q, k, v)
+    mask = torch.tensor([[t <= L - n + i for t in range(L)] for i in range(n)])
+    tq = torch.from_numpy(q).double().permute(1, 0, 2)
+    tk = torch.from_numpy(k).double().permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+    tv = torch.from_numpy(v).double().permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+    ro = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask[None])
+    np.testing.assert_allclose(o, ro.permute(1, 0, 2).numpy(), atol=1e-13, rtol=0)
+    s = torch.where(mask[None], tq @ tk.transpose(1, 2) / math.sqrt(D), -math.inf)
+    np.testing.assert_allclose(l, (torch.logsumexp(s, -1) * LOG2E).T.numpy(), atol=1e-13)
+
+
+def test_closed_forms():
+    D = 8
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((1, 1, D)).astype(np.float32)
+    k1 = rng.standard_normal((1, 1, D)).astype(np.float32)
+    v1 = rng.standard_normal((1, 1, D)).astype(np.float32)
+    o, l = oracle.causal_attention(q, k1, v1)
+    s = float((q.astype(np.float64) * k1).sum()) / math.sqrt(D)
+    np.testing.assert_allclose(o[0, 0], v1[0, 0], atol=1e-15)
+    assert abs(l[0, 0] - s * LOG2E) < 1e-13
+    # n identical keys -> mean of values, lse = (s + ln n) / ln 2
+    n = 7
+    K = np.repeat(k1, n, 0)
+    V = rng.standard_normal((n, 1, D)).astype(np.float32)
+    o, l = oracle.causal_attention(q, K, V)
+    np.testing.assert_allclose(o[0, 0], V[:, 0].astype(np.float64).mean(0), atol=1e-14)
+    assert abs(l[0, 0] - (s + math.log(n)) * LOG2E) < 1e-13
+    # constant V -> V whatever the keys
+    K = rng.standard_normal((n, 1, D)).astype(np.float32)
+    V = np.repeat(v1, n, 0)
+    o, _ = oracle.causal_attention(q, K, V)
+    np.testing.assert_allclose(o[0, 0], v1[0, 0], atol=1e-14)
+
+
+def test_empty_visible_set():
+    wl = gen.Workload("t", 1, 0, 3, 2, 1, 8, "f32", 4, "random", depth_cap=2)
+    inp = gen.make_inputs(wl, 0, "cpu")
+    o, l = oracle_attn(inp, np.zeros((1, 3), np.uint64))
+    assert (o == 0).all() and np.isneginf(l).all()
+
+
+def test_nan_in_node_leaks_only_to_descendants():
+    wl, inp, m = small_case(6, N=16, B=1)
+    base_o, base_l = oracle_attn(inp, m)
+    j = 5
+    P = int(inp.prefix_len[0])
+    t = P + j
+    pg = int(inp.page_table[0, t // wl.page_size])
+    inp.k_cache[pg, 0, t % wl.page_size] = float("nan")
+    inp.v_cache[pg, 1, t % wl.page_size] = float("nan")
+    o, l = oracle_attn(inp, m)
+    g = wl.Hq // wl.Hkv
+    for r in range(wl.R):
+        sees = (int(m[0, r]) >> j) & 1
+        for h in range(wl.Hq):
+            if sees and h // g in (0, 1):
+                assert np.isnan(o[0, r, h]).any()
+            else:
+                assert np.array_equal(o[0, r, h], base_o[0, r, h])
+                assert base_l[0, r, h] == l[0, r, h]
+
+
+def test_page_permutation_invariance():
+    wl, inp, m = small_case(7)
+    o, l = oracle_attn(inp, m)
+    # move every page to a new physical index and rewrite the table
+    n_pages = inp.k_cache.shape[0]
+    perm = np.random.default_rng(1).permutation(n_pages)
+    inv = np.argsort(perm)
+    k2 = inp.k_cache[torch.from_numpy(inv)]
+    v2 = inp.v_cache[torch.from_numpy(inv)]
+    pt2 = perm[inp.page_table].astype(np.int32)
+    o2, l2 = oracle.tree_attention(gen.bf16_bits(inp.q), gen.bf16_bits(k2), gen.bf16_bits(v2),
+                                   inp.strides, pt2, wl.page_size, inp.prefix_len, m, wl.W,
+                                   wl.Hkv)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+
+
+def test_row_subset_matches_full():
+    wl, inp, m = small_case(8)
+    o, l = oracle_attn(inp, m)
+    rows = np.array([0, 5, 17, wl.B * wl.R * wl.Hq - 1])
+    so, sl = oracle_attn(inp, m, rows=rows)
+    assert np.array_equal(so, o.reshape(-1, wl.D)[rows])
+    assert np.array_equal(sl, l.reshape(-1)[rows])
+
+
+def test_merge_example_and_split_invariance():
+    g = load("merge.txt")
+    Z, O = g["Z"], g["O"]
+    out, lse = oracle.merge(np.array(O, float).reshape(2, 1, 1), np.log2(np.array(Z, float)).reshape(2, 1))
+    assert out[0, 0] == g["merged"][0] != g["not_the_average"][0]
+    assert abs(lse[0] - math.log2(sum(Z))) < 1e-15
+    # attention over A u B equals the merge of the parts, for random splits
+    rng = np.random.default_rng(9)
+    L, D = 40, 8
+    q = rng.standard_normal((1, 1, D)).astype(np.float32)
+    k = rng.standard_normal((L, 1, D)).astype(np.float32)
+    v = rng.standard_normal((L, 1, D)).astype(np.float32)
+    full_o, full_l = oracle.causal_attention(q, k, v)
+    for _ in range(5):
+        sel = rng.random(L) < 0.4
+        parts = []
+        for s in (sel, ~sel):
+            po, pl = oracle.causal_attention(q, k[s], v[s])
+            parts.append((po[0], pl[0]))
+        mo, ml = oracle.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+        np.testing.assert_allclose(mo, full_o[0], atol=1e-13)
+        assert abs(ml[0] - full_l[0, 0]) < 1e-13
+    # empty parts carry no weight
+    mo, ml = oracle.merge(np.stack([full_o[0], np.zeros_like(full_o[0])]),
+                          np.stack([full_l[0], np.array([-np.inf])]))
+    np.testing.assert_allclose(mo, full_o[0], atol=1e-15)
+    mo, ml = oracle.merge(np.zeros((2, 1, D)), np.full((2, 1), -np.inf))
+    assert (mo == 0).all() and np.isneginf(ml).all()
+
+
+# ---------------------------------------------------------------------------
+# greedy verify
+# ---------------------------------------------------------------------------
+
+def recursive_trees(N):
+    """Every parent array with parents[0] = -1 and parents[i] in [0, i)."""
+    for tail in itertools.product(*[range(i) for i in range(1, N)]):
+        yield np.array((-1,) + tail, np.int32)
+
+
+def root_paths(par):
+    N = len(par)
+    kids = [[c for c in range(N) if par[c] == v] for v in range(N)]
+    paths, stack = [], [[0]]
+    while stack:
+        p = stack.pop()
+        paths.append(p)
+        for c in kids[p[-1]]:
+            stack.append(p + [c])
+    return paths, kids
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6])
+def test_greedy_brute_force(N):
+    rng = np.random.default_rng(N)
+    trees = list(recursive_trees(N))
+    for par in trees:
+        for _ in range(3 if N == 6 else 8):
+            draft = rng.integers(0, 3, N).astype(np.int32)
+            target = rng.integers(0, 3, N).astype(np.int32)
+            r = oracle.verify_greedy(draft[None], target[None], par[None])
+            a = int(r["accept_len"][0])
+            path = r["accepted_path"][0, :a].tolist()
+            assert r["accepted_path"][0, a:].tolist() == [-1] * (N - a)
+            paths, kids = root_paths(par)
+
+            def consistent(p):
+                return all(draft[p[k]] == target[p[k - 1]] for k in range(1, len(p)))
+            assert path in paths and consistent(path)
+            # not extendable, and the smallest consistent child at every depth
+            assert not any(draft[c] == target[path[-1]] for c in kids[path[-1]])
+            for k in range(1, a):
+                ok = [c for c in kids[path[k - 1]] if draft[c] == target[path[k - 1]]]
+                assert path[k] == min(ok)
+            assert r["accepted_tokens"][0, :a].tolist() == [int(target[p]) for p in path]
+            # distinct sibling tokens -> the unique longest consistent path
+            sib_distinct = all(len({int(draft[c]) for c in ks}) == len(ks) for ks in kids)
+            if sib_distinct:
+                best = max((p for p in paths if consistent(p)), key=len)
+                assert len([p for p in paths if consistent(p) and len(p) == len(best)]) == 1
+                assert path == best
+
+
+def test_chain_accept_example():
+    g = load("chain_accept.txt")
+    # chain R D1 D2 D3; row k predicts the token of row k + 1; row 3 predicts B
+    draft = np.array([[100, 11, 12, 13]], np.int32)      # R D1 D2 D3
+    target = np.array([[11, 12, 13, 99]], np.int32)      # D1 D2 D3 B
+    r = oracle.verify_greedy(draft, target, gen.chain_tree(4)[None])
+    assert r["accept_len"][0] == g["accept_lens"][0] == g["num_correct_drafts"][0] + 1
+    assert r["accepted_tokens"][0].tolist() == [11, 12, 13, 99]      # D1 D2 D3 B
+    assert r["accepted_path"][0].tolist() == [0, 1, 2, 3]            # R D1 D2 D3 rows
+    # first mismatch stops the chain: accept_len = 1 + leading matches
+    target2 = np.array([[11, 55, 13, 99]], np.int32)
+    assert oracle.verify_greedy(draft, target2, gen.chain_tree(4)[None])["accept_len"][0] == 2
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_greedy_path_properties(seed):
+    rng = np.random.default_rng(100 + seed)
+    B, N = 32, 64
+    par = np.stack([gen.random_tree(rng, N, 8) for _ in range(B)])
+    dr, tg = zip(*[gen.tokens_for(rng, p, 0.7) for p in par])
+    r = oracle.verify_greedy(np.stack(dr), np.stack(tg), par)
+    depth = oracle.build_masks(par)["depth"]
+    for b in range(B):
+        a = r["accept_len"][b]
+        p = r["accepted_path"][b, :a]
+        assert p[0] == 0 and (np.diff(p) > 0).all()
+        assert all(par[b, p[k]] == p[k - 1] for k in range(1, a))
+        assert 1 <= a <= depth[b].max() + 1
+
+
+# ---------------------------------------------------------------------------
+# compaction
+# ---------------------------------------------------------------------------
+
+def test_compaction_worked_example():
+    g = load("compaction.txt")
+    N = g["block_slots"][0]
+    idx = g["accept_index"] + [-1] * (N - len(g["accept_index"]))
+    rng = np.random.default_rng(0)
+    for dt in (np.float32, np.uint16, np.uint8):   # fp32, bf16 and fp8 bit patterns
+        rows = 24
+        buf = rng.integers(0, 255, (2, N, rows)).astype(dt)
+        before = buf.copy()
+        isz = buf.itemsize
+        oracle.compact_rows([dict(buf=buf, stride_token=rows * isz, stride_batch=N * rows * isz,
+                                  row_bytes=rows * isz)],
+                            np.array([idx, list(range(N))], np.int32),
+                            np.array(g["accept_lens"] + [3], np.int32))
+        src = [i for i in idx if i >= 0]
+        assert np.array_equal(buf[0, g["moved_to"]], before[0, src])
+        assert np.array_equal(buf[0, 4:], before[0, 4:])       # overshoot untouched
+        assert np.array_equal(buf[1], before[1])               # chain: nothing moves
+
+
+def test_compaction_overlap_reads_before_writes():
+    N, rows = 8, 4
+    buf = np.arange(N * rows, dtype=np.int32).reshape(1, N, rows)
+    before = buf.copy()
+    path = np.array([[0, 2, 5, -1, -1, -1, -1, -1]], np.int32)
+    oracle.compact_rows([dict(buf=buf, stride_token=16, stride_batch=N * 16, row_bytes=16)],
+                        path, np.array([3], np.int32))
+    assert np.array_equal(buf[0, :3], before[0, [0, 2, 5]])
+
+
+def test_compaction_paged_heads():
+    """Paged HND cache: only the accepted window rows of each head move."""
+    B, N, Hkv, D, ps = 2, 6, 3, 4, 4
+    P = np.array([5, 9], np.int32)
+    max_pages = 4
+    n_pages = 1 + B * max_pages
+    pt = (np.random.default_rng(1).permutation(n_pages - 1) + 1).astype(np.int32).reshape(B, max_pages)
+    cache = np.random.default_rng(2).integers(0, 1 << 15, (n_pages, Hkv, ps, D)).astype(np.uint16)
+    before = cache.copy()
+    path = np.array([[0, 3, 4, -1, -1, -1], [0, 1, 5, -1, -1, -1]], np.int32)
+    alen = np.array([3, 3], np.int32)
+    oracle.compact_rows([dict(buf=cache, page_table=pt, prefix_len=P, page_size=ps,
+                              stride_page=Hkv * ps * D * 2, stride_head=ps * D * 2,
+                              stride_token=D * 2, n_heads=Hkv, row_bytes=D * 2)], path, alen)
+    expect = before.copy()
+    for b in range(B):
+        for i in range(alen[b]):
+            s, d = P[b] + path[b, i], P[b] + i
+            expect[pt[b, d // ps], :, d % ps] = before[pt[b, s // ps], :, s % ps]
+    assert np.array_equal(cache, expect)
