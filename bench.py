@@ -1,0 +1,243 @@
+"""Benchmark of one draft-tree verify step on one MI355X.
+
+A step is one pass of the whole path over one batch of the long-context
+verify workload (B 4, P 131072, N 64 random trees of depth <= 8, Hq 32,
+Hkv 8, D 128, bf16, page size 64): tree_build_masks -> tree_attention_prefix
+-> tree_attention_window_merge -> verify_tree_greedy -> compact_window_rows
+(K cache, V cache and a hidden-state table) -> tree_shift_positions(-1).
+Inputs are resident in HBM before the timed region.
+
+Prints one JSON line (see the design doc for every field).  `value` is the KV
+bytes the step must read divided by the step time; the roofline object is
+for the dominant kernel (the split-K prefix), timed with HIP events on the
+stream it runs on.  `cpu_baseline` times the CPU fp64 oracle on a bounded
+sample of rows of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import tree_attention_verify_amd as tav  # noqa: E402
+from tree_attention_verify_amd import inputs as gen  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "tree-verify attention KV GB/s + rows/s, % of MI355X HBM peak at long ctx"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kv_bytes(wl, P_vis, with_window=True):
+    e = 2 if wl.dtype == "bf16" else 4
+    keys = P_vis + (wl.W if with_window else 0)
+    return wl.B * keys * wl.Hkv * wl.D * 2 * e
+
+
+def attn_flops(wl, masks_np, P_vis):
+    pop = sum(bin(int(x)).count("1") for x in masks_np.reshape(-1))
+    return 4.0 * wl.D * wl.Hq * (wl.B * wl.R * P_vis + pop)
+
+
+class Step:
+    """Preallocated buffers and the ctypes calls of one verify step."""
+
+    def __init__(self, wl, inp, hidden_dim=4096):
+        self.wl, self.inp = wl, inp
+        d = "cuda"
+        self.L = tav.lib()
+        t = lambda x, dt=torch.int32: torch.as_tensor(np.ascontiguousarray(x)).to(dt).to(d)
+        self.parents = t(inp.parents)
+        self.prefix_len = t(inp.prefix_len)
+        self.page_table = t(inp.page_table)
+        self.draft, self.target = t(inp.draft), t(inp.target)
+        B, N, R = wl.B, wl.N, wl.R
+        self.depth = torch.empty((B, N), dtype=torch.int32, device=d)
+        self.masks = torch.empty((B, N), dtype=torch.int64, device=d)
+        self.positions = torch.empty((B, N), dtype=torch.int32, device=d)
+        self.tree_error = torch.empty((B,), dtype=torch.int32, device=d)
+        self.out = torch.empty_like(inp.q)
+        self.lse = torch.empty((B, R, wl.Hq), dtype=torch.float32, device=d)
+        self.path = torch.empty((B, N), dtype=torch.int32, device=d)
+        self.alen = torch.empty((B,), dtype=torch.int32, device=d)
+        self.tokens = torch.empty((B, N), dtype=torch.int32, device=d)
+        self.hidden = torch.randn((B, N, hidden_dim), device=d).to(torch.bfloat16)
+        sp, sh, st, Hkv, ps = tav.kv_strides(inp.k_cache, inp.layout)
+        self.kv = (sp, sh, st, inp.k_cache.shape[0], ps)
+        self.code = tav.TAV_BF16 if wl.dtype == "bf16" else tav.TAV_F32
+        nbytes = tav.tree_attention_workspace_size(inp.q.dtype, B, R, wl.Hq, wl.Hkv, wl.D, wl.P,
+                                                   wl.prefix_window, ps)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=d)
+        tables = [tav.RowTable.paged_kv(inp.k_cache, self.page_table, self.prefix_len),
+                  tav.RowTable.paged_kv(inp.v_cache, self.page_table, self.prefix_len),
+                  tav.RowTable.dense_rows(self.hidden)]
+        self.tables = (tav.TavRows * 3)()
+        for i, tb in enumerate(tables):
+            self.tables[i] = tav.TavRows(
+                tb.buf.data_ptr(), None if tb.page_table is None else tb.page_table.data_ptr(),
+                None if tb.prefix_len is None else tb.prefix_len.data_ptr(),
+                0 if tb.page_table is None else tb.page_table.shape[1], tb.page_size,
+                tb.num_pages, tb.stride_page, tb.stride_token, tb.stride_head, tb.stride_batch,
+                tb.n_heads, tb.row_bytes)
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def _attn(self, fn):
+        wl, inp = self.wl, self.inp
+        sp, sh, st, npages, ps = self.kv
+        rc = fn(inp.q.data_ptr(), inp.k_cache.data_ptr(), inp.v_cache.data_ptr(), self.code,
+                sp, sh, st, npages, self.page_table.data_ptr(), self.page_table.shape[1], ps,
+                self.prefix_len.data_ptr(), wl.P, wl.prefix_window, self.masks.data_ptr(),
+                wl.W, wl.B, wl.R, wl.Hq, wl.Hkv, wl.D, 0.0, self.out.data_ptr(),
+                self.lse.data_ptr(), self.ws.data_ptr(), self.ws.numel(), self.stream)
+        assert rc == 0, self.L.tav_last_error()
+
+    def run(self, ev=None):
+        L, wl = self.L, self.wl
+        B, N = wl.B, wl.N
+        assert L.tree_build_masks(self.parents.data_ptr(), B, N, self.prefix_len.data_ptr(),
+                                  self.depth.data_ptr(), self.masks.data_ptr(),
+                                  self.positions.data_ptr(), self.tree_error.data_ptr(),
+                                  self.stream) == 0
+        if ev is not None:
+            ev[0].record()
+        self._attn(L.tree_attention_prefix)
+        if ev is not None:
+            ev[1].record()
+        self._attn(L.tree_attention_window_merge)
+        assert L.verify_tree_greedy(self.draft.data_ptr(), self.target.data_ptr(),
+                                    self.parents.data_ptr(), B, N, self.path.data_ptr(),
+                                    self.alen.data_ptr(), self.tokens.data_ptr(),
+                                    self.stream) == 0
+        assert L.compact_window_rows(self.tables, 3, self.path.data_ptr(), self.alen.data_ptr(),
+                                     B, N, self.stream) == 0
+        assert L.tree_shift_positions(self.positions.data_ptr(), self.depth.data_ptr(), B, N, -1,
+                                      self.stream) == 0
+
+
+def cpu_baseline(wl, inp, masks_np, budget_s):
+    """The CPU fp64 oracle on a bounded sample of rows of the same workload."""
+    import oracle
+    kc, vc = gen.bf16_bits(inp.k_cache), gen.bf16_bits(inp.v_cache)
+    q = gen.bf16_bits(inp.q)
+    n_rows = wl.B * wl.R * wl.Hq
+    rng = np.random.default_rng(0)
+    cores = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    threads = min(cores, int(omp)) if omp else cores
+    n, total_t, done = 16, 0.0, 0
+    while True:
+        rows = rng.integers(0, n_rows, n)
+        t0 = time.perf_counter()
+        oracle.tree_attention(q, kc, vc, inp.strides, inp.page_table, wl.page_size,
+                              inp.prefix_len, masks_np, wl.W, wl.Hkv,
+                              prefix_window=wl.prefix_window, rows=rows)
+        dt = time.perf_counter() - t0
+        total_t += dt
+        done += n
+        if total_t >= budget_s or done >= n_rows:
+            break
+        n = int(min(n_rows - done, max(16, n * min(4.0, (budget_s - total_t) / max(dt, 1e-3)))))
+    t_full = total_t * n_rows / done
+    P_vis = min(wl.P, wl.prefix_window) if wl.prefix_window else wl.P
+    return {"value": kv_bytes(wl, P_vis) / t_full / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "rows_per_s": n_rows / t_full,
+            "sample": "%d of %d (request, row, head) rows of the same workload, %.1f s of fp64 "
+                      "oracle time, scaled to the whole step" % (done, n_rows, total_t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long64", choices=sorted(gen.WORKLOADS))
+    ap.add_argument("--seed", type=int, default=4)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle time for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = gen.WORKLOADS[args.workload]
+    log("workload", wl)
+    t0 = time.perf_counter()
+    inp = gen.make_inputs(wl, args.seed, "cuda")
+    torch.cuda.synchronize()
+    log("inputs ready in %.1f s" % (time.perf_counter() - t0))
+    step = Step(wl, inp)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    pairs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+             for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step.run(pairs[i])
+    end.record()
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host
+    ms_step = start.elapsed_time(end) / args.steps
+    prefix_ms = [a.elapsed_time(b) for a, b in pairs]
+    prefix_avg = float(np.mean(prefix_ms))
+    log("timed %d steps: %.3f ms/step (host %.3f ms/step), prefix kernel avg %.3f ms "
+        "(min %.3f max %.3f)" % (args.steps, ms_step, t_host * 1e3 / args.steps, prefix_avg,
+                                 min(prefix_ms), max(prefix_ms)))
+
+    masks_np = step.masks.cpu().numpy().view(np.uint64)
+    P_vis = min(wl.P, wl.prefix_window) if wl.prefix_window else wl.P
+    kvb = kv_bytes(wl, P_vis)
+    rows = wl.B * wl.R
+    value = kvb / (ms_step * 1e-3) / 1e9
+    e = 2 if wl.dtype == "bf16" else 4
+    prefix_bytes = kv_bytes(wl, P_vis, with_window=False) + wl.B * wl.R * wl.Hq * wl.D * e
+    achieved = prefix_bytes / (prefix_avg * 1e-3) / 1e9
+    flops = attn_flops(wl, masks_np, P_vis)
+    prefix_flops = 4.0 * wl.D * wl.Hq * wl.B * wl.R * P_vis
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": "%s: B %d, P %d, N %d random trees depth<=%d, Hq %d, Hkv %d, D %d, "
+                               "page size %d" % (wl.name, wl.B, wl.P, wl.N, wl.depth_cap, wl.Hq,
+                                                 wl.Hkv, wl.D, wl.page_size),
+                   "B": wl.B, "P": wl.P, "N": wl.N, "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D,
+                   "page_size": wl.page_size, "parallelism": "1 GPU"},
+        "rows_per_s": round(rows / (ms_step * 1e-3), 1),
+        "head_rows_per_s": round(rows * wl.Hq / (ms_step * 1e-3), 1),
+        "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
+        "attention_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "roofline": {"kernel": "k_prefix_mfma (split-K prefix)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_ms": round(prefix_avg, 4),
+                     "mfma_tflops": round(prefix_flops / (prefix_avg * 1e-3) / 1e12, 1),
+                     "mfma_frac": round(prefix_flops / (prefix_avg * 1e-3) / 1e12
+                                        / MFMA_BF16_PEAK_TFS, 4)},
+    }
+    if args.cpu_budget > 0:
+        log("cpu baseline (oracle), budget %.0f s" % args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(wl, inp, masks_np, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,267 @@
+/*
+ * treeverify.h -- C ABI of the MI355X (gfx950) draft-tree verify path.
+ *
+ * One verify round of draft-tree speculative decoding on one GPU:
+ *   tree_build_masks     parents -> depth, 64-bit ancestor masks, positions
+ *   tree_attention       paged prefix + masked tree window -> out, base-2 LSE
+ *   verify_tree_greedy   draft tokens, target argmax -> accepted path
+ *   compact_window_rows  accepted path -> rows moved to the window's front
+ *   tree_shift_positions load_step / compact_rows position shifts
+ *
+ * Sources (page title, section):
+ *  [DTS] "Draft-tree speculation" (tokenspeed design notes)
+ *  [ETA] "EAGLE Tree Attention candidate layout, positions and visibility"
+ *        (SGLang EAGLE tree-verify analysis)
+ *  [MEM] "Medusa, EAGLE-1/2/3, MTP, and tree attention" (course chapter)
+ *  [DDT] "From Greedy to Sampling: The Architecture of Choice in DDTree
+ *        Speculative Decoding"
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers owned by the caller, unless marked "host".
+ *    Arrays are dense row-major with the shapes given.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues kernels on it: no host synchronisation, no allocation, no
+ *    global mutable state, so calls can be captured in a HIP graph.
+ *  - All arguments are checked on the host before anything is launched; a
+ *    violation returns a non-zero status, launches nothing, and
+ *    tav_last_error() names every failed check ([DTS] "Scope": refuse up
+ *    front and report every blocker together).  Device-side data that the
+ *    host cannot see (parent arrays, page-table entries, per-request lengths)
+ *    never causes an out-of-bounds access; what happens to it is stated per
+ *    entry point.
+ */
+#ifndef TREEVERIFY_H
+#define TREEVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TAV_OK = 0,
+    TAV_ERR_INVALID_ARG = 1, /* null pointer, negative size, limit violated */
+    TAV_ERR_UNSUPPORTED = 2, /* well-formed but outside what is implemented */
+    TAV_ERR_WORKSPACE = 3,   /* workspace too small or misaligned          */
+    TAV_ERR_HIP = 4          /* a HIP launch failed                         */
+} tav_status;
+
+typedef enum {
+    TAV_F32 = 0,  /* IEEE fp32 */
+    TAV_BF16 = 1  /* bfloat16 */
+} tav_dtype;
+
+/* Text of the last failure on the calling thread ("" after a success). */
+const char *tav_last_error(void);
+
+/* Library version string. */
+const char *tav_version(void);
+
+/*
+ * Ancestor masks, depth and positions of each request's draft tree.
+ * [ETA] section 1: row i sees key j of the window iff j == i or j is an
+ * ancestor of i; [DTS] "One tree attention ...": that visibility is one
+ * 64-bit mask per row (bit j = window node j); [ETA] section 2 and [DTS]
+ * "Position follows depth, slot follows node index": node i's RoPE position
+ * is vc + depth[i].
+ *
+ * parents    int32 [B][N]  node 0 is the root (-1); parents[i] in [0, i)
+ * B, N       B >= 0, 1 <= N <= 64
+ * vc         int32 [B] or NULL (0): committed prefix length per request
+ * depth      int32 [B][N]  out: number of ancestors
+ * masks      uint64 [B][N] out: bit i and the bits of all ancestors of i
+ * positions  int32 [B][N] or NULL: out vc[b] + depth
+ * tree_error int32 [B] or NULL: out 0, or 1 + the first node whose parent is
+ *            invalid ([MEM] "Building the mask, for real": a missing parent
+ *            is rejected, never treated as a root).  For such a request
+ *            masks are 0 and depth/positions are -1.
+ */
+tav_status tree_build_masks(const int32_t *parents, int32_t B, int32_t N,
+                            const int32_t *vc, int32_t *depth, uint64_t *masks,
+                            int32_t *positions, int32_t *tree_error, void *stream);
+
+/*
+ * In-place position shift: positions[b][i] += direction * (depth[b][i] - i).
+ * direction +1 is load_step (vc + i -> vc + depth), -1 is compact_rows
+ * (vc + depth -> vc + i); the two cancel for any depth buffer ([DTS]
+ * "Position follows depth, slot follows node index").
+ * positions, depth int32 [B][N]; B >= 0; 1 <= N <= 64; direction = +1 or -1.
+ */
+tav_status tree_shift_positions(int32_t *positions, const int32_t *depth, int32_t B,
+                                int32_t N, int32_t direction, void *stream);
+
+/*
+ * Bytes of device workspace tree_attention needs for these sizes (the same
+ * arguments it takes).  0 means the arguments are invalid.
+ */
+size_t tree_attention_workspace_size(tav_dtype dtype, int32_t B, int32_t R, int32_t Hq,
+                                     int32_t Hkv, int32_t D, int32_t max_prefix_len,
+                                     int32_t prefix_window, int32_t page_size);
+
+/*
+ * Tree attention over a paged KV cache: every row attends the committed
+ * prefix plus exactly the window nodes its ancestor mask selects, and the
+ * result carries the base-2 log-sum-exp of the whole visible set.
+ * [DTS] "One tree attention: the leaf's decode for the prefix, a small kernel
+ * for the tree" (the cascade: a prefix decode, a masked window part, and a
+ * merge of both through their base-2 LSE); [ETA] section 4 (the same cascade
+ * on FlashAttention: common prefix, per-query ancestor suffix, LSE merge).
+ *
+ * Row r of request b, query head h uses kv head h / (Hq / Hkv) and sees, with
+ * P = prefix_len[b]:
+ *   prefix keys at logical positions [p_lo, P), p_lo = max(0, P -
+ *   prefix_window) when prefix_window > 0 (a frozen sliding window, [DTS]
+ *   "One tree attention ...", lanes with per-row tables), else 0; and
+ *   window node j at logical position P + j for every j < W whose bit is set
+ *   in masks[b][r].
+ * Scores are sm_scale * q.k (sm_scale <= 0 means 1/sqrt(D)); keys that are
+ * not visible are never used, so non-finite values there never reach an
+ * output.  A row with no visible key gets out = 0, lse2 = -inf.
+ *
+ * q          [B][R][Hq][D] dtype, contiguous
+ * k_cache, v_cache  paged pools of dtype: element (page, kv head g, slot s,
+ *            channel d) at page*stride_page + g*stride_head + s*stride_token + d
+ *            (strides in elements; channels contiguous; e.g. HND
+ *            [pages][Hkv][page_size][D] or NHD [pages][page_size][Hkv][D]).
+ *            Pointers and strides must give 16-byte aligned rows.
+ * num_pages  pages in each pool; page-table entries outside [0, num_pages)
+ *            are clamped into it (memory-safe, results for that key undefined)
+ * page_table int32 [B][max_pages]: logical position t of request b lives in
+ *            page page_table[b][t / page_size] at slot t % page_size
+ * page_size  a power of two in [1, 1024]
+ * prefix_len int32 [B]: P per request, in [0, max_prefix_len] (values
+ *            outside are clamped); the window keys follow it
+ * max_prefix_len  host bound on prefix_len; max_pages * page_size must be
+ *            >= max_prefix_len + W
+ * masks      uint64 [B][R] (bits >= W are ignored)
+ * B >= 0; 1 <= R <= 64; 0 <= W <= 64; Hq % Hkv == 0; D in {64, 128}
+ * dtype      TAV_BF16 (bf16 MFMA prefix, fp32 accumulation) or TAV_F32
+ *            (fp32 vector-ALU path)
+ * out        [B][R][Hq][D] dtype (bf16 rounded to nearest even)
+ * lse2       float [B][R][Hq] or NULL: log2 of the sum over visible keys of
+ *            exp(score) (so 2^lse2 is the softmax denominator)
+ * workspace  device memory of >= tree_attention_workspace_size(...) bytes,
+ *            256-byte aligned; contents are scratch between calls
+ */
+tav_status tree_attention(const void *q, const void *k_cache, const void *v_cache,
+                          tav_dtype dtype, int64_t stride_page, int64_t stride_head,
+                          int64_t stride_token, int64_t num_pages,
+                          const int32_t *page_table, int32_t max_pages, int32_t page_size,
+                          const int32_t *prefix_len, int32_t max_prefix_len,
+                          int32_t prefix_window, const uint64_t *masks, int32_t W,
+                          int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t D,
+                          float sm_scale, void *out, float *lse2, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
+ * The two phases of tree_attention as separate calls, with tree_attention's
+ * arguments and contract; tree_attention is exactly tree_attention_prefix
+ * followed by tree_attention_window_merge on the same stream and workspace.
+ * They mirror the cascade's split ([DTS] "One tree attention ...": the
+ * prefix decode, then the window part and the merge), so a caller can place
+ * other work between them or time them apart.
+ *   tree_attention_prefix        reads q, the K/V prefix pages, page_table and
+ *                                prefix_len; writes the split-K prefix partials
+ *                                into the workspace (masks, W, out, lse2 unused
+ *                                and may be NULL / 0)
+ *   tree_attention_window_merge  reads the workspace partials of a preceding
+ *                                tree_attention_prefix with the same arguments,
+ *                                the window keys and masks; writes out and lse2
+ */
+tav_status tree_attention_prefix(const void *q, const void *k_cache, const void *v_cache,
+                                 tav_dtype dtype, int64_t stride_page, int64_t stride_head,
+                                 int64_t stride_token, int64_t num_pages,
+                                 const int32_t *page_table, int32_t max_pages, int32_t page_size,
+                                 const int32_t *prefix_len, int32_t max_prefix_len,
+                                 int32_t prefix_window, const uint64_t *masks, int32_t W,
+                                 int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t D,
+                                 float sm_scale, void *out, float *lse2, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+tav_status tree_attention_window_merge(const void *q, const void *k_cache, const void *v_cache,
+                                       tav_dtype dtype, int64_t stride_page, int64_t stride_head,
+                                       int64_t stride_token, int64_t num_pages,
+                                       const int32_t *page_table, int32_t max_pages,
+                                       int32_t page_size, const int32_t *prefix_len,
+                                       int32_t max_prefix_len, int32_t prefix_window,
+                                       const uint64_t *masks, int32_t W, int32_t B, int32_t R,
+                                       int32_t Hq, int32_t Hkv, int32_t D, float sm_scale,
+                                       void *out, float *lse2, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
+/*
+ * Greedy tree verify ([MEM] "Walking the accepted path"): from the root, move
+ * to the child whose draft token equals the target's argmax at the current
+ * node; stop when no child matches.  Ties between children carrying the same
+ * token go to the lowest node index.  The walk takes at most N nodes.
+ *
+ * draft_tokens, target_argmax, parents  int32 [B][N]; B >= 0; 1 <= N <= 64
+ * accepted_path   int32 [B][N] out: node indices, -1 padded
+ *                 (the single owner of the path, [DTS] "The tree is a
+ *                 parameter of the chain path")
+ * accept_len      int32 [B] out: nodes on the path, counting the root
+ *                 ([ETA] section 2: accept_lens = correct drafts + 1)
+ * accepted_tokens int32 [B][N] or NULL: out target_argmax[path[k]] for
+ *                 k < accept_len (the last is the bonus token), -1 after
+ */
+tav_status verify_tree_greedy(const int32_t *draft_tokens, const int32_t *target_argmax,
+                              const int32_t *parents, int32_t B, int32_t N,
+                              int32_t *accepted_path, int32_t *accept_len,
+                              int32_t *accepted_tokens, void *stream);
+
+/*
+ * One row table for compact_window_rows: a buffer holding, per (request,
+ * window slot), n_heads segments of row_bytes bytes (e.g. one layer's K cache
+ * with n_heads = Hkv and row_bytes = D * element size, or a hidden-state
+ * buffer with n_heads = 1).  All strides are in BYTES.
+ *   paged (page_table != NULL): window slot i of request b is logical
+ *     position prefix_len[b] + i; segment h of it is at
+ *     base + page*stride_page + h*stride_head + (pos % page_size)*stride_token
+ *     with page = page_table[b*max_pages + pos / page_size]
+ *   dense (page_table == NULL): at base + b*stride_batch + i*stride_token
+ *     + h*stride_head
+ * row_bytes, the strides and base must be multiples of 4.  Each physical
+ * region must appear in at most one table of a call ([DTS] "Recurrent state
+ * follows the parent": each region moves once per cache group).
+ */
+typedef struct {
+    void *base;
+    const int32_t *page_table; /* device int32 [B][max_pages], or NULL */
+    const int32_t *prefix_len; /* device int32 [B] (paged tables)       */
+    int32_t max_pages;
+    int32_t page_size;         /* power of two in [1, 1024] (paged)     */
+    int64_t num_pages;         /* pages in the pool (paged), for bounds */
+    int64_t stride_page;
+    int64_t stride_token;
+    int64_t stride_head;
+    int64_t stride_batch;      /* dense tables */
+    int32_t n_heads;
+    int32_t row_bytes;
+} tav_rows;
+
+/*
+ * Moves the accepted path's rows to the window's leading slots in every
+ * table: for i < accept_len[b], row i <- row accepted_path[b][i], copied as
+ * 32-bit words so any element type works ([DTS] "The tree is a parameter of
+ * the chain path": compact_window_rows copies words; [MEM] "Discarding the
+ * rejected branches' KV").  Every source row of a request is read before any
+ * row is written, so overlapping paths such as [0, 2, 5] are safe.  Rows at
+ * or past accept_len, other requests and other bytes are not touched.
+ *
+ * tables   HOST array of n_tables descriptors (copied at call time)
+ * accepted_path int32 [B][N], accept_len int32 [B] (device, e.g. from
+ *          verify_tree_greedy).  accept_len is clamped to [0, N]; a path
+ *          entry outside [0, N), or a row whose page falls outside the table,
+ *          is skipped.
+ * B >= 0; 1 <= N <= 64; 0 <= n_tables
+ */
+tav_status compact_window_rows(const tav_rows *tables, int32_t n_tables,
+                               const int32_t *accepted_path, const int32_t *accept_len,
+                               int32_t B, int32_t N, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREEVERIFY_H */

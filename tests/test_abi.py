@@ -1,0 +1,146 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/treeverify.h declares, and rejects bad arguments on the host with a
+message naming every failed check, before anything is launched.
+
+The rejected calls pass placeholder pointers, so they are only run where no
+GPU is visible (a validation bug must never turn them into a launch).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import tree_attention_verify_amd as tav
+from tree_attention_verify_amd import build as tav_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "treeverify.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(tav.LIB_PATH):
+        tav_build.build()
+    return tav.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:tav_status|size_t|const char \*)\s*(\w+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("tree_build_masks", "tree_attention", "verify_tree_greedy", "compact_window_rows",
+              "tree_shift_positions", "tree_attention_workspace_size"):
+        assert n in names
+    assert set(names) == set(tav.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert L.tav_version().decode().startswith("treeverify")
+
+
+def test_workspace_size_host_only(L):
+    f = tav.tree_attention_workspace_size
+    n = f(torch.bfloat16, 4, 64, 32, 8, 128, 131072, 0, 64)
+    assert n > 0 and n % 256 == 0
+    # fp32 partials: at least one (o, lse) per row
+    assert n >= 4 * 64 * 32 * 129 * 4
+    assert f(torch.bfloat16, 4, 65, 32, 8, 128, 1024, 0, 64) == 0      # R > 64
+    assert f(torch.bfloat16, 4, 8, 30, 8, 128, 1024, 0, 64) == 0       # Hq % Hkv
+    assert f(torch.bfloat16, 4, 8, 32, 8, 96, 1024, 0, 64) == 0        # D
+    assert f(torch.bfloat16, 4, 8, 32, 8, 128, 1024, 0, 48) == 0       # page size
+    assert f(torch.float32, 0, 8, 32, 8, 128, 0, 0, 16) > 0            # empty batch is fine
+
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                            reason="placeholder pointers: run where no GPU is visible")
+FAKE = 1 << 40  # 256-byte aligned placeholder, never dereferenced
+
+
+def attn_call(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=tav.TAV_BF16, sp=8 * 64 * 128, sh=64 * 128, st=128,
+             num_pages=100, pt=FAKE, max_pages=20, ps=64, plen=FAKE, maxp=1000, pw=0, masks=FAKE,
+             W=64, B=2, R=64, Hq=32, Hkv=8, D=128, scale=0.0, out=FAKE, lse=FAKE, ws=FAKE,
+             wsb=1 << 30)
+    a.update(kw)
+    st = L.tree_attention(a["q"], a["k"], a["v"], a["dtype"], a["sp"], a["sh"], a["st"],
+                          a["num_pages"], a["pt"], a["max_pages"], a["ps"], a["plen"], a["maxp"],
+                          a["pw"], a["masks"], a["W"], a["B"], a["R"], a["Hq"], a["Hkv"], a["D"],
+                          a["scale"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+    return st, L.tav_last_error().decode()
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status,words", [
+    (dict(R=65), 1, ["R must be in [1, 64]"]),
+    (dict(W=65), 1, ["W must be in [0, 64]"]),
+    (dict(Hq=30), 1, ["multiple of Hkv"]),
+    (dict(D=96), 2, ["D must be 64 or 128"]),
+    (dict(ps=48), 2, ["page_size"]),
+    (dict(dtype=7), 2, ["dtype"]),
+    (dict(max_pages=16), 1, ["must cover max_prefix_len + W"]),
+    (dict(wsb=1024), 3, ["workspace has 1024 bytes"]),
+    (dict(ws=FAKE + 16), 3, ["256-byte aligned"]),
+    (dict(q=None), 1, ["q, k_cache and v_cache must be set"]),
+    (dict(masks=None), 1, ["masks is NULL"]),
+    (dict(st=100), 2, ["multiples of 16 bytes"]),
+    (dict(scale=float("nan")), 1, ["sm_scale must be finite"]),
+    (dict(B=-1), 1, ["B must be >= 0"]),
+])
+def test_tree_attention_rejects(L, kw, status, words):
+    st, msg = attn_call(L, **kw)
+    assert st == status, msg
+    for w in words:
+        assert w in msg, msg
+
+
+@no_gpu
+def test_tree_attention_reports_every_blocker(L):
+    st, msg = attn_call(L, R=65, D=96, ps=48, W=70)
+    assert st != 0
+    for w in ("R must be", "D must be", "page_size", "W must be"):
+        assert w in msg, msg
+
+
+@no_gpu
+def test_small_entry_points_reject(L):
+    assert L.tree_build_masks(FAKE, 2, 65, None, FAKE, FAKE, None, None, None) == 1
+    assert "N must be in [1, 64]" in L.tav_last_error().decode()
+    assert L.tree_build_masks(None, 2, 8, None, FAKE, FAKE, None, None, None) == 1
+    assert "parents is NULL" in L.tav_last_error().decode()
+    assert L.tree_shift_positions(FAKE, FAKE, 2, 8, 0, None) == 1
+    assert "direction" in L.tav_last_error().decode()
+    assert L.verify_tree_greedy(FAKE, FAKE, FAKE, 2, 0, FAKE, FAKE, None, None) == 1
+    assert L.verify_tree_greedy(FAKE, None, FAKE, 2, 8, FAKE, FAKE, None, None) == 1
+    assert "target_argmax is NULL" in L.tav_last_error().decode()
+    t = (tav.TavRows * 1)()
+    t[0] = tav.TavRows(FAKE, None, None, 0, 1, 0, 0, 64, 0, 0, 1, 6)   # row_bytes % 4 != 0
+    assert L.compact_window_rows(t, 1, FAKE, FAKE, 2, 8, None) == 1
+    assert "row_bytes" in L.tav_last_error().decode()
+    t[0] = tav.TavRows(FAKE, FAKE, None, 4, 16, 10, 0, 64, 0, 0, 1, 64)  # paged, no prefix_len
+    assert L.compact_window_rows(t, 1, FAKE, FAKE, 2, 8, None) == 1
+    assert "prefix_len is NULL" in L.tav_last_error().decode()
+
+
+def test_empty_batch_is_a_no_op(L):
+    # B = 0 launches nothing and succeeds (no pointer is touched)
+    assert L.tree_build_masks(None, 0, 8, None, None, None, None, None, None) == 0
+    assert L.verify_tree_greedy(None, None, None, 0, 8, None, None, None, None) == 0
+    assert L.tree_shift_positions(None, None, 0, 8, 1, None) == 0
+    st, msg = attn_call(L, B=0, q=None, k=None, v=None, pt=None, plen=None, masks=None,
+                        out=None, lse=None, ws=None)
+    assert st == 0, msg
+    assert L.compact_window_rows(None, 0, None, None, 0, 8, None) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    with pytest.raises(ValueError):
+        tav.tree_build_masks(torch.zeros((1, 4), dtype=torch.int32))

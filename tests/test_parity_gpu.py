@@ -1,0 +1,333 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU fp64 oracle.
+
+Bars: masks, depth, positions, tree errors, accepted paths, accept lengths,
+accepted tokens and compaction bit-exact; attention out max |err| <= 1e-2 and
+lse2 max |err| <= 1e-3 against the fp64 oracle on the same bf16-rounded (or
+fp32) inputs.  Reduced sizes are checked element by element over every row;
+the full workload sizes, in the launch configuration the benchmark times, are
+checked on sampled rows plus whole-output properties (finite everywhere).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_attention_verify_amd as tav
+from tree_attention_verify_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+LSE_TOL = 1e-3
+
+
+def say(*a):
+    print("[parity]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tav.lib()  # loud failure if the HIP library is missing
+
+
+def dev(x, dtype=torch.int32):
+    return torch.as_tensor(np.ascontiguousarray(x)).to(dtype).cuda()
+
+
+def masks_np(t):
+    return t.cpu().numpy().view(np.uint64)
+
+
+def gpu_masks(inp):
+    r = tav.tree_build_masks(dev(inp.parents), vc=dev(inp.prefix_len))
+    torch.cuda.synchronize()
+    return r
+
+
+def run_attention(inp, masks_dev, prefix_window=None):
+    wl = inp.wl
+    pw = wl.prefix_window if prefix_window is None else prefix_window
+    out, lse = tav.tree_attention(inp.q, inp.k_cache, inp.v_cache, dev(inp.page_table),
+                                  dev(inp.prefix_len), masks_dev, wl.W,
+                                  max_prefix_len=int(inp.prefix_len.max()), layout=inp.layout,
+                                  prefix_window=pw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def oracle_attention(inp, masks, rows=None, prefix_window=None):
+    wl = inp.wl
+    pw = wl.prefix_window if prefix_window is None else prefix_window
+    return oracle.tree_attention(gen.bf16_bits(inp.q), gen.bf16_bits(inp.k_cache),
+                                 gen.bf16_bits(inp.v_cache), inp.strides, inp.page_table,
+                                 wl.page_size, inp.prefix_len, masks, wl.W, wl.Hkv,
+                                 prefix_window=pw, rows=rows)
+
+
+def check_attention(out, lse, ref_o, ref_l, rows=None, tag=""):
+    o = out.float().cpu().numpy().reshape(-1, out.shape[-1])
+    l = lse.cpu().numpy().reshape(-1)
+    if rows is not None:
+        o, l = o[rows], l[rows]
+    ref_o = ref_o.reshape(o.shape)
+    ref_l = ref_l.reshape(l.shape)
+    assert np.isfinite(o).all(), tag + ": non-finite output"
+    err = float(np.abs(o - ref_o).max())
+    both_inf = np.isneginf(l) & np.isneginf(ref_l)
+    lerr = float(np.abs(np.where(both_inf, 0.0, l - ref_l)).max())
+    say(tag, "max|out err| = %.2e  max|lse2 err| = %.2e" % (err, lerr))
+    assert err <= OUT_TOL, tag
+    assert lerr <= LSE_TOL, tag
+
+
+# ---------------------------------------------------------------------------
+# reduced-size cases: several tiles, ragged tails, every row checked
+# ---------------------------------------------------------------------------
+
+W_ = gen.WORKLOADS
+SMALL = {
+    "worked": (W_["worked"], None),
+    "random16": (W_["random16"].with_(B=3, P=1000), [1000, 37, 513]),
+    "eagle64": (W_["eagle64"].with_(B=2, P=700), [700, 333]),
+    "long64": (W_["long64"].with_(B=2, P=3000), [3000, 2049]),
+    "lanes": (W_["lanes"].with_(B=4, P=5000, prefix_window=1000), [5000, 999, 1000, 4500]),
+    "chain8": (W_["chain8"].with_(B=4, P=2000), [2000, 1, 64, 1999]),
+    "rows128": (W_["random16"].with_(name="rows128", B=2, P=900, N=32), [900, 700]),
+    "d64_bf16": (W_["random16"].with_(name="d64", B=2, P=777, N=16, Hq=8, Hkv=2, D=64),
+                 [777, 100]),
+    "f32_d128": (W_["worked"].with_(name="f32", B=2, P=300, N=8, Hq=8, Hkv=4, D=128,
+                                    tree="random", depth_cap=4), [300, 17]),
+}
+
+
+@pytest.fixture(scope="module", params=sorted(SMALL))
+def small(request):
+    name = request.param
+    wl, pl = SMALL[name]
+    say("case", name, wl)
+    inp = gen.make_inputs(wl, 11, "cuda", prefix_lens=pl)
+    return name, inp
+
+
+def test_masks_bit_exact(small):
+    name, inp = small
+    if inp.wl.tree == "lanes":
+        pytest.skip("lane masks are drafter inputs")
+    g = gpu_masks(inp)
+    r = oracle.build_masks(inp.parents, vc=inp.prefix_len)
+    assert np.array_equal(masks_np(g["masks"]), r["masks"])
+    assert np.array_equal(g["depth"].cpu().numpy(), r["depth"])
+    assert np.array_equal(g["positions"].cpu().numpy(), r["positions"])
+    assert np.array_equal(g["tree_error"].cpu().numpy(), r["tree_error"])
+
+
+def test_greedy_bit_exact(small):
+    name, inp = small
+    if inp.wl.tree == "lanes":
+        pytest.skip("no verify for draft lanes")
+    g = tav.verify_tree_greedy(dev(inp.draft), dev(inp.target), dev(inp.parents))
+    r = oracle.verify_greedy(inp.draft, inp.target, inp.parents)
+    for k in ("accepted_path", "accept_len", "accepted_tokens"):
+        assert np.array_equal(g[k].cpu().numpy(), r[k]), k
+
+
+def test_attention_parity(small):
+    name, inp = small
+    if inp.wl.tree == "lanes":
+        m_np = inp.lane_masks
+        m_dev = dev(m_np.view(np.int64), torch.int64)
+    else:
+        g = gpu_masks(inp)
+        m_dev = g["masks"]
+        m_np = oracle.build_masks(inp.parents)["masks"]
+    out, lse = run_attention(inp, m_dev)
+    ro, rl = oracle_attention(inp, m_np)
+    check_attention(out, lse, ro, rl, tag=name)
+
+
+def test_compaction_bit_exact(small):
+    name, inp = small
+    if inp.wl.tree == "lanes":
+        pytest.skip("no verify for draft lanes")
+    wl = inp.wl
+    g = tav.verify_tree_greedy(dev(inp.draft), dev(inp.target), dev(inp.parents))
+    r = oracle.verify_greedy(inp.draft, inp.target, inp.parents)
+    hidden = torch.randint(-2**31, 2**31 - 1, (wl.B, wl.N, 72), dtype=torch.int32,
+                           device="cuda")
+    kc, vc, hc = (inp.k_cache.cpu().clone(), inp.v_cache.cpu().clone(), hidden.cpu().clone())
+    pt = dev(inp.page_table)
+    pl = dev(inp.prefix_len)
+    tables = [tav.RowTable.paged_kv(inp.k_cache, pt, pl, inp.layout),
+              tav.RowTable.paged_kv(inp.v_cache, pt, pl, inp.layout),
+              tav.RowTable.dense_rows(hidden)]
+    tav.compact_window_rows(tables, g["accepted_path"], g["accept_len"])
+    torch.cuda.synchronize()
+    host_tables = []
+    for t, buf in zip(tables, (kc, vc, hc)):
+        nb = buf.view(torch.uint8).numpy() if buf.dtype != torch.bfloat16 else \
+            buf.view(torch.int16).numpy().view(np.uint8)
+        host_tables.append(dict(buf=nb, page_table=None if t.page_table is None else inp.page_table,
+                                prefix_len=None if t.page_table is None else inp.prefix_len,
+                                page_size=t.page_size, stride_page=t.stride_page,
+                                stride_token=t.stride_token, stride_head=t.stride_head,
+                                stride_batch=t.stride_batch, n_heads=t.n_heads,
+                                row_bytes=t.row_bytes))
+    oracle.compact_rows(host_tables, r["accepted_path"], r["accept_len"])
+    for t, h in zip(tables, host_tables):
+        got = t.buf.cpu().contiguous()
+        got = got.view(torch.int16).numpy().view(np.uint8) if got.dtype == torch.bfloat16 \
+            else got.view(torch.uint8).numpy()
+        assert np.array_equal(got, h["buf"]), "compaction differs"
+
+
+def test_shift_bit_exact(small):
+    name, inp = small
+    if inp.wl.tree == "lanes":
+        pytest.skip("no positions for draft lanes")
+    g = gpu_masks(inp)
+    depth = g["depth"].cpu().numpy()
+    chain = inp.prefix_len[:, None] + np.arange(inp.wl.N, dtype=np.int32)[None]
+    p = dev(chain)
+    tav.tree_shift_positions(p, g["depth"], +1)
+    torch.cuda.synchronize()
+    up = oracle.shift_positions(chain, depth, +1)
+    assert np.array_equal(p.cpu().numpy(), up)
+    assert np.array_equal(up, g["positions"].cpu().numpy())
+    tav.tree_shift_positions(p, g["depth"], -1)
+    torch.cuda.synchronize()
+    assert np.array_equal(p.cpu().numpy(), chain)
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_short_and_empty_prefixes(dtype):
+    pl = [0, 1, 15, 16, 17, 63, 64, 65]
+    wl = gen.Workload("edge", len(pl), 65, 8, 8, 2, 128, dtype, 16, "random", depth_cap=3)
+    inp = gen.make_inputs(wl, 3, "cuda", prefix_lens=pl)
+    g = gpu_masks(inp)
+    out, lse = run_attention(inp, g["masks"])
+    ro, rl = oracle_attention(inp, oracle.build_masks(inp.parents)["masks"])
+    check_attention(out, lse, ro, rl, tag="short-prefix-" + dtype)
+
+
+def test_nhd_layout_and_high_mask_bits():
+    wl = gen.Workload("nhd", 2, 300, 12, 16, 4, 128, "bf16", 16, "random", depth_cap=5)
+    inp = gen.make_inputs(wl, 4, "cuda", layout="NHD", prefix_lens=[300, 123])
+    m = oracle.build_masks(inp.parents)["masks"]
+    noisy = m | (np.uint64(0xFFFF) << np.uint64(48))        # bits >= W must be ignored
+    out, lse = run_attention(inp, dev(noisy.view(np.int64), torch.int64))
+    ro, rl = oracle_attention(inp, m)
+    check_attention(out, lse, ro, rl, tag="NHD")
+
+
+def test_nan_in_node_leaks_only_to_descendants():
+    wl = gen.Workload("nan", 1, 200, 16, 8, 2, 128, "bf16", 16, "random", depth_cap=4)
+    inp = gen.make_inputs(wl, 5, "cuda")
+    j = 6
+    t = int(inp.prefix_len[0]) + j
+    pg = int(inp.page_table[0, t // wl.page_size])
+    inp.k_cache[pg, 0, t % wl.page_size] = float("nan")
+    m = oracle.build_masks(inp.parents)["masks"]
+    out, lse = run_attention(inp, dev(m.view(np.int64), torch.int64))
+    ro, rl = oracle_attention(inp, m)
+    o = out.float().cpu().numpy()
+    G = wl.Hq // wl.Hkv
+    for r in range(wl.R):
+        sees = (int(m[0, r]) >> j) & 1
+        for h in range(wl.Hq):
+            if sees and h // G == 0:
+                assert not np.isfinite(o[0, r, h]).all()
+            else:
+                assert np.isfinite(o[0, r, h]).all()
+                assert np.abs(o[0, r, h] - ro[0, r, h]).max() <= OUT_TOL
+
+
+def test_bad_trees_flagged():
+    par = np.array([[-1, 0, 0, 1, 2, 3, 4, 5],
+                    [-1, 0, 5, 1, 2, 3, 4, 5],      # forward reference at node 2
+                    [0, 0, 1, 2, 3, 4, 5, 6],       # no root
+                    [-1, 0, 1, 2, -1, 4, 5, 6]], np.int32)  # second root at node 4
+    vc = np.array([10, 20, 30, 40], np.int32)
+    g = tav.tree_build_masks(dev(par), vc=dev(vc))
+    torch.cuda.synchronize()
+    r = oracle.build_masks(par, vc=vc)
+    assert r["tree_error"].tolist() == [0, 3, 1, 5]
+    assert np.array_equal(g["tree_error"].cpu().numpy(), r["tree_error"])
+    assert np.array_equal(masks_np(g["masks"]), r["masks"])
+    assert np.array_equal(g["depth"].cpu().numpy(), r["depth"])
+    assert np.array_equal(g["positions"].cpu().numpy(), r["positions"])
+
+
+def test_greedy_ties_and_width():
+    rng = np.random.default_rng(0)
+    B, N = 64, 64
+    par = np.stack([gen.random_tree(rng, N, int(rng.integers(1, 12))) for _ in range(B)])
+    draft = rng.integers(0, 3, (B, N)).astype(np.int32)    # many equal sibling tokens
+    target = rng.integers(0, 3, (B, N)).astype(np.int32)
+    g = tav.verify_tree_greedy(dev(draft), dev(target), dev(par))
+    r = oracle.verify_greedy(draft, target, par)
+    for k in ("accepted_path", "accept_len", "accepted_tokens"):
+        assert np.array_equal(g[k].cpu().numpy(), r[k]), k
+    for n in (1, 2, 63):
+        g = tav.verify_tree_greedy(dev(draft[:, :n]), dev(target[:, :n]), dev(par[:, :n]))
+        r = oracle.verify_greedy(draft[:, :n], target[:, :n], par[:, :n])
+        assert np.array_equal(g["accepted_path"].cpu().numpy(), r["accepted_path"])
+
+
+def test_chain_equals_causal():
+    wl = W_["chain8"].with_(B=2, P=500)
+    inp = gen.make_inputs(wl, 6, "cuda")
+    g = gpu_masks(inp)
+    out, lse = run_attention(inp, g["masks"])
+    for b in range(wl.B):
+        L = wl.P + wl.N
+        pt = inp.page_table[b]
+        kk = inp.k_cache[torch.as_tensor(pt.astype(np.int64)).cuda()]   # [pages][Hkv][ps][D]
+        vv = inp.v_cache[torch.as_tensor(pt.astype(np.int64)).cuda()]
+        kk = kk.permute(0, 2, 1, 3).reshape(-1, wl.Hkv, wl.D)[:L]
+        vv = vv.permute(0, 2, 1, 3).reshape(-1, wl.Hkv, wl.D)[:L]
+        co, cl = oracle.causal_attention(gen.bf16_bits(inp.q[b]), gen.bf16_bits(kk),
+                                         gen.bf16_bits(vv))
+        check_attention(out[b:b + 1], lse[b:b + 1], co, cl, tag="chain-vs-causal")
+
+
+# ---------------------------------------------------------------------------
+# full workload sizes, sampled rows
+# ---------------------------------------------------------------------------
+
+FULL = ["random16", "eagle64", "long64", "lanes", "chain8"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    wl = W_[name]
+    say("full", name, wl)
+    inp = gen.make_inputs(wl, 1000 + FULL.index(name), "cuda")
+    if wl.tree == "lanes":
+        m_np = inp.lane_masks
+        m_dev = dev(m_np.view(np.int64), torch.int64)
+    else:
+        g = gpu_masks(inp)
+        r = oracle.build_masks(inp.parents, vc=inp.prefix_len)
+        assert np.array_equal(masks_np(g["masks"]), r["masks"])
+        assert np.array_equal(g["positions"].cpu().numpy(), r["positions"])
+        m_dev, m_np = g["masks"], r["masks"]
+        gv = tav.verify_tree_greedy(dev(inp.draft), dev(inp.target), dev(inp.parents))
+        rv = oracle.verify_greedy(inp.draft, inp.target, inp.parents)
+        for k in ("accepted_path", "accept_len", "accepted_tokens"):
+            assert np.array_equal(gv[k].cpu().numpy(), rv[k]), k
+    out, lse = run_attention(inp, m_dev)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    n_rows = wl.B * wl.R * wl.Hq
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, n_rows - 1], rng.integers(0, n_rows, 40)]))
+    ro, rl = oracle_attention(inp, m_np, rows=rows)
+    check_attention(out, lse, ro, rl, rows=rows, tag="full-" + name)

@@ -1,1 +1,295 @@
-"""MI355X-native draft-tree verify path (HIP kernels behind a C ABI)."""
+"""MI355X (gfx950) draft-tree verify path: HIP kernels behind a C ABI.
+
+This module is the thin Python binding of ``libtreeverify.so`` (see
+``include/treeverify.h`` for the contract of every call).  It only checks
+torch tensors and marshals pointers, sizes and the current HIP stream; every
+step of the path runs in the library's kernels.  The library must be built
+(``python -m tree_attention_verify_amd.build``); nothing here falls back to
+another implementation.
+
+Entry points (same names as the C ABI):
+  tree_build_masks, tree_shift_positions, tree_attention,
+  tree_attention_workspace_size, verify_tree_greedy, compact_window_rows
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtreeverify.so")
+
+TAV_F32, TAV_BF16 = 0, 1
+_STATUS = {0: "TAV_OK", 1: "TAV_ERR_INVALID_ARG", 2: "TAV_ERR_UNSUPPORTED",
+           3: "TAV_ERR_WORKSPACE", 4: "TAV_ERR_HIP"}
+
+# Every function the header declares.
+EXPORTS = ("tav_last_error", "tav_version", "tree_build_masks", "tree_shift_positions",
+           "tree_attention_workspace_size", "tree_attention", "tree_attention_prefix",
+           "tree_attention_window_merge", "verify_tree_greedy", "compact_window_rows")
+
+
+class TavError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s: %s" % (_STATUS.get(status, status), msg))
+        self.status = status
+
+
+class TavRows(ctypes.Structure):
+    """Mirror of the C tav_rows descriptor."""
+    _fields_ = [
+        ("base", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("prefix_len", ctypes.c_void_p),
+        ("max_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("stride_page", ctypes.c_int64),
+        ("stride_token", ctypes.c_int64),
+        ("stride_head", ctypes.c_int64),
+        ("stride_batch", ctypes.c_int64),
+        ("n_heads", ctypes.c_int32),
+        ("row_bytes", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libtreeverify.so is not built: run "
+                               "`python -m tree_attention_verify_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.tav_last_error.restype = ctypes.c_char_p
+        L.tav_last_error.argtypes = []
+        L.tav_version.restype = ctypes.c_char_p
+        L.tav_version.argtypes = []
+        L.tree_build_masks.argtypes = [P, I32, I32, P, P, P, P, P, P]
+        L.tree_shift_positions.argtypes = [P, P, I32, I32, I32, P]
+        L.tree_attention_workspace_size.argtypes = [ctypes.c_int, I32, I32, I32, I32, I32, I32,
+                                                    I32, I32]
+        L.tree_attention_workspace_size.restype = ctypes.c_size_t
+        attn = [P, P, P, ctypes.c_int, I64, I64, I64, I64, P, I32, I32, P, I32, I32, P, I32, I32,
+                I32, I32, I32, I32, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
+        for f in ("tree_attention", "tree_attention_prefix", "tree_attention_window_merge"):
+            getattr(L, f).argtypes = attn
+            getattr(L, f).restype = ctypes.c_int
+        L.verify_tree_greedy.argtypes = [P, P, P, I32, I32, P, P, P, P]
+        L.compact_window_rows.argtypes = [ctypes.POINTER(TavRows), I32, P, P, I32, I32, P]
+        for f in ("tree_build_masks", "tree_shift_positions", "tree_attention",
+                  "verify_tree_greedy", "compact_window_rows"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise TavError(status, lib().tav_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, device=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be on a GPU device" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def tree_build_masks(parents: torch.Tensor, vc: Optional[torch.Tensor] = None,
+                     positions: bool = True):
+    """parents int32 [B][N] -> dict(depth int32, masks int64 (uint64 bits),
+    positions int32 or None, tree_error int32 [B])."""
+    _need(parents, "parents", torch.int32)
+    B, N = parents.shape
+    dev = parents.device
+    depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    masks = torch.empty((B, N), dtype=torch.int64, device=dev)
+    err = torch.empty((B,), dtype=torch.int32, device=dev)
+    pos = torch.empty((B, N), dtype=torch.int32, device=dev) if positions else None
+    if vc is not None:
+        _need(vc, "vc", torch.int32, dev, (B,))
+    _check(lib().tree_build_masks(_ptr(parents), B, N, _ptr(vc), _ptr(depth), _ptr(masks),
+                                  _ptr(pos), _ptr(err), _stream(dev)))
+    return {"depth": depth, "masks": masks, "positions": pos, "tree_error": err}
+
+
+def tree_shift_positions(positions: torch.Tensor, depth: torch.Tensor, direction: int):
+    """In place: positions += direction * (depth - i)."""
+    _need(positions, "positions", torch.int32)
+    B, N = positions.shape
+    _need(depth, "depth", torch.int32, positions.device, (B, N))
+    _check(lib().tree_shift_positions(_ptr(positions), _ptr(depth), B, N, int(direction),
+                                      _stream(positions.device)))
+    return positions
+
+
+def tree_attention_workspace_size(dtype, B, R, Hq, Hkv, D, max_prefix_len, prefix_window,
+                                  page_size) -> int:
+    code = TAV_BF16 if dtype == torch.bfloat16 else TAV_F32
+    return int(lib().tree_attention_workspace_size(code, B, R, Hq, Hkv, D, max_prefix_len,
+                                                   prefix_window, page_size))
+
+
+def kv_strides(cache: torch.Tensor, layout: str):
+    """(page, head, token) element strides of a 4-D paged cache."""
+    if cache.dim() != 4 or cache.stride(3) != 1:
+        raise ValueError("K/V caches must be 4-D with contiguous channels")
+    if layout == "HND":      # [pages][Hkv][page_size][D]
+        return cache.stride(0), cache.stride(1), cache.stride(2), cache.shape[1], cache.shape[2]
+    if layout == "NHD":      # [pages][page_size][Hkv][D]
+        return cache.stride(0), cache.stride(2), cache.stride(1), cache.shape[2], cache.shape[1]
+    raise ValueError("layout must be 'HND' or 'NHD'")
+
+
+def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   page_table: torch.Tensor, prefix_len: torch.Tensor, masks: torch.Tensor,
+                   W: int, *, max_prefix_len: int, layout: str = "HND", prefix_window: int = 0,
+                   sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                   lse2: Optional[torch.Tensor] = None, return_lse: bool = True,
+                   workspace: Optional[torch.Tensor] = None, phase: str = "all"):
+    """Tree attention (see include/treeverify.h).  q [B][R][Hq][D] fp32/bf16;
+    k_cache/v_cache paged pools in `layout`; page_table int32 [B][max_pages];
+    prefix_len int32 [B]; masks int64 [B][R] (uint64 bit patterns).
+    phase: "all" (tree_attention), "prefix" (tree_attention_prefix) or
+    "window_merge" (tree_attention_window_merge; pass the workspace the
+    prefix phase filled).
+    Returns (out [B][R][Hq][D], lse2 float32 [B][R][Hq] or None)."""
+    fn = {"all": "tree_attention", "prefix": "tree_attention_prefix",
+          "window_merge": "tree_attention_window_merge"}[phase]
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("q must be float32 or bfloat16")
+    _need(q, "q", q.dtype)
+    dev = q.device
+    B, R, Hq, D = q.shape
+    _need(k_cache, "k_cache", q.dtype, dev)
+    _need(v_cache, "v_cache", q.dtype, dev)
+    sp, sh, st, Hkv, ps = kv_strides(k_cache, layout)
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("v_cache must have k_cache's shape")
+    _need(page_table, "page_table", torch.int32, dev)
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [B][max_pages]")
+    _need(prefix_len, "prefix_len", torch.int32, dev, (B,))
+    _need(masks, "masks", torch.int64, dev, (B, R))
+    dt = TAV_BF16 if q.dtype == torch.bfloat16 else TAV_F32
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", q.dtype, dev, q.shape)
+    if lse2 is None and return_lse:
+        lse2 = torch.empty((B, R, Hq), dtype=torch.float32, device=dev)
+    elif lse2 is not None:
+        _need(lse2, "lse2", torch.float32, dev, (B, R, Hq))
+    need = lib().tree_attention_workspace_size(dt, B, R, Hq, Hkv, D, max_prefix_len,
+                                               prefix_window, ps)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", torch.uint8, dev)
+    _check(getattr(lib(), fn)(_ptr(q), _ptr(k_cache), _ptr(v_cache), dt, sp, sh, st,
+                                k_cache.shape[0], _ptr(page_table), page_table.shape[1], ps,
+                                _ptr(prefix_len), int(max_prefix_len), int(prefix_window),
+                                _ptr(masks), int(W), B, R, Hq, Hkv, D, float(sm_scale),
+                                _ptr(out), _ptr(lse2), _ptr(workspace), workspace.numel(),
+                                _stream(dev)))
+    return out, lse2
+
+
+def verify_tree_greedy(draft_tokens: torch.Tensor, target_argmax: torch.Tensor,
+                       parents: torch.Tensor, tokens: bool = True):
+    """-> dict(accepted_path int32 [B][N], accept_len int32 [B],
+    accepted_tokens int32 [B][N] or None)."""
+    _need(parents, "parents", torch.int32)
+    B, N = parents.shape
+    dev = parents.device
+    _need(draft_tokens, "draft_tokens", torch.int32, dev, (B, N))
+    _need(target_argmax, "target_argmax", torch.int32, dev, (B, N))
+    path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    tok = torch.empty((B, N), dtype=torch.int32, device=dev) if tokens else None
+    _check(lib().verify_tree_greedy(_ptr(draft_tokens), _ptr(target_argmax), _ptr(parents), B, N,
+                                    _ptr(path), _ptr(alen), _ptr(tok), _stream(dev)))
+    return {"accepted_path": path, "accept_len": alen, "accepted_tokens": tok}
+
+
+@dataclasses.dataclass
+class RowTable:
+    """One buffer for compact_window_rows (byte strides; see tav_rows)."""
+    buf: torch.Tensor
+    row_bytes: int
+    stride_token: int
+    n_heads: int = 1
+    stride_head: int = 0
+    stride_batch: int = 0
+    page_table: Optional[torch.Tensor] = None
+    prefix_len: Optional[torch.Tensor] = None
+    page_size: int = 1
+    stride_page: int = 0
+    num_pages: int = 0
+
+    @staticmethod
+    def paged_kv(cache: torch.Tensor, page_table: torch.Tensor, prefix_len: torch.Tensor,
+                 layout: str = "HND") -> "RowTable":
+        sp, sh, st, Hkv, ps = kv_strides(cache, layout)
+        e = cache.element_size()
+        return RowTable(buf=cache, row_bytes=cache.shape[3] * e, stride_token=st * e,
+                        n_heads=Hkv, stride_head=sh * e, page_table=page_table,
+                        prefix_len=prefix_len, page_size=ps, stride_page=sp * e,
+                        num_pages=cache.shape[0])
+
+    @staticmethod
+    def dense_rows(rows: torch.Tensor) -> "RowTable":
+        """rows [B][N][...]: one row of prod(...) elements per window slot."""
+        e = rows.element_size()
+        per = rows[0, 0].numel() * e
+        return RowTable(buf=rows, row_bytes=per, stride_token=rows.stride(1) * e,
+                        stride_batch=rows.stride(0) * e)
+
+
+def compact_window_rows(tables: Sequence[RowTable], accepted_path: torch.Tensor,
+                        accept_len: torch.Tensor):
+    """Moves each request's accepted rows to the window's leading slots, in
+    place, in every table."""
+    _need(accepted_path, "accepted_path", torch.int32)
+    B, N = accepted_path.shape
+    dev = accepted_path.device
+    _need(accept_len, "accept_len", torch.int32, dev, (B,))
+    arr = (TavRows * max(1, len(tables)))()
+    for i, t in enumerate(tables):
+        if not t.buf.is_cuda or t.buf.device != dev:
+            raise ValueError("table %d buffer must be on %s" % (i, dev))
+        if t.page_table is not None:
+            _need(t.page_table, "page_table", torch.int32, dev)
+            _need(t.prefix_len, "prefix_len", torch.int32, dev, (B,))
+        arr[i] = TavRows(t.buf.data_ptr(), _ptr(t.page_table), _ptr(t.prefix_len),
+                         0 if t.page_table is None else t.page_table.shape[1], int(t.page_size),
+                         int(t.num_pages), int(t.stride_page), int(t.stride_token),
+                         int(t.stride_head), int(t.stride_batch), int(t.n_heads),
+                         int(t.row_bytes))
+    _check(lib().compact_window_rows(arr, len(tables), _ptr(accepted_path), _ptr(accept_len), B,
+                                     N, _stream(dev)))

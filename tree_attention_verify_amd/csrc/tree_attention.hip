@@ -1,0 +1,971 @@
+// tree_attention: split-K paged prefix decode + masked tree window + base-2
+// LSE merge, for gfx950 (CDNA4).
+//
+// The cascade follows "Draft-tree speculation", section "One tree attention:
+// the leaf's decode for the prefix, a small kernel for the tree" (every row
+// sees the committed prefix; the 64-bit ancestor mask applies only to the
+// last W keys; the two parts are merged through their base-2 log-sum-exp)
+// and the FlashAttention cascade of "EAGLE Tree Attention candidate layout,
+// positions and visibility", section 4 (common prefix for all queries, a
+// per-query ancestor suffix, and the merge O = sum Z_k O_k / sum Z_k).
+//
+// Kernels:
+//   k_prefix_mfma<D, NT, NKS>  bf16.  One workgroup (4 waves) per (request,
+//       kv head, row group, split).  All R x (Hq/Hkv) query rows of a kv head
+//       are folded into the MFMA N dimension, so one pass over a K/V page
+//       serves every row and head of the group.  Pages stream HBM -> LDS with
+//       direct-to-LDS 16-byte loads, NBUF stages deep; S^T = K Q^T and
+//       O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation;
+//       softmax is online in the exp2 domain.  Writes one (O, lse2) partial
+//       per split and key subset.
+//   k_prefix_f32<D>  fp32 inputs, vector ALU, one wave per (row, split).
+//   k_window_merge   one wave per (request, row, head): the masked window
+//       keys (popcount(mask) of them, never the unseen ones) and the merge of
+//       every prefix partial with the window part into out / lse2.
+#include <cmath>
+#include <type_traits>
+#include <utility>
+
+#include "tav_internal.h"
+
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kPtMax = 2048;        // page-table entries one split may span
+constexpr int kLdsStageBudget = 128 * 1024;
+
+__device__ inline float bf16_bits_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
+__device__ inline uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        x += __shfl_xor(x, o);
+    return x;
+}
+
+__device__ inline float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+
+// A softmax part with denominator l has keys unless l == 0.  A NaN l (a NaN
+// score or value among visible keys) is kept, so it reaches the output as the
+// definition's arithmetic would carry it; only l == 0 means "no key".
+__device__ inline bool has_keys(float l) { return !(l == 0.f); }
+
+// exp2 with exp2(-inf) = 0 (the hardware instruction handles it).
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Direct-to-LDS 16-byte load (global_load_lds_dwordx4): lane i's 16 bytes at
+// `src` land at LDS byte address lds_base + 16 i.  It is issued as inline
+// assembly so that the compiler does not track it as an LDS write: otherwise
+// its wait insertion makes LDS reads it cannot attribute to one buffer wait
+// for every such load in flight (vmcnt(0)), which would serialise the stage
+// pipeline.  Completion is established explicitly: wait_vmcnt<N>() for the
+// issuing wave, then a workgroup barrier.  lds_base must be wave-uniform.
+__device__ __forceinline__ void dma_load16(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_off(const void *p) {
+    return (uint32_t)(uintptr_t)(const LDS_AS void *)p;
+}
+
+// Combine lane l with lane l ^ 32 on the vector ALU (v_permlane32_swap):
+// after swapping a copy, one result holds the lower-half value of the pair and
+// the other the upper-half value.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(std::forward<F>(f));
+    }
+}
+
+// s_waitcnt vmcnt(N) without waiting on LGKM / EXP counters (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14).
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+struct PrefixArgs {
+    const void *q;
+    const void *k;
+    const void *v;
+    int64_t stride_page, stride_head, stride_token, num_pages;
+    const int32_t *page_table;
+    int32_t max_pages, ps_shift;
+    const int32_t *prefix_len;
+    int32_t max_prefix_len, prefix_window;
+    int32_t B, R, Hq, Hkv, G, M, RG, n_split, kps, S;
+    float c;  // sm_scale * log2(e): scores in the exp2 domain
+    float *ws_o;
+    float *ws_lse;
+};
+
+// Visible prefix range [lo, hi) of split `split` of request b.
+struct KeyRange {
+    int lo, hi;
+};
+__device__ inline KeyRange split_range(const PrefixArgs &a, int b, int split) {
+    int P = a.prefix_len[b];
+    P = P < 0 ? 0 : (P > a.max_prefix_len ? a.max_prefix_len : P);
+    const int p_lo = (a.prefix_window > 0 && P > a.prefix_window) ? P - a.prefix_window : 0;
+    const int lo = p_lo + split * a.kps;
+    int hi = lo + a.kps;
+    hi = hi < P ? hi : P;
+    return {lo, hi < lo ? lo : hi};
+}
+
+__device__ inline int64_t clamp_page(int64_t p, int64_t n) { return p < 0 ? 0 : (p >= n ? n - 1 : p); }
+
+// XOR swizzle of the 16-byte chunks of a key row in LDS.  It makes both LDS
+// read patterns conflict-free: the K operand (lanes = 32 keys, one chunk) and
+// the transposing V reads (16-lane groups = 4 keys x 32 bytes).
+template <int D>
+__device__ inline int swz(int key) {
+    const int x = ((key & 3) << 1) | ((key >> 2) & 1);
+    return D == 128 ? (x | (key & 8)) : x;
+}
+
+template <int D, int NKS>
+struct MfmaCfg {
+    static constexpr int SK = 32 * NKS;           // keys per stage
+    static constexpr int CH = D / 8;              // 16-byte chunks per key row
+    static constexpr int ROWB = D * 2;            // bytes per key row (bf16)
+    static constexpr int SB = SK * ROWB * 2;      // stage bytes, K then V
+    static constexpr int NBUF0 = kLdsStageBudget / SB;
+    static constexpr int NBUF = NBUF0 > 8 ? 8 : NBUF0;
+    static constexpr int LPS = SB / (256 * 16);   // 16-byte loads per thread per stage
+    static_assert(NBUF >= 2, "stage too large");
+    static_assert((NBUF - 2) * LPS < 64, "vmcnt range");
+};
+
+template <int D, int NT, int NKS>
+__global__ void __launch_bounds__(256, 1) k_prefix_mfma(PrefixArgs a) {
+    using C = MfmaCfg<D, NKS>;
+    constexpr int SK = C::SK, CH = C::CH, ROWB = C::ROWB, SB = C::SB, NBUF = C::NBUF,
+                  LPS = C::LPS;
+    constexpr int NRB = 4 / NKS;                  // row blocks per workgroup
+    constexpr int ROWS_WG = NRB * NT * 32;
+    constexpr int KSTEPS = D / 16;
+    constexpr int DT = D / 32;                    // 32-wide d tiles
+
+    __shared__ __attribute__((aligned(16))) char lds[NBUF * SB];
+    __shared__ int32_t pt[kPtMax];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hl = lane >> 5;  // lane half
+    const int l32 = lane & 31;
+
+    // Work unit.  Workgroups are dispatched round-robin over the 8 XCDs; the
+    // row groups of one (request, kv head, split) read the same pages, so
+    // they are kept on one XCD (one L2) when the unit count allows it.
+    const int units = a.B * a.Hkv * a.n_split;
+    int rg, unit;
+    const int id = blockIdx.x;
+    if (a.RG > 1 && (units & 7) == 0) {
+        const int xcd = id & 7, slot = id >> 3;
+        rg = slot % a.RG;
+        unit = (slot / a.RG) * 8 + xcd;
+    } else {
+        rg = id % a.RG;
+        unit = id / a.RG;
+    }
+    const int split = unit % a.n_split;
+    const int g = (unit / a.n_split) % a.Hkv;
+    const int b = unit / (a.n_split * a.Hkv);
+
+    const KeyRange kr = split_range(a, b, split);
+    const int nkeys = kr.hi - kr.lo;
+    const int ns = (nkeys + SK - 1) / SK;
+    const int rbw = w % NRB;   // this wave's row block
+    const int ks = w / NRB;    // this wave's key subset within a stage
+    const int rows_base = rg * ROWS_WG + rbw * NT * 32;
+
+    // page-table slice of this split
+    const int lp0 = nkeys > 0 ? (kr.lo >> a.ps_shift) : 0;
+    const int npt = nkeys > 0 ? ((kr.hi - 1) >> a.ps_shift) - lp0 + 1 : 0;
+    for (int i = tid; i < npt && i < kPtMax; i += 256)
+        pt[i] = (int32_t)clamp_page(a.page_table[(int64_t)b * a.max_pages + lp0 + i], a.num_pages);
+    // zero the stage buffers once: the last, partial stage leaves rows unloaded
+    // and they must hold finite values (their softmax weight is exactly 0)
+    for (int i = tid; i < NBUF * SB / 16; i += 256)
+        reinterpret_cast<int4 *>(lds)[i] = make_int4(0, 0, 0, 0);
+
+    // Q^T operand in registers: lane (row n = l32, half hl) holds
+    // Q[row][16 kk + 8 hl .. +8] for each k step.
+    bf16x8 qv[NT][KSTEPS];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int m = rows_base + nt * 32 + l32;
+        const bool ok = m < a.M;
+        const int r = ok ? m / a.G : 0, hh = ok ? m % a.G : 0;
+        const uint16_t *qp = (const uint16_t *)a.q +
+                             (((int64_t)b * a.R + r) * a.Hq + (int64_t)g * a.G + hh) * D + 8 * hl;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            int4 v4 = ok ? *(const int4 *)(qp + 16 * kk) : make_int4(0, 0, 0, 0);
+            qv[nt][kk] = __builtin_bit_cast(bf16x8, v4);
+        }
+    }
+    __syncthreads();
+
+    const uint16_t *kbase = (const uint16_t *)a.k + (int64_t)g * a.stride_head;
+    const uint16_t *vbase = (const uint16_t *)a.v + (int64_t)g * a.stride_head;
+    const int ps_mask = (1 << a.ps_shift) - 1;
+    const uint32_t lds0 = lds_off(lds);
+
+    // Issue the direct-to-LDS loads of stage st: slot s of the stage (16
+    // bytes) holds chunk (s % CH) ^ swz(key) of key s / CH, the K slots first,
+    // then the V slots.  Keys past the split are not loaded.
+    auto issue = [&](int st) {
+        const uint32_t sbase = lds0 + (uint32_t)((st % NBUF) * SB);
+        const int key_base = kr.lo + st * SK;
+#pragma unroll
+        for (int i = 0; i < LPS; ++i) {
+            const int slot = i * 256 + w * 64 + lane;
+            const int region = (i * 256 + w * 64) / (SK * CH);   // wave-uniform
+            const int s2 = slot - region * (SK * CH);
+            const int key = s2 / CH;
+            const int c = (s2 % CH) ^ swz<D>(key);
+            const int t = key_base + key;
+            if (t < kr.hi) {
+                const int64_t page = pt[(t >> a.ps_shift) - lp0];
+                const uint16_t *src = (region ? vbase : kbase) + page * a.stride_page +
+                                      (int64_t)(t & ps_mask) * a.stride_token + c * 8;
+                dma_load16(src, __builtin_amdgcn_readfirstlane(sbase + (i * 256 + w * 64) * 16));
+            }
+        }
+    };
+
+    f32x16 o[NT][DT];
+    float m_run[NT], l_run[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        m_run[nt] = -INFINITY;
+        l_run[nt] = 0.f;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                o[nt][t][r] = 0.f;
+    }
+
+    for (int st = 0; st < NBUF - 1 && st < ns; ++st)
+        issue(st);
+
+    const int G16 = lane >> 4, a4 = lane & 3, j4 = (lane >> 2) & 3;
+    const int krow_l = l32;                      // K operand: key of this lane
+    for (int it = 0; it < ns; ++it) {
+        // Stage `it` is complete once at most the loads of the later, full
+        // stages are outstanding.  When the last (partial) stage is among the
+        // outstanding ones some of its instructions may be skipped, so wait
+        // for everything then.
+        if (it + NBUF - 2 < ns - 1)
+            wait_vmcnt<(NBUF - 2) * LPS>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();  // every wave's loads of stage it landed; stage it-1 is free
+        if (it + NBUF - 1 < ns)
+            issue(it + NBUF - 1);
+
+        const char *Kb = lds + (it % NBUF) * SB;
+        const char *Vb = Kb + SB / 2;
+        const int key0 = ks * 32;
+        const int first = kr.lo + it * SK + key0;  // absolute key of this wave's block
+        if (first >= kr.hi)
+            continue;
+        // S^T[key][row] = sum_d K[key][d] Q[row][d]
+        f32x16 s[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                s[nt][r] = 0.f;
+        const int krow = key0 + krow_l;
+        const int ksw = swz<D>(krow);
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            const bf16x8 ka = *(const bf16x8 *)(Kb + krow * ROWB + (((2 * kk + hl) ^ ksw) * 16));
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                s[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[nt][kk], s[nt], 0, 0, 0);
+        }
+        // keys past the end of the split are not visible
+        if (first + 32 > kr.hi) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = 8 * (r >> 2) + 4 * hl + (r & 3);
+                    if (first + key >= kr.hi)
+                        s[nt][r] = -INFINITY;
+                }
+        }
+        // online softmax in the exp2 domain; the running max is only raised
+        // when a block exceeds it by more than 2^8, so rescaling of O is rare
+        // and weights stay <= 256
+        bf16x8 pb[NT][2];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            float mx = s[nt][0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r)
+                mx = fmaxf(mx, s[nt][r]);
+            mx = pair_max(mx);
+            const float mb = mx * a.c;
+            if (__ballot(mb > m_run[nt] + 8.f)) {
+                const float mnew = fmaxf(m_run[nt], mb);
+                const float alpha = fast_exp2(m_run[nt] - mnew);  // 0 when m_run = -inf
+                l_run[nt] *= alpha;
+#pragma unroll
+                for (int t = 0; t < DT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        o[nt][t][r] *= alpha;
+                m_run[nt] = mnew;
+            }
+            const float mu = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
+            float ps[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                ps[r] = fast_exp2(fmaf(s[nt][r], a.c, -mu));
+                l_run[nt] += ps[r];
+            }
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    pb[nt][cc][t] = (__bf16)ps[cc * 8 + t];
+        }
+        // O^T[d][row] += sum_key V[key][d] P[row][key].  The P operand is the
+        // S accumulator as is: the key order inside each 16-key chunk is
+        // permuted identically for V (transposing LDS reads) and P, which
+        // leaves the sum unchanged.  V^T operand of d tile t, chunk cc, half
+        // hr: lane (G16, a4, j4) points at key key0 + 16 cc + 8 hr + 4 (G16/2)
+        // + j4, channels d0 .. d0 + 3; the 16-lane group's read transposes
+        // the 4 keys x 4 channels.
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            const int d0 = ((G16 & 1) ? D / 2 : 0) + 16 * t + 4 * a4;
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                i16x4 half[2];
+#pragma unroll
+                for (int hr = 0; hr < 2; ++hr) {
+                    const int key = key0 + cc * 16 + hr * 8 + 4 * (G16 >> 1) + j4;
+                    const char *p =
+                        Vb + key * ROWB + (((d0 >> 3) ^ swz<D>(key)) * 16) + (a4 & 1) * 8;
+                    half[hr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p);
+                }
+                struct {
+                    i16x4 lo, hi;
+                } pair{half[0], half[1]};
+                const bf16x8 va = __builtin_bit_cast(bf16x8, pair);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    o[nt][t] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[nt][cc], o[nt][t], 0, 0, 0);
+            }
+        }
+    }
+
+    // partial (O / l, lse2) of this split and key subset
+    const int sidx = split * NKS + ks;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const float lt = pair_sum(l_run[nt]);
+        const int m = rows_base + nt * 32 + l32;
+        if (m < a.M) {
+            const int r = m / a.G, hh = m % a.G;
+            const int64_t row = ((int64_t)b * a.R + r) * a.Hq + (int64_t)g * a.G + hh;
+            const float inv = has_keys(lt) ? 1.f / lt : 0.f;
+            float *dst = a.ws_o + (row * a.S + sidx) * D;
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int d = ((q4 >> 1) ? D / 2 : 0) + 16 * t + 8 * (q4 & 1) + 4 * hl;
+                    float4 v4 = make_float4(o[nt][t][4 * q4] * inv, o[nt][t][4 * q4 + 1] * inv,
+                                            o[nt][t][4 * q4 + 2] * inv, o[nt][t][4 * q4 + 3] * inv);
+                    *(float4 *)(dst + d) = v4;
+                }
+            if (hl == 0)
+                a.ws_lse[row * a.S + sidx] = has_keys(lt) ? m_run[nt] + __log2f(lt) : -INFINITY;
+        }
+    }
+}
+
+// fp32 prefix: one wave per (row, split); lanes over keys for the scores,
+// lanes over channels for the weighted sum of values.
+template <int D>
+__global__ void __launch_bounds__(64) k_prefix_f32(PrefixArgs a) {
+    constexpr int VPL = D / 64;
+    __shared__ float qs[D];
+    __shared__ float pw[64];
+    __shared__ int64_t offs[64];
+    const int lane = threadIdx.x;
+    const int64_t gw = blockIdx.x;
+    const int64_t row = gw / a.n_split;
+    const int split = (int)(gw % a.n_split);
+    const int h = (int)(row % a.Hq);
+    const int b = (int)(row / ((int64_t)a.Hq * a.R));
+    const int g = h / a.G;
+    const float *q = (const float *)a.q + row * D;
+    const float *kp = (const float *)a.k + (int64_t)g * a.stride_head;
+    const float *vp = (const float *)a.v + (int64_t)g * a.stride_head;
+    for (int d = lane; d < D; d += 64)
+        qs[d] = q[d];
+    __syncthreads();
+    const KeyRange kr = split_range(a, b, split);
+    const int ps_mask = (1 << a.ps_shift) - 1;
+    float m = -INFINITY, l = 0.f, o[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        o[i] = 0.f;
+    for (int base = kr.lo; base < kr.hi; base += 64) {
+        const int t = base + lane;
+        const bool valid = t < kr.hi;
+        float u = -INFINITY;
+        int64_t off = 0;
+        if (valid) {
+            const int64_t page =
+                clamp_page(a.page_table[(int64_t)b * a.max_pages + (t >> a.ps_shift)], a.num_pages);
+            off = page * a.stride_page + (int64_t)(t & ps_mask) * a.stride_token;
+            float acc = 0.f;
+#pragma unroll 4
+            for (int d = 0; d < D; d += 4) {
+                const float4 k4 = *(const float4 *)(kp + off + d);
+                acc = fmaf(qs[d], k4.x, acc);
+                acc = fmaf(qs[d + 1], k4.y, acc);
+                acc = fmaf(qs[d + 2], k4.z, acc);
+                acc = fmaf(qs[d + 3], k4.w, acc);
+            }
+            u = acc * a.c;
+        }
+        const float mnew = fmaxf(m, wave_max(u));
+        if (mnew == -INFINITY)
+            continue;
+        const float alpha = fast_exp2(m - mnew);
+        const float p = valid ? fast_exp2(u - mnew) : 0.f;
+        l = l * alpha + wave_sum(p);
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            o[i] *= alpha;
+        pw[lane] = p;
+        offs[lane] = off;
+        __syncthreads();
+        const int nv = kr.hi - base < 64 ? kr.hi - base : 64;
+        for (int i = 0; i < nv; ++i) {
+            const float pi = pw[i];
+            const float *vr = vp + offs[i];
+#pragma unroll
+            for (int j = 0; j < VPL; ++j)
+                o[j] = fmaf(pi, vr[lane + 64 * j], o[j]);
+        }
+        __syncthreads();
+        m = mnew;
+    }
+    const float inv = has_keys(l) ? 1.f / l : 0.f;
+    float *dst = a.ws_o + (row * a.S + split) * D;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+        dst[lane + 64 * j] = o[j] * inv;
+    if (lane == 0)
+        a.ws_lse[row * a.S + split] = has_keys(l) ? m + __log2f(l) : -INFINITY;
+}
+
+struct MergeArgs {
+    const void *q;
+    const void *k;
+    const void *v;
+    int bf16;
+    int64_t stride_page, stride_head, stride_token, num_pages;
+    const int32_t *page_table;
+    int32_t max_pages, ps_shift;
+    const int32_t *prefix_len;
+    int32_t max_prefix_len;
+    const uint64_t *masks;
+    int32_t W, B, R, Hq, G, D, S;
+    float c;
+    const float *ws_o;
+    const float *ws_lse;
+    void *out;
+    float *lse2;
+};
+
+template <int D, bool BF16>
+__device__ inline void load_row(const void *base, int64_t off, int lane, float (&x)[D / 64]) {
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) {
+        if (BF16)
+            x[j] = bf16_bits_to_f32(((const uint16_t *)base)[off + lane * (D / 64) + j]);
+        else
+            x[j] = ((const float *)base)[off + lane * (D / 64) + j];
+    }
+}
+
+// Window part and merge: one wave per (request b, row r, head h).  The window
+// keys are the set bits j < W of the row's ancestor mask, at logical position
+// P + j; unseen window slots are never read.  The window's (o, lse2) is then
+// merged with the S prefix partials: lse2 = log2 sum_k 2^lse2_k and
+// out = sum_k 2^(lse2_k - lse2) o_k.
+template <int D, bool BF16>
+__global__ void __launch_bounds__(256) k_window_merge(MergeArgs a) {
+    constexpr int VPL = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (int64_t)a.B * a.R * a.Hq)
+        return;
+    const int h = (int)(row % a.Hq);
+    const int r = (int)((row / a.Hq) % a.R);
+    const int b = (int)(row / ((int64_t)a.Hq * a.R));
+    const int g = h / a.G;
+    float q[VPL];
+    load_row<D, BF16>(a.q, row * D, lane, q);
+    int P = a.prefix_len[b];
+    P = P < 0 ? 0 : (P > a.max_prefix_len ? a.max_prefix_len : P);
+    uint64_t msk = a.W > 0 ? a.masks[(int64_t)b * a.R + r] : 0ull;
+    if (a.W < 64)
+        msk &= (1ull << a.W) - 1ull;
+    const int ps_mask = (1 << a.ps_shift) - 1;
+    float mw = -INFINITY, lw = 0.f, ow[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+        ow[j] = 0.f;
+    while (msk) {
+        const int j = __ffsll((unsigned long long)msk) - 1;
+        msk &= msk - 1;
+        const int t = P + j;
+        const int64_t page =
+            clamp_page(a.page_table[(int64_t)b * a.max_pages + (t >> a.ps_shift)], a.num_pages);
+        const int64_t off = page * a.stride_page + (int64_t)g * a.stride_head +
+                            (int64_t)(t & ps_mask) * a.stride_token;
+        float kx[VPL], vx[VPL];
+        load_row<D, BF16>(a.k, off, lane, kx);
+        load_row<D, BF16>(a.v, off, lane, vx);
+        float dot = 0.f;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            dot = fmaf(q[i], kx[i], dot);
+        const float u = wave_sum(dot) * a.c;
+        const float mnew = fmaxf(mw, u);
+        const float alpha = fast_exp2(mw - mnew);
+        const float p = fast_exp2(u - mnew);
+        lw = lw * alpha + p;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            ow[i] = fmaf(p, vx[i], ow[i] * alpha);
+        mw = mnew;
+    }
+    const float lse_w = has_keys(lw) ? mw + __log2f(lw) : -INFINITY;
+    const float *lp = a.ws_lse + row * a.S;
+    // max over the parts' lse2, NaN-propagating (a NaN part makes the row NaN)
+    float mx = lse_w;
+    for (int s = 0; s < a.S; ++s) {
+        const float ls = lp[s];
+        mx = (ls > mx || ls != ls) ? ls : mx;
+    }
+    float acc[VPL];
+    float res_lse = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        acc[i] = 0.f;
+    if (mx != -INFINITY) {
+        float zs = 0.f;
+        for (int s = 0; s < a.S; ++s) {
+            const float ls = lp[s];
+            if (ls == -INFINITY)
+                continue;
+            const float z = fast_exp2(ls - mx);
+            zs += z;
+            const float *op = a.ws_o + (row * a.S + s) * D + lane * VPL;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i)
+                acc[i] = fmaf(z, op[i], acc[i]);
+        }
+        if (lse_w != -INFINITY) {
+            const float z = fast_exp2(lse_w - mx);
+            const float inv = 1.f / lw;
+            zs += z;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i)
+                acc[i] = fmaf(z, ow[i] * inv, acc[i]);
+        }
+        const float inv = 1.f / zs;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            acc[i] *= inv;
+        res_lse = mx + __log2f(zs);
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        if (BF16)
+            ((uint16_t *)a.out)[row * D + lane * VPL + i] = f32_to_bf16_bits(acc[i]);
+        else
+            ((float *)a.out)[row * D + lane * VPL + i] = acc[i];
+    }
+    if (a.lse2 && lane == 0)
+        a.lse2[row] = res_lse;
+}
+
+// ---------------------------------------------------------------------------
+// host plan
+// ---------------------------------------------------------------------------
+
+struct Plan {
+    bool mfma;
+    int NT, NKS, RG, n_split, kps, S;
+    size_t o_bytes, lse_off, bytes;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Plan make_plan(tav_dtype dtype, int B, int R, int Hq, int Hkv, int D, int max_prefix_len,
+               int prefix_window, int page_size) {
+    Plan p{};
+    const int G = Hq / Hkv;
+    const long long M = (long long)R * G;
+    const int max_vis = prefix_window > 0 && prefix_window < max_prefix_len ? prefix_window
+                                                                            : max_prefix_len;
+    if (dtype == TAV_BF16) {
+        p.mfma = true;
+        if (M <= 32) {
+            p.NT = 1;
+            p.NKS = 4;
+        } else if (M <= 64) {
+            p.NT = 2;
+            p.NKS = 4;
+        } else if (M <= 128) {
+            p.NT = 2;
+            p.NKS = 2;
+        } else {
+            p.NT = 2;
+            p.NKS = 1;
+        }
+        const int rows_wg = (4 / p.NKS) * p.NT * 32;
+        p.RG = (int)((M + rows_wg - 1) / rows_wg);
+        const int SK = 32 * p.NKS;
+        const long long base = (long long)B * Hkv * p.RG;
+        int n = base > 0 ? (int)((256 + base - 1) / base) : 1;
+        const int by_stages = max_vis / (4 * SK);            // >= 4 stages per split
+        n = n < by_stages ? n : by_stages;
+        n = n < 1 ? 1 : n;
+        // keys per split: a whole number of stages whose page-table slice
+        // (kps / page_size + 2 entries at most) fits the LDS slice
+        int kps;
+        for (;;) {
+            kps = (max_vis + n - 1) / n;
+            kps = ((kps + SK - 1) / SK) * SK;
+            if (kps < SK)
+                kps = SK;
+            if ((long long)kps / page_size + 2 <= kPtMax)
+                break;
+            ++n;
+        }
+        p.kps = kps;
+        p.n_split = max_vis > 0 ? (max_vis + kps - 1) / kps : 1;
+        p.S = p.n_split * p.NKS;
+    } else {
+        p.mfma = false;
+        p.NT = p.NKS = p.RG = 1;
+        const long long rows = (long long)B * R * Hq;
+        int n = rows > 0 ? (int)((1024 + rows - 1) / rows) : 1;
+        const int by_keys = max_vis / 256;
+        n = n < by_keys ? n : by_keys;
+        n = n < 1 ? 1 : n;
+        int kps = (max_vis + n - 1) / n;
+        p.kps = kps < 1 ? 1 : kps;
+        p.n_split = max_vis > 0 ? (max_vis + p.kps - 1) / p.kps : 1;
+        p.S = p.n_split;
+    }
+    const size_t rows = (size_t)B * R * Hq;
+    p.o_bytes = align256(rows * p.S * D * sizeof(float));
+    p.lse_off = p.o_bytes;
+    p.bytes = p.o_bytes + align256(rows * p.S * sizeof(float));
+    if (p.bytes < 256)
+        p.bytes = 256;  // a valid size is never 0
+    return p;
+}
+
+bool shape_ok(tav_dtype dtype, int B, int R, int Hq, int Hkv, int D, int max_prefix_len,
+              int prefix_window, int page_size, tav::Checks *c) {
+    tav::Checks local;
+    tav::Checks &k = c ? *c : local;
+    using tav::str;
+    k.need(dtype == TAV_F32 || dtype == TAV_BF16, TAV_ERR_UNSUPPORTED,
+           "dtype must be TAV_F32 or TAV_BF16, got " + str(dtype));
+    k.need(B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
+    k.need(R >= 1 && R <= 64, TAV_ERR_INVALID_ARG, "R must be in [1, 64], got " + str(R));
+    k.need(Hq >= 1 && Hkv >= 1, TAV_ERR_INVALID_ARG,
+           "Hq and Hkv must be >= 1, got " + str(Hq) + ", " + str(Hkv));
+    k.need(Hkv >= 1 && Hq % Hkv == 0, TAV_ERR_INVALID_ARG,
+           "Hq must be a multiple of Hkv, got " + str(Hq) + " % " + str(Hkv));
+    k.need(D == 64 || D == 128, TAV_ERR_UNSUPPORTED, "D must be 64 or 128, got " + str(D));
+    k.need(max_prefix_len >= 0, TAV_ERR_INVALID_ARG,
+           "max_prefix_len must be >= 0, got " + str(max_prefix_len));
+    k.need(prefix_window >= 0, TAV_ERR_INVALID_ARG,
+           "prefix_window must be >= 0, got " + str(prefix_window));
+    k.need(tav::is_pow2(page_size) && page_size <= 1024, TAV_ERR_UNSUPPORTED,
+           "page_size must be a power of two in [1, 1024], got " + str(page_size));
+    k.need((long long)B * R * Hq <= (1LL << 30), TAV_ERR_INVALID_ARG, "B * R * Hq is too large");
+    return k.status == TAV_OK;
+}
+
+template <int D, int NT, int NKS>
+void launch_mfma(const Plan &p, const PrefixArgs &a, hipStream_t s) {
+    const unsigned grid = (unsigned)((long long)a.B * a.Hkv * p.RG * p.n_split);
+    hipLaunchKernelGGL((k_prefix_mfma<D, NT, NKS>), dim3(grid), dim3(256), 0, s, a);
+}
+
+template <int D>
+void launch_mfma_d(const Plan &p, const PrefixArgs &a, hipStream_t s) {
+    if (p.NT == 1)
+        launch_mfma<D, 1, 4>(p, a, s);
+    else if (p.NKS == 4)
+        launch_mfma<D, 2, 4>(p, a, s);
+    else if (p.NKS == 2)
+        launch_mfma<D, 2, 2>(p, a, s);
+    else
+        launch_mfma<D, 2, 1>(p, a, s);
+}
+
+// Arguments of one tree_attention call after validation.
+struct Call {
+    Plan p;
+    PrefixArgs a;
+    MergeArgs m;
+    int D;
+    bool bf16;
+};
+
+// Validates every argument (all failures are reported together) and builds
+// the launch arguments.  `phase`: 1 = prefix only, 2 = window + merge only,
+// 3 = both.
+tav_status prepare(const char *fn, int phase, Call &call, const void *q, const void *k_cache,
+                   const void *v_cache, tav_dtype dtype, int64_t stride_page,
+                   int64_t stride_head, int64_t stride_token, int64_t num_pages,
+                   const int32_t *page_table, int32_t max_pages, int32_t page_size,
+                   const int32_t *prefix_len, int32_t max_prefix_len, int32_t prefix_window,
+                   const uint64_t *masks, int32_t W, int32_t B, int32_t R, int32_t Hq,
+                   int32_t Hkv, int32_t D, float sm_scale, void *out, float *lse2,
+                   void *workspace, size_t workspace_bytes) {
+    using tav::str;
+    tav::Checks c;
+    shape_ok(dtype, B, R, Hq, Hkv, D, max_prefix_len, prefix_window, page_size, &c);
+    c.need(W >= 0 && W <= 64, TAV_ERR_INVALID_ARG, "W must be in [0, 64], got " + str(W));
+    c.need(max_pages >= 1, TAV_ERR_INVALID_ARG, "max_pages must be >= 1, got " + str(max_pages));
+    c.need((long long)max_pages * page_size >= (long long)max_prefix_len + W, TAV_ERR_INVALID_ARG,
+           "max_pages * page_size (" + str((long long)max_pages * page_size) +
+               ") must cover max_prefix_len + W (" + str((long long)max_prefix_len + W) + ")");
+    c.need(num_pages >= 1, TAV_ERR_INVALID_ARG, "num_pages must be >= 1, got " + str(num_pages));
+    c.need(std::isfinite(sm_scale), TAV_ERR_INVALID_ARG, "sm_scale must be finite");
+    const int esz = dtype == TAV_F32 ? 4 : 2;
+    c.need(stride_page >= 0 && stride_head >= 0 && stride_token >= 0, TAV_ERR_INVALID_ARG,
+           "strides must be >= 0");
+    c.need((stride_page * esz) % 16 == 0 && (stride_head * esz) % 16 == 0 &&
+               (stride_token * esz) % 16 == 0,
+           TAV_ERR_UNSUPPORTED, "K/V strides must be multiples of 16 bytes");
+    if (B > 0) {
+        c.need(q && k_cache && v_cache, TAV_ERR_INVALID_ARG, "q, k_cache and v_cache must be set");
+        c.need(page_table && prefix_len, TAV_ERR_INVALID_ARG, "page_table and prefix_len must be set");
+        if (phase & 2) {
+            c.need(W == 0 || masks, TAV_ERR_INVALID_ARG, "masks is NULL");
+            c.need(out, TAV_ERR_INVALID_ARG, "out is NULL");
+        }
+        c.need(workspace, TAV_ERR_WORKSPACE, "workspace is NULL");
+        c.need((((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15) == 0,
+               TAV_ERR_UNSUPPORTED, "q, k_cache, v_cache and out must be 16-byte aligned");
+        c.need(((uintptr_t)workspace & 255) == 0, TAV_ERR_WORKSPACE,
+               "workspace must be 256-byte aligned");
+    }
+    if (c.status == TAV_OK) {
+        call.p = make_plan(dtype, B, R, Hq, Hkv, D, max_prefix_len, prefix_window, page_size);
+        c.need(workspace_bytes >= call.p.bytes, TAV_ERR_WORKSPACE,
+               "workspace has " + str((long long)workspace_bytes) + " bytes, needs " +
+                   str((long long)call.p.bytes));
+    }
+    if (c.status != TAV_OK)
+        return tav::finish(fn, c);
+
+    const Plan &p = call.p;
+    const float scale = sm_scale > 0.f ? sm_scale : 1.f / std::sqrt((float)D);
+    PrefixArgs &a = call.a;
+    a = PrefixArgs{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.stride_page = stride_page;
+    a.stride_head = stride_head;
+    a.stride_token = stride_token;
+    a.num_pages = num_pages;
+    a.page_table = page_table;
+    a.max_pages = max_pages;
+    a.ps_shift = tav::ilog2(page_size);
+    a.prefix_len = prefix_len;
+    a.max_prefix_len = max_prefix_len;
+    a.prefix_window = prefix_window;
+    a.B = B;
+    a.R = R;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.M = R * a.G;
+    a.RG = p.RG;
+    a.n_split = p.n_split;
+    a.kps = p.kps;
+    a.S = p.S;
+    a.c = scale * kLog2e;
+    a.ws_o = (float *)workspace;
+    a.ws_lse = (float *)((char *)workspace + p.lse_off);
+
+    MergeArgs &m = call.m;
+    m = MergeArgs{};
+    m.q = q;
+    m.k = k_cache;
+    m.v = v_cache;
+    m.bf16 = dtype == TAV_BF16;
+    m.stride_page = stride_page;
+    m.stride_head = stride_head;
+    m.stride_token = stride_token;
+    m.num_pages = num_pages;
+    m.page_table = page_table;
+    m.max_pages = max_pages;
+    m.ps_shift = a.ps_shift;
+    m.prefix_len = prefix_len;
+    m.max_prefix_len = max_prefix_len;
+    m.masks = masks;
+    m.W = W;
+    m.B = B;
+    m.R = R;
+    m.Hq = Hq;
+    m.G = a.G;
+    m.D = D;
+    m.S = p.S;
+    m.c = a.c;
+    m.ws_o = a.ws_o;
+    m.ws_lse = a.ws_lse;
+    m.out = out;
+    m.lse2 = lse2;
+    call.D = D;
+    call.bf16 = dtype == TAV_BF16;
+    return TAV_OK;
+}
+
+void launch_prefix(const Call &c, hipStream_t s) {
+    const Plan &p = c.p;
+    if (p.mfma) {
+        if (c.D == 128)
+            launch_mfma_d<128>(p, c.a, s);
+        else
+            launch_mfma_d<64>(p, c.a, s);
+    } else {
+        const unsigned grid = (unsigned)((long long)c.a.B * c.a.R * c.a.Hq * p.n_split);
+        if (c.D == 128)
+            hipLaunchKernelGGL(k_prefix_f32<128>, dim3(grid), dim3(64), 0, s, c.a);
+        else
+            hipLaunchKernelGGL(k_prefix_f32<64>, dim3(grid), dim3(64), 0, s, c.a);
+    }
+}
+
+void launch_merge(const Call &c, hipStream_t s) {
+    const MergeArgs &m = c.m;
+    const unsigned grid = (unsigned)(((long long)m.B * m.R * m.Hq + 3) / 4);
+    if (c.D == 128) {
+        if (c.bf16)
+            hipLaunchKernelGGL((k_window_merge<128, true>), dim3(grid), dim3(256), 0, s, m);
+        else
+            hipLaunchKernelGGL((k_window_merge<128, false>), dim3(grid), dim3(256), 0, s, m);
+    } else {
+        if (c.bf16)
+            hipLaunchKernelGGL((k_window_merge<64, true>), dim3(grid), dim3(256), 0, s, m);
+        else
+            hipLaunchKernelGGL((k_window_merge<64, false>), dim3(grid), dim3(256), 0, s, m);
+    }
+}
+
+}  // namespace
+
+extern "C" size_t tree_attention_workspace_size(tav_dtype dtype, int32_t B, int32_t R, int32_t Hq,
+                                                int32_t Hkv, int32_t D, int32_t max_prefix_len,
+                                                int32_t prefix_window, int32_t page_size) {
+    if (!shape_ok(dtype, B, R, Hq, Hkv, D, max_prefix_len, prefix_window, page_size, nullptr))
+        return 0;
+    return make_plan(dtype, B, R, Hq, Hkv, D, max_prefix_len, prefix_window, page_size).bytes;
+}
+
+#define TAV_ATTN_PARAMS                                                                         \
+    const void *q, const void *k_cache, const void *v_cache, tav_dtype dtype,                   \
+        int64_t stride_page, int64_t stride_head, int64_t stride_token, int64_t num_pages,     \
+        const int32_t *page_table, int32_t max_pages, int32_t page_size,                        \
+        const int32_t *prefix_len, int32_t max_prefix_len, int32_t prefix_window,              \
+        const uint64_t *masks, int32_t W, int32_t B, int32_t R, int32_t Hq, int32_t Hkv,       \
+        int32_t D, float sm_scale, void *out, float *lse2, void *workspace,                     \
+        size_t workspace_bytes, void *stream
+#define TAV_ATTN_ARGS                                                                           \
+    q, k_cache, v_cache, dtype, stride_page, stride_head, stride_token, num_pages, page_table,  \
+        max_pages, page_size, prefix_len, max_prefix_len, prefix_window, masks, W, B, R, Hq,    \
+        Hkv, D, sm_scale, out, lse2, workspace, workspace_bytes
+
+static tav_status run_phases(const char *fn, int phase, TAV_ATTN_PARAMS) {
+    Call call;
+    const tav_status st = prepare(fn, phase, call, TAV_ATTN_ARGS);
+    if (st != TAV_OK || B == 0)
+        return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (phase & 1) {
+        launch_prefix(call, s);
+        const tav_status e = tav::launched(fn);
+        if (e != TAV_OK)
+            return e;
+    }
+    if (phase & 2)
+        launch_merge(call, s);
+    return tav::launched(fn);
+}
+
+extern "C" tav_status tree_attention(TAV_ATTN_PARAMS) {
+    return run_phases("tree_attention", 3, TAV_ATTN_ARGS, stream);
+}
+
+extern "C" tav_status tree_attention_prefix(TAV_ATTN_PARAMS) {
+    return run_phases("tree_attention_prefix", 1, TAV_ATTN_ARGS, stream);
+}
+
+extern "C" tav_status tree_attention_window_merge(TAV_ATTN_PARAMS) {
+    return run_phases("tree_attention_window_merge", 2, TAV_ATTN_ARGS, stream);
+}
