@@ -32,6 +32,7 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -159,26 +160,32 @@ __device__ inline int swz(int key) {
     return D == 128 ? (x | (key & 8)) : x;
 }
 
-template <int D, int NKS>
+template <int D, int NRB, int NKS>
 struct MfmaCfg {
+    static constexpr int WAVES = NRB * NKS;       // waves per workgroup
+    static constexpr int THREADS = 64 * WAVES;
     static constexpr int SK = 32 * NKS;           // keys per stage
     static constexpr int CH = D / 8;              // 16-byte chunks per key row
     static constexpr int ROWB = D * 2;            // bytes per key row (bf16)
     static constexpr int SB = SK * ROWB * 2;      // stage bytes, K then V
     static constexpr int NBUF0 = kLdsStageBudget / SB;
     static constexpr int NBUF = NBUF0 > 8 ? 8 : NBUF0;
-    static constexpr int LPS = SB / (256 * 16);   // 16-byte loads per thread per stage
+    static constexpr int LPS = SB / (THREADS * 16);   // 16-byte loads per thread per stage
     static_assert(NBUF >= 2, "stage too large");
+    static_assert(LPS >= 1 && SB % (THREADS * 16) == 0, "stage split");
     static_assert((NBUF - 2) * LPS < 64, "vmcnt range");
 };
 
-template <int D, int NT, int NKS>
-__global__ void __launch_bounds__(256, 1) k_prefix_mfma(PrefixArgs a) {
-    using C = MfmaCfg<D, NKS>;
+// Split-K paged prefix decode on MFMA.  One workgroup = WAVES waves = NRB row
+// blocks of 32 folded query rows x NKS key subsets; every wave owns 32 rows
+// and, per stage, one 32-key block.  With 8 waves a SIMD holds two waves, so
+// one wave's MFMAs overlap the other's softmax.
+template <int D, int NRB, int NKS>
+__global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a) {
+    using C = MfmaCfg<D, NRB, NKS>;
     constexpr int SK = C::SK, CH = C::CH, ROWB = C::ROWB, SB = C::SB, NBUF = C::NBUF,
-                  LPS = C::LPS;
-    constexpr int NRB = 4 / NKS;                  // row blocks per workgroup
-    constexpr int ROWS_WG = NRB * NT * 32;
+                  LPS = C::LPS, THREADS = C::THREADS;
+    constexpr int ROWS_WG = NRB * 32;
     constexpr int KSTEPS = D / 16;
     constexpr int DT = D / 32;                    // 32-wide d tiles
 
@@ -214,24 +221,23 @@ __global__ void __launch_bounds__(256, 1) k_prefix_mfma(PrefixArgs a) {
     const int ns = (nkeys + SK - 1) / SK;
     const int rbw = w % NRB;   // this wave's row block
     const int ks = w / NRB;    // this wave's key subset within a stage
-    const int rows_base = rg * ROWS_WG + rbw * NT * 32;
+    const int rows_base = rg * ROWS_WG + rbw * 32;
 
     // page-table slice of this split
     const int lp0 = nkeys > 0 ? (kr.lo >> a.ps_shift) : 0;
     const int npt = nkeys > 0 ? ((kr.hi - 1) >> a.ps_shift) - lp0 + 1 : 0;
-    for (int i = tid; i < npt && i < kPtMax; i += 256)
+    for (int i = tid; i < npt && i < kPtMax; i += THREADS)
         pt[i] = (int32_t)clamp_page(a.page_table[(int64_t)b * a.max_pages + lp0 + i], a.num_pages);
     // zero the stage buffers once: the last, partial stage leaves rows unloaded
     // and they must hold finite values (their softmax weight is exactly 0)
-    for (int i = tid; i < NBUF * SB / 16; i += 256)
+    for (int i = tid; i < NBUF * SB / 16; i += THREADS)
         reinterpret_cast<int4 *>(lds)[i] = make_int4(0, 0, 0, 0);
 
     // Q^T operand in registers: lane (row n = l32, half hl) holds
     // Q[row][16 kk + 8 hl .. +8] for each k step.
-    bf16x8 qv[NT][KSTEPS];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int m = rows_base + nt * 32 + l32;
+    bf16x8 qv[KSTEPS];
+    {
+        const int m = rows_base + l32;
         const bool ok = m < a.M;
         const int r = ok ? m / a.G : 0, hh = ok ? m % a.G : 0;
         const uint16_t *qp = (const uint16_t *)a.q +
@@ -239,57 +245,64 @@ __global__ void __launch_bounds__(256, 1) k_prefix_mfma(PrefixArgs a) {
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
             int4 v4 = ok ? *(const int4 *)(qp + 16 * kk) : make_int4(0, 0, 0, 0);
-            qv[nt][kk] = __builtin_bit_cast(bf16x8, v4);
+            qv[kk] = __builtin_bit_cast(bf16x8, v4);
         }
     }
     __syncthreads();
 
-    const uint16_t *kbase = (const uint16_t *)a.k + (int64_t)g * a.stride_head;
-    const uint16_t *vbase = (const uint16_t *)a.v + (int64_t)g * a.stride_head;
     const int ps_mask = (1 << a.ps_shift) - 1;
     const uint32_t lds0 = lds_off(lds);
+    // Loader roles, fixed for the whole kernel: load i of this thread fills
+    // stage slot i*THREADS + tid, i.e. chunk (slot % CH) ^ swz(key) of key
+    // slot / CH of the K region (first half of the slots) or the V region.
+    const uint16_t *src_base[LPS];
+    int ld_key[LPS];
+#pragma unroll
+    for (int i = 0; i < LPS; ++i) {
+        const int slot = i * THREADS + tid;
+        const int region = (i * THREADS + w * 64) / (SK * CH);   // wave-uniform
+        const int s2 = slot - region * (SK * CH);
+        ld_key[i] = s2 / CH;
+        src_base[i] = (const uint16_t *)(region ? a.v : a.k) + (int64_t)g * a.stride_head +
+                      (((s2 % CH) ^ swz<D>(ld_key[i])) * 8);
+    }
 
-    // Issue the direct-to-LDS loads of stage st: slot s of the stage (16
-    // bytes) holds chunk (s % CH) ^ swz(key) of key s / CH, the K slots first,
-    // then the V slots.  Keys past the split are not loaded.
+    // Issue the direct-to-LDS loads of stage st.  All page-table reads come
+    // first so that the loads are not each held up by an LDS read.
     auto issue = [&](int st) {
         const uint32_t sbase = lds0 + (uint32_t)((st % NBUF) * SB);
         const int key_base = kr.lo + st * SK;
+        int64_t page[LPS];
 #pragma unroll
         for (int i = 0; i < LPS; ++i) {
-            const int slot = i * 256 + w * 64 + lane;
-            const int region = (i * 256 + w * 64) / (SK * CH);   // wave-uniform
-            const int s2 = slot - region * (SK * CH);
-            const int key = s2 / CH;
-            const int c = (s2 % CH) ^ swz<D>(key);
-            const int t = key_base + key;
-            if (t < kr.hi) {
-                const int64_t page = pt[(t >> a.ps_shift) - lp0];
-                const uint16_t *src = (region ? vbase : kbase) + page * a.stride_page +
-                                      (int64_t)(t & ps_mask) * a.stride_token + c * 8;
-                dma_load16(src, __builtin_amdgcn_readfirstlane(sbase + (i * 256 + w * 64) * 16));
-            }
+            const int t = key_base + ld_key[i];
+            page[i] = t < kr.hi ? pt[(t >> a.ps_shift) - lp0] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < LPS; ++i) {
+            const int t = key_base + ld_key[i];
+            if (t < kr.hi)
+                dma_load16(src_base[i] + page[i] * a.stride_page +
+                               (int64_t)(t & ps_mask) * a.stride_token,
+                           __builtin_amdgcn_readfirstlane(sbase + (i * THREADS + w * 64) * 16));
         }
     };
 
-    f32x16 o[NT][DT];
-    float m_run[NT], l_run[NT];
+    f32x16 o[DT];
+    float m_run = -INFINITY, l_run = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        m_run[nt] = -INFINITY;
-        l_run[nt] = 0.f;
+    for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                o[nt][t][r] = 0.f;
-    }
+        for (int r = 0; r < 16; ++r)
+            o[t][r] = 0.f;
 
     for (int st = 0; st < NBUF - 1 && st < ns; ++st)
         issue(st);
 
     const int G16 = lane >> 4, a4 = lane & 3, j4 = (lane >> 2) & 3;
-    const int krow_l = l32;                      // K operand: key of this lane
+    const int key0 = ks * 32;
+    const int krow = key0 + l32;                 // K operand: key of this lane
+    const int ksw = swz<D>(krow);
     for (int it = 0; it < ns; ++it) {
         // Stage `it` is complete once at most the loads of the later, full
         // stages are outstanding.  When the last (partial) stage is among the
@@ -305,73 +318,58 @@ __global__ void __launch_bounds__(256, 1) k_prefix_mfma(PrefixArgs a) {
 
         const char *Kb = lds + (it % NBUF) * SB;
         const char *Vb = Kb + SB / 2;
-        const int key0 = ks * 32;
         const int first = kr.lo + it * SK + key0;  // absolute key of this wave's block
         if (first >= kr.hi)
             continue;
         // S^T[key][row] = sum_d K[key][d] Q[row][d]
-        f32x16 s[NT];
+        f32x16 s;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                s[nt][r] = 0.f;
-        const int krow = key0 + krow_l;
-        const int ksw = swz<D>(krow);
+        for (int r = 0; r < 16; ++r)
+            s[r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
             const bf16x8 ka = *(const bf16x8 *)(Kb + krow * ROWB + (((2 * kk + hl) ^ ksw) * 16));
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                s[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[nt][kk], s[nt], 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[kk], s, 0, 0, 0);
         }
         // keys past the end of the split are not visible
         if (first + 32 > kr.hi) {
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = 8 * (r >> 2) + 4 * hl + (r & 3);
-                    if (first + key >= kr.hi)
-                        s[nt][r] = -INFINITY;
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int key = 8 * (r >> 2) + 4 * hl + (r & 3);
+                if (first + key >= kr.hi)
+                    s[r] = -INFINITY;
+            }
         }
         // online softmax in the exp2 domain; the running max is only raised
         // when a block exceeds it by more than 2^8, so rescaling of O is rare
         // and weights stay <= 256
-        bf16x8 pb[NT][2];
+        float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            float mx = s[nt][0];
+        for (int r = 3; r < 16; ++r)
+            mx = fmaxf(mx, s[r]);
+        mx = pair_max(mx);
+        const float mb = mx * a.c;
+        if (__ballot(mb > m_run + 8.f)) {
+            const float mnew = fmaxf(m_run, mb);
+            const float alpha = fast_exp2(m_run - mnew);  // 0 when m_run = -inf
+            l_run *= alpha;
 #pragma unroll
-            for (int r = 1; r < 16; ++r)
-                mx = fmaxf(mx, s[nt][r]);
-            mx = pair_max(mx);
-            const float mb = mx * a.c;
-            if (__ballot(mb > m_run[nt] + 8.f)) {
-                const float mnew = fmaxf(m_run[nt], mb);
-                const float alpha = fast_exp2(m_run[nt] - mnew);  // 0 when m_run = -inf
-                l_run[nt] *= alpha;
+            for (int t = 0; t < DT; ++t)
 #pragma unroll
-                for (int t = 0; t < DT; ++t)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        o[nt][t][r] *= alpha;
-                m_run[nt] = mnew;
-            }
-            const float mu = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
-            float ps[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                ps[r] = fast_exp2(fmaf(s[nt][r], a.c, -mu));
-                l_run[nt] += ps[r];
-            }
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    pb[nt][cc][t] = (__bf16)ps[cc * 8 + t];
+                for (int r = 0; r < 16; ++r)
+                    o[t][r] *= alpha;
+            m_run = mnew;
         }
+        const float mu = m_run == -INFINITY ? 0.f : m_run;
+        bf16x8 pb[2];
+        float lsum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pr = fast_exp2(fmaf(s[r], a.c, -mu));
+            lsum += pr;
+            pb[r >> 3][r & 7] = (__bf16)pr;
+        }
+        l_run += lsum;
         // O^T[d][row] += sum_key V[key][d] P[row][key].  The P operand is the
         // S accumulator as is: the key order inside each 16-key chunk is
         // permuted identically for V (transposing LDS reads) and P, which
@@ -396,37 +394,332 @@ __global__ void __launch_bounds__(256, 1) k_prefix_mfma(PrefixArgs a) {
                     i16x4 lo, hi;
                 } pair{half[0], half[1]};
                 const bf16x8 va = __builtin_bit_cast(bf16x8, pair);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    o[nt][t] =
-                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[nt][cc], o[nt][t], 0, 0, 0);
+                o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[cc], o[t], 0, 0, 0);
             }
         }
     }
 
     // partial (O / l, lse2) of this split and key subset
     const int sidx = split * NKS + ks;
+    const float lt = pair_sum(l_run);
+    const int m = rows_base + l32;
+    if (m < a.M) {
+        const int r = m / a.G, hh = m % a.G;
+        const int64_t row = ((int64_t)b * a.R + r) * a.Hq + (int64_t)g * a.G + hh;
+        const float inv = has_keys(lt) ? 1.f / lt : 0.f;
+        float *dst = a.ws_o + (row * a.S + sidx) * D;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const float lt = pair_sum(l_run[nt]);
-        const int m = rows_base + nt * 32 + l32;
-        if (m < a.M) {
-            const int r = m / a.G, hh = m % a.G;
-            const int64_t row = ((int64_t)b * a.R + r) * a.Hq + (int64_t)g * a.G + hh;
-            const float inv = has_keys(lt) ? 1.f / lt : 0.f;
-            float *dst = a.ws_o + (row * a.S + sidx) * D;
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d = ((q4 >> 1) ? D / 2 : 0) + 16 * t + 8 * (q4 & 1) + 4 * hl;
+                float4 v4 = make_float4(o[t][4 * q4] * inv, o[t][4 * q4 + 1] * inv,
+                                        o[t][4 * q4 + 2] * inv, o[t][4 * q4 + 3] * inv);
+                *(float4 *)(dst + d) = v4;
+            }
+        if (hl == 0)
+            a.ws_lse[row * a.S + sidx] = has_keys(lt) ? m_run + __log2f(lt) : -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Software-pipelined prefix kernel for wide row groups (256 folded rows:
+// 8 waves x 32 rows, every wave reads every key).  Per 32-key block u a wave
+// issues the S MFMAs of block u + 1 before the softmax of block u, so the
+// MFMA pipe works while the vector ALU computes exponentials; stages are 64
+// keys (two blocks), NBUF deep, with one workgroup barrier per stage.
+//
+// LDS layout of a stage (SK = 64 keys), chosen so that every operand read is
+// one per-lane base plus an immediate offset:
+//   K region: D/16 sub-regions kk (MFMA k steps), each SK keys x 32 bytes
+//     (channels 16 kk .. 16 kk + 15); the two 16-byte halves of a key's 32
+//     bytes are swapped when swk(key) = 1.
+//   V region: D/32 sub-regions t (32-channel tiles), each SK keys x 64 bytes
+//     holding channels [16t, 16t + 16) then [D/2 + 16t, D/2 + 16t + 16); the
+//     two 32-byte halves of a key's 64 bytes are swapped when swv(key) = 1.
+// Both swaps make the reads bank-conflict-free: 8 (or 16) consecutive keys of
+// a K read hit distinct 16-byte bank groups; the 4 keys x 32 bytes of a
+// transposing V read hit distinct 32-byte bank groups.
+// ---------------------------------------------------------------------------
+__device__ inline int swk(int key) { return ((key >> 2) ^ (key >> 3)) & 1; }
+__device__ inline int swv(int key) { return (key >> 1) & 1; }
+
+template <int D>
+struct PipeCfg {
+    static constexpr int WAVES = 8;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int SK = 64;                 // keys per stage (2 blocks)
+    static constexpr int KSTEPS = D / 16;
+    static constexpr int DT = D / 32;
+    static constexpr int KREG = SK * D * 2;       // bytes of the K region
+    static constexpr int SB = 2 * KREG;           // stage bytes
+    static constexpr int NBUF0 = kLdsStageBudget / SB;
+    static constexpr int NBUF = NBUF0 > 8 ? 8 : NBUF0;
+    static constexpr int PF = NBUF - 2;           // stages in flight ahead of the current one
+    static constexpr int LPS = SB / (THREADS * 16);
+    static_assert(NBUF >= 3 && LPS >= 1 && SB % (THREADS * 16) == 0, "stage split");
+    static_assert((PF - 1) * LPS < 64, "vmcnt range");
+};
+
+template <int D>
+__global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
+    using C = PipeCfg<D>;
+    constexpr int SK = C::SK, SB = C::SB, NBUF = C::NBUF, PF = C::PF, LPS = C::LPS,
+                  THREADS = C::THREADS, KREG = C::KREG, KSTEPS = C::KSTEPS, DT = C::DT;
+    constexpr int ROWS_WG = 256;
+
+    __shared__ __attribute__((aligned(16))) char lds[NBUF * SB];
+    __shared__ int32_t pt[kPtMax];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hl = lane >> 5;
+    const int l32 = lane & 31;
+
+    const int units = a.B * a.Hkv * a.n_split;
+    int rg, unit;
+    const int id = blockIdx.x;
+    if (a.RG > 1 && (units & 7) == 0) {
+        const int xcd = id & 7, slot = id >> 3;
+        rg = slot % a.RG;
+        unit = (slot / a.RG) * 8 + xcd;
+    } else {
+        rg = id % a.RG;
+        unit = id / a.RG;
+    }
+    const int split = unit % a.n_split;
+    const int g = (unit / a.n_split) % a.Hkv;
+    const int b = unit / (a.n_split * a.Hkv);
+
+    const KeyRange kr = split_range(a, b, split);
+    const int nkeys = kr.hi - kr.lo;
+    const int ns = (nkeys + SK - 1) / SK;
+    const int nb = (nkeys + 31) / 32;
+    const int rows_base = rg * ROWS_WG + w * 32;
+
+    const int lp0 = nkeys > 0 ? (kr.lo >> a.ps_shift) : 0;
+    const int npt = nkeys > 0 ? ((kr.hi - 1) >> a.ps_shift) - lp0 + 1 : 0;
+    for (int i = tid; i < npt && i < kPtMax; i += THREADS)
+        pt[i] = (int32_t)clamp_page(a.page_table[(int64_t)b * a.max_pages + lp0 + i], a.num_pages);
+    for (int i = tid; i < NBUF * SB / 16; i += THREADS)
+        reinterpret_cast<int4 *>(lds)[i] = make_int4(0, 0, 0, 0);
+
+    bf16x8 qv[KSTEPS];
+    {
+        const int m = rows_base + l32;
+        const bool ok = m < a.M;
+        const int r = ok ? m / a.G : 0, hh = ok ? m % a.G : 0;
+        const uint16_t *qp = (const uint16_t *)a.q +
+                             (((int64_t)b * a.R + r) * a.Hq + (int64_t)g * a.G + hh) * D + 8 * hl;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            int4 v4 = ok ? *(const int4 *)(qp + 16 * kk) : make_int4(0, 0, 0, 0);
+            qv[kk] = __builtin_bit_cast(bf16x8, v4);
+        }
+    }
+    __syncthreads();
+
+    // loader roles (fixed): load i fills stage slot i * THREADS + tid
+    const int ps_mask = (1 << a.ps_shift) - 1;
+    const uint32_t lds0 = lds_off(lds);
+    const uint16_t *src_base[LPS];
+    int ld_key[LPS];
+#pragma unroll
+    for (int i = 0; i < LPS; ++i) {
+        const int slot = i * THREADS + tid;
+        const bool vreg = (i * THREADS + w * 64) >= SK * (D / 8);   // wave-uniform
+        int key, dch;
+        if (!vreg) {
+            const int sk = slot;
+            const int kk = sk / (SK * 2), rem = sk % (SK * 2);
+            key = rem / 2;
+            dch = 2 * kk + ((rem & 1) ^ swk(key));
+        } else {
+            const int sv = slot - SK * (D / 8);
+            const int t = sv / (SK * 4), rem = sv % (SK * 4);
+            key = rem / 4;
+            const int c = (rem & 3) ^ (2 * swv(key));
+            dch = (c >> 1) * (D / 16) + 2 * t + (c & 1);
+        }
+        ld_key[i] = key;
+        src_base[i] = (const uint16_t *)(vreg ? a.v : a.k) + (int64_t)g * a.stride_head + dch * 8;
+    }
+    auto issue = [&](int st) {
+        const uint32_t sbase = lds0 + (uint32_t)((st % NBUF) * SB);
+        const int key_base = kr.lo + st * SK;
+        int64_t page[LPS];
+#pragma unroll
+        for (int i = 0; i < LPS; ++i) {
+            const int t = key_base + ld_key[i];
+            page[i] = t < kr.hi ? pt[(t >> a.ps_shift) - lp0] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < LPS; ++i) {
+            const int t = key_base + ld_key[i];
+            if (t < kr.hi)
+                dma_load16(src_base[i] + page[i] * a.stride_page +
+                               (int64_t)(t & ps_mask) * a.stride_token,
+                           __builtin_amdgcn_readfirstlane(sbase + (i * THREADS + w * 64) * 16));
+        }
+    };
+    // Stage st is complete once at most the loads of the later, full stages
+    // are outstanding (all of them when the partial last stage is among
+    // them); then the barrier publishes every wave's loads and frees the
+    // buffer of stage st - 2 for stage st + PF.
+    auto stage_ready = [&](int st) {
+        if (st + PF - 1 < ns - 1)
+            wait_vmcnt<(PF - 1) * LPS>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();
+        if (st + PF < ns)
+            issue(st + PF);
+    };
+
+    // per-lane operand offsets inside a stage
+    const uint32_t koff = l32 * 32 + ((hl ^ swk(l32)) * 16);
+    const int G16 = lane >> 4, a4 = lane & 3, j4 = (lane >> 2) & 3;
+    const uint32_t voff = KREG + (4 * (G16 >> 1) + j4) * 64 +
+                          (((2 * (G16 & 1) + (a4 >> 1)) ^ (2 * ((j4 >> 1) & 1))) * 16) +
+                          (a4 & 1) * 8;
+
+    f32x16 o[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            o[t][r] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // S^T of block u: keys [32 u, 32 u + 32) of the split
+    auto qk = [&](int u) {
+        const char *kb = lds + ((u >> 1) % NBUF) * SB + (u & 1) * 1024 + koff;
+        f32x16 acc;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            const bf16x8 ka = *(const bf16x8 *)(kb + kk * (SK * 32));
+            if (kk == 0)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[kk], f32x16{}, 0, 0, 0);
+            else
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[kk], acc, 0, 0, 0);
+        }
+        return acc;
+    };
+
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+    // Softmax of block u from its S^T, in the exp2 domain, returning the P^T
+    // operand.  The running max is only raised when a block exceeds it by
+    // more than 2^8, so rescaling O is rare and weights stay <= 256.
+    auto rescale_if_needed = [&](const f32x16 &sv) {
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+#pragma unroll
+        for (int r = 3; r < 16; ++r)
+            mx = fmaxf(mx, sv[r]);
+        mx = pair_max(mx);
+        const float mb = mx * a.c;
+        if (__ballot(mb > m_run + 8.f)) {
+            const float mnew = fmaxf(m_run, mb);
+            const float alpha = fast_exp2(m_run - mnew);  // 0 when m_run = -inf
+            l_run *= alpha;
 #pragma unroll
             for (int t = 0; t < DT; ++t)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int d = ((q4 >> 1) ? D / 2 : 0) + 16 * t + 8 * (q4 & 1) + 4 * hl;
-                    float4 v4 = make_float4(o[nt][t][4 * q4] * inv, o[nt][t][4 * q4 + 1] * inv,
-                                            o[nt][t][4 * q4 + 2] * inv, o[nt][t][4 * q4 + 3] * inv);
-                    *(float4 *)(dst + d) = v4;
-                }
-            if (hl == 0)
-                a.ws_lse[row * a.S + sidx] = has_keys(lt) ? m_run[nt] + __log2f(lt) : -INFINITY;
+                for (int r = 0; r < 16; ++r)
+                    o[t][r] *= alpha;
+            m_run = mnew;
         }
+    };
+    auto weights = [&](const f32x16 &sv, bf16x8 (&pb)[2]) {
+        const float mu = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            pb[r >> 3][r & 7] = (__bf16)fast_exp2(fmaf(sv[r], a.c, -mu));
+        // the row sum adds the bf16 weights the MFMA multiplies
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bf16x2 pr = {pb[cc][2 * e], pb[cc][2 * e + 1]};
+                l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+            }
+    };
+    // O^T += V^T P^T for block u (transposing V reads, see above)
+    auto pv = [&](int u, const bf16x8 (&pb)[2]) {
+        const char *vb = lds + ((u >> 1) % NBUF) * SB + (u & 1) * 2048 + voff;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const char *p = vb + t * (SK * 64) + cc * 1024;
+                struct {
+                    i16x4 lo, hi;
+                } pair{__builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p),
+                       __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(p + 512))};
+                o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pair),
+                                                               pb[cc], o[t], 0, 0, 0);
+            }
+        }
+    };
+
+    for (int st = 0; st < PF && st < ns; ++st)
+        issue(st);
+    if (nb > 0) {
+        stage_ready(0);
+        f32x16 s = qk(0);
+        // every block but the last is full: S of block u + 1 is computed
+        // while the vector ALU turns S of block u into weights
+        for (int u = 0; u + 1 < nb; ++u) {
+            if (((u + 1) & 1) == 0)
+                stage_ready((u + 1) >> 1);
+            rescale_if_needed(s);
+            bf16x8 pb[2];
+            const f32x16 s_next = qk(u + 1);
+            weights(s, pb);
+#pragma unroll
+            for (int i = 0; i < KSTEPS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // K operand read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // S MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // weights VALU
+            }
+            pv(u, pb);
+            s = s_next;
+        }
+        // the last block may be partial: keys past the split are not visible
+        const int u = nb - 1;
+        const int lim = kr.hi - (kr.lo + u * 32);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = 8 * (r >> 2) + 4 * hl + (r & 3);
+            if (key >= lim)
+                s[r] = -INFINITY;
+        }
+        rescale_if_needed(s);
+        bf16x8 pb[2];
+        weights(s, pb);
+        pv(u, pb);
+    }
+
+    const int sidx = split;
+    const float lt = pair_sum(l_run);
+    const int m = rows_base + l32;
+    if (m < a.M) {
+        const int r = m / a.G, hh = m % a.G;
+        const int64_t row = ((int64_t)b * a.R + r) * a.Hq + (int64_t)g * a.G + hh;
+        const float inv = has_keys(lt) ? 1.f / lt : 0.f;
+        float *dst = a.ws_o + (row * a.S + sidx) * D;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d = ((q4 >> 1) ? D / 2 : 0) + 16 * t + 8 * (q4 & 1) + 4 * hl;
+                float4 v4 = make_float4(o[t][4 * q4] * inv, o[t][4 * q4 + 1] * inv,
+                                        o[t][4 * q4 + 2] * inv, o[t][4 * q4 + 3] * inv);
+                *(float4 *)(dst + d) = v4;
+            }
+        if (hl == 0)
+            a.ws_lse[row * a.S + sidx] = has_keys(lt) ? m_run + __log2f(lt) : -INFINITY;
     }
 }
 
@@ -649,7 +942,7 @@ __global__ void __launch_bounds__(256) k_window_merge(MergeArgs a) {
 
 struct Plan {
     bool mfma;
-    int NT, NKS, RG, n_split, kps, S;
+    int NT, NRB, NKS, RG, n_split, kps, S;
     size_t o_bytes, lse_off, bytes;
 };
 
@@ -664,22 +957,23 @@ Plan make_plan(tav_dtype dtype, int B, int R, int Hq, int Hkv, int D, int max_pr
                                                                             : max_prefix_len;
     if (dtype == TAV_BF16) {
         p.mfma = true;
+        p.NT = 1;
         if (M <= 32) {
-            p.NT = 1;
+            p.NRB = 1;
             p.NKS = 4;
         } else if (M <= 64) {
-            p.NT = 2;
+            p.NRB = 2;
             p.NKS = 4;
         } else if (M <= 128) {
-            p.NT = 2;
+            p.NRB = 4;
             p.NKS = 2;
         } else {
-            p.NT = 2;
+            p.NRB = 8;
             p.NKS = 1;
         }
-        const int rows_wg = (4 / p.NKS) * p.NT * 32;
+        const int rows_wg = p.NRB * 32;
         p.RG = (int)((M + rows_wg - 1) / rows_wg);
-        const int SK = 32 * p.NKS;
+        const int SK = p.NRB == 8 ? 64 : 32 * p.NKS;
         const long long base = (long long)B * Hkv * p.RG;
         int n = base > 0 ? (int)((256 + base - 1) / base) : 1;
         const int by_stages = max_vis / (4 * SK);            // >= 4 stages per split
@@ -702,7 +996,7 @@ Plan make_plan(tav_dtype dtype, int B, int R, int Hq, int Hkv, int D, int max_pr
         p.S = p.n_split * p.NKS;
     } else {
         p.mfma = false;
-        p.NT = p.NKS = p.RG = 1;
+        p.NT = p.NRB = p.NKS = p.RG = 1;
         const long long rows = (long long)B * R * Hq;
         int n = rows > 0 ? (int)((1024 + rows - 1) / rows) : 1;
         const int by_keys = max_vis / 256;
@@ -746,22 +1040,24 @@ bool shape_ok(tav_dtype dtype, int B, int R, int Hq, int Hkv, int D, int max_pre
     return k.status == TAV_OK;
 }
 
-template <int D, int NT, int NKS>
+template <int D, int NRB, int NKS>
 void launch_mfma(const Plan &p, const PrefixArgs &a, hipStream_t s) {
     const unsigned grid = (unsigned)((long long)a.B * a.Hkv * p.RG * p.n_split);
-    hipLaunchKernelGGL((k_prefix_mfma<D, NT, NKS>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_prefix_mfma<D, NRB, NKS>), dim3(grid), dim3(64 * NRB * NKS), 0, s, a);
 }
 
 template <int D>
 void launch_mfma_d(const Plan &p, const PrefixArgs &a, hipStream_t s) {
-    if (p.NT == 1)
+    if (p.NRB == 1)
         launch_mfma<D, 1, 4>(p, a, s);
-    else if (p.NKS == 4)
+    else if (p.NRB == 2)
         launch_mfma<D, 2, 4>(p, a, s);
-    else if (p.NKS == 2)
-        launch_mfma<D, 2, 2>(p, a, s);
-    else
-        launch_mfma<D, 2, 1>(p, a, s);
+    else if (p.NRB == 4)
+        launch_mfma<D, 4, 2>(p, a, s);
+    else {
+        const unsigned grid = (unsigned)((long long)a.B * a.Hkv * p.RG * p.n_split);
+        hipLaunchKernelGGL((k_prefix_mfma_pipe<D>), dim3(grid), dim3(512), 0, s, a);
+    }
 }
 
 // Arguments of one tree_attention call after validation.
