@@ -37,8 +37,9 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kPtMax = 2048;        // page-table entries one split may span
-constexpr int kLdsStageBudget = 128 * 1024;
+constexpr int kPtMax = 1024;        // page-table entries one split may span
+constexpr int kLdsStageBudget = 144 * 1024;
+constexpr int kPipeStageKeys = 32;   // keys per stage of the pipelined kernel (32 or 64)
 
 __device__ inline float bf16_bits_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
@@ -429,41 +430,44 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
 // MFMA pipe works while the vector ALU computes exponentials; stages are 64
 // keys (two blocks), NBUF deep, with one workgroup barrier per stage.
 //
-// LDS layout of a stage (SK = 64 keys), chosen so that every operand read is
-// one per-lane base plus an immediate offset:
-//   K region: D/16 sub-regions kk (MFMA k steps), each SK keys x 32 bytes
-//     (channels 16 kk .. 16 kk + 15); the two 16-byte halves of a key's 32
-//     bytes are swapped when swk(key) = 1.
-//   V region: D/32 sub-regions t (32-channel tiles), each SK keys x 64 bytes
-//     holding channels [16t, 16t + 16) then [D/2 + 16t, D/2 + 16t + 16); the
-//     two 32-byte halves of a key's 64 bytes are swapped when swv(key) = 1.
-// Both swaps make the reads bank-conflict-free: 8 (or 16) consecutive keys of
-// a K read hit distinct 16-byte bank groups; the 4 keys x 32 bytes of a
-// transposing V read hit distinct 32-byte bank groups.
-// ---------------------------------------------------------------------------
-__device__ inline int swk(int key) { return ((key >> 2) ^ (key >> 3)) & 1; }
-__device__ inline int swv(int key) { return (key >> 1) & 1; }
+// LDS layout of a stage of SK keys.  The K and V regions are each a sequence of
+// 128-byte pieces [chunk group cg][key k]: piece (cg, k) holds the 16-byte
+// chunks 8 cg .. 8 cg + 7 of key k (one half row for D = 128), in the order
+//   K: chunk 8 cg + (pos ^ xk(k)) at position pos, xk(k) = (k ^ ((k >> 3) & 1)) & 7
+//   V: chunk 8 cg + (pos ^ yv(k, cg)) at position pos, yv = 2 ((k & 3) ^ (cg & 1))
+// A direct-to-LDS load therefore always reads whole 128-byte lines (8 lanes per
+// line, in permuted order, which still coalesces), and the operand reads are
+// bank-conflict-free with 32 or 64 banks: the 8 (16) keys of one K read land
+// on distinct 16-byte slots of a 128 (256) byte window, and the 4 keys x 32
+// bytes of a transposing V read, with the neighbouring 16-lane group, on
+// disjoint 32-byte slots.  Each lane reads through 4 precomputed K offsets
+// (one per k step mod 4) and 4 V offsets (one per channel tile); chunk group,
+// key chunk and block are immediates.
+__device__ inline int xk(int k) { return (k ^ ((k >> 3) & 1)) & 7; }
+__device__ inline int yv(int k, int cg) { return 2 * ((k & 3) ^ (cg & 1)); }
 
-template <int D>
+template <int D, int SK_>
 struct PipeCfg {
     static constexpr int WAVES = 8;
     static constexpr int THREADS = 64 * WAVES;
-    static constexpr int SK = 64;                 // keys per stage (2 blocks)
+    static constexpr int SK = SK_;                // keys per stage
+    static constexpr int BPS = SK / 32;           // 32-key blocks per stage
     static constexpr int KSTEPS = D / 16;
     static constexpr int DT = D / 32;
     static constexpr int KREG = SK * D * 2;       // bytes of the K region
     static constexpr int SB = 2 * KREG;           // stage bytes
     static constexpr int NBUF0 = kLdsStageBudget / SB;
-    static constexpr int NBUF = NBUF0 > 8 ? 8 : NBUF0;
+    static constexpr int NBUF = NBUF0 > 12 ? 12 : NBUF0;
     static constexpr int PF = NBUF - 2;           // stages in flight ahead of the current one
     static constexpr int LPS = SB / (THREADS * 16);
     static_assert(NBUF >= 3 && LPS >= 1 && SB % (THREADS * 16) == 0, "stage split");
     static_assert((PF - 1) * LPS < 64, "vmcnt range");
 };
 
-template <int D>
+template <int D, int SK_>
 __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
-    using C = PipeCfg<D>;
+    using C = PipeCfg<D, SK_>;
+    constexpr int BPS = C::BPS;
     constexpr int SK = C::SK, SB = C::SB, NBUF = C::NBUF, PF = C::PF, LPS = C::LPS,
                   THREADS = C::THREADS, KREG = C::KREG, KSTEPS = C::KSTEPS, DT = C::DT;
     constexpr int ROWS_WG = 256;
@@ -529,19 +533,10 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
     for (int i = 0; i < LPS; ++i) {
         const int slot = i * THREADS + tid;
         const bool vreg = (i * THREADS + w * 64) >= SK * (D / 8);   // wave-uniform
-        int key, dch;
-        if (!vreg) {
-            const int sk = slot;
-            const int kk = sk / (SK * 2), rem = sk % (SK * 2);
-            key = rem / 2;
-            dch = 2 * kk + ((rem & 1) ^ swk(key));
-        } else {
-            const int sv = slot - SK * (D / 8);
-            const int t = sv / (SK * 4), rem = sv % (SK * 4);
-            key = rem / 4;
-            const int c = (rem & 3) ^ (2 * swv(key));
-            dch = (c >> 1) * (D / 16) + 2 * t + (c & 1);
-        }
+        // slot -> (key, 16-byte chunk) of the piece layout described above
+        const int rs = vreg ? slot - SK * (D / 8) : slot;
+        const int cg = rs / (SK * 8), key = (rs / 8) % SK, pos = rs % 8;
+        const int dch = cg * 8 + (pos ^ (vreg ? yv(key, cg) : xk(key)));
         ld_key[i] = key;
         src_base[i] = (const uint16_t *)(vreg ? a.v : a.k) + (int64_t)g * a.stride_head + dch * 8;
     }
@@ -577,12 +572,19 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
             issue(st + PF);
     };
 
-    // per-lane operand offsets inside a stage
-    const uint32_t koff = l32 * 32 + ((hl ^ swk(l32)) * 16);
+    // per-lane operand offsets inside a stage (piece layout)
+    constexpr int CGB = SK * 128;            // bytes per chunk group
+    uint32_t koff[4], voff[DT];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        koff[q] = l32 * 128 + (((2 * q + hl) ^ xk(l32)) * 16);
     const int G16 = lane >> 4, a4 = lane & 3, j4 = (lane >> 2) & 3;
-    const uint32_t voff = KREG + (4 * (G16 >> 1) + j4) * 64 +
-                          (((2 * (G16 & 1) + (a4 >> 1)) ^ (2 * ((j4 >> 1) & 1))) * 16) +
-                          (a4 & 1) * 8;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+        const int c = (G16 & 1) * (D / 16) + 2 * t + (a4 >> 1);   // chunk of channels d0..d0+3
+        const int cg = c / 8, key = 4 * (G16 >> 1) + j4;
+        voff[t] = KREG + cg * CGB + key * 128 + (((c % 8) ^ yv(key, cg)) * 16) + (a4 & 1) * 8;
+    }
 
     f32x16 o[DT];
 #pragma unroll
@@ -594,11 +596,11 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
 
     // S^T of block u: keys [32 u, 32 u + 32) of the split
     auto qk = [&](int u) {
-        const char *kb = lds + ((u >> 1) % NBUF) * SB + (u & 1) * 1024 + koff;
+        const char *kb = lds + ((u / BPS) % NBUF) * SB + (u % BPS) * (32 * 128);
         f32x16 acc;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-            const bf16x8 ka = *(const bf16x8 *)(kb + kk * (SK * 32));
+            const bf16x8 ka = *(const bf16x8 *)(kb + (kk / 4) * CGB + koff[kk % 4]);
             if (kk == 0)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[kk], f32x16{}, 0, 0, 0);
             else
@@ -647,16 +649,16 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
     };
     // O^T += V^T P^T for block u (transposing V reads, see above)
     auto pv = [&](int u, const bf16x8 (&pb)[2]) {
-        const char *vb = lds + ((u >> 1) % NBUF) * SB + (u & 1) * 2048 + voff;
+        const char *vb = lds + ((u / BPS) % NBUF) * SB + (u % BPS) * (32 * 128);
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
-                const char *p = vb + t * (SK * 64) + cc * 1024;
+                const char *p = vb + voff[t] + cc * (16 * 128);
                 struct {
                     i16x4 lo, hi;
                 } pair{__builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p),
-                       __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(p + 512))};
+                       __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(p + 8 * 128))};
                 o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pair),
                                                                pb[cc], o[t], 0, 0, 0);
             }
@@ -671,8 +673,8 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
         // every block but the last is full: S of block u + 1 is computed
         // while the vector ALU turns S of block u into weights
         for (int u = 0; u + 1 < nb; ++u) {
-            if (((u + 1) & 1) == 0)
-                stage_ready((u + 1) >> 1);
+            if ((u + 1) % BPS == 0)
+                stage_ready((u + 1) / BPS);
             rescale_if_needed(s);
             bf16x8 pb[2];
             const f32x16 s_next = qk(u + 1);
@@ -973,7 +975,7 @@ Plan make_plan(tav_dtype dtype, int B, int R, int Hq, int Hkv, int D, int max_pr
         }
         const int rows_wg = p.NRB * 32;
         p.RG = (int)((M + rows_wg - 1) / rows_wg);
-        const int SK = p.NRB == 8 ? 64 : 32 * p.NKS;
+        const int SK = p.NRB == 8 ? kPipeStageKeys : 32 * p.NKS;
         const long long base = (long long)B * Hkv * p.RG;
         int n = base > 0 ? (int)((256 + base - 1) / base) : 1;
         const int by_stages = max_vis / (4 * SK);            // >= 4 stages per split
@@ -1056,7 +1058,7 @@ void launch_mfma_d(const Plan &p, const PrefixArgs &a, hipStream_t s) {
         launch_mfma<D, 4, 2>(p, a, s);
     else {
         const unsigned grid = (unsigned)((long long)a.B * a.Hkv * p.RG * p.n_split);
-        hipLaunchKernelGGL((k_prefix_mfma_pipe<D>), dim3(grid), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((k_prefix_mfma_pipe<D, kPipeStageKeys>), dim3(grid), dim3(512), 0, s, a);
     }
 }
 
