@@ -14,6 +14,9 @@ stream it runs on.  `cpu_baseline` times the CPU fp64 oracle on a bounded
 sample of rows of the same workload.
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -32,6 +35,94 @@ from tree_attention_verify_amd import inputs as gen  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "tree-verify attention KV GB/s + rows/s, % of MI355X HBM peak at long ctx"
+KERNEL_SRC = os.path.join(ROOT, "tree_attention_verify_amd", "csrc", "tree_attention.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 1 << 30          # plain copy used to calibrate the HBM byte counters
+PREFIX_KERNEL = "k_prefix_mfma"
+COPY_KERNEL = "copyBuffer"
+
+
+def kernel_hash():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(workload):
+    """HBM bytes per prefix launch from the committed counter summary, or None
+    when it is missing or the kernel source changed since it was taken."""
+    f = os.path.join(PROFILES, "%s_prefix_traffic.json" % workload)
+    if not os.path.exists(f):
+        return None
+    t = json.load(open(f))
+    if t.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return t
+
+
+def _csv_rows(pattern):
+    rows = []
+    for f in glob.glob(pattern, recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def summarize_traffic(workload, fetch_dir, write_dir, cmd):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the prefix kernel, each
+    scaled by what the same counter reads for a plain 1 GiB copy."""
+    def avg(rows, counter, name_has, largest=False):
+        v = [float(r["Counter_Value"]) for r in rows
+             if r["Counter_Name"] == counter and name_has in r["Kernel_Name"]]
+        if largest and v:   # the 1 GiB calibration copies, not smaller copies of the run
+            v = [x for x in v if x >= 0.9 * max(v)]
+        return sum(v) / len(v) if v else float("nan"), len(v)
+    fr = _csv_rows(os.path.join(fetch_dir, "**", "*counter_collection.csv"))
+    wr = _csv_rows(os.path.join(write_dir, "**", "*counter_collection.csv"))
+    pf, npf = avg(fr, "FETCH_SIZE", PREFIX_KERNEL)
+    pw, npw = avg(wr, "WRITE_SIZE", PREFIX_KERNEL)
+    cf, ncf = avg(fr, "FETCH_SIZE", COPY_KERNEL, largest=True)
+    cw, ncw = avg(wr, "WRITE_SIZE", COPY_KERNEL, largest=True)
+    f_scale = COPY_BYTES / (cf * 1024.0)
+    w_scale = COPY_BYTES / (cw * 1024.0)
+    wl = gen.WORKLOADS[workload]
+    P_vis = min(wl.P, wl.prefix_window) if wl.prefix_window else wl.P
+    e = 2 if wl.dtype == "bf16" else 4
+    algo = kv_bytes(wl, P_vis, with_window=False) + wl.B * wl.R * wl.Hq * wl.D * e
+    t = {"workload": workload, "kernel_source_sha256_16": kernel_hash(),
+         "prefix_fetch_kib_per_dispatch": pf, "prefix_write_kib_per_dispatch": pw,
+         "copy_fetch_kib_per_dispatch": cf, "copy_write_kib_per_dispatch": cw,
+         "copy_bytes_each_way": COPY_BYTES, "fetch_scale": f_scale, "write_scale": w_scale,
+         "prefix_read_bytes": pf * 1024 * f_scale, "prefix_write_bytes": pw * 1024 * w_scale,
+         "prefix_traffic_bytes": pf * 1024 * f_scale + pw * 1024 * w_scale,
+         "prefix_algorithmic_bytes": algo, "dispatches": [npf, npw, ncf, ncw], "command": cmd}
+    os.makedirs(PROFILES, exist_ok=True)
+    json.dump(t, open(os.path.join(PROFILES, "%s_prefix_traffic.json" % workload), "w"), indent=1)
+    with open(os.path.join(PROFILES, "%s_prefix_traffic.md" % workload), "w") as f:
+        f.write("# HBM traffic of the split-K prefix kernel, workload %s\n\n" % workload)
+        f.write("Command (FETCH_SIZE pass, then the same with WRITE_SIZE):\n\n    %s\n\n" % cmd)
+        f.write("| counter | prefix kernel (KiB/dispatch) | 1 GiB copy (KiB/dispatch) | scale |\n|---|---|---|---|\n")
+        f.write("| FETCH_SIZE | %.0f | %.0f | %.4f |\n" % (pf, cf, f_scale))
+        f.write("| WRITE_SIZE | %.0f | %.0f | %.4f |\n\n" % (pw, cw, w_scale))
+        f.write("Scaled HBM bytes per launch: read %.4g, write %.4g, total %.4g; algorithmic "
+                "bytes %.4g (ratio %.3f).  Kernel source sha256[:16] %s.\n"
+                % (t["prefix_read_bytes"], t["prefix_write_bytes"], t["prefix_traffic_bytes"],
+                   algo, t["prefix_traffic_bytes"] / algo, t["kernel_source_sha256_16"]))
+    print(json.dumps(t))
+
+
+def summarize_stats(workload, stats_dir, cmd):
+    rows = _csv_rows(os.path.join(stats_dir, "**", "*kernel_stats.csv"))
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, "%s_kernel_stats.md" % workload)
+    with open(out, "w") as f:
+        f.write("# rocprofv3 kernel statistics, workload %s\n\nCommand:\n\n    %s\n\n" % (workload, cmd))
+        f.write("| kernel | calls | average (us) | min (us) | max (us) | share |\n|---|---|---|---|---|---|\n")
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+            name = r["Name"]
+            name = name if len(name) < 90 else name[:87] + "..."
+            f.write("| %s | %s | %.1f | %.1f | %.1f | %.1f%% |\n" % (
+                name.replace("|", "/"), r["Calls"], float(r["AverageNs"]) / 1e3,
+                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+        f.write("\nKernel source sha256[:16] %s.\n" % kernel_hash())
+    print(open(out).read())
 
 
 def log(*a):
@@ -164,7 +255,19 @@ def main():
     ap.add_argument("--seed", type=int, default=4)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB copy (calibrates FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "CMD"),
+                    help="write profiles/<workload>_prefix_traffic.{json,md} from rocprofv3 CSVs")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_DIR", "CMD"),
+                    help="write profiles/<workload>_kernel_stats.md from rocprofv3 --stats CSVs")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(args.workload, *args.summarize_traffic)
+        return
+    if args.summarize_stats:
+        summarize_stats(args.workload, *args.summarize_stats)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -201,6 +304,14 @@ def main():
         "(min %.3f max %.3f)" % (args.steps, ms_step, t_host * 1e3 / args.steps, prefix_avg,
                                  min(prefix_ms), max(prefix_ms)))
 
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     masks_np = step.masks.cpu().numpy().view(np.uint64)
     P_vis = min(wl.P, wl.prefix_window) if wl.prefix_window else wl.P
     kvb = kv_bytes(wl, P_vis)
@@ -227,12 +338,17 @@ def main():
         "attention_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "roofline": {"kernel": "k_prefix_mfma (split-K prefix)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": prefix_bytes,
                      "avg_launch_ms": round(prefix_avg, 4),
                      "mfma_tflops": round(prefix_flops / (prefix_avg * 1e-3) / 1e12, 1),
                      "mfma_frac": round(prefix_flops / (prefix_avg * 1e-3) / 1e12
                                         / MFMA_BF16_PEAK_TFS, 4)},
     }
+    t = traffic_for(wl.name)
+    if t is not None:
+        res["roofline"]["traffic"] = round(t["prefix_traffic_bytes"])
+        res["roofline"]["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     if args.cpu_budget > 0:
         log("cpu baseline (oracle), budget %.0f s" % args.cpu_budget)
         res["cpu_baseline"] = cpu_baseline(wl, inp, masks_np, args.cpu_budget)

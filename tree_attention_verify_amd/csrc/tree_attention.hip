@@ -39,7 +39,7 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kPtMax = 1024;        // page-table entries one split may span
 constexpr int kLdsStageBudget = 144 * 1024;
-constexpr int kPipeStageKeys = 32;   // keys per stage of the pipelined kernel (32 or 64)
+constexpr int kPipeStageKeys = 64;   // keys per stage of the pipelined kernel (32 or 64)
 
 __device__ inline float bf16_bits_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
