@@ -121,7 +121,9 @@ def summarize_stats(workload, stats_dir, cmd):
             f.write("| %s | %s | %.1f | %.1f | %.1f | %.1f%% |\n" % (
                 name.replace("|", "/"), r["Calls"], float(r["AverageNs"]) / 1e3,
                 float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
-        f.write("\nKernel source sha256[:16] %s.\n" % kernel_hash())
+        f.write("\nThe at::native and __amd_rocclr kernels are the seeded input generation and "
+                "host-to-device copies before the timed region; the prefix kernel's calls "
+                "include the warm-up steps.  Kernel source sha256[:16] %s.\n" % kernel_hash())
     print(open(out).read())
 
 

@@ -125,7 +125,8 @@ size_t tree_attention_workspace_size(tav_dtype dtype, int32_t B, int32_t R, int3
  *            channel d) at page*stride_page + g*stride_head + s*stride_token + d
  *            (strides in elements; channels contiguous; e.g. HND
  *            [pages][Hkv][page_size][D] or NHD [pages][page_size][Hkv][D]).
- *            Pointers and strides must give 16-byte aligned rows.
+ *            Pointers and strides must give 16-byte aligned rows, and
+ *            stride_token must be below 2^27 bytes.
  * num_pages  pages in each pool; page-table entries outside [0, num_pages)
  *            are clamped into it (memory-safe, results for that key undefined)
  * page_table int32 [B][max_pages]: logical position t of request b lives in

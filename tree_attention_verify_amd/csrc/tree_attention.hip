@@ -81,8 +81,11 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // for every such load in flight (vmcnt(0)), which would serialise the stage
 // pipeline.  Completion is established explicitly: wait_vmcnt<N>() for the
 // issuing wave, then a workgroup barrier.  lds_base must be wave-uniform.
+// Pages are read once per call, so the loads carry the non-temporal hint:
+// streaming them past the caches costs less energy per byte, and the chip
+// runs this kernel at its board power limit.
 __device__ __forceinline__ void dma_load16(const void *src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                  :
                  : "v"(src), "s"(lds_base)
                  : "memory", "m0");
@@ -425,10 +428,19 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
 
 // ---------------------------------------------------------------------------
 // Software-pipelined prefix kernel for wide row groups (256 folded rows:
-// 8 waves x 32 rows, every wave reads every key).  Per 32-key block u a wave
-// issues the S MFMAs of block u + 1 before the softmax of block u, so the
-// MFMA pipe works while the vector ALU computes exponentials; stages are 64
-// keys (two blocks), NBUF deep, with one workgroup barrier per stage.
+// 8 waves x 32 rows, every wave reads every key).  Stages are 64 keys, NBUF
+// deep, with one workgroup barrier per stage.  Per 32-key block u a wave
+// issues the O^T += V^T P^T MFMAs of block u - 1 interleaved with the softmax
+// weights of block u, then the S MFMAs of block u + 1, so the MFMA pipe
+// works while the vector ALU computes exponentials (two waves per SIMD fill
+// each other's gaps); each MFMA operand is read from LDS one phase ahead of
+// its use.
+// The softmax reference max mu is taken from the first block and raised only
+// when the running sum of weights would pass kSumLimit (rare): weights are
+// bf16 with the fp32 exponent range and accumulate in fp32, so their
+// magnitude costs no precision, and the common path needs no per-block row
+// max.  A weight sum of at least 1 (the key that set mu) keeps every weight
+// that underflows below 2^-126 negligible.
 //
 // LDS layout of a stage of SK keys.  The K and V regions are each a sequence of
 // 128-byte pieces [chunk group cg][key k]: piece (cg, k) holds the 16-byte
@@ -443,8 +455,27 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
 // disjoint 32-byte slots.  Each lane reads through 4 precomputed K offsets
 // (one per k step mod 4) and 4 V offsets (one per channel tile); chunk group,
 // key chunk and block are immediates.
+//
+// Loads: every load instruction covers all SK keys of one chunk group, wave w
+// taking keys 8 w .. 8 w + 7 of the stage.  With pages of 8 or more keys those
+// 8 keys share one page, so the page base is wave-uniform (scalar registers)
+// and a lane only adds a fixed 32-bit offset: stages then start at the 8-key
+// boundary at or below the split start, and keys outside [lo, hi) are neither
+// loaded nor visible.  Smaller pages take a per-lane page lookup.
 __device__ inline int xk(int k) { return (k ^ ((k >> 3) & 1)) & 7; }
 __device__ inline int yv(int k, int cg) { return 2 * ((k & 3) ^ (cg & 1)); }
+
+constexpr float kSumLimit = 1048576.f;   // 2^20
+
+// Direct-to-LDS 16-byte load with a wave-uniform 64-bit base and a per-lane
+// 32-bit byte offset; lane i's 16 bytes land at LDS byte lds_base + 16 i.
+// Completion is tracked as for dma_load16.
+__device__ __forceinline__ void dma_load16_s(const void *base, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds_base)
+                 : "memory", "m0");
+}
 
 template <int D, int SK_>
 struct PipeCfg {
@@ -460,6 +491,8 @@ struct PipeCfg {
     static constexpr int NBUF = NBUF0 > 12 ? 12 : NBUF0;
     static constexpr int PF = NBUF - 2;           // stages in flight ahead of the current one
     static constexpr int LPS = SB / (THREADS * 16);
+    static_assert(THREADS == SK * 8, "one load instruction covers every key of a stage");
+    static_assert(BPS == 2, "block u + 2 starts a stage exactly when u is even");
     static_assert(NBUF >= 3 && LPS >= 1 && SB % (THREADS * 16) == 0, "stage split");
     static_assert((PF - 1) * LPS < 64, "vmcnt range");
 };
@@ -497,12 +530,15 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
     const int b = unit / (a.n_split * a.Hkv);
 
     const KeyRange kr = split_range(a, b, split);
-    const int nkeys = kr.hi - kr.lo;
+    const bool wave_pages = a.ps_shift >= 3;
+    // stages cover [kb0, hi); kb0 is in the page of lo
+    const int kb0 = wave_pages ? (kr.lo & ~7) : kr.lo;
+    const int nkeys = kr.hi > kr.lo ? kr.hi - kb0 : 0;
     const int ns = (nkeys + SK - 1) / SK;
     const int nb = (nkeys + 31) / 32;
     const int rows_base = rg * ROWS_WG + w * 32;
 
-    const int lp0 = nkeys > 0 ? (kr.lo >> a.ps_shift) : 0;
+    const int lp0 = nkeys > 0 ? (kb0 >> a.ps_shift) : 0;
     const int npt = nkeys > 0 ? ((kr.hi - 1) >> a.ps_shift) - lp0 + 1 : 0;
     for (int i = tid; i < npt && i < kPtMax; i += THREADS)
         pt[i] = (int32_t)clamp_page(a.page_table[(int64_t)b * a.max_pages + lp0 + i], a.num_pages);
@@ -524,38 +560,55 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
     }
     __syncthreads();
 
-    // loader roles (fixed): load i fills stage slot i * THREADS + tid
+    // Loader roles (fixed): load i of a stage fills LDS slot i * THREADS + tid,
+    // i.e. chunk group cg(i), key 8 w + (lane >> 3), position lane & 7.
     const int ps_mask = (1 << a.ps_shift) - 1;
     const uint32_t lds0 = lds_off(lds);
-    const uint16_t *src_base[LPS];
-    int ld_key[LPS];
+    const int key_l = lane >> 3;
+    const int wkey = 8 * w + key_l;
+    // element offset of this lane's 16-byte chunk within its key's row, per load
+    auto chunk = [&](int i) {
+        const bool vreg = i * THREADS >= SK * (D / 8);
+        const int cg = (vreg ? i * THREADS - SK * (D / 8) : i * THREADS) / (SK * 8);
+        return cg * 8 * 8 + ((lane & 7) ^ (vreg ? yv(wkey, cg) : xk(wkey))) * 8;
+    };
+    uint32_t ld_off[LPS];   // byte offsets of this lane's chunks from its key's row
 #pragma unroll
-    for (int i = 0; i < LPS; ++i) {
-        const int slot = i * THREADS + tid;
-        const bool vreg = (i * THREADS + w * 64) >= SK * (D / 8);   // wave-uniform
-        // slot -> (key, 16-byte chunk) of the piece layout described above
-        const int rs = vreg ? slot - SK * (D / 8) : slot;
-        const int cg = rs / (SK * 8), key = (rs / 8) % SK, pos = rs % 8;
-        const int dch = cg * 8 + (pos ^ (vreg ? yv(key, cg) : xk(key)));
-        ld_key[i] = key;
-        src_base[i] = (const uint16_t *)(vreg ? a.v : a.k) + (int64_t)g * a.stride_head + dch * 8;
-    }
+    for (int i = 0; i < LPS; ++i)
+        ld_off[i] = (uint32_t)(chunk(i) * 2);
+    const uint32_t lane_tok = (uint32_t)(key_l * a.stride_token * 2);
     auto issue = [&](int st) {
-        const uint32_t sbase = lds0 + (uint32_t)((st % NBUF) * SB);
-        const int key_base = kr.lo + st * SK;
-        int64_t page[LPS];
+        const uint32_t sbase = lds0 + (uint32_t)((st % NBUF) * SB) + w * 64 * 16;
+        const int k0 = kb0 + st * SK + 8 * w;   // this wave's first key (wave-uniform)
+        if (k0 >= kr.hi)
+            return;
+        const int t = k0 + key_l;
+        const bool in = (k0 >= kr.lo && k0 + 8 <= kr.hi) || (t >= kr.lo && t < kr.hi);
+        if (wave_pages) {
+            const int64_t pg = __builtin_amdgcn_readfirstlane(pt[(k0 >> a.ps_shift) - lp0]);
+            const int64_t off = pg * a.stride_page + (int64_t)g * a.stride_head +
+                                (int64_t)(k0 & ps_mask) * a.stride_token;
+            const uint16_t *kp = (const uint16_t *)a.k + off;
+            const uint16_t *vp = (const uint16_t *)a.v + off;
+            if (in) {
 #pragma unroll
-        for (int i = 0; i < LPS; ++i) {
-            const int t = key_base + ld_key[i];
-            page[i] = t < kr.hi ? pt[(t >> a.ps_shift) - lp0] : 0;
-        }
+                for (int i = 0; i < LPS; ++i) {
+                    const bool vreg = i * THREADS >= SK * (D / 8);
+                    dma_load16_s(vreg ? vp : kp, lane_tok + ld_off[i], sbase + i * THREADS * 16);
+                }
+            }
+        } else {
+            const int64_t page = in ? pt[(t >> a.ps_shift) - lp0] : 0;
+            const int64_t off = page * a.stride_page + (int64_t)g * a.stride_head +
+                                (int64_t)(t & ps_mask) * a.stride_token;
+            if (in) {
 #pragma unroll
-        for (int i = 0; i < LPS; ++i) {
-            const int t = key_base + ld_key[i];
-            if (t < kr.hi)
-                dma_load16(src_base[i] + page[i] * a.stride_page +
-                               (int64_t)(t & ps_mask) * a.stride_token,
-                           __builtin_amdgcn_readfirstlane(sbase + (i * THREADS + w * 64) * 16));
+                for (int i = 0; i < LPS; ++i) {
+                    const bool vreg = i * THREADS >= SK * (D / 8);
+                    dma_load16((const uint16_t *)(vreg ? a.v : a.k) + off + chunk(i),
+                               sbase + i * THREADS * 16);
+                }
+            }
         }
     };
     // Stage st is complete once at most the loads of the later, full stages
@@ -592,66 +645,20 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             o[t][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    float mu = 0.f;      // reference max of the weights (exp2 domain, finite)
+    float l_run = 0.f;
 
-    // S^T of block u: keys [32 u, 32 u + 32) of the split
-    auto qk = [&](int u) {
-        const char *kb = lds + ((u / BPS) % NBUF) * SB + (u % BPS) * (32 * 128);
-        f32x16 acc;
+    auto block_base = [&](int u) { return lds + ((u / BPS) % NBUF) * SB + (u % BPS) * (32 * 128); };
+    auto load_k = [&](int u, bf16x8 (&ka)[KSTEPS]) {
+        const char *kb = block_base(u);
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-            const bf16x8 ka = *(const bf16x8 *)(kb + (kk / 4) * CGB + koff[kk % 4]);
-            if (kk == 0)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[kk], f32x16{}, 0, 0, 0);
-            else
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[kk], acc, 0, 0, 0);
-        }
-        return acc;
+        for (int kk = 0; kk < KSTEPS; ++kk)
+            ka[kk] = *(const bf16x8 *)(kb + (kk / 4) * CGB + koff[kk % 4]);
     };
-
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-    // Softmax of block u from its S^T, in the exp2 domain, returning the P^T
-    // operand.  The running max is only raised when a block exceeds it by
-    // more than 2^8, so rescaling O is rare and weights stay <= 256.
-    auto rescale_if_needed = [&](const f32x16 &sv) {
-        float mx = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+    auto load_v = [&](int u, bf16x8 (&va)[DT][2]) {
+        const char *vb = block_base(u);
 #pragma unroll
-        for (int r = 3; r < 16; ++r)
-            mx = fmaxf(mx, sv[r]);
-        mx = pair_max(mx);
-        const float mb = mx * a.c;
-        if (__ballot(mb > m_run + 8.f)) {
-            const float mnew = fmaxf(m_run, mb);
-            const float alpha = fast_exp2(m_run - mnew);  // 0 when m_run = -inf
-            l_run *= alpha;
-#pragma unroll
-            for (int t = 0; t < DT; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    o[t][r] *= alpha;
-            m_run = mnew;
-        }
-    };
-    auto weights = [&](const f32x16 &sv, bf16x8 (&pb)[2]) {
-        const float mu = m_run == -INFINITY ? 0.f : m_run;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            pb[r >> 3][r & 7] = (__bf16)fast_exp2(fmaf(sv[r], a.c, -mu));
-        // the row sum adds the bf16 weights the MFMA multiplies
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bf16x2 pr = {pb[cc][2 * e], pb[cc][2 * e + 1]};
-                l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
-            }
-    };
-    // O^T += V^T P^T for block u (transposing V reads, see above)
-    auto pv = [&](int u, const bf16x8 (&pb)[2]) {
-        const char *vb = lds + ((u / BPS) % NBUF) * SB + (u % BPS) * (32 * 128);
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
+        for (int t = 0; t < DT; ++t)
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 const char *p = vb + voff[t] + cc * (16 * 128);
@@ -659,9 +666,102 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
                     i16x4 lo, hi;
                 } pair{__builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p),
                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(p + 8 * 128))};
-                o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pair),
-                                                               pb[cc], o[t], 0, 0, 0);
+                va[t][cc] = __builtin_bit_cast(bf16x8, pair);
             }
+    };
+    // S^T of one block: keys x rows, lane l holding row l % 32
+    auto qk = [&](const bf16x8 (&ka)[KSTEPS]) {
+        f32x16 acc;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qv[kk], kk ? acc : f32x16{}, 0, 0, 0);
+        return acc;
+    };
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    // bf16 weights of one block and their sum (the values the MFMA multiplies)
+    auto weights = [&](const f32x16 &sv, bf16x8 (&pb)[2], float &lb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            pb[r >> 3][r & 7] = (__bf16)fast_exp2(fmaf(sv[r], a.c, -mu));
+        float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            l0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[0][2 * e], pb[0][2 * e + 1]}, ones, l0, false);
+            l1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[1][2 * e], pb[1][2 * e + 1]}, ones, l1, false);
+        }
+        lb = l0 + l1;
+    };
+    auto row_max = [&](const f32x16 &sv) {
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+#pragma unroll
+        for (int r = 3; r < 16; ++r)
+            mx = fmaxf(mx, sv[r]);
+        return pair_max(mx) * a.c;
+    };
+    // Raise the reference to this block's row max, rescale what has been
+    // accumulated, and recompute the block's weights.
+    auto rebase = [&](const f32x16 &sv, bf16x8 (&pb)[2], float &lb) {
+        const float mx = row_max(sv);
+        const float mnew = mx < INFINITY ? fmaxf(mu, mx) : mu;
+        const float alpha = fast_exp2(mu - mnew);
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                o[t][r] *= alpha;
+        mu = mnew;
+        weights(sv, pb, lb);
+    };
+    // rebase when the running sum would pass kSumLimit, then count the block
+    auto check = [&](const f32x16 &sv, bf16x8 (&pb)[2], float lb) {
+        if (__ballot(!(l_run + lb <= kSumLimit)))
+            rebase(sv, pb, lb);
+        l_run += lb;
+    };
+    // O^T += V^T P^T for one block
+    auto pv = [&](const bf16x8 (&va)[DT][2], const bf16x8 (&pb)[2]) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+                o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t][cc], pb[cc], o[t], 0, 0, 0);
+    };
+    // scores of keys outside [lo, hi) of the split become -inf (block u)
+    auto mask_block = [&](f32x16 &sv, int u) {
+        const int k0 = kb0 + u * 32 + 4 * hl;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 8 * (r >> 2) + (r & 3);
+            if (key < kr.lo || key >= kr.hi)
+                sv[r] = -INFINITY;
+        }
+    };
+
+    // One block u (1 <= u <= nb - 2).  Phase 1: O accumulates block u - 1 on
+    // the MFMA pipe while the vector ALU turns S of block u into weights.
+    // Phase 2: the V operands of block u are read, S of block u + 1 runs on
+    // the MFMA pipe (into the registers S of block u has left), and the K
+    // operands of block u + 2 are read.  Each LDS read lands during the
+    // other phase; the two waves of a SIMD fill each other's gaps.  Every
+    // block but the last is full.
+    auto step = [&](int u, f32x16 &s, const bf16x8 (&pb_prev)[2], bf16x8 (&pb_cur)[2],
+                    bool new_stage, bf16x8 (&ka)[KSTEPS], bf16x8 (&va)[DT][2]) {
+        float lb;
+        pv(va, pb_prev);
+        weights(s, pb_cur, lb);
+#pragma unroll
+        for (int i = 0; i < 2 * DT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // O MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);    // weights VALU
+        }
+        check(s, pb_cur, lb);
+        load_v(u, va);
+        s = qk(ka);
+        if (u + 2 < nb) {
+            if (new_stage)
+                stage_ready((u + 2) / BPS);
+            load_k(u + 2, ka);
         }
     };
 
@@ -669,38 +769,57 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
         issue(st);
     if (nb > 0) {
         stage_ready(0);
-        f32x16 s = qk(0);
-        // every block but the last is full: S of block u + 1 is computed
-        // while the vector ALU turns S of block u into weights
-        for (int u = 0; u + 1 < nb; ++u) {
-            if ((u + 1) % BPS == 0)
-                stage_ready((u + 1) / BPS);
-            rescale_if_needed(s);
-            bf16x8 pb[2];
-            const f32x16 s_next = qk(u + 1);
-            weights(s, pb);
-#pragma unroll
-            for (int i = 0; i < KSTEPS; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // K operand read
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // S MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // weights VALU
+        bf16x8 ka[KSTEPS], va[DT][2], pa[2], pbb[2];
+        f32x16 s;
+        load_k(0, ka);
+        s = qk(ka);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nb > 1)
+            load_k(1, ka);   // block 1 is in stage 0
+        mask_block(s, 0);
+        mu = row_max(s);
+        mu = fabsf(mu) < INFINITY ? mu : 0.f;
+        if (nb == 1) {
+            float lb;
+            load_v(0, va);
+            weights(s, pa, lb);
+            check(s, pa, lb);
+            pv(va, pa);
+        } else {
+            {
+                // block 0 (no O work yet)
+                float lb;
+                weights(s, pa, lb);
+                check(s, pa, lb);
+                load_v(0, va);
+                s = qk(ka);
+                if (nb > 2) {
+                    stage_ready(1);
+                    load_k(2, ka);
+                }
             }
-            pv(u, pb);
-            s = s_next;
+            // blocks 1 .. nb - 2, two per trip so that the weight registers
+            // alternate roles without copies; block u + 2 starts a stage
+            // exactly when u is even
+            int u = 1;
+            for (; u + 1 <= nb - 2; u += 2) {
+                step(u, s, pa, pbb, false, ka, va);
+                step(u + 1, s, pbb, pa, true, ka, va);
+            }
+            if (u == nb - 2) {
+                step(u, s, pa, pbb, false, ka, va);
+                pa[0] = pbb[0];
+                pa[1] = pbb[1];
+            }
+            // the last block may be partial: keys past the split are not visible
+            float lb;
+            pv(va, pa);
+            mask_block(s, nb - 1);
+            weights(s, pbb, lb);
+            check(s, pbb, lb);
+            load_v(nb - 1, va);
+            pv(va, pbb);
         }
-        // the last block may be partial: keys past the split are not visible
-        const int u = nb - 1;
-        const int lim = kr.hi - (kr.lo + u * 32);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (key >= lim)
-                s[r] = -INFINITY;
-        }
-        rescale_if_needed(s);
-        bf16x8 pb[2];
-        weights(s, pb);
-        pv(u, pb);
     }
 
     const int sidx = split;
@@ -721,7 +840,7 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
                 *(float4 *)(dst + d) = v4;
             }
         if (hl == 0)
-            a.ws_lse[row * a.S + sidx] = has_keys(lt) ? m_run + __log2f(lt) : -INFINITY;
+            a.ws_lse[row * a.S + sidx] = has_keys(lt) ? mu + __log2f(lt) : -INFINITY;
     }
 }
 
@@ -1098,6 +1217,8 @@ tav_status prepare(const char *fn, int phase, Call &call, const void *q, const v
     c.need((stride_page * esz) % 16 == 0 && (stride_head * esz) % 16 == 0 &&
                (stride_token * esz) % 16 == 0,
            TAV_ERR_UNSUPPORTED, "K/V strides must be multiples of 16 bytes");
+    c.need(stride_token * esz < (1LL << 27), TAV_ERR_UNSUPPORTED,
+           "stride_token must be below 2^27 bytes");
     if (B > 0) {
         c.need(q && k_cache && v_cache, TAV_ERR_INVALID_ARG, "q, k_cache and v_cache must be set");
         c.need(page_table && prefix_len, TAV_ERR_INVALID_ARG, "page_table and prefix_len must be set");
