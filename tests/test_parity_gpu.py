@@ -102,6 +102,11 @@ SMALL = {
                  [777, 100]),
     "f32_d128": (W_["worked"].with_(name="f32", B=2, P=300, N=8, Hq=8, Hkv=4, D=128,
                                     tree="random", depth_cap=4), [300, 17]),
+    # 512 folded rows and one split: the window kernel merges and writes the output
+    "onesplit512": (W_["long64"].with_(name="onesplit512", B=2, P=500, N=64, Hq=32, Hkv=4,
+                                       page_size=16), [500, 131]),
+    # W = 33: a second, mostly empty 32-key window block
+    "w33": (W_["random16"].with_(name="w33", B=2, P=640, N=33, depth_cap=5), [640, 90]),
 }
 
 
@@ -248,6 +253,50 @@ def test_nan_in_node_leaks_only_to_descendants():
             else:
                 assert np.isfinite(o[0, r, h]).all()
                 assert np.abs(o[0, r, h] - ro[0, r, h]).max() <= OUT_TOL
+
+
+def _same_nonfinite(ours, ref, tol, tag):
+    """Element-wise: where the oracle is finite, ours is finite and within tol;
+    where it is NaN / +inf / -inf, ours is the same."""
+    assert np.array_equal(np.isnan(ours), np.isnan(ref)), tag + ": NaN pattern"
+    assert np.array_equal(np.isposinf(ours), np.isposinf(ref)), tag + ": +inf pattern"
+    assert np.array_equal(np.isneginf(ours), np.isneginf(ref)), tag + ": -inf pattern"
+    fin = np.isfinite(ref)
+    if fin.any():
+        assert np.abs(ours[fin] - ref[fin]).max() <= tol, tag
+
+
+@pytest.mark.parametrize("shape", ["rows64", "rows512"])
+def test_nonfinite_window_values_reach_only_rows_that_see_them(shape):
+    # window K NaN at node j1, V NaN at one channel of j2, V +inf and -inf at
+    # one channel of j3 and j4: a row is non-finite exactly where the exact
+    # softmax over its own visible keys is
+    if shape == "rows64":
+        wl = gen.Workload("nfw", 1, 200, 16, 8, 2, 128, "bf16", 16, "random", depth_cap=4)
+    else:
+        wl = gen.Workload("nfw", 2, 300, 64, 16, 2, 128, "bf16", 16, "random", depth_cap=6)
+    inp = gen.make_inputs(wl, 9, "cuda")
+
+    def slot(j):
+        t = int(inp.prefix_len[0]) + j
+        return int(inp.page_table[0, t // wl.page_size]), t % wl.page_size
+
+    j1, j2, j3, j4 = 3, 5, 6, 9
+    pg, sl = slot(j1)
+    inp.k_cache[pg, 0, sl] = float("nan")
+    pg, sl = slot(j2)
+    inp.v_cache[pg, 0, sl, 5] = float("nan")
+    pg, sl = slot(j3)
+    inp.v_cache[pg, 0, sl, 77] = float("inf")
+    pg, sl = slot(j4)
+    inp.v_cache[pg, 0, sl, 77] = float("-inf")
+    m = oracle.build_masks(inp.parents)["masks"]
+    out, lse = run_attention(inp, dev(m.view(np.int64), torch.int64))
+    ro, rl = oracle_attention(inp, m)
+    _same_nonfinite(out.float().cpu().numpy(), ro.reshape(out.shape), OUT_TOL, shape + " out")
+    _same_nonfinite(lse.cpu().numpy(), rl.reshape(lse.shape), LSE_TOL, shape + " lse2")
+    sees = lambda j: ((m[0].astype(np.uint64) >> np.uint64(j)) & np.uint64(1)).astype(bool)
+    assert sees(j1).any() and sees(j2).any() and sees(j3).any(), "the tree must reach the poisoned nodes"
 
 
 def test_bad_trees_flagged():

@@ -677,17 +677,19 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qv[kk], kk ? acc : f32x16{}, 0, 0, 0);
         return acc;
     };
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     // bf16 weights of one block and their sum (the values the MFMA multiplies)
     auto weights = [&](const f32x16 &sv, bf16x8 (&pb)[2], float &lb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            pb[r >> 3][r & 7] = (__bf16)fast_exp2(fmaf(sv[r], a.c, -mu));
+        // the sum is taken over the fp32 weights: with few dominant keys the
+        // bf16 rounding of the MFMA operand would not average out of lse2
         float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            l0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[0][2 * e], pb[0][2 * e + 1]}, ones, l0, false);
-            l1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[1][2 * e], pb[1][2 * e + 1]}, ones, l1, false);
+        for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(fmaf(sv[r], a.c, -mu));
+            pb[r >> 3][r & 7] = (__bf16)p;
+            if (r & 1)
+                l1 += p;
+            else
+                l0 += p;
         }
         lb = l0 + l1;
     };
@@ -934,10 +936,10 @@ struct MergeArgs {
     const int32_t *prefix_len;
     int32_t max_prefix_len;
     const uint64_t *masks;
-    int32_t W, B, R, Hq, G, D, S;
+    int32_t W, B, R, Hq, Hkv, G, D, S;
     float c;
-    const float *ws_o;
-    const float *ws_lse;
+    float *ws_o;     // partials [row][S][D]; the window kernel writes the last slot
+    float *ws_lse;
     void *out;
     float *lse2;
 };
@@ -1057,6 +1059,342 @@ __global__ void __launch_bounds__(256) k_window_merge(MergeArgs a) {
         a.lse2[row] = res_lse;
 }
 
+
+// Window part and merge for bf16 on MFMA.  One workgroup of NW waves per
+// (request b, kv head g, group of 32 NW folded rows); a wave owns 32 rows.
+// The W window keys of (b, g) (logical positions P .. P + W - 1) are staged
+// in LDS, S^T = K_w Q^T and O^T = V_w^T P^T run on v_mfma_f32_32x32x16_bf16
+// with each row's ancestor mask applied to the scores, and the window's
+// (o, lse2) is merged with the S prefix partials of the row:
+// lse2 = log2 sum_k 2^lse2_k, out = sum_k 2^(lse2_k - lse2) o_k.
+//
+// A window key is shared by every row of the tile, so a non-finite V value
+// of a key that a row cannot see would otherwise reach it as 0 * inf.  Such
+// values are set to 0 in LDS and their keys flagged; a row that sees a
+// flagged key then adds, per channel, the sum of the non-finite values of
+// its visible flagged keys to its window output, which is what the exact
+// weighted sum gives (positive weights keep infinities and NaN).
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW) k_window_mfma(MergeArgs a) {
+    constexpr int KSTEPS = D / 16, DT = D / 32, CH = D / 8, ROWB = D * 2;
+    constexpr int THREADS = 64 * NW;
+    __shared__ __attribute__((aligned(16))) char kw[64 * ROWB];
+    __shared__ __attribute__((aligned(16))) char vw[64 * ROWB];
+    __shared__ uint32_t bad[2];   // keys 0..31, 32..63 with a non-finite V value
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int hl = lane >> 5;
+    const int l32 = lane & 31;
+    const int M = a.R * a.G;
+    const int RGw = (M + 32 * NW - 1) / (32 * NW);
+    const int rg = blockIdx.x % RGw;
+    const int g = (blockIdx.x / RGw) % a.Hkv;
+    const int b = blockIdx.x / (RGw * a.Hkv);
+    int P = a.prefix_len[b];
+    P = P < 0 ? 0 : (P > a.max_prefix_len ? a.max_prefix_len : P);
+    const int W = a.W;
+    const int ps_mask = (1 << a.ps_shift) - 1;
+
+    // Stage the window keys: key k's 16-byte chunk c sits at LDS byte
+    // k * ROWB + 16 (c ^ swz(k)).  Slot i = k * CH + pos of a region is filled
+    // by a direct-to-LDS load of chunk pos ^ swz(k); rows of keys >= W are
+    // zero.
+    constexpr int NL = 64 * CH / THREADS;   // slots per thread and region
+    static_assert(64 * CH % THREADS == 0, "slot split");
+    if (tid < 2)
+        bad[tid] = 0u;
+    int32_t pg[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int key = (i * THREADS + tid) / CH;
+        const int t = P + (key < W ? key : 0);
+        pg[i] = key < W ? (int32_t)clamp_page(a.page_table[(int64_t)b * a.max_pages + (t >> a.ps_shift)],
+                                              a.num_pages)
+                        : 0;
+    }
+    const uint32_t kw0 = lds_off(kw), vw0 = lds_off(vw);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int slot = i * THREADS + tid, key = slot / CH, pos = slot % CH;
+        if (key < W) {
+            const int t = P + key;
+            const int64_t off = (int64_t)pg[i] * a.stride_page + (int64_t)g * a.stride_head +
+                                (int64_t)(t & ps_mask) * a.stride_token + ((pos ^ swz<D>(key)) * 8);
+            const uint32_t at = (uint32_t)((i * THREADS + w * 64) * 16);
+            dma_load16((const uint16_t *)a.k + off, __builtin_amdgcn_readfirstlane(kw0 + at));
+            dma_load16((const uint16_t *)a.v + off, __builtin_amdgcn_readfirstlane(vw0 + at));
+        } else {
+            *(int4 *)(kw + slot * 16) = make_int4(0, 0, 0, 0);
+            *(int4 *)(vw + slot * 16) = make_int4(0, 0, 0, 0);
+        }
+    }
+    const int m = rg * 32 * NW + w * 32 + l32;   // this lane's folded row
+    const bool ok = m < M;
+    const int r = ok ? m / a.G : 0, hh = ok ? m % a.G : 0;
+    const int64_t row = ((int64_t)b * a.R + r) * a.Hq + (int64_t)g * a.G + hh;
+    bf16x8 qv[KSTEPS];
+    {
+        const uint16_t *qp = (const uint16_t *)a.q + row * D + 8 * hl;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            int4 v4 = ok ? *(const int4 *)(qp + 16 * kk) : make_int4(0, 0, 0, 0);
+            qv[kk] = __builtin_bit_cast(bf16x8, v4);
+        }
+    }
+    uint64_t rmask = ok && W > 0 ? a.masks[(int64_t)b * a.R + r] : 0ull;
+    if (W < 64)
+        rmask &= (1ull << W) - 1ull;
+    wait_vmcnt<0>();
+    __syncthreads();
+    // non-finite V values: zero them in LDS and flag their keys
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int slot = i * THREADS + tid, key = slot / CH;
+        if (key < W) {
+            uint4 u = *(const uint4 *)(vw + slot * 16);
+            uint32_t x[4] = {u.x, u.y, u.z, u.w};
+            bool nf = false;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int hh2 = 0; hh2 < 2; ++hh2)
+                    if (((x[e] >> (16 * hh2)) & 0x7F80u) == 0x7F80u) {
+                        nf = true;
+                        x[e] &= ~(0xFFFFu << (16 * hh2));
+                    }
+            if (nf) {
+                *(uint4 *)(vw + slot * 16) = make_uint4(x[0], x[1], x[2], x[3]);
+                atomicOr(&bad[key >> 5], 1u << (key & 31));
+            }
+        }
+    }
+    __syncthreads();
+
+    // window scores, exact row max, weights and O over the (at most two)
+    // 32-key blocks
+    const int nkb = (W + 31) / 32;
+    f32x16 s[2];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        if (kb >= nkb)
+            break;
+        const int krow = kb * 32 + l32;
+        const int ksw = swz<D>(krow);
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            const bf16x8 ka = *(const bf16x8 *)(kw + krow * ROWB + (((2 * kk + hl) ^ ksw) * 16));
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[kk], kk ? s[kb] : f32x16{}, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int j = kb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
+            if (!((rmask >> j) & 1ull))
+                s[kb][e] = -INFINITY;
+            mx = fmaxf(mx, s[kb][e]);
+        }
+    }
+    mx = pair_max(mx) * a.c;
+    const float mu = mx == -INFINITY ? 0.f : mx;
+    f32x16 o[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            o[t][e] = 0.f;
+    float l = 0.f;
+    const int G16 = lane >> 4, a4 = lane & 3, j4 = (lane >> 2) & 3;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        if (kb >= nkb)
+            break;
+        // weights split into a bf16 head and a bf16 remainder: the window
+        // has few keys, so their rounding would not average out
+        bf16x8 pb[2], pr[2];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float p = fast_exp2(fmaf(s[kb][e], a.c, -mu));
+            const __bf16 ph = (__bf16)p;
+            pb[e >> 3][e & 7] = ph;
+            pr[e >> 3][e & 7] = (__bf16)(p - (float)ph);
+            l += p;
+        }
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            const int d0 = ((G16 & 1) ? D / 2 : 0) + 16 * t + 4 * a4;
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                i16x4 half[2];
+#pragma unroll
+                for (int hr = 0; hr < 2; ++hr) {
+                    const int key = kb * 32 + cc * 16 + hr * 8 + 4 * (G16 >> 1) + j4;
+                    const char *p = vw + key * ROWB + (((d0 >> 3) ^ swz<D>(key)) * 16) + (a4 & 1) * 8;
+                    half[hr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)p);
+                }
+                struct {
+                    i16x4 lo, hi;
+                } pair{half[0], half[1]};
+                const bf16x8 va = __builtin_bit_cast(bf16x8, pair);
+                o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[cc], o[t], 0, 0, 0);
+                o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pr[cc], o[t], 0, 0, 0);
+            }
+        }
+    }
+    const float lt = pair_sum(l);
+    const float lse_w = has_keys(lt) ? mu + __log2f(lt) : -INFINITY;
+    const float inv_w = has_keys(lt) ? 1.f / lt : 0.f;
+    // lane value o[t][e] is channel d(t, e) of row m
+    auto chan = [&](int t, int e) {
+        return ((e >> 3) ? D / 2 : 0) + 16 * t + 8 * ((e >> 2) & 1) + 4 * hl + (e & 3);
+    };
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            o[t][e] *= inv_w;
+    // visible keys with non-finite V values (rare): add those values
+    uint64_t vbad = rmask & (((uint64_t)bad[1] << 32) | bad[0]);
+    if (__ballot(vbad != 0ull)) {
+        while (vbad) {
+            const int j = __ffsll((unsigned long long)vbad) - 1;
+            vbad &= vbad - 1;
+            const int t_ = P + j;
+            const int64_t page =
+                clamp_page(a.page_table[(int64_t)b * a.max_pages + (t_ >> a.ps_shift)], a.num_pages);
+            const uint16_t *vr = (const uint16_t *)a.v + page * a.stride_page +
+                                 (int64_t)g * a.stride_head + (int64_t)(t_ & ps_mask) * a.stride_token;
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const uint16_t h = vr[chan(t, e)];
+                    if ((h & 0x7F80u) == 0x7F80u)
+                        o[t][e] += bf16_bits_to_f32(h);
+                }
+        }
+    }
+    if (!ok)
+        return;
+    if (a.S == 2) {
+        // a single prefix partial: merge it here (NaN-propagating max) and
+        // write the row's output
+        const float lp = a.ws_lse[row * 2];
+        const float mall = (lp > lse_w || lp != lp) ? lp : lse_w;
+        float res_lse = -INFINITY;
+        const float *op = a.ws_o + row * 2 * D;
+        if (mall != -INFINITY) {
+            const float zp = lp != -INFINITY ? fast_exp2(lp - mall) : 0.f;
+            const float zw = lse_w != -INFINITY ? fast_exp2(lse_w - mall) : 0.f;
+            const float inv = 1.f / (zp + zw);
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const float4 v4 = *(const float4 *)(op + chan(t, 4 * q4));
+                    const float pv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float wv = lse_w != -INFINITY ? zw * o[t][4 * q4 + e] : 0.f;
+                        o[t][4 * q4 + e] = (lp != -INFINITY ? fmaf(zp, pv[e], wv) : wv) * inv;
+                    }
+                }
+            res_lse = mall + __log2f(zp + zw);
+        } else {
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    o[t][e] = 0.f;
+        }
+        uint16_t *out = (uint16_t *)a.out + row * D;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const uint32_t lo = f32_to_bf16_bits(o[t][4 * q4]) |
+                                    ((uint32_t)f32_to_bf16_bits(o[t][4 * q4 + 1]) << 16);
+                const uint32_t hi = f32_to_bf16_bits(o[t][4 * q4 + 2]) |
+                                    ((uint32_t)f32_to_bf16_bits(o[t][4 * q4 + 3]) << 16);
+                *(uint2 *)(out + chan(t, 4 * q4)) = make_uint2(lo, hi);
+            }
+        if (a.lse2 && hl == 0)
+            a.lse2[row] = res_lse;
+        return;
+    }
+    // the window's partial goes to the last slot of the row
+    float *dst = a.ws_o + (row * a.S + (a.S - 1)) * D;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            *(float4 *)(dst + chan(t, 4 * q4)) =
+                make_float4(o[t][4 * q4], o[t][4 * q4 + 1], o[t][4 * q4 + 2], o[t][4 * q4 + 3]);
+    if (hl == 0)
+        a.ws_lse[row * a.S + (a.S - 1)] = lse_w;
+}
+
+// Merge of the S partials of a row (prefix splits and the window, bf16
+// path): one wave per (request, row, head), lanes over channels.
+// lse2 = log2 sum_k 2^lse2_k, out = sum_k 2^(lse2_k - lse2) o_k; the max is
+// NaN-propagating, so a NaN partial makes the row NaN.
+template <int D>
+__global__ void __launch_bounds__(256) k_merge(MergeArgs a) {
+    constexpr int VPL = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (int64_t)a.B * a.R * a.Hq)
+        return;
+    const float *lp = a.ws_lse + row * a.S;
+    float mx = -INFINITY;
+    for (int s0 = 0; s0 < a.S; s0 += 64) {
+        float ls = s0 + lane < a.S ? lp[s0 + lane] : -INFINITY;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float y = __shfl_xor(ls, off);
+            ls = (ls != ls || y != y) ? __builtin_nanf("") : fmaxf(ls, y);
+        }
+        mx = (ls != ls || mx != mx) ? __builtin_nanf("") : fmaxf(mx, ls);
+    }
+    float acc[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        acc[i] = 0.f;
+    float res_lse = -INFINITY;
+    if (mx != -INFINITY) {
+        float zs = 0.f;
+        const float *op = a.ws_o + row * a.S * D + lane * VPL;
+#pragma unroll 4
+        for (int s = 0; s < a.S; ++s) {
+            const float ls = lp[s];
+            const float z = ls != -INFINITY ? fast_exp2(ls - mx) : 0.f;
+            zs += z;
+            float x[VPL];
+#pragma unroll
+            for (int i = 0; i < VPL; ++i)
+                x[i] = op[(int64_t)s * D + i];
+            if (ls != -INFINITY) {
+#pragma unroll
+                for (int i = 0; i < VPL; ++i)
+                    acc[i] = fmaf(z, x[i], acc[i]);
+            }
+        }
+        const float inv = 1.f / zs;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            acc[i] *= inv;
+        res_lse = mx + __log2f(zs);
+    }
+    uint16_t *dst = (uint16_t *)a.out + row * D + lane * VPL;
+    if (VPL == 2)
+        *(uint32_t *)dst = f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[VPL - 1]) << 16);
+    else
+        dst[0] = f32_to_bf16_bits(acc[0]);
+    if (a.lse2 && lane == 0)
+        a.lse2[row] = res_lse;
+}
+
 // ---------------------------------------------------------------------------
 // host plan
 // ---------------------------------------------------------------------------
@@ -1114,7 +1452,7 @@ Plan make_plan(tav_dtype dtype, int B, int R, int Hq, int Hkv, int D, int max_pr
         }
         p.kps = kps;
         p.n_split = max_vis > 0 ? (max_vis + kps - 1) / kps : 1;
-        p.S = p.n_split * p.NKS;
+        p.S = p.n_split * p.NKS + 1;   // the last slot holds the window partial
     } else {
         p.mfma = false;
         p.NT = p.NRB = p.NKS = p.RG = 1;
@@ -1292,6 +1630,7 @@ tav_status prepare(const char *fn, int phase, Call &call, const void *q, const v
     m.B = B;
     m.R = R;
     m.Hq = Hq;
+    m.Hkv = Hkv;
     m.G = a.G;
     m.D = D;
     m.S = p.S;
@@ -1321,9 +1660,40 @@ void launch_prefix(const Call &c, hipStream_t s) {
     }
 }
 
+template <int D, int NW>
+void launch_window_mfma(const MergeArgs &m, hipStream_t s) {
+    const int M = m.R * m.G;
+    const unsigned grid = (unsigned)((long long)m.B * m.Hkv * ((M + 32 * NW - 1) / (32 * NW)));
+    hipLaunchKernelGGL((k_window_mfma<D, NW>), dim3(grid), dim3(64 * NW), 0, s, m);
+}
+
+template <int D>
+void launch_window_mfma_d(const MergeArgs &m, hipStream_t s) {
+    const int M = m.R * m.G;
+    if (M <= 32)
+        launch_window_mfma<D, 1>(m, s);
+    else if (M <= 64)
+        launch_window_mfma<D, 2>(m, s);
+    else
+        launch_window_mfma<D, 4>(m, s);
+}
+
 void launch_merge(const Call &c, hipStream_t s) {
     const MergeArgs &m = c.m;
     const unsigned grid = (unsigned)(((long long)m.B * m.R * m.Hq + 3) / 4);
+    if (c.bf16) {
+        // with a single prefix partial the window kernel writes the output
+        if (c.D == 128) {
+            launch_window_mfma_d<128>(m, s);
+            if (m.S > 2)
+                hipLaunchKernelGGL(k_merge<128>, dim3(grid), dim3(256), 0, s, m);
+        } else {
+            launch_window_mfma_d<64>(m, s);
+            if (m.S > 2)
+                hipLaunchKernelGGL(k_merge<64>, dim3(grid), dim3(256), 0, s, m);
+        }
+        return;
+    }
     if (c.D == 128) {
         if (c.bf16)
             hipLaunchKernelGGL((k_window_merge<128, true>), dim3(grid), dim3(256), 0, s, m);

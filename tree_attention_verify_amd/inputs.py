@@ -71,6 +71,19 @@ class Workload:
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
 
+    def describe(self) -> str:
+        tree = {
+            "worked": "the worked 5-node tree [root, A, B, C, D]",
+            "random": "N %d random trees (depth <= %d)" % (self.N, self.depth_cap),
+            "eagle": "EAGLE beam trees (top-%d, %d steps, best %d nodes + root)"
+                     % (self.eagle_topk, self.eagle_steps, self.N - 1),
+            "chain": "a chain of N %d" % self.N,
+            "lanes": "draft lanes (K %d, S %d, W %d) over a frozen %d-key window"
+                     % (self.lane_k, self.lane_steps, self.W, self.prefix_window),
+        }[self.tree]
+        return "%s: B %d, P %d, %s, Hq %d, Hkv %d, D %d, %s, page size %d" % (
+            self.name, self.B, self.P, tree, self.Hq, self.Hkv, self.D, self.dtype, self.page_size)
+
 
 WORKLOADS = {
     "worked": Workload("worked", 1, 128, 5, 4, 1, 64, "f32", 16, "worked"),
