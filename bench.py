@@ -251,14 +251,19 @@ def cpu_baseline(wl, inp, masks_np, budget_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the board's power management settles within about 100 steps; the default
+    # times the steady state that back-to-back verify rounds run in
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="long64", choices=sorted(gen.WORKLOADS))
     ap.add_argument("--seed", type=int, default=4)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB copy (calibrates FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
+                    help="after the timed steps, run steps back to back for SECONDS (for board "
+                         "power and clock readings taken meanwhile) and report their rate")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "CMD"),
                     help="write profiles/<workload>_prefix_traffic.{json,md} from rocprofv3 CSVs")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_DIR", "CMD"),
@@ -305,6 +310,17 @@ def main():
     log("timed %d steps: %.3f ms/step (host %.3f ms/step), prefix kernel avg %.3f ms "
         "(min %.3f max %.3f)" % (args.steps, ms_step, t_host * 1e3 / args.steps, prefix_avg,
                                  min(prefix_ms), max(prefix_ms)))
+
+    sustained = None
+    if args.sustain > 0:
+        n, t_s = 0, time.perf_counter()
+        while time.perf_counter() - t_s < args.sustain:
+            for _ in range(50):
+                step.run()
+            torch.cuda.synchronize()
+            n += 50
+        sustained = (time.perf_counter() - t_s) * 1e3 / n
+        log("sustained: %d steps back to back, %.4f ms/step" % (n, sustained))
 
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
@@ -353,6 +369,8 @@ def main():
         rf.update({"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS,
                    "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
                    "algorithmic_flops": prefix_flops, "hbm_gbs": round(achieved, 1)})
+    if sustained is not None:
+        res["sustained_ms_per_step"] = round(sustained, 4)
     t = traffic_for(wl.name)
     if t is not None:
         res["roofline"]["traffic"] = round(t["prefix_traffic_bytes"])
