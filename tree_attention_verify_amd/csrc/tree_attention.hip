@@ -91,6 +91,16 @@ __device__ __forceinline__ void dma_load16(const void *src, uint32_t lds_base) {
                  : "memory", "m0");
 }
 
+// Direct-to-LDS 16-byte load with a wave-uniform 64-bit base and a per-lane
+// 32-bit byte offset; lane i's 16 bytes land at LDS byte lds_base + 16 i.
+// Completion is tracked as for dma_load16.
+__device__ __forceinline__ void dma_load16_s(const void *base, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds_base)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_off(const void *p) {
     return (uint32_t)(uintptr_t)(const LDS_AS void *)p;
 }
@@ -221,14 +231,20 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
     const int b = unit / (a.n_split * a.Hkv);
 
     const KeyRange kr = split_range(a, b, split);
-    const int nkeys = kr.hi - kr.lo;
+    // With pages of 8 or more keys the keys of one load instruction (64 / CH
+    // consecutive keys) share a page, so loads take a wave-uniform page base;
+    // stages then start at the 8-key boundary at or below the split start and
+    // keys outside [lo, hi) are neither loaded nor visible.
+    const bool wave_pages = a.ps_shift >= 3;
+    const int kb0 = wave_pages ? (kr.lo & ~7) : kr.lo;
+    const int nkeys = kr.hi > kr.lo ? kr.hi - kb0 : 0;
     const int ns = (nkeys + SK - 1) / SK;
     const int rbw = w % NRB;   // this wave's row block
     const int ks = w / NRB;    // this wave's key subset within a stage
     const int rows_base = rg * ROWS_WG + rbw * 32;
 
     // page-table slice of this split
-    const int lp0 = nkeys > 0 ? (kr.lo >> a.ps_shift) : 0;
+    const int lp0 = nkeys > 0 ? (kb0 >> a.ps_shift) : 0;
     const int npt = nkeys > 0 ? ((kr.hi - 1) >> a.ps_shift) - lp0 + 1 : 0;
     for (int i = tid; i < npt && i < kPtMax; i += THREADS)
         pt[i] = (int32_t)clamp_page(a.page_table[(int64_t)b * a.max_pages + lp0 + i], a.num_pages);
@@ -271,24 +287,54 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
                       (((s2 % CH) ^ swz<D>(ld_key[i])) * 8);
     }
 
-    // Issue the direct-to-LDS loads of stage st.  All page-table reads come
-    // first so that the loads are not each held up by an LDS read.
+    // Issue the direct-to-LDS loads of stage st.  Load i of a wave covers KPI
+    // consecutive keys (one per CH lanes); this lane's chunk position and
+    // swizzle depend only on the key modulo 16, so its 32-bit offset is fixed.
+    constexpr int KPI = 64 / CH;
+    constexpr int LH = LPS / 2;   // loads per region (K, then V)
+    static_assert((THREADS / CH) % (D == 128 ? 16 : 8) == 0, "swizzle period divides a load's key step");
+    const uint32_t lane_off =
+        (uint32_t)((lane / CH) * a.stride_token * 2 +
+                   (((lane % CH) ^ swz<D>((w * 64 + lane) / CH)) * 16));
     auto issue = [&](int st) {
         const uint32_t sbase = lds0 + (uint32_t)((st % NBUF) * SB);
-        const int key_base = kr.lo + st * SK;
-        int64_t page[LPS];
+        const int kst = kb0 + st * SK;
+        if (wave_pages) {
+            int32_t pgs[LH];
 #pragma unroll
-        for (int i = 0; i < LPS; ++i) {
-            const int t = key_base + ld_key[i];
-            page[i] = t < kr.hi ? pt[(t >> a.ps_shift) - lp0] : 0;
-        }
+            for (int j = 0; j < LH; ++j) {
+                const int k0 = kst + (j * THREADS + w * 64) / CH;
+                pgs[j] = k0 < kr.hi ? pt[(k0 >> a.ps_shift) - lp0] : 0;
+            }
 #pragma unroll
-        for (int i = 0; i < LPS; ++i) {
-            const int t = key_base + ld_key[i];
-            if (t < kr.hi)
-                dma_load16(src_base[i] + page[i] * a.stride_page +
-                               (int64_t)(t & ps_mask) * a.stride_token,
-                           __builtin_amdgcn_readfirstlane(sbase + (i * THREADS + w * 64) * 16));
+            for (int i = 0; i < LPS; ++i) {
+                const int j = i % LH;
+                const int k0 = kst + (j * THREADS + w * 64) / CH;   // wave-uniform
+                if (k0 >= kr.hi)
+                    continue;
+                const int t = k0 + lane / CH;
+                const bool in = (k0 >= kr.lo && k0 + KPI <= kr.hi) || (t >= kr.lo && t < kr.hi);
+                const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(pgs[j]) * a.stride_page +
+                                    (int64_t)g * a.stride_head + (int64_t)(k0 & ps_mask) * a.stride_token;
+                const uint16_t *base = (const uint16_t *)(i >= LH ? a.v : a.k) + off;
+                if (in)
+                    dma_load16_s(base, lane_off, sbase + (i * THREADS + w * 64) * 16);
+            }
+        } else {
+            int64_t page[LPS];
+#pragma unroll
+            for (int i = 0; i < LPS; ++i) {
+                const int t = kst + ld_key[i];
+                page[i] = t < kr.hi ? pt[(t >> a.ps_shift) - lp0] : 0;
+            }
+#pragma unroll
+            for (int i = 0; i < LPS; ++i) {
+                const int t = kst + ld_key[i];
+                if (t < kr.hi)
+                    dma_load16(src_base[i] + page[i] * a.stride_page +
+                                   (int64_t)(t & ps_mask) * a.stride_token,
+                               __builtin_amdgcn_readfirstlane(sbase + (i * THREADS + w * 64) * 16));
+            }
         }
     };
 
@@ -322,7 +368,7 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
 
         const char *Kb = lds + (it % NBUF) * SB;
         const char *Vb = Kb + SB / 2;
-        const int first = kr.lo + it * SK + key0;  // absolute key of this wave's block
+        const int first = kb0 + it * SK + key0;  // absolute key of this wave's block
         if (first >= kr.hi)
             continue;
         // S^T[key][row] = sum_d K[key][d] Q[row][d]
@@ -335,12 +381,12 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
             const bf16x8 ka = *(const bf16x8 *)(Kb + krow * ROWB + (((2 * kk + hl) ^ ksw) * 16));
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[kk], s, 0, 0, 0);
         }
-        // keys past the end of the split are not visible
-        if (first + 32 > kr.hi) {
+        // keys outside the split are not visible
+        if (first < kr.lo || first + 32 > kr.hi) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = 8 * (r >> 2) + 4 * hl + (r & 3);
-                if (first + key >= kr.hi)
+                const int key = first + 8 * (r >> 2) + 4 * hl + (r & 3);
+                if (key < kr.lo || key >= kr.hi)
                     s[r] = -INFINITY;
             }
         }
@@ -467,15 +513,6 @@ __device__ inline int yv(int k, int cg) { return 2 * ((k & 3) ^ (cg & 1)); }
 
 constexpr float kSumLimit = 1048576.f;   // 2^20
 
-// Direct-to-LDS 16-byte load with a wave-uniform 64-bit base and a per-lane
-// 32-bit byte offset; lane i's 16 bytes land at LDS byte lds_base + 16 i.
-// Completion is tracked as for dma_load16.
-__device__ __forceinline__ void dma_load16_s(const void *base, uint32_t voff, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-                 :
-                 : "v"(voff), "s"(base), "s"(lds_base)
-                 : "memory", "m0");
-}
 
 template <int D, int SK_>
 struct PipeCfg {
