@@ -169,6 +169,8 @@ __device__ inline char *row_addr(const RowTable &t, int b, int slot, int h) {
 // disjoint bytes.
 __global__ void __launch_bounds__(256) k_compact_rows(CompactArgs a) {
     __shared__ uint32_t stage[64][kCompactWords];
+    __shared__ const char *src_row[64];   // segment 0 of the source slot of row i, or null
+    __shared__ char *dst_row[64];         // segment 0 of slot i, or null
     const RowTable &t = a.t[blockIdx.z];
     const int b = blockIdx.y;
     const int w = blockIdx.x * kCompactWords + threadIdx.x;
@@ -176,25 +178,31 @@ __global__ void __launch_bounds__(256) k_compact_rows(CompactArgs a) {
         return;  // uniform per block
     int n = a.accept_len[b];
     n = n < 0 ? 0 : (n > a.N ? a.N : n);
-    const bool active = w < t.words_per_slot;
-    const int h = active ? w / t.row_words : 0;
-    const int off = active ? (w - h * t.row_words) * 4 : 0;
-    for (int i = 0; i < n; ++i) {
+    // the row addresses first, all in parallel; then every copy's load is
+    // independent of the others
+    if ((int)threadIdx.x < n) {
+        const int i = threadIdx.x;
         const int src = a.path[(int64_t)b * a.N + i];
-        if (active && src >= 0 && src < a.N) {
-            const char *p = row_addr(t, b, src, h);
-            if (p)
-                stage[i][threadIdx.x] = *(const uint32_t *)(p + off);
-        }
+        const char *sp = src >= 0 && src < a.N ? row_addr(t, b, src, 0) : nullptr;
+        src_row[i] = sp;
+        dst_row[i] = sp ? row_addr(t, b, i, 0) : nullptr;
     }
     __syncthreads();
+    const bool active = w < t.words_per_slot;
+    const int h = active ? w / t.row_words : 0;
+    const int64_t off = active ? (int64_t)h * t.stride_head + (int64_t)(w - h * t.row_words) * 4 : 0;
+#pragma unroll 8
     for (int i = 0; i < n; ++i) {
-        const int src = a.path[(int64_t)b * a.N + i];
-        if (active && src >= 0 && src < a.N && row_addr(t, b, src, h)) {
-            char *p = row_addr(t, b, i, h);
-            if (p)
-                *(uint32_t *)(p + off) = stage[i][threadIdx.x];
-        }
+        const char *p = src_row[i];
+        if (active && p)
+            stage[i][threadIdx.x] = *(const uint32_t *)(p + off);
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int i = 0; i < n; ++i) {
+        char *p = dst_row[i];
+        if (active && p)
+            *(uint32_t *)(p + off) = stage[i][threadIdx.x];
     }
 }
 
