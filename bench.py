@@ -127,6 +127,13 @@ def summarize_stats(workload, stats_dir, cmd):
     print(open(out).read())
 
 
+def prefix_kernel_name(wl):
+    """The split-K prefix kernel the library launches for this shape."""
+    if wl.dtype != "bf16":
+        return "k_prefix_f32"
+    return "k_prefix_mfma_pipe" if wl.R * (wl.Hq // wl.Hkv) > 128 else "k_prefix_mfma"
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -352,7 +359,7 @@ def main():
         "head_rows_per_s": round(rows * wl.Hq / (ms_step * 1e-3), 1),
         "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
         "attention_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
-        "roofline": {"kernel": "k_prefix_mfma (split-K prefix)", "bound": "hbm",
+        "roofline": {"kernel": prefix_kernel_name(wl), "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "algorithmic_bytes": prefix_bytes,
