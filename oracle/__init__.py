@@ -59,7 +59,9 @@ def lib():
         P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         L.orc_build_masks.argtypes = [P, I, I, P, P, P, P, P]
         L.orc_shift_positions.argtypes = [P, P, I, I, I]
-        L.orc_tree_attention.argtypes = [P, P, P, I, I64, I64, I64, P, I, I, P, I,
+        L.orc_e4m3_decode.argtypes = [I]
+        L.orc_e4m3_decode.restype = D
+        L.orc_tree_attention.argtypes = [P, P, P, I, I, I64, I64, I64, P, I, I, P, I,
                                          P, I, I, I, I, I, I, D, P, I64, P, P]
         L.orc_causal_attention.argtypes = [P, P, P, I, I, I, I, I, I, D, P, P]
         L.orc_merge.argtypes = [P, P, I, I, I, P, P]
@@ -87,7 +89,16 @@ def _dtype_code(a: np.ndarray) -> int:
         return 0
     if a.dtype == np.uint16:  # raw bf16 bit patterns
         return 1
-    raise TypeError("oracle inputs are float32 or raw bf16 (uint16) arrays, got %s" % a.dtype)
+    if a.dtype == np.uint8:   # raw FP8 E4M3 codes (K/V caches only)
+        return 2
+    raise TypeError("oracle inputs are float32, raw bf16 (uint16) or raw E4M3 (uint8) arrays, "
+                    "got %s" % a.dtype)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """fp64 values of FP8 E4M3 codes (the oracle's decoder)."""
+    codes = np.asarray(codes, dtype=np.int64).ravel()
+    return np.array([lib().orc_e4m3_decode(int(c)) for c in codes], np.float64)
 
 
 def _check(rc, name):
@@ -135,7 +146,10 @@ def tree_attention(q, k_cache, v_cache, strides, page_table, page_size, prefix_l
     dt = _dtype_code(q)
     k_cache = np.ascontiguousarray(k_cache)
     v_cache = np.ascontiguousarray(v_cache)
-    assert k_cache.dtype == q.dtype and v_cache.dtype == q.dtype
+    kvdt = _dtype_code(k_cache)
+    assert v_cache.dtype == k_cache.dtype
+    assert kvdt == dt or (kvdt == 2 and dt == 1), "FP8 caches take a bf16 query"
+    assert dt != 2, "the query is fp32 or bf16"
     B, R, Hq, D = q.shape
     page_table = _c(page_table, np.int32)
     prefix_len = _c(prefix_len, np.int32)
@@ -152,7 +166,7 @@ def tree_attention(q, k_cache, v_cache, strides, page_table, page_size, prefix_l
         rp, nr = rows, rows.size
     sp, sh, st = (int(x) for x in strides)
     _check(lib().orc_tree_attention(
-        _p(q), _p(k_cache), _p(v_cache), dt, sp, sh, st, _p(page_table),
+        _p(q), _p(k_cache), _p(v_cache), dt, kvdt, sp, sh, st, _p(page_table),
         page_table.shape[1], int(page_size), _p(prefix_len), int(prefix_window),
         _p(masks), int(W), B, R, Hq, int(Hkv), D, float(sm_scale), _p(rp), nr,
         _p(out), _p(lse)), "tree_attention")

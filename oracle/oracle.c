@@ -34,15 +34,42 @@
 /* element access                                                      */
 /* ------------------------------------------------------------------ */
 
-/* dtype codes of this file: 0 = fp32, 1 = bf16 (raw 16-bit patterns). */
+/*
+ * dtype codes of this file: 0 = fp32, 1 = bf16 (raw 16-bit patterns),
+ * 2 = FP8 E4M3 (raw bytes).  E4M3 here is the OCP 8-bit format with 1 sign,
+ * 4 exponent (bias 7) and 3 mantissa bits, no infinities, and NaN for
+ * exponent and mantissa all ones; it is the unscaled FP8 KV cache format of
+ * [DTS] "One tree attention ..." (an FP8 E4M3 cache changes no structure).
+ */
+static double orc_e4m3(uint8_t b)
+{
+    int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);            /* subnormal: m/8 * 2^(1-7) */
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
 static double orc_load(const void *base, int dtype, int64_t idx)
 {
     if (dtype == 0)
         return (double)((const float *)base)[idx];
+    if (dtype == 2)
+        return orc_e4m3(((const uint8_t *)base)[idx]);
     uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
     return (double)f;
+}
+
+/* Exposed for the pins: the decoded value of one E4M3 code. */
+double orc_e4m3_decode(int code)
+{
+    return orc_e4m3((uint8_t)code);
 }
 
 /* ------------------------------------------------------------------ */
@@ -142,7 +169,7 @@ int orc_shift_positions(int32_t *pos, const int32_t *depth, int B, int N,
  * kofs/vofs hold the element offset of each key's row.
  */
 static void orc_softmax_row(const void *qb, int64_t qofs, const void *kb,
-                            const void *vb, int dtype, const int64_t *kofs,
+                            const void *vb, int qdt, int kvdt, const int64_t *kofs,
                             int nk, int D, double scale, double *s,
                             double *out, double *lse2)
 {
@@ -156,7 +183,7 @@ static void orc_softmax_row(const void *qb, int64_t qofs, const void *kb,
     for (int t = 0; t < nk; ++t) {
         double acc = 0.0;
         for (int d = 0; d < D; ++d)
-            acc += orc_load(qb, dtype, qofs + d) * orc_load(kb, dtype, kofs[t] + d);
+            acc += orc_load(qb, qdt, qofs + d) * orc_load(kb, kvdt, kofs[t] + d);
         s[t] = scale * acc;
         if (s[t] > m)
             m = s[t];
@@ -166,7 +193,7 @@ static void orc_softmax_row(const void *qb, int64_t qofs, const void *kb,
         double w = exp(s[t] - m);
         Z += w;
         for (int d = 0; d < D; ++d)
-            out[d] += w * orc_load(vb, dtype, kofs[t] + d);
+            out[d] += w * orc_load(vb, kvdt, kofs[t] + d);
     }
     for (int d = 0; d < D; ++d)
         out[d] /= Z;
@@ -193,13 +220,15 @@ static void orc_softmax_row(const void *qb, int64_t qofs, const void *kb,
  * page*stride_page + g*stride_head + slot*stride_token, channels contiguous.
  * Keys that are not visible are never read.
  *
+ * q holds dtype elements, k_cache and v_cache kv_dtype elements (an FP8
+ * cache takes a bf16 query, which is not quantised).
  * rows: optional list of flat row ids ((b*R + r)*Hq + h); out/lse2 then hold
  * n_rows entries in list order.  With rows == NULL every row is computed and
  * out is [B][R][Hq][D], lse2 [B][R][Hq].
  * q is [B][R][Hq][D] contiguous.  sm_scale <= 0 means 1/sqrt(D).
  */
 int orc_tree_attention(const void *q, const void *k_cache, const void *v_cache,
-                       int dtype, int64_t stride_page, int64_t stride_head,
+                       int dtype, int kv_dtype, int64_t stride_page, int64_t stride_head,
                        int64_t stride_token, const int32_t *page_table,
                        int max_pages, int page_size, const int32_t *prefix_len,
                        int prefix_window, const uint64_t *masks, int W, int B,
@@ -245,8 +274,8 @@ int orc_tree_attention(const void *q, const void *k_cache, const void *v_cache,
                          (int64_t)(t % page_size) * stride_token;
         }
         int64_t qofs = (((int64_t)b * R + r) * Hq + h) * D;
-        orc_softmax_row(q, qofs, k_cache, v_cache, dtype, kofs, nk, D, sm_scale,
-                        s, out + n * D, lse2 + n);
+        orc_softmax_row(q, qofs, k_cache, v_cache, dtype, kv_dtype, kofs, nk, D,
+                        sm_scale, s, out + n * D, lse2 + n);
         free(kofs);
         free(s);
     }
@@ -279,7 +308,7 @@ int orc_causal_attention(const void *q, const void *k, const void *v,
         double *s = (double *)malloc(sizeof(double) * nk);
         for (int t = 0; t < nk; ++t)
             kofs[t] = ((int64_t)t * Hkv + g) * D;
-        orc_softmax_row(q, id * D, k, v, dtype, kofs, nk, D, sm_scale, s,
+        orc_softmax_row(q, id * D, k, v, dtype, dtype, kofs, nk, D, sm_scale, s,
                         out + id * D, lse2 + id);
         free(kofs);
         free(s);

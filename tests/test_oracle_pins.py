@@ -178,8 +178,8 @@ def test_fresh_spec_is_the_chain():
 # ---------------------------------------------------------------------------
 
 def small_case(seed, tree="random", B=2, P=37, N=12, Hq=4, Hkv=2, D=16, ps=8,
-               dtype="bf16", layout="HND", prefix_window=0):
-    wl = gen.Workload("t", B, P, N, Hq, Hkv, D, dtype, ps, tree, depth_cap=4)
+               dtype="bf16", layout="HND", prefix_window=0, kv_dtype=""):
+    wl = gen.Workload("t", B, P, N, Hq, Hkv, D, dtype, ps, tree, depth_cap=4, kv_dtype=kv_dtype)
     inp = gen.make_inputs(wl, seed, "cpu", layout=layout)
     m = oracle.build_masks(inp.parents)["masks"]
     return wl, inp, m
@@ -240,6 +240,40 @@ def sdpa_reference(inp, masks, prefix_window=0):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_tree_attention_matches_sdpa(layout, dtype):
     wl, inp, m = small_case(1, dtype=dtype, layout=layout)
+    o, l = oracle_attn(inp, m)
+    ro, rl = sdpa_reference(inp, m)
+    assert np.isfinite(o).all()
+    np.testing.assert_allclose(o, ro, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(l, rl, atol=1e-12, rtol=0)
+
+
+def test_e4m3_decode_matches_torch_on_every_code():
+    """The oracle's E4M3 decoder against torch's float8_e4m3fn, all 256 codes."""
+    ours = oracle.e4m3_decode(np.arange(256))
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    assert np.array_equal(np.signbit(ours[fin]), np.signbit(ref[fin]))
+
+
+def test_e4m3_decode_format_values():
+    """Values fixed by the E4M3 format (bias 7, 3 mantissa bits, no inf)."""
+    d = lambda c: float(oracle.e4m3_decode([c])[0])
+    assert d(0x00) == 0.0 and not math.copysign(1.0, d(0x00)) < 0
+    assert d(0x80) == 0.0 and math.copysign(1.0, d(0x80)) < 0
+    assert d(0x01) == 2.0 ** -9 and d(0x07) == 7 * 2.0 ** -9      # subnormals
+    assert d(0x08) == 2.0 ** -6                                    # smallest normal
+    assert d(0x38) == 1.0 and d(0x3C) == 1.5 and d(0xB8) == -1.0
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0                  # largest finite
+    assert math.isnan(d(0x7F)) and math.isnan(d(0xFF))
+
+
+@pytest.mark.parametrize("layout", ["HND", "NHD"])
+def test_fp8_cache_attention_matches_sdpa(layout):
+    """An FP8 E4M3 cache with a bf16 query: the oracle reads the decoded
+    cache values, the library routine gets them as fp64."""
+    wl, inp, m = small_case(3, layout=layout, kv_dtype="fp8")
     o, l = oracle_attn(inp, m)
     ro, rl = sdpa_reference(inp, m)
     assert np.isfinite(o).all()

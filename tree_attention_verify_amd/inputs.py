@@ -59,6 +59,11 @@ class Workload:
     lane_steps: int = 0
     eagle_topk: int = 0
     eagle_steps: int = 0
+    kv_dtype: str = ""  # K/V cache dtype when it differs from dtype: "fp8" (E4M3, bf16 q)
+
+    @property
+    def kv(self) -> str:
+        return self.kv_dtype or self.dtype
 
     @property
     def R(self) -> int:
@@ -81,8 +86,9 @@ class Workload:
             "lanes": "draft lanes (K %d, S %d, W %d) over a frozen %d-key window"
                      % (self.lane_k, self.lane_steps, self.W, self.prefix_window),
         }[self.tree]
+        dt = self.dtype if self.kv == self.dtype else "%s q, %s E4M3 K/V" % (self.dtype, self.kv)
         return "%s: B %d, P %d, %s, Hq %d, Hkv %d, D %d, %s, page size %d" % (
-            self.name, self.B, self.P, tree, self.Hq, self.Hkv, self.D, self.dtype, self.page_size)
+            self.name, self.B, self.P, tree, self.Hq, self.Hkv, self.D, dt, self.page_size)
 
 
 WORKLOADS = {
@@ -96,6 +102,9 @@ WORKLOADS = {
     "lanes": Workload("lanes", 64, 32768, 4, 32, 8, 128, "bf16", 16, "lanes",
                       prefix_window=4096, lane_k=4, lane_steps=4),
     "chain8": Workload("chain8", 64, 32768, 8, 32, 8, 128, "bf16", 16, "chain"),
+    # the long-context workload over an FP8 E4M3 K/V cache (bf16 query and output)
+    "long64_fp8": Workload("long64_fp8", 4, 131072, 64, 32, 8, 128, "bf16", 64, "random",
+                           depth_cap=8, kv_dtype="fp8"),
 }
 
 
@@ -220,7 +229,7 @@ def tokens_for(rng, parents: np.ndarray, agree: Optional[float]) -> tuple[np.nda
 # tensors
 # ---------------------------------------------------------------------------
 
-TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 
 
 def _randn_into(out: torch.Tensor, gen: torch.Generator, chunk: int = 1 << 26):
@@ -292,12 +301,12 @@ def make_inputs(wl: Workload, seed: int, device="cpu", layout: str = "HND",
     page_table = (r_pt.permutation(n_pages - 1) + 1).astype(np.int32).reshape(B, max_pages)
     q = kc = vc = None
     if with_tensors:
-        dt = TORCH_DTYPE[wl.dtype]
+        dt, kvt = TORCH_DTYPE[wl.dtype], TORCH_DTYPE[wl.kv]
         dev = torch.device(device)
         shape = (n_pages, wl.Hkv, ps, wl.D) if layout == "HND" else (n_pages, ps, wl.Hkv, wl.D)
         q = torch.empty((B, wl.R, wl.Hq, wl.D), dtype=dt, device=dev)
-        kc = torch.empty(shape, dtype=dt, device=dev)
-        vc = torch.empty(shape, dtype=dt, device=dev)
+        kc = torch.empty(shape, dtype=kvt, device=dev)
+        vc = torch.empty(shape, dtype=kvt, device=dev)
         for k, t in enumerate((q, kc, vc)):
             g = torch.Generator(device=dev)
             g.manual_seed(_torch_seed(seed, k))
@@ -328,8 +337,11 @@ def _poison(kc, vc, page_table, prefix_lens, wl, layout):
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
-    """Raw bit patterns of a bf16 tensor (uint16 numpy) or the fp32 values."""
+    """Raw bit patterns of a bf16 (uint16 numpy) or FP8 E4M3 (uint8 numpy)
+    tensor, or the fp32 values."""
     t = t.detach().cpu().contiguous()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
     return t.numpy()
