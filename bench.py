@@ -84,7 +84,7 @@ def summarize_traffic(workload, fetch_dir, write_dir, cmd):
     w_scale = COPY_BYTES / (cw * 1024.0)
     wl = gen.WORKLOADS[workload]
     P_vis = min(wl.P, wl.prefix_window) if wl.prefix_window else wl.P
-    e = 2 if wl.dtype == "bf16" else 4
+    e = ELEM_BYTES[wl.dtype]
     algo = kv_bytes(wl, P_vis, with_window=False) + wl.B * wl.R * wl.Hq * wl.D * e
     t = {"workload": workload, "kernel_source_sha256_16": kernel_hash(),
          "prefix_fetch_kib_per_dispatch": pf, "prefix_write_kib_per_dispatch": pw,
@@ -138,8 +138,11 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+
+
 def kv_bytes(wl, P_vis, with_window=True):
-    e = 2 if wl.dtype == "bf16" else 4
+    e = ELEM_BYTES[wl.kv]
     keys = P_vis + (wl.W if with_window else 0)
     return wl.B * keys * wl.Hkv * wl.D * 2 * e
 
@@ -174,9 +177,9 @@ class Step:
         self.hidden = torch.randn((B, N, hidden_dim), device=d).to(torch.bfloat16)
         sp, sh, st, Hkv, ps = tav.kv_strides(inp.k_cache, inp.layout)
         self.kv = (sp, sh, st, inp.k_cache.shape[0], ps)
-        self.code = tav.TAV_BF16 if wl.dtype == "bf16" else tav.TAV_F32
+        self.code = tav._code(inp.q.dtype, inp.k_cache.dtype)
         nbytes = tav.tree_attention_workspace_size(inp.q.dtype, B, R, wl.Hq, wl.Hkv, wl.D, wl.P,
-                                                   wl.prefix_window, ps)
+                                                   wl.prefix_window, ps, inp.k_cache.dtype)
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=d)
         tables = [tav.RowTable.paged_kv(inp.k_cache, self.page_table, self.prefix_len),
                   tav.RowTable.paged_kv(inp.v_cache, self.page_table, self.prefix_len),
@@ -342,7 +345,7 @@ def main():
     kvb = kv_bytes(wl, P_vis)
     rows = wl.B * wl.R
     value = kvb / (ms_step * 1e-3) / 1e9
-    e = 2 if wl.dtype == "bf16" else 4
+    e = ELEM_BYTES[wl.dtype]
     prefix_bytes = kv_bytes(wl, P_vis, with_window=False) + wl.B * wl.R * wl.Hq * wl.D * e
     achieved = prefix_bytes / (prefix_avg * 1e-3) / 1e9
     flops = attn_flops(wl, masks_np, P_vis)

@@ -49,8 +49,11 @@ typedef enum {
 } tav_status;
 
 typedef enum {
-    TAV_F32 = 0,  /* IEEE fp32 */
-    TAV_BF16 = 1  /* bfloat16 */
+    TAV_F32 = 0,      /* IEEE fp32 */
+    TAV_BF16 = 1,     /* bfloat16 */
+    TAV_FP8_E4M3 = 2  /* tree_attention only: K/V caches in FP8 E4M3 (1 byte:
+                         sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+                         infinities, NaN at all ones; unscaled), q and out bf16 */
 } tav_dtype;
 
 /* Text of the last failure on the calling thread ("" after a success). */
@@ -138,9 +141,13 @@ size_t tree_attention_workspace_size(tav_dtype dtype, int32_t B, int32_t R, int3
  *            >= max_prefix_len + W
  * masks      uint64 [B][R] (bits >= W are ignored)
  * B >= 0; 1 <= R <= 64; 0 <= W <= 64; Hq % Hkv == 0; D in {64, 128}
- * dtype      TAV_BF16 (bf16 MFMA prefix, fp32 accumulation) or TAV_F32
- *            (fp32 vector-ALU path)
- * out        [B][R][Hq][D] dtype (bf16 rounded to nearest even)
+ * dtype      TAV_BF16 (bf16 MFMA prefix, fp32 accumulation), TAV_F32
+ *            (fp32 vector-ALU path) or TAV_FP8_E4M3: an unscaled FP8 E4M3
+ *            K/V cache ([DTS] "One tree attention ...": an FP8 cache changes
+ *            no structure) with a bf16 query, which is not quantised; the
+ *            cache values are widened exactly to bf16 in LDS and the bf16
+ *            path runs on them.  Strides count elements (bytes for FP8).
+ * out        [B][R][Hq][D] in q's dtype (bf16 rounded to nearest even)
  * lse2       float [B][R][Hq] or NULL: log2 of the sum over visible keys of
  *            exp(score) (so 2^lse2 is the softmax denominator)
  * workspace  device memory of >= tree_attention_workspace_size(...) bytes,

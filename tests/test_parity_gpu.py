@@ -107,6 +107,21 @@ SMALL = {
                                        page_size=16), [500, 131]),
     # W = 33: a second, mostly empty 32-key window block
     "w33": (W_["random16"].with_(name="w33", B=2, P=640, N=33, depth_cap=5), [640, 90]),
+    # FP8 E4M3 K/V caches (bf16 query): every prefix kernel shape and the window
+    "fp8_rows64": (W_["random16"].with_(name="fp8_64", B=3, P=1000, kv_dtype="fp8"),
+                   [1000, 37, 513]),
+    "fp8_chain8": (W_["chain8"].with_(name="fp8_chain", B=4, P=2000, kv_dtype="fp8"),
+                   [2000, 1, 64, 1999]),
+    "fp8_lanes": (W_["lanes"].with_(name="fp8_lanes", B=4, P=5000, prefix_window=1000,
+                                    kv_dtype="fp8"), [5000, 999, 1000, 4500]),
+    "fp8_rows128": (W_["random16"].with_(name="fp8_128", B=2, P=900, N=32, kv_dtype="fp8"),
+                    [900, 700]),
+    "fp8_long64": (W_["long64"].with_(name="fp8_long", B=2, P=3000, kv_dtype="fp8"),
+                   [3000, 2049]),
+    "fp8_onesplit512": (W_["long64"].with_(name="fp8_one", B=2, P=500, N=64, Hq=32, Hkv=4,
+                                           page_size=16, kv_dtype="fp8"), [500, 131]),
+    "fp8_d64": (W_["random16"].with_(name="fp8_d64", B=2, P=777, N=16, Hq=8, Hkv=2, D=64,
+                                     kv_dtype="fp8"), [777, 100]),
 }
 
 
@@ -299,6 +314,32 @@ def test_nonfinite_window_values_reach_only_rows_that_see_them(shape):
     assert sees(j1).any() and sees(j2).any() and sees(j3).any(), "the tree must reach the poisoned nodes"
 
 
+@pytest.mark.parametrize("shape", ["rows64", "rows512"])
+def test_fp8_nonfinite_window_values(shape):
+    # FP8 E4M3 caches hold NaN but no infinities: NaN in window K at node j1
+    # and in one V channel at node j2
+    if shape == "rows64":
+        wl = gen.Workload("nf8", 1, 200, 16, 8, 2, 128, "bf16", 16, "random", depth_cap=4,
+                          kv_dtype="fp8")
+    else:
+        wl = gen.Workload("nf8", 2, 300, 64, 16, 2, 128, "bf16", 16, "random", depth_cap=6,
+                          kv_dtype="fp8")
+    inp = gen.make_inputs(wl, 13, "cuda")
+    j1, j2 = 2, 7
+    for j, cache, ch in ((j1, inp.k_cache, None), (j2, inp.v_cache, 33)):
+        t = int(inp.prefix_len[0]) + j
+        pg, sl = int(inp.page_table[0, t // wl.page_size]), t % wl.page_size
+        if ch is None:
+            cache[pg, 0, sl] = float("nan")
+        else:
+            cache[pg, 0, sl, ch] = float("nan")
+    m = oracle.build_masks(inp.parents)["masks"]
+    out, lse = run_attention(inp, dev(m.view(np.int64), torch.int64))
+    ro, rl = oracle_attention(inp, m)
+    _same_nonfinite(out.float().cpu().numpy(), ro.reshape(out.shape), OUT_TOL, shape + " fp8 out")
+    _same_nonfinite(lse.cpu().numpy(), rl.reshape(lse.shape), LSE_TOL, shape + " fp8 lse2")
+
+
 def test_bad_trees_flagged():
     par = np.array([[-1, 0, 0, 1, 2, 3, 4, 5],
                     [-1, 0, 5, 1, 2, 3, 4, 5],      # forward reference at node 2
@@ -352,7 +393,7 @@ def test_chain_equals_causal():
 # full workload sizes, sampled rows
 # ---------------------------------------------------------------------------
 
-FULL = ["random16", "eagle64", "long64", "lanes", "chain8"]
+FULL = ["random16", "eagle64", "long64", "lanes", "chain8", "long64_fp8"]
 
 
 @pytest.mark.parametrize("name", FULL)

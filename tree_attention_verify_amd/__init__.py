@@ -23,7 +23,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtreeverify.so")
 
-TAV_F32, TAV_BF16 = 0, 1
+TAV_F32, TAV_BF16, TAV_FP8_E4M3 = 0, 1, 2
 _STATUS = {0: "TAV_OK", 1: "TAV_ERR_INVALID_ARG", 2: "TAV_ERR_UNSUPPORTED",
            3: "TAV_ERR_WORKSPACE", 4: "TAV_ERR_HIP"}
 
@@ -148,9 +148,23 @@ def tree_shift_positions(positions: torch.Tensor, depth: torch.Tensor, direction
     return positions
 
 
+def _code(q_dtype, kv_dtype=None) -> int:
+    """tav_dtype of a (query, K/V cache) dtype pair."""
+    kv_dtype = q_dtype if kv_dtype is None else kv_dtype
+    if q_dtype == torch.bfloat16 and kv_dtype == torch.float8_e4m3fn:
+        return TAV_FP8_E4M3
+    if q_dtype != kv_dtype:
+        raise TypeError("K/V caches must have q's dtype, or be float8_e4m3fn under a bf16 q")
+    if q_dtype == torch.bfloat16:
+        return TAV_BF16
+    if q_dtype == torch.float32:
+        return TAV_F32
+    raise TypeError("q must be float32 or bfloat16, got %s" % q_dtype)
+
+
 def tree_attention_workspace_size(dtype, B, R, Hq, Hkv, D, max_prefix_len, prefix_window,
-                                  page_size) -> int:
-    code = TAV_BF16 if dtype == torch.bfloat16 else TAV_F32
+                                  page_size, kv_dtype=None) -> int:
+    code = _code(dtype, kv_dtype)
     return int(lib().tree_attention_workspace_size(code, B, R, Hq, Hkv, D, max_prefix_len,
                                                    prefix_window, page_size))
 
@@ -173,7 +187,8 @@ def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                    lse2: Optional[torch.Tensor] = None, return_lse: bool = True,
                    workspace: Optional[torch.Tensor] = None, phase: str = "all"):
     """Tree attention (see include/treeverify.h).  q [B][R][Hq][D] fp32/bf16;
-    k_cache/v_cache paged pools in `layout`; page_table int32 [B][max_pages];
+    k_cache/v_cache paged pools in `layout`, of q's dtype or float8_e4m3fn
+    under a bf16 q; page_table int32 [B][max_pages];
     prefix_len int32 [B]; masks int64 [B][R] (uint64 bit patterns).
     phase: "all" (tree_attention), "prefix" (tree_attention_prefix) or
     "window_merge" (tree_attention_window_merge; pass the workspace the
@@ -181,13 +196,12 @@ def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     Returns (out [B][R][Hq][D], lse2 float32 [B][R][Hq] or None)."""
     fn = {"all": "tree_attention", "prefix": "tree_attention_prefix",
           "window_merge": "tree_attention_window_merge"}[phase]
-    if q.dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError("q must be float32 or bfloat16")
+    dt = _code(q.dtype, k_cache.dtype)
     _need(q, "q", q.dtype)
     dev = q.device
     B, R, Hq, D = q.shape
-    _need(k_cache, "k_cache", q.dtype, dev)
-    _need(v_cache, "v_cache", q.dtype, dev)
+    _need(k_cache, "k_cache", k_cache.dtype, dev)
+    _need(v_cache, "v_cache", k_cache.dtype, dev)
     sp, sh, st, Hkv, ps = kv_strides(k_cache, layout)
     if tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("v_cache must have k_cache's shape")
@@ -196,7 +210,6 @@ def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         raise ValueError("page_table must be [B][max_pages]")
     _need(prefix_len, "prefix_len", torch.int32, dev, (B,))
     _need(masks, "masks", torch.int64, dev, (B, R))
-    dt = TAV_BF16 if q.dtype == torch.bfloat16 else TAV_F32
     if out is None:
         out = torch.empty_like(q)
     else:

@@ -101,6 +101,25 @@ __device__ __forceinline__ void dma_load16_s(const void *base, uint32_t voff, ui
                  : "memory", "m0");
 }
 
+// 16 FP8 E4M3 values (one 16-byte chunk) -> 16 bf16 values (two chunks);
+// the conversion is exact (every E4M3 value, NaN included, is a bf16 value).
+__device__ __forceinline__ void fp8x16_to_bf16(const int4 x, int4 &lo, int4 &hi) {
+    auto c0 = [](int w) {
+        return __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w, 1.0f, false));
+    };
+    auto c1 = [](int w) {
+        return __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w, 1.0f, true));
+    };
+    lo = make_int4(c0(x.x), c1(x.x), c0(x.y), c1(x.y));
+    hi = make_int4(c0(x.z), c1(x.z), c0(x.w), c1(x.w));
+}
+
+// fp32 value of one FP8 E4M3 code
+__device__ __forceinline__ float fp8_to_f32(uint8_t b) {
+    const int w = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)b, 1.0f, false));
+    return __uint_as_float((uint32_t)w << 16);
+}
+
 __device__ __forceinline__ uint32_t lds_off(const void *p) {
     return (uint32_t)(uintptr_t)(const LDS_AS void *)p;
 }
@@ -132,6 +151,15 @@ template <int N>
 __device__ inline void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Completes a value loaded from memory where it is called.  The compiler
+// otherwise places the wait for the load before the value's first use,
+// which inside a pipelined loop (with its state merged over the back edge)
+// becomes a wait for every outstanding load, the in-flight stages included.
+template <typename T>
+__device__ __forceinline__ void settle(T &x) {
+    asm volatile("" : "+v"(x));
 }
 
 struct PrefixArgs {
@@ -194,7 +222,7 @@ struct MfmaCfg {
 // blocks of 32 folded query rows x NKS key subsets; every wave owns 32 rows
 // and, per stage, one 32-key block.  With 8 waves a SIMD holds two waves, so
 // one wave's MFMAs overlap the other's softmax.
-template <int D, int NRB, int NKS>
+template <int D, int NRB, int NKS, bool KV8>
 __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a) {
     using C = MfmaCfg<D, NRB, NKS>;
     constexpr int SK = C::SK, CH = C::CH, ROWB = C::ROWB, SB = C::SB, NBUF = C::NBUF,
@@ -235,7 +263,7 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
     // consecutive keys) share a page, so loads take a wave-uniform page base;
     // stages then start at the 8-key boundary at or below the split start and
     // keys outside [lo, hi) are neither loaded nor visible.
-    const bool wave_pages = a.ps_shift >= 3;
+    const bool wave_pages = !KV8 && a.ps_shift >= 3;
     const int kb0 = wave_pages ? (kr.lo & ~7) : kr.lo;
     const int nkeys = kr.hi > kr.lo ? kr.hi - kb0 : 0;
     const int ns = (nkeys + SK - 1) / SK;
@@ -267,6 +295,9 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
             int4 v4 = ok ? *(const int4 *)(qp + 16 * kk) : make_int4(0, 0, 0, 0);
             qv[kk] = __builtin_bit_cast(bf16x8, v4);
         }
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk)
+            settle(qv[kk]);
     }
     __syncthreads();
 
@@ -338,6 +369,56 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
         }
     };
 
+    // FP8 E4M3 caches: each thread loads its 16-byte chunks (16 values of one
+    // row) of a stage into registers and converts them into the bf16 stage
+    // layout above, so the MFMA code is the bf16 code.  Two register sets
+    // (stage x in set x & 1) keep two stages in flight: as many bytes as one
+    // bf16 stage, twice the keys.
+    constexpr int C8 = D / 16;                                // 16-byte chunks per fp8 row
+    constexpr int LP8 = KV8 ? 2 * SK * C8 / THREADS : 1;      // chunks per thread and stage
+    static_assert(!KV8 || (2 * SK * C8) % THREADS == 0, "fp8 slot split");
+    int4 f8a[LP8], f8b[LP8];
+    // Every load is issued, also for stages past the last one (keys at or
+    // past the split end re-read its last key and are zeroed at conversion):
+    // with no conditional loads the compiler's count of outstanding loads is
+    // exact, and its wait for one set leaves the other in flight.
+    auto load8 = [&](int st, int4 (&f8)[LP8]) {
+        const int kst = kb0 + st * SK;
+        int64_t page[LP8];
+#pragma unroll
+        for (int i = 0; i < LP8; ++i) {
+            const int s2 = (i * THREADS + tid) % (SK * C8);
+            const int t = min(kst + s2 / C8, kr.hi - 1);
+            page[i] = pt[(t >> a.ps_shift) - lp0];
+        }
+#pragma unroll
+        for (int i = 0; i < LP8; ++i) {
+            const int slot = i * THREADS + tid;
+            const int region = slot / (SK * C8), s2 = slot % (SK * C8);
+            const int t = min(kst + s2 / C8, kr.hi - 1);
+            const uint8_t *src = (const uint8_t *)(region ? a.v : a.k) + page[i] * a.stride_page +
+                                 (int64_t)g * a.stride_head + (int64_t)(t & ps_mask) * a.stride_token +
+                                 (s2 % C8) * 16;
+            f8[i] = *(const int4 *)src;
+        }
+    };
+    auto convert8 = [&](int st, const int4 (&f8)[LP8]) {
+        char *buf = lds + (st % NBUF) * SB;
+#pragma unroll
+        for (int i = 0; i < LP8; ++i) {
+            const int slot = i * THREADS + tid;
+            const int region = slot / (SK * C8), s2 = slot % (SK * C8);
+            const int key = s2 / C8, c8 = s2 % C8;
+            int4 lo, hi;
+            fp8x16_to_bf16(f8[i], lo, hi);
+            if (kb0 + st * SK + key >= kr.hi)
+                lo = hi = make_int4(0, 0, 0, 0);
+            char *row = buf + region * (SB / 2) + key * ROWB;
+            *(int4 *)(row + (((2 * c8) ^ swz<D>(key)) * 16)) = lo;
+            *(int4 *)(row + (((2 * c8 + 1) ^ swz<D>(key)) * 16)) = hi;
+        }
+    };
+
     f32x16 o[DT];
     float m_run = -INFINITY, l_run = 0.f;
 #pragma unroll
@@ -346,31 +427,35 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
         for (int r = 0; r < 16; ++r)
             o[t][r] = 0.f;
 
-    for (int st = 0; st < NBUF - 1 && st < ns; ++st)
-        issue(st);
+    // convert stage st + 1 (stage st + 2 stays in flight) and reuse its
+    // register set for stage st + 3
+    auto advance8 = [&](int st, int4 (&f8)[LP8]) {
+        convert8(st + 1, f8);
+        load8(st + 3, f8);
+    };
+    if constexpr (KV8) {
+        if (ns > 0) {
+            load8(0, f8a);
+            load8(1, f8b);
+            convert8(0, f8a);
+            load8(2, f8a);
+        }
+    } else {
+        for (int st = 0; st < NBUF - 1 && st < ns; ++st)
+            issue(st);
+    }
 
     const int G16 = lane >> 4, a4 = lane & 3, j4 = (lane >> 2) & 3;
     const int key0 = ks * 32;
     const int krow = key0 + l32;                 // K operand: key of this lane
     const int ksw = swz<D>(krow);
-    for (int it = 0; it < ns; ++it) {
-        // Stage `it` is complete once at most the loads of the later, full
-        // stages are outstanding.  When the last (partial) stage is among the
-        // outstanding ones some of its instructions may be skipped, so wait
-        // for everything then.
-        if (it + NBUF - 2 < ns - 1)
-            wait_vmcnt<(NBUF - 2) * LPS>();
-        else
-            wait_vmcnt<0>();
-        __syncthreads();  // every wave's loads of stage it landed; stage it-1 is free
-        if (it + NBUF - 1 < ns)
-            issue(it + NBUF - 1);
-
+    // one stage of keys: S, softmax weights and O for this wave's 32 keys
+    auto compute = [&](int it) {
         const char *Kb = lds + (it % NBUF) * SB;
         const char *Vb = Kb + SB / 2;
         const int first = kb0 + it * SK + key0;  // absolute key of this wave's block
         if (first >= kr.hi)
-            continue;
+            return;
         // S^T[key][row] = sum_d K[key][d] Q[row][d]
         f32x16 s;
 #pragma unroll
@@ -447,6 +532,37 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
                 o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[cc], o[t], 0, 0, 0);
             }
         }
+    };
+
+    if constexpr (KV8) {
+        // Stage it was converted in the previous trip; after the barrier no
+        // wave reads the buffer stage it + 1 is converted into.  Unrolled by
+        // two so each trip names its register set statically; a trip past
+        // the last stage computes nothing (its keys are all at or past the
+        // split end).
+        for (int it = 0; it < ns; it += 2) {
+            __syncthreads();
+            advance8(it, f8b);
+            compute(it);
+            __syncthreads();
+            advance8(it + 1, f8a);
+            compute(it + 1);
+        }
+    } else {
+        for (int it = 0; it < ns; ++it) {
+            // Stage `it` is complete once at most the loads of the later, full
+            // stages are outstanding.  When the last (partial) stage is among
+            // the outstanding ones some of its instructions may be skipped, so
+            // wait for everything then.
+            if (it + NBUF - 2 < ns - 1)
+                wait_vmcnt<(NBUF - 2) * LPS>();
+            else
+                wait_vmcnt<0>();
+            __syncthreads();  // every wave's loads of stage it landed; stage it-1 is free
+            if (it + NBUF - 1 < ns)
+                issue(it + NBUF - 1);
+            compute(it);
+        }
     }
 
     // partial (O / l, lse2) of this split and key subset
@@ -514,7 +630,7 @@ __device__ inline int yv(int k, int cg) { return 2 * ((k & 3) ^ (cg & 1)); }
 constexpr float kSumLimit = 1048576.f;   // 2^20
 
 
-template <int D, int SK_>
+template <int D, int SK_, bool KV8>
 struct PipeCfg {
     static constexpr int WAVES = 8;
     static constexpr int THREADS = 64 * WAVES;
@@ -522,10 +638,17 @@ struct PipeCfg {
     static constexpr int BPS = SK / 32;           // 32-key blocks per stage
     static constexpr int KSTEPS = D / 16;
     static constexpr int DT = D / 32;
-    static constexpr int KREG = SK * D * 2;       // bytes of the K region
-    static constexpr int SB = 2 * KREG;           // stage bytes
+    static constexpr int KREG = SK * D * 2;       // bytes of the K region (bf16)
+    static constexpr int SB = 2 * KREG;           // stage bytes (bf16)
+    // FP8 E4M3 caches: a ring of F8 raw stages (half the bytes) feeds a ring
+    // of 3 converted bf16 stages
+    static constexpr int F8 = 3;
+    static constexpr int SB8 = SB / 2;
+    static constexpr int LPS8 = SB8 / (THREADS * 16);
     static constexpr int NBUF0 = kLdsStageBudget / SB;
-    static constexpr int NBUF = NBUF0 > 12 ? 12 : NBUF0;
+    static constexpr int NBUF = KV8 ? 3 : (NBUF0 > 12 ? 12 : NBUF0);
+    static_assert(!KV8 || (LPS8 >= 1 && SB8 % (THREADS * 16) == 0 && NBUF * SB + F8 * SB8 <= kLdsStageBudget),
+                  "fp8 stage split");
     static constexpr int PF = NBUF - 2;           // stages in flight ahead of the current one
     static constexpr int LPS = SB / (THREADS * 16);
     static_assert(THREADS == SK * 8, "one load instruction covers every key of a stage");
@@ -534,15 +657,16 @@ struct PipeCfg {
     static_assert((PF - 1) * LPS < 64, "vmcnt range");
 };
 
-template <int D, int SK_>
+template <int D, int SK_, bool KV8>
 __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
-    using C = PipeCfg<D, SK_>;
+    using C = PipeCfg<D, SK_, KV8>;
     constexpr int BPS = C::BPS;
     constexpr int SK = C::SK, SB = C::SB, NBUF = C::NBUF, PF = C::PF, LPS = C::LPS,
                   THREADS = C::THREADS, KREG = C::KREG, KSTEPS = C::KSTEPS, DT = C::DT;
     constexpr int ROWS_WG = 256;
 
-    __shared__ __attribute__((aligned(16))) char lds[NBUF * SB];
+    constexpr int F8 = C::F8, SB8 = C::SB8, LPS8 = C::LPS8;
+    __shared__ __attribute__((aligned(16))) char lds[NBUF * SB + (KV8 ? F8 * SB8 : 0)];
     __shared__ int32_t pt[kPtMax];
 
     const int tid = threadIdx.x;
@@ -567,7 +691,7 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
     const int b = unit / (a.n_split * a.Hkv);
 
     const KeyRange kr = split_range(a, b, split);
-    const bool wave_pages = a.ps_shift >= 3;
+    const bool wave_pages = !KV8 && a.ps_shift >= 3;
     // stages cover [kb0, hi); kb0 is in the page of lo
     const int kb0 = wave_pages ? (kr.lo & ~7) : kr.lo;
     const int nkeys = kr.hi > kr.lo ? kr.hi - kb0 : 0;
@@ -594,6 +718,9 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
             int4 v4 = ok ? *(const int4 *)(qp + 16 * kk) : make_int4(0, 0, 0, 0);
             qv[kk] = __builtin_bit_cast(bf16x8, v4);
         }
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk)
+            settle(qv[kk]);
     }
     __syncthreads();
 
@@ -652,7 +779,7 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
     // are outstanding (all of them when the partial last stage is among
     // them); then the barrier publishes every wave's loads and frees the
     // buffer of stage st - 2 for stage st + PF.
-    auto stage_ready = [&](int st) {
+    auto stage_ready_bf16 = [&](int st) {
         if (st + PF - 1 < ns - 1)
             wait_vmcnt<(PF - 1) * LPS>();
         else
@@ -660,6 +787,80 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
         __syncthreads();
         if (st + PF < ns)
             issue(st + PF);
+    };
+
+    // FP8 E4M3 caches.  Raw slot i * THREADS + tid of a stage holds 16-byte
+    // chunk c8 of key `key` of region K or V; the thread that loads it also
+    // converts it (after its own load has landed) into bf16 chunks 2 c8 and
+    // 2 c8 + 1 of the piece layout, so the raw ring needs no barrier.
+    constexpr int C8 = D / 16;
+    const uint32_t lds8 = lds0 + (uint32_t)(NBUF * SB);
+    auto slot8 = [&](int i, int &region, int &key, int &c8) {
+        const int slot = i * THREADS + tid;
+        region = slot / (SK * C8);
+        const int s2 = slot % (SK * C8);
+        key = s2 / C8;
+        c8 = s2 % C8;
+    };
+    auto issue8 = [&](int st) {
+        const int kst = kb0 + st * SK;
+        const uint32_t rbase = lds8 + (uint32_t)((st % F8) * SB8);
+#pragma unroll 1
+        for (int i = 0; i < LPS8; ++i) {
+            int region, key, c8;
+            slot8(i, region, key, c8);
+            const int t = kst + key;
+            const int64_t page = t < kr.hi ? pt[(t >> a.ps_shift) - lp0] : 0;
+            const uint8_t *src = (const uint8_t *)(region ? a.v : a.k) + page * a.stride_page +
+                                 (int64_t)g * a.stride_head + (int64_t)(t & ps_mask) * a.stride_token +
+                                 c8 * 16;
+            if (t < kr.hi)
+                dma_load16(src, __builtin_amdgcn_readfirstlane(rbase + (i * THREADS + w * 64) * 16));
+        }
+    };
+    auto convert8 = [&](int st) {
+        const int kst = kb0 + st * SK;
+        const char *raw = lds + NBUF * SB + (st % F8) * SB8;
+        char *buf = lds + (st % NBUF) * SB;
+#pragma unroll 1
+        for (int i = 0; i < LPS8; ++i) {
+            int region, key, c8;
+            slot8(i, region, key, c8);
+            int4 x = make_int4(0, 0, 0, 0);
+            if (kst + key < kr.hi)
+                x = *(const int4 *)(raw + (i * THREADS + tid) * 16);
+            int4 h[2];
+            fp8x16_to_bf16(x, h[0], h[1]);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int c = 2 * c8 + e, cg = c / 8;
+                const int pos = (c % 8) ^ (region ? yv(key, cg) : xk(key));
+                *(int4 *)(buf + region * KREG + cg * (SK * 128) + key * 128 + pos * 16) = h[e];
+            }
+        }
+    };
+    // Stage st is ready once its conversion (one stage earlier) is published:
+    // wait for this thread's raw chunks of stage st + 1 (those of st + 2 may
+    // still be in flight), publish, convert st + 1, and issue st + 3 into
+    // the raw buffer st has left.
+    auto stage_ready8 = [&](int st) {
+        if (st + 1 < ns) {
+            if (st + 2 <= ns - 2)
+                wait_vmcnt<LPS8>();
+            else
+                wait_vmcnt<0>();
+        }
+        __syncthreads();
+        if (st + 1 < ns)
+            convert8(st + 1);
+        if (st + F8 < ns)
+            issue8(st + F8);
+    };
+    auto stage_ready = [&](int st) {
+        if constexpr (KV8)
+            stage_ready8(st);
+        else
+            stage_ready_bf16(st);
     };
 
     // per-lane operand offsets inside a stage (piece layout)
@@ -804,8 +1005,20 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
         }
     };
 
-    for (int st = 0; st < PF && st < ns; ++st)
-        issue(st);
+    if constexpr (KV8) {
+        for (int st = 0; st < F8 && st < ns; ++st)
+            issue8(st);
+        if (ns > 0) {
+            if (ns >= F8 + 1)
+                wait_vmcnt<(F8 - 1) * LPS8>();
+            else
+                wait_vmcnt<0>();
+            convert8(0);
+        }
+    } else {
+        for (int st = 0; st < PF && st < ns; ++st)
+            issue(st);
+    }
     if (nb > 0) {
         stage_ready(0);
         bf16x8 ka[KSTEPS], va[DT][2], pa[2], pbb[2];
@@ -1111,10 +1324,12 @@ __global__ void __launch_bounds__(256) k_window_merge(MergeArgs a) {
 // flagged key then adds, per channel, the sum of the non-finite values of
 // its visible flagged keys to its window output, which is what the exact
 // weighted sum gives (positive weights keep infinities and NaN).
-template <int D, int NW>
+template <int D, int NW, bool KV8>
 __global__ void __launch_bounds__(64 * NW) k_window_mfma(MergeArgs a) {
     constexpr int KSTEPS = D / 16, DT = D / 32, CH = D / 8, ROWB = D * 2;
     constexpr int THREADS = 64 * NW;
+    constexpr int NL = 64 * CH / THREADS;   // bf16 slots per thread and region
+    static_assert(64 * CH % THREADS == 0, "slot split");
     __shared__ __attribute__((aligned(16))) char kw[64 * ROWB];
     __shared__ __attribute__((aligned(16))) char vw[64 * ROWB];
     __shared__ uint32_t bad[2];   // keys 0..31, 32..63 with a non-finite V value
@@ -1134,37 +1349,77 @@ __global__ void __launch_bounds__(64 * NW) k_window_mfma(MergeArgs a) {
     const int W = a.W;
     const int ps_mask = (1 << a.ps_shift) - 1;
 
-    // Stage the window keys: key k's 16-byte chunk c sits at LDS byte
-    // k * ROWB + 16 (c ^ swz(k)).  Slot i = k * CH + pos of a region is filled
-    // by a direct-to-LDS load of chunk pos ^ swz(k); rows of keys >= W are
-    // zero.
-    constexpr int NL = 64 * CH / THREADS;   // slots per thread and region
-    static_assert(64 * CH % THREADS == 0, "slot split");
     if (tid < 2)
         bad[tid] = 0u;
-    int32_t pg[NL];
+    if constexpr (KV8) {
+        // FP8 E4M3 caches: each thread loads 16-byte chunks (16 values) of
+        // K and V, converts them exactly to bf16, zeroes and flags non-finite
+        // V values, and writes the bf16 layout below
+        constexpr int C8 = D / 16;
+        __syncthreads();
+        for (int i = tid; i < 64 * C8; i += THREADS) {
+            const int key = i / C8, c8 = i % C8;
+            int4 k8 = make_int4(0, 0, 0, 0), v8 = make_int4(0, 0, 0, 0);
+            if (key < W) {
+                const int t = P + key;
+                const int64_t page = clamp_page(a.page_table[(int64_t)b * a.max_pages + (t >> a.ps_shift)],
+                                                a.num_pages);
+                const int64_t off = page * a.stride_page + (int64_t)g * a.stride_head +
+                                    (int64_t)(t & ps_mask) * a.stride_token + c8 * 16;
+                k8 = *(const int4 *)((const uint8_t *)a.k + off);
+                v8 = *(const int4 *)((const uint8_t *)a.v + off);
+            }
+            int4 kh[2], vh[2];
+            fp8x16_to_bf16(k8, kh[0], kh[1]);
+            fp8x16_to_bf16(v8, vh[0], vh[1]);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        const int key = (i * THREADS + tid) / CH;
-        const int t = P + (key < W ? key : 0);
-        pg[i] = key < W ? (int32_t)clamp_page(a.page_table[(int64_t)b * a.max_pages + (t >> a.ps_shift)],
-                                              a.num_pages)
-                        : 0;
-    }
-    const uint32_t kw0 = lds_off(kw), vw0 = lds_off(vw);
+            for (int e = 0; e < 2; ++e) {
+                uint32_t x[4] = {(uint32_t)vh[e].x, (uint32_t)vh[e].y, (uint32_t)vh[e].z, (uint32_t)vh[e].w};
+                bool nf = false;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        const int slot = i * THREADS + tid, key = slot / CH, pos = slot % CH;
-        if (key < W) {
-            const int t = P + key;
-            const int64_t off = (int64_t)pg[i] * a.stride_page + (int64_t)g * a.stride_head +
-                                (int64_t)(t & ps_mask) * a.stride_token + ((pos ^ swz<D>(key)) * 8);
-            const uint32_t at = (uint32_t)((i * THREADS + w * 64) * 16);
-            dma_load16((const uint16_t *)a.k + off, __builtin_amdgcn_readfirstlane(kw0 + at));
-            dma_load16((const uint16_t *)a.v + off, __builtin_amdgcn_readfirstlane(vw0 + at));
-        } else {
-            *(int4 *)(kw + slot * 16) = make_int4(0, 0, 0, 0);
-            *(int4 *)(vw + slot * 16) = make_int4(0, 0, 0, 0);
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int hh2 = 0; hh2 < 2; ++hh2)
+                        if (((x[q] >> (16 * hh2)) & 0x7F80u) == 0x7F80u) {
+                            nf = true;
+                            x[q] &= ~(0xFFFFu << (16 * hh2));
+                        }
+                if (nf)
+                    atomicOr(&bad[key >> 5], 1u << (key & 31));
+                const int at = key * ROWB + (((2 * c8 + e) ^ swz<D>(key)) * 16);
+                *(int4 *)(kw + at) = kh[e];
+                *(int4 *)(vw + at) = make_int4((int)x[0], (int)x[1], (int)x[2], (int)x[3]);
+            }
+        }
+    } else {
+        // Stage the window keys: key k's 16-byte chunk c sits at LDS byte
+        // k * ROWB + 16 (c ^ swz(k)).  Slot i = k * CH + pos of a region is filled
+        // by a direct-to-LDS load of chunk pos ^ swz(k); rows of keys >= W are
+        // zero.
+        int32_t pg[NL];
+    #pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int key = (i * THREADS + tid) / CH;
+            const int t = P + (key < W ? key : 0);
+            pg[i] = key < W ? (int32_t)clamp_page(a.page_table[(int64_t)b * a.max_pages + (t >> a.ps_shift)],
+                                                  a.num_pages)
+                            : 0;
+        }
+        const uint32_t kw0 = lds_off(kw), vw0 = lds_off(vw);
+    #pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int slot = i * THREADS + tid, key = slot / CH, pos = slot % CH;
+            if (key < W) {
+                const int t = P + key;
+                const int64_t off = (int64_t)pg[i] * a.stride_page + (int64_t)g * a.stride_head +
+                                    (int64_t)(t & ps_mask) * a.stride_token + ((pos ^ swz<D>(key)) * 8);
+                const uint32_t at = (uint32_t)((i * THREADS + w * 64) * 16);
+                dma_load16((const uint16_t *)a.k + off, __builtin_amdgcn_readfirstlane(kw0 + at));
+                dma_load16((const uint16_t *)a.v + off, __builtin_amdgcn_readfirstlane(vw0 + at));
+            } else {
+                *(int4 *)(kw + slot * 16) = make_int4(0, 0, 0, 0);
+                *(int4 *)(vw + slot * 16) = make_int4(0, 0, 0, 0);
+            }
         }
     }
     const int m = rg * 32 * NW + w * 32 + l32;   // this lane's folded row
@@ -1187,7 +1442,7 @@ __global__ void __launch_bounds__(64 * NW) k_window_mfma(MergeArgs a) {
     __syncthreads();
     // non-finite V values: zero them in LDS and flag their keys
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
+    for (int i = 0; i < (KV8 ? 0 : NL); ++i) {
         const int slot = i * THREADS + tid, key = slot / CH;
         if (key < W) {
             uint4 u = *(const uint4 *)(vw + slot * 16);
@@ -1300,15 +1555,16 @@ __global__ void __launch_bounds__(64 * NW) k_window_mfma(MergeArgs a) {
             const int t_ = P + j;
             const int64_t page =
                 clamp_page(a.page_table[(int64_t)b * a.max_pages + (t_ >> a.ps_shift)], a.num_pages);
-            const uint16_t *vr = (const uint16_t *)a.v + page * a.stride_page +
-                                 (int64_t)g * a.stride_head + (int64_t)(t_ & ps_mask) * a.stride_token;
+            const int64_t vo = page * a.stride_page + (int64_t)g * a.stride_head +
+                               (int64_t)(t_ & ps_mask) * a.stride_token;
 #pragma unroll
             for (int t = 0; t < DT; ++t)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const uint16_t h = vr[chan(t, e)];
-                    if ((h & 0x7F80u) == 0x7F80u)
-                        o[t][e] += bf16_bits_to_f32(h);
+                    const float x = KV8 ? fp8_to_f32(((const uint8_t *)a.v)[vo + chan(t, e)])
+                                        : bf16_bits_to_f32(((const uint16_t *)a.v)[vo + chan(t, e)]);
+                    if (!(fabsf(x) < INFINITY))
+                        o[t][e] += x;
                 }
         }
     }
@@ -1451,7 +1707,7 @@ Plan make_plan(tav_dtype dtype, int B, int R, int Hq, int Hkv, int D, int max_pr
     const long long M = (long long)R * G;
     const int max_vis = prefix_window > 0 && prefix_window < max_prefix_len ? prefix_window
                                                                             : max_prefix_len;
-    if (dtype == TAV_BF16) {
+    if (dtype == TAV_BF16 || dtype == TAV_FP8_E4M3) {
         p.mfma = true;
         p.NT = 1;
         if (M <= 32) {
@@ -1517,8 +1773,8 @@ bool shape_ok(tav_dtype dtype, int B, int R, int Hq, int Hkv, int D, int max_pre
     tav::Checks local;
     tav::Checks &k = c ? *c : local;
     using tav::str;
-    k.need(dtype == TAV_F32 || dtype == TAV_BF16, TAV_ERR_UNSUPPORTED,
-           "dtype must be TAV_F32 or TAV_BF16, got " + str(dtype));
+    k.need(dtype == TAV_F32 || dtype == TAV_BF16 || dtype == TAV_FP8_E4M3, TAV_ERR_UNSUPPORTED,
+           "dtype must be TAV_F32, TAV_BF16 or TAV_FP8_E4M3, got " + str(dtype));
     k.need(B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
     k.need(R >= 1 && R <= 64, TAV_ERR_INVALID_ARG, "R must be in [1, 64], got " + str(R));
     k.need(Hq >= 1 && Hkv >= 1, TAV_ERR_INVALID_ARG,
@@ -1536,23 +1792,23 @@ bool shape_ok(tav_dtype dtype, int B, int R, int Hq, int Hkv, int D, int max_pre
     return k.status == TAV_OK;
 }
 
-template <int D, int NRB, int NKS>
+template <int D, int NRB, int NKS, bool KV8>
 void launch_mfma(const Plan &p, const PrefixArgs &a, hipStream_t s) {
     const unsigned grid = (unsigned)((long long)a.B * a.Hkv * p.RG * p.n_split);
-    hipLaunchKernelGGL((k_prefix_mfma<D, NRB, NKS>), dim3(grid), dim3(64 * NRB * NKS), 0, s, a);
+    hipLaunchKernelGGL((k_prefix_mfma<D, NRB, NKS, KV8>), dim3(grid), dim3(64 * NRB * NKS), 0, s, a);
 }
 
-template <int D>
+template <int D, bool KV8>
 void launch_mfma_d(const Plan &p, const PrefixArgs &a, hipStream_t s) {
     if (p.NRB == 1)
-        launch_mfma<D, 1, 4>(p, a, s);
+        launch_mfma<D, 1, 4, KV8>(p, a, s);
     else if (p.NRB == 2)
-        launch_mfma<D, 2, 4>(p, a, s);
+        launch_mfma<D, 2, 4, KV8>(p, a, s);
     else if (p.NRB == 4)
-        launch_mfma<D, 4, 2>(p, a, s);
+        launch_mfma<D, 4, 2, KV8>(p, a, s);
     else {
         const unsigned grid = (unsigned)((long long)a.B * a.Hkv * p.RG * p.n_split);
-        hipLaunchKernelGGL((k_prefix_mfma_pipe<D, kPipeStageKeys>), dim3(grid), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((k_prefix_mfma_pipe<D, kPipeStageKeys, KV8>), dim3(grid), dim3(512), 0, s, a);
     }
 }
 
@@ -1562,7 +1818,8 @@ struct Call {
     PrefixArgs a;
     MergeArgs m;
     int D;
-    bool bf16;
+    bool bf16;   // bf16 query and output (bf16 or FP8 K/V)
+    bool kv8;    // FP8 E4M3 K/V
 };
 
 // Validates every argument (all failures are reported together) and builds
@@ -1586,7 +1843,7 @@ tav_status prepare(const char *fn, int phase, Call &call, const void *q, const v
                ") must cover max_prefix_len + W (" + str((long long)max_prefix_len + W) + ")");
     c.need(num_pages >= 1, TAV_ERR_INVALID_ARG, "num_pages must be >= 1, got " + str(num_pages));
     c.need(std::isfinite(sm_scale), TAV_ERR_INVALID_ARG, "sm_scale must be finite");
-    const int esz = dtype == TAV_F32 ? 4 : 2;
+    const int esz = dtype == TAV_F32 ? 4 : (dtype == TAV_FP8_E4M3 ? 1 : 2);   // K/V element bytes
     c.need(stride_page >= 0 && stride_head >= 0 && stride_token >= 0, TAV_ERR_INVALID_ARG,
            "strides must be >= 0");
     c.need((stride_page * esz) % 16 == 0 && (stride_head * esz) % 16 == 0 &&
@@ -1652,7 +1909,7 @@ tav_status prepare(const char *fn, int phase, Call &call, const void *q, const v
     m.q = q;
     m.k = k_cache;
     m.v = v_cache;
-    m.bf16 = dtype == TAV_BF16;
+    m.bf16 = dtype != TAV_F32;
     m.stride_page = stride_page;
     m.stride_head = stride_head;
     m.stride_token = stride_token;
@@ -1677,7 +1934,8 @@ tav_status prepare(const char *fn, int phase, Call &call, const void *q, const v
     m.out = out;
     m.lse2 = lse2;
     call.D = D;
-    call.bf16 = dtype == TAV_BF16;
+    call.bf16 = dtype != TAV_F32;
+    call.kv8 = dtype == TAV_FP8_E4M3;
     return TAV_OK;
 }
 
@@ -1685,9 +1943,9 @@ void launch_prefix(const Call &c, hipStream_t s) {
     const Plan &p = c.p;
     if (p.mfma) {
         if (c.D == 128)
-            launch_mfma_d<128>(p, c.a, s);
+            c.kv8 ? launch_mfma_d<128, true>(p, c.a, s) : launch_mfma_d<128, false>(p, c.a, s);
         else
-            launch_mfma_d<64>(p, c.a, s);
+            c.kv8 ? launch_mfma_d<64, true>(p, c.a, s) : launch_mfma_d<64, false>(p, c.a, s);
     } else {
         const unsigned grid = (unsigned)((long long)c.a.B * c.a.R * c.a.Hq * p.n_split);
         if (c.D == 128)
@@ -1697,22 +1955,22 @@ void launch_prefix(const Call &c, hipStream_t s) {
     }
 }
 
-template <int D, int NW>
+template <int D, int NW, bool KV8>
 void launch_window_mfma(const MergeArgs &m, hipStream_t s) {
     const int M = m.R * m.G;
     const unsigned grid = (unsigned)((long long)m.B * m.Hkv * ((M + 32 * NW - 1) / (32 * NW)));
-    hipLaunchKernelGGL((k_window_mfma<D, NW>), dim3(grid), dim3(64 * NW), 0, s, m);
+    hipLaunchKernelGGL((k_window_mfma<D, NW, KV8>), dim3(grid), dim3(64 * NW), 0, s, m);
 }
 
-template <int D>
+template <int D, bool KV8>
 void launch_window_mfma_d(const MergeArgs &m, hipStream_t s) {
     const int M = m.R * m.G;
     if (M <= 32)
-        launch_window_mfma<D, 1>(m, s);
+        launch_window_mfma<D, 1, KV8>(m, s);
     else if (M <= 64)
-        launch_window_mfma<D, 2>(m, s);
+        launch_window_mfma<D, 2, KV8>(m, s);
     else
-        launch_window_mfma<D, 4>(m, s);
+        launch_window_mfma<D, 4, KV8>(m, s);
 }
 
 void launch_merge(const Call &c, hipStream_t s) {
@@ -1721,11 +1979,11 @@ void launch_merge(const Call &c, hipStream_t s) {
     if (c.bf16) {
         // with a single prefix partial the window kernel writes the output
         if (c.D == 128) {
-            launch_window_mfma_d<128>(m, s);
+            c.kv8 ? launch_window_mfma_d<128, true>(m, s) : launch_window_mfma_d<128, false>(m, s);
             if (m.S > 2)
                 hipLaunchKernelGGL(k_merge<128>, dim3(grid), dim3(256), 0, s, m);
         } else {
-            launch_window_mfma_d<64>(m, s);
+            c.kv8 ? launch_window_mfma_d<64, true>(m, s) : launch_window_mfma_d<64, false>(m, s);
             if (m.S > 2)
                 hipLaunchKernelGGL(k_merge<64>, dim3(grid), dim3(256), 0, s, m);
         }

@@ -105,6 +105,8 @@ WORKLOADS = {
     # the long-context workload over an FP8 E4M3 K/V cache (bf16 query and output)
     "long64_fp8": Workload("long64_fp8", 4, 131072, 64, 32, 8, 128, "bf16", 64, "random",
                            depth_cap=8, kv_dtype="fp8"),
+    "chain8_fp8": Workload("chain8_fp8", 64, 32768, 8, 32, 8, 128, "bf16", 16, "chain",
+                           kv_dtype="fp8"),
 }
 
 
