@@ -61,6 +61,8 @@ def lib():
         L.orc_shift_positions.argtypes = [P, P, I, I, I]
         L.orc_e4m3_decode.argtypes = [I]
         L.orc_e4m3_decode.restype = D
+        L.orc_e4m3_round.argtypes = [D]
+        L.orc_e4m3_round.restype = D
         L.orc_tree_attention.argtypes = [P, P, P, I, I, I64, I64, I64, P, I, I, P, I,
                                          P, I, I, I, I, I, I, D, P, I64, P, P]
         L.orc_causal_attention.argtypes = [P, P, P, I, I, I, I, I, I, D, P, P]
@@ -99,6 +101,13 @@ def e4m3_decode(codes) -> np.ndarray:
     """fp64 values of FP8 E4M3 codes (the oracle's decoder)."""
     codes = np.asarray(codes, dtype=np.int64).ravel()
     return np.array([lib().orc_e4m3_decode(int(c)) for c in codes], np.float64)
+
+
+def e4m3_round(x) -> np.ndarray:
+    """Each value rounded to the nearest E4M3 value (ties to even, saturating
+    at +-448, NaN kept), as fp64."""
+    x = np.asarray(x, np.float64).ravel()
+    return np.array([lib().orc_e4m3_round(float(v)) for v in x], np.float64)
 
 
 def _check(rc, name):

@@ -72,6 +72,32 @@ double orc_e4m3_decode(int code)
     return orc_e4m3((uint8_t)code);
 }
 
+/*
+ * x rounded to the nearest E4M3 value, ties to the even code (mantissa LSB
+ * 0); magnitudes past the largest finite value (448) give +-448, NaN stays
+ * NaN.  Written as a search over the 127 non-negative finite codes, whose
+ * values increase with the code.  This is the cast of the query that the
+ * prefix half of the cascade takes under an FP8 cache ([DTS] "One tree
+ * attention ...": the leaf's decode takes the query cast to FP8, the window
+ * kernel the unquantised query).
+ */
+double orc_e4m3_round(double x)
+{
+    if (isnan(x))
+        return NAN;
+    double a = fabs(x) > 448.0 ? 448.0 : fabs(x), best = 0.0, err = INFINITY;
+    int best_code = 0;
+    for (int c = 0; c < 127; ++c) {
+        double v = orc_e4m3((uint8_t)c), e = fabs(v - a);
+        if (e < err || (e == err && (c & 1) == 0 && (best_code & 1) == 1)) {
+            err = e;
+            best = v;
+            best_code = c;
+        }
+    }
+    return x < 0 || (x == 0 && signbit(x)) ? -best : best;
+}
+
 /* ------------------------------------------------------------------ */
 /* tree metadata                                                       */
 /* ------------------------------------------------------------------ */
@@ -162,7 +188,8 @@ int orc_shift_positions(int32_t *pos, const int32_t *depth, int B, int N,
 
 /*
  * Softmax attention of one query row over an ordered list of keys, in fp64.
- * s_t = scale * sum_d q[d] k_t[d];  m = max s;  Z = sum exp(s_t - m);
+ * s_t = scale * sum_d q[d] k_t[d], where the first nq8 keys take q rounded
+ * to E4M3 (orc_e4m3_round) instead of q;  m = max s;  Z = sum exp(s_t - m);
  * o = sum exp(s_t - m) v_t / Z;  lse2 = (m + ln Z) / ln 2, the base-2
  * log-sum-exp of the scores ([DTS] "One tree attention ...": both halves of
  * the cascade carry a base-2 log-sum-exp).  No key: o = 0, lse2 = -inf.
@@ -170,7 +197,7 @@ int orc_shift_positions(int32_t *pos, const int32_t *depth, int B, int N,
  */
 static void orc_softmax_row(const void *qb, int64_t qofs, const void *kb,
                             const void *vb, int qdt, int kvdt, const int64_t *kofs,
-                            int nk, int D, double scale, double *s,
+                            int nk, int nq8, int D, double scale, double *s,
                             double *out, double *lse2)
 {
     for (int d = 0; d < D; ++d)
@@ -179,11 +206,17 @@ static void orc_softmax_row(const void *qb, int64_t qofs, const void *kb,
         *lse2 = -INFINITY;
         return;
     }
+    double *qv = (double *)malloc(sizeof(double) * 2 * D), *q8 = qv + D;
+    for (int d = 0; d < D; ++d) {
+        qv[d] = orc_load(qb, qdt, qofs + d);
+        q8[d] = orc_e4m3_round(qv[d]);
+    }
     double m = -INFINITY;
     for (int t = 0; t < nk; ++t) {
+        const double *qq = t < nq8 ? q8 : qv;
         double acc = 0.0;
         for (int d = 0; d < D; ++d)
-            acc += orc_load(qb, qdt, qofs + d) * orc_load(kb, kvdt, kofs[t] + d);
+            acc += qq[d] * orc_load(kb, kvdt, kofs[t] + d);
         s[t] = scale * acc;
         if (s[t] > m)
             m = s[t];
@@ -198,6 +231,7 @@ static void orc_softmax_row(const void *qb, int64_t qofs, const void *kb,
     for (int d = 0; d < D; ++d)
         out[d] /= Z;
     *lse2 = (m + log(Z)) / log(2.0);
+    free(qv);
 }
 
 /*
@@ -220,8 +254,12 @@ static void orc_softmax_row(const void *qb, int64_t qofs, const void *kb,
  * page*stride_page + g*stride_head + slot*stride_token, channels contiguous.
  * Keys that are not visible are never read.
  *
- * q holds dtype elements, k_cache and v_cache kv_dtype elements (an FP8
- * cache takes a bf16 query, which is not quantised).
+ * q holds dtype elements, k_cache and v_cache kv_dtype elements.  An FP8
+ * cache takes a bf16 query: prefix keys are scored with the query rounded
+ * to E4M3, window keys with the bf16 query itself ([DTS] "One tree
+ * attention ...": the leaf's decode takes the query cast to FP8, while the
+ * window kernel takes the unquantised query and widens the window's FP8
+ * K/V after loading them).
  * rows: optional list of flat row ids ((b*R + r)*Hq + h); out/lse2 then hold
  * n_rows entries in list order.  With rows == NULL every row is computed and
  * out is [B][R][Hq][D], lse2 [B][R][Hq].
@@ -255,7 +293,7 @@ int orc_tree_attention(const void *q, const void *k_cache, const void *v_cache,
         int nk_max = P - p_lo + W;
         int64_t *kofs = (int64_t *)malloc(sizeof(int64_t) * (nk_max > 0 ? nk_max : 1));
         double *s = (double *)malloc(sizeof(double) * (nk_max > 0 ? nk_max : 1));
-        int nk = 0;
+        int nk = 0, nq8 = 0;
         uint64_t m = masks[(int64_t)b * R + r];
         for (int t = p_lo; t < P + W; ++t) {
             if (t >= P) {
@@ -272,9 +310,11 @@ int orc_tree_attention(const void *q, const void *k_cache, const void *v_cache,
             int64_t page = page_table[(int64_t)b * max_pages + lp];
             kofs[nk++] = page * stride_page + (int64_t)g * stride_head +
                          (int64_t)(t % page_size) * stride_token;
+            if (t < P && kv_dtype == 2)
+                nq8 = nk;
         }
         int64_t qofs = (((int64_t)b * R + r) * Hq + h) * D;
-        orc_softmax_row(q, qofs, k_cache, v_cache, dtype, kv_dtype, kofs, nk, D,
+        orc_softmax_row(q, qofs, k_cache, v_cache, dtype, kv_dtype, kofs, nk, nq8, D,
                         sm_scale, s, out + n * D, lse2 + n);
         free(kofs);
         free(s);
@@ -308,7 +348,7 @@ int orc_causal_attention(const void *q, const void *k, const void *v,
         double *s = (double *)malloc(sizeof(double) * nk);
         for (int t = 0; t < nk; ++t)
             kofs[t] = ((int64_t)t * Hkv + g) * D;
-        orc_softmax_row(q, id * D, k, v, dtype, dtype, kofs, nk, D, sm_scale, s,
+        orc_softmax_row(q, id * D, k, v, dtype, dtype, kofs, nk, 0, D, sm_scale, s,
                         out + id * D, lse2 + id);
         free(kofs);
         free(s);

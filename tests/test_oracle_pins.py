@@ -269,14 +269,95 @@ def test_e4m3_decode_format_values():
     assert math.isnan(d(0x7F)) and math.isnan(d(0xFF))
 
 
+def test_e4m3_round_matches_torch_on_every_bf16_value_in_range():
+    """The oracle's E4M3 rounding against torch's float8_e4m3fn cast (round
+    to nearest even) on every finite bf16 value of magnitude <= 448."""
+    bits = torch.arange(1 << 16, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    x = bits.float()
+    x = x[torch.isfinite(x) & (x.abs() <= 448)]
+    ours = oracle.e4m3_round(x.double().numpy())
+    ref = x.to(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(np.signbit(ours), np.signbit(ref))
+
+
+def test_e4m3_round_format_values():
+    """Ties, saturation and special values fixed by the E4M3 format."""
+    r = lambda v: float(oracle.e4m3_round([v])[0])
+    assert r(1.0625) == 1.0 and r(1.1875) == 1.25          # ties go to the even mantissa
+    assert r(-1.0625) == -1.0 and r(2.0 ** -10) == 0.0      # subnormal tie to 0
+    assert r(3 * 2.0 ** -10) == 2.0 ** -8                  # between 2^-9 (odd) and 2^-8
+    assert r(0.3) == 0.3125 and r(-0.3) == -0.3125
+    assert r(448.0) == 448.0 and r(449.0) == 448.0 and r(470.0) == 448.0
+    assert r(1e30) == 448.0 and r(-1e30) == -448.0 and r(math.inf) == 448.0
+    assert math.isnan(r(math.nan))
+    assert r(0.0) == 0.0 and math.copysign(1.0, r(-0.0)) < 0
+
+
+def sdpa_reference_fp8(inp, masks):
+    """An FP8 cache: prefix keys are scored with the query rounded to E4M3,
+    window keys with the bf16 query.  torch SDPA in fp64 computes both at
+    once on channel-concatenated operands: q' = [q8, q] and
+    k' = [k on prefix keys else 0, k on window keys else 0], scale 1/sqrt(D)."""
+    wl = inp.wl
+    kk, vv = logical_kv(inp)
+    T = kk.shape[1]
+    g = wl.Hq // wl.Hkv
+    outs, lses = [], []
+    for b in range(wl.B):
+        P = int(inp.prefix_len[b])
+        dense = torch.zeros(wl.R, T, dtype=torch.bool)
+        dense[:, :P] = True
+        for r in range(wl.R):
+            for j in range(wl.W):
+                if (int(masks[b, r]) >> j) & 1:
+                    dense[r, P + j] = True
+        q = inp.q[b].double().permute(1, 0, 2)                       # [Hq][R][D]
+        q8 = q.float().to(torch.float8_e4m3fn).double()
+        k = kk[b].permute(1, 0, 2).repeat_interleave(g, 0)            # [Hq][T][D]
+        v = vv[b].permute(1, 0, 2).repeat_interleave(g, 0)
+        seen = dense.any(0)[None, :, None]
+        k = torch.where(seen, k, 0.0)
+        v = torch.where(seen, v, 0.0)
+        pre = (torch.arange(T) < P)[None, :, None]
+        k2 = torch.cat([torch.where(pre, k, 0.0), torch.where(pre, 0.0, k)], -1)
+        q2 = torch.cat([q8, q], -1)
+        sc = 1.0 / math.sqrt(wl.D)
+        o = torch.nn.functional.scaled_dot_product_attention(q2, k2, v, attn_mask=dense[None], scale=sc)
+        s = (q2 @ k2.transpose(1, 2)) * sc
+        s = torch.where(dense[None], s, -math.inf)
+        outs.append(o.permute(1, 0, 2))
+        lses.append((torch.logsumexp(s, -1) * LOG2E).permute(1, 0))
+    return torch.stack(outs).numpy(), torch.stack(lses).numpy()
+
+
 @pytest.mark.parametrize("layout", ["HND", "NHD"])
 def test_fp8_cache_attention_matches_sdpa(layout):
     """An FP8 E4M3 cache with a bf16 query: the oracle reads the decoded
-    cache values, the library routine gets them as fp64."""
+    cache values and scores prefix keys with the E4M3-rounded query, window
+    keys with the bf16 query; the library routine gets the same operands as
+    fp64."""
     wl, inp, m = small_case(3, layout=layout, kv_dtype="fp8")
     o, l = oracle_attn(inp, m)
-    ro, rl = sdpa_reference(inp, m)
+    ro, rl = sdpa_reference_fp8(inp, m)
     assert np.isfinite(o).all()
+    np.testing.assert_allclose(o, ro, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(l, rl, atol=1e-12, rtol=0)
+    # the query cast matters: scoring every key with the bf16 query differs
+    bo, bl = sdpa_reference(inp, m)
+    assert np.abs(l - bl).max() > 1e-4
+
+
+def test_fp8_query_cast_applies_to_prefix_keys_only():
+    """With no prefix the FP8 cache's rows equal plain attention over the
+    decoded window with the bf16 query (the window takes the unquantised
+    query); with no window bits beyond the root they all use the E4M3 query
+    on the prefix."""
+    wl = gen.Workload("t", 2, 0, 12, 4, 2, 16, "bf16", 8, "random", depth_cap=4, kv_dtype="fp8")
+    inp = gen.make_inputs(wl, 7, "cpu", prefix_lens=np.array([0, 0]))
+    m = oracle.build_masks(inp.parents)["masks"]
+    o, l = oracle_attn(inp, m)
+    ro, rl = sdpa_reference(inp, m)
     np.testing.assert_allclose(o, ro, atol=1e-12, rtol=0)
     np.testing.assert_allclose(l, rl, atol=1e-12, rtol=0)
 
