@@ -340,6 +340,40 @@ def test_fp8_nonfinite_window_values(shape):
     _same_nonfinite(lse.cpu().numpy(), rl.reshape(lse.shape), LSE_TOL, shape + " fp8 lse2")
 
 
+@pytest.mark.parametrize("shape", ["rows16", "rows64", "rows256"])
+def test_fp8_prefix_query_cast(shape):
+    # Query values that E4M3 cannot hold, all rounding down by 1/17 (ties to
+    # the even code: 1.0625 -> 1, 2.125 -> 2, 0.53125 -> 0.5, 4.25 -> 4), and
+    # keys with their sign bit cleared, so every score shifts the same way:
+    # the prefix scores use the rounded query and the window scores the bf16
+    # query.  Scoring the prefix with the bf16 query, or the window with the
+    # rounded one, is then far outside the tolerance.  Every prefix kernel
+    # shape: 16, 64 and 256 folded rows.
+    R, Hq = {"rows16": (4, 4), "rows64": (16, 4), "rows256": (64, 4)}[shape]
+    wl = gen.Workload("q8", 2, 700, R, Hq, 1, 128, "bf16", 16, "random", depth_cap=5,
+                      kv_dtype="fp8")
+    inp = gen.make_inputs(wl, 17, "cuda")
+    vals = torch.tensor([1.0625, 2.125, 0.53125, 4.25], dtype=torch.bfloat16, device="cuda")
+    idx = torch.randint(0, 4, inp.q.shape, generator=torch.Generator("cuda").manual_seed(5),
+                        device="cuda")
+    inp.q.copy_(vals[idx])
+    inp.k_cache.view(torch.uint8).bitwise_and_(0x7F)
+    m = oracle.build_masks(inp.parents)["masks"]
+    out, lse = run_attention(inp, dev(m.view(np.int64), torch.int64))
+    ro, rl = oracle_attention(inp, m)
+    check_attention(out, lse, ro, rl, tag=shape + " fp8 q cast")
+    # the other readings, from caches widened to bf16 (exact): the bf16 query
+    # on every key, and the rounded query on every key
+    k16, v16 = inp.k_cache.to(torch.bfloat16), inp.v_cache.to(torch.bfloat16)
+    q8 = inp.q.float().to(torch.float8_e4m3fn).to(torch.bfloat16)
+    got = lse.cpu().numpy()
+    for qq in (inp.q, q8):
+        alt = oracle.tree_attention(gen.bf16_bits(qq), gen.bf16_bits(k16), gen.bf16_bits(v16),
+                                    inp.strides, inp.page_table, wl.page_size, inp.prefix_len,
+                                    m, wl.W, wl.Hkv)
+        assert np.abs(got - alt[1].reshape(got.shape)).max() > 5 * LSE_TOL
+
+
 def test_bad_trees_flagged():
     par = np.array([[-1, 0, 0, 1, 2, 3, 4, 5],
                     [-1, 0, 5, 1, 2, 3, 4, 5],      # forward reference at node 2

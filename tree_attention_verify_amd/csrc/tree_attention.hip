@@ -114,6 +114,37 @@ __device__ __forceinline__ void fp8x16_to_bf16(const int4 x, int4 &lo, int4 &hi)
     hi = make_int4(c0(x.z), c1(x.z), c0(x.w), c1(x.w));
 }
 
+// x rounded to the nearest FP8 E4M3 value (ties to even), as fp32; magnitudes
+// past the largest finite value (448) give +-448 and NaN stays NaN.  Above
+// the subnormal range an E4M3 value has 4 significant bits, so the quantum
+// at binary exponent e is 2^(e - 3); below 2^-6 it is 2^-9.  Scaling by
+// those powers of two is exact and v_rndne_f32 rounds ties to even.
+__device__ inline float round_e4m3(float x) {
+    if (!(fabsf(x) <= 448.f))
+        return x != x ? x : copysignf(448.f, x);
+    const float a = fabsf(x);
+    int e = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;
+    e = e < -6 ? -6 : e;
+    const float up = __uint_as_float((uint32_t)(3 - e + 127) << 23);     // 2^(3 - e)
+    const float dn = __uint_as_float((uint32_t)(e - 3 + 127) << 23);     // 2^(e - 3)
+    return copysignf(__builtin_rintf(a * up) * dn, x);
+}
+
+// The query operand of the prefix under an FP8 cache: each bf16 value rounded
+// to E4M3 (held as bf16, which represents every E4M3 value exactly).  The
+// products with E4M3 keys are then exact, as in an FP8 matrix product.
+__device__ inline bf16x8 bf16x8_round_e4m3(bf16x8 v) {
+    // element access through a whole-vector cast: a bit cast of a single
+    // subscripted element reads element 0 whatever the index
+    typedef __attribute__((__vector_size__(8 * sizeof(uint16_t)))) uint16_t u16x8;
+    const u16x8 u = __builtin_bit_cast(u16x8, v);
+    u16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        r[i] = f32_to_bf16_bits(round_e4m3(bf16_bits_to_f32(u[i])));
+    return __builtin_bit_cast(bf16x8, r);
+}
+
 // fp32 value of one FP8 E4M3 code
 __device__ __forceinline__ float fp8_to_f32(uint8_t b) {
     const int w = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)b, 1.0f, false));
@@ -294,6 +325,8 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
         for (int kk = 0; kk < KSTEPS; ++kk) {
             int4 v4 = ok ? *(const int4 *)(qp + 16 * kk) : make_int4(0, 0, 0, 0);
             qv[kk] = __builtin_bit_cast(bf16x8, v4);
+            if constexpr (KV8)
+                qv[kk] = bf16x8_round_e4m3(qv[kk]);
         }
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk)
@@ -717,6 +750,8 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
         for (int kk = 0; kk < KSTEPS; ++kk) {
             int4 v4 = ok ? *(const int4 *)(qp + 16 * kk) : make_int4(0, 0, 0, 0);
             qv[kk] = __builtin_bit_cast(bf16x8, v4);
+            if constexpr (KV8)
+                qv[kk] = bf16x8_round_e4m3(qv[kk]);
         }
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk)
