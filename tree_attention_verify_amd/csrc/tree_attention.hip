@@ -673,15 +673,17 @@ struct PipeCfg {
     static constexpr int DT = D / 32;
     static constexpr int KREG = SK * D * 2;       // bytes of the K region (bf16)
     static constexpr int SB = 2 * KREG;           // stage bytes (bf16)
-    // FP8 E4M3 caches: a ring of F8 raw stages (half the bytes) feeds a ring
-    // of 3 converted bf16 stages
-    static constexpr int F8 = 3;
+    // FP8 E4M3 caches: a ring of F8 raw stages (K then V, half the bytes of
+    // a bf16 stage) and a ring of NBUF stages of V widened to bf16 (KREG
+    // bytes each).  The scores read the raw K directly.
+    static constexpr int F8 = 6;
     static constexpr int SB8 = SB / 2;
     static constexpr int LPS8 = SB8 / (THREADS * 16);
     static constexpr int NBUF0 = kLdsStageBudget / SB;
     static constexpr int NBUF = KV8 ? 3 : (NBUF0 > 12 ? 12 : NBUF0);
-    static_assert(!KV8 || (LPS8 >= 1 && SB8 % (THREADS * 16) == 0 && NBUF * SB + F8 * SB8 <= kLdsStageBudget),
+    static_assert(!KV8 || (LPS8 == 2 && SB8 % (THREADS * 16) == 0 && NBUF * KREG + F8 * SB8 <= kLdsStageBudget),
                   "fp8 stage split");
+    static_assert(!KV8 || D == 128, "fp8 scores take two 64-channel MFMA steps");
     static constexpr int PF = NBUF - 2;           // stages in flight ahead of the current one
     static constexpr int LPS = SB / (THREADS * 16);
     static_assert(THREADS == SK * 8, "one load instruction covers every key of a stage");
@@ -699,7 +701,10 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
     constexpr int ROWS_WG = 256;
 
     constexpr int F8 = C::F8, SB8 = C::SB8, LPS8 = C::LPS8;
-    __shared__ __attribute__((aligned(16))) char lds[NBUF * SB + (KV8 ? F8 * SB8 : 0)];
+    // bf16: NBUF stages of K and V; FP8: NBUF stages of widened V, then the
+    // F8 raw stages
+    constexpr int VRING = KV8 ? NBUF * KREG : NBUF * SB;
+    __shared__ __attribute__((aligned(16))) char lds[VRING + (KV8 ? F8 * SB8 : 0)];
     __shared__ int32_t pt[kPtMax];
 
     const int tid = threadIdx.x;
@@ -736,26 +741,58 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
     const int npt = nkeys > 0 ? ((kr.hi - 1) >> a.ps_shift) - lp0 + 1 : 0;
     for (int i = tid; i < npt && i < kPtMax; i += THREADS)
         pt[i] = (int32_t)clamp_page(a.page_table[(int64_t)b * a.max_pages + lp0 + i], a.num_pages);
-    for (int i = tid; i < NBUF * SB / 16; i += THREADS)
+    for (int i = tid; i < VRING / 16; i += THREADS)
         reinterpret_cast<int4 *>(lds)[i] = make_int4(0, 0, 0, 0);
 
-    bf16x8 qv[KSTEPS];
+    // Q^T operand.  bf16: lane (row l32, half hl) holds Q[row][16 kk + 8 hl
+    // .. +8] per 16-channel k step.  FP8: the query rounded to E4M3, lane
+    // holding Q[row][64 kk + 32 hl .. +32] per 64-channel k step, the byte
+    // order of the K operand's 32 bytes (the FP8 product pairs the bytes of
+    // the two operands position by position).
+    constexpr int QREGS = KV8 ? 2 : KSTEPS;
+    typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+    bf16x8 qv[KV8 ? 1 : KSTEPS];
+    i32x8 qv8[KV8 ? 2 : 1];
     {
         const int m = rows_base + l32;
         const bool ok = m < a.M;
         const int r = ok ? m / a.G : 0, hh = ok ? m % a.G : 0;
-        const uint16_t *qp = (const uint16_t *)a.q +
-                             (((int64_t)b * a.R + r) * a.Hq + (int64_t)g * a.G + hh) * D + 8 * hl;
+        const uint16_t *qrow = (const uint16_t *)a.q +
+                               (((int64_t)b * a.R + r) * a.Hq + (int64_t)g * a.G + hh) * D;
+        if constexpr (KV8) {
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-            int4 v4 = ok ? *(const int4 *)(qp + 16 * kk) : make_int4(0, 0, 0, 0);
-            qv[kk] = __builtin_bit_cast(bf16x8, v4);
-            if constexpr (KV8)
-                qv[kk] = bf16x8_round_e4m3(qv[kk]);
+            for (int kk = 0; kk < QREGS; ++kk) {
+                const uint16_t *qp = qrow + 64 * kk + 32 * hl;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int4 v4 = ok ? *(const int4 *)(qp + 8 * c) : make_int4(0, 0, 0, 0);
+                    typedef __attribute__((__vector_size__(8 * sizeof(uint16_t)))) uint16_t u16x8;
+                    const u16x8 u = __builtin_bit_cast(u16x8, v4);
+                    float f[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        f[e] = round_e4m3(bf16_bits_to_f32(u[e]));
+                    // exact: every value is an E4M3 value
+                    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+                    lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+                    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+                    hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+                    qv8[kk][2 * c] = lo;
+                    qv8[kk][2 * c + 1] = hi;
+                }
+                settle(qv8[kk]);
+            }
+        } else {
+            const uint16_t *qp = qrow + 8 * hl;
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk) {
+                int4 v4 = ok ? *(const int4 *)(qp + 16 * kk) : make_int4(0, 0, 0, 0);
+                qv[kk] = __builtin_bit_cast(bf16x8, v4);
+            }
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk)
+                settle(qv[kk]);
         }
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk)
-            settle(qv[kk]);
     }
     __syncthreads();
 
@@ -824,72 +861,59 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
             issue(st + PF);
     };
 
-    // FP8 E4M3 caches.  Raw slot i * THREADS + tid of a stage holds 16-byte
-    // chunk c8 of key `key` of region K or V; the thread that loads it also
-    // converts it (after its own load has landed) into bf16 chunks 2 c8 and
-    // 2 c8 + 1 of the piece layout, so the raw ring needs no barrier.
-    constexpr int C8 = D / 16;
-    const uint32_t lds8 = lds0 + (uint32_t)(NBUF * SB);
-    auto slot8 = [&](int i, int &region, int &key, int &c8) {
-        const int slot = i * THREADS + tid;
-        region = slot / (SK * C8);
-        const int s2 = slot % (SK * C8);
-        key = s2 / C8;
-        c8 = s2 % C8;
-    };
+    // FP8 E4M3 caches.  A raw stage is SK key rows of D bytes of K, then of
+    // V; thread tid loads 16-byte slot tid of each: key tid / 8, position
+    // tid % 8.  K rows are read by every wave as the MFMA operand, with
+    // position p of key k holding chunk p ^ xk8(k) (conflict-free operand
+    // reads: the 16 keys of a 16-lane group land on distinct 16-byte slots
+    // of 256 bytes).  The thread that loads a V chunk widens it (after its
+    // own load has landed) into bf16 chunks 2 c8 and 2 c8 + 1 of the piece
+    // layout, so V needs no barrier between the raw and the widened ring.
+    // At stage_ready8(st) the raw stages issued are those up to st + F8 - 3;
+    // stage st + 1 must have landed (its V is widened now, its K is read
+    // after the next barrier) and the buffer of stage st - 2, which no wave
+    // reads any more, takes stage st + F8 - 2.
+    static_assert(!KV8 || D / 16 == 8, "one raw row is 8 chunks");
+    auto xk8 = [](int k) { return (k >> 1) & 7; };
+    const uint32_t lds8 = lds0 + (uint32_t)VRING;
+    const int key8 = tid >> 3, pos8 = tid & 7;
     auto issue8 = [&](int st) {
-        const int kst = kb0 + st * SK;
-        const uint32_t rbase = lds8 + (uint32_t)((st % F8) * SB8);
-#pragma unroll 1
-        for (int i = 0; i < LPS8; ++i) {
-            int region, key, c8;
-            slot8(i, region, key, c8);
-            const int t = kst + key;
-            const int64_t page = t < kr.hi ? pt[(t >> a.ps_shift) - lp0] : 0;
-            const uint8_t *src = (const uint8_t *)(region ? a.v : a.k) + page * a.stride_page +
-                                 (int64_t)g * a.stride_head + (int64_t)(t & ps_mask) * a.stride_token +
-                                 c8 * 16;
-            if (t < kr.hi)
-                dma_load16(src, __builtin_amdgcn_readfirstlane(rbase + (i * THREADS + w * 64) * 16));
+        const int t = kb0 + st * SK + key8;
+        const uint32_t rbase = lds8 + (uint32_t)((st % F8) * SB8) + w * 64 * 16;
+        if (t < kr.hi) {
+            const int64_t off = (int64_t)pt[(t >> a.ps_shift) - lp0] * a.stride_page +
+                                (int64_t)g * a.stride_head + (int64_t)(t & ps_mask) * a.stride_token;
+            dma_load16((const uint8_t *)a.k + off + ((pos8 ^ xk8(key8)) * 16), rbase);
+            dma_load16((const uint8_t *)a.v + off + pos8 * 16, rbase + THREADS * 16);
         }
     };
     auto convert8 = [&](int st) {
-        const int kst = kb0 + st * SK;
-        const char *raw = lds + NBUF * SB + (st % F8) * SB8;
-        char *buf = lds + (st % NBUF) * SB;
-#pragma unroll 1
-        for (int i = 0; i < LPS8; ++i) {
-            int region, key, c8;
-            slot8(i, region, key, c8);
-            int4 x = make_int4(0, 0, 0, 0);
-            if (kst + key < kr.hi)
-                x = *(const int4 *)(raw + (i * THREADS + tid) * 16);
-            int4 h[2];
-            fp8x16_to_bf16(x, h[0], h[1]);
+        const char *raw = lds + VRING + (st % F8) * SB8 + SB8 / 2 + tid * 16;
+        char *buf = lds + (st % NBUF) * KREG;
+        int4 x = make_int4(0, 0, 0, 0);
+        if (kb0 + st * SK + key8 < kr.hi)
+            x = *(const int4 *)raw;
+        int4 h[2];
+        fp8x16_to_bf16(x, h[0], h[1]);
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int c = 2 * c8 + e, cg = c / 8;
-                const int pos = (c % 8) ^ (region ? yv(key, cg) : xk(key));
-                *(int4 *)(buf + region * KREG + cg * (SK * 128) + key * 128 + pos * 16) = h[e];
-            }
+        for (int e = 0; e < 2; ++e) {
+            const int c = 2 * pos8 + e, cg = c / 8;
+            const int pos = (c % 8) ^ yv(key8, cg);
+            *(int4 *)(buf + cg * (SK * 128) + key8 * 128 + pos * 16) = h[e];
         }
     };
-    // Stage st is ready once its conversion (one stage earlier) is published:
-    // wait for this thread's raw chunks of stage st + 1 (those of st + 2 may
-    // still be in flight), publish, convert st + 1, and issue st + 3 into
-    // the raw buffer st has left.
     auto stage_ready8 = [&](int st) {
         if (st + 1 < ns) {
-            if (st + 2 <= ns - 2)
-                wait_vmcnt<LPS8>();
+            if (st + F8 - 3 <= ns - 2)
+                wait_vmcnt<(F8 - 4) * LPS8>();
             else
                 wait_vmcnt<0>();
         }
         __syncthreads();
         if (st + 1 < ns)
             convert8(st + 1);
-        if (st + F8 < ns)
-            issue8(st + F8);
+        if (st + F8 - 2 < ns)
+            issue8(st + F8 - 2);
     };
     auto stage_ready = [&](int st) {
         if constexpr (KV8)
@@ -909,7 +933,7 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
     for (int t = 0; t < DT; ++t) {
         const int c = (G16 & 1) * (D / 16) + 2 * t + (a4 >> 1);   // chunk of channels d0..d0+3
         const int cg = c / 8, key = 4 * (G16 >> 1) + j4;
-        voff[t] = KREG + cg * CGB + key * 128 + (((c % 8) ^ yv(key, cg)) * 16) + (a4 & 1) * 8;
+        voff[t] = cg * CGB + key * 128 + (((c % 8) ^ yv(key, cg)) * 16) + (a4 & 1) * 8;
     }
 
     f32x16 o[DT];
@@ -922,14 +946,41 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
     float l_run = 0.f;
 
     auto block_base = [&](int u) { return lds + ((u / BPS) % NBUF) * SB + (u % BPS) * (32 * 128); };
-    auto load_k = [&](int u, bf16x8 (&ka)[KSTEPS]) {
-        const char *kb = block_base(u);
+    // V region of block u (the widened ring for FP8)
+    auto vblock_base = [&](int u) {
+        if constexpr (KV8)
+            return lds + ((u / BPS) % NBUF) * KREG + (u % BPS) * (32 * 128);
+        else
+            return block_base(u) + KREG;
+    };
+    // FP8 K operand: lane (key l32, half hl) reads chunks 4 kk + 2 hl + e of
+    // its key row, e = 0, 1: channels 64 kk + 32 hl .. +32, as the query
+    uint32_t koff8[2][2];
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk)
-            ka[kk] = *(const bf16x8 *)(kb + (kk / 4) * CGB + koff[kk % 4]);
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            koff8[kk][e] = l32 * D + (((4 * kk + 2 * hl + e) ^ xk8(l32)) * 16);
+    typedef i32x8 KOp[KV8 ? 2 : KSTEPS];
+    typedef bf16x8 KOpB[KV8 ? 1 : KSTEPS];
+    auto load_k = [&](int u, auto &ka) {
+        if constexpr (KV8) {
+            const char *kb = lds + VRING + ((u / BPS) % F8) * SB8 + (u % BPS) * (32 * D);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int4 x0 = *(const int4 *)(kb + koff8[kk][0]);
+                const int4 x1 = *(const int4 *)(kb + koff8[kk][1]);
+                ka[kk] = i32x8{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            }
+        } else {
+            const char *kb = block_base(u);
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk)
+                ka[kk] = *(const bf16x8 *)(kb + (kk / 4) * CGB + koff[kk % 4]);
+        }
     };
     auto load_v = [&](int u, bf16x8 (&va)[DT][2]) {
-        const char *vb = block_base(u);
+        const char *vb = vblock_base(u);
 #pragma unroll
         for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -942,12 +993,21 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
                 va[t][cc] = __builtin_bit_cast(bf16x8, pair);
             }
     };
-    // S^T of one block: keys x rows, lane l holding row l % 32
-    auto qk = [&](const bf16x8 (&ka)[KSTEPS]) {
+    // S^T of one block: keys x rows, lane l holding row l % 32.  FP8: two
+    // E4M3 x E4M3 MFMA steps of 64 channels (format 0 = E4M3 for both
+    // operands, block scales 2^0).
+    auto qk = [&](const auto &ka) {
         f32x16 acc;
+        if constexpr (KV8) {
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qv[kk], kk ? acc : f32x16{}, 0, 0, 0);
+            for (int kk = 0; kk < 2; ++kk)
+                acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[kk], qv8[kk], kk ? acc : f32x16{},
+                                                                      0, 0, 0, 127, 0, 127);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qv[kk], kk ? acc : f32x16{}, 0, 0, 0);
+        }
         return acc;
     };
     // bf16 weights of one block and their sum (the values the MFMA multiplies)
@@ -1021,7 +1081,7 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
     // other phase; the two waves of a SIMD fill each other's gaps.  Every
     // block but the last is full.
     auto step = [&](int u, f32x16 &s, const bf16x8 (&pb_prev)[2], bf16x8 (&pb_cur)[2],
-                    bool new_stage, bf16x8 (&ka)[KSTEPS], bf16x8 (&va)[DT][2]) {
+                    bool new_stage, auto &ka, bf16x8 (&va)[DT][2]) {
         float lb;
         pv(va, pb_prev);
         weights(s, pb_cur, lb);
@@ -1041,11 +1101,13 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
     };
 
     if constexpr (KV8) {
-        for (int st = 0; st < F8 && st < ns; ++st)
+        // raw stages 0 .. F8 - 3 in flight; widen V of stage 0 once its own
+        // loads have landed
+        for (int st = 0; st < F8 - 2 && st < ns; ++st)
             issue8(st);
         if (ns > 0) {
-            if (ns >= F8 + 1)
-                wait_vmcnt<(F8 - 1) * LPS8>();
+            if (F8 - 3 <= ns - 2)
+                wait_vmcnt<(F8 - 3) * LPS8>();
             else
                 wait_vmcnt<0>();
             convert8(0);
@@ -1056,7 +1118,8 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
     }
     if (nb > 0) {
         stage_ready(0);
-        bf16x8 ka[KSTEPS], va[DT][2], pa[2], pbb[2];
+        std::conditional_t<KV8, KOp, KOpB> ka;
+        bf16x8 va[DT][2], pa[2], pbb[2];
         f32x16 s;
         load_k(0, ka);
         s = qk(ka);
@@ -1751,7 +1814,9 @@ Plan make_plan(tav_dtype dtype, int B, int R, int Hq, int Hkv, int D, int max_pr
         } else if (M <= 64) {
             p.NRB = 2;
             p.NKS = 4;
-        } else if (M <= 128) {
+        } else if (M <= 128 || (dtype == TAV_FP8_E4M3 && D != 128)) {
+            // (the pipelined kernel's FP8 path takes 128-channel heads; other
+            // FP8 widths run 128-row groups here)
             p.NRB = 4;
             p.NKS = 2;
         } else {
@@ -1841,7 +1906,7 @@ void launch_mfma_d(const Plan &p, const PrefixArgs &a, hipStream_t s) {
         launch_mfma<D, 2, 4, KV8>(p, a, s);
     else if (p.NRB == 4)
         launch_mfma<D, 4, 2, KV8>(p, a, s);
-    else {
+    else if constexpr (!KV8 || D == 128) {
         const unsigned grid = (unsigned)((long long)a.B * a.Hkv * p.RG * p.n_split);
         hipLaunchKernelGGL((k_prefix_mfma_pipe<D, kPipeStageKeys, KV8>), dim3(grid), dim3(512), 0, s, a);
     }
