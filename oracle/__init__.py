@@ -63,6 +63,12 @@ def lib():
         L.orc_e4m3_decode.restype = D
         L.orc_e4m3_round.argtypes = [D]
         L.orc_e4m3_round.restype = D
+        L.orc_philox4x32_10.argtypes = [P, P, P]
+        L.orc_philox4x32_10.restype = None
+        L.orc_gumbel_uniform.argtypes = [ctypes.c_uint64, I64, I64]
+        L.orc_gumbel_uniform.restype = D
+        L.orc_sample_gumbel.argtypes = [P, I, I64, I, I, I, P, P, P, P, P, P]
+        L.orc_sample_gumbel.restype = ctypes.c_int
         L.orc_tree_attention.argtypes = [P, P, P, I, I, I64, I64, I64, P, I, I, P, I,
                                          P, I, I, I, I, I, I, D, P, I64, P, P]
         L.orc_causal_attention.argtypes = [P, P, P, I, I, I, I, I, I, D, P, P]
@@ -251,3 +257,42 @@ def compact_rows(tables, accepted_path, accept_len):
                          int(t.get("n_heads", 1)), int(t["row_bytes"]))
     _check(lib().orc_compact_rows(arr, len(tables), _p(accepted_path), _p(accept_len),
                                   B, N), "compact_rows")
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    """Philox4x32-10 of one 4-word counter under a 2-word key (uint32)."""
+    c = _c(np.asarray(ctr, np.uint32), np.uint32)
+    k = _c(np.asarray(key, np.uint32), np.uint32)
+    out = np.empty(4, np.uint32)
+    lib().orc_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def gumbel_uniform(seed, pos, v) -> float:
+    """The uniform in (0, 1) of token v at key position pos under seed."""
+    return float(lib().orc_gumbel_uniform(int(seed) & (2**64 - 1), int(pos), int(v)))
+
+
+def sample_gumbel(logits, temperature, seed, positions):
+    """Gumbel-max sampled target token of every verify row.
+
+    logits: [B][N][V] float32 or uint16 (bf16 bits); temperature float [B]
+    (<= 0: greedy); seed uint64 [B]; positions int32 [B][N] (vc + depth, the
+    node's own position: the key is the position it predicts, one more).
+    Returns (tokens int32 [B][N], zmax float64 [B][N], z2 float64 [B][N]):
+    the winning perturbed score and the best score of any other token.
+    """
+    logits = np.ascontiguousarray(logits)
+    dt = _dtype_code(logits)
+    assert dt in (0, 1)
+    B, N, V = logits.shape
+    temperature = _c(temperature, np.float32)
+    seed = _c(np.asarray(seed, np.uint64), np.uint64)
+    positions = _c(positions, np.int32)
+    assert temperature.shape == (B,) and seed.shape == (B,) and positions.shape == (B, N)
+    tokens = np.empty((B, N), np.int32)
+    zmax = np.empty((B, N), np.float64)
+    z2 = np.empty((B, N), np.float64)
+    _check(lib().orc_sample_gumbel(_p(logits), dt, V, V, B, N, _p(temperature), _p(seed),
+                                   _p(positions), _p(tokens), _p(zmax), _p(z2)), "sample_gumbel")
+    return tokens, zmax, z2

@@ -523,3 +523,103 @@ int orc_compact_rows(const orc_rows *tables, int n_tables,
     }
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* sampled verify: Gumbel-max draws keyed by (seed, position)          */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and
+ * Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC 2011): ten rounds
+ * of the Philox S-box on a 4 x 32-bit counter under a 2 x 32-bit key.  A
+ * round multiplies counter words 0 and 2 by 0xD2511F53 and 0xCD9E8D57 into
+ * 64-bit products (hi, lo) and outputs {hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1,
+ * lo0}; between rounds the key advances by the Weyl constants 0x9E3779B9
+ * and 0xBB67AE85.  The pages name no generator; this one is specified in
+ * full by its publication, so the kernels implement it independently.
+ */
+void orc_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4])
+{
+    uint32_t c[4] = {ctr_in[0], ctr_in[1], ctr_in[2], ctr_in[3]};
+    uint32_t k0 = key_in[0], k1 = key_in[1];
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+        uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = lo1;
+        c[2] = n2;
+        c[3] = lo0;
+    }
+    for (int i = 0; i < 4; ++i)
+        out[i] = c[i];
+}
+
+/*
+ * The uniform of token v at key position pos under a request seed: Philox
+ * counter {v / 4, pos, 0, 0}, key {seed low 32 bits, seed high 32 bits},
+ * output word v % 4; its top 24 bits b give u = (b + 1/2) / 2^24 in (0, 1).
+ */
+double orc_gumbel_uniform(uint64_t seed, int64_t pos, int64_t v)
+{
+    uint32_t ctr[4] = {(uint32_t)(v / 4), (uint32_t)pos, 0u, 0u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t o[4];
+    orc_philox4x32_10(ctr, key, o);
+    return ((double)(o[v % 4] >> 8) + 0.5) / 16777216.0;
+}
+
+/*
+ * Sampled target tokens of every verify row ([DTS] "Sampled verify keys
+ * noise by position"): the row of node i of request b draws its token by
+ * Gumbel-max, keyed by (seed[b], the position the node predicts), which is
+ * positions[b][i] + 1 with positions = vc + depth (so siblings share their
+ * noise, and a chain row draws what plain decoding draws at that position).
+ *   z_v = logits[v] / T + g_v,   g_v = -ln(-ln u_v),   token = argmax_v z_v
+ * with the lowest v winning ties and NaN ranking last (an all-NaN or all
+ * -inf row gives token 0).  T = temperature[b]; T <= 0 is greedy: the argmax
+ * of the logits themselves.  logits holds dtype elements (0 fp32, 1 bf16),
+ * row (b*N + i) at element offset (b*N + i) * row_stride.  zmax (optional)
+ * receives the winning z (fp64) and z2 (optional) the best z of any other
+ * token, so a caller can tell how close the decision was.
+ */
+int orc_sample_gumbel(const void *logits, int dtype, int64_t row_stride, int V, int B,
+                      int N, const float *temperature, const uint64_t *seed,
+                      const int32_t *positions, int32_t *tokens, double *zmax, double *z2)
+{
+    if (V < 1 || B < 0 || N < 1 || (dtype != 0 && dtype != 1))
+        return ORC_BAD;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t row = 0; row < (int64_t)B * N; ++row) {
+        int b = (int)(row / N);
+        double T = temperature[b];
+        int64_t key_pos = (int64_t)positions[row] + 1;
+        double best = -INFINITY, second = -INFINITY;
+        int arg = 0;
+        for (int64_t v = 0; v < V; ++v) {
+            double l = orc_load(logits, dtype, row * row_stride + v);
+            double z = T > 0 ? l / T - log(-log(orc_gumbel_uniform(seed[b], key_pos, v))) : l;
+            if (isnan(z))
+                z = -INFINITY;
+            if (z > best) {
+                second = best;
+                best = z;
+                arg = (int)v;
+            } else if (z > second) {
+                second = z;
+            }
+        }
+        tokens[row] = arg;
+        if (zmax)
+            zmax[row] = best;
+        if (z2)
+            z2[row] = second;
+    }
+    return ORC_OK;
+}

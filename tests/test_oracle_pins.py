@@ -672,3 +672,111 @@ def test_compaction_paged_heads():
             s, d = P[b] + path[b, i], P[b] + i
             expect[pt[b, d // ps], :, d % ps] = before[pt[b, s // ps], :, s % ps]
     assert np.array_equal(cache, expect)
+
+
+# ---------------------------------------------------------------------------
+# sampled verify: Gumbel-max draws keyed by (seed, position)
+# ---------------------------------------------------------------------------
+
+def test_philox4x32_10_known_answers():
+    g = load("philox4x32_kat.txt")
+    for i in range(3):
+        h = lambda k: [int(str(x), 16) for x in g["%s%d" % (k, i)]]
+        assert oracle.philox4x32_10(h("ctr"), h("key")).tolist() == h("out")
+
+
+def test_gumbel_uniforms_are_uniform_on_the_open_interval():
+    u = np.array([oracle.gumbel_uniform(12345, p, v) for p in range(40) for v in range(500)])
+    assert (u > 0).all() and (u < 1).all()
+    # 20000 draws: mean and variance of U(0, 1) within 5 standard errors
+    assert abs(u.mean() - 0.5) < 5 * math.sqrt(1 / 12 / u.size)
+    assert abs(u.var() - 1 / 12) < 5 * math.sqrt(1 / 180 / u.size)
+    # 24-bit grid: 2^24 u - 1/2 is an integer
+    k = u * 2 ** 24 - 0.5
+    assert np.array_equal(k, np.round(k))
+    # different seeds and positions give different streams
+    assert oracle.gumbel_uniform(1, 7, 3) != oracle.gumbel_uniform(2, 7, 3)
+    assert oracle.gumbel_uniform(1, 7, 3) != oracle.gumbel_uniform(1, 8, 3)
+
+
+def _sample(logits, T, seed, pos):
+    lg = np.ascontiguousarray(logits, np.float32)
+    B, N, _ = lg.shape
+    return oracle.sample_gumbel(lg, np.full(B, T, np.float32), np.full(B, seed, np.uint64),
+                                np.asarray(pos, np.int32).reshape(B, N))
+
+
+def test_gumbel_max_draws_follow_the_softmax():
+    """Gumbel-max samples exactly softmax(logits / T): 20000 draws of a
+    5-token row at distinct positions, chi-square against that law."""
+    l = np.array([0.5, -1.0, 2.0, 0.0, 1.25], np.float32)
+    T = 0.8
+    B, N = 400, 50
+    logits = np.broadcast_to(l, (B, N, 5))
+    tok, _, _ = _sample(logits, T, 99, np.arange(B * N))
+    p = np.exp(l / T - np.max(l / T))
+    p /= p.sum()
+    cnt = np.bincount(tok.ravel(), minlength=5)
+    exp = p * tok.size
+    chi2 = float(((cnt - exp) ** 2 / exp).sum())
+    assert chi2 < 20.5            # 4 degrees of freedom: P(chi2 > 20.5) < 4e-4
+
+
+def test_zero_temperature_is_the_argmax():
+    rng = np.random.default_rng(3)
+    logits = rng.standard_normal((3, 7, 300)).astype(np.float32)
+    logits[1, 2, 10] = logits[1, 2, 200] = 50.0                 # tie: the lower index
+    tok, _, _ = _sample(logits, 0.0, 5, np.zeros((3, 7)))
+    assert np.array_equal(tok, np.argmax(logits, -1))
+    assert tok[1, 2] == 10
+
+
+def test_noise_is_keyed_by_the_predicted_position():
+    """Rows with equal logits draw equal tokens when their positions are
+    equal (siblings at one depth), and the draw follows the key position
+    vc + depth + 1, not the row."""
+    rng = np.random.default_rng(4)
+    row = rng.standard_normal(1000).astype(np.float32)
+    logits = np.broadcast_to(row, (1, 64, 1000))
+    pos = np.repeat(np.arange(16), 4)                           # 4 siblings per depth
+    tok, _, _ = _sample(logits, 1.0, 7, pos)
+    t = tok.reshape(16, 4)
+    assert (t == t[:, :1]).all()
+    assert len(set(t[:, 0].tolist())) > 4                       # depths differ
+    # the key is the position the node predicts: a row at position p draws
+    # with the uniforms of key position p + 1
+    z = row / 1.0 - np.log(-np.log([oracle.gumbel_uniform(7, 3 + 1, v) for v in range(1000)]))
+    assert t[3, 0] == int(np.argmax(z))
+
+
+def test_gumbel_scores_and_special_values():
+    rng = np.random.default_rng(6)
+    logits = rng.standard_normal((2, 4, 257)).astype(np.float32)
+    logits[0, 1, :] = np.nan
+    logits[0, 1, 100] = -3.0                                    # NaN ranks last
+    logits[0, 2, :] = -np.inf                                    # no candidate: token 0
+    logits[1, 3, 5] = np.nan
+    tok, zmax, z2 = _sample(logits, 1.3, 11, np.arange(8) + 40)
+    assert tok[0, 1] == 100 and tok[0, 2] == 0 and tok[1, 3] != 5
+    # the winning score is l / T + g of the winning token; z2 is the runner-up
+    b, i = 1, 0
+    v = int(tok[b, i])
+    g = -math.log(-math.log(oracle.gumbel_uniform(11, 40 + b * 4 + i + 1, v)))
+    assert zmax[b, i] == float(logits[b, i, v]) / np.float32(1.3).astype(np.float64) + g
+    assert z2[b, i] < zmax[b, i]
+
+
+def test_sampled_chain_verify_accepts_matching_drafts():
+    """A chain whose draft tokens are the draws of their parents' rows is
+    accepted whole ([DTS]: acceptance is the greedy tree walk over the draws,
+    accepting a child when it equals its parent's draw)."""
+    rng = np.random.default_rng(8)
+    N, V = 8, 64
+    logits = rng.standard_normal((1, N, V)).astype(np.float32)
+    par = np.array([[-1] + list(range(N - 1))], np.int32)
+    pos = oracle.build_masks(par, vc=np.array([100]))["positions"]
+    tok, _, _ = _sample(logits, 0.9, 21, pos)
+    draft = np.concatenate([[[0]], tok[:, :-1]], 1).astype(np.int32)
+    r = oracle.verify_greedy(draft, tok, par)
+    assert int(r["accept_len"][0]) == N
+    assert r["accepted_tokens"][0].tolist() == tok[0].tolist()
