@@ -34,6 +34,11 @@ from tree_attention_verify_amd import inputs as gen  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+MFMA_FP8_PEAK_TFS = 5000.0     # MI355X dense fp8 MFMA, TFLOP/s
+# fp32 vector ALU without packed instructions: 256 CUs x 4 SIMDs x 16 lanes x
+# 2.4 GHz = 39.3 T lane operations per second (157.3 TFLOP/s counts packed
+# FMAs, two lanes' worth of two flops each)
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 METRIC = "tree-verify attention KV GB/s + rows/s, % of MI355X HBM peak at long ctx"
 KERNEL_SRC = os.path.join(ROOT, "tree_attention_verify_amd", "csrc", "tree_attention.hip")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -131,7 +136,8 @@ def prefix_kernel_name(wl):
     """The split-K prefix kernel the library launches for this shape."""
     if wl.dtype != "bf16":
         return "k_prefix_f32"
-    return "k_prefix_mfma_pipe" if wl.R * (wl.Hq // wl.Hkv) > 128 else "k_prefix_mfma"
+    wide = wl.R * (wl.Hq // wl.Hkv) > 128 and (wl.kv != "fp8" or wl.D == 128)
+    return "k_prefix_mfma_pipe" if wide else "k_prefix_mfma"
 
 
 def log(*a):
@@ -258,6 +264,109 @@ def cpu_baseline(wl, inp, masks_np, budget_s):
                       "oracle time, scaled to the whole step" % (done, n_rows, total_t)}
 
 
+SAMPLED_METRIC = "sampled tree verify: target logits GB/s (Gumbel-max draws + greedy walk)"
+# vector ALU operations per logit of the Gumbel-max draw: a quarter of a
+# Philox4x32-10 block (10 rounds of 2 32x32->64 multiplies and 2 three-way
+# XORs), the uniform and its complement (2 conversions, 2 FMAs), the series
+# (4 FMAs) and the two logarithms with their scalings (4), the select, the
+# score FMA, the NaN clamp and the compare with its two selects (6), and
+# the bf16 widening (1)
+SAMPLE_OPS_PER_LOGIT = 10 + 4 + 4 + 4 + 1 + 6 + 1
+
+
+def run_sampled(args):
+    """Sampled verify on the EAGLE-style verify shape: 32 requests x 64 rows,
+    a 128256-token vocabulary of bf16 logits (525 MB): one step is
+    tree_sample_gumbel (the draws) then verify_tree_greedy over them."""
+    L = tav.lib()
+    wl = gen.WORKLOADS["eagle64"]
+    B, N, V = wl.B, wl.N, gen.SAMPLE_VOCAB
+    inp = gen.make_inputs(wl, args.seed, "cpu", with_tensors=False)
+    # every request samples (temperature > 0): greedy rows would skip the noise
+    s = gen.make_sample_inputs(B, N, V, args.seed, "bf16", "cuda", temperatures=(0.6, 1.0, 1.3))
+    t = lambda x, dt=torch.int32: torch.as_tensor(np.ascontiguousarray(x)).to(dt).to("cuda")
+    parents = t(inp.parents)
+    m = tav.tree_build_masks(parents, vc=t(np.full(B, wl.P, np.int32)))
+    positions = m["positions"]
+    temp = t(s.temperature, torch.float32)
+    seed = t(s.seed.view(np.int64), torch.int64)
+    draft = t(inp.draft)
+    ws = torch.empty(tav.tree_sample_workspace_size(B, N, V), dtype=torch.uint8, device="cuda")
+    draws = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    path = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    alen = torch.empty((B,), dtype=torch.int32, device="cuda")
+    toks = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    lg = s.logits
+
+    def run(ev=None):
+        if ev is not None:
+            ev[0].record()
+        assert L.tree_sample_gumbel(lg.data_ptr(), tav.TAV_BF16, lg.stride(1), V, B, N,
+                                    temp.data_ptr(), seed.data_ptr(), positions.data_ptr(),
+                                    draws.data_ptr(), ws.data_ptr(), ws.numel(), stream) == 0
+        if ev is not None:
+            ev[1].record()
+        assert L.verify_tree_greedy(draft.data_ptr(), draws.data_ptr(), parents.data_ptr(), B, N,
+                                    path.data_ptr(), alen.data_ptr(), toks.data_ptr(),
+                                    stream) == 0
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    pairs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+             for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        run(pairs[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+    nbytes = B * N * V * 2
+    ops = SAMPLE_OPS_PER_LOGIT * B * N * V
+    res = {"metric": SAMPLED_METRIC, "value": round(nbytes / (ms_step * 1e-3) / 1e9, 2),
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "sampled verify, %d requests x %d rows (EAGLE top-8 trees), "
+                                  "vocabulary %d, bf16 logits N(0, 4)" % (B, N, V),
+                      "temperatures": sorted(set(float(x) for x in s.temperature))},
+           "rows_per_s": round(B * N / (ms_step * 1e-3), 1),
+           "roofline": {"kernel": "k_gumbel_partial", "bound": "alu",
+                        "achieved": round(ops / (k_ms * 1e-3) / 1e12, 2),
+                        "peak": round(VALU_PEAK_TOPS, 2), "unit": "T ops/s",
+                        "frac": round(ops / (k_ms * 1e-3) / 1e12 / VALU_PEAK_TOPS, 4),
+                        "ops_per_logit": SAMPLE_OPS_PER_LOGIT, "traffic": None,
+                        "avg_launch_ms": round(k_ms, 4),
+                        "hbm_gbs": round(nbytes / (k_ms * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(nbytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+    if args.cpu_budget > 0:
+        import oracle
+        rng = np.random.default_rng(0)
+        pos_np = positions.cpu().numpy()
+        n, total_t, done = 8, 0.0, 0
+        while total_t < args.cpu_budget and done < B * N and n > 0:
+            rows = [(int(rng.integers(B)), int(rng.integers(N))) for _ in range(n)]
+            sub = np.stack([gen.bf16_bits(lg[b, i]) for b, i in rows])[:, None, :]
+            t0 = time.perf_counter()
+            oracle.sample_gumbel(sub, np.array([s.temperature[b] for b, _ in rows], np.float32),
+                                 np.array([s.seed[b] for b, _ in rows], np.uint64),
+                                 np.array([[pos_np[b, i]] for b, i in rows], np.int32))
+            total_t += time.perf_counter() - t0
+            done += n
+            n = min(2 * n, 256, B * N - done)
+        t_full = total_t * B * N / done
+        cores = len(os.sched_getaffinity(0))
+        omp = os.environ.get("OMP_NUM_THREADS")
+        res["cpu_baseline"] = {"value": round(nbytes / t_full / 1e9, 4), "unit": "GB/s",
+                               "cores": min(cores, int(omp)) if omp else cores, "kind": "oracle",
+                               "sample": "%d of %d rows, %.1f s of fp64 oracle time, scaled to "
+                                         "the whole step" % (done, B * N, total_t)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,6 +380,9 @@ def main():
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB copy (calibrates FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--sampled", action="store_true",
+                    help="time the sampled verify (Gumbel-max draws over a 128256-token "
+                         "vocabulary, then the greedy walk) instead of the attention step")
     ap.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
                     help="after the timed steps, run steps back to back for SECONDS (for board "
                          "power and clock readings taken meanwhile) and report their rate")
@@ -290,6 +402,9 @@ def main():
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.sampled:
+        run_sampled(args)
+        return
     wl = gen.WORKLOADS[args.workload]
     log("workload", wl)
     t0 = time.perf_counter()
@@ -373,12 +488,19 @@ def main():
     }
     # shapes past the ridge (flop per byte above peak MFMA / peak HBM) are
     # MFMA-bound: report the prefix kernel against the bf16 MFMA peak instead
-    if prefix_flops / prefix_bytes > MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9):
+    # The wide-row kernel under an FP8 cache runs the scores (half the flops)
+    # on the FP8 MFMA and PV on bf16: its peak is the harmonic combination.
+    mfma_peak = MFMA_BF16_PEAK_TFS
+    if wl.kv == "fp8" and prefix_kernel_name(wl) == "k_prefix_mfma_pipe":
+        mfma_peak = 2.0 / (1.0 / MFMA_FP8_PEAK_TFS + 1.0 / MFMA_BF16_PEAK_TFS)
+    if prefix_flops / prefix_bytes > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9):
         rf = res["roofline"]
         tfs = prefix_flops / (prefix_avg * 1e-3) / 1e12
-        rf.update({"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS,
-                   "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+        rf.update({"bound": "mfma", "achieved": round(tfs, 1), "peak": round(mfma_peak, 1),
+                   "unit": "TFLOP/s", "frac": round(tfs / mfma_peak, 4),
                    "algorithmic_flops": prefix_flops, "hbm_gbs": round(achieved, 1)})
+        if mfma_peak != MFMA_BF16_PEAK_TFS:
+            rf["peak_note"] = "scores on the fp8 MFMA (5000), PV on bf16 (2500)"
     if sustained is not None:
         res["sustained_ms_per_step"] = round(sustained, 4)
     t = traffic_for(wl.name)

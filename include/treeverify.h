@@ -5,6 +5,8 @@
  *   tree_build_masks     parents -> depth, 64-bit ancestor masks, positions
  *   tree_attention       paged prefix + masked tree window -> out, base-2 LSE
  *   verify_tree_greedy   draft tokens, target argmax -> accepted path
+ *   tree_sample_gumbel   logits -> target draws keyed by (seed, position),
+ *                        for the sampled verify
  *   compact_window_rows  accepted path -> rows moved to the window's front
  *   tree_shift_positions load_step / compact_rows position shifts
  *
@@ -271,6 +273,40 @@ typedef struct {
 tav_status compact_window_rows(const tav_rows *tables, int32_t n_tables,
                                const int32_t *accepted_path, const int32_t *accept_len,
                                int32_t B, int32_t N, void *stream);
+
+/*
+ * Sampled verify ([DTS] "Sampled verify keys noise by position"): the target
+ * token of every verify row drawn by Gumbel-max, keyed by (seed of the
+ * request, the position the node predicts) -- positions[b][i] + 1, where
+ * positions is vc + depth as tree_build_masks writes it -- never by the row,
+ * so siblings share their noise and a chain row draws what plain decoding
+ * draws at that position.  Acceptance is then verify_tree_greedy with these
+ * tokens as target_argmax (a child is accepted when it equals its parent's
+ * draw).
+ *
+ * Noise: Philox4x32-10 (Salmon et al., "Parallel Random Numbers: As Easy as
+ * 1, 2, 3", SC 2011; the pages name no generator) at counter {v / 4, key
+ * position, 0, 0} under key {seed & 0xffffffff, seed >> 32}; word v % 4 of
+ * token v, top 24 bits b: u = (b + 1/2) / 2^24, g = -ln(-ln u).
+ * z_v = logits[v] / T + g_v in fp32; token = argmax_v z_v, the lowest v on
+ * ties, NaN ranking last (a row of -inf / NaN only gives token 0).
+ * T = temperature[b]; T <= 0 (or NaN) takes the argmax of the logits.
+ *
+ * logits      device [B][N][row_stride] elements of dtype (TAV_BF16 or
+ *             TAV_F32), V used per row; 16-byte aligned, row_stride >= V and
+ *             row_stride * element size a multiple of 16 bytes
+ * temperature device float [B]; seed device uint64 [B]
+ * positions   device int32 [B][N]
+ * tokens      device int32 [B][N] out
+ * workspace   device memory of >= tree_sample_workspace_size(B, N, V)
+ *             bytes, 256-byte aligned; scratch between calls
+ * B >= 0; 1 <= N <= 64; V >= 1
+ */
+size_t tree_sample_workspace_size(int32_t B, int32_t N, int32_t V);
+tav_status tree_sample_gumbel(const void *logits, tav_dtype dtype, int64_t row_stride, int32_t V,
+                              int32_t B, int32_t N, const float *temperature,
+                              const uint64_t *seed, const int32_t *positions, int32_t *tokens,
+                              void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

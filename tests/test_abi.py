@@ -144,3 +144,47 @@ def test_empty_batch_is_a_no_op(L):
 def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         tav.tree_build_masks(torch.zeros((1, 4), dtype=torch.int32))
+
+
+def test_sample_workspace_size_host_only(L):
+    n = L.tree_sample_workspace_size(32, 64, 128256)
+    assert n > 0 and n % 256 == 0
+    assert L.tree_sample_workspace_size(32, 64, 128256) >= 32 * 64 * 8   # (z, token) per row
+    assert L.tree_sample_workspace_size(-1, 64, 100) == 0
+    assert L.tree_sample_workspace_size(2, 0, 100) == 0
+    assert L.tree_sample_workspace_size(2, 8, 0) == 0
+
+
+def sample_call(L, **kw):
+    a = dict(logits=FAKE, dtype=tav.TAV_BF16, rs=128256, V=128256, B=2, N=8, T=FAKE, seed=FAKE,
+             pos=FAKE, tok=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    st = L.tree_sample_gumbel(a["logits"], a["dtype"], a["rs"], a["V"], a["B"], a["N"], a["T"],
+                              a["seed"], a["pos"], a["tok"], a["ws"], a["wsb"], None)
+    return st, L.tav_last_error().decode()
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status,words", [
+    (dict(N=65), 1, ["N must be in [1, 64]"]),
+    (dict(V=0), 1, ["V must be >= 1"]),
+    (dict(dtype=tav.TAV_FP8_E4M3), 2, ["logits dtype"]),
+    (dict(rs=100), 1, ["row_stride must be >= V"]),
+    (dict(rs=128260, V=128257), 1, ["multiple of 16 bytes"]),
+    (dict(logits=FAKE + 8), 1, ["16-byte aligned"]),
+    (dict(seed=None), 1, ["seed is NULL"]),
+    (dict(pos=None), 1, ["positions is NULL"]),
+    (dict(wsb=64), 3, ["workspace too small"]),
+    (dict(ws=FAKE + 64), 3, ["256-byte aligned"]),
+])
+def test_tree_sample_gumbel_rejects(L, kw, status, words):
+    st, msg = sample_call(L, **kw)
+    assert st == status, msg
+    for w in words:
+        assert w in msg, msg
+
+
+def test_sample_empty_batch_is_a_no_op(L):
+    st, msg = sample_call(L, B=0, logits=None, T=None, seed=None, pos=None, tok=None, ws=None,
+                          wsb=0)
+    assert st == 0, msg

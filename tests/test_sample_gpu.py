@@ -1,0 +1,202 @@
+"""GPU parity of the sampled verify: Gumbel-max draws keyed by (seed,
+predicted position) through the C ABI, against the CPU fp64 oracle.
+
+The draw is an argmax decided in floating point.  The kernel scores in fp32
+and the oracle in fp64, so a row whose two best perturbed scores are closer
+than the fp32 error of the scores may legitimately go either way.  Every row
+must therefore either match the oracle's token, or pick a token whose oracle
+score is within TIE_TOL of the oracle's best (a near tie); and near ties must
+be rare.  Greedy rows (temperature 0) compare plain logits and are
+bit-exact.  The accepted paths of the sampled verify are then bit-exact
+against the oracle's greedy walk over the same draws.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_attention_verify_amd as tav
+from tree_attention_verify_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+TIE_TOL = 1e-4     # absolute, on perturbed scores of magnitude <= ~30
+
+
+def say(*a):
+    print("[sample]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tav.lib()
+
+
+def dev(x, dtype=torch.int32):
+    return torch.as_tensor(np.ascontiguousarray(x)).to(dtype).cuda()
+
+
+def bits(t):
+    return gen.bf16_bits(t.contiguous())
+
+
+def oracle_z(lrow, T, seed, pos, v):
+    """fp64 perturbed score of token v of one row."""
+    l = float(lrow[v])
+    if not T > 0:
+        return l if l == l else -math.inf
+    u = oracle.gumbel_uniform(seed, int(pos) + 1, v)
+    z = l / float(np.float32(T)) - math.log(-math.log(u))
+    return z if z == z else -math.inf
+
+
+def check_draws(got, s, positions, rows=None, tag=""):
+    """got int32 [B][N] from the GPU; the oracle on the listed (b, i) rows (all
+    by default)."""
+    B, N, V = s.logits.shape
+    if rows is None:
+        rows = [(b, i) for b in range(B) for i in range(N)]
+    lg = s.logits.detach().float().cpu().numpy()
+    sub = np.stack([lg[b, i] for b, i in rows])[:, None, :].astype(np.float32)
+    temps = np.array([s.temperature[b] for b, _ in rows], np.float32)
+    seeds = np.array([s.seed[b] for b, _ in rows], np.uint64)
+    pos = np.array([[positions[b, i]] for b, i in rows], np.int32)
+    if s.logits.dtype == torch.bfloat16:
+        sub_in = np.stack([bits(s.logits[b, i]) for b, i in rows])[:, None, :]
+    else:
+        sub_in = sub
+    tok, zmax, z2 = oracle.sample_gumbel(sub_in, temps, seeds, pos)
+    ties = 0
+    for n, (b, i) in enumerate(rows):
+        g, o = int(got[b, i]), int(tok[n, 0])
+        if g == o:
+            continue
+        assert temps[n] > 0, "%s greedy row (%d, %d): %d vs %d" % (tag, b, i, g, o)
+        assert 0 <= g < V, (tag, b, i, g)
+        zg = oracle_z(sub[n, 0], temps[n], int(seeds[n]), pos[n, 0], g)
+        assert zg >= zmax[n, 0] - TIE_TOL, "%s row (%d, %d): token %d (z %.7f) vs %d (z %.7f)" % (
+            tag, b, i, g, zg, o, zmax[n, 0])
+        ties += 1
+    say(tag, "%d rows, %d near-tie differences" % (len(rows), ties))
+    assert ties <= max(1, len(rows) // 100)
+    return tok
+
+
+def tree_positions(B, N, seed, vc):
+    wl = gen.Workload("s", B, 0, N, 4, 1, 64, "bf16", 16, "random", depth_cap=6)
+    inp = gen.make_inputs(wl, seed, "cpu", with_tensors=False)
+    r = oracle.build_masks(inp.parents, vc=vc)
+    return inp, r["positions"]
+
+
+CASES = {
+    # name: (B, N, V, dtype, row_stride)
+    "bf16_v50k": (3, 16, 50000, "bf16", None),
+    "bf16_ragged": (4, 8, 12345, "bf16", 12352),
+    "f32_v1003": (2, 64, 1003, "f32", 1004),
+    "bf16_v7": (2, 5, 7, "bf16", 8),
+    "bf16_v1": (1, 3, 1, "bf16", 8),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_sample_parity_every_row(name):
+    B, N, V, dt, rs = CASES[name]
+    say("case", name, B, N, V, dt, rs)
+    s = gen.make_sample_inputs(B, N, V, 5, dt, "cuda", row_stride=rs)
+    vc = np.arange(B, dtype=np.int32) * 1000 + 77
+    inp, pos = tree_positions(B, N, 9, vc)
+    got = tav.tree_sample_gumbel(s.logits, dev(s.temperature, torch.float32),
+                                 dev(s.seed.view(np.int64), torch.int64), dev(pos))
+    torch.cuda.synchronize()
+    check_draws(got.cpu().numpy(), s, pos, tag=name)
+
+
+def test_sample_special_values():
+    B, N, V = 2, 4, 3000
+    s = gen.make_sample_inputs(B, N, V, 6, "bf16", "cuda")
+    s.temperature[:] = [1.0, 0.0]
+    lg = s.logits
+    lg[0, 0, :] = float("nan")
+    lg[0, 0, 2999] = -5.0                    # NaN ranks last: the only number wins
+    lg[0, 1, :] = float("-inf")              # nothing to draw: token 0
+    lg[0, 2, 17] = float("inf")              # +inf wins whatever the noise
+    lg[1, 0, :] = 3.0                        # greedy tie: the lowest index
+    lg[1, 1, 1234] = float("nan")
+    pos = np.array([[5, 6, 6, 7], [100, 101, 101, 102]], np.int32)
+    got = tav.tree_sample_gumbel(lg, dev(s.temperature, torch.float32),
+                                 dev(s.seed.view(np.int64), torch.int64), dev(pos))
+    torch.cuda.synchronize()
+    g = got.cpu().numpy()
+    assert g[0, 0] == 2999 and g[0, 1] == 0 and g[0, 2] == 17 and g[1, 0] == 0
+    assert g[1, 1] != 1234
+    check_draws(g, s, pos, tag="special")
+
+
+def test_siblings_share_noise_on_gpu():
+    # every row holds the same logits; rows at equal positions draw equally
+    B, N, V = 1, 64, 40000
+    s = gen.make_sample_inputs(B, N, V, 8, "bf16", "cuda")
+    s.logits[0, :, :] = s.logits[0, :1, :].clone()
+    s.temperature[:] = 1.0
+    pos = np.repeat(np.arange(16, dtype=np.int32), 4)[None, :] + 300
+    got = tav.tree_sample_gumbel(s.logits, dev(s.temperature, torch.float32),
+                                 dev(s.seed.view(np.int64), torch.int64), dev(pos))
+    torch.cuda.synchronize()
+    g = got.cpu().numpy().reshape(16, 4)
+    assert (g == g[:, :1]).all()
+    assert len(set(g[:, 0].tolist())) > 4
+    check_draws(got.cpu().numpy(), s, pos, rows=[(0, 4 * k) for k in range(16)], tag="siblings")
+
+
+def test_sampled_verify_matches_oracle_walk():
+    # drafts drawn to agree with the target's draws along random branches
+    B, N, V = 8, 16, 32000
+    wl = gen.WORKLOADS["random16"].with_(B=B)
+    inp = gen.make_inputs(wl, 12, "cpu", with_tensors=False)
+    vc = np.full(B, 2048, np.int32)
+    pos = oracle.build_masks(inp.parents, vc=vc)["positions"]
+    s = gen.make_sample_inputs(B, N, V, 12, "bf16", "cuda")
+    s.temperature[:] = 0.8
+    Tg, Sg = dev(s.temperature, torch.float32), dev(s.seed.view(np.int64), torch.int64)
+    draws = tav.tree_sample_gumbel(s.logits, Tg, Sg, dev(pos))
+    torch.cuda.synchronize()
+    d = draws.cpu().numpy()
+    # each node's draft token: its parent's draw with probability 0.7
+    rng = np.random.default_rng(3)
+    draft = rng.integers(0, V, size=(B, N)).astype(np.int32)
+    for b in range(B):
+        for i in range(1, N):
+            if rng.random() < 0.7:
+                draft[b, i] = d[b, inp.parents[b, i]]
+    r = tav.verify_tree_sampled(dev(draft), s.logits, Tg, Sg, dev(pos), dev(inp.parents))
+    torch.cuda.synchronize()
+    tok = check_draws(r["draws"].cpu().numpy(), s, pos, tag="verify")
+    ro = oracle.verify_greedy(draft, r["draws"].cpu().numpy(), inp.parents)
+    for k in ("accepted_path", "accept_len", "accepted_tokens"):
+        assert np.array_equal(r[k].cpu().numpy(), ro[k]), k
+    assert int(ro["accept_len"].max()) > 1
+
+
+def test_sample_full_size_sampled_rows():
+    # the eagle64 verify shape: 32 requests x 64 rows over a 128256-token
+    # vocabulary (bf16, 525 MB of logits), in the launch the benchmark times;
+    # 48 rows checked against the oracle, every draw in range
+    B, N, V = 32, 64, gen.SAMPLE_VOCAB
+    s = gen.make_sample_inputs(B, N, V, 3, "bf16", "cuda")
+    wl = gen.WORKLOADS["eagle64"]
+    inp = gen.make_inputs(wl, 3, "cpu", with_tensors=False)
+    pos = oracle.build_masks(inp.parents, vc=np.full(B, wl.P, np.int32))["positions"]
+    got = tav.tree_sample_gumbel(s.logits, dev(s.temperature, torch.float32),
+                                 dev(s.seed.view(np.int64), torch.int64), dev(pos))
+    torch.cuda.synchronize()
+    g = got.cpu().numpy()
+    assert ((g >= 0) & (g < V)).all()
+    rng = np.random.default_rng(1)
+    rows = sorted({(int(rng.integers(B)), int(rng.integers(N))) for _ in range(48)})
+    check_draws(g, s, pos, rows=rows, tag="full")

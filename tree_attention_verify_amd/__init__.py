@@ -9,7 +9,10 @@ another implementation.
 
 Entry points (same names as the C ABI):
   tree_build_masks, tree_shift_positions, tree_attention,
-  tree_attention_workspace_size, verify_tree_greedy, compact_window_rows
+  tree_attention_workspace_size, verify_tree_greedy, compact_window_rows,
+  tree_sample_gumbel, tree_sample_workspace_size
+plus verify_tree_sampled (tree_sample_gumbel, then verify_tree_greedy over
+the draws).
 """
 from __future__ import annotations
 
@@ -30,7 +33,8 @@ _STATUS = {0: "TAV_OK", 1: "TAV_ERR_INVALID_ARG", 2: "TAV_ERR_UNSUPPORTED",
 # Every function the header declares.
 EXPORTS = ("tav_last_error", "tav_version", "tree_build_masks", "tree_shift_positions",
            "tree_attention_workspace_size", "tree_attention", "tree_attention_prefix",
-           "tree_attention_window_merge", "verify_tree_greedy", "compact_window_rows")
+           "tree_attention_window_merge", "verify_tree_greedy", "compact_window_rows",
+           "tree_sample_workspace_size", "tree_sample_gumbel")
 
 
 class TavError(RuntimeError):
@@ -85,8 +89,12 @@ def lib() -> ctypes.CDLL:
             getattr(L, f).restype = ctypes.c_int
         L.verify_tree_greedy.argtypes = [P, P, P, I32, I32, P, P, P, P]
         L.compact_window_rows.argtypes = [ctypes.POINTER(TavRows), I32, P, P, I32, I32, P]
+        L.tree_sample_workspace_size.argtypes = [I32, I32, I32]
+        L.tree_sample_workspace_size.restype = ctypes.c_size_t
+        L.tree_sample_gumbel.argtypes = [P, ctypes.c_int, I64, I32, I32, I32, P, P, P, P, P,
+                                         ctypes.c_size_t, P]
         for f in ("tree_build_masks", "tree_shift_positions", "tree_attention",
-                  "verify_tree_greedy", "compact_window_rows"):
+                  "verify_tree_greedy", "compact_window_rows", "tree_sample_gumbel"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -248,6 +256,53 @@ def verify_tree_greedy(draft_tokens: torch.Tensor, target_argmax: torch.Tensor,
     _check(lib().verify_tree_greedy(_ptr(draft_tokens), _ptr(target_argmax), _ptr(parents), B, N,
                                     _ptr(path), _ptr(alen), _ptr(tok), _stream(dev)))
     return {"accepted_path": path, "accept_len": alen, "accepted_tokens": tok}
+
+
+def tree_sample_workspace_size(B: int, N: int, V: int) -> int:
+    return int(lib().tree_sample_workspace_size(B, N, V))
+
+
+def tree_sample_gumbel(logits: torch.Tensor, temperature: torch.Tensor, seed: torch.Tensor,
+                       positions: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+    """Gumbel-max target draw of every verify row, keyed by (seed[b],
+    positions[b][i] + 1).
+
+    logits bf16 or float32 [B][N][V] (rows may be padded: the last dim's
+    stride must span a multiple of 16 bytes); temperature float32 [B] (<= 0:
+    greedy argmax); seed int64 [B] (the uint64 seed's bits); positions int32
+    [B][N] (vc + depth).  -> tokens int32 [B][N]."""
+    if logits.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("logits must be bfloat16 or float32, got %s" % logits.dtype)
+    if not logits.is_cuda or logits.dim() != 3 or logits.stride(2) != 1 \
+            or logits.stride(0) != logits.shape[1] * logits.stride(1):
+        raise ValueError("logits must be a [B][N][V] GPU tensor with unit channel stride and "
+                         "rows at a constant stride")
+    B, N, V = logits.shape
+    dev = logits.device
+    _need(temperature, "temperature", torch.float32, dev, (B,))
+    _need(seed, "seed", torch.int64, dev, (B,))
+    _need(positions, "positions", torch.int32, dev, (B, N))
+    need = tree_sample_workspace_size(B, N, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    dt = TAV_BF16 if logits.dtype == torch.bfloat16 else TAV_F32
+    _check(lib().tree_sample_gumbel(_ptr(logits), dt, logits.stride(1), V, B, N, _ptr(temperature),
+                                    _ptr(seed), _ptr(positions), _ptr(tokens), _ptr(workspace),
+                                    workspace.numel(), _stream(dev)))
+    return tokens
+
+
+def verify_tree_sampled(draft_tokens: torch.Tensor, logits: torch.Tensor,
+                        temperature: torch.Tensor, seed: torch.Tensor, positions: torch.Tensor,
+                        parents: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+    """Sampled verify: the Gumbel-max draws of every row, then the greedy
+    tree walk over them.  -> dict(draws, accepted_path, accept_len,
+    accepted_tokens)."""
+    draws = tree_sample_gumbel(logits, temperature, seed, positions, workspace)
+    r = verify_tree_greedy(draft_tokens, draws, parents)
+    r["draws"] = draws
+    return r
 
 
 @dataclasses.dataclass

@@ -347,3 +347,39 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.float8_e4m3fn:
         return t.view(torch.uint8).numpy()
     return t.numpy()
+
+
+# ---------------------------------------------------------------------------
+# sampled verify inputs
+# ---------------------------------------------------------------------------
+
+SAMPLE_VOCAB = 128256   # vocabulary of the Llama-3 family (shapes only)
+
+
+@dataclasses.dataclass
+class SampleInputs:
+    logits: torch.Tensor        # [B][N][V] (a view of [B][N][row_stride] when padded)
+    temperature: np.ndarray     # [B] float32 (0 = greedy)
+    seed: np.ndarray            # [B] uint64
+
+
+def make_sample_inputs(B: int, N: int, V: int, seed: int, dtype: str = "bf16",
+                       device="cpu", scale: float = 2.0, row_stride: Optional[int] = None,
+                       temperatures=(0.0, 0.6, 1.0, 1.3)) -> SampleInputs:
+    """Seeded target logits of every verify row, N(0, scale^2) drawn in fp32
+    and rounded to the dtype, with a per-request temperature drawn from
+    `temperatures` and a per-request 64-bit seed.  row_stride > V pads each
+    row (the padding holds NaN, which no draw may read)."""
+    r = _streams(seed + 104729, 1)[0]
+    rs = V if row_stride is None else row_stride
+    dev = torch.device(device)
+    buf = torch.full((B, N, rs), float("nan"), dtype=TORCH_DTYPE[dtype], device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(_torch_seed(seed, 11))
+    vals = torch.empty((B, N, V), dtype=TORCH_DTYPE[dtype], device=dev)
+    _randn_into(vals, g)
+    buf[:, :, :V] = vals * scale if dtype == "f32" else (vals.float() * scale).to(buf.dtype)
+    temperature = r.choice(np.asarray(temperatures, np.float32), size=B).astype(np.float32)
+    seeds = r.integers(0, 2 ** 63, size=B, dtype=np.int64).astype(np.uint64) * np.uint64(2) + \
+        r.integers(0, 2, size=B).astype(np.uint64)
+    return SampleInputs(buf[:, :, :V], temperature, seeds)
