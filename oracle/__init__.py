@@ -69,6 +69,12 @@ def lib():
         L.orc_gumbel_uniform.restype = D
         L.orc_sample_gumbel.argtypes = [P, I, I64, I, I, I, P, P, P, P, P, P]
         L.orc_sample_gumbel.restype = ctypes.c_int
+        L.orc_beam_step.argtypes = [P, P, P, P, I, I, I, I, I, P, P, P, P, P]
+        L.orc_beam_step.restype = ctypes.c_int
+        L.orc_select_candidates.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P]
+        L.orc_select_candidates.restype = ctypes.c_int
+        L.orc_retrieve_links.argtypes = [P, I, I, P, P]
+        L.orc_retrieve_links.restype = ctypes.c_int
         L.orc_tree_attention.argtypes = [P, P, P, I, I, I64, I64, I64, P, I, I, P, I,
                                          P, I, I, I, I, I, I, D, P, I64, P, P]
         L.orc_causal_attention.argtypes = [P, P, P, I, I, I, I, I, I, D, P, P]
@@ -296,3 +302,56 @@ def sample_gumbel(logits, temperature, seed, positions):
     _check(lib().orc_sample_gumbel(_p(logits), dt, V, V, B, N, _p(temperature), _p(seed),
                                    _p(positions), _p(tokens), _p(zmax), _p(z2)), "sample_gumbel")
     return tokens, zmax, z2
+
+
+def beam_step(scores, surv_idx, child_p, child_tok, pool, pool_base):
+    """One EAGLE-2 expansion step.  scores float32 [B][S], surv_idx int32
+    [B][S], child_p float32 [B][S][K], child_tok int32 [B][S][K]; pool = dict
+    of "scores" float32 [B][C], "parents" int32 [B][C], "tokens" int32 [B][C],
+    updated in place at entries pool_base .. pool_base + S*K - 1.  Returns
+    (next_scores float32 [B][K], next_idx int32 [B][K])."""
+    scores = _c(scores, np.float32)
+    surv_idx = _c(surv_idx, np.int32)
+    child_p = _c(child_p, np.float32)
+    child_tok = _c(child_tok, np.int32)
+    B, S, K = child_p.shape
+    C = pool["scores"].shape[1]
+    for k in ("scores", "parents", "tokens"):
+        assert pool[k].flags.c_contiguous
+    ns = np.empty((B, K), np.float32)
+    ni = np.empty((B, K), np.int32)
+    _check(lib().orc_beam_step(_p(scores), _p(surv_idx), _p(child_p), _p(child_tok), B, S, K, C,
+                               int(pool_base), _p(pool["scores"]), _p(pool["parents"]),
+                               _p(pool["tokens"]), _p(ns), _p(ni)), "beam_step")
+    return ns, ni
+
+
+def select_candidates(pool_scores, pool_parents, pool_tokens, root_tokens, N, order=0):
+    """The verify tree from a candidate pool: the N - 1 best candidates
+    (score descending, lower pool index on ties, NaN last), numbered by pool
+    order (order 0) or depth first best child first (order 1), the root as
+    node 0.  Returns dict(parents, tokens, selected int32 [B][N],
+    tree_error int32 [B])."""
+    sc = _c(pool_scores, np.float32)
+    pp = _c(pool_parents, np.int32)
+    pt = _c(pool_tokens, np.int32)
+    rt = _c(root_tokens, np.int32)
+    B, C = sc.shape
+    out = {k: np.empty((B, N), np.int32) for k in ("parents", "tokens", "selected")}
+    out["tree_error"] = np.empty((B,), np.int32)
+    _check(lib().orc_select_candidates(_p(sc), _p(pp), _p(pt), _p(rt), B, C, int(N), int(order),
+                                       _p(out["parents"]), _p(out["tokens"]),
+                                       _p(out["selected"]), _p(out["tree_error"])),
+           "select_candidates")
+    return out
+
+
+def retrieve_links(parents):
+    """(next_token, next_sibling) int32 [B][N]: first child and next sibling
+    in node order, -1 where there is none."""
+    par = _c(parents, np.int32)
+    B, N = par.shape
+    nt = np.empty((B, N), np.int32)
+    nsb = np.empty((B, N), np.int32)
+    _check(lib().orc_retrieve_links(_p(par), B, N, _p(nt), _p(nsb)), "retrieve_links")
+    return nt, nsb

@@ -623,3 +623,238 @@ int orc_sample_gumbel(const void *logits, int dtype, int64_t row_stride, int V, 
     }
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* tree construction: EAGLE-2 beam, global selection, numbering, links */
+/* ------------------------------------------------------------------ */
+
+/* Candidate order of the tree construction: the higher score first, then the
+ * lower candidate id; a NaN score ranks after every number ([DTS] "Tree
+ * construction is deterministic": ties go to the lower candidate id, NaN
+ * scores rank last).  Returns 1 when candidate a comes before b. */
+static int orc_cand_before(float sa, int a, float sb, int b)
+{
+    int na = isnan(sa), nb = isnan(sb);
+    if (na != nb)
+        return nb;           /* the number before the NaN */
+    if (!na && sa != sb)
+        return sa > sb;
+    return a < b;
+}
+
+/*
+ * One EAGLE-2 expansion step for every request ([MEM] "EAGLE-2: the tree
+ * stops being a constant": the surviving paths' cumulative scores are
+ * multiplied by the new conditional probabilities and the best topk paths
+ * are kept; [ETA] "candidate pool to verify rows": score_list / token_list /
+ * parents_list, cumulative path scores).  Survivor s (score scores[b][s],
+ * pool index surv_idx[b][s], -1 for the root) has K children with
+ * conditional probabilities child_p[b][s][j] and tokens child_tok[b][s][j].
+ * Child (s, j) is pool entry pool_base + s*K + j with score
+ * scores[b][s] * child_p[b][s][j] (an fp32 product), parent surv_idx[b][s]
+ * and its token.  The K best children by orc_cand_before (flat index s*K + j
+ * as the id) are the next survivors: next_scores[b][r], next_idx[b][r] =
+ * their pool indices, best first.  Pool arrays are [B][C]; 1 <= n_surv,
+ * K <= n_surv * K.
+ */
+int orc_beam_step(const float *scores, const int32_t *surv_idx, const float *child_p,
+                  const int32_t *child_tok, int B, int n_surv, int K, int C, int pool_base,
+                  float *pool_scores, int32_t *pool_parents, int32_t *pool_tokens,
+                  float *next_scores, int32_t *next_idx)
+{
+    int n = n_surv * K;
+    if (B < 0 || n_surv < 1 || K < 1 || pool_base < 0 || pool_base + n > C)
+        return ORC_BAD;
+    float *cs = (float *)malloc(sizeof(float) * n);
+    int *used = (int *)malloc(sizeof(int) * n);
+    for (int b = 0; b < B; ++b) {
+        for (int s = 0; s < n_surv; ++s)
+            for (int j = 0; j < K; ++j) {
+                int f = s * K + j;
+                float p = child_p[((int64_t)b * n_surv + s) * K + j];
+                cs[f] = scores[(int64_t)b * n_surv + s] * p;
+                pool_scores[(int64_t)b * C + pool_base + f] = cs[f];
+                pool_parents[(int64_t)b * C + pool_base + f] = surv_idx[(int64_t)b * n_surv + s];
+                pool_tokens[(int64_t)b * C + pool_base + f] =
+                    child_tok[((int64_t)b * n_surv + s) * K + j];
+                used[f] = 0;
+            }
+        /* K times: the best child not taken yet */
+        for (int r = 0; r < K; ++r) {
+            int best = -1;
+            for (int f = 0; f < n; ++f)
+                if (!used[f] && (best < 0 || orc_cand_before(cs[f], f, cs[best], best)))
+                    best = f;
+            used[best] = 1;
+            next_scores[(int64_t)b * K + r] = cs[best];
+            next_idx[(int64_t)b * K + r] = pool_base + best;
+        }
+    }
+    free(cs);
+    free(used);
+    return ORC_OK;
+}
+
+/*
+ * The verify tree of every request from its candidate pool ([MEM]
+ * organize_draft_results: flatten the score pool, take the num_draft_token
+ * - 1 best, sort the selected indices, gather their tokens, keep the parent
+ * topology; [ETA] "the verify root is not an ordinary draft candidate": the
+ * previous round's bonus token is prepended as node 0).  Pool entry c of
+ * request b has score pool_scores[b][c], parent pool index
+ * pool_parents[b][c] (-1 = the root) and token pool_tokens[b][c].
+ *
+ * The N - 1 best candidates by orc_cand_before are kept.  order 0 numbers
+ * them by ascending pool index (the pool order); order 1 numbers the tree
+ * depth first with each node's best child first ([DTS] "Tree construction
+ * is deterministic": the most likely path is then 0, 1, 2, ...).  Node 0 is
+ * the root with token root_tokens[b]; parents[b][i] is the node of entry
+ * i's parent; selected[b][i] is entry i's pool index (-1 for the root).
+ * Every kept candidate's parent must be kept or be the root ([MEM] "a
+ * missing parent must be rejected or repaired, never treated as a root"),
+ * and must precede it in the pool (as every expansion step appends after
+ * the candidates it expands);
+ * otherwise tree_error[b] = 1 + the first node (in pool order) whose parent
+ * is missing, and parents/tokens/selected of b are -1.  C >= N - 1.
+ */
+int orc_select_candidates(const float *pool_scores, const int32_t *pool_parents,
+                          const int32_t *pool_tokens, const int32_t *root_tokens, int B, int C,
+                          int N, int order, int32_t *parents, int32_t *tokens,
+                          int32_t *selected, int32_t *tree_error)
+{
+    if (B < 0 || N < 1 || N > 64 || C < N - 1 || (order != 0 && order != 1))
+        return ORC_BAD;
+    int *kept = (int *)malloc(sizeof(int) * (C + 1));
+    int *node_of = (int *)malloc(sizeof(int) * (C + 1));
+    for (int b = 0; b < B; ++b) {
+        const float *sc = pool_scores + (int64_t)b * C;
+        const int32_t *pp = pool_parents + (int64_t)b * C;
+        for (int c = 0; c < C; ++c)
+            kept[c] = 0;
+        /* N - 1 times: the best candidate not taken yet */
+        for (int r = 0; r < N - 1; ++r) {
+            int best = -1;
+            for (int c = 0; c < C; ++c)
+                if (!kept[c] && (best < 0 || orc_cand_before(sc[c], c, sc[best], best)))
+                    best = c;
+            kept[best] = 1;
+        }
+        /* closure */
+        int bad = -1, node = 1;
+        for (int c = 0; c < C; ++c) {
+            node_of[c] = -1;
+            if (!kept[c])
+                continue;
+            int p = pp[c];
+            if (bad < 0 && p != -1 && (p < 0 || p >= c || !kept[p]))
+                bad = node;
+            node_of[c] = node++;
+        }
+        if (tree_error)
+            tree_error[b] = bad < 0 ? 0 : 1 + bad;
+        int32_t *par = parents + (int64_t)b * N, *tok = tokens + (int64_t)b * N;
+        int32_t *sel = selected + (int64_t)b * N;
+        if (bad >= 0) {
+            for (int i = 0; i < N; ++i)
+                par[i] = tok[i] = sel[i] = -1;
+            continue;
+        }
+        /* pool order: entry rank among kept candidates by pool index */
+        int32_t tmp_sel[64];
+        tmp_sel[0] = -1;
+        for (int c = 0; c < C; ++c)
+            if (kept[c])
+                tmp_sel[node_of[c]] = c;
+        if (order == 1) {
+            /* depth first, best child first: an explicit stack of nodes
+             * (pool-order numbers); children pushed worst first */
+            int stack[64], sp = 0, next = 0, newnum[64];
+            stack[sp++] = 0;
+            while (sp > 0) {
+                int u = stack[--sp];
+                newnum[u] = next++;
+                int ch[64], nch = 0;
+                for (int i = 1; i < N; ++i) {
+                    int pc = pp[tmp_sel[i]];
+                    int pu = pc == -1 ? 0 : node_of[pc];
+                    if (pu == u)
+                        ch[nch++] = i;
+                }
+                /* sort children best first (insertion sort by the candidate order) */
+                for (int x = 1; x < nch; ++x)
+                    for (int y = x; y > 0; --y) {
+                        int a = ch[y], bb = ch[y - 1];
+                        if (orc_cand_before(sc[tmp_sel[a]], tmp_sel[a], sc[tmp_sel[bb]], tmp_sel[bb])) {
+                            ch[y] = bb;
+                            ch[y - 1] = a;
+                        }
+                    }
+                for (int x = nch - 1; x >= 0; --x)
+                    stack[sp++] = ch[x];
+            }
+            for (int i = 0; i < N; ++i) {
+                int c = tmp_sel[i];
+                int ni = newnum[i];
+                sel[ni] = c;
+                if (i == 0) {
+                    par[ni] = -1;
+                    tok[ni] = root_tokens[b];
+                } else {
+                    int pc = pp[c];
+                    par[ni] = pc == -1 ? 0 : newnum[node_of[pc]];
+                    tok[ni] = pool_tokens[(int64_t)b * C + c];
+                }
+            }
+        } else {
+            for (int i = 0; i < N; ++i) {
+                int c = tmp_sel[i];
+                sel[i] = c;
+                if (i == 0) {
+                    par[i] = -1;
+                    tok[i] = root_tokens[b];
+                } else {
+                    int pc = pp[c];
+                    par[i] = pc == -1 ? 0 : node_of[pc];
+                    tok[i] = pool_tokens[(int64_t)b * C + c];
+                }
+            }
+        }
+    }
+    free(kept);
+    free(node_of);
+    return ORC_OK;
+}
+
+/*
+ * First-child / next-sibling links of every tree ([MEM] "Flattening, and the
+ * two link arrays": retrieve_next_token[p] is p's first child,
+ * retrieve_next_sibling[i] is i's next sibling; [DDT] compile_ddtree_retrieve).
+ * Children are taken in node order (with depth-first best-child-first
+ * numbering, or pool order, that is the order the trees are numbered in);
+ * -1 where there is none.
+ */
+int orc_retrieve_links(const int32_t *parents, int B, int N, int32_t *next_token,
+                       int32_t *next_sibling)
+{
+    if (B < 0 || N < 1)
+        return ORC_BAD;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *par = parents + (int64_t)b * N;
+        for (int i = 0; i < N; ++i) {
+            next_token[(int64_t)b * N + i] = -1;
+            next_sibling[(int64_t)b * N + i] = -1;
+            for (int j = 0; j < N; ++j)
+                if (par[j] == i) {
+                    next_token[(int64_t)b * N + i] = j;
+                    break;
+                }
+            if (par[i] >= 0)
+                for (int j = i + 1; j < N; ++j)
+                    if (par[j] == par[i]) {
+                        next_sibling[(int64_t)b * N + i] = j;
+                        break;
+                    }
+        }
+    }
+    return ORC_OK;
+}

@@ -780,3 +780,223 @@ def test_sampled_chain_verify_accepts_matching_drafts():
     r = oracle.verify_greedy(draft, tok, par)
     assert int(r["accept_len"][0]) == N
     assert r["accepted_tokens"][0].tolist() == tok[0].tolist()
+
+
+# ---------------------------------------------------------------------------
+# tree construction: beam, selection, numbering, links
+# ---------------------------------------------------------------------------
+
+def test_retrieve_links_worked_examples():
+    g = load("retrieve.txt")
+    for k in ("eagle", "ddtree"):
+        nt, ns = oracle.retrieve_links(np.array([g[k + "_parents"]]))
+        assert nt[0].tolist() == g[k + "_next_token"]
+        assert ns[0].tolist() == g[k + "_next_sibling"]
+    # positions of the EAGLE example from its parents (vc = 5)
+    r = oracle.build_masks(np.array([g["eagle_parents"]]), vc=np.array([5]))
+    assert r["positions"][0].tolist() == g["eagle_positions"]
+    d = oracle.build_masks(np.array([g["ddtree_parents"]]))["depth"][0]
+    assert d[1:].tolist() == g["ddtree_depths"]
+
+
+def _walk_links(nt, ns):
+    """Depth-first traversal through the links; the order nodes are met."""
+    seen, stack = [], [0]
+    while stack:
+        u = stack.pop()
+        seen.append(u)
+        kids, c = [], nt[u]
+        while c != -1:
+            kids.append(c)
+            c = ns[c]
+        stack.extend(reversed(kids))
+    return seen
+
+
+def test_retrieve_links_cover_random_trees():
+    rng = np.random.default_rng(12)
+    for _ in range(200):
+        N = int(rng.integers(1, 65))
+        par = np.array([-1] + [int(rng.integers(0, i)) for i in range(1, N)], np.int32)
+        nt, ns = oracle.retrieve_links(par[None])
+        order = _walk_links(nt[0], ns[0])
+        assert sorted(order) == list(range(N))          # every node exactly once
+        for i in range(N):                              # links agree with the parents
+            kids = [j for j in range(N) if par[j] == i]
+            assert nt[0, i] == (kids[0] if kids else -1)
+            if i:
+                sib = [j for j in range(i + 1, N) if par[j] == par[i]]
+                assert ns[0, i] == (sib[0] if sib else -1)
+
+
+def _pool(rows):
+    B = 1
+    sc = np.array([[r[0] for r in rows]], np.float32)
+    pp = np.array([[r[1] for r in rows]], np.int32)
+    tk = np.array([[r[2] for r in rows]], np.int32)
+    return sc, pp, tk
+
+
+def test_beam_step_worked_scores():
+    g = load("beam.txt")
+    s = np.array([g["survivor_scores_milli"]], np.float32) / 1000
+    p = (np.array(g["child_p_milli"], np.float32) / 1000).reshape(1, 2, 2)
+    pool = {"scores": np.zeros((1, 6), np.float32), "parents": np.zeros((1, 6), np.int32),
+            "tokens": np.zeros((1, 6), np.int32)}
+    ns, ni = oracle.beam_step(s, np.array([[0, 1]], np.int32), p,
+                              np.array([[[10, 11], [12, 13]]], np.int32), pool, 2)
+    np.testing.assert_allclose(pool["scores"][0, 2:], np.array(g["path_scores_milli"]) / 1000,
+                               rtol=1e-6)
+    assert pool["parents"][0, 2:].tolist() == [0, 0, 1, 1]
+    assert pool["tokens"][0, 2:].tolist() == [10, 11, 12, 13]
+    assert ni[0].tolist() == [2, 4]                     # C (0.42), then D (0.32)
+    np.testing.assert_allclose(ns[0], [0.42, 0.32], rtol=1e-6)
+    # the products are fp32 products of the fp32 inputs
+    assert pool["scores"][0, 2] == np.float32(s[0, 0]) * np.float32(p[0, 0, 0])
+
+
+def test_beam_step_ties_and_nan_against_brute_force():
+    rng = np.random.default_rng(5)
+    for trial in range(100):
+        S, K = int(rng.integers(1, 5)), int(rng.integers(1, 9))
+        s = rng.choice([0.5, 0.25, 1.0, np.nan], size=(2, S)).astype(np.float32)
+        p = rng.choice([0.5, 0.25, 1.0, 0.125, np.nan], size=(2, S, K)).astype(np.float32)
+        C = 3 + S * K
+        pool = {"scores": np.zeros((2, C), np.float32), "parents": np.zeros((2, C), np.int32),
+                "tokens": np.zeros((2, C), np.int32)}
+        ns, ni = oracle.beam_step(s, np.tile(np.arange(S, dtype=np.int32), (2, 1)), p,
+                                  np.zeros((2, S, K), np.int32), pool, 3)
+        for b in range(2):
+            cs = (s[b][:, None] * p[b]).ravel()
+            key = lambda f: (1, 0.0, f) if np.isnan(cs[f]) else (0, -float(cs[f]), f)
+            want = sorted(range(S * K), key=key)[:K]
+            assert ni[b].tolist() == [3 + f for f in want]
+
+
+def _brute_select(sc, pp, N):
+    key = lambda c: (1, 0.0, c) if np.isnan(sc[c]) else (0, -float(sc[c]), c)
+    return sorted(sorted(range(len(sc)), key=key)[:N - 1])
+
+
+def test_select_candidates_closure_snippet():
+    """[MEM]'s tiny reference: parents [-1, 0, 1, 0], scores [1, .5, .5, .4];
+    the two best non-root nodes are 1 and 2 (the tie goes to the parent's
+    lower id), the set is closed, and node 2 sees root, 1 and itself."""
+    g = load("closure.txt")
+    sc, pp, tk = _pool([(0.5, -1, 7), (0.5, 0, 8), (0.4, -1, 9)])   # pool ids = nodes 1..3
+    r = oracle.select_candidates(sc, pp, tk, np.array([3]), N=3)
+    assert r["tree_error"][0] == 0
+    assert r["selected"][0].tolist() == [-1, 0, 1]
+    assert r["parents"][0].tolist() == [-1, 0, 1]
+    assert r["tokens"][0].tolist() == [3, 7, 8]
+    m = oracle.build_masks(r["parents"])["masks"][0]
+    assert [(int(m[2]) >> j) & 1 for j in range(3)] == [1, 1, 1]
+    assert g  # the fixture of the same snippet is present
+
+
+def test_select_candidates_against_brute_force():
+    rng = np.random.default_rng(9)
+    for trial in range(300):
+        C = int(rng.integers(1, 90))
+        N = int(rng.integers(1, min(C + 1, 64) + 1))
+        # a pool whose scores never exceed the parent's (the drafter's rule),
+        # with many exact ties
+        pp = np.array([-1 if c == 0 or rng.random() < 0.3 else int(rng.integers(0, c))
+                       for c in range(C)], np.int32)
+        sc = np.empty(C, np.float32)
+        for c in range(C):
+            q = np.float32(rng.choice([1.0, 0.5, 0.75, 0.25]))
+            sc[c] = q if pp[c] < 0 else sc[pp[c]] * q
+        tk = rng.integers(0, 1000, C).astype(np.int32)
+        for order in (0, 1):
+            r = oracle.select_candidates(sc[None], pp[None], tk[None], np.array([5]), N, order)
+            assert r["tree_error"][0] == 0
+            want = _brute_select(sc, pp, N)
+            sel = r["selected"][0]
+            assert sel[0] == -1 and sorted(sel[1:].tolist()) == want
+            par = r["parents"][0]
+            assert all(0 <= par[i] < i for i in range(1, N))        # a valid ABI tree
+            for i in range(1, N):                                     # topology kept
+                c, pc = sel[i], pp[sel[i]]
+                assert (par[i] == 0) if pc == -1 else (sel[par[i]] == pc)
+                assert r["tokens"][0, i] == tk[c]
+            if order == 0:
+                assert sel[1:].tolist() == want                       # pool order
+
+
+def test_depth_first_best_child_first_numbering():
+    """[DTS]: depth first, each node's best child first, so the most likely
+    path is 0, 1, 2, ...; every subtree occupies a contiguous block."""
+    rng = np.random.default_rng(10)
+    for trial in range(100):
+        C = int(rng.integers(8, 80))
+        pp = np.array([-1 if c < 3 else int(rng.integers(0, c)) for c in range(C)], np.int32)
+        sc = np.empty(C, np.float32)
+        for c in range(C):
+            q = np.float32(rng.random())
+            sc[c] = q if pp[c] < 0 else sc[pp[c]] * q
+        N = int(rng.integers(2, min(C, 63) + 2))
+        r = oracle.select_candidates(sc[None], pp[None], np.zeros((1, C), np.int32),
+                                     np.array([0]), N, order=1)
+        par, sel = r["parents"][0], r["selected"][0]
+        score = lambda i: np.inf if i == 0 else sc[sel[i]]
+        # greedy path of best children is 0, 1, 2, ...
+        u, k = 0, 0
+        while True:
+            kids = [j for j in range(N) if par[j] == u]
+            if not kids:
+                break
+            best = max(kids, key=lambda j: (score(j), -sel[j]))
+            k += 1
+            assert best == k
+            u = best
+        # preorder: a node's subtree is the block right after it
+        depth_first = [0]
+        for i in range(1, N):
+            assert par[i] < i
+        size = np.ones(N, int)
+        for i in range(N - 1, 0, -1):
+            size[par[i]] += size[i]
+        for i in range(N):
+            kids = [j for j in range(N) if par[j] == i]
+            nxt = i + 1
+            for j in sorted(kids):
+                assert j == nxt
+                nxt += size[j]
+
+
+def test_select_candidates_rejects_missing_parents():
+    # a child scored above its parent (against the drafter's rule) is kept
+    # without it: rejected, never treated as a root
+    sc, pp, tk = _pool([(0.5, -1, 1), (0.1, -1, 2), (0.3, 1, 3), (0.2, -1, 4)])
+    r = oracle.select_candidates(sc, pp, tk, np.array([0]), N=3)
+    assert r["tree_error"][0] == 1 + 2                  # node 2 (pool entry 2) lacks entry 1
+    assert (r["parents"][0] == -1).all()
+    # a parent after its child in the pool is rejected too
+    sc, pp, tk = _pool([(0.5, 1, 1), (0.6, -1, 2)])
+    assert oracle.select_candidates(sc, pp, tk, np.array([0]), N=3)["tree_error"][0] == 1 + 1
+
+
+def test_eagle_defaults_pool_and_tree_sizes():
+    """[MEM]: the SGLang Llama defaults (num_steps, topk, num_draft_tokens) =
+    (5, 4, 8) give a pool of 4 + 4 * 16 = 68 candidates, of which the best 7
+    plus the root are verified."""
+    rng = np.random.default_rng(2)
+    K, S, N = 4, 5, 8
+    C = K + (S - 1) * K * K
+    assert C == 68
+    pool = {"scores": np.zeros((1, C), np.float32), "parents": np.zeros((1, C), np.int32),
+            "tokens": np.zeros((1, C), np.int32)}
+    s, idx = np.ones((1, 1), np.float32), np.full((1, 1), -1, np.int32)
+    base = 0
+    for step in range(S):
+        n_s = s.shape[1]
+        p = rng.dirichlet(np.ones(K), size=(1, n_s)).astype(np.float32)
+        s, idx = oracle.beam_step(s, idx, p, rng.integers(0, 1000, (1, n_s, K)).astype(np.int32),
+                                  pool, base)
+        base += n_s * K
+    assert base == C
+    r = oracle.select_candidates(pool["scores"], pool["parents"], pool["tokens"], np.array([1]), N)
+    assert r["tree_error"][0] == 0 and (r["selected"][0, 1:] >= 0).all()
+    d = oracle.build_masks(r["parents"])["depth"][0]
+    assert d.max() <= S
