@@ -2,6 +2,8 @@
  * treeverify.h -- C ABI of the MI355X (gfx950) draft-tree verify path.
  *
  * One verify round of draft-tree speculative decoding on one GPU:
+ *   tree_beam_step, tree_select_candidates, tree_retrieve_links
+ *                        the tree from the drafter's candidate pool
  *   tree_build_masks     parents -> depth, 64-bit ancestor masks, positions
  *   tree_attention       paged prefix + masked tree window -> out, base-2 LSE
  *   verify_tree_greedy   draft tokens, target argmax -> accepted path
@@ -307,6 +309,65 @@ tav_status tree_sample_gumbel(const void *logits, tav_dtype dtype, int64_t row_s
                               int32_t B, int32_t N, const float *temperature,
                               const uint64_t *seed, const int32_t *positions, int32_t *tokens,
                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Tree construction, the step before the verify path.  Candidate order: the
+ * higher score first, the lower candidate id on equal scores, NaN after
+ * every number ([DTS] "Tree construction is deterministic").
+ *
+ * tree_beam_step: one EAGLE-2 expansion ([MEM] "EAGLE-2: the tree stops
+ * being a constant": the surviving paths' cumulative scores times the new
+ * conditional probabilities, the topk best paths kept; [ETA] "candidate pool
+ * to verify rows": cumulative path scores, e.g. 0.60 x 0.70 = 0.42).
+ *   scores     float [B][n_surv]: the survivors' cumulative scores (1 for
+ *              the root at the first step)
+ *   surv_idx   int32 [B][n_surv]: their pool indices (-1 for the root)
+ *   child_p    float [B][n_surv][K]: each survivor's children's conditional
+ *              probabilities; child_tok int32 [B][n_surv][K] their tokens
+ *   pool_*     [B][C] candidate pool; entries pool_base + s*K + j are written:
+ *              score scores[s] * child_p[s][j] (fp32 product), parent
+ *              surv_idx[s], token child_tok[s][j]
+ *   next_scores float [B][K], next_idx int32 [B][K] out: the K best children
+ *              (flat index s*K + j as the id), best first, as pool indices.
+ *              They may be the scores / surv_idx buffers (every input is read
+ *              before any output is written).
+ *   1 <= n_surv, K; n_surv * K <= 1024; pool_base + n_surv * K <= C
+ *
+ * tree_select_candidates: the verify tree from a request's pool ([MEM]
+ * organize_draft_results: the num_draft_token - 1 best of the flattened
+ * pool, sorted, tokens gathered, parent topology kept; [ETA] "the verify root
+ * is not an ordinary draft candidate": the previous bonus token is node 0).
+ *   pool_scores float [B][C], pool_parents int32 [B][C] (-1 = root; a parent
+ *              must precede its child), pool_tokens int32 [B][C]
+ *   root_tokens int32 [B]
+ *   order      0: nodes in pool order; 1: depth first, each node's best
+ *              child first ([DTS]: the most likely path is 0, 1, 2, ...)
+ *   parents, tokens int32 [B][N] out: the tree (parents[i] < i) and its
+ *              tokens; selected int32 [B][N] out: each node's pool index (-1
+ *              for the root)
+ *   tree_error int32 [B] or NULL out: 0, or 1 + the first node (pool order)
+ *              whose parent is not kept or does not precede it ([MEM]: a
+ *              missing parent is rejected, never treated as a root); that
+ *              request's outputs are then -1
+ *   1 <= N <= 64; max(1, N - 1) <= C <= 8192
+ *
+ * tree_retrieve_links: first-child / next-sibling arrays in node order
+ * ([MEM] "Flattening, and the two link arrays"; [DDT] compile_ddtree_retrieve)
+ *   parents int32 [B][N]; next_token, next_sibling int32 [B][N] out (-1 =
+ *   none).  1 <= N <= 64
+ */
+tav_status tree_beam_step(const float *scores, const int32_t *surv_idx, const float *child_p,
+                          const int32_t *child_tok, int32_t B, int32_t n_surv, int32_t K,
+                          int32_t C, int32_t pool_base, float *pool_scores,
+                          int32_t *pool_parents, int32_t *pool_tokens, float *next_scores,
+                          int32_t *next_idx, void *stream);
+tav_status tree_select_candidates(const float *pool_scores, const int32_t *pool_parents,
+                                  const int32_t *pool_tokens, const int32_t *root_tokens,
+                                  int32_t B, int32_t C, int32_t N, int32_t order,
+                                  int32_t *parents, int32_t *tokens, int32_t *selected,
+                                  int32_t *tree_error, void *stream);
+tav_status tree_retrieve_links(const int32_t *parents, int32_t B, int32_t N,
+                               int32_t *next_token, int32_t *next_sibling, void *stream);
 
 #ifdef __cplusplus
 }

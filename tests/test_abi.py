@@ -188,3 +188,36 @@ def test_sample_empty_batch_is_a_no_op(L):
     st, msg = sample_call(L, B=0, logits=None, T=None, seed=None, pos=None, tok=None, ws=None,
                           wsb=0)
     assert st == 0, msg
+
+
+@no_gpu
+def test_tree_construction_entry_points_reject(L):
+    # beam step: the pool range and the candidate limit
+    assert L.tree_beam_step(FAKE, FAKE, FAKE, FAKE, 2, 4, 4, 10, 0, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            None) == 1
+    assert "pool_base" in L.tav_last_error().decode()
+    assert L.tree_beam_step(FAKE, FAKE, FAKE, FAKE, 2, 64, 32, 5000, 0, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, None) == 2
+    assert "<= 1024" in L.tav_last_error().decode()
+    assert L.tree_beam_step(None, FAKE, FAKE, FAKE, 2, 4, 4, 100, 0, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            None) == 1
+    # selection: N, C and order
+    assert L.tree_select_candidates(FAKE, FAKE, FAKE, FAKE, 2, 100, 65, 0, FAKE, FAKE, FAKE, None,
+                                    None) == 1
+    assert "N must be in [1, 64]" in L.tav_last_error().decode()
+    assert L.tree_select_candidates(FAKE, FAKE, FAKE, FAKE, 2, 5, 8, 0, FAKE, FAKE, FAKE, None,
+                                    None) == 1
+    assert "C must be >=" in L.tav_last_error().decode()
+    assert L.tree_select_candidates(FAKE, FAKE, FAKE, FAKE, 2, 9000, 8, 0, FAKE, FAKE, FAKE, None,
+                                    None) == 2
+    assert L.tree_select_candidates(FAKE, FAKE, FAKE, FAKE, 2, 100, 8, 2, FAKE, FAKE, FAKE, None,
+                                    None) == 1
+    assert "order" in L.tav_last_error().decode()
+    assert L.tree_retrieve_links(FAKE, 2, 0, FAKE, FAKE, None) == 1
+    assert L.tree_retrieve_links(None, 2, 8, FAKE, FAKE, None) == 1
+    # empty batches launch nothing
+    assert L.tree_beam_step(None, None, None, None, 0, 4, 4, 100, 0, None, None, None, None, None,
+                            None) == 0
+    assert L.tree_select_candidates(None, None, None, None, 0, 100, 8, 1, None, None, None, None,
+                                    None) == 0
+    assert L.tree_retrieve_links(None, 0, 8, None, None, None) == 0

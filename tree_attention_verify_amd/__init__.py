@@ -10,7 +10,8 @@ another implementation.
 Entry points (same names as the C ABI):
   tree_build_masks, tree_shift_positions, tree_attention,
   tree_attention_workspace_size, verify_tree_greedy, compact_window_rows,
-  tree_sample_gumbel, tree_sample_workspace_size
+  tree_sample_gumbel, tree_sample_workspace_size, tree_beam_step,
+  tree_select_candidates, tree_retrieve_links
 plus verify_tree_sampled (tree_sample_gumbel, then verify_tree_greedy over
 the draws).
 """
@@ -34,7 +35,8 @@ _STATUS = {0: "TAV_OK", 1: "TAV_ERR_INVALID_ARG", 2: "TAV_ERR_UNSUPPORTED",
 EXPORTS = ("tav_last_error", "tav_version", "tree_build_masks", "tree_shift_positions",
            "tree_attention_workspace_size", "tree_attention", "tree_attention_prefix",
            "tree_attention_window_merge", "verify_tree_greedy", "compact_window_rows",
-           "tree_sample_workspace_size", "tree_sample_gumbel")
+           "tree_sample_workspace_size", "tree_sample_gumbel", "tree_beam_step",
+           "tree_select_candidates", "tree_retrieve_links")
 
 
 class TavError(RuntimeError):
@@ -93,8 +95,12 @@ def lib() -> ctypes.CDLL:
         L.tree_sample_workspace_size.restype = ctypes.c_size_t
         L.tree_sample_gumbel.argtypes = [P, ctypes.c_int, I64, I32, I32, I32, P, P, P, P, P,
                                          ctypes.c_size_t, P]
+        L.tree_beam_step.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P]
+        L.tree_select_candidates.argtypes = [P, P, P, P, I32, I32, I32, I32, P, P, P, P, P]
+        L.tree_retrieve_links.argtypes = [P, I32, I32, P, P, P]
         for f in ("tree_build_masks", "tree_shift_positions", "tree_attention",
-                  "verify_tree_greedy", "compact_window_rows", "tree_sample_gumbel"):
+                  "verify_tree_greedy", "compact_window_rows", "tree_sample_gumbel",
+                  "tree_beam_step", "tree_select_candidates", "tree_retrieve_links"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -303,6 +309,62 @@ def verify_tree_sampled(draft_tokens: torch.Tensor, logits: torch.Tensor,
     r = verify_tree_greedy(draft_tokens, draws, parents)
     r["draws"] = draws
     return r
+
+
+def tree_beam_step(scores: torch.Tensor, surv_idx: torch.Tensor, child_p: torch.Tensor,
+                   child_tok: torch.Tensor, pool_scores: torch.Tensor, pool_parents: torch.Tensor,
+                   pool_tokens: torch.Tensor, pool_base: int):
+    """One EAGLE-2 expansion: writes the step's pool entries in place and
+    returns (next_scores float32 [B][K], next_idx int32 [B][K])."""
+    _need(child_p, "child_p", torch.float32)
+    B, S, K = child_p.shape
+    dev = child_p.device
+    _need(scores, "scores", torch.float32, dev, (B, S))
+    _need(surv_idx, "surv_idx", torch.int32, dev, (B, S))
+    _need(child_tok, "child_tok", torch.int32, dev, (B, S, K))
+    _need(pool_scores, "pool_scores", torch.float32, dev)
+    C = pool_scores.shape[1]
+    _need(pool_parents, "pool_parents", torch.int32, dev, (B, C))
+    _need(pool_tokens, "pool_tokens", torch.int32, dev, (B, C))
+    ns = torch.empty((B, K), dtype=torch.float32, device=dev)
+    ni = torch.empty((B, K), dtype=torch.int32, device=dev)
+    _check(lib().tree_beam_step(_ptr(scores), _ptr(surv_idx), _ptr(child_p), _ptr(child_tok), B, S,
+                                K, C, int(pool_base), _ptr(pool_scores), _ptr(pool_parents),
+                                _ptr(pool_tokens), _ptr(ns), _ptr(ni), _stream(dev)))
+    return ns, ni
+
+
+def tree_select_candidates(pool_scores: torch.Tensor, pool_parents: torch.Tensor,
+                           pool_tokens: torch.Tensor, root_tokens: torch.Tensor, N: int,
+                           order: int = 0):
+    """The verify tree from the candidate pool.  -> dict(parents, tokens,
+    selected int32 [B][N], tree_error int32 [B])."""
+    _need(pool_scores, "pool_scores", torch.float32)
+    B, C = pool_scores.shape
+    dev = pool_scores.device
+    _need(pool_parents, "pool_parents", torch.int32, dev, (B, C))
+    _need(pool_tokens, "pool_tokens", torch.int32, dev, (B, C))
+    _need(root_tokens, "root_tokens", torch.int32, dev, (B,))
+    out = {k: torch.empty((B, N), dtype=torch.int32, device=dev)
+           for k in ("parents", "tokens", "selected")}
+    out["tree_error"] = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(lib().tree_select_candidates(_ptr(pool_scores), _ptr(pool_parents), _ptr(pool_tokens),
+                                        _ptr(root_tokens), B, C, int(N), int(order),
+                                        _ptr(out["parents"]), _ptr(out["tokens"]),
+                                        _ptr(out["selected"]), _ptr(out["tree_error"]),
+                                        _stream(dev)))
+    return out
+
+
+def tree_retrieve_links(parents: torch.Tensor):
+    """-> (next_token, next_sibling) int32 [B][N]."""
+    _need(parents, "parents", torch.int32)
+    B, N = parents.shape
+    dev = parents.device
+    nt = torch.empty((B, N), dtype=torch.int32, device=dev)
+    ns = torch.empty((B, N), dtype=torch.int32, device=dev)
+    _check(lib().tree_retrieve_links(_ptr(parents), B, N, _ptr(nt), _ptr(ns), _stream(dev)))
+    return nt, ns
 
 
 @dataclasses.dataclass
