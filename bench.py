@@ -367,6 +367,67 @@ def run_sampled(args):
     print(json.dumps(res), flush=True)
 
 
+def run_tree_build(args):
+    """Tree construction on the EAGLE-style verify shape (32 requests, top-8
+    beam over 6 expansion steps into a 328-candidate pool, N = 64): one step
+    is the six tree_beam_step launches, tree_select_candidates (depth-first
+    numbering) and tree_retrieve_links.  Latency-bound; reported in us."""
+    L = tav.lib()
+    B, K, S, N = 32, 8, 6, 64
+    C = K + (S - 1) * K * K
+    rng = np.random.default_rng(args.seed)
+    t = lambda x, dt=torch.int32: torch.as_tensor(np.ascontiguousarray(x)).to(dt).to("cuda")
+    steps = []
+    for i in range(S):
+        n_s = 1 if i == 0 else K
+        steps.append((t(rng.dirichlet(np.ones(K), size=(B, n_s)).astype(np.float32), torch.float32),
+                      t(rng.integers(0, gen.SAMPLE_VOCAB, size=(B, n_s, K)).astype(np.int32)), n_s))
+    ps = torch.zeros((B, C), dtype=torch.float32, device="cuda")
+    pp = torch.zeros((B, C), dtype=torch.int32, device="cuda")
+    pt = torch.zeros((B, C), dtype=torch.int32, device="cuda")
+    sc = torch.ones((B, K), dtype=torch.float32, device="cuda")
+    si = torch.full((B, K), -1, dtype=torch.int32, device="cuda")
+    roots = t(np.arange(B, dtype=np.int32))
+    par = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    tok, sel, err = torch.empty_like(par), torch.empty_like(par), torch.empty((B,), dtype=torch.int32, device="cuda")
+    nt, nsb = torch.empty_like(par), torch.empty_like(par)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        sc.fill_(1.0)
+        si.fill_(-1)
+        base = 0
+        for p, tk, n_s in steps:
+            assert L.tree_beam_step(sc.data_ptr(), si.data_ptr(), p.data_ptr(), tk.data_ptr(), B, n_s,
+                                    K, C, base, ps.data_ptr(), pp.data_ptr(), pt.data_ptr(),
+                                    sc.data_ptr(), si.data_ptr(), stream) == 0
+            base += n_s * K
+        assert L.tree_select_candidates(ps.data_ptr(), pp.data_ptr(), pt.data_ptr(), roots.data_ptr(),
+                                        B, C, N, 1, par.data_ptr(), tok.data_ptr(), sel.data_ptr(),
+                                        err.data_ptr(), stream) == 0
+        assert L.tree_retrieve_links(par.data_ptr(), B, N, nt.data_ptr(), nsb.data_ptr(), stream) == 0
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        run()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    assert int(err.max()) == 0
+    print(json.dumps({"metric": "tree construction latency (EAGLE top-8 x 6 steps, N 64)",
+                      "value": round(ms * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": args.steps,
+                      "warmup": args.warmup, "ms_per_step": round(ms, 4),
+                      "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+                      "dtype": "f32", "data": "synthetic",
+                      "config": {"workload": "tree construction: B 32, topk 8, 6 steps, pool %d, "
+                                             "N 64, depth-first numbering" % C},
+                      "trees_per_s": round(B / (ms * 1e-3), 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -383,6 +444,8 @@ def main():
     ap.add_argument("--sampled", action="store_true",
                     help="time the sampled verify (Gumbel-max draws over a 128256-token "
                          "vocabulary, then the greedy walk) instead of the attention step")
+    ap.add_argument("--tree-build", action="store_true",
+                    help="time tree construction (beam steps, selection, links) instead")
     ap.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
                     help="after the timed steps, run steps back to back for SECONDS (for board "
                          "power and clock readings taken meanwhile) and report their rate")
@@ -404,6 +467,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.sampled:
         run_sampled(args)
+        return
+    if args.tree_build:
+        run_tree_build(args)
         return
     wl = gen.WORKLOADS[args.workload]
     log("workload", wl)

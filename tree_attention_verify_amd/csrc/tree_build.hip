@@ -28,16 +28,49 @@
 namespace {
 
 constexpr int kBuildThreads = 256;
+constexpr int kSelectThreads = 1024;    // the rank phase of the selection
 constexpr int kMaxBeamCands = 1024;     // n_surv * K per step
 constexpr int kMaxPool = 8192;          // candidates per request
 
+// Lane j's value in every lane (j wave-uniform): v_readlane, no LDS trip.
+__device__ inline int lane_val(int x, int j) { return __builtin_amdgcn_readlane(x, j); }
+__device__ inline float lane_val(float x, int j) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
+}
+__device__ inline uint64_t lane_val(uint64_t x, int j) {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(x >> 32), j) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, j);
+}
+
+// The candidate order as integers: a key that increases with the score
+// (equal for -0 and +0, the lowest for NaN), then the lower id first.
+__device__ inline int order_key(float s) {
+    s = s + 0.0f;                         // -0 -> +0
+    const int i = __float_as_int(s);
+    const int k = i >= 0 ? i : (i ^ 0x7fffffff);
+    return s != s ? INT_MIN : k;
+}
+__device__ inline bool before_k(int ka, int a, int kb, int b) {
+    return ka > kb || (ka == kb && a < b);
+}
 __device__ inline bool before(float sa, int a, float sb, int b) {
-    const bool na = sa != sa, nb = sb != sb;
-    if (na != nb)
-        return nb;
-    if (!na && sa != sb)
-        return sa > sb;
-    return a < b;
+    return before_k(order_key(sa), a, order_key(sb), b);
+}
+
+// Rank of candidate (z, id) in an LDS array of n scores: how many come
+// before it, counted up to `limit` (the count may pass it by up to 7).  The
+// scan goes 8 entries per check of the limit, so the LDS reads (the same
+// address in every lane: broadcasts) are issued back to back.
+__device__ inline int rank_in(const int *key, int n, int kz, int id, int limit) {
+    int rank = 0, g = 0;
+    for (; g + 8 <= n && rank < limit; g += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            rank += before_k(key[g + u], g + u, kz, id) ? 1 : 0;
+    }
+    for (; g < n && rank < limit; ++g)
+        rank += before_k(key[g], g, kz, id) ? 1 : 0;
+    return rank;
 }
 
 __global__ void __launch_bounds__(kBuildThreads)
@@ -47,6 +80,7 @@ k_beam_step(const float *__restrict__ scores, const int32_t *__restrict__ surv_i
             int32_t *__restrict__ pool_parents, int32_t *__restrict__ pool_tokens,
             float *next_scores, int32_t *next_idx) {
     __shared__ float cs[kMaxBeamCands];
+    __shared__ int ck[kMaxBeamCands];
     const int b = blockIdx.x;
     const int n = n_surv * K;
     // every input is read before any output is written (the survivor arrays
@@ -55,6 +89,7 @@ k_beam_step(const float *__restrict__ scores, const int32_t *__restrict__ surv_i
     for (int f = threadIdx.x, k = 0; f < n; f += kBuildThreads, ++k) {
         const int s = f / K;
         cs[f] = scores[(int64_t)b * n_surv + s] * child_p[(int64_t)b * n + f];
+        ck[f] = order_key(cs[f]);
         par_of[k] = surv_idx[(int64_t)b * n_surv + s];
     }
     __syncthreads();
@@ -63,9 +98,7 @@ k_beam_step(const float *__restrict__ scores, const int32_t *__restrict__ surv_i
         pool_scores[(int64_t)b * C + pool_base + f] = z;
         pool_parents[(int64_t)b * C + pool_base + f] = par_of[k];
         pool_tokens[(int64_t)b * C + pool_base + f] = child_tok[(int64_t)b * n + f];
-        int rank = 0;
-        for (int g = 0; g < n && rank < K; ++g)
-            rank += before(cs[g], g, z, f) ? 1 : 0;
+        const int rank = rank_in(ck, n, ck[f], f, K);
         if (rank < K) {
             next_scores[(int64_t)b * K + rank] = z;
             next_idx[(int64_t)b * K + rank] = pool_base + f;
@@ -78,24 +111,28 @@ k_beam_step(const float *__restrict__ scores, const int32_t *__restrict__ surv_i
 // (wave 0, lane = node) orders them, links parents, checks closure and, for
 // the depth-first numbering, computes each node's preorder index from its
 // ancestor mask and its better siblings' subtree sizes.
-__global__ void __launch_bounds__(kBuildThreads)
+__global__ void __launch_bounds__(kSelectThreads)
 k_select_tree(const float *__restrict__ pool_scores, const int32_t *__restrict__ pool_parents,
               const int32_t *__restrict__ pool_tokens, const int32_t *__restrict__ root_tokens,
               int C, int N, int order, int32_t *__restrict__ parents, int32_t *__restrict__ tokens,
               int32_t *__restrict__ selected, int32_t *__restrict__ tree_error) {
-    __shared__ float sc[kMaxPool];
+    __shared__ int sk[kMaxPool];
+    __shared__ int32_t spar[kMaxPool];
+    __shared__ int32_t stok[kMaxPool];
     __shared__ int32_t kept[64];
     const int b = blockIdx.x;
     const float *ps = pool_scores + (int64_t)b * C;
-    for (int c = threadIdx.x; c < C; c += kBuildThreads)
-        sc[c] = ps[c];
+    // the whole pool is staged in LDS with coalesced loads, so the per-node
+    // steps below read no global memory
+    for (int c = threadIdx.x; c < C; c += kSelectThreads) {
+        sk[c] = order_key(ps[c]);
+        spar[c] = pool_parents[(int64_t)b * C + c];
+        stok[c] = pool_tokens[(int64_t)b * C + c];
+    }
     __syncthreads();
     const int M = N - 1;
-    for (int c = threadIdx.x; c < C; c += kBuildThreads) {
-        const float z = sc[c];
-        int rank = 0;
-        for (int g = 0; g < C && rank < M; ++g)
-            rank += before(sc[g], g, z, c) ? 1 : 0;
+    for (int c = threadIdx.x; c < C; c += kSelectThreads) {
+        const int rank = rank_in(sk, C, sk[c], c, M);
         if (rank < M)
             kept[rank] = c;
     }
@@ -121,20 +158,14 @@ k_select_tree(const float *__restrict__ pool_scores, const int32_t *__restrict__
         return;
     // lane i now takes pool-order node i
     const int ci = in ? cand_of[lane] : -1;
-    int pn = -1;
-    bool bad = false;
-    if (in && lane >= 1) {
-        const int p = pool_parents[(int64_t)b * C + ci];
-        if (p == -1) {
-            pn = 0;
-        } else {
-            bad = p < 0 || p >= ci;
-            for (int j = 1; j < N && !bad && pn < 0; ++j)
-                if (cand_of[j] == p)
-                    pn = j;
-            bad = bad || pn < 0;
-        }
+    const int p0 = (in && lane >= 1) ? spar[ci] : -1;
+    int pn = p0 == -1 ? 0 : -1;
+    for (int j = 1; j < N; ++j) {
+        const int cj = lane_val(ci, j);
+        pn = (p0 >= 0 && cj == p0) ? j : pn;
     }
+    const bool bad = in && lane >= 1 && (p0 < -1 || p0 >= ci || pn < 0);
+    pn = (in && lane >= 1) ? pn : -1;
     const uint64_t badm = __ballot(bad);
     int32_t *par = parents + (int64_t)b * N, *tok = tokens + (int64_t)b * N;
     int32_t *sel = selected + (int64_t)b * N;
@@ -147,7 +178,7 @@ k_select_tree(const float *__restrict__ pool_scores, const int32_t *__restrict__
     }
     if (lane == 0 && tree_error)
         tree_error[b] = 0;
-    const int my_tok = !in ? 0 : (lane == 0 ? root_tokens[b] : pool_tokens[(int64_t)b * C + ci]);
+    const int my_tok = !in ? 0 : (lane == 0 ? root_tokens[b] : stok[ci]);
     if (order == 0) {
         if (in) {
             par[lane] = lane == 0 ? -1 : pn;
@@ -171,26 +202,22 @@ k_select_tree(const float *__restrict__ pool_scores, const int32_t *__restrict__
     }
     // subtree sizes: how many nodes have this one among their ancestors
     int size = 0;
-    for (int j = 0; j < N; ++j) {
-        const uint32_t lo = __shfl((uint32_t)acc, j), hi = __shfl((uint32_t)(acc >> 32), j);
-        const uint64_t mj = ((uint64_t)hi << 32) | lo;
-        size += (int)((mj >> lane) & 1);
-    }
+    for (int j = 0; j < N; ++j)
+        size += (int)((lane_val(acc, j) >> lane) & 1);
     // offset within the parent's block: 1 + the sizes of the better siblings
-    const float my_sc = (in && lane >= 1) ? sc[ci] : 0.f;
+    const int my_k = (in && lane >= 1) ? sk[ci] : 0;
     int offset = 1;
     for (int j = 1; j < N; ++j) {
-        const int pj = __shfl(pn, j);
-        const int cj = __shfl(ci, j);
-        const float sj = __shfl(my_sc, j);
-        const int szj = __shfl(size, j);
-        if (in && lane >= 1 && j != lane && pj == pn && before(sj, cj, my_sc, ci))
-            offset += szj;
+        const int pj = lane_val(pn, j);
+        const int cj = lane_val(ci, j);
+        const int kj = lane_val(my_k, j);
+        const int szj = lane_val(size, j);
+        offset += (in && lane >= 1 && j != lane && pj == pn && before_k(kj, cj, my_k, ci)) ? szj : 0;
     }
     // preorder index: the offsets of the node and its ancestors (root 0)
     int pre = 0;
     for (int j = 1; j < N; ++j) {
-        const int oj = __shfl(offset, j);
+        const int oj = lane_val(offset, j);
         if ((acc >> j) & 1)
             pre += oj;
     }
@@ -218,11 +245,11 @@ k_retrieve_links(const int32_t *__restrict__ parents, int B, int N, int32_t *__r
         if (lane == i && m)
             nt = __ffsll((unsigned long long)m) - 1;
     }
+    // next sibling: the lowest later lane with the same parent
     int ns = -1;
-    for (int j = 0; j < N; ++j) {
-        const int pj = __shfl(par, j);
-        if (in && j > lane && ns < 0 && pj == par && par >= 0)
-            ns = j;
+    for (int j = N - 1; j >= 1; --j) {
+        const int pj = lane_val(par, j);
+        ns = (in && j > lane && pj == par && par >= 0) ? j : ns;
     }
     if (in) {
         next_token[(int64_t)b * N + lane] = nt;
@@ -289,7 +316,7 @@ extern "C" tav_status tree_select_candidates(const float *pool_scores, const int
     }
     if (c.status != TAV_OK || B == 0)
         return tav::finish("tree_select_candidates", c);
-    hipLaunchKernelGGL(k_select_tree, dim3((unsigned)B), dim3(kBuildThreads), 0, S(stream),
+    hipLaunchKernelGGL(k_select_tree, dim3((unsigned)B), dim3(kSelectThreads), 0, S(stream),
                        pool_scores, pool_parents, pool_tokens, root_tokens, C, N, order, parents,
                        tokens, selected, tree_error);
     return tav::launched("tree_select_candidates");
