@@ -75,6 +75,9 @@ def lib():
         L.orc_select_candidates.restype = ctypes.c_int
         L.orc_retrieve_links.argtypes = [P, I, I, P, P]
         L.orc_retrieve_links.restype = ctypes.c_int
+        L.orc_mla_attention.argtypes = [P, P, I, I64, I64, P, I, I, P, P, I, I, I, I, I, I, D,
+                                        P, I64, P, P]
+        L.orc_mla_attention.restype = ctypes.c_int
         L.orc_tree_attention.argtypes = [P, P, P, I, I, I64, I64, I64, P, I, I, P, I,
                                          P, I, I, I, I, I, I, D, P, I64, P, P]
         L.orc_causal_attention.argtypes = [P, P, P, I, I, I, I, I, I, D, P, P]
@@ -355,3 +358,39 @@ def retrieve_links(parents):
     nsb = np.empty((B, N), np.int32)
     _check(lib().orc_retrieve_links(_p(par), B, N, _p(nt), _p(nsb)), "retrieve_links")
     return nt, nsb
+
+
+def mla_attention(q, latent, strides, page_table, page_size, prefix_len, masks, W, Dc, Dr,
+                  sm_scale=0.0, rows=None):
+    """fp64 tree attention over an MLA latent cache.
+
+    q: [B][R][Hq][Dc + Dr] float32 or uint16 (bf16 bits); latent: a flat
+    pool of the same dtype with (page, token) strides in elements, Dc + Dr
+    contiguous channels per token (latent part, then rotary part).  Returns
+    (out float64 [B][R][Hq][Dc], lse2 float64 [B][R][Hq]) or, for a rows
+    list, ([n][Dc], [n])."""
+    q = np.ascontiguousarray(q)
+    dt = _dtype_code(q)
+    latent = np.ascontiguousarray(latent)
+    assert _dtype_code(latent) == dt and dt in (0, 1)
+    B, R, Hq, Dk = q.shape
+    assert Dk == Dc + Dr
+    page_table = _c(page_table, np.int32)
+    prefix_len = _c(prefix_len, np.int32)
+    masks = _c(masks, np.uint64)
+    if rows is None:
+        out = np.empty((B, R, Hq, Dc), np.float64)
+        lse = np.empty((B, R, Hq), np.float64)
+        rp, nr = None, 0
+    else:
+        rows = _c(rows, np.int64)
+        out = np.empty((rows.size, Dc), np.float64)
+        lse = np.empty((rows.size,), np.float64)
+        rp, nr = rows, rows.size
+    sp, st = (int(x) for x in strides)
+    _check(lib().orc_mla_attention(_p(q), _p(latent), dt, sp, st, _p(page_table),
+                                   page_table.shape[1], int(page_size), _p(prefix_len),
+                                   _p(masks), int(W), B, R, Hq, int(Dc), int(Dr),
+                                   float(sm_scale), _p(rp), nr, _p(out), _p(lse)),
+           "mla_attention")
+    return out, lse

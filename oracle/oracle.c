@@ -858,3 +858,99 @@ int orc_retrieve_links(const int32_t *parents, int B, int N, int32_t *next_token
     }
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* MLA: the same cascade over a latent cache                            */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Tree attention over an MLA latent cache ([DTS] "One tree attention ...":
+ * MLA runs the same cascade over its latent cache; a token's latent row is
+ * read once, its kv_lora_rank (Dc) leading channels are both the key's
+ * latent part and the value, and the rotary channels after them (Dr, zero
+ * for GQA) add a second score product).  Every query head reads the one
+ * latent row of a token:
+ *   s_t = scale * (sum_{d < Dc} q[d] c_t[d] + sum_{d < Dr} q[Dc + d] r_t[d]),
+ *   o = sum_t softmax(s)_t c_t  (Dc channels),  lse2 = base-2 log-sum-exp,
+ * over the visible keys of the row: the committed prefix [0, P) and window
+ * node j at logical position P + j for the set bits j < W of the row's mask
+ * (the same visibility as orc_tree_attention).  The latent row of logical
+ * position t is at page_table[b][t / ps] * stride_page + (t % ps) *
+ * stride_token, Dc + Dr contiguous elements.  q is [B][R][Hq][Dc + Dr]
+ * (dtype, bf16 or fp32, as the latent cache), out [B][R][Hq][Dc] fp64, lse2
+ * [B][R][Hq]; or n_rows listed rows ((b*R + r)*Hq + h).  sm_scale <= 0
+ * means 1/sqrt(Dc + Dr).
+ */
+int orc_mla_attention(const void *q, const void *latent, int dtype, int64_t stride_page,
+                      int64_t stride_token, const int32_t *page_table, int max_pages,
+                      int page_size, const int32_t *prefix_len, const uint64_t *masks, int W,
+                      int B, int R, int Hq, int Dc, int Dr, double sm_scale,
+                      const int64_t *rows, int64_t n_rows, double *out, double *lse2)
+{
+    if (W < 0 || W > 64 || page_size <= 0 || Dc < 1 || Dr < 0 || (dtype != 0 && dtype != 1))
+        return ORC_BAD;
+    const int Dk = Dc + Dr;
+    if (sm_scale <= 0.0)
+        sm_scale = 1.0 / sqrt((double)Dk);
+    int64_t total = rows ? n_rows : (int64_t)B * R * Hq;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t n = 0; n < total; ++n) {
+        int64_t id = rows ? rows[n] : n;
+        int r = (int)((id / Hq) % R);
+        int b = (int)(id / ((int64_t)Hq * R));
+        int P = prefix_len[b];
+        uint64_t m = masks[(int64_t)b * R + r];
+        int nk_max = P + W;
+        int64_t *kofs = (int64_t *)malloc(sizeof(int64_t) * (nk_max > 0 ? nk_max : 1));
+        double *s = (double *)malloc(sizeof(double) * (nk_max > 0 ? nk_max : 1));
+        double *qv = (double *)malloc(sizeof(double) * Dk);
+        int nk = 0;
+        for (int t = 0; t < P + W; ++t) {
+            if (t >= P && !((m >> (t - P)) & 1))
+                continue;
+            int lp = t / page_size;
+            if (lp >= max_pages) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            int64_t page = page_table[(int64_t)b * max_pages + lp];
+            kofs[nk++] = page * stride_page + (int64_t)(t % page_size) * stride_token;
+        }
+        for (int d = 0; d < Dk; ++d)
+            qv[d] = orc_load(q, dtype, id * Dk + d);
+        double *o = out + n * Dc;
+        for (int d = 0; d < Dc; ++d)
+            o[d] = 0.0;
+        if (nk == 0) {
+            lse2[n] = -INFINITY;
+        } else {
+            double mx = -INFINITY;
+            for (int t = 0; t < nk; ++t) {
+                double acc = 0.0;
+                for (int d = 0; d < Dc; ++d)          /* latent part */
+                    acc += qv[d] * orc_load(latent, dtype, kofs[t] + d);
+                for (int d = 0; d < Dr; ++d)          /* rotary part */
+                    acc += qv[Dc + d] * orc_load(latent, dtype, kofs[t] + Dc + d);
+                s[t] = sm_scale * acc;
+                if (s[t] > mx)
+                    mx = s[t];
+            }
+            double Z = 0.0;
+            for (int t = 0; t < nk; ++t) {
+                double w = exp(s[t] - mx);
+                Z += w;
+                for (int d = 0; d < Dc; ++d)          /* the value is the latent part */
+                    o[d] += w * orc_load(latent, dtype, kofs[t] + d);
+            }
+            for (int d = 0; d < Dc; ++d)
+                o[d] /= Z;
+            lse2[n] = (mx + log(Z)) / log(2.0);
+        }
+        free(kofs);
+        free(s);
+        free(qv);
+    }
+    return bad ? ORC_BAD : ORC_OK;
+}

@@ -6,6 +6,7 @@ force enumeration, an independent characterisation (boolean reachability),
 or a library routine (torch scaled_dot_product_attention in fp64 on the CPU
 with an explicit dense mask).  CPU only.
 """
+import dataclasses
 import itertools
 import math
 
@@ -1000,3 +1001,82 @@ def test_eagle_defaults_pool_and_tree_sizes():
     assert r["tree_error"][0] == 0 and (r["selected"][0, 1:] >= 0).all()
     d = oracle.build_masks(r["parents"])["depth"][0]
     assert d.max() <= S
+
+
+# ---------------------------------------------------------------------------
+# MLA latent cascade
+# ---------------------------------------------------------------------------
+
+def mla_small(seed=3, **kw):
+    wl = gen.MlaWorkload("t", 2, 45, 10, 4, 32, 8, 8, depth_cap=4).with_(**kw)
+    inp = gen.make_mla_inputs(wl, seed, "cpu", prefix_lens=np.array([45, 13])[:wl.B])
+    m = oracle.build_masks(inp.parents)["masks"]
+    return wl, inp, m
+
+
+def mla_oracle(inp, m, **kw):
+    wl = inp.wl
+    return oracle.mla_attention(gen.bf16_bits(inp.q), gen.bf16_bits(inp.latent), inp.strides,
+                                inp.page_table, wl.page_size, inp.prefix_len, m, wl.W, wl.Dc,
+                                wl.Dr, **kw)
+
+
+def test_mla_matches_sdpa():
+    """fp64 SDPA with the key = the whole latent row (Dc + Dr channels) and
+    the value = its Dc leading channels, one latent row shared by all heads."""
+    wl, inp, m = mla_small()
+    o, l = mla_oracle(inp, m)
+    lat = inp.latent.double()
+    pt = torch.from_numpy(inp.page_table.astype(np.int64))
+    rows = lat[pt].reshape(wl.B, -1, wl.Dc + wl.Dr)            # [B][T][Dk] logical
+    T = rows.shape[1]
+    for b in range(wl.B):
+        P = int(inp.prefix_len[b])
+        dense = torch.zeros(wl.R, T, dtype=torch.bool)
+        dense[:, :P] = True
+        for r in range(wl.R):
+            for j in range(wl.W):
+                if (int(m[b, r]) >> j) & 1:
+                    dense[r, P + j] = True
+        seen = dense.any(0)[:, None]
+        k = torch.where(seen, rows[b], 0.0)
+        v = k[:, :wl.Dc]
+        q = inp.q[b].double().permute(1, 0, 2)                    # [Hq][R][Dk]
+        ro = torch.nn.functional.scaled_dot_product_attention(
+            q, k[None].expand(wl.Hq, -1, -1), v[None].expand(wl.Hq, -1, -1), attn_mask=dense[None])
+        s = (q @ k.T) / math.sqrt(wl.Dc + wl.Dr)
+        rl = torch.logsumexp(torch.where(dense[None], s, -math.inf), -1) * LOG2E
+        np.testing.assert_allclose(o[b], ro.permute(1, 0, 2).numpy(), atol=1e-12, rtol=0)
+        np.testing.assert_allclose(l[b], rl.permute(1, 0).numpy(), atol=1e-12, rtol=0)
+
+
+def test_mla_without_rotary_is_shared_kv_attention():
+    """Dr = 0: the latent row is both key and value of a single kv head, so
+    the result equals the plain tree attention with Hkv = 1 and D = Dc on a
+    cache whose K and V pools are the latent pool."""
+    wl, inp, m = mla_small(Dr=0)
+    o, l = mla_oracle(inp, m)
+    bits = gen.bf16_bits(inp.latent)
+    # the latent pool [pages][ps][Dc] is an HND K/V pool with one head
+    strides = (wl.page_size * wl.Dc, wl.page_size * wl.Dc, wl.Dc)
+    ro, rl = oracle.tree_attention(gen.bf16_bits(inp.q), bits, bits, strides, inp.page_table,
+                                   wl.page_size, inp.prefix_len, m, wl.W, 1)
+    assert np.array_equal(o, ro) and np.array_equal(l, rl)
+
+
+def test_mla_rotary_part_adds_a_score_product():
+    """Zeroing the query's rotary channels equals dropping the rotary part
+    (Dr = 0 on the latent channels alone, with the same scale)."""
+    wl, inp, m = mla_small()
+    q0 = inp.q.clone()
+    q0[..., wl.Dc:] = 0
+    inp0 = dataclasses.replace(inp, q=q0)
+    o, l = mla_oracle(inp0, m, sm_scale=1 / math.sqrt(wl.Dc + wl.Dr))
+    wl2 = wl.with_(Dr=0)
+    inp2 = dataclasses.replace(inp, wl=wl2, q=inp.q[..., :wl.Dc].contiguous(),
+                               latent=inp.latent[..., :wl.Dc].contiguous())
+    o2, l2 = mla_oracle(inp2, m, sm_scale=1 / math.sqrt(wl.Dc + wl.Dr))
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+    # and the rotary part does change the scores
+    o3, l3 = mla_oracle(inp, m)
+    assert np.abs(l3 - l).max() > 1e-3

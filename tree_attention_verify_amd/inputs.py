@@ -383,3 +383,94 @@ def make_sample_inputs(B: int, N: int, V: int, seed: int, dtype: str = "bf16",
     seeds = r.integers(0, 2 ** 63, size=B, dtype=np.int64).astype(np.uint64) * np.uint64(2) + \
         r.integers(0, 2, size=B).astype(np.uint64)
     return SampleInputs(buf[:, :, :V], temperature, seeds)
+
+
+# ---------------------------------------------------------------------------
+# MLA latent-cache inputs
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class MlaWorkload:
+    name: str
+    B: int
+    P: int
+    N: int
+    Hq: int
+    Dc: int          # kv_lora_rank: latent channels (the key's latent part and the value)
+    Dr: int          # rotary channels of the key
+    page_size: int
+    depth_cap: int = 6
+    dtype: str = "bf16"
+
+    @property
+    def W(self) -> int:
+        return self.N
+
+    @property
+    def R(self) -> int:
+        return self.N
+
+    def with_(self, **kw) -> "MlaWorkload":
+        return dataclasses.replace(self, **kw)
+
+    def describe(self) -> str:
+        return ("%s: B %d, P %d, N %d random trees (depth <= %d), Hq %d, latent %d + rotary %d, "
+                "%s, page size %d" % (self.name, self.B, self.P, self.N, self.depth_cap, self.Hq,
+                                      self.Dc, self.Dr, self.dtype, self.page_size))
+
+
+MLA_WORKLOADS = {
+    # one tensor-parallel share (16 of 128 heads) of a DeepSeek-style MLA layer
+    "mla16": MlaWorkload("mla16", 8, 8192, 16, 16, 512, 64, 64),
+    # every head of such a layer on one GPU
+    "mla128": MlaWorkload("mla128", 4, 32768, 16, 128, 512, 64, 64),
+}
+
+
+@dataclasses.dataclass
+class MlaInputs:
+    wl: MlaWorkload
+    parents: np.ndarray          # [B][N]
+    prefix_len: np.ndarray       # [B]
+    page_table: np.ndarray       # [B][max_pages]
+    q: torch.Tensor              # [B][N][Hq][Dc + Dr]
+    latent: torch.Tensor         # [pages][page_size][Dc + Dr]
+
+    @property
+    def strides(self):
+        """(page, token) strides in elements."""
+        return (self.wl.page_size * (self.wl.Dc + self.wl.Dr), self.wl.Dc + self.wl.Dr)
+
+
+def make_mla_inputs(wl: MlaWorkload, seed: int, device="cpu",
+                    prefix_lens: Optional[np.ndarray] = None) -> MlaInputs:
+    """Seeded MLA verify inputs: random trees, the absorbed query and the
+    latent cache N(0, 1) (rounded to bf16), a shuffled page table; page 0 and
+    every slot past prefix + window hold NaN."""
+    r_tree, _, r_pt, _ = _streams(seed + 7777, 4)
+    B, N = wl.B, wl.N
+    parents = np.stack([random_tree(r_tree, N, wl.depth_cap) for _ in range(B)]).astype(np.int32)
+    if prefix_lens is None:
+        prefix_lens = np.full(B, wl.P, np.int32)
+    prefix_lens = np.asarray(prefix_lens, np.int32)
+    ps = wl.page_size
+    max_pages = max(1, math.ceil((int(prefix_lens.max()) + wl.W) / ps))
+    n_pages = 1 + B * max_pages
+    page_table = (r_pt.permutation(n_pages - 1) + 1).astype(np.int32).reshape(B, max_pages)
+    dt = TORCH_DTYPE[wl.dtype]
+    dev = torch.device(device)
+    Dk = wl.Dc + wl.Dr
+    q = torch.empty((B, N, wl.Hq, Dk), dtype=dt, device=dev)
+    lat = torch.empty((n_pages, ps, Dk), dtype=dt, device=dev)
+    for k, t in enumerate((q, lat)):
+        g = torch.Generator(device=dev)
+        g.manual_seed(_torch_seed(seed + 7777, k))
+        _randn_into(t, g)
+    lat[0] = float("nan")
+    for b in range(B):
+        end = int(prefix_lens[b]) + wl.W
+        for lp in range(end // ps, max_pages):
+            first = max(0, end - lp * ps)
+            if first < ps:
+                lat[int(page_table[b, lp]), first:] = float("nan")
+    return MlaInputs(wl, parents, prefix_lens, page_table, q, lat)
