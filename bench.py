@@ -428,6 +428,83 @@ def run_tree_build(args):
                       "trees_per_s": round(B / (ms * 1e-3), 1)}), flush=True)
 
 
+def run_mla(args):
+    """The verify cascade over an MLA latent cache (tree_attention_mla: the
+    split-K prefix and the window + merge) on one of the MLA workloads."""
+    L = tav.lib()
+    wl = gen.MLA_WORKLOADS[args.mla]
+    log("workload", wl.describe())
+    inp = gen.make_mla_inputs(wl, args.seed, "cuda")
+    t = lambda x, dt=torch.int32: torch.as_tensor(np.ascontiguousarray(x)).to(dt).to("cuda")
+    parents = t(inp.parents)
+    m = tav.tree_build_masks(parents)
+    masks = m["masks"]
+    pt, pl = t(inp.page_table), t(inp.prefix_len)
+    Dk = wl.Dc + wl.Dr
+    ps = wl.page_size
+    nbytes = tav.tree_attention_mla_workspace_size(wl.B, wl.R, wl.Hq, wl.Dc, wl.Dr, wl.P, ps)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.B, wl.R, wl.Hq, wl.Dc), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((wl.B, wl.R, wl.Hq), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        assert L.tree_attention_mla(inp.q.data_ptr(), inp.latent.data_ptr(), tav.TAV_BF16, ps * Dk,
+                                    Dk, inp.latent.shape[0], pt.data_ptr(), pt.shape[1], ps,
+                                    pl.data_ptr(), wl.P, masks.data_ptr(), wl.W, wl.B, wl.R,
+                                    wl.Hq, wl.Dc, wl.Dr, 0.0, out.data_ptr(), lse.data_ptr(),
+                                    ws.data_ptr(), ws.numel(), stream) == 0, L.tav_last_error()
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        run()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    masks_np = masks.cpu().numpy().view(np.uint64)
+    pop = sum(bin(int(x)).count("1") for x in masks_np.reshape(-1))
+    per_key = 2 * Dk + 2 * wl.Dc
+    flops = per_key * wl.Hq * (wl.B * wl.R * wl.P + pop)
+    kvb = wl.B * (wl.P + wl.W) * Dk * 2
+    tfs = flops / (ms * 1e-3) / 1e12
+    res = {"metric": "MLA tree-verify attention: latent KV GB/s and TFLOP/s", "value": round(kvb / (ms * 1e-3) / 1e9, 2),
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": wl.describe()},
+           "rows_per_s": round(wl.B * wl.R / (ms * 1e-3), 1),
+           "roofline": {"kernel": "k_mla_prefix + k_mla_window_merge", "bound": "mfma",
+                        "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                        "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "algorithmic_flops": flops,
+                        "flop_per_kv_byte": round(flops / kvb, 1), "traffic": None}}
+    if args.cpu_budget > 0:
+        import oracle as orc
+        rng = np.random.default_rng(0)
+        n_rows = wl.B * wl.R * wl.Hq
+        n, total_t, done = 4, 0.0, 0
+        qb, lb = gen.bf16_bits(inp.q), gen.bf16_bits(inp.latent)
+        while total_t < args.cpu_budget and done < n_rows:
+            rows = rng.integers(0, n_rows, n)
+            t0 = time.perf_counter()
+            orc.mla_attention(qb, lb, inp.strides, inp.page_table, ps, inp.prefix_len, masks_np,
+                              wl.W, wl.Dc, wl.Dr, rows=rows)
+            total_t += time.perf_counter() - t0
+            done += n
+            n = min(2 * n, 512)
+        t_full = total_t * n_rows / done
+        cores = len(os.sched_getaffinity(0))
+        omp = os.environ.get("OMP_NUM_THREADS")
+        res["cpu_baseline"] = {"value": round(kvb / t_full / 1e9, 5), "unit": "GB/s",
+                               "cores": min(cores, int(omp)) if omp else cores, "kind": "oracle",
+                               "sample": "%d of %d (request, row, head) rows, %.1f s of fp64 oracle "
+                                         "time, scaled to the whole step" % (done, n_rows, total_t)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -444,6 +521,8 @@ def main():
     ap.add_argument("--sampled", action="store_true",
                     help="time the sampled verify (Gumbel-max draws over a 128256-token "
                          "vocabulary, then the greedy walk) instead of the attention step")
+    ap.add_argument("--mla", choices=sorted(gen.MLA_WORKLOADS),
+                    help="time the cascade over an MLA latent cache on this workload instead")
     ap.add_argument("--tree-build", action="store_true",
                     help="time tree construction (beam steps, selection, links) instead")
     ap.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
@@ -470,6 +549,9 @@ def main():
         return
     if args.tree_build:
         run_tree_build(args)
+        return
+    if args.mla:
+        run_mla(args)
         return
     wl = gen.WORKLOADS[args.workload]
     log("workload", wl)

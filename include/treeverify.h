@@ -6,6 +6,7 @@
  *                        the tree from the drafter's candidate pool
  *   tree_build_masks     parents -> depth, 64-bit ancestor masks, positions
  *   tree_attention       paged prefix + masked tree window -> out, base-2 LSE
+ *   tree_attention_mla   the same cascade over an MLA latent cache
  *   verify_tree_greedy   draft tokens, target argmax -> accepted path
  *   tree_sample_gumbel   logits -> target draws keyed by (seed, position),
  *                        for the sampled verify
@@ -308,6 +309,40 @@ size_t tree_sample_workspace_size(int32_t B, int32_t N, int32_t V);
 tav_status tree_sample_gumbel(const void *logits, tav_dtype dtype, int64_t row_stride, int32_t V,
                               int32_t B, int32_t N, const float *temperature,
                               const uint64_t *seed, const int32_t *positions, int32_t *tokens,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The same cascade over an MLA latent cache ([DTS] "One tree attention ...":
+ * MLA runs the cascade over its latent cache; a token's latent row is read
+ * once, its kv_lora_rank (Dc) leading channels are both the key's latent
+ * part and the value, and the rotary channels after them (Dr; 0 when there
+ * are none) add a second score product).  Every query head reads the one
+ * latent row of a token; visibility as tree_attention (the whole prefix,
+ * plus window node j at logical position P + j for the set bits j < W of
+ * the row's mask).
+ *   s_t = sm_scale * (q[:Dc] . c_t + q[Dc:] . r_t),  out = softmax(s) . c,
+ *   lse2 = log2 sum_t exp(s_t)
+ * q          [B][R][Hq][Dc + Dr] bf16 (the absorbed query)
+ * latent     paged pool: the row of logical position t is at element
+ *            page_table[b][t / page_size] * stride_page + (t % page_size) *
+ *            stride_token, Dc + Dr contiguous bf16 (latent part, then the
+ *            rotary part); strides in elements, rows 16-byte aligned
+ * page_table, prefix_len, max_prefix_len, masks, W, B, R as tree_attention
+ * Dc == 512; Dr in {0, 64}; dtype TAV_BF16; page_size a power of two <= 1024
+ * sm_scale   <= 0 selects 1/sqrt(Dc + Dr)
+ * out        [B][R][Hq][Dc] bf16 (round to nearest even); lse2 float
+ *            [B][R][Hq] or NULL
+ * workspace  >= tree_attention_mla_workspace_size(...) bytes, 256-byte
+ *            aligned; scratch between calls
+ */
+size_t tree_attention_mla_workspace_size(int32_t B, int32_t R, int32_t Hq, int32_t Dc,
+                                         int32_t Dr, int32_t max_prefix_len, int32_t page_size);
+tav_status tree_attention_mla(const void *q, const void *latent, tav_dtype dtype,
+                              int64_t stride_page, int64_t stride_token, int64_t num_pages,
+                              const int32_t *page_table, int32_t max_pages, int32_t page_size,
+                              const int32_t *prefix_len, int32_t max_prefix_len,
+                              const uint64_t *masks, int32_t W, int32_t B, int32_t R, int32_t Hq,
+                              int32_t Dc, int32_t Dr, float sm_scale, void *out, float *lse2,
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /*

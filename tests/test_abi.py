@@ -221,3 +221,28 @@ def test_tree_construction_entry_points_reject(L):
     assert L.tree_select_candidates(None, None, None, None, 0, 100, 8, 1, None, None, None, None,
                                     None) == 0
     assert L.tree_retrieve_links(None, 0, 8, None, None, None) == 0
+
+
+@no_gpu
+def test_tree_attention_mla_rejects(L):
+    def call(**kw):
+        a = dict(q=FAKE, lat=FAKE, dtype=tav.TAV_BF16, sp=64 * 576, st=576, num_pages=100,
+                 pt=FAKE, max_pages=20, ps=64, plen=FAKE, maxp=1000, masks=FAKE, W=16, B=2, R=16,
+                 Hq=16, Dc=512, Dr=64, scale=0.0, out=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        st = L.tree_attention_mla(a["q"], a["lat"], a["dtype"], a["sp"], a["st"], a["num_pages"],
+                                  a["pt"], a["max_pages"], a["ps"], a["plen"], a["maxp"],
+                                  a["masks"], a["W"], a["B"], a["R"], a["Hq"], a["Dc"], a["Dr"],
+                                  a["scale"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+        return st, L.tav_last_error().decode()
+    for kw, status, word in ((dict(Dc=256), 2, "Dc"), (dict(Dr=32), 2, "Dr must be 0 or 64"),
+                             (dict(dtype=tav.TAV_F32), 2, "TAV_BF16"), (dict(R=65), 1, "R must be"),
+                             (dict(max_pages=10), 1, "must cover"), (dict(st=100), 2, "16-byte"),
+                             (dict(wsb=100), 3, "workspace has"), (dict(masks=None), 1, "masks")):
+        st, msg = call(**kw)
+        assert st == status and word in msg, (kw, st, msg)
+    assert L.tree_attention_mla_workspace_size(2, 16, 16, 512, 64, 1000, 64) > 0
+    assert L.tree_attention_mla_workspace_size(2, 16, 16, 256, 64, 1000, 64) == 0
+    st, msg = call(B=0, q=None, lat=None, pt=None, plen=None, masks=None, out=None, lse=None,
+                   ws=None)
+    assert st == 0, msg

@@ -11,7 +11,8 @@ Entry points (same names as the C ABI):
   tree_build_masks, tree_shift_positions, tree_attention,
   tree_attention_workspace_size, verify_tree_greedy, compact_window_rows,
   tree_sample_gumbel, tree_sample_workspace_size, tree_beam_step,
-  tree_select_candidates, tree_retrieve_links
+  tree_select_candidates, tree_retrieve_links, tree_attention_mla,
+  tree_attention_mla_workspace_size
 plus verify_tree_sampled (tree_sample_gumbel, then verify_tree_greedy over
 the draws).
 """
@@ -36,7 +37,8 @@ EXPORTS = ("tav_last_error", "tav_version", "tree_build_masks", "tree_shift_posi
            "tree_attention_workspace_size", "tree_attention", "tree_attention_prefix",
            "tree_attention_window_merge", "verify_tree_greedy", "compact_window_rows",
            "tree_sample_workspace_size", "tree_sample_gumbel", "tree_beam_step",
-           "tree_select_candidates", "tree_retrieve_links")
+           "tree_select_candidates", "tree_retrieve_links", "tree_attention_mla_workspace_size",
+           "tree_attention_mla")
 
 
 class TavError(RuntimeError):
@@ -98,9 +100,15 @@ def lib() -> ctypes.CDLL:
         L.tree_beam_step.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P, P]
         L.tree_select_candidates.argtypes = [P, P, P, P, I32, I32, I32, I32, P, P, P, P, P]
         L.tree_retrieve_links.argtypes = [P, I32, I32, P, P, P]
+        L.tree_attention_mla_workspace_size.argtypes = [I32] * 7
+        L.tree_attention_mla_workspace_size.restype = ctypes.c_size_t
+        L.tree_attention_mla.argtypes = [P, P, ctypes.c_int, I64, I64, I64, P, I32, I32, P, I32,
+                                         P, I32, I32, I32, I32, I32, I32, ctypes.c_float, P, P, P,
+                                         ctypes.c_size_t, P]
         for f in ("tree_build_masks", "tree_shift_positions", "tree_attention",
                   "verify_tree_greedy", "compact_window_rows", "tree_sample_gumbel",
-                  "tree_beam_step", "tree_select_candidates", "tree_retrieve_links"):
+                  "tree_beam_step", "tree_select_candidates", "tree_retrieve_links",
+                  "tree_attention_mla"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -309,6 +317,46 @@ def verify_tree_sampled(draft_tokens: torch.Tensor, logits: torch.Tensor,
     r = verify_tree_greedy(draft_tokens, draws, parents)
     r["draws"] = draws
     return r
+
+
+def tree_attention_mla_workspace_size(B: int, R: int, Hq: int, Dc: int, Dr: int,
+                                      max_prefix_len: int, page_size: int) -> int:
+    return int(lib().tree_attention_mla_workspace_size(B, R, Hq, Dc, Dr, max_prefix_len,
+                                                       page_size))
+
+
+def tree_attention_mla(q: torch.Tensor, latent: torch.Tensor, page_table: torch.Tensor,
+                       prefix_len: torch.Tensor, masks: torch.Tensor, W: int, Dc: int = 512,
+                       max_prefix_len: Optional[int] = None, sm_scale: float = 0.0,
+                       workspace: Optional[torch.Tensor] = None):
+    """Tree attention over an MLA latent cache.  q bf16 [B][R][Hq][Dc + Dr];
+    latent bf16 [pages][page_size][Dc + Dr]; page_table int32 [B][max_pages];
+    prefix_len int32 [B]; masks int64 (uint64 bits) [B][R].  -> (out bf16
+    [B][R][Hq][Dc], lse2 float32 [B][R][Hq])."""
+    _need(q, "q", torch.bfloat16)
+    B, R, Hq, Dk = q.shape
+    Dr = Dk - Dc
+    dev = q.device
+    _need(latent, "latent", torch.bfloat16, dev)
+    if latent.dim() != 3 or latent.shape[2] != Dk:
+        raise ValueError("latent must be [pages][page_size][Dc + Dr]")
+    pages, ps = latent.shape[0], latent.shape[1]
+    _need(page_table, "page_table", torch.int32, dev)
+    _need(prefix_len, "prefix_len", torch.int32, dev, (B,))
+    _need(masks, "masks", torch.int64, dev, (B, R))
+    if max_prefix_len is None:
+        max_prefix_len = int(prefix_len.max().item()) if B > 0 else 0
+    need = tree_attention_mla_workspace_size(B, R, Hq, Dc, Dr, max_prefix_len, ps)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, R, Hq, Dc), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, R, Hq), dtype=torch.float32, device=dev)
+    _check(lib().tree_attention_mla(_ptr(q), _ptr(latent), TAV_BF16, ps * Dk, Dk, pages,
+                                    _ptr(page_table), page_table.shape[1], ps, _ptr(prefix_len),
+                                    int(max_prefix_len), _ptr(masks), int(W), B, R, Hq, Dc, Dr,
+                                    float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                    workspace.numel(), _stream(dev)))
+    return out, lse
 
 
 def tree_beam_step(scores: torch.Tensor, surv_idx: torch.Tensor, child_p: torch.Tensor,

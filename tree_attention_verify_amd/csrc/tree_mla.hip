@@ -1,0 +1,626 @@
+// tree_attention_mla: the verify cascade over an MLA latent cache, for gfx950.
+//
+// "Draft-tree speculation", section "One tree attention ...": MLA runs the
+// same cascade over its latent cache.  A token's latent row is read once:
+// its kv_lora_rank (Dc) leading channels are both the key's latent part and
+// the value, and the rotary channels after them (Dr) add a second score
+// product.  Every query head reads the one latent row, so all R x Hq query
+// rows of a request are folded into the MFMA N dimension against one K/V
+// stream.
+//
+// Kernels:
+//   k_mla_prefix<DR>  split-K prefix decode.  One workgroup of 4 waves (one
+//       per SIMD) owns 128 folded rows, a wave 32, and one half of the
+//       Dc = 512 value channels; per 32-key block a wave runs S^T = K Q^T
+//       over the Dc + Dr channels (36 steps of v_mfma_f32_32x32x16_bf16 for
+//       Dr = 64) and O^T += V^T P^T over its 256 value channels (8 tiles x
+//       2).  The two channel halves of a (request, row group, split) are
+//       separate workgroups on one XCD (they read the same latent rows
+//       through one L2) and compute the same scores: a whole 512-channel
+//       accumulator with the query in registers would not fit the register
+//       file.  Latent rows stream HBM -> LDS with direct-to-LDS 16-byte
+//       loads, three stages deep; the same LDS bytes are read as the K
+//       operand and, transposed, as the V operand.
+//   k_mla_window_merge<DR>  one wave per (request, row, head): the masked
+//       window keys (never the unseen ones) with lanes over channels, then
+//       the merge of the prefix partials through their base-2 LSE.
+//
+// LDS layout of a stage of 32 keys: 128-byte pieces [chunk group G][key k]
+// (G = 8 consecutive 16-byte chunks of the row); chunk c of key k sits at
+// position (c & 7) ^ h(k) of its piece, h(k) = rot3((k >> 1) & 7) with rot3
+// moving bit 0 to bit 2.  The 16 keys of a K operand read then fall on
+// distinct 16-byte bank slots (key parity selects the half of the 256-byte
+// bank row, h the slot), and a transposing V read (4 keys x 4 chunks per 32
+// lanes) on distinct 8-byte slots: keys two apart differ in bit 2 of h.
+#include <cmath>
+
+#include "tav_internal.h"
+
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+#define MLA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2eM = 1.4426950408889634f;
+constexpr int kMlaPt = 1024;            // page-table entries one split may span
+constexpr float kMlaSumLimit = 1048576.f;
+
+__device__ inline uint16_t mla_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Direct-to-LDS 16-byte load: lane i's 16 bytes land at LDS byte lds_base +
+// 16 i; completion by vmcnt then a workgroup barrier (see the prefix kernel
+// of tree_attention.hip for why it is inline assembly).
+__device__ __forceinline__ void mla_dma16(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :
+                 : "v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+template <int N>
+__device__ inline void mla_wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <typename T>
+__device__ __forceinline__ void mla_settle(T &x) {
+    asm volatile("" : "+v"(x));
+}
+
+__device__ inline float mla_pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float mla_pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline int mla_h(int k) {
+    const int x = (k >> 1) & 7;
+    return ((x & 1) << 2) | (x >> 1);
+}
+
+struct MlaArgs {
+    const uint16_t *q;
+    const uint16_t *lat;
+    int64_t stride_page, stride_token, num_pages;
+    const int32_t *page_table;
+    int32_t max_pages, ps_shift;
+    const int32_t *prefix_len;
+    int32_t max_prefix_len;
+    const uint64_t *masks;
+    int32_t W, B, R, Hq, M, RG, n_split, kps;
+    float c;        // sm_scale * log2(e)
+    float *ws_o;    // [rows][n_split][512]
+    float *ws_lse;  // [rows][n_split]
+    uint16_t *out;  // [B][R][Hq][512]
+    float *lse2;    // [B][R][Hq] or null
+};
+
+template <int DR>
+struct MlaCfg {
+    static constexpr int DC = 512;
+    static constexpr int DK = DC + DR;
+    static constexpr int KSTEPS = DK / 16;
+    static constexpr int NG = DK / 64;             // 8-chunk groups per row
+    static constexpr int DT = DC / 64;             // value tiles per channel half
+    static constexpr int SK = 32;                  // keys per stage
+    static constexpr int SB = NG * SK * 128;       // stage bytes
+    static constexpr int NBUF = 3;
+    static constexpr int LOADS = NG * SK * 8 / 64; // load instructions per stage (64 lanes each)
+    static constexpr int LPW = LOADS / 4;          // per wave
+    static_assert(DK % 64 == 0 && LOADS % 4 == 0, "row shape");
+    static_assert(NBUF * SB + kMlaPt * 4 <= 160 * 1024, "LDS");
+};
+
+template <int DR>
+__global__ void __launch_bounds__(256, 1) k_mla_prefix(MlaArgs a) {
+    using C = MlaCfg<DR>;
+    constexpr int DK = C::DK, KSTEPS = C::KSTEPS, DT = C::DT, SK = C::SK, SB = C::SB,
+                  NBUF = C::NBUF, LPW = C::LPW;
+    __shared__ __attribute__((aligned(16))) char lds[NBUF * SB];
+    __shared__ int32_t pt[kMlaPt];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hl = lane >> 5, l32 = lane & 31;
+    // blocks 16 g + 8 half + x, x < 8, take unit 8 g + x: the two halves of
+    // a unit are 8 blocks apart, on one XCD
+    const int id = blockIdx.x;
+    const int half = (id >> 3) & 1;
+    const int u = ((id >> 4) << 3) | (id & 7);
+    if (u >= a.B * a.RG * a.n_split)
+        return;   // uniform per workgroup, before any barrier
+    const int rg = u % a.RG;
+    const int unit = u / a.RG;
+    const int split = unit % a.n_split;
+    const int b = unit / a.n_split;
+
+    int P = a.prefix_len[b];
+    P = P < 0 ? 0 : (P > a.max_prefix_len ? a.max_prefix_len : P);
+    const int lo = split * a.kps;
+    const int hi = min(P, lo + a.kps) > lo ? min(P, lo + a.kps) : lo;
+    const int nkeys = hi - lo;
+    const int ns = (nkeys + SK - 1) / SK;
+
+    const int lp0 = nkeys > 0 ? (lo >> a.ps_shift) : 0;
+    const int npt = nkeys > 0 ? ((hi - 1) >> a.ps_shift) - lp0 + 1 : 0;
+    for (int i = tid; i < npt && i < kMlaPt; i += 256) {
+        int64_t p = a.page_table[(int64_t)b * a.max_pages + lp0 + i];
+        pt[i] = (int32_t)(p < 0 ? 0 : (p >= a.num_pages ? a.num_pages - 1 : p));
+    }
+    // keys past the split end are never loaded: their slots must hold finite
+    // values (their weight is exactly 0)
+    for (int i = tid; i < NBUF * SB / 16; i += 256)
+        reinterpret_cast<int4 *>(lds)[i] = make_int4(0, 0, 0, 0);
+
+    // Q^T operand: lane (row l32, half hl) holds Q[row][16 kk + 8 hl .. +8]
+    const int m = rg * 128 + w * 32 + l32;
+    const bool row_ok = m < a.M;
+    bf16x8 qv[KSTEPS];
+    {
+        const int r = row_ok ? m / a.Hq : 0, hh = row_ok ? m % a.Hq : 0;
+        const uint16_t *qp = a.q + (((int64_t)b * a.R + r) * a.Hq + hh) * DK + 8 * hl;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            const int4 v4 = row_ok ? *(const int4 *)(qp + 16 * kk) : make_int4(0, 0, 0, 0);
+            qv[kk] = __builtin_bit_cast(bf16x8, v4);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk)
+            mla_settle(qv[kk]);
+    }
+    __syncthreads();
+
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const MLA_LDS void *)lds;
+    const int ps_mask = (1 << a.ps_shift) - 1;
+    // load instruction L of a stage fills pieces (G = L / 4, keys 8 (L % 4)
+    // .. +7): lane i takes key 8 (L % 4) + i / 8, position i % 8
+    auto issue = [&](int st) {
+        const uint32_t sbase = lds0 + (uint32_t)((st % NBUF) * SB);
+#pragma unroll
+        for (int x = 0; x < LPW; ++x) {
+            const int L = w + 4 * x;
+            const int G = L / 4, key = 8 * (L % 4) + (lane >> 3), pos = lane & 7;
+            const int t = lo + st * SK + key;
+            const uint32_t dst = sbase + (uint32_t)((G * SK + 8 * (L % 4)) * 128);
+            if (t < hi) {
+                const int64_t pg = pt[(t >> a.ps_shift) - lp0];
+                const uint16_t *src = a.lat + pg * a.stride_page + (int64_t)(t & ps_mask) * a.stride_token +
+                                      (8 * G + (pos ^ mla_h(key))) * 8;
+                mla_dma16(src, __builtin_amdgcn_readfirstlane(dst));
+            }
+        }
+    };
+
+    // per-lane operand offsets inside a stage
+    auto kaddr = [&](int c) { return (c >> 3) * (SK * 128) + l32 * 128 + (((c & 7) ^ mla_h(l32)) * 16); };
+    const int G16 = lane >> 4, a4 = lane & 3, j4 = (lane >> 2) & 3;
+
+    f32x16 o[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            o[t][r] = 0.f;
+    float mu = 0.f, l_run = 0.f;
+    bool first = true;
+
+    auto compute = [&](int st) {
+        const char *base = lds + (st % NBUF) * SB;
+        const int k0 = lo + st * SK;
+        // S^T[key][row] over the Dc + Dr channels
+        f32x16 s;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            s[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            const bf16x8 ka = *(const bf16x8 *)(base + kaddr(2 * kk + hl));
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[kk], s, 0, 0, 0);
+        }
+        // keys past the split end are not visible
+        if (k0 + SK > hi) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+                if (key >= hi)
+                    s[r] = -INFINITY;
+            }
+        }
+        // softmax in the exp2 domain; the reference mu is the first block's
+        // row max and is raised only when the running sum would pass 2^20
+        // (rescaling the 512-channel accumulator is rare)
+        float mx = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r)
+            mx = fmaxf(mx, s[r]);
+        mx = mla_pair_max(mx) * a.c;
+        if (first) {
+            mu = fabsf(mx) < INFINITY ? mx : 0.f;
+            first = false;
+        }
+        float p[16], lb = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -mu));
+            lb += p[r];
+        }
+        if (__ballot(!(l_run + lb <= kMlaSumLimit))) {
+            const float mnew = mx < INFINITY ? fmaxf(mu, mx) : mu;
+            const float alpha = __builtin_amdgcn_exp2f(mu - mnew);
+            l_run *= alpha;
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    o[t][r] *= alpha;
+            mu = mnew;
+            lb = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -mu));
+                lb += p[r];
+            }
+        }
+        l_run += lb;
+        bf16x8 pb[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            pb[r >> 3][r & 7] = (__bf16)p[r];
+        // O^T[d][row] += sum_key V[key][d] P[row][key]: the V^T operand of
+        // tile t (channels 32 t .. 32 t + 31), chunk cc, half hr: lane (G16,
+        // a4, j4) points at key 16 cc + 8 hr + 4 (G16 / 2) + j4, channels
+        // 32 t + 16 (G16 & 1) + 4 a4 .. +3; the same key order as the P
+        // operand, so the sum is unchanged
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            const int d0 = 256 * half + 32 * t + 16 * (G16 & 1) + 4 * a4;
+            const int c = d0 >> 3;
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                i16x4 half[2];
+#pragma unroll
+                for (int hr = 0; hr < 2; ++hr) {
+                    const int key = cc * 16 + hr * 8 + 4 * (G16 >> 1) + j4;
+                    const char *pv = base + (c >> 3) * (SK * 128) + key * 128 +
+                                     (((c & 7) ^ mla_h(key)) * 16) + (a4 & 1) * 8;
+                    half[hr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4 *)pv);
+                }
+                struct {
+                    i16x4 lo, hi;
+                } pair{half[0], half[1]};
+                o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pair), pb[cc],
+                                                               o[t], 0, 0, 0);
+            }
+        }
+    };
+
+    for (int st = 0; st < NBUF - 1 && st < ns; ++st)
+        issue(st);
+    for (int st = 0; st < ns; ++st) {
+        // stage st complete once at most the loads of stage st + 1 (a full
+        // stage) are outstanding; all of them when st + 1 is the last
+        if (st + 1 < ns - 1)
+            mla_wait_vmcnt<LPW>();
+        else
+            mla_wait_vmcnt<0>();
+        __syncthreads();
+        if (st + NBUF - 1 < ns)
+            issue(st + NBUF - 1);
+        compute(st);
+    }
+
+    const float lt = mla_pair_sum(l_run);
+    if (row_ok) {
+        const int r = m / a.Hq, hh = m % a.Hq;
+        const int64_t row = ((int64_t)b * a.R + r) * a.Hq + hh;
+        const float inv = lt != 0.f ? 1.f / lt : 0.f;
+        float *dst = a.ws_o + (row * a.n_split + split) * 512 + 256 * half;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d = 32 * t + 16 * (q4 >> 1) + 8 * (q4 & 1) + 4 * hl;
+                *(float4 *)(dst + d) = make_float4(o[t][4 * q4] * inv, o[t][4 * q4 + 1] * inv,
+                                                   o[t][4 * q4 + 2] * inv, o[t][4 * q4 + 3] * inv);
+            }
+        if (hl == 0 && half == 0)
+            a.ws_lse[row * a.n_split + split] = lt != 0.f ? mu + __log2f(lt) : -INFINITY;
+    }
+}
+
+// Window part and merge: one wave per (request b, row r, head h).  The
+// window keys are the set bits j < W of the row's mask at logical position
+// P + j; lane l holds channels 8 l .. 8 l + 7 of the latent part (and, for
+// l < Dr / 8, rotary channels 8 l .. +7).  Online softmax over the window
+// keys, then the merge with the n_split prefix partials:
+// lse2 = log2 sum_k 2^lse2_k, out = sum_k 2^(lse2_k - lse2) o_k.
+template <int DR>
+__global__ void __launch_bounds__(256) k_mla_window_merge(MlaArgs a) {
+    constexpr int DK = 512 + DR;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (int64_t)a.B * a.R * a.Hq)
+        return;
+    const int r = (int)((row / a.Hq) % a.R);
+    const int b = (int)(row / ((int64_t)a.Hq * a.R));
+    int P = a.prefix_len[b];
+    P = P < 0 ? 0 : (P > a.max_prefix_len ? a.max_prefix_len : P);
+    const uint16_t *qp = a.q + row * DK;
+    float qc[8], qr[8];
+    {
+        const int4 x = *(const int4 *)(qp + 8 * lane);
+        const uint32_t u[4] = {(uint32_t)x.x, (uint32_t)x.y, (uint32_t)x.z, (uint32_t)x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qc[2 * e] = __uint_as_float(u[e] << 16);
+            qc[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+        }
+        int4 y = make_int4(0, 0, 0, 0);
+        if (DR > 0 && lane < DR / 8)
+            y = *(const int4 *)(qp + 512 + 8 * lane);
+        const uint32_t v[4] = {(uint32_t)y.x, (uint32_t)y.y, (uint32_t)y.z, (uint32_t)y.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qr[2 * e] = __uint_as_float(v[e] << 16);
+            qr[2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+        }
+    }
+    float mw = -INFINITY, lw = 0.f, ow[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        ow[e] = 0.f;
+    uint64_t bits = a.masks[(int64_t)b * a.R + r];
+    if (a.W < 64)
+        bits &= (1ull << a.W) - 1;
+    const int ps = 1 << a.ps_shift;
+    while (bits) {
+        const int j = __builtin_ctzll(bits);
+        bits &= bits - 1;
+        const int t = P + j;
+        const int lp = t >> a.ps_shift;
+        if (lp >= a.max_pages)
+            continue;
+        int64_t pg = a.page_table[(int64_t)b * a.max_pages + lp];
+        pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+        const uint16_t *kr = a.lat + pg * a.stride_page + (int64_t)(t & (ps - 1)) * a.stride_token;
+        const int4 x = *(const int4 *)(kr + 8 * lane);
+        const uint32_t u[4] = {(uint32_t)x.x, (uint32_t)x.y, (uint32_t)x.z, (uint32_t)x.w};
+        float kv[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kv[2 * e] = __uint_as_float(u[e] << 16);
+            kv[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+        }
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            d = fmaf(qc[e], kv[e], d);
+        if (DR > 0 && lane < DR / 8) {
+            const int4 y = *(const int4 *)(kr + 512 + 8 * lane);
+            const uint32_t v[4] = {(uint32_t)y.x, (uint32_t)y.y, (uint32_t)y.z, (uint32_t)y.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                d = fmaf(qr[2 * e], __uint_as_float(v[e] << 16), d);
+                d = fmaf(qr[2 * e + 1], __uint_as_float(v[e] & 0xffff0000u), d);
+            }
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1)
+            d += __shfl_xor(d, o);
+        const float sj = d * a.c;     // exp2 domain
+        const float mnew = fmaxf(mw, sj);
+        const float alpha = __builtin_amdgcn_exp2f(mw - mnew);
+        const float pj = __builtin_amdgcn_exp2f(sj - mnew);
+        lw = lw * alpha + pj;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            ow[e] = ow[e] * alpha + pj * kv[e];
+        mw = mnew;
+    }
+    // merge: the window part (o = ow / lw, lse2 = mw + log2 lw) and the
+    // prefix partials
+    float mx = lw != 0.f ? mw + __log2f(lw) : -INFINITY;
+    const float lse_w = mx;
+    for (int k = 0; k < a.n_split; ++k) {
+        const float l = a.ws_lse[row * a.n_split + k];
+        mx = (l != l || mx != mx) ? NAN : fmaxf(mx, l);
+    }
+    float acc[8], z = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        acc[e] = 0.f;
+    if (mx == -INFINITY) {
+        // no key at all: out = 0, lse2 = -inf
+    } else {
+        if (lse_w != -INFINITY) {
+            const float zw = __builtin_amdgcn_exp2f(lse_w - mx);
+            const float inv = 1.f / lw;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                acc[e] = zw * ow[e] * inv;
+            z = zw;
+        }
+        for (int k = 0; k < a.n_split; ++k) {
+            const float l = a.ws_lse[row * a.n_split + k];
+            if (l == -INFINITY)
+                continue;
+            const float zk = __builtin_amdgcn_exp2f(l - mx);
+            const float4 *src = (const float4 *)(a.ws_o + (row * a.n_split + k) * 512 + 8 * lane);
+            const float4 p0 = src[0], p1 = src[1];
+            acc[0] = fmaf(zk, p0.x, acc[0]);
+            acc[1] = fmaf(zk, p0.y, acc[1]);
+            acc[2] = fmaf(zk, p0.z, acc[2]);
+            acc[3] = fmaf(zk, p0.w, acc[3]);
+            acc[4] = fmaf(zk, p1.x, acc[4]);
+            acc[5] = fmaf(zk, p1.y, acc[5]);
+            acc[6] = fmaf(zk, p1.z, acc[6]);
+            acc[7] = fmaf(zk, p1.w, acc[7]);
+            z += zk;
+        }
+    }
+    const float invz = z != 0.f ? 1.f / z : 0.f;
+    uint32_t packed[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        packed[e] = (uint32_t)mla_bf16_bits(acc[2 * e] * invz) |
+                    ((uint32_t)mla_bf16_bits(acc[2 * e + 1] * invz) << 16);
+    *(int4 *)(a.out + row * 512 + 8 * lane) =
+        make_int4((int)packed[0], (int)packed[1], (int)packed[2], (int)packed[3]);
+    if (a.lse2 && lane == 0)
+        a.lse2[row] = mx == -INFINITY ? -INFINITY : mx + __log2f(z);
+}
+
+struct MlaPlan {
+    int RG, n_split, kps;
+    size_t o_bytes, bytes;
+};
+
+inline size_t mla_align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+MlaPlan mla_plan(int B, int R, int Hq, int max_prefix_len, int page_size) {
+    MlaPlan p{};
+    const long long M = (long long)R * Hq;
+    p.RG = (int)((M + 127) / 128);
+    const long long base = (long long)B * p.RG;
+    int n = base > 0 ? (int)((256 + base - 1) / base) : 1;
+    const int by_keys = max_prefix_len / 128;            // >= 4 stages per split
+    n = n < by_keys ? n : by_keys;
+    n = n < 1 ? 1 : n;
+    int kps;
+    for (;;) {
+        kps = (max_prefix_len + n - 1) / n;
+        kps = ((kps + 31) / 32) * 32;
+        if (kps < 32)
+            kps = 32;
+        if ((long long)kps / page_size + 2 <= kMlaPt)
+            break;
+        ++n;
+    }
+    p.kps = kps;
+    p.n_split = max_prefix_len > 0 ? (max_prefix_len + kps - 1) / kps : 1;
+    const long long rows = (long long)B * R * Hq;
+    p.o_bytes = mla_align256((size_t)rows * p.n_split * 512 * sizeof(float));
+    p.bytes = p.o_bytes + mla_align256((size_t)rows * p.n_split * sizeof(float));
+    return p;
+}
+
+inline hipStream_t MS(void *s) { return (hipStream_t)s; }
+
+}  // namespace
+
+using tav::Checks;
+using tav::str;
+
+extern "C" size_t tree_attention_mla_workspace_size(int32_t B, int32_t R, int32_t Hq, int32_t Dc,
+                                                    int32_t Dr, int32_t max_prefix_len,
+                                                    int32_t page_size) {
+    if (B < 0 || R < 1 || R > 64 || Hq < 1 || Dc != 512 || (Dr != 0 && Dr != 64) ||
+        max_prefix_len < 0 || !tav::is_pow2(page_size) || page_size > 1024)
+        return 0;
+    return mla_plan(B, R, Hq, max_prefix_len, page_size).bytes;
+}
+
+extern "C" tav_status tree_attention_mla(const void *q, const void *latent, tav_dtype dtype,
+                                         int64_t stride_page, int64_t stride_token,
+                                         int64_t num_pages, const int32_t *page_table,
+                                         int32_t max_pages, int32_t page_size,
+                                         const int32_t *prefix_len, int32_t max_prefix_len,
+                                         const uint64_t *masks, int32_t W, int32_t B, int32_t R,
+                                         int32_t Hq, int32_t Dc, int32_t Dr, float sm_scale,
+                                         void *out, float *lse2, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+    Checks c;
+    c.need(B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
+    c.need(R >= 1 && R <= 64, TAV_ERR_INVALID_ARG, "R must be in [1, 64], got " + str(R));
+    c.need(W >= 0 && W <= 64, TAV_ERR_INVALID_ARG, "W must be in [0, 64], got " + str(W));
+    c.need(Hq >= 1, TAV_ERR_INVALID_ARG, "Hq must be >= 1, got " + str(Hq));
+    c.need(Dc == 512, TAV_ERR_UNSUPPORTED, "Dc (kv_lora_rank) must be 512, got " + str(Dc));
+    c.need(Dr == 0 || Dr == 64, TAV_ERR_UNSUPPORTED, "Dr must be 0 or 64, got " + str(Dr));
+    c.need(dtype == TAV_BF16, TAV_ERR_UNSUPPORTED, "the MLA path takes TAV_BF16, got " + str(dtype));
+    c.need(tav::is_pow2(page_size) && page_size <= 1024, TAV_ERR_UNSUPPORTED,
+           "page_size must be a power of two <= 1024, got " + str(page_size));
+    c.need(max_prefix_len >= 0, TAV_ERR_INVALID_ARG, "max_prefix_len must be >= 0");
+    c.need(max_pages >= 1 && (long long)max_pages * page_size >= (long long)max_prefix_len + W,
+           TAV_ERR_INVALID_ARG, "max_pages * page_size must cover max_prefix_len + W");
+    c.need(num_pages >= 1, TAV_ERR_INVALID_ARG, "num_pages must be >= 1");
+    c.need(stride_token >= Dc + Dr && (stride_token * 2) % 16 == 0 && (stride_page * 2) % 16 == 0,
+           TAV_ERR_UNSUPPORTED,
+           "latent rows must hold Dc + Dr contiguous elements at 16-byte aligned strides");
+    c.need(std::isfinite(sm_scale), TAV_ERR_INVALID_ARG, "sm_scale must be finite");
+    if (B > 0) {
+        c.need(q && latent && page_table && prefix_len && masks && out, TAV_ERR_INVALID_ARG,
+               "q, latent, page_table, prefix_len, masks and out must be set");
+        c.need(((uintptr_t)q & 15) == 0 && ((uintptr_t)latent & 15) == 0 && ((uintptr_t)out & 15) == 0,
+               TAV_ERR_INVALID_ARG, "q, latent and out must be 16-byte aligned");
+        if (c.status == TAV_OK) {
+            const MlaPlan p = mla_plan(B, R, Hq, max_prefix_len, page_size);
+            c.need(workspace && ((uintptr_t)workspace & 255) == 0, TAV_ERR_WORKSPACE,
+                   "workspace must be set and 256-byte aligned");
+            c.need(workspace_bytes >= p.bytes, TAV_ERR_WORKSPACE,
+                   "workspace has " + str((long long)workspace_bytes) + " bytes, needs " +
+                       str((long long)p.bytes));
+        }
+    }
+    if (c.status != TAV_OK || B == 0)
+        return tav::finish("tree_attention_mla", c);
+    const MlaPlan p = mla_plan(B, R, Hq, max_prefix_len, page_size);
+    MlaArgs a{};
+    a.q = (const uint16_t *)q;
+    a.lat = (const uint16_t *)latent;
+    a.stride_page = stride_page;
+    a.stride_token = stride_token;
+    a.num_pages = num_pages;
+    a.page_table = page_table;
+    a.max_pages = max_pages;
+    a.ps_shift = tav::ilog2(page_size);
+    a.prefix_len = prefix_len;
+    a.max_prefix_len = max_prefix_len;
+    a.masks = masks;
+    a.W = W;
+    a.B = B;
+    a.R = R;
+    a.Hq = Hq;
+    a.M = R * Hq;
+    a.RG = p.RG;
+    a.n_split = p.n_split;
+    a.kps = p.kps;
+    const float scale = sm_scale > 0.f ? sm_scale : 1.f / std::sqrt((float)(Dc + Dr));
+    a.c = scale * kLog2eM;
+    a.ws_o = (float *)workspace;
+    a.ws_lse = (float *)((char *)workspace + p.o_bytes);
+    a.out = (uint16_t *)out;
+    a.lse2 = lse2;
+    if (max_prefix_len > 0) {
+        const long long units = (long long)B * p.RG * p.n_split;
+        const unsigned grid = (unsigned)(((units + 7) / 8) * 16);
+        if (Dr == 64)
+            hipLaunchKernelGGL(k_mla_prefix<64>, dim3(grid), dim3(256), 0, MS(stream), a);
+        else
+            hipLaunchKernelGGL(k_mla_prefix<0>, dim3(grid), dim3(256), 0, MS(stream), a);
+        tav_status st = tav::launched("tree_attention_mla");
+        if (st != TAV_OK)
+            return st;
+    } else {
+        a.n_split = 0;
+    }
+    const long long rows = (long long)B * R * Hq;
+    if (Dr == 64)
+        hipLaunchKernelGGL(k_mla_window_merge<64>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                           MS(stream), a);
+    else
+        hipLaunchKernelGGL(k_mla_window_merge<0>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                           MS(stream), a);
+    return tav::launched("tree_attention_mla");
+}
