@@ -45,7 +45,6 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 constexpr float kLog2eM = 1.4426950408889634f;
 constexpr int kMlaPt = 1024;            // page-table entries one split may span
-constexpr float kMlaSumLimit = 1048576.f;
 
 __device__ inline uint16_t mla_bf16_bits(float f) {
     uint32_t u = __float_as_uint(f);
@@ -208,26 +207,36 @@ __global__ void __launch_bounds__(256, 1) k_mla_prefix(MlaArgs a) {
     const int G16 = lane >> 4, a4 = lane & 3, j4 = (lane >> 2) & 3;
 
     f32x16 o[DT];
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            o[t][r] = 0.f;
-    float mu = 0.f, l_run = 0.f;
-    bool first = true;
+    float mu = 0.f, l_run = 0.f, seen = -INFINITY;
+    bool have_mu = false;
 
+    // One 32-key block.  The weights are exp2(s c - mu) with mu fixed for the
+    // whole pass: the first block's row max in the first pass.  Later keys
+    // may exceed it; up to 2^64 the weights and their sums stay far inside
+    // fp32 range and keep full relative precision.  When a row's max passes
+    // mu + 64 the pass is repeated with mu = that row's max over the split
+    // (then every weight is <= 1), so the accumulator is never rescaled.
     auto compute = [&](int st) {
         const char *base = lds + (st % NBUF) * SB;
         const int k0 = lo + st * SK;
-        // S^T[key][row] over the Dc + Dr channels
+        // S^T[key][row] over the Dc + Dr channels; the K operands are read
+        // four steps ahead of their MFMA
         f32x16 s;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             s[r] = 0.f;
+        constexpr int KP = 4;
+        bf16x8 kr[KP];
+#pragma unroll
+        for (int i = 0; i < KP; ++i)
+            kr[i] = *(const bf16x8 *)(base + kaddr(2 * i + hl));
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-            const bf16x8 ka = *(const bf16x8 *)(base + kaddr(2 * kk + hl));
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[kk], s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[kk % KP], qv[kk], s, 0, 0, 0);
+            if (kk + KP < KSTEPS)
+                kr[kk % KP] = *(const bf16x8 *)(base + kaddr(2 * (kk + KP) + hl));
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
         }
         // keys past the split end are not visible
         if (k0 + SK > hi) {
@@ -238,87 +247,103 @@ __global__ void __launch_bounds__(256, 1) k_mla_prefix(MlaArgs a) {
                     s[r] = -INFINITY;
             }
         }
-        // softmax in the exp2 domain; the reference mu is the first block's
-        // row max and is raised only when the running sum would pass 2^20
-        // (rescaling the 512-channel accumulator is rare)
         float mx = s[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r)
             mx = fmaxf(mx, s[r]);
         mx = mla_pair_max(mx) * a.c;
-        if (first) {
+        seen = fmaxf(seen, mx);
+        if (!have_mu) {
             mu = fabsf(mx) < INFINITY ? mx : 0.f;
-            first = false;
+            have_mu = true;
         }
-        float p[16], lb = 0.f;
+        bf16x8 pb[2];
+        float lb0 = 0.f, lb1 = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -mu));
-            lb += p[r];
+            const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -mu));
+            pb[r >> 3][r & 7] = (__bf16)pr;
+            if (r & 1)
+                lb1 += pr;
+            else
+                lb0 += pr;
         }
-        if (__ballot(!(l_run + lb <= kMlaSumLimit))) {
-            const float mnew = mx < INFINITY ? fmaxf(mu, mx) : mu;
-            const float alpha = __builtin_amdgcn_exp2f(mu - mnew);
-            l_run *= alpha;
-#pragma unroll
-            for (int t = 0; t < DT; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    o[t][r] *= alpha;
-            mu = mnew;
-            lb = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -mu));
-                lb += p[r];
-            }
-        }
-        l_run += lb;
-        bf16x8 pb[2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            pb[r >> 3][r & 7] = (__bf16)p[r];
+        l_run += lb0 + lb1;
         // O^T[d][row] += sum_key V[key][d] P[row][key]: the V^T operand of
-        // tile t (channels 32 t .. 32 t + 31), chunk cc, half hr: lane (G16,
+        // tile t (channels 256 half + 32 t .. +31), chunk cc, half hr: lane (G16,
         // a4, j4) points at key 16 cc + 8 hr + 4 (G16 / 2) + j4, channels
         // 32 t + 16 (G16 & 1) + 4 a4 .. +3; the same key order as the P
-        // operand, so the sum is unchanged
+        // operand, so the sum is unchanged.  Operands one tile ahead.
+        auto vread = [&](int t, int cc, int hr) {
+            const int c = (256 * half + 32 * t + 16 * (G16 & 1) + 4 * a4) >> 3;
+            const int key = cc * 16 + hr * 8 + 4 * (G16 >> 1) + j4;
+            const char *pv = base + (c >> 3) * (SK * 128) + key * 128 +
+                             (((c & 7) ^ mla_h(key)) * 16) + (a4 & 1) * 8;
+            return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4 *)pv);
+        };
+        i16x4 vr[2][2][2];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int hr = 0; hr < 2; ++hr)
+                vr[0][cc][hr] = vread(0, cc, hr);
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
-            const int d0 = 256 * half + 32 * t + 16 * (G16 & 1) + 4 * a4;
-            const int c = d0 >> 3;
+            if (t + 1 < DT) {
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                    for (int hr = 0; hr < 2; ++hr)
+                        vr[(t + 1) & 1][cc][hr] = vread(t + 1, cc, hr);
+            }
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
-                i16x4 half[2];
-#pragma unroll
-                for (int hr = 0; hr < 2; ++hr) {
-                    const int key = cc * 16 + hr * 8 + 4 * (G16 >> 1) + j4;
-                    const char *pv = base + (c >> 3) * (SK * 128) + key * 128 +
-                                     (((c & 7) ^ mla_h(key)) * 16) + (a4 & 1) * 8;
-                    half[hr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4 *)pv);
-                }
                 struct {
                     i16x4 lo, hi;
-                } pair{half[0], half[1]};
+                } pair{vr[t & 1][cc][0], vr[t & 1][cc][1]};
                 o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pair), pb[cc],
                                                                o[t], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // LDS reads of tile t + 1
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMAs of tile t
         }
     };
 
-    for (int st = 0; st < NBUF - 1 && st < ns; ++st)
-        issue(st);
-    for (int st = 0; st < ns; ++st) {
-        // stage st complete once at most the loads of stage st + 1 (a full
-        // stage) are outstanding; all of them when st + 1 is the last
-        if (st + 1 < ns - 1)
-            mla_wait_vmcnt<LPW>();
-        else
-            mla_wait_vmcnt<0>();
+    __shared__ int redo_flag;
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                o[t][r] = 0.f;
+        l_run = 0.f;
+        for (int st = 0; st < NBUF - 1 && st < ns; ++st)
+            issue(st);
+        for (int st = 0; st < ns; ++st) {
+            // stage st complete once at most the loads of stage st + 1 (a full
+            // stage) are outstanding; all of them when st + 1 is the last
+            if (st + 1 < ns - 1)
+                mla_wait_vmcnt<LPW>();
+            else
+                mla_wait_vmcnt<0>();
+            __syncthreads();
+            if (st + NBUF - 1 < ns)
+                issue(st + NBUF - 1);
+            compute(st);
+        }
+        // repeat with the exact row max when some row passed mu + 64 (the
+        // decision is the workgroup's: the stages are shared)
+        const bool need = __ballot(seen > mu + 64.f) != 0;
+        if (tid == 0)
+            redo_flag = 0;
         __syncthreads();
-        if (st + NBUF - 1 < ns)
-            issue(st + NBUF - 1);
-        compute(st);
+        if (need && lane == 0)
+            redo_flag = 1;
+        __syncthreads();
+        if (pass == 1 || redo_flag == 0)
+            break;
+        mu = fabsf(seen) < INFINITY ? seen : 0.f;
+        __syncthreads();    // every wave is done with the stages before they refill
     }
 
     const float lt = mla_pair_sum(l_run);
