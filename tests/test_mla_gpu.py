@@ -90,3 +90,21 @@ def test_mla_full_size_sampled_rows(name):
     rng = np.random.default_rng(0)
     rows = np.sort(rng.choice(wl.B * wl.R * wl.Hq, size=24, replace=False))
     check(inp, m, out, lse, rows=rows, tag=name)
+
+
+def test_mla_late_dominant_key_repeats_the_pass():
+    # Every head's query is all ones and one late prefix key holds 3.0 in
+    # every channel: its score passes the first block's row max by far more
+    # than 64 (log2 units), so each split holding it is computed again with
+    # the exact row max as the reference; the result is still the oracle's.
+    wl = gen.MlaWorkload("m", 2, 2000, 8, 16, 512, 64, 64)
+    inp = gen.make_mla_inputs(wl, 31, "cuda", prefix_lens=np.array([2000, 1500]))
+    inp.q.fill_(1.0)
+    for b, t in ((0, 1900), (1, 700)):
+        pg = int(inp.page_table[b, t // wl.page_size])
+        inp.latent[pg, t % wl.page_size, :] = 3.0
+    m = oracle.build_masks(inp.parents)["masks"]
+    out, lse = run(inp, m)
+    check(inp, m, out, lse, tag="late dominant key")
+    # the dominant key's latent part is the output
+    assert torch.allclose(out.float(), torch.full_like(out.float(), 3.0), atol=1e-2)
