@@ -494,7 +494,7 @@ def run_mla(args):
                               wl.W, wl.Dc, wl.Dr, rows=rows)
             total_t += time.perf_counter() - t0
             done += n
-            n = min(2 * n, 512)
+            n = min(2 * n, 512, n_rows - done)
         t_full = total_t * n_rows / done
         cores = len(os.sched_getaffinity(0))
         omp = os.environ.get("OMP_NUM_THREADS")

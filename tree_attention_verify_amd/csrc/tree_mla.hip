@@ -9,29 +9,31 @@
 // stream.
 //
 // Kernels:
-//   k_mla_prefix<DR>  split-K prefix decode.  One workgroup of 4 waves (one
-//       per SIMD) owns 128 folded rows, a wave 32, and one half of the
-//       Dc = 512 value channels; per 32-key block a wave runs S^T = K Q^T
-//       over the Dc + Dr channels (36 steps of v_mfma_f32_32x32x16_bf16 for
-//       Dr = 64) and O^T += V^T P^T over its 256 value channels (8 tiles x
-//       2).  The two channel halves of a (request, row group, split) are
-//       separate workgroups on one XCD (they read the same latent rows
-//       through one L2) and compute the same scores: a whole 512-channel
-//       accumulator with the query in registers would not fit the register
-//       file.  Latent rows stream HBM -> LDS with direct-to-LDS 16-byte
-//       loads, three stages deep; the same LDS bytes are read as the K
-//       operand and, transposed, as the V operand.
+//   k_mla_prefix<DR>  split-K prefix decode.  One workgroup of 8 waves (two
+//       per SIMD, at most 256 registers each) owns 128 folded rows, a wave
+//       16, and one half of the Dc = 512 value channels; per 32-key block a
+//       wave runs S^T = K Q^T for two 16-key tiles over the Dc + Dr channels
+//       (2 x 18 steps of v_mfma_f32_16x16x32_bf16 for Dr = 64) and O^T +=
+//       V^T P^T over its 256 value channels (16 tiles, one step each).  The
+//       two channel halves of a (request, row group, split) are separate
+//       workgroups on one XCD and compute the same scores: the query (576
+//       channels) and a whole 512-channel accumulator of 16 rows would not
+//       fit one wave's 256 registers.  Latent rows stream HBM -> LDS with
+//       direct-to-LDS 16-byte loads, four stages deep; the same LDS bytes
+//       are read as the K operand and, transposed, as the V operand.
 //   k_mla_window_merge<DR>  one wave per (request, row, head): the masked
 //       window keys (never the unseen ones) with lanes over channels, then
 //       the merge of the prefix partials through their base-2 LSE.
 //
-// LDS layout of a stage of 32 keys: 128-byte pieces [chunk group G][key k]
-// (G = 8 consecutive 16-byte chunks of the row); chunk c of key k sits at
-// position (c & 7) ^ h(k) of its piece, h(k) = rot3((k >> 1) & 7) with rot3
-// moving bit 0 to bit 2.  The 16 keys of a K operand read then fall on
-// distinct 16-byte bank slots (key parity selects the half of the 256-byte
-// bank row, h the slot), and a transposing V read (4 keys x 4 chunks per 32
-// lanes) on distinct 8-byte slots: keys two apart differ in bit 2 of h.
+// LDS layout of a stage of 32 keys: 1 KB blocks [chunk group G][key block
+// K8] (G = 8 consecutive 16-byte chunks of the row, K8 = 8 consecutive
+// keys); inside a block, chunk c of key k sits at 16-byte slot 16 (c % 8 /
+// 2) + 8 (c % 2) + k % 8, i.e. four 256-byte runs of one chunk pair, each
+// [chunk parity][key].  The K operand read of 32 lanes (16 keys x chunks 4 s
+// + {0, 1}) then covers two whole 256-byte runs, and the transposing V read
+// of 32 lanes (8 keys x 2 chunks) one run: both run at the full LDS rate on
+// gfx950 (measured), where 16-byte reads from 16 separate 128-byte key rows
+// ran at half of it.
 #include <cmath>
 
 #include "tav_internal.h"
@@ -40,7 +42,7 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 #define MLA_LDS __attribute__((address_space(3)))
 
 constexpr float kLog2eM = 1.4426950408889634f;
@@ -75,18 +77,19 @@ __device__ __forceinline__ void mla_settle(T &x) {
     asm volatile("" : "+v"(x));
 }
 
-__device__ inline float mla_pair_max(float x) {
+// max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one row of a
+// 16 x 16 MFMA result)
+__device__ inline float mla_quad_max(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
-__device__ inline float mla_pair_sum(float x) {
+__device__ inline float mla_quad_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ inline int mla_h(int k) {
-    const int x = (k >> 1) & 7;
-    return ((x & 1) << 2) | (x >> 1);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 struct MlaArgs {
@@ -110,40 +113,42 @@ template <int DR>
 struct MlaCfg {
     static constexpr int DC = 512;
     static constexpr int DK = DC + DR;
-    static constexpr int KSTEPS = DK / 16;
+    static constexpr int KS = DK / 32;             // 32-channel score steps
     static constexpr int NG = DK / 64;             // 8-chunk groups per row
-    static constexpr int DT = DC / 64;             // value tiles per channel half
+    static constexpr int NT = DC / 2 / 16;         // 16-channel value tiles per channel half
     static constexpr int SK = 32;                  // keys per stage
     static constexpr int SB = NG * SK * 128;       // stage bytes
-    static constexpr int NBUF = 3;
+    static constexpr int NBUF = 4;
     static constexpr int LOADS = NG * SK * 8 / 64; // load instructions per stage (64 lanes each)
-    static constexpr int LPW = LOADS / 4;          // per wave
-    static_assert(DK % 64 == 0 && LOADS % 4 == 0, "row shape");
+    static constexpr int LPW = LOADS / 4;          // per loading wave (waves 0..3)
+    static_assert(DK % 64 == 0 && LOADS % 4 == 0 && LPW == NG && KS % 2 == 0, "row shape");
     static_assert(NBUF * SB + kMlaPt * 4 <= 160 * 1024, "LDS");
 };
 
 template <int DR>
-__global__ void __launch_bounds__(256, 1) k_mla_prefix(MlaArgs a) {
+__global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
     using C = MlaCfg<DR>;
-    constexpr int DK = C::DK, KSTEPS = C::KSTEPS, DT = C::DT, SK = C::SK, SB = C::SB,
+    constexpr int DK = C::DK, KS = C::KS, NT = C::NT, SK = C::SK, SB = C::SB,
                   NBUF = C::NBUF, LPW = C::LPW;
     __shared__ __attribute__((aligned(16))) char lds[NBUF * SB];
     __shared__ int32_t pt[kMlaPt];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hl = lane >> 5, l32 = lane & 31;
-    // blocks 16 g + 8 half + x, x < 8, take unit 8 g + x: the two halves of
-    // a unit are 8 blocks apart, on one XCD
+    const int g = lane >> 4, i16 = lane & 15;
+    // A stream U = (request, split) has 2 RG workgroups (row group, channel
+    // half), j = 2 rg + half; they take blocks 8 (2 RG (U / 8) + j) + U % 8.
+    // Blocks are dealt to the eight XCDs in turn, so every reader of a
+    // stream's latent rows sits on XCD U % 8 and one L2 serves them all.
     const int id = blockIdx.x;
-    const int half = (id >> 3) & 1;
-    const int u = ((id >> 4) << 3) | (id & 7);
-    if (u >= a.B * a.RG * a.n_split)
+    const int per = 2 * a.RG;
+    const int U = ((id >> 3) / per) * 8 + (id & 7);
+    const int j = (id >> 3) % per;
+    const int rg = j >> 1, half = j & 1;
+    if (U >= a.B * a.n_split)
         return;   // uniform per workgroup, before any barrier
-    const int rg = u % a.RG;
-    const int unit = u / a.RG;
-    const int split = unit % a.n_split;
-    const int b = unit / a.n_split;
+    const int split = U % a.n_split;
+    const int b = U / a.n_split;
 
     int P = a.prefix_len[b];
     P = P < 0 ? 0 : (P > a.max_prefix_len ? a.max_prefix_len : P);
@@ -154,59 +159,91 @@ __global__ void __launch_bounds__(256, 1) k_mla_prefix(MlaArgs a) {
 
     const int lp0 = nkeys > 0 ? (lo >> a.ps_shift) : 0;
     const int npt = nkeys > 0 ? ((hi - 1) >> a.ps_shift) - lp0 + 1 : 0;
-    for (int i = tid; i < npt && i < kMlaPt; i += 256) {
+    for (int i = tid; i < npt && i < kMlaPt; i += 512) {
         int64_t p = a.page_table[(int64_t)b * a.max_pages + lp0 + i];
         pt[i] = (int32_t)(p < 0 ? 0 : (p >= a.num_pages ? a.num_pages - 1 : p));
     }
     // keys past the split end are never loaded: their slots must hold finite
     // values (their weight is exactly 0)
-    for (int i = tid; i < NBUF * SB / 16; i += 256)
+    for (int i = tid; i < NBUF * SB / 16; i += 512)
         reinterpret_cast<int4 *>(lds)[i] = make_int4(0, 0, 0, 0);
 
-    // Q^T operand: lane (row l32, half hl) holds Q[row][16 kk + 8 hl .. +8]
-    const int m = rg * 128 + w * 32 + l32;
+    // Q^T operand of score step s: lane (g, i16) holds Q[row i16 of the
+    // wave][32 s + 8 g .. +8]
+    const int m = rg * 128 + w * 16 + i16;
     const bool row_ok = m < a.M;
-    bf16x8 qv[KSTEPS];
+    bf16x8 qv[KS];
     {
         const int r = row_ok ? m / a.Hq : 0, hh = row_ok ? m % a.Hq : 0;
-        const uint16_t *qp = a.q + (((int64_t)b * a.R + r) * a.Hq + hh) * DK + 8 * hl;
+        const uint16_t *qp = a.q + (((int64_t)b * a.R + r) * a.Hq + hh) * DK + 8 * g;
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-            const int4 v4 = row_ok ? *(const int4 *)(qp + 16 * kk) : make_int4(0, 0, 0, 0);
-            qv[kk] = __builtin_bit_cast(bf16x8, v4);
+        for (int s = 0; s < KS; ++s) {
+            const int4 v4 = row_ok ? *(const int4 *)(qp + 32 * s) : make_int4(0, 0, 0, 0);
+            qv[s] = __builtin_bit_cast(bf16x8, v4);
         }
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk)
-            mla_settle(qv[kk]);
+        for (int s = 0; s < KS; ++s)
+            mla_settle(qv[s]);
     }
     __syncthreads();
 
     const uint32_t lds0 = (uint32_t)(uintptr_t)(const MLA_LDS void *)lds;
     const int ps_mask = (1 << a.ps_shift) - 1;
-    // load instruction L of a stage fills pieces (G = L / 4, keys 8 (L % 4)
-    // .. +7): lane i takes key 8 (L % 4) + i / 8, position i % 8
+    // Waves 0..3 load the stages.  Load x of wave w fills the 1 KB block
+    // (G = x, keys 8 w .. 8 w + 7): lane i takes key 8 w + i % 8 and chunk 8 x
+    // + 2 (i / 16) + (i / 8) % 2, so a lane's loads of one stage all read one
+    // latent row (one page lookup) and each load reads eight whole 128-byte
+    // row segments.
+    const int dkey = 8 * (w & 3) + (lane & 7);
+    const int dpos = 2 * (lane >> 4) + ((lane >> 3) & 1);
     auto issue = [&](int st) {
-        const uint32_t sbase = lds0 + (uint32_t)((st % NBUF) * SB);
+        if (w >= 4)
+            return;
+        const uint32_t sbase = lds0 + (uint32_t)((st % NBUF) * SB + 8 * w * 128);
+        const int t = lo + st * SK + dkey;
+        if (t < hi) {
+            const int64_t pg = pt[(t >> a.ps_shift) - lp0];
+            const uint16_t *src = a.lat + pg * a.stride_page + (int64_t)(t & ps_mask) * a.stride_token + dpos * 8;
 #pragma unroll
-        for (int x = 0; x < LPW; ++x) {
-            const int L = w + 4 * x;
-            const int G = L / 4, key = 8 * (L % 4) + (lane >> 3), pos = lane & 7;
-            const int t = lo + st * SK + key;
-            const uint32_t dst = sbase + (uint32_t)((G * SK + 8 * (L % 4)) * 128);
-            if (t < hi) {
-                const int64_t pg = pt[(t >> a.ps_shift) - lp0];
-                const uint16_t *src = a.lat + pg * a.stride_page + (int64_t)(t & ps_mask) * a.stride_token +
-                                      (8 * G + (pos ^ mla_h(key))) * 8;
-                mla_dma16(src, __builtin_amdgcn_readfirstlane(dst));
-            }
+            for (int x = 0; x < LPW; ++x)
+                mla_dma16(src + 64 * x, __builtin_amdgcn_readfirstlane(sbase + (uint32_t)(x * SK * 128)));
         }
     };
 
-    // per-lane operand offsets inside a stage
-    auto kaddr = [&](int c) { return (c >> 3) * (SK * 128) + l32 * 128 + (((c & 7) ^ mla_h(l32)) * 16); };
-    const int G16 = lane >> 4, a4 = lane & 3, j4 = (lane >> 2) & 3;
+    // Per-lane operand offsets inside a stage.  K operand of step s, tile tt:
+    // lane (g, i16) reads key 16 tt + i16, chunk 4 s + g: block (s / 2, key /
+    // 8), pair run 2 (s % 2) + g / 2, parity g % 2.  The step parts are
+    // immediates, koff[tt] the rest.
+    uint32_t koff[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const int key = 16 * tt + i16;
+        koff[tt] = (uint32_t)((key >> 3) * 1024 + ((g >> 1) * 16 + (g & 1) * 8 + (key & 7)) * 16);
+    }
+    // V^T operand of value tile T (channels 256 half + 16 T .. +15), key tile
+    // tt: lane (g, j4 = i16 / 4, a4 = i16 % 4) points at key 16 tt + 4 g +
+    // j4, channels 16 T + 4 a4 .. +3 (chunk 32 half + 2 T + a4 / 2); the
+    // transposing read hands lane i16 channel i16 of those four keys, in the
+    // order of the P operand.  Block (4 half + T / 4, key / 8) and pair run
+    // T % 4 are immediates, voff[tt] the rest.
+    uint32_t voff[2];
+    {
+        const int j4 = i16 >> 2, a4 = i16 & 3;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int key = 16 * tt + 4 * g + j4;
+            voff[tt] = (uint32_t)((key >> 3) * 1024 + ((a4 >> 1) * 8 + (key & 7)) * 16 + (a4 & 1) * 8);
+        }
+    }
+    // key of score value r of tile tt held by this lane, relative to the block
+    int kofs[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            kofs[tt][r] = 16 * tt + 4 * g + r;
 
-    f32x16 o[DT];
+    f32x4 o[NT];
     float mu = 0.f, l_run = 0.f, seen = -INFINITY;
     bool have_mu = false;
 
@@ -218,118 +255,118 @@ __global__ void __launch_bounds__(256, 1) k_mla_prefix(MlaArgs a) {
     // (then every weight is <= 1), so the accumulator is never rescaled.
     auto compute = [&](int st) {
         const char *base = lds + (st % NBUF) * SB;
-        const int k0 = lo + st * SK;
-        // S^T[key][row] over the Dc + Dr channels; the K operands are read
-        // four steps ahead of their MFMA
-        f32x16 s;
+        // S^T[key][row] of the two key tiles over the Dc + Dr channels, four
+        // K operands in flight
+        const char *kb[2] = {base + koff[0], base + koff[1]};
+        auto kread = [&](int s, int tt) {
+            return *(const bf16x8 *)(kb[tt] + (s >> 1) * (SK * 128) + (s & 1) * 512);
+        };
+        f32x4 s0, s1;
+        bf16x8 ka0 = kread(0, 0), kb0 = kread(0, 1), ka1 = kread(1, 0), kb1 = kread(1, 1);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            s[r] = 0.f;
-        constexpr int KP = 4;
-        bf16x8 kr[KP];
-#pragma unroll
-        for (int i = 0; i < KP; ++i)
-            kr[i] = *(const bf16x8 *)(base + kaddr(2 * i + hl));
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[kk % KP], qv[kk], s, 0, 0, 0);
-            if (kk + KP < KSTEPS)
-                kr[kk % KP] = *(const bf16x8 *)(base + kaddr(2 * (kk + KP) + hl));
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-        }
-        // keys past the split end are not visible
-        if (k0 + SK > hi) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-                if (key >= hi)
-                    s[r] = -INFINITY;
+        for (int s = 0; s < KS; s += 2) {
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qv[s], s ? s0 : f32x4{}, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb0, qv[s], s ? s1 : f32x4{}, 0, 0, 0);
+            if (s + 2 < KS) {
+                ka0 = kread(s + 2, 0);
+                kb0 = kread(s + 2, 1);
+            }
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qv[s + 1], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb1, qv[s + 1], s1, 0, 0, 0);
+            if (s + 3 < KS) {
+                ka1 = kread(s + 3, 0);
+                kb1 = kread(s + 3, 1);
             }
         }
-        float mx = s[0];
+        // keys past the split end are not visible
+        const int lim = hi - (lo + st * SK);
+        float sv[8];
 #pragma unroll
-        for (int r = 1; r < 16; ++r)
-            mx = fmaxf(mx, s[r]);
-        mx = mla_pair_max(mx) * a.c;
+        for (int r = 0; r < 4; ++r) {
+            sv[r] = kofs[0][r] < lim ? s0[r] : -INFINITY;
+            sv[4 + r] = kofs[1][r] < lim ? s1[r] : -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mx = fmaxf(mx, fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        mx = mla_quad_max(mx) * a.c;
         seen = fmaxf(seen, mx);
         if (!have_mu) {
             mu = fabsf(mx) < INFINITY ? mx : 0.f;
             have_mu = true;
         }
-        bf16x8 pb[2];
+        // P^T operand: k slot 8 g + e is key kofs[e / 4][e % 4]
+        bf16x8 pb;
         float lb0 = 0.f, lb1 = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -mu));
-            pb[r >> 3][r & 7] = (__bf16)pr;
-            if (r & 1)
+        for (int e = 0; e < 8; ++e) {
+            const float pr = __builtin_amdgcn_exp2f(fmaf(sv[e], a.c, -mu));
+            pb[e] = (__bf16)pr;
+            if (e & 1)
                 lb1 += pr;
             else
                 lb0 += pr;
         }
         l_run += lb0 + lb1;
-        // O^T[d][row] += sum_key V[key][d] P[row][key]: the V^T operand of
-        // tile t (channels 256 half + 32 t .. +31), chunk cc, half hr: lane (G16,
-        // a4, j4) points at key 16 cc + 8 hr + 4 (G16 / 2) + j4, channels
-        // 32 t + 16 (G16 & 1) + 4 a4 .. +3; the same key order as the P
-        // operand, so the sum is unchanged.  Operands one tile ahead.
-        auto vread = [&](int t, int cc, int hr) {
-            const int c = (256 * half + 32 * t + 16 * (G16 & 1) + 4 * a4) >> 3;
-            const int key = cc * 16 + hr * 8 + 4 * (G16 >> 1) + j4;
-            const char *pv = base + (c >> 3) * (SK * 128) + key * 128 +
-                             (((c & 7) ^ mla_h(key)) * 16) + (a4 & 1) * 8;
-            return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4 *)pv);
+        // O^T[d][row] += sum_key V[key][d] P[row][key], V operands two tiles
+        // ahead
+        uint32_t vb[2];
+        const uint32_t vstage = (uint32_t)(uintptr_t)(const MLA_LDS void *)base + half * (4 * SK * 128);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            vb[tt] = vstage + voff[tt];
+            asm volatile("" : "+v"(vb[tt]));
+        }
+        auto vread = [&](int T, int tt) {
+            return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (MLA_LDS i16x4 *)(uintptr_t)(vb[tt] + (T >> 2) * (SK * 128) + (T & 3) * 256));
         };
-        i16x4 vr[2][2][2];
+        i16x4 vr[3][2];
+        vr[0][0] = vread(0, 0);
+        vr[0][1] = vread(0, 1);
+        vr[1][0] = vread(1, 0);
+        vr[1][1] = vread(1, 1);
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-            for (int hr = 0; hr < 2; ++hr)
-                vr[0][cc][hr] = vread(0, cc, hr);
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-            if (t + 1 < DT) {
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-                    for (int hr = 0; hr < 2; ++hr)
-                        vr[(t + 1) & 1][cc][hr] = vread(t + 1, cc, hr);
+        for (int T = 0; T < NT; ++T) {
+            if (T + 2 < NT) {
+                vr[(T + 2) % 3][0] = vread(T + 2, 0);
+                vr[(T + 2) % 3][1] = vread(T + 2, 1);
             }
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                struct {
-                    i16x4 lo, hi;
-                } pair{vr[t & 1][cc][0], vr[t & 1][cc][1]};
-                o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pair), pb[cc],
-                                                               o[t], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // LDS reads of tile t + 1
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMAs of tile t
+            struct {
+                i16x4 lo, hi;
+            } pair{vr[T % 3][0], vr[T % 3][1]};
+            o[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pair), pb, o[T], 0, 0, 0);
         }
     };
+    // Wait until stage st has landed, given that the k stages after it have
+    // been issued since (every stage but the last is full).  Only the loading
+    // waves have loads outstanding.
+    auto wait_stage = [&](int st, int k) {
+        if (k >= 2 && st + 2 < ns - 1)
+            mla_wait_vmcnt<2 * LPW>();
+        else if (k >= 1 && st + 1 < ns - 1)
+            mla_wait_vmcnt<LPW>();
+        else
+            mla_wait_vmcnt<0>();
+    };
 
+    // Per pass: stages 0 .. NBUF - 2 are issued up front; block u waits for
+    // stage u, and once every wave is past the barrier, stage u + NBUF - 1
+    // goes into the buffer block u - 1 has left.
+    static_assert(NBUF == 4, "three stages ahead");
     __shared__ int redo_flag;
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                o[t][r] = 0.f;
+        for (int T = 0; T < NT; ++T)
+            o[T] = f32x4{0.f, 0.f, 0.f, 0.f};
         l_run = 0.f;
         for (int st = 0; st < NBUF - 1 && st < ns; ++st)
             issue(st);
-        for (int st = 0; st < ns; ++st) {
-            // stage st complete once at most the loads of stage st + 1 (a full
-            // stage) are outstanding; all of them when st + 1 is the last
-            if (st + 1 < ns - 1)
-                mla_wait_vmcnt<LPW>();
-            else
-                mla_wait_vmcnt<0>();
+        for (int u = 0; u < ns; ++u) {
+            wait_stage(u, (u + 2 < ns ? u + 2 : ns - 1) - u);
             __syncthreads();
-            if (st + NBUF - 1 < ns)
-                issue(st + NBUF - 1);
-            compute(st);
+            if (u + NBUF - 1 < ns)
+                issue(u + NBUF - 1);
+            compute(u);
         }
         // repeat with the exact row max when some row passed mu + 64 (the
         // decision is the workgroup's: the stages are shared)
@@ -346,21 +383,16 @@ __global__ void __launch_bounds__(256, 1) k_mla_prefix(MlaArgs a) {
         __syncthreads();    // every wave is done with the stages before they refill
     }
 
-    const float lt = mla_pair_sum(l_run);
+    const float lt = mla_quad_sum(l_run);
     if (row_ok) {
         const int r = m / a.Hq, hh = m % a.Hq;
         const int64_t row = ((int64_t)b * a.R + r) * a.Hq + hh;
         const float inv = lt != 0.f ? 1.f / lt : 0.f;
-        float *dst = a.ws_o + (row * a.n_split + split) * 512 + 256 * half;
+        float *dst = a.ws_o + (row * a.n_split + split) * 512 + 256 * half + 4 * g;
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = 32 * t + 16 * (q4 >> 1) + 8 * (q4 & 1) + 4 * hl;
-                *(float4 *)(dst + d) = make_float4(o[t][4 * q4] * inv, o[t][4 * q4 + 1] * inv,
-                                                   o[t][4 * q4 + 2] * inv, o[t][4 * q4 + 3] * inv);
-            }
-        if (hl == 0 && half == 0)
+        for (int T = 0; T < NT; ++T)
+            *(float4 *)(dst + 16 * T) = make_float4(o[T][0] * inv, o[T][1] * inv, o[T][2] * inv, o[T][3] * inv);
+        if (g == 0 && half == 0)
             a.ws_lse[row * a.n_split + split] = lt != 0.f ? mu + __log2f(lt) : -INFINITY;
     }
 }
@@ -523,6 +555,14 @@ MlaPlan mla_plan(int B, int R, int Hq, int max_prefix_len, int page_size) {
     const int by_keys = max_prefix_len / 128;            // >= 4 stages per split
     n = n < by_keys ? n : by_keys;
     n = n < 1 ? 1 : n;
+    // a multiple of 8 (request, split) streams keeps the eight XCDs equally
+    // busy (each stream lives on one XCD); take one if it costs at most twice
+    // the splits
+    for (int m = n; m <= 2 * n && m <= by_keys; ++m)
+        if (((long long)B * m) % 8 == 0) {
+            n = m;
+            break;
+        }
     int kps;
     for (;;) {
         kps = (max_prefix_len + n - 1) / n;
@@ -628,12 +668,12 @@ extern "C" tav_status tree_attention_mla(const void *q, const void *latent, tav_
     a.out = (uint16_t *)out;
     a.lse2 = lse2;
     if (max_prefix_len > 0) {
-        const long long units = (long long)B * p.RG * p.n_split;
-        const unsigned grid = (unsigned)(((units + 7) / 8) * 16);
+        const long long streams = (long long)B * p.n_split;
+        const unsigned grid = (unsigned)(((streams + 7) / 8) * 8 * 2 * p.RG);
         if (Dr == 64)
-            hipLaunchKernelGGL(k_mla_prefix<64>, dim3(grid), dim3(256), 0, MS(stream), a);
+            hipLaunchKernelGGL(k_mla_prefix<64>, dim3(grid), dim3(512), 0, MS(stream), a);
         else
-            hipLaunchKernelGGL(k_mla_prefix<0>, dim3(grid), dim3(256), 0, MS(stream), a);
+            hipLaunchKernelGGL(k_mla_prefix<0>, dim3(grid), dim3(512), 0, MS(stream), a);
         tav_status st = tav::launched("tree_attention_mla");
         if (st != TAV_OK)
             return st;
