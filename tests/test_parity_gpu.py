@@ -427,7 +427,7 @@ def test_chain_equals_causal():
 # full workload sizes, sampled rows
 # ---------------------------------------------------------------------------
 
-FULL = ["random16", "eagle64", "long64", "lanes", "chain8", "long64_fp8"]
+FULL = ["random16", "eagle64", "long64", "lanes", "chain8", "long64_fp8", "chain8_fp8"]
 
 
 @pytest.mark.parametrize("name", FULL)

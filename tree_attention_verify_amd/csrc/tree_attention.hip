@@ -261,8 +261,21 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
     constexpr int ROWS_WG = NRB * 32;
     constexpr int KSTEPS = D / 16;
     constexpr int DT = D / 32;                    // 32-wide d tiles
+    // FP8 rows of 128 channels are staged raw by direct-to-LDS loads: a stage
+    // is SK rows of K, then SK rows of V, D bytes each
+    // (a 4-wave workgroup keeps two raw stages, 64 KB, so that two workgroups
+    // share a CU and each SIMD runs two waves; wider workgroups fill the CU
+    // alone and keep up to eight)
+    constexpr bool KVD = KV8 && D == 128;
+    constexpr int SB8 = SK * D * 2;
+    constexpr int NB8A = (THREADS <= 256 ? 64 * 1024 : kLdsStageBudget) / SB8;
+    constexpr int NBUF8 = NB8A > 8 ? 8 : NB8A;
+    constexpr int LPS8 = SB8 / (THREADS * 16);    // 16-byte loads per thread per raw stage
+    static_assert(!KVD || (NBUF8 >= 2 && LPS8 >= 1 && SB8 % (THREADS * 16) == 0 &&
+                           (NBUF8 - 2) * LPS8 < 64), "fp8 stage split");
+    constexpr int LDSB = KVD ? NBUF8 * SB8 : NBUF * SB;
 
-    __shared__ __attribute__((aligned(16))) char lds[NBUF * SB];
+    __shared__ __attribute__((aligned(16))) char lds[LDSB];
     __shared__ int32_t pt[kPtMax];
 
     const int tid = threadIdx.x;
@@ -294,7 +307,7 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
     // consecutive keys) share a page, so loads take a wave-uniform page base;
     // stages then start at the 8-key boundary at or below the split start and
     // keys outside [lo, hi) are neither loaded nor visible.
-    const bool wave_pages = !KV8 && a.ps_shift >= 3;
+    const bool wave_pages = (!KV8 || KVD) && a.ps_shift >= 3;
     const int kb0 = wave_pages ? (kr.lo & ~7) : kr.lo;
     const int nkeys = kr.hi > kr.lo ? kr.hi - kb0 : 0;
     const int ns = (nkeys + SK - 1) / SK;
@@ -309,13 +322,46 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
         pt[i] = (int32_t)clamp_page(a.page_table[(int64_t)b * a.max_pages + lp0 + i], a.num_pages);
     // zero the stage buffers once: the last, partial stage leaves rows unloaded
     // and they must hold finite values (their softmax weight is exactly 0)
-    for (int i = tid; i < NBUF * SB / 16; i += THREADS)
+    for (int i = tid; i < LDSB / 16; i += THREADS)
         reinterpret_cast<int4 *>(lds)[i] = make_int4(0, 0, 0, 0);
 
-    // Q^T operand in registers: lane (row n = l32, half hl) holds
-    // Q[row][16 kk + 8 hl .. +8] for each k step.
-    bf16x8 qv[KSTEPS];
-    {
+    // Q^T operand in registers.  bf16 (and FP8 heads of 64 channels, with the
+    // query rounded to E4M3 and held as bf16): lane (row n = l32, half hl)
+    // holds Q[row][16 kk + 8 hl .. +8] for each k step.  FP8 heads of 128
+    // channels: the query rounded to E4M3 and packed, lane holding
+    // Q[row][64 kk + 32 hl .. +32] per 64-channel step, the byte order of the
+    // K operand (the FP8 product pairs the two operands byte by byte).
+    typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+    bf16x8 qv[KVD ? 1 : KSTEPS];
+    i32x8 qv8[KVD ? 2 : 1];
+    if constexpr (KVD) {
+        const int m = rows_base + l32;
+        const bool ok = m < a.M;
+        const int r = ok ? m / a.G : 0, hh = ok ? m % a.G : 0;
+        const uint16_t *qrow = (const uint16_t *)a.q +
+                               (((int64_t)b * a.R + r) * a.Hq + (int64_t)g * a.G + hh) * D;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int4 v4 = ok ? *(const int4 *)(qrow + 64 * kk + 32 * hl + 8 * c) : make_int4(0, 0, 0, 0);
+                typedef __attribute__((__vector_size__(8 * sizeof(uint16_t)))) uint16_t u16x8;
+                const u16x8 u = __builtin_bit_cast(u16x8, v4);
+                float f[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    f[e] = round_e4m3(bf16_bits_to_f32(u[e]));
+                // exact: every value is an E4M3 value
+                int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+                lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+                int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+                hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+                qv8[kk][2 * c] = lo;
+                qv8[kk][2 * c + 1] = hi;
+            }
+            settle(qv8[kk]);
+        }
+    } else {
         const int m = rows_base + l32;
         const bool ok = m < a.M;
         const int r = ok ? m / a.G : 0, hh = ok ? m % a.G : 0;
@@ -402,14 +448,70 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
         }
     };
 
-    // FP8 E4M3 caches: each thread loads its 16-byte chunks (16 values of one
-    // row) of a stage into registers and converts them into the bf16 stage
-    // layout above, so the MFMA code is the bf16 code.  Two register sets
-    // (stage x in set x & 1) keep two stages in flight: as many bytes as one
-    // bf16 stage, twice the keys.
+    // FP8 E4M3 rows of 128 channels: load i of wave w is load I = i WAVES + w
+    // of the raw stage, region I / (SK / 8) (K, then V), keys 8 (I % (SK / 8))
+    // .. +7 of the stage; lane l takes key + l / 8 and 16-byte position l % 8,
+    // which holds chunk position ^ xk8(key) in a K row and position ^
+    // yv8(key) in a V row.  Each load reads eight whole 128-byte rows.  The
+    // swizzles depend on the key modulo 16 only, so a lane has one offset per
+    // region and key-group parity.  xk8 puts the 32 keys of a K operand read
+    // (one chunk) on every 16-byte bank slot twice; yv8 puts the 8 keys x 2
+    // chunks (c and c + 4) of a 32-lane transposing V read on 16 distinct
+    // slots.
+    auto xk8s = [](int k) { return (k >> 1) & 7; };
+    auto yv8s = [](int k) { return ((k >> 1) & 1) | ((k >> 2) & 2); };
+    uint32_t loff8[2][2];
+#pragma unroll
+    for (int rg8 = 0; rg8 < 2; ++rg8)
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            const int key = 8 * par + (lane >> 3), pos = lane & 7;
+            const int c = pos ^ (rg8 ? yv8s(key) : xk8s(key));
+            loff8[rg8][par] = (uint32_t)((lane >> 3) * a.stride_token + c * 16);
+        }
+    auto issue8d = [&](int st) {
+        const uint32_t sbase = lds0 + (uint32_t)((st % NBUF8) * SB8);
+        const int kst = kb0 + st * SK;
+        // the page of each load's key group, all read before the first load
+        int32_t pg8[LPS8];
+#pragma unroll
+        for (int i = 0; i < LPS8; ++i) {
+            const int k0 = kst + 8 * ((i * (THREADS / 64) + w) % (SK / 8));
+            pg8[i] = wave_pages && k0 < kr.hi ? pt[(k0 >> a.ps_shift) - lp0] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < LPS8; ++i) {
+            const int I = i * (THREADS / 64) + w;                   // wave-uniform
+            const int region = I / (SK / 8), kg8 = I % (SK / 8);
+            const int k0 = kst + 8 * kg8;
+            if (k0 >= kr.hi)
+                continue;
+            const int t = k0 + (lane >> 3);
+            const bool in = (k0 >= kr.lo && k0 + 8 <= kr.hi) || (t >= kr.lo && t < kr.hi);
+            const uint32_t dst = sbase + (uint32_t)(region * SK * D + kg8 * 1024);
+            const uint8_t *src = (const uint8_t *)(region ? a.v : a.k) + (int64_t)g * a.stride_head;
+            if (wave_pages) {
+                const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(pg8[i]) * a.stride_page +
+                                    (int64_t)(k0 & ps_mask) * a.stride_token;
+                if (in)
+                    dma_load16_s(src + off, loff8[region][kg8 & 1], dst);
+            } else if (in) {
+                const int key = 8 * kg8 + (lane >> 3);
+                const int c = (lane & 7) ^ (region ? yv8s(key) : xk8s(key));
+                dma_load16(src + (int64_t)pt[(t >> a.ps_shift) - lp0] * a.stride_page +
+                               (int64_t)(t & ps_mask) * a.stride_token + c * 16,
+                           dst);
+            }
+        }
+    };
+
+    // FP8 E4M3 rows of 64 channels: each thread loads its 16-byte chunks (16
+    // values of one row) of a stage into registers and converts them into the
+    // bf16 stage layout above, so the MFMA code is the bf16 code.  Two
+    // register sets (stage x in set x & 1) keep two stages in flight.
     constexpr int C8 = D / 16;                                // 16-byte chunks per fp8 row
-    constexpr int LP8 = KV8 ? 2 * SK * C8 / THREADS : 1;      // chunks per thread and stage
-    static_assert(!KV8 || (2 * SK * C8) % THREADS == 0, "fp8 slot split");
+    constexpr int LP8 = (KV8 && !KVD) ? 2 * SK * C8 / THREADS : 1;   // chunks per thread and stage
+    static_assert(!KV8 || KVD || (2 * SK * C8) % THREADS == 0, "fp8 slot split");
     int4 f8a[LP8], f8b[LP8];
     // Every load is issued, also for stages past the last one (keys at or
     // past the split end re-read its last key and are zeroed at conversion):
@@ -466,7 +568,10 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
         convert8(st + 1, f8);
         load8(st + 3, f8);
     };
-    if constexpr (KV8) {
+    if constexpr (KVD) {
+        for (int st = 0; st < NBUF8 - 1 && st < ns; ++st)
+            issue8d(st);
+    } else if constexpr (KV8) {
         if (ns > 0) {
             load8(0, f8a);
             load8(1, f8b);
@@ -484,20 +589,34 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
     const int ksw = swz<D>(krow);
     // one stage of keys: S, softmax weights and O for this wave's 32 keys
     auto compute = [&](int it) {
-        const char *Kb = lds + (it % NBUF) * SB;
-        const char *Vb = Kb + SB / 2;
+        const char *Kb = KVD ? lds + (it % NBUF8) * SB8 : lds + (it % NBUF) * SB;
+        const char *Vb = KVD ? Kb + SK * D : Kb + SB / 2;
         const int first = kb0 + it * SK + key0;  // absolute key of this wave's block
         if (first >= kr.hi)
             return;
-        // S^T[key][row] = sum_d K[key][d] Q[row][d]
+        // S^T[key][row] = sum_d K[key][d] Q[row][d]; FP8 rows: two E4M3 x
+        // E4M3 steps of 64 channels (unit block scales), lane (key l32, half
+        // hl) reading chunks 4 kk + 2 hl + e of its key row
         f32x16 s;
+        if constexpr (KVD) {
+            const char *kr0 = Kb + krow * D;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            s[r] = 0.f;
+            for (int kk = 0; kk < 2; ++kk) {
+                const int4 x0 = *(const int4 *)(kr0 + (((4 * kk + 2 * hl) ^ xk8s(krow)) * 16));
+                const int4 x1 = *(const int4 *)(kr0 + (((4 * kk + 2 * hl + 1) ^ xk8s(krow)) * 16));
+                const i32x8 ka = i32x8{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qv8[kk], kk ? s : f32x16{}, 0, 0, 0,
+                                                                    127, 0, 127);
+            }
+        } else {
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-            const bf16x8 ka = *(const bf16x8 *)(Kb + krow * ROWB + (((2 * kk + hl) ^ ksw) * 16));
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[kk], s, 0, 0, 0);
+            for (int r = 0; r < 16; ++r)
+                s[r] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk) {
+                const bf16x8 ka = *(const bf16x8 *)(Kb + krow * ROWB + (((2 * kk + hl) ^ ksw) * 16));
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[kk], s, 0, 0, 0);
+            }
         }
         // keys outside the split are not visible
         if (first < kr.lo || first + 32 > kr.hi) {
@@ -545,6 +664,39 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
         // hr: lane (G16, a4, j4) points at key key0 + 16 cc + 8 hr + 4 (G16/2)
         // + j4, channels d0 .. d0 + 3; the 16-lane group's read transposes
         // the 4 keys x 4 channels.
+        if constexpr (KVD) {
+            // FP8 rows: V^T operand of d tile t (channels 16 t .. +15 and
+            // D / 2 + 16 t .. +15, as for bf16 rows), chunk cc, by one
+            // transposing byte read per lane and a widening to bf16.  Lane j
+            // of 16-lane group G16 points at key key0 + 16 cc + 4 hl + (e & 3)
+            // + 8 (e >> 2), e = j / 2, bytes 8 (j & 1) .. +7 of chunk (G16 &
+            // 1) D / 32 + t; the read hands lane i byte i % 8 of lanes 2 e + i
+            // / 8, i.e. channel (G16 & 1) D / 2 + 16 t + i of the 8 keys, in
+            // the key order of the P operand.
+            typedef __attribute__((ext_vector_type(2))) int v2i;
+            const int e8 = (lane & 15) >> 1;
+            const int vkey = key0 + 4 * hl + (e8 & 3) + 8 * (e8 >> 2);
+            const int vy = yv8s(vkey);
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                const int vc = ((G16 & 1) * (D / 32) + t) ^ vy;
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    const char *p = Vb + (vkey + 16 * cc) * D + vc * 16 + 8 * (lane & 1);
+                    const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i *)p);
+                    auto w0 = [](int x) {
+                        return __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)x, 1.0f, false));
+                    };
+                    auto w1 = [](int x) {
+                        return __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)x, 1.0f, true));
+                    };
+                    const int4 w4 = make_int4(w0(r.x), w1(r.x), w0(r.y), w1(r.y));
+                    o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w4), pb[cc], o[t],
+                                                                   0, 0, 0);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
             const int d0 = ((G16 & 1) ? D / 2 : 0) + 16 * t + 4 * a4;
@@ -567,7 +719,20 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
         }
     };
 
-    if constexpr (KV8) {
+    if constexpr (KVD) {
+        for (int it = 0; it < ns; ++it) {
+            // as for bf16 rows: stage `it` is complete once at most the loads
+            // of the later, full stages are outstanding
+            if (it + NBUF8 - 2 < ns - 1)
+                wait_vmcnt<(NBUF8 - 2) * LPS8>();
+            else
+                wait_vmcnt<0>();
+            __syncthreads();
+            if (it + NBUF8 - 1 < ns)
+                issue8d(it + NBUF8 - 1);
+            compute(it);
+        }
+    } else if constexpr (KV8) {
         // Stage it was converted in the previous trip; after the barrier no
         // wave reads the buffer stage it + 1 is converted into.  Unrolled by
         // two so each trip names its register set statically; a trip past
