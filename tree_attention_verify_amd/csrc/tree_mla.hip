@@ -10,17 +10,15 @@
 //
 // Kernels:
 //   k_mla_prefix<DR>  split-K prefix decode.  One workgroup of 8 waves (two
-//       per SIMD, at most 256 registers each) owns 128 folded rows, a wave
-//       16, and one half of the Dc = 512 value channels; per 32-key block a
-//       wave runs S^T = K Q^T for two 16-key tiles over the Dc + Dr channels
-//       (2 x 18 steps of v_mfma_f32_16x16x32_bf16 for Dr = 64) and O^T +=
-//       V^T P^T over its 256 value channels (16 tiles, one step each).  The
-//       two channel halves of a (request, row group, split) are separate
-//       workgroups on one XCD and compute the same scores: the query (576
-//       channels) and a whole 512-channel accumulator of 16 rows would not
-//       fit one wave's 256 registers.  Latent rows stream HBM -> LDS with
-//       direct-to-LDS 16-byte loads, four stages deep; the same LDS bytes
-//       are read as the K operand and, transposed, as the V operand.
+//       per SIMD, at most 256 registers each) owns 64 folded rows and all
+//       Dc = 512 value channels.  Per 32-key block each wave first scores one
+//       16-row x 16-key tile over the Dc + Dr channels (18 steps of
+//       v_mfma_f32_16x16x32_bf16 for Dr = 64, the query of its 16 rows in
+//       registers) and writes its bf16 weights to LDS; after a barrier each
+//       wave accumulates O^T += V^T P^T for 64 value channels of all 64 rows
+//       (16 MFMAs).  Every score is computed once.  Latent rows stream HBM ->
+//       LDS with direct-to-LDS 16-byte loads, four stages deep; the same LDS
+//       bytes are read as the K operand and, transposed, as the V operand.
 //   k_mla_window_merge<DR>  one wave per (request, row, head): the masked
 //       window keys (never the unseen ones) with lanes over channels, then
 //       the merge of the prefix partials through their base-2 LSE.
@@ -115,36 +113,38 @@ struct MlaCfg {
     static constexpr int DK = DC + DR;
     static constexpr int KS = DK / 32;             // 32-channel score steps
     static constexpr int NG = DK / 64;             // 8-chunk groups per row
-    static constexpr int NT = DC / 2 / 16;         // 16-channel value tiles per channel half
     static constexpr int SK = 32;                  // keys per stage
     static constexpr int SB = NG * SK * 128;       // stage bytes
     static constexpr int NBUF = 4;
     static constexpr int LOADS = NG * SK * 8 / 64; // load instructions per stage (64 lanes each)
     static constexpr int LPW = LOADS / 4;          // per loading wave (waves 0..3)
-    static_assert(DK % 64 == 0 && LOADS % 4 == 0 && LPW == NG && KS % 2 == 0, "row shape");
-    static_assert(NBUF * SB + kMlaPt * 4 <= 160 * 1024, "LDS");
+    static constexpr int PB = 64 * SK * 2;         // bf16 weights of a block: 64 rows x 32 keys
+    static_assert(DK % 64 == 0 && LOADS % 4 == 0 && LPW == NG && KS >= 4, "row shape");
+    static_assert(NBUF * SB + PB + kMlaPt * 4 + 3 * 2 * 64 * 4 <= 160 * 1024, "LDS");
 };
 
 template <int DR>
 __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
     using C = MlaCfg<DR>;
-    constexpr int DK = C::DK, KS = C::KS, NT = C::NT, SK = C::SK, SB = C::SB,
-                  NBUF = C::NBUF, LPW = C::LPW;
+    constexpr int DK = C::DK, KS = C::KS, SK = C::SK, SB = C::SB, NBUF = C::NBUF, LPW = C::LPW;
     __shared__ __attribute__((aligned(16))) char lds[NBUF * SB];
+    __shared__ __attribute__((aligned(16))) char pbuf[C::PB];
     __shared__ int32_t pt[kMlaPt];
+    __shared__ float xrow[3][2][64];   // per-row exchange between the two key tiles
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, i16 = lane & 15;
-    // A stream U = (request, split) has 2 RG workgroups (row group, channel
-    // half), j = 2 rg + half; they take blocks 8 (2 RG (U / 8) + j) + U % 8.
-    // Blocks are dealt to the eight XCDs in turn, so every reader of a
-    // stream's latent rows sits on XCD U % 8 and one L2 serves them all.
+    // Score role: row tile rt (16 rows) x key tile kt (16 keys of each block).
+    // Value role: channels 64 w .. 64 w + 63 for all 64 rows.
+    const int rt = w & 3, kt = w >> 2;
+    // A stream U = (request, split) has RG workgroups (64-row groups); they
+    // take blocks 8 (RG (U / 8) + rg) + U % 8.  Blocks are dealt to the eight
+    // XCDs in turn, so every reader of a stream's latent rows sits on XCD
+    // U % 8 and one L2 serves them all.
     const int id = blockIdx.x;
-    const int per = 2 * a.RG;
-    const int U = ((id >> 3) / per) * 8 + (id & 7);
-    const int j = (id >> 3) % per;
-    const int rg = j >> 1, half = j & 1;
+    const int U = ((id >> 3) / a.RG) * 8 + (id & 7);
+    const int rg = (id >> 3) % a.RG;
     if (U >= a.B * a.n_split)
         return;   // uniform per workgroup, before any barrier
     const int split = U % a.n_split;
@@ -168,9 +168,9 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
     for (int i = tid; i < NBUF * SB / 16; i += 512)
         reinterpret_cast<int4 *>(lds)[i] = make_int4(0, 0, 0, 0);
 
-    // Q^T operand of score step s: lane (g, i16) holds Q[row i16 of the
-    // wave][32 s + 8 g .. +8]
-    const int m = rg * 128 + w * 16 + i16;
+    // Q^T operand of score step s: lane (g, i16) holds Q[row 16 rt + i16 of
+    // the group][32 s + 8 g .. +8]
+    const int m = rg * 64 + rt * 16 + i16;
     const bool row_ok = m < a.M;
     bf16x8 qv[KS];
     {
@@ -210,131 +210,104 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
         }
     };
 
-    // Per-lane operand offsets inside a stage.  K operand of step s, tile tt:
-    // lane (g, i16) reads key 16 tt + i16, chunk 4 s + g: block (s / 2, key /
-    // 8), pair run 2 (s % 2) + g / 2, parity g % 2.  The step parts are
-    // immediates, koff[tt] the rest.
-    uint32_t koff[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        const int key = 16 * tt + i16;
-        koff[tt] = (uint32_t)((key >> 3) * 1024 + ((g >> 1) * 16 + (g & 1) * 8 + (key & 7)) * 16);
+    // K operand of step s (score role): lane (g, i16) reads key 16 kt + i16,
+    // chunk 4 s + g: block (s / 2, key / 8), pair run 2 (s % 2) + g / 2,
+    // parity g % 2; the step parts are immediates.
+    uint32_t koff;
+    {
+        const int key = 16 * kt + i16;
+        koff = (uint32_t)((key >> 3) * 1024 + ((g >> 1) * 16 + (g & 1) * 8 + (key & 7)) * 16);
     }
-    // V^T operand of value tile T (channels 256 half + 16 T .. +15), key tile
-    // tt: lane (g, j4 = i16 / 4, a4 = i16 % 4) points at key 16 tt + 4 g +
-    // j4, channels 16 T + 4 a4 .. +3 (chunk 32 half + 2 T + a4 / 2); the
-    // transposing read hands lane i16 channel i16 of those four keys, in the
-    // order of the P operand.  Block (4 half + T / 4, key / 8) and pair run
-    // T % 4 are immediates, voff[tt] the rest.
+    // The weights of a block in LDS: [row tile][k group g][row i16] 16-byte
+    // chunks, k slot 8 g + e holding key 4 g + e (e < 4) or 16 + 4 g + e - 4
+    // (e >= 4).  A score lane (g, i16) of key tile kt holds exactly keys 16 kt
+    // + 4 g .. +3 of row 16 rt + i16, i.e. half e / 4 = kt of its chunk; a
+    // value lane (g, i16) reads the whole chunk (row tile, g, i16), which is
+    // the P^T operand of k slots 8 g .. +7 (16 lanes read 256 contiguous
+    // bytes).
+    const uint32_t pw_off = (uint32_t)(rt * 1024 + g * 256 + i16 * 16 + kt * 8);
+    const uint32_t pr_off = (uint32_t)(g * 256 + i16 * 16);
+    // V^T operand of channel tile ct (channels 64 w + 16 ct .. +15), half tt:
+    // lane (g, j4 = i16 / 4, a4 = i16 % 4) points at key 16 tt + 4 g + j4,
+    // channels 64 w + 16 ct + 4 a4 .. +3 (chunk 8 w + 2 ct + a4 / 2); the
+    // transposing read hands lane i16 channel i16 of those four keys, k slots
+    // 8 g + 4 tt .. +3 of the P operand.  Block (w, key / 8) is part of the
+    // offset, the pair run ct an immediate.
     uint32_t voff[2];
     {
         const int j4 = i16 >> 2, a4 = i16 & 3;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const int key = 16 * tt + 4 * g + j4;
-            voff[tt] = (uint32_t)((key >> 3) * 1024 + ((a4 >> 1) * 8 + (key & 7)) * 16 + (a4 & 1) * 8);
+            voff[tt] = (uint32_t)(w * (SK * 128) + (key >> 3) * 1024 + ((a4 >> 1) * 8 + (key & 7)) * 16 +
+                                  (a4 & 1) * 8);
         }
     }
-    // key of score value r of tile tt held by this lane, relative to the block
-    int kofs[2][4];
+
+    f32x4 o[4][4];   // [channel tile][row tile]
+    float mu = 0.f, l_part = 0.f, seen = -INFINITY;
+
+    // S^T[key][row] of this wave's tile over the Dc + Dr channels, four K
+    // operands in flight; keys past the split end are -inf.
+    auto score = [&](int st) {
+        const char *kb = lds + (st % NBUF) * SB + koff;
+        auto kread = [&](int s) { return *(const bf16x8 *)(kb + (s >> 1) * (SK * 128) + (s & 1) * 512); };
+        f32x4 sc;
+        bf16x8 k0 = kread(0), k1 = kread(1), k2 = kread(2), k3 = kread(3);
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+        for (int s = 0; s < KS; s += 4) {
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qv[s], s ? sc : f32x4{}, 0, 0, 0);
+            if (s + 4 < KS)
+                k0 = kread(s + 4);
+            if (s + 1 < KS) {
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qv[s + 1], sc, 0, 0, 0);
+                if (s + 5 < KS)
+                    k1 = kread(s + 5);
+            }
+            if (s + 2 < KS) {
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k2, qv[s + 2], sc, 0, 0, 0);
+                if (s + 6 < KS)
+                    k2 = kread(s + 6);
+            }
+            if (s + 3 < KS) {
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k3, qv[s + 3], sc, 0, 0, 0);
+                if (s + 7 < KS)
+                    k3 = kread(s + 7);
+            }
+        }
+        const int lim = hi - (lo + st * SK) - 16 * kt - 4 * g;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            kofs[tt][r] = 16 * tt + 4 * g + r;
-
-    f32x4 o[NT];
-    float mu = 0.f, l_run = 0.f, seen = -INFINITY;
-    bool have_mu = false;
-
-    // One 32-key block.  The weights are exp2(s c - mu) with mu fixed for the
-    // whole pass: the first block's row max in the first pass.  Later keys
-    // may exceed it; up to 2^64 the weights and their sums stay far inside
-    // fp32 range and keep full relative precision.  When a row's max passes
-    // mu + 64 the pass is repeated with mu = that row's max over the split
-    // (then every weight is <= 1), so the accumulator is never rescaled.
-    auto compute = [&](int st) {
-        const char *base = lds + (st % NBUF) * SB;
-        // S^T[key][row] of the two key tiles over the Dc + Dr channels, four
-        // K operands in flight
-        const char *kb[2] = {base + koff[0], base + koff[1]};
-        auto kread = [&](int s, int tt) {
-            return *(const bf16x8 *)(kb[tt] + (s >> 1) * (SK * 128) + (s & 1) * 512);
-        };
-        f32x4 s0, s1;
-        bf16x8 ka0 = kread(0, 0), kb0 = kread(0, 1), ka1 = kread(1, 0), kb1 = kread(1, 1);
+            sc[r] = r < lim ? sc[r] : -INFINITY;
+        return sc;
+    };
+    // row max of this wave's 16 keys (over the four lane groups), exchanged
+    // with the other key tile through xrow[slot]; a workgroup barrier inside
+    auto row_max_both = [&](float mx, int slot) {
+        mx = mla_quad_max(mx);
+        if (g == 0)
+            xrow[slot][kt][rt * 16 + i16] = mx;
+        __syncthreads();
+        return fmaxf(mx, xrow[slot][kt ^ 1][rt * 16 + i16]);
+    };
+    // O^T[d][row] += sum_key V[key][d] P[row][key] for this wave's 64 channels
+    // and all 64 rows
+    auto pv = [&](int st) {
+        const uint32_t vb = (uint32_t)(uintptr_t)(const MLA_LDS void *)(lds + (st % NBUF) * SB);
+        bf16x8 pr[4];
 #pragma unroll
-        for (int s = 0; s < KS; s += 2) {
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qv[s], s ? s0 : f32x4{}, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb0, qv[s], s ? s1 : f32x4{}, 0, 0, 0);
-            if (s + 2 < KS) {
-                ka0 = kread(s + 2, 0);
-                kb0 = kread(s + 2, 1);
-            }
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qv[s + 1], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb1, qv[s + 1], s1, 0, 0, 0);
-            if (s + 3 < KS) {
-                ka1 = kread(s + 3, 0);
-                kb1 = kread(s + 3, 1);
-            }
-        }
-        // keys past the split end are not visible
-        const int lim = hi - (lo + st * SK);
-        float sv[8];
+        for (int t4 = 0; t4 < 4; ++t4)
+            pr[t4] = *(const bf16x8 *)(pbuf + t4 * 1024 + pr_off);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            sv[r] = kofs[0][r] < lim ? s0[r] : -INFINITY;
-            sv[4 + r] = kofs[1][r] < lim ? s1[r] : -INFINITY;
-        }
-        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-        mx = fmaxf(mx, fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        mx = mla_quad_max(mx) * a.c;
-        seen = fmaxf(seen, mx);
-        if (!have_mu) {
-            mu = fabsf(mx) < INFINITY ? mx : 0.f;
-            have_mu = true;
-        }
-        // P^T operand: k slot 8 g + e is key kofs[e / 4][e % 4]
-        bf16x8 pb;
-        float lb0 = 0.f, lb1 = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float pr = __builtin_amdgcn_exp2f(fmaf(sv[e], a.c, -mu));
-            pb[e] = (__bf16)pr;
-            if (e & 1)
-                lb1 += pr;
-            else
-                lb0 += pr;
-        }
-        l_run += lb0 + lb1;
-        // O^T[d][row] += sum_key V[key][d] P[row][key], V operands two tiles
-        // ahead
-        uint32_t vb[2];
-        const uint32_t vstage = (uint32_t)(uintptr_t)(const MLA_LDS void *)base + half * (4 * SK * 128);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            vb[tt] = vstage + voff[tt];
-            asm volatile("" : "+v"(vb[tt]));
-        }
-        auto vread = [&](int T, int tt) {
-            return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (MLA_LDS i16x4 *)(uintptr_t)(vb[tt] + (T >> 2) * (SK * 128) + (T & 3) * 256));
-        };
-        i16x4 vr[3][2];
-        vr[0][0] = vread(0, 0);
-        vr[0][1] = vread(0, 1);
-        vr[1][0] = vread(1, 0);
-        vr[1][1] = vread(1, 1);
-#pragma unroll
-        for (int T = 0; T < NT; ++T) {
-            if (T + 2 < NT) {
-                vr[(T + 2) % 3][0] = vread(T + 2, 0);
-                vr[(T + 2) % 3][1] = vread(T + 2, 1);
-            }
+        for (int ct = 0; ct < 4; ++ct) {
             struct {
                 i16x4 lo, hi;
-            } pair{vr[T % 3][0], vr[T % 3][1]};
-            o[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pair), pb, o[T], 0, 0, 0);
+            } pair{__builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4 *)(uintptr_t)(vb + voff[0] + ct * 256)),
+                   __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4 *)(uintptr_t)(vb + voff[1] + ct * 256))};
+            const bf16x8 va = __builtin_bit_cast(bf16x8, pair);
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4)
+                o[ct][t4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pr[t4], o[ct][t4], 0, 0, 0);
         }
     };
     // Wait until stage st has landed, given that the k stages after it have
@@ -349,16 +322,26 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
             mla_wait_vmcnt<0>();
     };
 
-    // Per pass: stages 0 .. NBUF - 2 are issued up front; block u waits for
-    // stage u, and once every wave is past the barrier, stage u + NBUF - 1
-    // goes into the buffer block u - 1 has left.
+    // The weights are exp2(s c - mu) with mu fixed for a whole pass: the
+    // first block's row max (over both key tiles) in the first pass.  Later
+    // keys may exceed it; up to 2^64 the weights and their sums stay far
+    // inside fp32 range and keep full relative precision.  When a row's max
+    // passes mu + 64 the pass is repeated with mu = that row's max over the
+    // split (then every weight is <= 1), so the accumulator is never
+    // rescaled.  Per block u: wait for stage u; after the barrier (every wave
+    // is done with block u - 1, its stage and the weight buffer) stage u +
+    // NBUF - 1 goes into the buffer block u - 1 has left; the score waves
+    // write the weights; after a second barrier every wave accumulates its
+    // channels.
     static_assert(NBUF == 4, "three stages ahead");
     __shared__ int redo_flag;
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-        for (int T = 0; T < NT; ++T)
-            o[T] = f32x4{0.f, 0.f, 0.f, 0.f};
-        l_run = 0.f;
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4)
+                o[ct][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+        l_part = 0.f;
         for (int st = 0; st < NBUF - 1 && st < ns; ++st)
             issue(st);
         for (int u = 0; u < ns; ++u) {
@@ -366,11 +349,31 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
             __syncthreads();
             if (u + NBUF - 1 < ns)
                 issue(u + NBUF - 1);
-            compute(u);
+            const f32x4 sc = score(u);
+            float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * a.c;
+            if (pass == 0 && u == 0) {
+                mx = row_max_both(mx, 0);
+                mu = fabsf(mx) < INFINITY ? mx : 0.f;
+            } else {
+                mx = mla_quad_max(mx);
+            }
+            seen = fmaxf(seen, mx);
+            typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+            bf16x4 pw;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float pr = __builtin_amdgcn_exp2f(fmaf(sc[r], a.c, -mu));
+                pw[r] = (__bf16)pr;
+                l_part += pr;
+            }
+            *(bf16x4 *)(pbuf + pw_off) = pw;
+            __syncthreads();
+            pv(u);
         }
-        // repeat with the exact row max when some row passed mu + 64 (the
-        // decision is the workgroup's: the stages are shared)
-        const bool need = __ballot(seen > mu + 64.f) != 0;
+        // repeat with the exact row max (over both key tiles) when some row
+        // passed mu + 64; the decision is the workgroup's: the stages are shared
+        const float seen_row = row_max_both(seen, 1);
+        const bool need = __ballot(seen_row > mu + 64.f) != 0;
         if (tid == 0)
             redo_flag = 0;
         __syncthreads();
@@ -379,21 +382,37 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
         __syncthreads();
         if (pass == 1 || redo_flag == 0)
             break;
-        mu = fabsf(seen) < INFINITY ? seen : 0.f;
+        mu = fabsf(seen_row) < INFINITY ? seen_row : 0.f;
         __syncthreads();    // every wave is done with the stages before they refill
     }
 
-    const float lt = mla_quad_sum(l_run);
-    if (row_ok) {
-        const int r = m / a.Hq, hh = m % a.Hq;
+    // the row sums of both key tiles, and mu, for the value waves
+    {
+        const float lq = mla_quad_sum(l_part);
+        if (g == 0) {
+            xrow[2][kt][rt * 16 + i16] = lq;
+            if (kt == 0)
+                xrow[1][0][rt * 16 + i16] = mu;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+        const int mr = rg * 64 + t4 * 16 + i16;
+        if (mr >= a.M)
+            continue;
+        const float lt = xrow[2][0][t4 * 16 + i16] + xrow[2][1][t4 * 16 + i16];
+        const float mur = xrow[1][0][t4 * 16 + i16];
+        const int r = mr / a.Hq, hh = mr % a.Hq;
         const int64_t row = ((int64_t)b * a.R + r) * a.Hq + hh;
         const float inv = lt != 0.f ? 1.f / lt : 0.f;
-        float *dst = a.ws_o + (row * a.n_split + split) * 512 + 256 * half + 4 * g;
+        float *dst = a.ws_o + (row * a.n_split + split) * 512 + 64 * w + 4 * g;
 #pragma unroll
-        for (int T = 0; T < NT; ++T)
-            *(float4 *)(dst + 16 * T) = make_float4(o[T][0] * inv, o[T][1] * inv, o[T][2] * inv, o[T][3] * inv);
-        if (g == 0 && half == 0)
-            a.ws_lse[row * a.n_split + split] = lt != 0.f ? mu + __log2f(lt) : -INFINITY;
+        for (int ct = 0; ct < 4; ++ct)
+            *(float4 *)(dst + 16 * ct) = make_float4(o[ct][t4][0] * inv, o[ct][t4][1] * inv,
+                                                     o[ct][t4][2] * inv, o[ct][t4][3] * inv);
+        if (w == 0 && g == 0)
+            a.ws_lse[row * a.n_split + split] = lt != 0.f ? mur + __log2f(lt) : -INFINITY;
     }
 }
 
@@ -549,7 +568,7 @@ inline size_t mla_align256(size_t x) { return (x + 255) & ~size_t(255); }
 MlaPlan mla_plan(int B, int R, int Hq, int max_prefix_len, int page_size) {
     MlaPlan p{};
     const long long M = (long long)R * Hq;
-    p.RG = (int)((M + 127) / 128);
+    p.RG = (int)((M + 63) / 64);
     const long long base = (long long)B * p.RG;
     int n = base > 0 ? (int)((256 + base - 1) / base) : 1;
     const int by_keys = max_prefix_len / 128;            // >= 4 stages per split
@@ -669,7 +688,7 @@ extern "C" tav_status tree_attention_mla(const void *q, const void *latent, tav_
     a.lse2 = lse2;
     if (max_prefix_len > 0) {
         const long long streams = (long long)B * p.n_split;
-        const unsigned grid = (unsigned)(((streams + 7) / 8) * 8 * 2 * p.RG);
+        const unsigned grid = (unsigned)(((streams + 7) / 8) * 8 * p.RG);
         if (Dr == 64)
             hipLaunchKernelGGL(k_mla_prefix<64>, dim3(grid), dim3(512), 0, MS(stream), a);
         else
