@@ -67,6 +67,10 @@ SMALL = {
     "norope": (gen.MlaWorkload("m", 2, 640, 16, 8, 512, 0, 32), [640, 1]),
     "noprefix": (gen.MlaWorkload("m", 2, 0, 12, 4, 512, 64, 64), [0, 0]),
     "long": (gen.MlaWorkload("m", 1, 9000, 16, 16, 512, 64, 64), [9000]),
+    # 80 folded rows (a second, partial 64-row group), pages of 8 keys
+    "ragged_rows": (gen.MlaWorkload("m", 2, 1500, 5, 16, 512, 64, 8), [1500, 777]),
+    # 15 folded rows, no rotary part, pages of 4 keys, a one-key prefix
+    "tiny": (gen.MlaWorkload("m", 3, 200, 5, 3, 512, 0, 4), [200, 33, 1]),
 }
 
 
