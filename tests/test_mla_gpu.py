@@ -112,3 +112,45 @@ def test_mla_late_dominant_key_repeats_the_pass():
     check(inp, m, out, lse, tag="late dominant key")
     # the dominant key's latent part is the output
     assert torch.allclose(out.float(), torch.full_like(out.float(), 3.0), atol=1e-2)
+
+
+def _same_nonfinite(ours, ref, tol, tag):
+    """Element-wise: where the oracle is finite, ours is finite and within tol;
+    where it is NaN / +inf / -inf, ours is the same."""
+    assert np.array_equal(np.isnan(ours), np.isnan(ref)), tag + ": NaN pattern"
+    assert np.array_equal(np.isposinf(ours), np.isposinf(ref)), tag + ": +inf pattern"
+    assert np.array_equal(np.isneginf(ours), np.isneginf(ref)), tag + ": -inf pattern"
+    fin = np.isfinite(ref)
+    if fin.any():
+        assert np.abs(ours[fin] - ref[fin]).max() <= tol, tag
+
+
+def test_mla_nonfinite_window_rows_reach_only_rows_that_see_them():
+    # NaN in a latent channel of window node j1, NaN in a rotary channel of
+    # j2, +inf in a latent channel of j3 (a score of +inf or -inf depending
+    # on the query's sign, and an infinite value channel): a row is
+    # non-finite exactly where the exact softmax over its visible keys is
+    wl = gen.MlaWorkload("nf", 2, 300, 16, 8, 512, 64, 16)
+    inp = gen.make_mla_inputs(wl, 13, "cuda", prefix_lens=np.array([300, 123]))
+
+    def slot(b, j):
+        t = int(inp.prefix_len[b]) + j
+        return int(inp.page_table[b, t // wl.page_size]), t % wl.page_size
+
+    j1, j2, j3 = 2, 4, 7
+    for b in range(wl.B):
+        pg, sl = slot(b, j1)
+        inp.latent[pg, sl, 17] = float("nan")
+        pg, sl = slot(b, j2)
+        inp.latent[pg, sl, 512 + 9] = float("nan")
+        pg, sl = slot(b, j3)
+        inp.latent[pg, sl, 300] = float("inf")
+    m = oracle.build_masks(inp.parents)["masks"]
+    out, lse = run(inp, m)
+    ro, rl = oracle.mla_attention(gen.bf16_bits(inp.q), gen.bf16_bits(inp.latent), inp.strides,
+                                  inp.page_table, wl.page_size, inp.prefix_len, m, wl.W, wl.Dc, wl.Dr)
+    _same_nonfinite(out.float().cpu().numpy().reshape(ro.shape), ro, OUT_TOL, "mla out")
+    _same_nonfinite(lse.cpu().numpy().reshape(rl.shape), rl, LSE_TOL, "mla lse2")
+    sees = lambda j: ((m.astype(np.uint64) >> np.uint64(j)) & np.uint64(1)).astype(bool)
+    assert sees(j1).any() and sees(j3).any() and (~sees(j1)).any(), "the trees must reach the nodes"
+    assert np.isfinite(ro).any() and not np.isfinite(ro).all()

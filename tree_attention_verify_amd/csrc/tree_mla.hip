@@ -419,9 +419,12 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
 // Window part and merge: one wave per (request b, row r, head h).  The
 // window keys are the set bits j < W of the row's mask at logical position
 // P + j; lane l holds channels 8 l .. 8 l + 7 of the latent part (and, for
-// l < Dr / 8, rotary channels 8 l .. +7).  Online softmax over the window
-// keys, then the merge with the n_split prefix partials:
-// lse2 = log2 sum_k 2^lse2_k, out = sum_k 2^(lse2_k - lse2) o_k.
+// l < Dr / 8, rotary channels 8 l .. +7).  Lane j looks up the latent row of
+// window key j (all page lookups at once); the keys are then taken eight at
+// a time with their row loads in flight together, with an online softmax
+// over the groups.  Then the merge with the n_split prefix partials (their
+// lse2 read at once, one per lane): lse2 = log2 sum_k 2^lse2_k, out = sum_k
+// 2^(lse2_k - lse2) o_k.
 template <int DR>
 __global__ void __launch_bounds__(256) k_mla_window_merge(MlaArgs a) {
     constexpr int DK = 512 + DR;
@@ -433,93 +436,134 @@ __global__ void __launch_bounds__(256) k_mla_window_merge(MlaArgs a) {
     const int b = (int)(row / ((int64_t)a.Hq * a.R));
     int P = a.prefix_len[b];
     P = P < 0 ? 0 : (P > a.max_prefix_len ? a.max_prefix_len : P);
-    const uint16_t *qp = a.q + row * DK;
-    float qc[8], qr[8];
-    {
-        const int4 x = *(const int4 *)(qp + 8 * lane);
+    auto widen = [](const int4 x, float (&f)[8]) {
         const uint32_t u[4] = {(uint32_t)x.x, (uint32_t)x.y, (uint32_t)x.z, (uint32_t)x.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            qc[2 * e] = __uint_as_float(u[e] << 16);
-            qc[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+            f[2 * e] = __uint_as_float(u[e] << 16);
+            f[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
         }
-        int4 y = make_int4(0, 0, 0, 0);
-        if (DR > 0 && lane < DR / 8)
-            y = *(const int4 *)(qp + 512 + 8 * lane);
-        const uint32_t v[4] = {(uint32_t)y.x, (uint32_t)y.y, (uint32_t)y.z, (uint32_t)y.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            qr[2 * e] = __uint_as_float(v[e] << 16);
-            qr[2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+    };
+    const uint16_t *qp = a.q + row * DK;
+    float qc[8], qr[8];
+    widen(*(const int4 *)(qp + 8 * lane), qc);
+    widen(DR > 0 && lane < DR / 8 ? *(const int4 *)(qp + 512 + 8 * lane) : make_int4(0, 0, 0, 0), qr);
+
+    uint64_t bits = a.masks[(int64_t)b * a.R + r];
+    if (a.W < 64)
+        bits &= (1ull << a.W) - 1;
+    // the latent row of window key `lane` (keys whose page falls outside the
+    // table are dropped from the set)
+    const int ps = 1 << a.ps_shift;
+    int64_t myrow = 0;
+    {
+        const int t = P + lane;
+        const int lp = t >> a.ps_shift;
+        const bool set = (bits >> lane) & 1;
+        if (set && lp < a.max_pages) {
+            int64_t pg = a.page_table[(int64_t)b * a.max_pages + lp];
+            pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+            myrow = pg * a.stride_page + (int64_t)(t & (ps - 1)) * a.stride_token;
         }
+        bits &= __ballot(set && lp < a.max_pages);
     }
     float mw = -INFINITY, lw = 0.f, ow[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
         ow[e] = 0.f;
-    uint64_t bits = a.masks[(int64_t)b * a.R + r];
-    if (a.W < 64)
-        bits &= (1ull << a.W) - 1;
-    const int ps = 1 << a.ps_shift;
     while (bits) {
-        const int j = __builtin_ctzll(bits);
-        bits &= bits - 1;
-        const int t = P + j;
-        const int lp = t >> a.ps_shift;
-        if (lp >= a.max_pages)
-            continue;
-        int64_t pg = a.page_table[(int64_t)b * a.max_pages + lp];
-        pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
-        const uint16_t *kr = a.lat + pg * a.stride_page + (int64_t)(t & (ps - 1)) * a.stride_token;
-        const int4 x = *(const int4 *)(kr + 8 * lane);
-        const uint32_t u[4] = {(uint32_t)x.x, (uint32_t)x.y, (uint32_t)x.z, (uint32_t)x.w};
-        float kv[8];
+        constexpr int GK = 8;
+        int js[GK];
+        int n = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            kv[2 * e] = __uint_as_float(u[e] << 16);
-            kv[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
-        }
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            d = fmaf(qc[e], kv[e], d);
-        if (DR > 0 && lane < DR / 8) {
-            const int4 y = *(const int4 *)(kr + 512 + 8 * lane);
-            const uint32_t v[4] = {(uint32_t)y.x, (uint32_t)y.y, (uint32_t)y.z, (uint32_t)y.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                d = fmaf(qr[2 * e], __uint_as_float(v[e] << 16), d);
-                d = fmaf(qr[2 * e + 1], __uint_as_float(v[e] & 0xffff0000u), d);
+        for (int i = 0; i < GK; ++i) {
+            js[i] = bits ? __builtin_ctzll(bits) : -1;
+            if (bits) {
+                bits &= bits - 1;
+                ++n;
             }
+        }
+        int4 xk[GK], xr[GK];
+#pragma unroll
+        for (int i = 0; i < GK; ++i) {
+            xk[i] = xr[i] = make_int4(0, 0, 0, 0);
+            if (js[i] >= 0) {
+                const int64_t ro = ((int64_t)__builtin_amdgcn_readlane((int)(myrow >> 32), js[i]) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)myrow, js[i]);
+                const uint16_t *kr = a.lat + ro;
+                xk[i] = *(const int4 *)(kr + 8 * lane);
+                if (DR > 0 && lane < DR / 8)
+                    xr[i] = *(const int4 *)(kr + 512 + 8 * lane);
+            }
+        }
+        float sj[GK];
+#pragma unroll
+        for (int i = 0; i < GK; ++i) {
+            float kv[8], rv[8];
+            widen(xk[i], kv);
+            widen(xr[i], rv);
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                d = fmaf(qc[e], kv[e], d);
+            if (DR > 0) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    d = fmaf(qr[e], rv[e], d);
+            }
+            sj[i] = d;
         }
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1)
-            d += __shfl_xor(d, o);
-        const float sj = d * a.c;     // exp2 domain
-        const float mnew = fmaxf(mw, sj);
-        const float alpha = __builtin_amdgcn_exp2f(mw - mnew);
-        const float pj = __builtin_amdgcn_exp2f(sj - mnew);
-        lw = lw * alpha + pj;
+#pragma unroll
+            for (int i = 0; i < GK; ++i)
+                sj[i] += __shfl_xor(sj[i], o);
+        float mg = mw;
+#pragma unroll
+        for (int i = 0; i < GK; ++i) {
+            sj[i] *= a.c;    // exp2 domain
+            if (i < n)
+                mg = fmaxf(mg, sj[i]);
+        }
+        // (equal maxima, both -inf included, leave the running sums as they are)
+        const float alpha = mw == mg ? 1.f : __builtin_amdgcn_exp2f(mw - mg);
+        lw *= alpha;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            ow[e] = ow[e] * alpha + pj * kv[e];
-        mw = mnew;
+            ow[e] *= alpha;
+#pragma unroll
+        for (int i = 0; i < GK; ++i) {
+            if (i < n) {
+                float kv[8];
+                widen(xk[i], kv);
+                const float pj = sj[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sj[i] - mg);
+                lw += pj;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    ow[e] = fmaf(pj, kv[e], ow[e]);
+            }
+        }
+        mw = mg;
     }
     // merge: the window part (o = ow / lw, lse2 = mw + log2 lw) and the
-    // prefix partials
-    float mx = lw != 0.f ? mw + __log2f(lw) : -INFINITY;
-    const float lse_w = mx;
-    for (int k = 0; k < a.n_split; ++k) {
-        const float l = a.ws_lse[row * a.n_split + k];
-        mx = (l != l || mx != mx) ? NAN : fmaxf(mx, l);
+    // prefix partials; lane k reads the lse2 of split k
+    const float lse_w = lw != 0.f ? mw + __log2f(lw) : -INFINITY;
+    float mx = lse_w;
+    for (int k0 = 0; k0 < a.n_split; k0 += 64) {
+        const float l = k0 + lane < a.n_split ? a.ws_lse[row * a.n_split + k0 + lane] : -INFINITY;
+        float lm = l;
+        bool nan = l != l;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1)
+            lm = fmaxf(lm, __shfl_xor(lm, o));
+        nan = __ballot(nan) != 0;
+        mx = (nan || mx != mx) ? NAN : fmaxf(mx, lm);
     }
     float acc[8], z = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
         acc[e] = 0.f;
-    if (mx == -INFINITY) {
-        // no key at all: out = 0, lse2 = -inf
-    } else {
+    if (mx != -INFINITY) {
         if (lse_w != -INFINITY) {
             const float zw = __builtin_amdgcn_exp2f(lse_w - mx);
             const float inv = 1.f / lw;
@@ -528,22 +572,53 @@ __global__ void __launch_bounds__(256) k_mla_window_merge(MlaArgs a) {
                 acc[e] = zw * ow[e] * inv;
             z = zw;
         }
-        for (int k = 0; k < a.n_split; ++k) {
-            const float l = a.ws_lse[row * a.n_split + k];
-            if (l == -INFINITY)
-                continue;
-            const float zk = __builtin_amdgcn_exp2f(l - mx);
-            const float4 *src = (const float4 *)(a.ws_o + (row * a.n_split + k) * 512 + 8 * lane);
-            const float4 p0 = src[0], p1 = src[1];
-            acc[0] = fmaf(zk, p0.x, acc[0]);
-            acc[1] = fmaf(zk, p0.y, acc[1]);
-            acc[2] = fmaf(zk, p0.z, acc[2]);
-            acc[3] = fmaf(zk, p0.w, acc[3]);
-            acc[4] = fmaf(zk, p1.x, acc[4]);
-            acc[5] = fmaf(zk, p1.y, acc[5]);
-            acc[6] = fmaf(zk, p1.z, acc[6]);
-            acc[7] = fmaf(zk, p1.w, acc[7]);
-            z += zk;
+        for (int k0 = 0; k0 < a.n_split; k0 += 64) {
+            const float l = k0 + lane < a.n_split ? a.ws_lse[row * a.n_split + k0 + lane] : -INFINITY;
+            // a split without keys (lse2 = -inf) is skipped, marked by -1
+            const float zl = l == -INFINITY ? -1.f : __builtin_amdgcn_exp2f(l - mx);
+            const int kn = a.n_split - k0 < 64 ? a.n_split - k0 : 64;
+            int k = 0;
+            for (; k + 4 <= kn; k += 4) {
+                float4 p[4][2];
+                float zk[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    zk[i] = __shfl(zl, k + i);
+                    const float4 *src = (const float4 *)(a.ws_o + (row * a.n_split + k0 + k + i) * 512 + 8 * lane);
+                    p[i][0] = src[0];
+                    p[i][1] = src[1];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (zk[i] < 0.f)
+                        continue;
+                    acc[0] = fmaf(zk[i], p[i][0].x, acc[0]);
+                    acc[1] = fmaf(zk[i], p[i][0].y, acc[1]);
+                    acc[2] = fmaf(zk[i], p[i][0].z, acc[2]);
+                    acc[3] = fmaf(zk[i], p[i][0].w, acc[3]);
+                    acc[4] = fmaf(zk[i], p[i][1].x, acc[4]);
+                    acc[5] = fmaf(zk[i], p[i][1].y, acc[5]);
+                    acc[6] = fmaf(zk[i], p[i][1].z, acc[6]);
+                    acc[7] = fmaf(zk[i], p[i][1].w, acc[7]);
+                    z += zk[i];
+                }
+            }
+            for (; k < kn; ++k) {
+                const float zk = __shfl(zl, k);
+                if (zk < 0.f)
+                    continue;
+                const float4 *src = (const float4 *)(a.ws_o + (row * a.n_split + k0 + k) * 512 + 8 * lane);
+                const float4 p0 = src[0], p1 = src[1];
+                acc[0] = fmaf(zk, p0.x, acc[0]);
+                acc[1] = fmaf(zk, p0.y, acc[1]);
+                acc[2] = fmaf(zk, p0.z, acc[2]);
+                acc[3] = fmaf(zk, p0.w, acc[3]);
+                acc[4] = fmaf(zk, p1.x, acc[4]);
+                acc[5] = fmaf(zk, p1.y, acc[5]);
+                acc[6] = fmaf(zk, p1.z, acc[6]);
+                acc[7] = fmaf(zk, p1.w, acc[7]);
+                z += zk;
+            }
         }
     }
     const float invz = z != 0.f ? 1.f / z : 0.f;
