@@ -238,6 +238,21 @@ def test_short_and_empty_prefixes(dtype):
     check_attention(out, lse, ro, rl, tag="short-prefix-" + dtype)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("rows", [32, 64, 256])
+@pytest.mark.parametrize("ps", [1, 2, 4])
+def test_small_pages(ps, rows, kv):
+    # pages of fewer than 8 keys: the loads look up a page per lane (every
+    # prefix kernel shape: 32, 64 and 256 folded rows)
+    n, hq = {32: (8, 8), 64: (16, 8), 256: (64, 8)}[rows]
+    wl = gen.Workload("sp", 2, 300, n, hq, 2, 128, "bf16", ps, "random", depth_cap=5, kv_dtype=kv)
+    inp = gen.make_inputs(wl, 20 + ps, "cuda", prefix_lens=[300, 77])
+    m = oracle.build_masks(inp.parents)["masks"]
+    out, lse = run_attention(inp, dev(m.view(np.int64), torch.int64))
+    ro, rl = oracle_attention(inp, m)
+    check_attention(out, lse, ro, rl, tag="pages of %d, %d rows, %s" % (ps, rows, kv))
+
+
 def test_nhd_layout_and_high_mask_bits():
     wl = gen.Workload("nhd", 2, 300, 12, 16, 4, 128, "bf16", 16, "random", depth_cap=5)
     inp = gen.make_inputs(wl, 4, "cuda", layout="NHD", prefix_lens=[300, 123])
