@@ -445,9 +445,10 @@ __global__ void __launch_bounds__(256) k_mla_window_merge(MlaArgs a) {
         }
     };
     const uint16_t *qp = a.q + row * DK;
-    float qc[8], qr[8];
-    widen(*(const int4 *)(qp + 8 * lane), qc);
-    widen(DR > 0 && lane < DR / 8 ? *(const int4 *)(qp + 512 + 8 * lane) : make_int4(0, 0, 0, 0), qr);
+    // the query stays packed (bf16) and is widened per key: fewer registers,
+    // more waves in flight
+    const int4 qcp = *(const int4 *)(qp + 8 * lane);
+    const int4 qrp = DR > 0 && lane < DR / 8 ? *(const int4 *)(qp + 512 + 8 * lane) : make_int4(0, 0, 0, 0);
 
     uint64_t bits = a.masks[(int64_t)b * a.R + r];
     if (a.W < 64)
@@ -499,9 +500,11 @@ __global__ void __launch_bounds__(256) k_mla_window_merge(MlaArgs a) {
         float sj[GK];
 #pragma unroll
         for (int i = 0; i < GK; ++i) {
-            float kv[8], rv[8];
+            float kv[8], rv[8], qc[8], qr[8];
             widen(xk[i], kv);
             widen(xr[i], rv);
+            widen(qcp, qc);
+            widen(qrp, qr);
             float d = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
@@ -578,18 +581,18 @@ __global__ void __launch_bounds__(256) k_mla_window_merge(MlaArgs a) {
             const float zl = l == -INFINITY ? -1.f : __builtin_amdgcn_exp2f(l - mx);
             const int kn = a.n_split - k0 < 64 ? a.n_split - k0 : 64;
             int k = 0;
-            for (; k + 4 <= kn; k += 4) {
-                float4 p[4][2];
-                float zk[4];
+            for (; k + 2 <= kn; k += 2) {
+                float4 p[2][2];
+                float zk[2];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < 2; ++i) {
                     zk[i] = __shfl(zl, k + i);
                     const float4 *src = (const float4 *)(a.ws_o + (row * a.n_split + k0 + k + i) * 512 + 8 * lane);
                     p[i][0] = src[0];
                     p[i][1] = src[1];
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < 2; ++i) {
                     if (zk[i] < 0.f)
                         continue;
                     acc[0] = fmaf(zk[i], p[i][0].x, acc[0]);
