@@ -465,6 +465,16 @@ def run_mla(args):
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+    sustained = None
+    if args.sustain > 0:
+        n, t_s = 0, time.perf_counter()
+        while time.perf_counter() - t_s < args.sustain:
+            for _ in range(50):
+                run()
+            torch.cuda.synchronize()
+            n += 50
+        sustained = (time.perf_counter() - t_s) * 1e3 / n
+        log("sustained: %d steps back to back, %.4f ms/step" % (n, sustained))
     masks_np = masks.cpu().numpy().view(np.uint64)
     pop = sum(bin(int(x)).count("1") for x in masks_np.reshape(-1))
     per_key = 2 * Dk + 2 * wl.Dc
@@ -481,6 +491,8 @@ def run_mla(args):
                         "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                         "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "algorithmic_flops": flops,
                         "flop_per_kv_byte": round(flops / kvb, 1), "traffic": None}}
+    if sustained is not None:
+        res["sustained_ms_per_step"] = round(sustained, 4)
     if args.cpu_budget > 0:
         import oracle as orc
         rng = np.random.default_rng(0)

@@ -117,18 +117,19 @@ struct MlaCfg {
     static constexpr int SB = NG * SK * 128;       // stage bytes
     static constexpr int NBUF = 4;
     static constexpr int LOADS = NG * SK * 8 / 64; // load instructions per stage (64 lanes each)
-    static constexpr int LPW = LOADS / 4;          // per loading wave (waves 0..3)
+    static constexpr int LA = (NG + 1) / 2;        // loads per stage of waves 0..3
+    static constexpr int LB = NG - LA;             // and of waves 4..7
     static constexpr int PB = 64 * SK * 2;         // bf16 weights of a block: 64 rows x 32 keys
-    static_assert(DK % 64 == 0 && LOADS % 4 == 0 && LPW == NG && KS >= 4, "row shape");
-    static_assert(NBUF * SB + PB + kMlaPt * 4 + 3 * 2 * 64 * 4 <= 160 * 1024, "LDS");
+    static_assert(DK % 64 == 0 && LOADS == 4 * NG && KS >= 2 * LA, "row shape");
+    static_assert(NBUF * SB + 2 * PB + kMlaPt * 4 + 3 * 2 * 64 * 4 <= 160 * 1024, "LDS");
 };
 
 template <int DR>
 __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
     using C = MlaCfg<DR>;
-    constexpr int DK = C::DK, KS = C::KS, SK = C::SK, SB = C::SB, NBUF = C::NBUF, LPW = C::LPW;
+    constexpr int DK = C::DK, KS = C::KS, SK = C::SK, SB = C::SB, NBUF = C::NBUF, LA = C::LA, LB = C::LB;
     __shared__ __attribute__((aligned(16))) char lds[NBUF * SB];
-    __shared__ __attribute__((aligned(16))) char pbuf[C::PB];
+    __shared__ __attribute__((aligned(16))) char pbuf[2 * C::PB];   // weights of blocks u, u + 1
     __shared__ int32_t pt[kMlaPt];
     __shared__ float xrow[3][2][64];   // per-row exchange between the two key tiles
 
@@ -189,25 +190,40 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
 
     const uint32_t lds0 = (uint32_t)(uintptr_t)(const MLA_LDS void *)lds;
     const int ps_mask = (1 << a.ps_shift) - 1;
-    // Waves 0..3 load the stages.  Load x of wave w fills the 1 KB block
-    // (G = x, keys 8 w .. 8 w + 7): lane i takes key 8 w + i % 8 and chunk 8 x
-    // + 2 (i / 16) + (i / 8) % 2, so a lane's loads of one stage all read one
-    // latent row (one page lookup) and each load reads eight whole 128-byte
-    // row segments.
+    // Every wave loads part of each stage.  Load x fills the 1 KB block (G =
+    // x, keys 8 (w % 4) .. +7): lane i takes key 8 (w % 4) + i % 8 and chunk
+    // 8 x + 2 (i / 16) + (i / 8) % 2, so a lane's loads of one stage all read
+    // one latent row (one page lookup) and each load reads eight whole
+    // 128-byte row segments.  Waves 0..3 take x < LA, waves 4..7 the rest.
     const int dkey = 8 * (w & 3) + (lane & 7);
     const int dpos = 2 * (lane >> 4) + ((lane >> 3) & 1);
-    auto issue = [&](int st) {
-        if (w >= 4)
-            return;
-        const uint32_t sbase = lds0 + (uint32_t)((st % NBUF) * SB + 8 * w * 128);
+    const int x0 = w < 4 ? 0 : LA;
+    const int nld = w < 4 ? LA : LB;
+    struct Loads {
+        const uint16_t *src;
+        uint32_t sbase;
+        bool on;
+    };
+    // the source row and LDS base of this lane's loads of stage st (none
+    // past the split end)
+    auto loads_of = [&](int st) {
+        Loads r;
         const int t = lo + st * SK + dkey;
-        if (t < hi) {
-            const int64_t pg = pt[(t >> a.ps_shift) - lp0];
-            const uint16_t *src = a.lat + pg * a.stride_page + (int64_t)(t & ps_mask) * a.stride_token + dpos * 8;
+        r.on = st < ns && t < hi;
+        const int64_t pg = pt[r.on ? (t >> a.ps_shift) - lp0 : 0];
+        r.src = a.lat + pg * a.stride_page + (int64_t)(t & ps_mask) * a.stride_token + dpos * 8 + 64 * x0;
+        r.sbase = lds0 + (uint32_t)((st % NBUF) * SB + 8 * (w & 3) * 128 + x0 * SK * 128);
+        return r;
+    };
+    auto load_one = [&](const Loads &r, int j) {
+        if (j < nld && r.on)
+            mla_dma16(r.src + 64 * j, __builtin_amdgcn_readfirstlane(r.sbase + (uint32_t)(j * SK * 128)));
+    };
+    auto issue = [&](int st) {
+        const Loads r = loads_of(st);
 #pragma unroll
-            for (int x = 0; x < LPW; ++x)
-                mla_dma16(src + 64 * x, __builtin_amdgcn_readfirstlane(sbase + (uint32_t)(x * SK * 128)));
-        }
+        for (int j = 0; j < LA; ++j)
+            load_one(r, j);
     };
 
     // K operand of step s (score role): lane (g, i16) reads key 16 kt + i16,
@@ -248,11 +264,12 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
     float mu = 0.f, l_part = 0.f, seen = -INFINITY;
 
     // S^T[key][row] of this wave's tile over the Dc + Dr channels, four K
-    // operands in flight; keys past the split end are -inf.
-    auto score = [&](int st) {
+    // operands in flight; keys past the split end are -inf.  When ld is
+    // given, its loads go out one after every other MFMA.
+    auto score = [&](int st, const Loads *ld) {
         const char *kb = lds + (st % NBUF) * SB + koff;
         auto kread = [&](int s) { return *(const bf16x8 *)(kb + (s >> 1) * (SK * 128) + (s & 1) * 512); };
-        f32x4 sc;
+        f32x4 sc, sd;
         bf16x8 k0 = kread(0), k1 = kread(1), k2 = kread(2), k3 = kread(3);
 #pragma unroll
         for (int s = 0; s < KS; s += 4) {
@@ -260,21 +277,26 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
             if (s + 4 < KS)
                 k0 = kread(s + 4);
             if (s + 1 < KS) {
-                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qv[s + 1], sc, 0, 0, 0);
+                sd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qv[s + 1], s ? sd : f32x4{}, 0, 0, 0);
                 if (s + 5 < KS)
                     k1 = kread(s + 5);
             }
+            if (ld && s / 2 < LA)
+                load_one(*ld, s / 2);
             if (s + 2 < KS) {
                 sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k2, qv[s + 2], sc, 0, 0, 0);
                 if (s + 6 < KS)
                     k2 = kread(s + 6);
             }
             if (s + 3 < KS) {
-                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k3, qv[s + 3], sc, 0, 0, 0);
+                sd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k3, qv[s + 3], sd, 0, 0, 0);
                 if (s + 7 < KS)
                     k3 = kread(s + 7);
             }
+            if (ld && s / 2 + 1 < LA)
+                load_one(*ld, s / 2 + 1);
         }
+        sc += sd;
         const int lim = hi - (lo + st * SK) - 16 * kt - 4 * g;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -292,12 +314,12 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
     };
     // O^T[d][row] += sum_key V[key][d] P[row][key] for this wave's 64 channels
     // and all 64 rows
-    auto pv = [&](int st) {
+    auto pv = [&](int st, int pb) {
         const uint32_t vb = (uint32_t)(uintptr_t)(const MLA_LDS void *)(lds + (st % NBUF) * SB);
         bf16x8 pr[4];
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4)
-            pr[t4] = *(const bf16x8 *)(pbuf + t4 * 1024 + pr_off);
+            pr[t4] = *(const bf16x8 *)(pbuf + pb * C::PB + t4 * 1024 + pr_off);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
             struct {
@@ -314,12 +336,38 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
     // been issued since (every stage but the last is full).  Only the loading
     // waves have loads outstanding.
     auto wait_stage = [&](int st, int k) {
-        if (k >= 2 && st + 2 < ns - 1)
-            mla_wait_vmcnt<2 * LPW>();
-        else if (k >= 1 && st + 1 < ns - 1)
-            mla_wait_vmcnt<LPW>();
-        else
-            mla_wait_vmcnt<0>();
+        const bool two = k >= 2 && st + 2 < ns - 1, one = k >= 1 && st + 1 < ns - 1;
+        if (w < 4) {
+            if (two)
+                mla_wait_vmcnt<2 * LA>();
+            else if (one)
+                mla_wait_vmcnt<LA>();
+            else
+                mla_wait_vmcnt<0>();
+        } else {
+            if (two)
+                mla_wait_vmcnt<2 * LB>();
+            else if (one)
+                mla_wait_vmcnt<LB>();
+            else
+                mla_wait_vmcnt<0>();
+        }
+    };
+
+    // bf16 weights of one block into weight buffer pb; their sum counts
+    // toward the row sums unless the block is a repeat
+    auto weights = [&](const f32x4 &sc, int pb, bool count) {
+        typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+        bf16x4 pw;
+        float sum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float pr = __builtin_amdgcn_exp2f(fmaf(sc[r], a.c, -mu));
+            pw[r] = (__bf16)pr;
+            sum += pr;
+        }
+        *(bf16x4 *)(pbuf + pb * C::PB + pw_off) = pw;
+        l_part += count ? sum : 0.f;
     };
 
     // The weights are exp2(s c - mu) with mu fixed for a whole pass: the
@@ -328,11 +376,14 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
     // inside fp32 range and keep full relative precision.  When a row's max
     // passes mu + 64 the pass is repeated with mu = that row's max over the
     // split (then every weight is <= 1), so the accumulator is never
-    // rescaled.  Per block u: wait for stage u; after the barrier (every wave
-    // is done with block u - 1, its stage and the weight buffer) stage u +
-    // NBUF - 1 goes into the buffer block u - 1 has left; the score waves
-    // write the weights; after a second barrier every wave accumulates its
-    // channels.
+    // rescaled.  Block 0 is scored first; then per block u, after one
+    // barrier (stage u + 1 has landed, the weights of block u are written,
+    // and every wave is done with block u - 1, its stage and its weight
+    // buffer) stage u + NBUF - 1 goes into the buffer of block u - 1, and
+    // each wave scores block u + 1 into the other weight buffer while it
+    // accumulates block u: the two MFMA streams are independent.  The last
+    // trip scores its own block again (discarded), so the trip is one basic
+    // block.
     static_assert(NBUF == 4, "three stages ahead");
     __shared__ int redo_flag;
     for (int pass = 0; pass < 2; ++pass) {
@@ -344,31 +395,31 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
         l_part = 0.f;
         for (int st = 0; st < NBUF - 1 && st < ns; ++st)
             issue(st);
-        for (int u = 0; u < ns; ++u) {
-            wait_stage(u, (u + 2 < ns ? u + 2 : ns - 1) - u);
+        if (ns > 0) {
+            wait_stage(0, ns - 1 < 2 ? ns - 1 : 2);
             __syncthreads();
-            if (u + NBUF - 1 < ns)
-                issue(u + NBUF - 1);
-            const f32x4 sc = score(u);
+            const f32x4 sc = score(0, nullptr);
             float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * a.c;
-            if (pass == 0 && u == 0) {
+            if (pass == 0) {
                 mx = row_max_both(mx, 0);
                 mu = fabsf(mx) < INFINITY ? mx : 0.f;
             } else {
                 mx = mla_quad_max(mx);
             }
             seen = fmaxf(seen, mx);
-            typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-            bf16x4 pw;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float pr = __builtin_amdgcn_exp2f(fmaf(sc[r], a.c, -mu));
-                pw[r] = (__bf16)pr;
-                l_part += pr;
-            }
-            *(bf16x4 *)(pbuf + pw_off) = pw;
+            weights(sc, 0, true);
+        }
+        for (int u = 0; u < ns; ++u) {
+            if (u + 1 < ns)
+                wait_stage(u + 1, u + 2 < ns ? 1 : 0);
             __syncthreads();
-            pv(u);
+            const bool more = u + 1 < ns;
+            const Loads ld = loads_of(u + NBUF - 1);
+            const f32x4 sc = score(more ? u + 1 : u, &ld);
+            const float mx = mla_quad_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * a.c);
+            seen = fmaxf(seen, mx);
+            weights(sc, (u + 1) & 1, more);
+            pv(u, u & 1);
         }
         // repeat with the exact row max (over both key tiles) when some row
         // passed mu + 64; the decision is the workgroup's: the stages are shared
