@@ -25,13 +25,13 @@
 //
 // LDS layout of a stage of 32 keys: 1 KB blocks [chunk group G][key block
 // K8] (G = 8 consecutive 16-byte chunks of the row, K8 = 8 consecutive
-// keys); inside a block, chunk c of key k sits at 16-byte slot 16 (c % 8 /
-// 2) + 8 (c % 2) + k % 8, i.e. four 256-byte runs of one chunk pair, each
-// [chunk parity][key].  The K operand read of 32 lanes (16 keys x chunks 4 s
-// + {0, 1}) then covers two whole 256-byte runs, and the transposing V read
-// of 32 lanes (8 keys x 2 chunks) one run: both run at the full LDS rate on
-// gfx950 (measured), where 16-byte reads from 16 separate 128-byte key rows
-// ran at half of it.
+// keys); inside a block key k owns the 128-byte row 128 (k % 8), its chunk c
+// at 16-byte slot (c % 8) ^ (k % 8).  Measured on gfx950: the K operand read
+// (16 keys x 4 chunks) and the transposing V read (16 keys x 2 chunks) both
+// run at the full LDS rate with this swizzle, and the direct-to-LDS loads,
+// eight lanes per 128-byte row segment, at the full L2 -> LDS rate; a layout
+// with consecutive lanes on different rows (which kept the LDS reads as fast)
+// loaded at about a quarter of it.
 #include <cmath>
 
 #include "tav_internal.h"
@@ -191,12 +191,12 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(const MLA_LDS void *)lds;
     const int ps_mask = (1 << a.ps_shift) - 1;
     // Every wave loads part of each stage.  Load x fills the 1 KB block (G =
-    // x, keys 8 (w % 4) .. +7): lane i takes key 8 (w % 4) + i % 8 and chunk
-    // 8 x + 2 (i / 16) + (i / 8) % 2, so a lane's loads of one stage all read
-    // one latent row (one page lookup) and each load reads eight whole
-    // 128-byte row segments.  Waves 0..3 take x < LA, waves 4..7 the rest.
-    const int dkey = 8 * (w & 3) + (lane & 7);
-    const int dpos = 2 * (lane >> 4) + ((lane >> 3) & 1);
+    // x, keys 8 (w % 4) .. +7): lane i takes key 8 (w % 4) + i / 8 and chunk
+    // 8 x + (i % 8 ^ i / 8), so a lane's loads of one stage all read one
+    // latent row (one page lookup) and every eight lanes read one whole
+    // 128-byte row segment.  Waves 0..3 take x < LA, waves 4..7 the rest.
+    const int dkey = 8 * (w & 3) + (lane >> 3);
+    const int dpos = (lane & 7) ^ (lane >> 3);
     const int x0 = w < 4 ? 0 : LA;
     const int nld = w < 4 ? LA : LB;
     struct Loads {
@@ -227,12 +227,13 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
     };
 
     // K operand of step s (score role): lane (g, i16) reads key 16 kt + i16,
-    // chunk 4 s + g: block (s / 2, key / 8), pair run 2 (s % 2) + g / 2,
-    // parity g % 2; the step parts are immediates.
+    // chunk 4 s + g: block (s / 2, key / 8), row key % 8, slot (4 (s % 2) + g)
+    // ^ (key % 8), which is koff's slot with bit 2 flipped for odd s; s / 2 is
+    // an immediate.
     uint32_t koff;
     {
         const int key = 16 * kt + i16;
-        koff = (uint32_t)((key >> 3) * 1024 + ((g >> 1) * 16 + (g & 1) * 8 + (key & 7)) * 16);
+        koff = (uint32_t)((key >> 3) * 1024 + (key & 7) * 128 + ((g ^ (key & 7)) * 16));
     }
     // The weights of a block in LDS: [row tile][k group g][row i16] 16-byte
     // chunks, k slot 8 g + e holding key 4 g + e (e < 4) or 16 + 4 g + e - 4
@@ -245,18 +246,20 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
     const uint32_t pr_off = (uint32_t)(g * 256 + i16 * 16);
     // V^T operand of channel tile ct (channels 64 w + 16 ct .. +15), half tt:
     // lane (g, j4 = i16 / 4, a4 = i16 % 4) points at key 16 tt + 4 g + j4,
-    // channels 64 w + 16 ct + 4 a4 .. +3 (chunk 8 w + 2 ct + a4 / 2); the
+    // channels 64 w + 16 ct + 4 a4 .. +3: chunk 8 w + 2 ct + a4 / 2 at slot
+    // (2 ct + a4 / 2) ^ (key % 8) of block (w, key / 8), byte 8 (a4 % 2); the
     // transposing read hands lane i16 channel i16 of those four keys, k slots
-    // 8 g + 4 tt .. +3 of the P operand.  Block (w, key / 8) is part of the
-    // offset, the pair run ct an immediate.
-    uint32_t voff[2];
+    // 8 g + 4 tt .. +3 of the P operand.
+    uint32_t voff[2][4];
     {
         const int j4 = i16 >> 2, a4 = i16 & 3;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const int key = 16 * tt + 4 * g + j4;
-            voff[tt] = (uint32_t)(w * (SK * 128) + (key >> 3) * 1024 + ((a4 >> 1) * 8 + (key & 7)) * 16 +
-                                  (a4 & 1) * 8);
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4)
+                voff[tt][c4] = (uint32_t)(w * (SK * 128) + (key >> 3) * 1024 + (key & 7) * 128 +
+                                          (((2 * c4 + (a4 >> 1)) ^ (key & 7)) * 16) + (a4 & 1) * 8);
         }
     }
 
@@ -268,7 +271,8 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
     // given, its loads go out one after every other MFMA.
     auto score = [&](int st, const Loads *ld) {
         const char *kb = lds + (st % NBUF) * SB + koff;
-        auto kread = [&](int s) { return *(const bf16x8 *)(kb + (s >> 1) * (SK * 128) + (s & 1) * 512); };
+        const char *kb1 = lds + (st % NBUF) * SB + (koff ^ 64u);
+        auto kread = [&](int s) { return *(const bf16x8 *)((s & 1 ? kb1 : kb) + (s >> 1) * (SK * 128)); };
         f32x4 sc, sd;
         bf16x8 k0 = kread(0), k1 = kread(1), k2 = kread(2), k3 = kread(3);
 #pragma unroll
@@ -324,8 +328,8 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
         for (int ct = 0; ct < 4; ++ct) {
             struct {
                 i16x4 lo, hi;
-            } pair{__builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4 *)(uintptr_t)(vb + voff[0] + ct * 256)),
-                   __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4 *)(uintptr_t)(vb + voff[1] + ct * 256))};
+            } pair{__builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4 *)(uintptr_t)(vb + voff[0][ct])),
+                   __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4 *)(uintptr_t)(vb + voff[1][ct]))};
             const bf16x8 va = __builtin_bit_cast(bf16x8, pair);
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4)
