@@ -268,16 +268,41 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
 
     // S^T[key][row] of this wave's tile over the Dc + Dr channels, four K
     // operands in flight; keys past the split end are -inf.  When ld is
-    // given, its loads go out one after every other MFMA.
-    auto score = [&](int st, const Loads *ld) {
+    // given, its loads go out one after every other MFMA.  With with_pv the
+    // same pass accumulates O^T[d][row] += sum_key V[key][d] P[row][key] of
+    // block pst (weights in buffer pb) for this wave's 64 channels and all 64
+    // rows: its operands are read first and its 16 MFMAs sit between the
+    // score steps, which they do not depend on.
+    auto score = [&](int st, const Loads *ld, bool with_pv, int pst, int pb) {
         const char *kb = lds + (st % NBUF) * SB + koff;
         const char *kb1 = lds + (st % NBUF) * SB + (koff ^ 64u);
         auto kread = [&](int s) { return *(const bf16x8 *)((s & 1 ? kb1 : kb) + (s >> 1) * (SK * 128)); };
+        // P^T and V^T operands of block pst, read before the score steps
+        bf16x8 pr[4], vr[4];
+        if (with_pv) {
+            const uint32_t vb = (uint32_t)(uintptr_t)(const MLA_LDS void *)(lds + (pst % NBUF) * SB);
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4)
+                pr[t4] = *(const bf16x8 *)(pbuf + pb * C::PB + t4 * 1024 + pr_off);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                struct {
+                    i16x4 lo, hi;
+                } pair{__builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4 *)(uintptr_t)(vb + voff[0][ct])),
+                       __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4 *)(uintptr_t)(vb + voff[1][ct]))};
+                vr[ct] = __builtin_bit_cast(bf16x8, pair);
+            }
+        }
+        auto pv_step = [&](int ct, int t4) {
+            if (with_pv && ct < 4)
+                o[ct][t4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vr[ct], pr[t4], o[ct][t4], 0, 0, 0);
+        };
         f32x4 sc, sd;
         bf16x8 k0 = kread(0), k1 = kread(1), k2 = kread(2), k3 = kread(3);
 #pragma unroll
         for (int s = 0; s < KS; s += 4) {
             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qv[s], s ? sc : f32x4{}, 0, 0, 0);
+            pv_step(s / 4, 0);
             if (s + 4 < KS)
                 k0 = kread(s + 4);
             if (s + 1 < KS) {
@@ -285,6 +310,7 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
                 if (s + 5 < KS)
                     k1 = kread(s + 5);
             }
+            pv_step(s / 4, 1);
             if (ld && s / 2 < LA)
                 load_one(*ld, s / 2);
             if (s + 2 < KS) {
@@ -292,11 +318,13 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
                 if (s + 6 < KS)
                     k2 = kread(s + 6);
             }
+            pv_step(s / 4, 2);
             if (s + 3 < KS) {
                 sd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k3, qv[s + 3], sd, 0, 0, 0);
                 if (s + 7 < KS)
                     k3 = kread(s + 7);
             }
+            pv_step(s / 4, 3);
             if (ld && s / 2 + 1 < LA)
                 load_one(*ld, s / 2 + 1);
         }
@@ -315,26 +343,6 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
             xrow[slot][kt][rt * 16 + i16] = mx;
         __syncthreads();
         return fmaxf(mx, xrow[slot][kt ^ 1][rt * 16 + i16]);
-    };
-    // O^T[d][row] += sum_key V[key][d] P[row][key] for this wave's 64 channels
-    // and all 64 rows
-    auto pv = [&](int st, int pb) {
-        const uint32_t vb = (uint32_t)(uintptr_t)(const MLA_LDS void *)(lds + (st % NBUF) * SB);
-        bf16x8 pr[4];
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4)
-            pr[t4] = *(const bf16x8 *)(pbuf + pb * C::PB + t4 * 1024 + pr_off);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            struct {
-                i16x4 lo, hi;
-            } pair{__builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4 *)(uintptr_t)(vb + voff[0][ct])),
-                   __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4 *)(uintptr_t)(vb + voff[1][ct]))};
-            const bf16x8 va = __builtin_bit_cast(bf16x8, pair);
-#pragma unroll
-            for (int t4 = 0; t4 < 4; ++t4)
-                o[ct][t4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pr[t4], o[ct][t4], 0, 0, 0);
-        }
     };
     // Wait until stage st has landed, given that the k stages after it have
     // been issued since (every stage but the last is full).  Only the loading
@@ -402,7 +410,7 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
         if (ns > 0) {
             wait_stage(0, ns - 1 < 2 ? ns - 1 : 2);
             __syncthreads();
-            const f32x4 sc = score(0, nullptr);
+            const f32x4 sc = score(0, nullptr, false, 0, 0);
             float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * a.c;
             if (pass == 0) {
                 mx = row_max_both(mx, 0);
@@ -419,11 +427,10 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
             __syncthreads();
             const bool more = u + 1 < ns;
             const Loads ld = loads_of(u + NBUF - 1);
-            const f32x4 sc = score(more ? u + 1 : u, &ld);
+            const f32x4 sc = score(more ? u + 1 : u, &ld, true, u, u & 1);
             const float mx = mla_quad_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * a.c);
             seen = fmaxf(seen, mx);
             weights(sc, (u + 1) & 1, more);
-            pv(u, u & 1);
         }
         // repeat with the exact row max (over both key tiles) when some row
         // passed mu + 64; the decision is the workgroup's: the stages are shared
