@@ -83,6 +83,8 @@ def lib():
         L.orc_causal_attention.argtypes = [P, P, P, I, I, I, I, I, I, D, P, P]
         L.orc_merge.argtypes = [P, P, I, I, I, P, P]
         L.orc_verify_greedy.argtypes = [P, P, P, I, I, P, P, P]
+        L.orc_verify_rejection.argtypes = [P, I64, I, P, P, P, P, P, I, I, P, P, P, P]
+        L.orc_verify_rejection.restype = ctypes.c_int
         L.orc_compact_rows.argtypes = [ctypes.POINTER(OrcRows), I, P, P, I, I]
         for f in ("orc_build_masks", "orc_shift_positions", "orc_tree_attention",
                   "orc_causal_attention", "orc_merge", "orc_verify_greedy",
@@ -235,6 +237,31 @@ def verify_greedy(draft, target, parents):
     _check(lib().orc_verify_greedy(_p(draft), _p(target), _p(parents), B, N,
                                    _p(path), _p(alen), _p(tok)), "verify_greedy")
     return {"accepted_path": path, "accept_len": alen, "accepted_tokens": tok}
+
+
+def verify_rejection(probs, draft, parents, coins, bonus_u, draft_score=None):
+    """Tree rejection sampling ([DDT] "The Implementation"; [DTS] "Sampled
+    verify keys noise by position"): probs float32 [B][N][V] target weights
+    per node, draft / parents int32 [B][N], coins / bonus_u float32 [B][N]
+    uniform in [0, 1), draft_score float32 [B][N] or None.  Returns the path,
+    accept_len, emitted tokens and, per request, how near its decisions came
+    to a tie (relative margin)."""
+    probs = _c(probs, np.float32)
+    draft = _c(draft, np.int32)
+    parents = _c(parents, np.int32)
+    coins = _c(coins, np.float32)
+    bonus_u = _c(bonus_u, np.float32)
+    B, N, V = probs.shape
+    sc = None if draft_score is None else _c(draft_score, np.float32)
+    path = np.empty((B, N), np.int32)
+    alen = np.empty((B,), np.int32)
+    tok = np.empty((B, N), np.int32)
+    margin = np.empty((B,), np.float64)
+    _check(lib().orc_verify_rejection(_p(probs), V, V, _p(draft), _p(parents),
+                                      None if sc is None else _p(sc), _p(coins), _p(bonus_u),
+                                      B, N, _p(path), _p(alen), _p(tok), _p(margin)),
+           "verify_rejection")
+    return {"accepted_path": path, "accept_len": alen, "accepted_tokens": tok, "margin": margin}
 
 
 def compact_rows(tables, accepted_path, accept_len):

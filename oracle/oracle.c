@@ -954,3 +954,156 @@ int orc_mla_attention(const void *q, const void *latent, int dtype, int64_t stri
     }
     return bad ? ORC_BAD : ORC_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* sampled verify by tree rejection sampling                           */
+/* ------------------------------------------------------------------ */
+
+/* a target weight as the walk uses it: positive finite entries, else 0 */
+static double orc_tw(float p)
+{
+    return (p > 0.0f && p < INFINITY) ? (double)p : 0.0;
+}
+
+/*
+ * Tree rejection sampling with the draft tokens as fixed candidates
+ * ([DDT] "The Implementation": a node's children are tried in descending
+ * draft probability and the first one passing the rejection test is
+ * accepted; [DTS] "Sampled verify keys noise by position": recursive
+ * rejection sampling is exact in distribution).  At node cur the target
+ * weights are w(v) = probs[cur][v] (positive finite entries, else 0) with
+ * total S; the residual after rejecting tokens R is w restricted to v not in
+ * R, of mass S - E with E = sum_{x in R} w(x).  Child c (token x) is
+ * accepted with the residual's probability of x:
+ *     coin[c] * (S - E) < (x in [0, V) and x not in R ? w(x) : 0)
+ * and a rejected valid token joins R.  Children are the nodes c with
+ * parents[c] == cur, taken in descending draft_score (all equal when
+ * draft_score is NULL), ties to the lower index.  An accepted child
+ * continues the walk; otherwise (or once the path holds N nodes) the walk
+ * stops at cur and the bonus token is the lowest v whose running sum of the
+ * residual exceeds bonus_u[cur] * (its total), summed in v order; the last v
+ * of positive residual when rounding leaves none, token 0 when the residual
+ * is all zero.  Every candidate token is emitted with its residual
+ * probability and the bonus with the rest, so the token emitted at every
+ * depth is distributed as the target there.
+ * Outputs as orc_verify_greedy: path (-1 padded), accept_len (counts the
+ * root), tokens[k] = draft[path[k + 1]] for k + 1 < accept_len and the bonus
+ * at k = accept_len - 1, -1 after.  margin (or NULL) gets, per request, the
+ * smallest |coin (S - E) - w(x)| / S over its tests and |running sum -
+ * target| / total around the bonus draw: how near the walk came to a tie.
+ */
+int orc_verify_rejection(const float *probs, int64_t row_stride, int V,
+                         const int32_t *draft, const int32_t *parents,
+                         const float *draft_score, const float *coins,
+                         const float *bonus_u, int B, int N, int32_t *path,
+                         int32_t *accept_len, int32_t *tokens, double *margin)
+{
+    if (N < 1 || N > 64 || V < 1 || row_stride < V)
+        return ORC_BAD;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *dr = draft + (int64_t)b * N;
+        const int32_t *par = parents + (int64_t)b * N;
+        int32_t *pb = path + (int64_t)b * N;
+        double mg = INFINITY;
+        for (int k = 0; k < N; ++k)
+            pb[k] = -1;
+        int len = 0, cur = 0;
+        pb[len++] = cur;
+        int32_t rej[64];
+        int nrej;
+        int bonus = 0;
+        for (;;) {
+            const float *row = probs + ((int64_t)b * N + cur) * row_stride;
+            double S = 0.0;
+            for (int v = 0; v < V; ++v)
+                S += orc_tw(row[v]);
+            double E = 0.0;
+            nrej = 0;
+            int next = -1;
+            if (len < N) {
+                int tried[64] = {0};
+                for (;;) {
+                    /* the untried child of highest draft score, lowest index on ties */
+                    int c = -1;
+                    for (int j = 0; j < N; ++j) {
+                        if (par[j] != cur || tried[j])
+                            continue;
+                        if (c < 0 || (draft_score && draft_score[(int64_t)b * N + j] >
+                                                         draft_score[(int64_t)b * N + c]))
+                            c = j;
+                    }
+                    if (c < 0)
+                        break;
+                    tried[c] = 1;
+                    const int x = dr[c];
+                    int valid = x >= 0 && x < V;
+                    for (int i = 0; valid && i < nrej; ++i)
+                        if (rej[i] == x)
+                            valid = 0;
+                    const double wx = valid ? orc_tw(row[x]) : 0.0;
+                    const double lhs = (double)coins[(int64_t)b * N + c] * (S - E);
+                    if (S > 0.0 && fabs(lhs - wx) / S < mg)
+                        mg = fabs(lhs - wx) / S;
+                    if (lhs < wx) {
+                        next = c;
+                        break;
+                    }
+                    if (valid) {
+                        E += wx;
+                        rej[nrej++] = x;
+                    }
+                }
+            }
+            if (next >= 0) {
+                cur = next;
+                pb[len++] = cur;
+                continue;
+            }
+            /* the bonus draw from the residual at cur */
+            double T = 0.0;
+            for (int v = 0; v < V; ++v) {
+                int out = 0;
+                for (int i = 0; i < nrej; ++i)
+                    if (rej[i] == v)
+                        out = 1;
+                T += out ? 0.0 : orc_tw(row[v]);
+            }
+            bonus = 0;
+            if (T > 0.0) {
+                const double target = (double)bonus_u[(int64_t)b * N + cur] * T;
+                double run = 0.0;
+                int last_pos = -1, found = -1;
+                for (int v = 0; v < V; ++v) {
+                    int out = 0;
+                    for (int i = 0; i < nrej; ++i)
+                        if (rej[i] == v)
+                            out = 1;
+                    const double r = out ? 0.0 : orc_tw(row[v]);
+                    if (r <= 0.0)
+                        continue;
+                    last_pos = v;
+                    const double before = run;
+                    run += r;
+                    if (found < 0 && run > target) {
+                        found = v;
+                        const double m1 = fabs(run - target) / T, m0 = fabs(target - before) / T;
+                        if (m1 < mg)
+                            mg = m1;
+                        if (m0 < mg)
+                            mg = m0;
+                    }
+                }
+                bonus = found >= 0 ? found : last_pos;
+            }
+            break;
+        }
+        accept_len[b] = len;
+        if (tokens)
+            for (int k = 0; k < N; ++k)
+                tokens[(int64_t)b * N + k] =
+                    k + 1 < len ? dr[pb[k + 1]] : (k + 1 == len ? bonus : -1);
+        if (margin)
+            margin[b] = mg;
+    }
+    return ORC_OK;
+}

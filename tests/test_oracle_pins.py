@@ -784,6 +784,135 @@ def test_sampled_chain_verify_accepts_matching_drafts():
 
 
 # ---------------------------------------------------------------------------
+# sampled verify by tree rejection sampling
+# ---------------------------------------------------------------------------
+
+def _chi2(tok, p, n_bins):
+    cnt = np.bincount(tok, minlength=n_bins)[:n_bins]
+    exp = p / p.sum() * len(tok)
+    return float(((cnt - exp) ** 2 / exp).sum())
+
+
+def test_rejection_emits_every_depth_from_the_target():
+    """[DTS] "Sampled verify keys noise by position": recursive rejection
+    sampling is exact in distribution.  40000 walks of one tree (root with
+    three children tried in draft-score order, the first of them with two
+    children of its own), unnormalised target rows: the first emitted token
+    follows the root's target law, and the second, given the walk entered
+    node 1 or leaf 2, follows that node's law (chi-square, 4 dof each)."""
+    rng = np.random.default_rng(17)
+    V, N, B = 5, 6, 40000
+    par = np.array([-1, 0, 0, 0, 1, 1], np.int32)
+    draft = np.array([0, 2, 0, 4, 1, 3], np.int32)
+    score = np.array([0.0, 0.2, 0.5, 0.3, 0.6, 0.1], np.float32)    # tried 2, 3, 1 at the root
+    rows = (rng.dirichlet(np.ones(V), N) * rng.uniform(0.5, 3.0, (N, 1))).astype(np.float32)
+    probs = np.broadcast_to(rows, (B, N, V))
+    r = oracle.verify_rejection(probs, np.tile(draft, (B, 1)), np.tile(par, (B, 1)),
+                                rng.random((B, N), np.float32), rng.random((B, N), np.float32),
+                                draft_score=np.tile(score, (B, 1)))
+    t1 = r["accepted_tokens"][:, 0]
+    assert _chi2(t1, rows[0].astype(np.float64), V) < 20.5   # P(chi2 > 20.5) < 4e-4
+    for node in (1, 2):
+        sel = (r["accept_len"] >= 2) & (r["accepted_path"][:, 1] == node)
+        assert sel.sum() > 3000
+        t2 = r["accepted_tokens"][sel, 1]
+        assert _chi2(t2, rows[node].astype(np.float64), V) < 20.5
+    # a leaf's walk ends there with its bonus; node 1 goes on or stops
+    assert (r["accept_len"][r["accepted_path"][:, 1] == 2] == 2).all()
+
+
+def test_rejection_chain_accept_length_closed_form():
+    """A chain is plain speculative sampling with fixed drafts: it accepts
+    draft k + 1 with probability p_k(x_{k+1}) / S_k once it reached node k,
+    so E[accept_len] = 1 + sum_k prod_{i <= k} p_i(x_{i+1}) / S_i."""
+    rng = np.random.default_rng(18)
+    V, N, B = 6, 5, 40000
+    par = np.arange(-1, N - 1, dtype=np.int32)
+    draft = rng.integers(0, V, N).astype(np.int32)
+    rows = rng.dirichlet(np.ones(V) * 0.7, N).astype(np.float32) * 2.0
+    q = [float(rows[i, draft[i + 1]]) / float(rows[i].astype(np.float64).sum()) for i in range(N - 1)]
+    expect = 1 + sum(float(np.prod(q[:k + 1])) for k in range(N - 1))
+    r = oracle.verify_rejection(np.broadcast_to(rows, (B, N, V)), np.tile(draft, (B, 1)),
+                                np.tile(par, (B, 1)), rng.random((B, N), np.float32),
+                                rng.random((B, N), np.float32))
+    lens = r["accept_len"].astype(np.float64)
+    assert abs(lens.mean() - expect) < 5 * lens.std() / math.sqrt(B)
+
+
+def test_rejection_one_hot_targets_are_the_greedy_walk():
+    """With every target row one-hot on y, the walk accepts exactly the
+    children carrying their parent's y (index order when no draft scores are
+    given) and the bonus is y: verify_greedy with target_argmax = y."""
+    rng = np.random.default_rng(19)
+    B, N, V = 64, 16, 12
+    par = np.stack([gen.random_tree(rng, N, 6) for _ in range(B)]).astype(np.int32)
+    y = rng.integers(0, 4, (B, N)).astype(np.int32)
+    draft = rng.integers(0, 4, (B, N)).astype(np.int32)
+    probs = np.zeros((B, N, V), np.float32)
+    np.put_along_axis(probs, y[..., None], 1.0, -1)
+    r = oracle.verify_rejection(probs, draft, par, rng.random((B, N), np.float32),
+                                rng.random((B, N), np.float32))
+    g = oracle.verify_greedy(draft, y, par)
+    assert np.array_equal(r["accepted_path"], g["accepted_path"])
+    assert np.array_equal(r["accept_len"], g["accept_len"])
+    assert np.array_equal(r["accepted_tokens"], g["accepted_tokens"])
+    assert (r["accept_len"] > 1).any() and (r["accept_len"] < N).all()
+
+
+def test_rejection_tries_children_in_descending_draft_score():
+    """Coins of 0 accept the first child tried whose token has weight:
+    the highest draft score, the lower index on ties; index order without
+    scores.  Coins just below 1 on a flat target reject every child, and the
+    bonus then avoids the rejected tokens."""
+    V, N = 16, 5
+    par = np.array([[-1, 0, 0, 0, 0]], np.int32)
+    draft = np.array([[0, 3, 5, 7, 9]], np.int32)
+    probs = np.full((1, N, V), 1.0 / V, np.float32)
+    zero = np.zeros((1, N), np.float32)
+    sc = np.array([[0.0, 0.3, 0.5, 0.5, 0.1]], np.float32)
+    r = oracle.verify_rejection(probs, draft, par, zero, zero, draft_score=sc)
+    assert r["accepted_path"][0, :2].tolist() == [0, 2]
+    r = oracle.verify_rejection(probs, draft, par, zero, zero)
+    assert r["accepted_path"][0, :2].tolist() == [0, 1]
+    p2 = probs.copy()
+    p2[0, 0, 5] = 0.0                       # child 2's token has no weight: skip to 3
+    r = oracle.verify_rejection(p2, draft, par, zero, zero, draft_score=sc)
+    assert r["accepted_path"][0, :2].tolist() == [0, 3]
+    high = np.full((1, N), np.nextafter(np.float32(1), np.float32(0)), np.float32)
+    for u in np.linspace(0, 0.999, 40, dtype=np.float32):
+        r = oracle.verify_rejection(probs, draft, par, high, np.full((1, N), u, np.float32))
+        assert int(r["accept_len"][0]) == 1
+        assert int(r["accepted_tokens"][0, 0]) not in (3, 5, 7, 9)
+
+
+def test_rejection_bonus_is_the_inverse_cdf():
+    """A root without children emits its bonus: the lowest v whose running
+    sum of the (cleaned) target row passes u times the row's total, i.e.
+    numpy's searchsorted on the cumulative sum; NaN, infinite and negative
+    entries carry no weight."""
+    rng = np.random.default_rng(20)
+    B, V = 300, 1000
+    probs = rng.random((B, 1, V)).astype(np.float32) ** 3
+    probs[rng.random((B, 1, V)) < 0.3] = 0.0
+    probs[0, 0, 10] = np.nan
+    probs[1, 0, 20] = np.inf
+    probs[2, 0, 30] = -5.0
+    u = rng.random((B, 1)).astype(np.float32)
+    r = oracle.verify_rejection(probs, np.zeros((B, 1), np.int32), np.full((B, 1), -1, np.int32),
+                                np.zeros((B, 1), np.float32), u)
+    w = np.where(np.isfinite(probs) & (probs > 0), probs, 0).astype(np.float64)[:, 0]
+    c = np.cumsum(w, 1)
+    ref = [int(np.searchsorted(c[b], u[b, 0] * c[b, -1], side="right")) for b in range(B)]
+    assert r["accepted_tokens"][:, 0].tolist() == ref
+    assert (r["accept_len"] == 1).all()
+    # an all-zero row gives token 0
+    r = oracle.verify_rejection(np.zeros((1, 1, 8), np.float32), np.zeros((1, 1), np.int32),
+                                np.full((1, 1), -1, np.int32), np.zeros((1, 1), np.float32),
+                                np.full((1, 1), 0.5, np.float32))
+    assert int(r["accepted_tokens"][0, 0]) == 0
+
+
+# ---------------------------------------------------------------------------
 # tree construction: beam, selection, numbering, links
 # ---------------------------------------------------------------------------
 
