@@ -367,6 +367,81 @@ def run_sampled(args):
     print(json.dumps(res), flush=True)
 
 
+REJECTION_METRIC = "sampled tree verify by rejection: visited target rows GB/s"
+
+
+def run_rejection(args):
+    """Sampled verify by tree rejection sampling on the EAGLE-style verify
+    shape: 32 requests x 64 rows (EAGLE top-8 trees), fp32 target rows over a
+    128256-token vocabulary (1.05 GB).  One step is one verify_tree_rejection
+    call; a request's walk reads the target rows of the nodes it visits, so
+    the algorithmic bytes are sum_b accept_len[b] * V * 4."""
+    L = tav.lib()
+    B, N, V = 32, 64, gen.SAMPLE_VOCAB
+    x = gen.make_rejection_inputs(B, N, V, args.seed, "cuda", tree="eagle")
+    t = lambda a, dt=torch.int32: torch.as_tensor(np.ascontiguousarray(a)).to(dt).to("cuda")
+    draft, parents = t(x.draft), t(x.parents)
+    score, coins, bu = t(x.draft_score, torch.float32), t(x.coins, torch.float32), \
+        t(x.bonus_u, torch.float32)
+    path = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    alen = torch.empty((B,), dtype=torch.int32, device="cuda")
+    toks = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    probs = x.probs
+
+    def run():
+        assert L.verify_tree_rejection(probs.data_ptr(), probs.stride(1), V, draft.data_ptr(),
+                                       parents.data_ptr(), score.data_ptr(), coins.data_ptr(),
+                                       bu.data_ptr(), B, N, path.data_ptr(), alen.data_ptr(),
+                                       toks.data_ptr(), stream) == 0
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        run()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    visited = int(alen.sum().item())
+    nbytes = visited * V * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {"metric": REJECTION_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic",
+           "config": {"workload": "rejection verify, %d requests x %d rows (EAGLE top-8 trees), "
+                                  "vocabulary %d, fp32 target rows" % (B, N, V),
+                      "mean_accept_len": round(visited / B, 3)},
+           "rows_per_s": round(B * N / (ms * 1e-3), 1),
+           "roofline": {"kernel": "k_verify_rejection", "bound": "hbm", "achieved": round(gbs, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "note": "one workgroup per request: %d CUs of 256 stream the rows" % B}}
+    if args.cpu_budget > 0:
+        import oracle
+        host = {k: np.ascontiguousarray(getattr(x, k)) for k in
+                ("draft", "parents", "draft_score", "coins", "bonus_u")}
+        n, total_t, done = 1, 0.0, 0
+        while total_t < args.cpu_budget and done < B:
+            sl = slice(done, min(done + n, B))
+            sub = np.ascontiguousarray(probs[sl].cpu().numpy())
+            t0 = time.perf_counter()
+            oracle.verify_rejection(sub, host["draft"][sl], host["parents"][sl], host["coins"][sl],
+                                    host["bonus_u"][sl], host["draft_score"][sl])
+            total_t += time.perf_counter() - t0
+            done = sl.stop
+            n = min(2 * n, 8)
+        t_full = total_t * B / done
+        res["cpu_baseline"] = {"value": round(nbytes / t_full / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": "%d of %d requests, %.2f s of fp64 oracle time, scaled "
+                                         "to the whole step" % (done, B, total_t)}
+    print(json.dumps(res), flush=True)
+
+
 def run_tree_build(args):
     """Tree construction on the EAGLE-style verify shape (32 requests, top-8
     beam over 6 expansion steps into a 328-candidate pool, N = 64): one step
@@ -533,6 +608,9 @@ def main():
     ap.add_argument("--sampled", action="store_true",
                     help="time the sampled verify (Gumbel-max draws over a 128256-token "
                          "vocabulary, then the greedy walk) instead of the attention step")
+    ap.add_argument("--rejection", action="store_true",
+                    help="time the sampled verify by tree rejection sampling (fp32 target rows "
+                         "over a 128256-token vocabulary) instead")
     ap.add_argument("--mla", choices=sorted(gen.MLA_WORKLOADS),
                     help="time the cascade over an MLA latent cache on this workload instead")
     ap.add_argument("--tree-build", action="store_true",
@@ -561,6 +639,9 @@ def main():
         return
     if args.tree_build:
         run_tree_build(args)
+        return
+    if args.rejection:
+        run_rejection(args)
         return
     if args.mla:
         run_mla(args)

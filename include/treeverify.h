@@ -10,6 +10,8 @@
  *   verify_tree_greedy   draft tokens, target argmax -> accepted path
  *   tree_sample_gumbel   logits -> target draws keyed by (seed, position),
  *                        for the sampled verify
+ *   verify_tree_rejection  target rows, draft tokens -> accepted path by
+ *                        tree rejection sampling
  *   compact_window_rows  accepted path -> rows moved to the window's front
  *   tree_shift_positions load_step / compact_rows position shifts
  *
@@ -310,6 +312,48 @@ tav_status tree_sample_gumbel(const void *logits, tav_dtype dtype, int64_t row_s
                               int32_t B, int32_t N, const float *temperature,
                               const uint64_t *seed, const int32_t *positions, int32_t *tokens,
                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Sampled verify by tree rejection sampling ([DDT] "The Implementation": a
+ * node's children are tried in descending draft probability and the first
+ * one passing the rejection test is accepted; [DTS] "Sampled verify keys
+ * noise by position": recursive rejection sampling is exact in
+ * distribution).  The draft tokens are fixed candidates.  At node cur,
+ * w(v) = probs[cur][v] where positive and finite (else 0), S = sum_v w(v),
+ * and R holds the tokens rejected so far at cur, of total weight E.  Child c
+ * (token x) is accepted when
+ *     coins[c] * (S - E) < w(x)      (0 when x is outside [0, V) or in R),
+ * i.e. with the residual's probability of x; otherwise x joins R.  Children
+ * are the nodes with parents[c] == cur, in descending draft_score, the lower
+ * index on ties (index order when draft_score is NULL).  An accepted child
+ * continues the walk.  When none is (or the path holds N nodes) the walk
+ * stops and the bonus token is drawn from the residual r = w without R: the
+ * lowest v whose running sum of r exceeds bonus_u[cur] * sum_v r(v) (the
+ * last v of positive residual if rounding leaves none; token 0 if r is all
+ * zero).  The token emitted at every depth is then distributed as the
+ * target row there.  Sums are fp32 in the kernel's order, so a decision
+ * within rounding of a tie may differ from an exact evaluation.
+ *
+ * probs        device fp32 [B][N][row_stride], V used per row: the target
+ *              distribution after the node (softmax at the sampling
+ *              temperature; rows need not sum to 1); 16-byte aligned,
+ *              row_stride >= V and a multiple of 4
+ * draft_tokens, parents  int32 [B][N] (parents[0] = -1 is the root)
+ * draft_score  fp32 [B][N] or NULL: the sibling order (e.g. the draft
+ *              probability of each node's token)
+ * coins, bonus_u  fp32 [B][N], uniform in [0, 1): the coin of each node's
+ *              test and the bonus draw at the node where the walk stops
+ * accepted_path, accept_len, accepted_tokens as verify_tree_greedy; the
+ *              tokens are draft[path[k + 1]] for k + 1 < accept_len and the
+ *              bonus at k = accept_len - 1 (NULL to skip)
+ * B >= 0; 1 <= N <= 64; 1 <= V <= 2^20
+ */
+tav_status verify_tree_rejection(const float *probs, int64_t row_stride, int32_t V,
+                                 const int32_t *draft_tokens, const int32_t *parents,
+                                 const float *draft_score, const float *coins,
+                                 const float *bonus_u, int32_t B, int32_t N,
+                                 int32_t *accepted_path, int32_t *accept_len,
+                                 int32_t *accepted_tokens, void *stream);
 
 /*
  * The same cascade over an MLA latent cache ([DTS] "One tree attention ...":

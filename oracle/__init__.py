@@ -244,8 +244,8 @@ def verify_rejection(probs, draft, parents, coins, bonus_u, draft_score=None):
     verify keys noise by position"): probs float32 [B][N][V] target weights
     per node, draft / parents int32 [B][N], coins / bonus_u float32 [B][N]
     uniform in [0, 1), draft_score float32 [B][N] or None.  Returns the path,
-    accept_len, emitted tokens and, per request, how near its decisions came
-    to a tie (relative margin)."""
+    accept_len, emitted tokens and, per request, how near its children's
+    tests came to a tie (relative margin)."""
     probs = _c(probs, np.float32)
     draft = _c(draft, np.int32)
     parents = _c(parents, np.int32)

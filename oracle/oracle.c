@@ -989,8 +989,8 @@ static double orc_tw(float p)
  * Outputs as orc_verify_greedy: path (-1 padded), accept_len (counts the
  * root), tokens[k] = draft[path[k + 1]] for k + 1 < accept_len and the bonus
  * at k = accept_len - 1, -1 after.  margin (or NULL) gets, per request, the
- * smallest |coin (S - E) - w(x)| / S over its tests and |running sum -
- * target| / total around the bonus draw: how near the walk came to a tie.
+ * smallest |coin (S - E) - w(x)| / S over its children's tests: how near the
+ * walk came to a tie (INFINITY when it tested none).
  */
 int orc_verify_rejection(const float *probs, int64_t row_stride, int V,
                          const int32_t *draft, const int32_t *parents,
@@ -1082,16 +1082,9 @@ int orc_verify_rejection(const float *probs, int64_t row_stride, int V,
                     if (r <= 0.0)
                         continue;
                     last_pos = v;
-                    const double before = run;
                     run += r;
-                    if (found < 0 && run > target) {
+                    if (found < 0 && run > target)
                         found = v;
-                        const double m1 = fabs(run - target) / T, m0 = fabs(target - before) / T;
-                        if (m1 < mg)
-                            mg = m1;
-                        if (m0 < mg)
-                            mg = m0;
-                    }
                 }
                 bonus = found >= 0 ? found : last_pos;
             }

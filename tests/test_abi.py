@@ -190,6 +190,39 @@ def test_sample_empty_batch_is_a_no_op(L):
     assert st == 0, msg
 
 
+def rejection_call(L, **kw):
+    a = dict(probs=FAKE, rs=128256, V=128256, draft=FAKE, par=FAKE, score=None, coins=FAKE,
+             bu=FAKE, B=4, N=64, path=FAKE, alen=FAKE, tok=FAKE)
+    a.update(kw)
+    st = L.verify_tree_rejection(a["probs"], a["rs"], a["V"], a["draft"], a["par"], a["score"],
+                                 a["coins"], a["bu"], a["B"], a["N"], a["path"], a["alen"],
+                                 a["tok"], None)
+    return st, L.tav_last_error().decode()
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status,words", [
+    (dict(N=0), 1, ["N must be in [1, 64]"]),
+    (dict(V=(1 << 20) + 1, rs=(1 << 20) + 4), 1, ["V must be in [1, 1048576]"]),
+    (dict(rs=1000), 1, ["row_stride must be >= V"]),
+    (dict(rs=128258), 1, ["multiple of 4 elements"]),
+    (dict(probs=FAKE + 4), 1, ["16-byte aligned"]),
+    (dict(coins=None, bu=None), 1, ["coins is NULL", "bonus_u is NULL"]),
+    (dict(path=None), 1, ["accepted_path is NULL"]),
+])
+def test_verify_tree_rejection_rejects(L, kw, status, words):
+    st, msg = rejection_call(L, **kw)
+    assert st == status, msg
+    for w in words:
+        assert w in msg, msg
+
+
+def test_rejection_empty_batch_is_a_no_op(L):
+    st, msg = rejection_call(L, B=0, probs=None, draft=None, par=None, coins=None, bu=None,
+                             path=None, alen=None, tok=None)
+    assert st == 0, msg
+
+
 @no_gpu
 def test_tree_construction_entry_points_reject(L):
     # beam step: the pool range and the candidate limit

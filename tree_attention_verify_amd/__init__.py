@@ -12,7 +12,7 @@ Entry points (same names as the C ABI):
   tree_attention_workspace_size, verify_tree_greedy, compact_window_rows,
   tree_sample_gumbel, tree_sample_workspace_size, tree_beam_step,
   tree_select_candidates, tree_retrieve_links, tree_attention_mla,
-  tree_attention_mla_workspace_size
+  tree_attention_mla_workspace_size, verify_tree_rejection
 plus verify_tree_sampled (tree_sample_gumbel, then verify_tree_greedy over
 the draws).
 """
@@ -38,7 +38,7 @@ EXPORTS = ("tav_last_error", "tav_version", "tree_build_masks", "tree_shift_posi
            "tree_attention_window_merge", "verify_tree_greedy", "compact_window_rows",
            "tree_sample_workspace_size", "tree_sample_gumbel", "tree_beam_step",
            "tree_select_candidates", "tree_retrieve_links", "tree_attention_mla_workspace_size",
-           "tree_attention_mla")
+           "tree_attention_mla", "verify_tree_rejection")
 
 
 class TavError(RuntimeError):
@@ -105,10 +105,11 @@ def lib() -> ctypes.CDLL:
         L.tree_attention_mla.argtypes = [P, P, ctypes.c_int, I64, I64, I64, P, I32, I32, P, I32,
                                          P, I32, I32, I32, I32, I32, I32, ctypes.c_float, P, P, P,
                                          ctypes.c_size_t, P]
+        L.verify_tree_rejection.argtypes = [P, I64, I32, P, P, P, P, P, I32, I32, P, P, P, P]
         for f in ("tree_build_masks", "tree_shift_positions", "tree_attention",
                   "verify_tree_greedy", "compact_window_rows", "tree_sample_gumbel",
                   "tree_beam_step", "tree_select_candidates", "tree_retrieve_links",
-                  "tree_attention_mla"):
+                  "tree_attention_mla", "verify_tree_rejection"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -317,6 +318,37 @@ def verify_tree_sampled(draft_tokens: torch.Tensor, logits: torch.Tensor,
     r = verify_tree_greedy(draft_tokens, draws, parents)
     r["draws"] = draws
     return r
+
+
+def verify_tree_rejection(probs: torch.Tensor, draft_tokens: torch.Tensor, parents: torch.Tensor,
+                          coins: torch.Tensor, bonus_u: torch.Tensor,
+                          draft_score: Optional[torch.Tensor] = None, tokens: bool = True):
+    """Tree rejection sampling: probs float32 [B][N][V] (the target
+    distribution after every node; rows may be padded to a stride of a
+    multiple of 4), draft_tokens / parents int32 [B][N], coins / bonus_u
+    float32 [B][N] uniform in [0, 1), draft_score float32 [B][N] or None
+    (the sibling order).  -> dict(accepted_path, accept_len,
+    accepted_tokens)."""
+    if probs.dtype != torch.float32 or not probs.is_cuda or probs.dim() != 3 \
+            or probs.stride(2) != 1 or probs.stride(0) != probs.shape[1] * probs.stride(1):
+        raise ValueError("probs must be a float32 [B][N][V] GPU tensor with unit channel stride "
+                         "and rows at a constant stride")
+    B, N, V = probs.shape
+    dev = probs.device
+    _need(draft_tokens, "draft_tokens", torch.int32, dev, (B, N))
+    _need(parents, "parents", torch.int32, dev, (B, N))
+    _need(coins, "coins", torch.float32, dev, (B, N))
+    _need(bonus_u, "bonus_u", torch.float32, dev, (B, N))
+    if draft_score is not None:
+        _need(draft_score, "draft_score", torch.float32, dev, (B, N))
+    path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    alen = torch.empty((B,), dtype=torch.int32, device=dev)
+    tok = torch.empty((B, N), dtype=torch.int32, device=dev) if tokens else None
+    _check(lib().verify_tree_rejection(_ptr(probs), probs.stride(1), V, _ptr(draft_tokens),
+                                       _ptr(parents), _ptr(draft_score), _ptr(coins),
+                                       _ptr(bonus_u), B, N, _ptr(path), _ptr(alen), _ptr(tok),
+                                       _stream(dev)))
+    return {"accepted_path": path, "accept_len": alen, "accepted_tokens": tok}
 
 
 def tree_attention_mla_workspace_size(B: int, R: int, Hq: int, Dc: int, Dr: int,

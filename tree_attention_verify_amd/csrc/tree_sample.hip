@@ -235,6 +235,306 @@ SamplePlan sample_plan(int B, int N, int V) {
     return p;
 }
 
+// ---------------------------------------------------------------------------
+// Tree rejection sampling ("From Greedy to Sampling ...", section "The
+// Implementation": a node's children are tried in descending draft
+// probability and the first passing the rejection test is accepted;
+// "Draft-tree speculation", section "Sampled verify keys noise by position":
+// recursive rejection sampling is exact in distribution).  The draft tokens
+// are fixed candidates: child c of node cur (token x) is accepted when
+// coin[c] * (S - E) < w(x), with w the node's target row (positive finite
+// entries, else 0), S its total and E the mass of the tokens already
+// rejected there, which leave the residual; the walk ends with a bonus token
+// drawn from the residual by inverse CDF.
+//
+// One workgroup of 16 waves per request.  A visited row is read once: each
+// wave sums 256-token tiles (eight 1 KB tiles in flight per wave, their
+// butterflies side by side), keeping every tile sum in LDS.  Meanwhile lane
+// j of wave 0 loads the weight of child j's token; with the row total, wave
+// 0 then tests every child at once: its rank in the trying order, whether
+// its token repeats an earlier sibling's, and the weight E of the distinct
+// tokens before it come from a pass over the children (readlane), and the
+// accepted child is the lowest-ranked one whose test passes.  At the last
+// node the tiles holding rejected tokens are summed again without them;
+// wave 0 scans the tile sums to the tile where the running sum passes
+// u * total, then that tile's lanes (four tokens each) to the token.
+constexpr int kRejWaves = 16;
+constexpr int kRejThreads = 64 * kRejWaves;
+constexpr int kRejTile = 256;                    // tokens per tile: 64 lanes x 4
+constexpr int kRejMaxV = 1 << 20;
+constexpr int kRejMaxTiles = kRejMaxV / kRejTile;
+constexpr int kRejBatch = 8;                     // tiles per wave in flight
+
+struct RejArgs {
+    const float *probs;
+    int64_t row_stride;
+    int32_t V, N;
+    const int32_t *draft, *parents;
+    const float *score, *coins, *bonus_u;
+    int32_t *path, *accept_len, *tokens;
+};
+
+__device__ inline float rej_w(float p) { return (p > 0.f && p < INFINITY) ? p : 0.f; }
+
+// sum over the 64 lanes; every lane gets the same value (the butterfly adds
+// the same two operands on both partners)
+__device__ inline float rej_wave_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1)
+        x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+// inclusive prefix sum over the 64 lanes
+__device__ inline float rej_wave_scan(float x, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_up(x, d, 64);
+        if (lane >= d)
+            x += y;
+    }
+    return x;
+}
+
+__global__ void __launch_bounds__(kRejThreads) k_verify_rejection(RejArgs a) {
+    __shared__ float tsum[kRejMaxTiles];
+    __shared__ float wpart[kRejWaves];
+    __shared__ int32_t s_par[64], s_dr[64], s_path[64], s_rej[64];
+    __shared__ float s_sc[64], s_coin[64], s_bu[64];
+    __shared__ int s_next, s_nrej, s_bonus;
+
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int N = a.N, V = a.V;
+    const int64_t nb = (int64_t)b * N;
+    if (tid < N) {
+        s_par[tid] = a.parents[nb + tid];
+        s_dr[tid] = a.draft[nb + tid];
+        s_sc[tid] = a.score ? a.score[nb + tid] : 0.f;
+        s_coin[tid] = a.coins[nb + tid];
+        s_bu[tid] = a.bonus_u[nb + tid];
+    }
+    if (tid == 0)
+        s_path[0] = 0;
+    __syncthreads();
+
+    const int ntiles = (V + kRejTile - 1) / kRejTile;
+    const int nfull = V / kRejTile;   // whole tiles
+    int cur = 0, len = 1;
+    const float *row;
+    for (;;) {
+        row = a.probs + (nb + cur) * a.row_stride;
+        // wave 0, lane j = node j: a child's token weight, loaded before the
+        // row's pass so that its latency overlaps it
+        const bool is_child = w == 0 && lane < N && len < N && s_par[lane] == cur;
+        const int xj = lane < N ? s_dr[lane] : -1;
+        const bool valid = is_child && xj >= 0 && xj < V;
+        const float wx = valid ? rej_w(row[xj]) : 0.f;
+        // tile sums of the row and this wave's share of the total: whole
+        // tiles with unconditional loads (a batch past the end rereads the
+        // last whole tile and drops it), then the partial tile
+        float acc = 0.f;
+        for (int t0 = w * kRejBatch; t0 < nfull; t0 += kRejWaves * kRejBatch) {
+            float4 x[kRejBatch];
+#pragma unroll
+            for (int i = 0; i < kRejBatch; ++i)
+                x[i] = *(const float4 *)(row + min(t0 + i, nfull - 1) * kRejTile + lane * 4);
+            // the batch's butterflies side by side (the same sums as
+            // rej_wave_sum, one wait per step instead of one per tile)
+            float ls[kRejBatch];
+#pragma unroll
+            for (int i = 0; i < kRejBatch; ++i)
+                ls[i] = (rej_w(x[i].x) + rej_w(x[i].y)) + (rej_w(x[i].z) + rej_w(x[i].w));
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1)
+#pragma unroll
+                for (int i = 0; i < kRejBatch; ++i)
+                    ls[i] += __shfl_xor(ls[i], m, 64);
+#pragma unroll
+            for (int i = 0; i < kRejBatch; ++i) {
+                if (t0 + i < nfull) {
+                    if (lane == 0)
+                        tsum[t0 + i] = ls[i];
+                    acc += ls[i];
+                }
+            }
+        }
+        if (nfull < ntiles && w == kRejWaves - 1) {
+            const int v0 = nfull * kRejTile + lane * 4;
+            float r[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                r[e] = v0 + e < V ? rej_w(row[v0 + e]) : 0.f;
+            const float s = rej_wave_sum((r[0] + r[1]) + (r[2] + r[3]));
+            if (lane == 0)
+                tsum[nfull] = s;
+            acc += s;
+        }
+        if (lane == 0)
+            wpart[w] = acc;
+        __syncthreads();
+        if (w == 0) {
+            float S = 0.f;
+            for (int i = 0; i < kRejWaves; ++i)
+                S += wpart[i];
+            // Siblings are tried in descending draft score, the lower index on
+            // ties: child j's rank counts the children before it, E_j the
+            // weight of the distinct valid tokens before it (all rejected if
+            // the walk reaches j), and a token repeating an earlier sibling's
+            // has no residual weight.
+            const float scj = lane < N ? s_sc[lane] : 0.f;
+            const uint64_t cm = __ballot(is_child), vmask = __ballot(valid);
+            auto lane_f = [](float v, int i) {
+                return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), i));
+            };
+            int rank = 0;
+            bool dup = false;
+            for (uint64_t m = cm; m; m &= m - 1) {   // the children only, i wave-uniform
+                const int i = __builtin_ctzll(m);
+                const float sci = lane_f(scj, i);
+                const int xi = __builtin_amdgcn_readlane(xj, i);
+                const bool before = sci > scj || (sci == scj && i < lane);
+                rank += before ? 1 : 0;
+                dup = dup || (before && ((vmask >> i) & 1) && xi == xj);
+            }
+            const uint64_t fmask = __ballot(valid && !dup);
+            float Ej = 0.f;
+            for (uint64_t m = cm; m; m &= m - 1) {
+                const int i = __builtin_ctzll(m);
+                const float sci = lane_f(scj, i);
+                const float wi = lane_f(wx, i);
+                const bool before = sci > scj || (sci == scj && i < lane);
+                Ej += (before && ((fmask >> i) & 1)) ? wi : 0.f;
+            }
+            const float wxe = valid && !dup ? wx : 0.f;
+            const bool pass = is_child && s_coin[lane < N ? lane : 0] * (S - Ej) < wxe;
+            // the first passing child in the trying order
+            int best = pass ? rank : 64;
+#pragma unroll
+            for (int m = 1; m < 64; m <<= 1)
+                best = min(best, __shfl_xor(best, m, 64));
+            const uint64_t win = __ballot(pass && rank == best);
+            const int next = win ? __builtin_ctzll(win) : -1;
+            // tokens rejected at this node when the walk stops here: every
+            // valid child token
+            const uint64_t vm = __ballot(valid);
+            if (valid)
+                s_rej[__builtin_popcountll(vm & ((1ull << lane) - 1))] = xj;
+            if (lane == 0) {
+                s_next = next;
+                s_nrej = next >= 0 ? 0 : __builtin_popcountll(vm);
+                if (next >= 0)
+                    s_path[len] = next;
+            }
+        }
+        __syncthreads();
+        const int next = s_next;
+        if (next < 0)
+            break;
+        cur = next;
+        ++len;
+    }
+
+    // the bonus: tiles holding rejected tokens summed again without them
+    const int nrej = s_nrej;
+    for (int i = w; i < nrej; i += kRejWaves) {
+        const int t = s_rej[i] / kRejTile;
+        const int v0 = t * kRejTile + lane * 4;
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int v = v0 + e;
+            r[e] = v < V ? rej_w(row[v]) : 0.f;
+            for (int k = 0; k < nrej; ++k)
+                r[e] = s_rej[k] == v ? 0.f : r[e];
+        }
+        const float s = rej_wave_sum((r[0] + r[1]) + (r[2] + r[3]));
+        if (lane == 0)
+            tsum[t] = s;   // waves sharing a tile write the same value
+    }
+    __syncthreads();
+    if (w == 0) {
+        // running sums over the tiles, 64 at a time, the same arithmetic in
+        // both passes
+        float run = 0.f;
+        for (int t0 = 0; t0 < ntiles; t0 += 64) {
+            const float x = t0 + lane < ntiles ? tsum[t0 + lane] : 0.f;
+            run += __shfl(rej_wave_scan(x, lane), 63, 64);
+        }
+        const float total = run;
+        const float target = s_bu[cur] * total;
+        int k = -1, last = -1;
+        float before = 0.f;
+        run = 0.f;
+        for (int t0 = 0; t0 < ntiles && k < 0; t0 += 64) {
+            const float x = t0 + lane < ntiles ? tsum[t0 + lane] : 0.f;
+            const float inc = rej_wave_scan(x, lane);
+            const float up = __shfl_up(inc, 1, 64);
+            const float exc = lane > 0 ? up : 0.f;
+            const uint64_t pass = __ballot(run + inc > target && x > 0.f);
+            const uint64_t pos = __ballot(x > 0.f);
+            if (pos)
+                last = t0 + 63 - __builtin_clzll(pos);
+            if (pass) {
+                const int l = __builtin_ctzll(pass);
+                k = t0 + l;
+                before = run + __shfl(exc, l, 64);
+            }
+            run += __shfl(inc, 63, 64);
+        }
+        int bonus = 0;
+        if (total > 0.f) {
+            const bool crossed = k >= 0;
+            if (!crossed)
+                k = last;
+            // tile k: lane l holds its tokens 4 l .. 4 l + 3 (rejected ones
+            // zeroed); the first lane whose running sum passes the target
+            // scans its four
+            const int v0 = k * kRejTile + lane * 4;
+            float r[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int v = v0 + e;
+                r[e] = v < V ? rej_w(row[v]) : 0.f;
+                for (int j = 0; j < nrej; ++j)
+                    r[e] = s_rej[j] == v ? 0.f : r[e];
+            }
+            const float ls = ((r[0] + r[1]) + r[2]) + r[3];
+            const float inc = rej_wave_scan(ls, lane);
+            const float up = __shfl_up(inc, 1, 64);
+            const float exc = lane > 0 ? up : 0.f;
+            const uint64_t hit = __ballot(crossed && ls > 0.f && before + inc > target);
+            const uint64_t nz = __ballot(ls > 0.f);
+            // no lane passes only through rounding: the tile's last positive token
+            const int l = hit ? __builtin_ctzll(hit) : (nz ? 63 - __builtin_clzll(nz) : 0);
+            int e_pick = -1, e_last = -1;
+            float cum = before + exc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (r[e] > 0.f) {
+                    e_last = e;
+                    cum += r[e];
+                    if (hit && e_pick < 0 && cum > target)
+                        e_pick = e;
+                }
+            }
+            const int e_sel = e_pick >= 0 ? e_pick : e_last;
+            bonus = k * kRejTile + 4 * l + __shfl(e_sel < 0 ? 0 : e_sel, l, 64);
+        }
+        if (lane == 0)
+            s_bonus = bonus;
+    }
+    __syncthreads();
+    if (tid < N) {
+        const int p = tid < len ? s_path[tid] : -1;
+        a.path[nb + tid] = p;
+        if (a.tokens)
+            a.tokens[nb + tid] = tid + 1 < len ? s_dr[s_path[tid + 1]] : (tid + 1 == len ? s_bonus : -1);
+    }
+    if (tid == 0)
+        a.accept_len[b] = len;
+}
+
 inline hipStream_t S(void *s) { return (hipStream_t)s; }
 
 }  // namespace
@@ -310,4 +610,49 @@ extern "C" tav_status tree_sample_gumbel(const void *logits, tav_dtype dtype, in
     hipLaunchKernelGGL(k_gumbel_reduce, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, S(stream),
                        a, rows);
     return tav::launched("tree_sample_gumbel");
+}
+
+extern "C" tav_status verify_tree_rejection(const float *probs, int64_t row_stride, int32_t V,
+                                            const int32_t *draft_tokens, const int32_t *parents,
+                                            const float *draft_score, const float *coins,
+                                            const float *bonus_u, int32_t B, int32_t N,
+                                            int32_t *accepted_path, int32_t *accept_len,
+                                            int32_t *accepted_tokens, void *stream) {
+    Checks c;
+    c.need(B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
+    c.need(N >= 1 && N <= 64, TAV_ERR_INVALID_ARG, "N must be in [1, 64], got " + str(N));
+    c.need(V >= 1 && V <= kRejMaxV, TAV_ERR_INVALID_ARG,
+           "V must be in [1, " + str(kRejMaxV) + "], got " + str(V));
+    c.need(row_stride >= V, TAV_ERR_INVALID_ARG,
+           "row_stride must be >= V, got " + str(row_stride) + " < " + str(V));
+    c.need(row_stride % 4 == 0, TAV_ERR_INVALID_ARG,
+           "row_stride must be a multiple of 4 elements, got " + str(row_stride));
+    c.need((long long)B * N * row_stride < (1LL << 62), TAV_ERR_INVALID_ARG, "probs too large");
+    if (B > 0) {
+        c.need(probs, TAV_ERR_INVALID_ARG, "probs is NULL");
+        c.need(((uintptr_t)probs & 15) == 0, TAV_ERR_INVALID_ARG, "probs is not 16-byte aligned");
+        c.need(draft_tokens, TAV_ERR_INVALID_ARG, "draft_tokens is NULL");
+        c.need(parents, TAV_ERR_INVALID_ARG, "parents is NULL");
+        c.need(coins, TAV_ERR_INVALID_ARG, "coins is NULL");
+        c.need(bonus_u, TAV_ERR_INVALID_ARG, "bonus_u is NULL");
+        c.need(accepted_path, TAV_ERR_INVALID_ARG, "accepted_path is NULL");
+        c.need(accept_len, TAV_ERR_INVALID_ARG, "accept_len is NULL");
+    }
+    if (c.status != TAV_OK || B == 0)
+        return tav::finish("verify_tree_rejection", c);
+    RejArgs a{};
+    a.probs = probs;
+    a.row_stride = row_stride;
+    a.V = V;
+    a.N = N;
+    a.draft = draft_tokens;
+    a.parents = parents;
+    a.score = draft_score;
+    a.coins = coins;
+    a.bonus_u = bonus_u;
+    a.path = accepted_path;
+    a.accept_len = accept_len;
+    a.tokens = accepted_tokens;
+    hipLaunchKernelGGL(k_verify_rejection, dim3((unsigned)B), dim3(kRejThreads), 0, S(stream), a);
+    return tav::launched("verify_tree_rejection");
 }

@@ -385,6 +385,75 @@ def make_sample_inputs(B: int, N: int, V: int, seed: int, dtype: str = "bf16",
     return SampleInputs(buf[:, :, :V], temperature, seeds)
 
 
+@dataclasses.dataclass
+class RejectionInputs:
+    probs: torch.Tensor          # float32 [B][N][V] (a view when the rows are padded)
+    parents: np.ndarray          # int32 [B][N]
+    draft: np.ndarray            # int32 [B][N]
+    draft_score: np.ndarray      # float32 [B][N]
+    coins: np.ndarray            # float32 [B][N], uniform in [0, 1)
+    bonus_u: np.ndarray          # float32 [B][N], uniform in [0, 1)
+
+
+def make_rejection_inputs(B: int, N: int, V: int, seed: int, device="cpu", tree: str = "eagle",
+                          scale: float = 2.0, row_stride: Optional[int] = None,
+                          agree: float = 0.75) -> RejectionInputs:
+    """Seeded inputs of the sampled verify by rejection.  Trees: EAGLE top-8
+    beam, random (depth <= 6) or a chain.  The target row after each node is
+    a mix of softmax(N(0, scale^2)) and a point mass on a "hot" token of
+    weight U(0.3, 0.9), in fp32.  A parent's first child drafts the hot token
+    with probability `agree` and otherwise, like every later sibling, a
+    token drawn from the parent's softmax part; a node's draft score is its
+    parent's target probability of its token.  Coins and bonus draws are
+    uniform fp32 in [0, 1).  row_stride > V pads the rows with NaN, which the
+    walk never reads."""
+    r = _streams(seed + 15485863, 1)[0]
+    if tree == "eagle":
+        parents = np.stack([eagle_tree(r, 8, 6, N) for _ in range(B)])
+    elif tree == "chain":
+        parents = np.tile(chain_tree(N), (B, 1))
+    else:
+        parents = np.stack([random_tree(r, N, 6) for _ in range(B)])
+    parents = parents.astype(np.int32)
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(_torch_seed(seed, 13))
+    rs = V if row_stride is None else row_stride
+    buf = torch.full((B, N, rs), float("nan"), dtype=torch.float32, device=dev)
+    logits = torch.empty((B, N, V), dtype=torch.float32, device=dev)
+    _randn_into(logits, g)
+    p0 = torch.softmax(logits * scale, -1)
+    del logits
+    hot = r.integers(0, V, (B, N))
+    mix = r.uniform(0.3, 0.9, (B, N)).astype(np.float32)
+    p = p0 * torch.as_tensor(1.0 - mix, device=dev)[..., None]
+    p.view(B * N, V)[torch.arange(B * N, device=dev), torch.as_tensor(hot.reshape(-1), device=dev)] += \
+        torch.as_tensor(mix.reshape(-1), device=dev)
+    buf[:, :, :V] = p
+    draws = torch.multinomial(p0.view(B * N, V), 8, replacement=True, generator=g)
+    draws = draws.view(B, N, 8).cpu().numpy()
+    del p0
+    draft = np.zeros((B, N), np.int32)
+    for b in range(B):
+        seen = {}
+        for c in range(1, N):
+            n = int(parents[b, c])
+            j = seen.get(n, 0)
+            seen[n] = j + 1
+            if j == 0 and r.random() < agree:
+                draft[b, c] = hot[b, n]
+            else:
+                draft[b, c] = draws[b, n, j % 8]
+    par_c = np.maximum(parents, 0)
+    score = p[torch.as_tensor(np.arange(B)[:, None], device=dev),
+              torch.as_tensor(par_c, device=dev), torch.as_tensor(draft.astype(np.int64), device=dev)]
+    score = score.cpu().numpy().astype(np.float32)
+    score[:, 0] = 1.0
+    coins = r.random((B, N), dtype=np.float32)
+    bonus_u = r.random((B, N), dtype=np.float32)
+    return RejectionInputs(buf[:, :, :V], parents, draft, score, coins, bonus_u)
+
+
 # ---------------------------------------------------------------------------
 # MLA latent-cache inputs
 # ---------------------------------------------------------------------------
