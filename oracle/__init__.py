@@ -85,6 +85,8 @@ def lib():
         L.orc_verify_greedy.argtypes = [P, P, P, I, I, P, P, P]
         L.orc_verify_rejection.argtypes = [P, I64, I, P, P, P, P, P, I, I, P, P, P, P]
         L.orc_verify_rejection.restype = ctypes.c_int
+        L.orc_verify_rejection_q.argtypes = [P, I64, P, I64, I, P, P, P, P, P, I, I, P, P, P, P]
+        L.orc_verify_rejection_q.restype = ctypes.c_int
         L.orc_compact_rows.argtypes = [ctypes.POINTER(OrcRows), I, P, P, I, I]
         for f in ("orc_build_masks", "orc_shift_positions", "orc_tree_attention",
                   "orc_causal_attention", "orc_merge", "orc_verify_greedy",
@@ -261,6 +263,31 @@ def verify_rejection(probs, draft, parents, coins, bonus_u, draft_score=None):
                                       None if sc is None else _p(sc), _p(coins), _p(bonus_u),
                                       B, N, _p(path), _p(alen), _p(tok), _p(margin)),
            "verify_rejection")
+    return {"accepted_path": path, "accept_len": alen, "accepted_tokens": tok, "margin": margin}
+
+
+def verify_rejection_q(probs, draft_q, draft, parents, coins, bonus_u, draft_score=None):
+    """Tree rejection sampling against the draft distribution of each node's
+    children ([DTS] "Sampled verify keys noise by position"): draft_q
+    float32 [B][N][V], row n the distribution that drew node n's children;
+    the rest as verify_rejection."""
+    probs = _c(probs, np.float32)
+    draft_q = _c(draft_q, np.float32)
+    draft = _c(draft, np.int32)
+    parents = _c(parents, np.int32)
+    coins = _c(coins, np.float32)
+    bonus_u = _c(bonus_u, np.float32)
+    B, N, V = probs.shape
+    assert draft_q.shape == (B, N, V)
+    sc = None if draft_score is None else _c(draft_score, np.float32)
+    path = np.empty((B, N), np.int32)
+    alen = np.empty((B,), np.int32)
+    tok = np.empty((B, N), np.int32)
+    margin = np.empty((B,), np.float64)
+    _check(lib().orc_verify_rejection_q(_p(probs), V, _p(draft_q), V, V, _p(draft), _p(parents),
+                                        None if sc is None else _p(sc), _p(coins), _p(bonus_u),
+                                        B, N, _p(path), _p(alen), _p(tok), _p(margin)),
+           "verify_rejection_q")
     return {"accepted_path": path, "accept_len": alen, "accepted_tokens": tok, "margin": margin}
 
 

@@ -1100,3 +1100,123 @@ int orc_verify_rejection(const float *probs, int64_t row_stride, int V,
     }
     return ORC_OK;
 }
+
+/*
+ * The same walk tested against the draft distribution that drew each node's
+ * children ([DTS] "Sampled verify keys noise by position": recursive
+ * rejection sampling against the draft q of a node's children, exact in
+ * distribution).  At node cur the residual starts as r = w / S (w, S as
+ * above) and q = draft_q[cur] (positive finite entries, else 0) over its
+ * total Q.  Child c (token x) is accepted when
+ *     coin[c] * q(x) / Q < r(x)           (probability min(1, r(x) / q(x)))
+ * (x outside [0, V) is rejected); otherwise r becomes max(0, r - q / Q)
+ * normalised (all zero when nothing is left).  The bonus is drawn from the
+ * final r as above (token 0 when r is all zero).  This is exact when the
+ * children are independent draws from q tested in an order that does not
+ * depend on the drawn tokens (the multi-candidate speculative sampling
+ * argument).  Outputs as orc_verify_rejection; margin covers the tests.
+ */
+int orc_verify_rejection_q(const float *probs, int64_t row_stride, const float *draft_q,
+                           int64_t q_row_stride, int V, const int32_t *draft,
+                           const int32_t *parents, const float *draft_score,
+                           const float *coins, const float *bonus_u, int B, int N,
+                           int32_t *path, int32_t *accept_len, int32_t *tokens, double *margin)
+{
+    if (N < 1 || N > 64 || V < 1 || row_stride < V || q_row_stride < V)
+        return ORC_BAD;
+    double *r = malloc(sizeof(double) * (size_t)V);
+    if (!r)
+        return ORC_BAD;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *dr = draft + (int64_t)b * N;
+        const int32_t *par = parents + (int64_t)b * N;
+        int32_t *pb = path + (int64_t)b * N;
+        double mg = INFINITY;
+        for (int k = 0; k < N; ++k)
+            pb[k] = -1;
+        int len = 0, cur = 0;
+        pb[len++] = cur;
+        int bonus = 0;
+        for (;;) {
+            const float *row = probs + ((int64_t)b * N + cur) * row_stride;
+            const float *qrow = draft_q + ((int64_t)b * N + cur) * q_row_stride;
+            double S = 0.0, Q = 0.0;
+            for (int v = 0; v < V; ++v) {
+                S += orc_tw(row[v]);
+                Q += orc_tw(qrow[v]);
+            }
+            for (int v = 0; v < V; ++v)
+                r[v] = S > 0.0 ? orc_tw(row[v]) / S : 0.0;
+            int next = -1;
+            if (len < N) {
+                int tried[64] = {0};
+                for (;;) {
+                    int c = -1;
+                    for (int j = 0; j < N; ++j) {
+                        if (par[j] != cur || tried[j])
+                            continue;
+                        if (c < 0 || (draft_score && draft_score[(int64_t)b * N + j] >
+                                                         draft_score[(int64_t)b * N + c]))
+                            c = j;
+                    }
+                    if (c < 0)
+                        break;
+                    tried[c] = 1;
+                    const int x = dr[c];
+                    if (x >= 0 && x < V) {
+                        const double qx = Q > 0.0 ? orc_tw(qrow[x]) / Q : 0.0;
+                        const double lhs = (double)coins[(int64_t)b * N + c] * qx;
+                        if (fabs(lhs - r[x]) < mg)
+                            mg = fabs(lhs - r[x]);
+                        if (lhs < r[x]) {
+                            next = c;
+                            break;
+                        }
+                    }
+                    /* rejected: the residual max(0, r - q) renormalised */
+                    double Z = 0.0;
+                    for (int v = 0; v < V; ++v) {
+                        const double qv = Q > 0.0 ? orc_tw(qrow[v]) / Q : 0.0;
+                        r[v] = r[v] > qv ? r[v] - qv : 0.0;
+                        Z += r[v];
+                    }
+                    for (int v = 0; v < V; ++v)
+                        r[v] = Z > 0.0 ? r[v] / Z : 0.0;
+                }
+            }
+            if (next >= 0) {
+                cur = next;
+                pb[len++] = cur;
+                continue;
+            }
+            double T = 0.0;
+            for (int v = 0; v < V; ++v)
+                T += r[v];
+            bonus = 0;
+            if (T > 0.0) {
+                const double target = (double)bonus_u[(int64_t)b * N + cur] * T;
+                double run = 0.0;
+                int last_pos = -1, found = -1;
+                for (int v = 0; v < V && found < 0; ++v) {
+                    if (r[v] <= 0.0)
+                        continue;
+                    last_pos = v;
+                    run += r[v];
+                    if (run > target)
+                        found = v;
+                }
+                bonus = found >= 0 ? found : last_pos;
+            }
+            break;
+        }
+        accept_len[b] = len;
+        if (tokens)
+            for (int k = 0; k < N; ++k)
+                tokens[(int64_t)b * N + k] =
+                    k + 1 < len ? dr[pb[k + 1]] : (k + 1 == len ? bonus : -1);
+        if (margin)
+            margin[b] = mg;
+    }
+    free(r);
+    return ORC_OK;
+}

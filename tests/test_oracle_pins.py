@@ -912,6 +912,63 @@ def test_rejection_bonus_is_the_inverse_cdf():
     assert int(r["accepted_tokens"][0, 0]) == 0
 
 
+def test_rejection_against_q_emits_the_target_law():
+    """[DTS] "Sampled verify keys noise by position": recursive rejection
+    sampling against the draft q that drew a node's children is exact.
+    40000 walks: the root's three children and node 1's two are drawn
+    independently from their parent's q each time and tried in index order;
+    the first emitted token follows the root's target law and the second,
+    through node 1, node 1's (chi-square, 4 dof)."""
+    rng = np.random.default_rng(23)
+    V, N, B = 5, 6, 40000
+    par = np.array([-1, 0, 0, 0, 1, 1], np.int32)
+    p = (rng.dirichlet(np.ones(V), N) * rng.uniform(0.5, 3.0, (N, 1))).astype(np.float32)
+    q = (rng.dirichlet(np.ones(V) * 0.8, N) * rng.uniform(0.5, 3.0, (N, 1))).astype(np.float32)
+    qn = q.astype(np.float64) / q.astype(np.float64).sum(1, keepdims=True)
+    draft = np.zeros((B, N), np.int32)
+    for c in range(1, N):
+        draft[:, c] = rng.choice(V, size=B, p=qn[par[c]])
+    r = oracle.verify_rejection_q(np.broadcast_to(p, (B, N, V)), np.broadcast_to(q, (B, N, V)),
+                                  draft, np.tile(par, (B, 1)), rng.random((B, N), np.float32),
+                                  rng.random((B, N), np.float32))
+    assert _chi2(r["accepted_tokens"][:, 0], p[0].astype(np.float64), V) < 20.5
+    sel = (r["accept_len"] >= 2) & (r["accepted_path"][:, 1] == 1)
+    assert sel.sum() > 3000
+    assert _chi2(r["accepted_tokens"][sel, 1], p[1].astype(np.float64), V) < 20.5
+
+
+def test_rejection_against_q_special_cases():
+    """q equal to the target accepts the first child tried whenever its token
+    has weight (min(1, p / q) = 1); on a chain whose q rows are one-hot on the
+    drafted token the walk is the fixed-candidate walk."""
+    rng = np.random.default_rng(24)
+    B, N, V = 200, 8, 30
+    par = np.stack([gen.random_tree(rng, N, 4) for _ in range(B)]).astype(np.int32)
+    p = rng.random((B, N, V)).astype(np.float32) + 0.01
+    draft = rng.integers(0, V, (B, N)).astype(np.int32)
+    coins = rng.random((B, N), np.float32)
+    bu = rng.random((B, N), np.float32)
+    r = oracle.verify_rejection_q(p, p, draft, par, coins, bu)
+    for b in range(B):
+        L = int(r["accept_len"][b])
+        path = r["accepted_path"][b, :L]
+        for k in range(L - 1):      # each step took the lowest-index child
+            kids = np.nonzero(par[b] == path[k])[0]
+            assert path[k + 1] == kids.min()
+        assert not (par[b] == path[-1]).any() or L == N
+    chain = np.tile(np.arange(-1, N - 1, dtype=np.int32), (B, 1))
+    q1 = np.zeros((B, N, V), np.float32)
+    for n in range(N - 1):
+        q1[np.arange(B), n, draft[:, n + 1]] = 1.0
+    q1[:, N - 1, 0] = 1.0
+    a = oracle.verify_rejection_q(p, q1, draft, chain, coins, bu)
+    f = oracle.verify_rejection(p, draft, chain, coins, bu)
+    same = (a["accepted_path"] == f["accepted_path"]).all(1) & (a["accept_len"] == f["accept_len"])
+    assert same.mean() > 0.99 and (a["accept_len"] > 1).any()
+    ok = same & (a["accepted_tokens"] == f["accepted_tokens"]).all(1)
+    assert ok.mean() > 0.99
+
+
 # ---------------------------------------------------------------------------
 # tree construction: beam, selection, numbering, links
 # ---------------------------------------------------------------------------
