@@ -378,7 +378,9 @@ def run_rejection(args):
     the algorithmic bytes are sum_b accept_len[b] * V * 4."""
     L = tav.lib()
     B, N, V = 32, 64, gen.SAMPLE_VOCAB
-    x = gen.make_rejection_inputs(B, N, V, args.seed, "cuda", tree="eagle")
+    with_q = args.rejection_q
+    x = gen.make_rejection_inputs(B, N, V, args.seed, "cuda", tree="eagle", with_q=with_q)
+    qptr, qstride = (x.draft_q.data_ptr(), x.draft_q.stride(1)) if with_q else (None, 0)
     t = lambda a, dt=torch.int32: torch.as_tensor(np.ascontiguousarray(a)).to(dt).to("cuda")
     draft, parents = t(x.draft), t(x.parents)
     score, coins, bu = t(x.draft_score, torch.float32), t(x.coins, torch.float32), \
@@ -390,7 +392,8 @@ def run_rejection(args):
     probs = x.probs
 
     def run():
-        assert L.verify_tree_rejection(probs.data_ptr(), probs.stride(1), V, draft.data_ptr(),
+        assert L.verify_tree_rejection(probs.data_ptr(), probs.stride(1), V, qptr, qstride,
+                                       draft.data_ptr(),
                                        parents.data_ptr(), score.data_ptr(), coins.data_ptr(),
                                        bu.data_ptr(), B, N, path.data_ptr(), alen.data_ptr(),
                                        toks.data_ptr(), stream) == 0
@@ -406,17 +409,19 @@ def run_rejection(args):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     visited = int(alen.sum().item())
-    nbytes = visited * V * 4
+    nbytes = visited * V * 4 * (2 if with_q else 1)
     gbs = nbytes / (ms * 1e-3) / 1e9
     res = {"metric": REJECTION_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
            "data": "synthetic",
-           "config": {"workload": "rejection verify, %d requests x %d rows (EAGLE top-8 trees), "
-                                  "vocabulary %d, fp32 target rows" % (B, N, V),
+           "config": {"workload": "rejection verify%s, %d requests x %d rows (EAGLE top-8 trees), "
+                                  "vocabulary %d, fp32 target rows"
+                                  % (" against the draft q" if with_q else "", B, N, V),
                       "mean_accept_len": round(visited / B, 3)},
            "rows_per_s": round(B * N / (ms * 1e-3), 1),
-           "roofline": {"kernel": "k_verify_rejection", "bound": "hbm", "achieved": round(gbs, 1),
+           "roofline": {"kernel": "k_verify_rejection_q" if with_q else "k_verify_rejection",
+                        "bound": "hbm", "achieved": round(gbs, 1),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                         "note": "one workgroup per request: %d CUs of 256 stream the rows" % B}}
@@ -428,9 +433,16 @@ def run_rejection(args):
         while total_t < args.cpu_budget and done < B:
             sl = slice(done, min(done + n, B))
             sub = np.ascontiguousarray(probs[sl].cpu().numpy())
+            qsub = np.ascontiguousarray(x.draft_q[sl].cpu().numpy()) if with_q else None
             t0 = time.perf_counter()
-            oracle.verify_rejection(sub, host["draft"][sl], host["parents"][sl], host["coins"][sl],
-                                    host["bonus_u"][sl], host["draft_score"][sl])
+            if with_q:
+                oracle.verify_rejection_q(sub, qsub, host["draft"][sl], host["parents"][sl],
+                                          host["coins"][sl], host["bonus_u"][sl],
+                                          host["draft_score"][sl])
+            else:
+                oracle.verify_rejection(sub, host["draft"][sl], host["parents"][sl],
+                                        host["coins"][sl], host["bonus_u"][sl],
+                                        host["draft_score"][sl])
             total_t += time.perf_counter() - t0
             done = sl.stop
             n = min(2 * n, 8)
@@ -611,6 +623,8 @@ def main():
     ap.add_argument("--rejection", action="store_true",
                     help="time the sampled verify by tree rejection sampling (fp32 target rows "
                          "over a 128256-token vocabulary) instead")
+    ap.add_argument("--rejection-q", action="store_true",
+                    help="the same, testing against the draft distributions (fp32 q rows too)")
     ap.add_argument("--mla", choices=sorted(gen.MLA_WORKLOADS),
                     help="time the cascade over an MLA latent cache on this workload instead")
     ap.add_argument("--tree-build", action="store_true",
@@ -640,7 +654,7 @@ def main():
     if args.tree_build:
         run_tree_build(args)
         return
-    if args.rejection:
+    if args.rejection or args.rejection_q:
         run_rejection(args)
         return
     if args.mla:

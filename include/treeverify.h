@@ -331,13 +331,29 @@ tav_status tree_sample_gumbel(const void *logits, tav_dtype dtype, int64_t row_s
  * lowest v whose running sum of r exceeds bonus_u[cur] * sum_v r(v) (the
  * last v of positive residual if rounding leaves none; token 0 if r is all
  * zero).  The token emitted at every depth is then distributed as the
- * target row there.  Sums are fp32 in the kernel's order, so a decision
- * within rounding of a tie may differ from an exact evaluation.
+ * target row there.
+ *
+ * With draft_q given, the children are tested against the draft
+ * distribution that drew them ([DTS] "Sampled verify keys noise by
+ * position": recursive rejection sampling against the draft q of a node's
+ * children).  At node cur the residual starts as r = w / S, q^ = q / Q with
+ * q = draft_q[cur] (positive finite entries) and Q its total; child c (token
+ * x) is accepted when coins[c] * q^(x) < r(x), probability min(1, r(x) /
+ * q^(x)); otherwise r becomes max(0, r - q^) renormalised (all zero when
+ * nothing is left).  The bonus is drawn from the final r as above.  This is
+ * exact when the children are independent draws from q tested in an order
+ * that does not depend on the drawn tokens.
+ *
+ * Sums are fp32 in the kernel's order, so a decision within rounding of a
+ * tie may differ from an exact evaluation.
  *
  * probs        device fp32 [B][N][row_stride], V used per row: the target
  *              distribution after the node (softmax at the sampling
  *              temperature; rows need not sum to 1); 16-byte aligned,
  *              row_stride >= V and a multiple of 4
+ * draft_q      device fp32 [B][N][q_row_stride] or NULL: row n is the draft
+ *              distribution that drew node n's children; 16-byte aligned,
+ *              q_row_stride >= V and a multiple of 4
  * draft_tokens, parents  int32 [B][N] (parents[0] = -1 is the root)
  * draft_score  fp32 [B][N] or NULL: the sibling order (e.g. the draft
  *              probability of each node's token)
@@ -349,6 +365,7 @@ tav_status tree_sample_gumbel(const void *logits, tav_dtype dtype, int64_t row_s
  * B >= 0; 1 <= N <= 64; 1 <= V <= 2^20
  */
 tav_status verify_tree_rejection(const float *probs, int64_t row_stride, int32_t V,
+                                 const float *draft_q, int64_t q_row_stride,
                                  const int32_t *draft_tokens, const int32_t *parents,
                                  const float *draft_score, const float *coins,
                                  const float *bonus_u, int32_t B, int32_t N,

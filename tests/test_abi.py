@@ -191,10 +191,11 @@ def test_sample_empty_batch_is_a_no_op(L):
 
 
 def rejection_call(L, **kw):
-    a = dict(probs=FAKE, rs=128256, V=128256, draft=FAKE, par=FAKE, score=None, coins=FAKE,
-             bu=FAKE, B=4, N=64, path=FAKE, alen=FAKE, tok=FAKE)
+    a = dict(probs=FAKE, rs=128256, V=128256, q=None, qs=0, draft=FAKE, par=FAKE, score=None,
+             coins=FAKE, bu=FAKE, B=4, N=64, path=FAKE, alen=FAKE, tok=FAKE)
     a.update(kw)
-    st = L.verify_tree_rejection(a["probs"], a["rs"], a["V"], a["draft"], a["par"], a["score"],
+    st = L.verify_tree_rejection(a["probs"], a["rs"], a["V"], a["q"], a["qs"], a["draft"],
+                                 a["par"], a["score"],
                                  a["coins"], a["bu"], a["B"], a["N"], a["path"], a["alen"],
                                  a["tok"], None)
     return st, L.tav_last_error().decode()
@@ -209,6 +210,8 @@ def rejection_call(L, **kw):
     (dict(probs=FAKE + 4), 1, ["16-byte aligned"]),
     (dict(coins=None, bu=None), 1, ["coins is NULL", "bonus_u is NULL"]),
     (dict(path=None), 1, ["accepted_path is NULL"]),
+    (dict(q=FAKE, qs=1000), 1, ["q_row_stride must be >= V"]),
+    (dict(q=FAKE + 8, qs=128258), 1, ["multiple of 4 elements", "draft_q is not 16-byte aligned"]),
 ])
 def test_verify_tree_rejection_rejects(L, kw, status, words):
     st, msg = rejection_call(L, **kw)

@@ -170,3 +170,68 @@ def test_rejection_emits_the_target_law_on_gpu():
     cnt = np.bincount(t1, minlength=V)
     exp = rows[0].astype(np.float64) / rows[0].astype(np.float64).sum() * B
     assert float(((cnt - exp) ** 2 / exp).sum()) < 20.5
+
+
+def _residual_q(p_row, q_row, n_rejected):
+    """fp64 residual after n rejections against q (for the bonus bracket)."""
+    w = np.where(np.isfinite(p_row) & (p_row > 0), p_row, 0).astype(np.float64)
+    qw = np.where(np.isfinite(q_row) & (q_row > 0), q_row, 0).astype(np.float64)
+    r = w / w.sum() if w.sum() > 0 else w
+    qh = qw / qw.sum() if qw.sum() > 0 else qw
+    for _ in range(n_rejected):
+        r = np.maximum(r - qh, 0.0)
+        z = r.sum()
+        r = r / z if z > 0 else r * 0.0
+    return r
+
+
+def run_and_check_q(x, tag=""):
+    B, N, V = x.probs.shape
+    r = tav.verify_tree_rejection(x.probs, dev(x.draft), dev(x.parents), dev(x.coins, torch.float32),
+                                  dev(x.bonus_u, torch.float32),
+                                  draft_score=dev(x.draft_score, torch.float32), draft_q=x.draft_q)
+    torch.cuda.synchronize()
+    ph = np.ascontiguousarray(x.probs.cpu().numpy())
+    qh = np.ascontiguousarray(x.draft_q.cpu().numpy())
+    ref = oracle.verify_rejection_q(ph, qh, x.draft, x.parents, x.coins, x.bonus_u, x.draft_score)
+    path = r["accepted_path"].cpu().numpy()
+    alen = r["accept_len"].cpu().numpy()
+    tok = r["accepted_tokens"].cpu().numpy()
+    walk_same = (path == ref["accepted_path"]).all(1) & (alen == ref["accept_len"])
+    near = ref["margin"] < MARGIN
+    bad = np.nonzero(~walk_same & ~near)[0]
+    assert bad.size == 0, (tag, bad[:5], path[bad[:1]], ref["accepted_path"][bad[:1]])
+    assert (~walk_same).sum() <= max(1, B // 50), tag
+    n_cdf = 0
+    for b in np.nonzero(walk_same)[0]:
+        L = int(alen[b])
+        assert (tok[b, :L - 1] == ref["accepted_tokens"][b, :L - 1]).all()
+        if tok[b, L - 1] == ref["accepted_tokens"][b, L - 1]:
+            continue
+        cur = int(path[b, L - 1])
+        nrej = int((x.parents[b] == cur).sum()) if L < N else 0
+        res = _residual_q(ph[b, cur], qh[b, cur], nrej)
+        c = np.cumsum(res)
+        target = float(x.bonus_u[b, cur]) * c[-1]
+        g = int(tok[b, L - 1])
+        assert res[g] > 0 and c[g] - res[g] <= target + CDF_TOL * c[-1] \
+            and c[g] >= target - CDF_TOL * c[-1], (tag, b, g)
+        n_cdf += 1
+    say(tag, "q form, B %d N %d V %d: %d of %d walks equal (%d near a tie), %d bonus draws off by "
+        "rounding, mean accept_len %.2f" % (B, N, V, int(walk_same.sum()), B, int(near.sum()),
+                                            n_cdf, float(alen.mean())))
+    assert n_cdf <= max(2, B // 4), tag
+
+
+@pytest.mark.parametrize("name", ["eagle_tiles", "random_ragged", "chain_deep", "padded_rows",
+                                  "one_tile"])
+def test_rejection_against_q_parity(name):
+    B, N, V, tree, rs, agree = CASES[name]
+    x = gen.make_rejection_inputs(B, N, V, 41, "cuda", tree=tree, row_stride=rs, agree=agree,
+                                  with_q=True)
+    run_and_check_q(x, tag="q " + name)
+
+
+def test_rejection_against_q_full_size():
+    x = gen.make_rejection_inputs(32, 64, gen.SAMPLE_VOCAB, 4, "cuda", tree="eagle", with_q=True)
+    run_and_check_q(x, tag="q full size")

@@ -105,7 +105,8 @@ def lib() -> ctypes.CDLL:
         L.tree_attention_mla.argtypes = [P, P, ctypes.c_int, I64, I64, I64, P, I32, I32, P, I32,
                                          P, I32, I32, I32, I32, I32, I32, ctypes.c_float, P, P, P,
                                          ctypes.c_size_t, P]
-        L.verify_tree_rejection.argtypes = [P, I64, I32, P, P, P, P, P, I32, I32, P, P, P, P]
+        L.verify_tree_rejection.argtypes = [P, I64, I32, P, I64, P, P, P, P, P, I32, I32, P, P, P,
+                                            P]
         for f in ("tree_build_masks", "tree_shift_positions", "tree_attention",
                   "verify_tree_greedy", "compact_window_rows", "tree_sample_gumbel",
                   "tree_beam_step", "tree_select_candidates", "tree_retrieve_links",
@@ -322,13 +323,15 @@ def verify_tree_sampled(draft_tokens: torch.Tensor, logits: torch.Tensor,
 
 def verify_tree_rejection(probs: torch.Tensor, draft_tokens: torch.Tensor, parents: torch.Tensor,
                           coins: torch.Tensor, bonus_u: torch.Tensor,
-                          draft_score: Optional[torch.Tensor] = None, tokens: bool = True):
+                          draft_score: Optional[torch.Tensor] = None, tokens: bool = True,
+                          draft_q: Optional[torch.Tensor] = None):
     """Tree rejection sampling: probs float32 [B][N][V] (the target
     distribution after every node; rows may be padded to a stride of a
     multiple of 4), draft_tokens / parents int32 [B][N], coins / bonus_u
     float32 [B][N] uniform in [0, 1), draft_score float32 [B][N] or None
-    (the sibling order).  -> dict(accepted_path, accept_len,
-    accepted_tokens)."""
+    (the sibling order), draft_q float32 [B][N][V] or None (the draft
+    distribution that drew each node's children: test against it).
+    -> dict(accepted_path, accept_len, accepted_tokens)."""
     if probs.dtype != torch.float32 or not probs.is_cuda or probs.dim() != 3 \
             or probs.stride(2) != 1 or probs.stride(0) != probs.shape[1] * probs.stride(1):
         raise ValueError("probs must be a float32 [B][N][V] GPU tensor with unit channel stride "
@@ -341,10 +344,19 @@ def verify_tree_rejection(probs: torch.Tensor, draft_tokens: torch.Tensor, paren
     _need(bonus_u, "bonus_u", torch.float32, dev, (B, N))
     if draft_score is not None:
         _need(draft_score, "draft_score", torch.float32, dev, (B, N))
+    qs = 0
+    if draft_q is not None:
+        if draft_q.dtype != torch.float32 or draft_q.device != dev or draft_q.dim() != 3 \
+                or tuple(draft_q.shape) != (B, N, V) or draft_q.stride(2) != 1 \
+                or draft_q.stride(0) != N * draft_q.stride(1):
+            raise ValueError("draft_q must be a float32 [B][N][V] tensor on the device of probs "
+                             "with unit channel stride and rows at a constant stride")
+        qs = draft_q.stride(1)
     path = torch.empty((B, N), dtype=torch.int32, device=dev)
     alen = torch.empty((B,), dtype=torch.int32, device=dev)
     tok = torch.empty((B, N), dtype=torch.int32, device=dev) if tokens else None
-    _check(lib().verify_tree_rejection(_ptr(probs), probs.stride(1), V, _ptr(draft_tokens),
+    _check(lib().verify_tree_rejection(_ptr(probs), probs.stride(1), V, _ptr(draft_q), qs,
+                                       _ptr(draft_tokens),
                                        _ptr(parents), _ptr(draft_score), _ptr(coins),
                                        _ptr(bonus_u), B, N, _ptr(path), _ptr(alen), _ptr(tok),
                                        _stream(dev)))

@@ -535,6 +535,252 @@ __global__ void __launch_bounds__(kRejThreads) k_verify_rejection(RejArgs a) {
         a.accept_len[b] = len;
 }
 
+// The walk against the draft distribution q that drew each node's children
+// ("Draft-tree speculation", section "Sampled verify keys noise by
+// position": recursive rejection sampling against that q, exact in
+// distribution).  At node cur the residual starts as r_0 = w / S and q^ =
+// q / Q (positive finite entries); child i (token x) in the trying order is
+// accepted when coin * q^(x) < r_i(x), else r_{i+1} = max(0, r_i - q^) /
+// Z_{i+1}.  r_i(v) depends only on w(v), q(v), S, Q and Z_1 .. Z_i, so a
+// test reads two floats and each rejection costs one pass over both rows
+// for the next Z; the bonus draws from the final residual through tile sums
+// as in k_verify_rejection.
+struct RejQArgs {
+    RejArgs a;
+    const float *q;
+    int64_t q_row_stride;
+};
+
+__global__ void __launch_bounds__(kRejThreads) k_verify_rejection_q(RejQArgs qa) {
+    const RejArgs &a = qa.a;
+    __shared__ float tsum[kRejMaxTiles];
+    __shared__ float red[2][kRejWaves];
+    __shared__ float zs[64];                      // Z_1 .. Z_k of the current node
+    __shared__ int32_t s_par[64], s_dr[64], s_path[64], s_ord[64];
+    __shared__ float s_sc[64], s_coin[64], s_bu[64];
+    __shared__ int s_nk, s_acc, s_bonus;
+
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int N = a.N, V = a.V;
+    const int64_t nb = (int64_t)b * N;
+    if (tid < N) {
+        s_par[tid] = a.parents[nb + tid];
+        s_dr[tid] = a.draft[nb + tid];
+        s_sc[tid] = a.score ? a.score[nb + tid] : 0.f;
+        s_coin[tid] = a.coins[nb + tid];
+        s_bu[tid] = a.bonus_u[nb + tid];
+    }
+    if (tid == 0)
+        s_path[0] = 0;
+    __syncthreads();
+
+    // the sum over the workgroup, the same value in every thread
+    auto block_sum2 = [&](float x, float y, float &sx, float &sy) {
+        x = rej_wave_sum(x);
+        y = rej_wave_sum(y);
+        if (lane == 0) {
+            red[0][w] = x;
+            red[1][w] = y;
+        }
+        __syncthreads();
+        sx = 0.f;
+        sy = 0.f;
+        for (int i = 0; i < kRejWaves; ++i) {
+            sx += red[0][i];
+            sy += red[1][i];
+        }
+        __syncthreads();
+    };
+
+    const int ntiles = (V + kRejTile - 1) / kRejTile;
+    int cur = 0, len = 1, nrej = 0;
+    float S = 0.f, Q = 0.f;
+    const float *row, *qrow;
+    // the residual after k rejections at token v
+    // f(p[v], q[v]) for every token of the two rows of node cur: 16-byte
+    // loads, four of each row in flight per thread, then the tail
+    auto over_rows = [&](auto f) {
+        const int V4 = V >> 2;
+        constexpr int U = 4;
+        for (int i0 = tid; i0 < V4; i0 += U * kRejThreads) {
+            float4 pv[U], qv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = min(i0 + u * kRejThreads, V4 - 1);
+                pv[u] = reinterpret_cast<const float4 *>(row)[i];
+                qv[u] = reinterpret_cast<const float4 *>(qrow)[i];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (i0 + u * kRejThreads < V4) {
+                    f(pv[u].x, qv[u].x);
+                    f(pv[u].y, qv[u].y);
+                    f(pv[u].z, qv[u].z);
+                    f(pv[u].w, qv[u].w);
+                }
+            }
+        }
+        for (int v = 4 * V4 + tid; v < V; v += kRejThreads)
+            f(row[v], qrow[v]);
+    };
+    auto resid = [&](float pv, float qv, int k) {
+        float r = S > 0.f ? rej_w(pv) / S : 0.f;
+        const float qh = Q > 0.f ? rej_w(qv) / Q : 0.f;
+        for (int j = 0; j < k; ++j)
+            r = zs[j] > 0.f ? fmaxf(r - qh, 0.f) / zs[j] : 0.f;
+        return r;
+    };
+    for (;;) {
+        row = a.probs + (nb + cur) * a.row_stride;
+        qrow = qa.q + (nb + cur) * qa.q_row_stride;
+        float sp = 0.f, sq = 0.f;
+        over_rows([&](float pv, float qv) {
+            sp += rej_w(pv);
+            sq += rej_w(qv);
+        });
+        block_sum2(sp, sq, S, Q);
+        // the children in their trying order (wave 0, as k_verify_rejection)
+        if (w == 0) {
+            const bool is_child = lane < N && len < N && s_par[lane] == cur;
+            const float scj = lane < N ? s_sc[lane] : 0.f;
+            const uint64_t cm = __ballot(is_child);
+            int rank = 0;
+            for (uint64_t m = cm; m; m &= m - 1) {
+                const int i = __builtin_ctzll(m);
+                const float sci = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scj), i));
+                rank += (sci > scj || (sci == scj && i < lane)) ? 1 : 0;
+            }
+            if (is_child)
+                s_ord[rank] = lane;
+            if (lane == 0)
+                s_nk = __builtin_popcountll(cm);
+        }
+        __syncthreads();
+        const int nk = s_nk;
+        int next = -1;
+        nrej = 0;
+        for (int i = 0; i < nk; ++i) {
+            const int c = s_ord[i];
+            if (tid == 0) {
+                const int x = s_dr[c];
+                bool acc = false;
+                if (x >= 0 && x < V) {
+                    const float qh = Q > 0.f ? rej_w(qrow[x]) / Q : 0.f;
+                    acc = s_coin[c] * qh < resid(row[x], qrow[x], i);
+                }
+                s_acc = acc;
+            }
+            __syncthreads();
+            if (s_acc) {
+                next = c;
+                break;
+            }
+            // rejected: Z_{i+1} = sum_v max(0, r_i(v) - q^(v))
+            float z = 0.f;
+            over_rows([&](float pv, float qv) {
+                const float qh = Q > 0.f ? rej_w(qv) / Q : 0.f;
+                z += fmaxf(resid(pv, qv, i) - qh, 0.f);
+            });
+            float z_all, unused;
+            block_sum2(z, 0.f, z_all, unused);
+            if (tid == 0)
+                zs[i] = z_all;
+            nrej = i + 1;
+            __syncthreads();
+        }
+        if (next < 0)
+            break;
+        if (tid == 0)
+            s_path[len] = next;
+        cur = next;
+        ++len;
+        __syncthreads();
+    }
+
+    // the bonus from r_nrej: tile sums, then the tile, then the token
+    for (int t = w; t < ntiles; t += kRejWaves) {
+        const int v0 = t * kRejTile + lane * 4;
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            r[e] = v0 + e < V ? resid(row[v0 + e], qrow[v0 + e], nrej) : 0.f;
+        const float s = rej_wave_sum((r[0] + r[1]) + (r[2] + r[3]));
+        if (lane == 0)
+            tsum[t] = s;
+    }
+    __syncthreads();
+    if (w == 0) {
+        float run = 0.f;
+        for (int t0 = 0; t0 < ntiles; t0 += 64) {
+            const float x = t0 + lane < ntiles ? tsum[t0 + lane] : 0.f;
+            run += __shfl(rej_wave_scan(x, lane), 63, 64);
+        }
+        const float total = run;
+        const float target = s_bu[cur] * total;
+        int k = -1, last = -1;
+        float before = 0.f;
+        run = 0.f;
+        for (int t0 = 0; t0 < ntiles && k < 0; t0 += 64) {
+            const float x = t0 + lane < ntiles ? tsum[t0 + lane] : 0.f;
+            const float inc = rej_wave_scan(x, lane);
+            const float up = __shfl_up(inc, 1, 64);
+            const float exc = lane > 0 ? up : 0.f;
+            const uint64_t pass = __ballot(run + inc > target && x > 0.f);
+            const uint64_t pos = __ballot(x > 0.f);
+            if (pos)
+                last = t0 + 63 - __builtin_clzll(pos);
+            if (pass) {
+                const int l = __builtin_ctzll(pass);
+                k = t0 + l;
+                before = run + __shfl(exc, l, 64);
+            }
+            run += __shfl(inc, 63, 64);
+        }
+        int bonus = 0;
+        if (total > 0.f) {
+            const bool crossed = k >= 0;
+            if (!crossed)
+                k = last;
+            const int v0 = k * kRejTile + lane * 4;
+            float r[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                r[e] = v0 + e < V ? resid(row[v0 + e], qrow[v0 + e], nrej) : 0.f;
+            const float ls = ((r[0] + r[1]) + r[2]) + r[3];
+            const float inc = rej_wave_scan(ls, lane);
+            const float up = __shfl_up(inc, 1, 64);
+            const float exc = lane > 0 ? up : 0.f;
+            const uint64_t hit = __ballot(crossed && ls > 0.f && before + inc > target);
+            const uint64_t nz = __ballot(ls > 0.f);
+            const int l = hit ? __builtin_ctzll(hit) : (nz ? 63 - __builtin_clzll(nz) : 0);
+            int e_pick = -1, e_last = -1;
+            float cum = before + exc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (r[e] > 0.f) {
+                    e_last = e;
+                    cum += r[e];
+                    if (hit && e_pick < 0 && cum > target)
+                        e_pick = e;
+                }
+            }
+            const int e_sel = e_pick >= 0 ? e_pick : e_last;
+            bonus = k * kRejTile + 4 * l + __shfl(e_sel < 0 ? 0 : e_sel, l, 64);
+        }
+        if (lane == 0)
+            s_bonus = bonus;
+    }
+    __syncthreads();
+    if (tid < N) {
+        a.path[nb + tid] = tid < len ? s_path[tid] : -1;
+        if (a.tokens)
+            a.tokens[nb + tid] = tid + 1 < len ? s_dr[s_path[tid + 1]] : (tid + 1 == len ? s_bonus : -1);
+    }
+    if (tid == 0)
+        a.accept_len[b] = len;
+}
+
 inline hipStream_t S(void *s) { return (hipStream_t)s; }
 
 }  // namespace
@@ -613,6 +859,7 @@ extern "C" tav_status tree_sample_gumbel(const void *logits, tav_dtype dtype, in
 }
 
 extern "C" tav_status verify_tree_rejection(const float *probs, int64_t row_stride, int32_t V,
+                                            const float *draft_q, int64_t q_row_stride,
                                             const int32_t *draft_tokens, const int32_t *parents,
                                             const float *draft_score, const float *coins,
                                             const float *bonus_u, int32_t B, int32_t N,
@@ -628,6 +875,14 @@ extern "C" tav_status verify_tree_rejection(const float *probs, int64_t row_stri
     c.need(row_stride % 4 == 0, TAV_ERR_INVALID_ARG,
            "row_stride must be a multiple of 4 elements, got " + str(row_stride));
     c.need((long long)B * N * row_stride < (1LL << 62), TAV_ERR_INVALID_ARG, "probs too large");
+    if (draft_q) {
+        c.need(q_row_stride >= V, TAV_ERR_INVALID_ARG,
+               "q_row_stride must be >= V, got " + str(q_row_stride) + " < " + str(V));
+        c.need(q_row_stride % 4 == 0, TAV_ERR_INVALID_ARG,
+               "q_row_stride must be a multiple of 4 elements, got " + str(q_row_stride));
+        c.need(((uintptr_t)draft_q & 15) == 0, TAV_ERR_INVALID_ARG, "draft_q is not 16-byte aligned");
+        c.need((long long)B * N * q_row_stride < (1LL << 62), TAV_ERR_INVALID_ARG, "draft_q too large");
+    }
     if (B > 0) {
         c.need(probs, TAV_ERR_INVALID_ARG, "probs is NULL");
         c.need(((uintptr_t)probs & 15) == 0, TAV_ERR_INVALID_ARG, "probs is not 16-byte aligned");
@@ -653,6 +908,13 @@ extern "C" tav_status verify_tree_rejection(const float *probs, int64_t row_stri
     a.path = accepted_path;
     a.accept_len = accept_len;
     a.tokens = accepted_tokens;
-    hipLaunchKernelGGL(k_verify_rejection, dim3((unsigned)B), dim3(kRejThreads), 0, S(stream), a);
+    if (draft_q) {
+        RejQArgs qa{a, draft_q, q_row_stride};
+        hipLaunchKernelGGL(k_verify_rejection_q, dim3((unsigned)B), dim3(kRejThreads), 0, S(stream),
+                           qa);
+    } else {
+        hipLaunchKernelGGL(k_verify_rejection, dim3((unsigned)B), dim3(kRejThreads), 0, S(stream),
+                           a);
+    }
     return tav::launched("verify_tree_rejection");
 }

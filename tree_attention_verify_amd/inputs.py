@@ -393,11 +393,12 @@ class RejectionInputs:
     draft_score: np.ndarray      # float32 [B][N]
     coins: np.ndarray            # float32 [B][N], uniform in [0, 1)
     bonus_u: np.ndarray          # float32 [B][N], uniform in [0, 1)
+    draft_q: Optional[torch.Tensor] = None   # float32 [B][N][V]: the drafter's rows
 
 
 def make_rejection_inputs(B: int, N: int, V: int, seed: int, device="cpu", tree: str = "eagle",
                           scale: float = 2.0, row_stride: Optional[int] = None,
-                          agree: float = 0.75) -> RejectionInputs:
+                          agree: float = 0.75, with_q: bool = False) -> RejectionInputs:
     """Seeded inputs of the sampled verify by rejection.  Trees: EAGLE top-8
     beam, random (depth <= 6) or a chain.  The target row after each node is
     a mix of softmax(N(0, scale^2)) and a point mass on a "hot" token of
@@ -406,7 +407,10 @@ def make_rejection_inputs(B: int, N: int, V: int, seed: int, device="cpu", tree:
     token drawn from the parent's softmax part; a node's draft score is its
     parent's target probability of its token.  Coins and bonus draws are
     uniform fp32 in [0, 1).  row_stride > V pads the rows with NaN, which the
-    walk never reads."""
+    walk never reads.  with_q adds the drafter's rows: the target's hot
+    token at weight U(0.2, 0.8) over a softmax of fresh N(0, scale^2)
+    logits, and then every child drafts a token drawn independently from its
+    parent's q row (its draft score the q probability of that token)."""
     r = _streams(seed + 15485863, 1)[0]
     if tree == "eagle":
         parents = np.stack([eagle_tree(r, 8, 6, N) for _ in range(B)])
@@ -445,13 +449,38 @@ def make_rejection_inputs(B: int, N: int, V: int, seed: int, device="cpu", tree:
             else:
                 draft[b, c] = draws[b, n, j % 8]
     par_c = np.maximum(parents, 0)
-    score = p[torch.as_tensor(np.arange(B)[:, None], device=dev),
-              torch.as_tensor(par_c, device=dev), torch.as_tensor(draft.astype(np.int64), device=dev)]
+    qv = None
+    src = p
+    if with_q:
+        ql = torch.empty((B, N, V), dtype=torch.float32, device=dev)
+        _randn_into(ql, g)
+        qmix = r.uniform(0.2, 0.8, (B, N)).astype(np.float32)
+        qv = torch.softmax(ql * scale, -1) * torch.as_tensor(1.0 - qmix, device=dev)[..., None]
+        del ql
+        qv.view(B * N, V)[torch.arange(B * N, device=dev),
+                          torch.as_tensor(hot.reshape(-1), device=dev)] += \
+            torch.as_tensor(qmix.reshape(-1), device=dev)
+        qd = torch.multinomial(qv.view(B * N, V), 8, replacement=True, generator=g)
+        qd = qd.view(B, N, 8).cpu().numpy()
+        for b in range(B):
+            seen = {}
+            for c in range(1, N):
+                n = int(parents[b, c])
+                j = seen.get(n, 0)
+                seen[n] = j + 1
+                draft[b, c] = qd[b, n, j % 8]
+        src = qv
+    score = src[torch.as_tensor(np.arange(B)[:, None], device=dev),
+                torch.as_tensor(par_c, device=dev), torch.as_tensor(draft.astype(np.int64), device=dev)]
     score = score.cpu().numpy().astype(np.float32)
     score[:, 0] = 1.0
     coins = r.random((B, N), dtype=np.float32)
     bonus_u = r.random((B, N), dtype=np.float32)
-    return RejectionInputs(buf[:, :, :V], parents, draft, score, coins, bonus_u)
+    if qv is not None:
+        qbuf = torch.full((B, N, rs), float("nan"), dtype=torch.float32, device=dev)
+        qbuf[:, :, :V] = qv
+        qv = qbuf[:, :, :V]
+    return RejectionInputs(buf[:, :, :V], parents, draft, score, coins, bonus_u, qv)
 
 
 # ---------------------------------------------------------------------------
