@@ -555,7 +555,7 @@ __global__ void __launch_bounds__(kRejThreads) k_verify_rejection_q(RejQArgs qa)
     const RejArgs &a = qa.a;
     __shared__ float tsum[kRejMaxTiles];
     __shared__ float red[2][kRejWaves];
-    __shared__ float zs[64];                      // Z_1 .. Z_k of the current node
+    __shared__ float zinv[64];                    // 1 / Z_1 .. 1 / Z_k at the current node (0: none left)
     __shared__ int32_t s_par[64], s_dr[64], s_path[64], s_ord[64];
     __shared__ float s_sc[64], s_coin[64], s_bu[64];
     __shared__ int s_nk, s_acc, s_bonus;
@@ -595,7 +595,7 @@ __global__ void __launch_bounds__(kRejThreads) k_verify_rejection_q(RejQArgs qa)
 
     const int ntiles = (V + kRejTile - 1) / kRejTile;
     int cur = 0, len = 1, nrej = 0;
-    float S = 0.f, Q = 0.f;
+    float S = 0.f, Q = 0.f, iS = 0.f, iQ = 0.f;
     const float *row, *qrow;
     // the residual after k rejections at token v
     // f(p[v], q[v]) for every token of the two rows of node cur: 16-byte
@@ -624,11 +624,12 @@ __global__ void __launch_bounds__(kRejThreads) k_verify_rejection_q(RejQArgs qa)
         for (int v = 4 * V4 + tid; v < V; v += kRejThreads)
             f(row[v], qrow[v]);
     };
+    // (reciprocals of the totals and normalisers, computed once each)
     auto resid = [&](float pv, float qv, int k) {
-        float r = S > 0.f ? rej_w(pv) / S : 0.f;
-        const float qh = Q > 0.f ? rej_w(qv) / Q : 0.f;
+        float r = rej_w(pv) * iS;
+        const float qh = rej_w(qv) * iQ;
         for (int j = 0; j < k; ++j)
-            r = zs[j] > 0.f ? fmaxf(r - qh, 0.f) / zs[j] : 0.f;
+            r = fmaxf(r - qh, 0.f) * zinv[j];
         return r;
     };
     for (;;) {
@@ -640,6 +641,8 @@ __global__ void __launch_bounds__(kRejThreads) k_verify_rejection_q(RejQArgs qa)
             sq += rej_w(qv);
         });
         block_sum2(sp, sq, S, Q);
+        iS = S > 0.f ? 1.f / S : 0.f;
+        iQ = Q > 0.f ? 1.f / Q : 0.f;
         // the children in their trying order (wave 0, as k_verify_rejection)
         if (w == 0) {
             const bool is_child = lane < N && len < N && s_par[lane] == cur;
@@ -666,8 +669,7 @@ __global__ void __launch_bounds__(kRejThreads) k_verify_rejection_q(RejQArgs qa)
                 const int x = s_dr[c];
                 bool acc = false;
                 if (x >= 0 && x < V) {
-                    const float qh = Q > 0.f ? rej_w(qrow[x]) / Q : 0.f;
-                    acc = s_coin[c] * qh < resid(row[x], qrow[x], i);
+                    acc = s_coin[c] * (rej_w(qrow[x]) * iQ) < resid(row[x], qrow[x], i);
                 }
                 s_acc = acc;
             }
@@ -678,14 +680,11 @@ __global__ void __launch_bounds__(kRejThreads) k_verify_rejection_q(RejQArgs qa)
             }
             // rejected: Z_{i+1} = sum_v max(0, r_i(v) - q^(v))
             float z = 0.f;
-            over_rows([&](float pv, float qv) {
-                const float qh = Q > 0.f ? rej_w(qv) / Q : 0.f;
-                z += fmaxf(resid(pv, qv, i) - qh, 0.f);
-            });
+            over_rows([&](float pv, float qv) { z += fmaxf(resid(pv, qv, i) - rej_w(qv) * iQ, 0.f); });
             float z_all, unused;
             block_sum2(z, 0.f, z_all, unused);
             if (tid == 0)
-                zs[i] = z_all;
+                zinv[i] = z_all > 0.f ? 1.f / z_all : 0.f;
             nrej = i + 1;
             __syncthreads();
         }
