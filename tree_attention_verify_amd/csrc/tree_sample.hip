@@ -701,16 +701,42 @@ __global__ void __launch_bounds__(kRejThreads) k_verify_rejection_q(RejQArgs qa)
         __syncthreads();
     }
 
-    // the bonus from r_nrej: tile sums, then the tile, then the token
-    for (int t = w; t < ntiles; t += kRejWaves) {
-        const int v0 = t * kRejTile + lane * 4;
+    // the bonus from r_nrej: tile sums (whole tiles by unconditional 16-byte
+    // loads, four tiles in flight per wave, then the partial tile), then the
+    // tile, then the token
+    const int nfull = V / kRejTile;
+    for (int t0 = w * 4; t0 < nfull; t0 += kRejWaves * 4) {
+        float4 pv[4], qv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int off = min(t0 + i, nfull - 1) * kRejTile + lane * 4;
+            pv[i] = *(const float4 *)(row + off);
+            qv[i] = *(const float4 *)(qrow + off);
+        }
+        float ls[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            ls[i] = (resid(pv[i].x, qv[i].x, nrej) + resid(pv[i].y, qv[i].y, nrej)) +
+                    (resid(pv[i].z, qv[i].z, nrej) + resid(pv[i].w, qv[i].w, nrej));
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ls[i] += __shfl_xor(ls[i], m, 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (t0 + i < nfull && lane == 0)
+                tsum[t0 + i] = ls[i];
+    }
+    if (nfull < ntiles && w == kRejWaves - 1) {
+        const int v0 = nfull * kRejTile + lane * 4;
         float r[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             r[e] = v0 + e < V ? resid(row[v0 + e], qrow[v0 + e], nrej) : 0.f;
         const float s = rej_wave_sum((r[0] + r[1]) + (r[2] + r[3]));
         if (lane == 0)
-            tsum[t] = s;
+            tsum[nfull] = s;
     }
     __syncthreads();
     if (w == 0) {
