@@ -235,3 +235,38 @@ def test_rejection_against_q_parity(name):
 def test_rejection_against_q_full_size():
     x = gen.make_rejection_inputs(32, 64, gen.SAMPLE_VOCAB, 4, "cuda", tree="eagle", with_q=True)
     run_and_check_q(x, tag="q full size")
+
+
+@pytest.mark.parametrize("form", ["fixed", "q"])
+def test_rejection_full_path_on_a_64_node_chain(form):
+    """Every target row puts all its weight on the next node's drafted
+    token: the walk takes all 64 nodes and the bonus is drawn at node 63 with
+    nothing rejected there (against q too, with q equal to the target)."""
+    B, N, V = 16, 64, 1000
+    rng = np.random.default_rng(51)
+    par = np.tile(np.arange(-1, N - 1, dtype=np.int32), (B, 1))
+    draft = rng.integers(0, V, (B, N)).astype(np.int32)
+    p = np.zeros((B, N, V), np.float32)
+    for n in range(N - 1):
+        p[np.arange(B), n, draft[:, n + 1]] = 1.0
+    p[:, N - 1, :] = rng.random((B, V)).astype(np.float32)
+    coins = rng.random((B, N)).astype(np.float32)
+    bu = rng.random((B, N)).astype(np.float32)
+    pt = torch.as_tensor(p).cuda()
+    r = tav.verify_tree_rejection(pt, dev(draft), dev(par), dev(coins, torch.float32),
+                                  dev(bu, torch.float32), draft_q=pt if form == "q" else None)
+    if form == "q":
+        ref = oracle.verify_rejection_q(p, p, draft, par, coins, bu)
+    else:
+        ref = oracle.verify_rejection(p, draft, par, coins, bu)
+    alen = r["accept_len"].cpu().numpy()
+    assert (alen == N).all() and (ref["accept_len"] == N).all()
+    assert np.array_equal(r["accepted_path"].cpu().numpy(), ref["accepted_path"])
+    tok = r["accepted_tokens"].cpu().numpy()
+    assert np.array_equal(tok[:, :N - 1], ref["accepted_tokens"][:, :N - 1])
+    c = np.cumsum(p[:, N - 1].astype(np.float64), 1)
+    for b in range(B):       # the bonus: the inverse CDF of node 63's row
+        g = int(tok[b, N - 1])
+        target = float(bu[b, N - 1]) * c[b, -1]
+        lo = c[b, g] - float(p[b, N - 1, g])
+        assert lo <= target + CDF_TOL * c[b, -1] and c[b, g] >= target - CDF_TOL * c[b, -1]
