@@ -282,3 +282,14 @@ def test_tree_attention_mla_rejects(L):
     st, msg = call(B=0, q=None, lat=None, pt=None, plen=None, masks=None, out=None, lse=None,
                    ws=None)
     assert st == 0, msg
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus N > 1 exits with a message before
+    touching a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 2, r.stderr[-500:]
+    assert "one GPU" in r.stderr and r.stdout == ""
