@@ -199,6 +199,11 @@ class Step:
                 tb.num_pages, tb.stride_page, tb.stride_token, tb.stride_head, tb.stride_batch,
                 tb.n_heads, tb.row_bytes)
         self.stream = torch.cuda.current_stream().cuda_stream
+        # draft lanes: the drafter's lane masks, and only the attention runs
+        # (lanes are not verified, so there is no walk or compaction)
+        self.lanes = wl.tree == "lanes"
+        if self.lanes:
+            self.masks = t(inp.lane_masks.view(np.int64), torch.int64)
 
     def _attn(self, fn):
         wl, inp = self.wl, self.inp
@@ -211,18 +216,26 @@ class Step:
         assert rc == 0, self.L.tav_last_error()
 
     def run(self, ev=None):
+        """One step.  ev: five events recorded at the step's start, before
+        and after the prefix launch, after the window/merge launch and at the
+        step's end (all on the step's stream)."""
         L, wl = self.L, self.wl
         B, N = wl.B, wl.N
-        assert L.tree_build_masks(self.parents.data_ptr(), B, N, self.prefix_len.data_ptr(),
-                                  self.depth.data_ptr(), self.masks.data_ptr(),
-                                  self.positions.data_ptr(), self.tree_error.data_ptr(),
-                                  self.stream) == 0
-        if ev is not None:
-            ev[0].record()
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        if not self.lanes:
+            assert L.tree_build_masks(self.parents.data_ptr(), B, N, self.prefix_len.data_ptr(),
+                                      self.depth.data_ptr(), self.masks.data_ptr(),
+                                      self.positions.data_ptr(), self.tree_error.data_ptr(),
+                                      self.stream) == 0
+        rec(1)
         self._attn(L.tree_attention_prefix)
-        if ev is not None:
-            ev[1].record()
+        rec(2)
         self._attn(L.tree_attention_window_merge)
+        rec(3)
+        if self.lanes:
+            rec(4)
+            return
         assert L.verify_tree_greedy(self.draft.data_ptr(), self.target.data_ptr(),
                                     self.parents.data_ptr(), B, N, self.path.data_ptr(),
                                     self.alen.data_ptr(), self.tokens.data_ptr(),
@@ -231,6 +244,7 @@ class Step:
                                      B, N, self.stream) == 0
         assert L.tree_shift_positions(self.positions.data_ptr(), self.depth.data_ptr(), B, N, -1,
                                       self.stream) == 0
+        rec(4)
 
 
 def cpu_baseline(wl, inp, masks_np, budget_s):
@@ -611,7 +625,11 @@ def main():
     # times the steady state that back-to-back verify rounds run in
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="long64", choices=sorted(gen.WORKLOADS))
+    ap.add_argument("--workload", default="long64", choices=sorted(gen.WORKLOADS) + ["all"],
+                    help="the verify workload to time; 'all' prints one line per "
+                         "configuration, each with the last-level cache flushed before every step")
+    ap.add_argument("--flush", action="store_true",
+                    help="flush the last-level cache before every step and report medians")
     ap.add_argument("--seed", type=int, default=4)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
@@ -660,36 +678,76 @@ def main():
     if args.mla:
         run_mla(args)
         return
-    wl = gen.WORKLOADS[args.workload]
+    if args.workload == "all":
+        for name in ALL_WORKLOADS:
+            res = bench_workload(gen.WORKLOADS[name], args, flushed=True)
+            print(json.dumps(res), flush=True)
+        return
+    res = bench_workload(gen.WORKLOADS[args.workload], args, flushed=args.flush)
+    print(json.dumps(res), flush=True)
+
+
+# every configuration of the verify path, one JSON line each under --workload all
+ALL_WORKLOADS = ["worked", "random16", "eagle64", "long64", "lanes", "chain8", "long64_fp8",
+                 "chain8_fp8", "long64_tp8"]
+FLUSH_BYTES = 512 << 20       # > the 256 MB last-level cache (MALL)
+
+
+def pct(xs):
+    xs = np.asarray(xs, np.float64)
+    return {"median": round(float(np.median(xs)), 4), "p10": round(float(np.percentile(xs, 10)), 4),
+            "p90": round(float(np.percentile(xs, 90)), 4), "mean": round(float(xs.mean()), 4)}
+
+
+def bench_workload(wl, args, flushed):
+    """One JSON result for workload wl.  Unflushed (the default run): W warm-up
+    steps, then K steps back to back between two events, each step's prefix
+    launch also bracketed by its own events.  Flushed (--flush, and every line
+    of --workload all): before every step a 512 MiB write evicts the
+    last-level cache, and each step is timed by its own events (prefix launch,
+    tree_attention = prefix + window/merge, whole step); the result reports
+    median, p10 and p90 over the K steps and takes the medians as its value."""
     log("workload", wl)
     t0 = time.perf_counter()
     inp = gen.make_inputs(wl, args.seed, "cuda")
     torch.cuda.synchronize()
     log("inputs ready in %.1f s" % (time.perf_counter() - t0))
     step = Step(wl, inp)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    for _ in range(args.warmup):
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda") if flushed else None
+    for i in range(args.warmup):
+        if flush is not None:
+            flush.fill_(i & 0xff)
         step.run()
     torch.cuda.synchronize()
     log("warmup done")
 
-    pairs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-             for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [[mk() for _ in range(5)] for _ in range(args.steps)]
+    start, end = mk(), mk()
     torch.cuda.synchronize()
     t_host = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        step.run(pairs[i])
+        if flush is not None:
+            flush.fill_(i & 0xff)
+        step.run(evs[i])
     end.record()
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
-    ms_step = start.elapsed_time(end) / args.steps
-    prefix_ms = [a.elapsed_time(b) for a, b in pairs]
-    prefix_avg = float(np.mean(prefix_ms))
-    log("timed %d steps: %.3f ms/step (host %.3f ms/step), prefix kernel avg %.3f ms "
-        "(min %.3f max %.3f)" % (args.steps, ms_step, t_host * 1e3 / args.steps, prefix_avg,
-                                 min(prefix_ms), max(prefix_ms)))
+    step_ms = [e[0].elapsed_time(e[4]) for e in evs]
+    prefix_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    attn_ms = [e[1].elapsed_time(e[3]) for e in evs]
+    if flushed:
+        ms_step = float(np.median(step_ms))
+        prefix_t = float(np.median(prefix_ms))
+    else:
+        ms_step = start.elapsed_time(end) / args.steps
+        prefix_t = float(np.mean(prefix_ms))
+    log("timed %d steps%s: %.4f ms/step (host %.3f ms/step incl. flushes), prefix kernel %s "
+        "%.4f ms (min %.4f max %.4f)" % (args.steps, " (LLC flushed before each)" if flushed else "",
+                                         ms_step, t_host * 1e3 / args.steps,
+                                         "median" if flushed else "avg", prefix_t,
+                                         min(prefix_ms), max(prefix_ms)))
 
     sustained = None
     if args.sustain > 0:
@@ -709,6 +767,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    del flush
 
     masks_np = step.masks.cpu().numpy().view(np.uint64)
     P_vis = min(wl.P, wl.prefix_window) if wl.prefix_window else wl.P
@@ -717,7 +776,7 @@ def main():
     value = kvb / (ms_step * 1e-3) / 1e9
     e = ELEM_BYTES[wl.dtype]
     prefix_bytes = kv_bytes(wl, P_vis, with_window=False) + wl.B * wl.R * wl.Hq * wl.D * e
-    achieved = prefix_bytes / (prefix_avg * 1e-3) / 1e9
+    achieved = prefix_bytes / (prefix_t * 1e-3) / 1e9
     flops = attn_flops(wl, masks_np, P_vis)
     prefix_flops = 4.0 * wl.D * wl.Hq * wl.B * wl.R * P_vis
     res = {
@@ -732,15 +791,23 @@ def main():
         "head_rows_per_s": round(rows * wl.Hq / (ms_step * 1e-3), 1),
         "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
         "attention_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "timing": {"llc_flushed": bool(flushed),
+                   "flush_bytes": FLUSH_BYTES if flushed else 0,
+                   "step_ms": pct(step_ms), "tree_attention_ms": pct(attn_ms),
+                   "prefix_ms": pct(prefix_ms),
+                   "value_from": "median step" if flushed else
+                                 "K back-to-back steps between two events"},
         "roofline": {"kernel": prefix_kernel_name(wl), "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "algorithmic_bytes": prefix_bytes,
-                     "avg_launch_ms": round(prefix_avg, 4),
-                     "mfma_tflops": round(prefix_flops / (prefix_avg * 1e-3) / 1e12, 1),
-                     "mfma_frac": round(prefix_flops / (prefix_avg * 1e-3) / 1e12
+                     "avg_launch_ms": round(prefix_t, 4),
+                     "mfma_tflops": round(prefix_flops / (prefix_t * 1e-3) / 1e12, 1),
+                     "mfma_frac": round(prefix_flops / (prefix_t * 1e-3) / 1e12
                                         / MFMA_BF16_PEAK_TFS, 4)},
     }
+    if flushed:
+        res["roofline"]["launch_ms_statistic"] = "median over flushed reps"
     # shapes past the ridge (flop per byte above peak MFMA / peak HBM) are
     # MFMA-bound: report the prefix kernel against the bf16 MFMA peak instead
     # The wide-row kernel under an FP8 cache runs the scores (half the flops)
@@ -748,24 +815,30 @@ def main():
     mfma_peak = MFMA_BF16_PEAK_TFS
     if wl.kv == "fp8" and prefix_kernel_name(wl) == "k_prefix_mfma_pipe":
         mfma_peak = 2.0 / (1.0 / MFMA_FP8_PEAK_TFS + 1.0 / MFMA_BF16_PEAK_TFS)
-    if prefix_flops / prefix_bytes > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9):
+    if wl.dtype == "bf16" and \
+            prefix_flops / prefix_bytes > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9):
         rf = res["roofline"]
-        tfs = prefix_flops / (prefix_avg * 1e-3) / 1e12
+        tfs = prefix_flops / (prefix_t * 1e-3) / 1e12
         rf.update({"bound": "mfma", "achieved": round(tfs, 1), "peak": round(mfma_peak, 1),
                    "unit": "TFLOP/s", "frac": round(tfs / mfma_peak, 4),
                    "algorithmic_flops": prefix_flops, "hbm_gbs": round(achieved, 1)})
         if mfma_peak != MFMA_BF16_PEAK_TFS:
             rf["peak_note"] = "scores on the fp8 MFMA (5000), PV on bf16 (2500)"
+    if wl.dtype == "f32":
+        res["roofline"]["note"] = "fp32 vector-ALU prefix on a 68 KB workload: launch-latency bound"
     if sustained is not None:
         res["sustained_ms_per_step"] = round(sustained, 4)
     t = traffic_for(wl.name)
     if t is not None:
         res["roofline"]["traffic"] = round(t["prefix_traffic_bytes"])
         res["roofline"]["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
-    if args.cpu_budget > 0:
-        log("cpu baseline (oracle), budget %.0f s" % args.cpu_budget)
-        res["cpu_baseline"] = cpu_baseline(wl, inp, masks_np, args.cpu_budget)
-    print(json.dumps(res), flush=True)
+    budget = args.cpu_budget if args.workload != "all" else min(args.cpu_budget, 3.0)
+    if budget > 0:
+        log("cpu baseline (oracle), budget %.0f s" % budget)
+        res["cpu_baseline"] = cpu_baseline(wl, inp, masks_np, budget)
+    del step, inp
+    torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":

@@ -19,6 +19,7 @@ Workloads (the shapes of the five synthetic verify configurations):
   lanes    B 64, P 32768, draft lanes K 4 over S 4 steps (R 4, W 12), frozen
            4096-key sliding window, Hq 32, Hkv 8, D 128, bf16, page size 16
   chain8   B 64, P 32768, chain tree N 8 (parent[i] = i - 1), same shapes
+  long64_tp8  long64 at one 8-way tensor-parallel share: Hq 4, Hkv 1
 
 Recipe: tree structure and tokens come from numpy PCG64 streams spawned from
 SeedSequence(seed); tensors from a torch generator seeded from the same
@@ -107,6 +108,10 @@ WORKLOADS = {
                            depth_cap=8, kv_dtype="fp8"),
     "chain8_fp8": Workload("chain8_fp8", 64, 32768, 8, 32, 8, 128, "bf16", 16, "chain",
                            kv_dtype="fp8"),
+    # one tensor-parallel share of long64 over 8 GPUs: each GPU holds one kv
+    # head and its 4 query heads, with the same trees and prefix
+    "long64_tp8": Workload("long64_tp8", 4, 131072, 64, 4, 1, 128, "bf16", 64, "random",
+                           depth_cap=8),
 }
 
 
