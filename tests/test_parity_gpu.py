@@ -122,6 +122,8 @@ SMALL = {
                                            page_size=16, kv_dtype="fp8"), [500, 131]),
     "fp8_d64": (W_["random16"].with_(name="fp8_d64", B=2, P=777, N=16, Hq=8, Hkv=2, D=64,
                                      kv_dtype="fp8"), [777, 100]),
+    # one 8-way tensor-parallel share of long64: one kv head, 4 query heads
+    "long64_tp8": (W_["long64_tp8"].with_(B=2, P=3000), [3000, 2049]),
 }
 
 
@@ -442,7 +444,16 @@ def test_chain_equals_causal():
 # full workload sizes, sampled rows
 # ---------------------------------------------------------------------------
 
-FULL = ["random16", "eagle64", "long64", "lanes", "chain8", "long64_fp8", "chain8_fp8"]
+FULL = ["random16", "eagle64", "long64", "lanes", "chain8", "long64_fp8", "chain8_fp8",
+        "long64_tp8"]
+
+
+def group_rows(wl, b, g):
+    """Flat (b * R + r) * Hq + h ids of every row of request b's kv head g:
+    all rows one prefix workgroup folds, over every split of the prefix."""
+    G = wl.Hq // wl.Hkv
+    return np.array([(b * wl.R + r) * wl.Hq + h for r in range(wl.R)
+                     for h in range(g * G, (g + 1) * G)], np.int64)
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -467,6 +478,8 @@ def test_full_size_sampled(name):
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
     n_rows = wl.B * wl.R * wl.Hq
     rng = np.random.default_rng(7)
-    rows = np.unique(np.concatenate([[0, n_rows - 1], rng.integers(0, n_rows, 40)]))
+    # every row of the last request's last kv head, plus rows sampled anywhere
+    rows = np.unique(np.concatenate([[0, n_rows - 1], rng.integers(0, n_rows, 40),
+                                     group_rows(wl, wl.B - 1, wl.Hkv - 1)]))
     ro, rl = oracle_attention(inp, m_np, rows=rows)
-    check_attention(out, lse, ro, rl, rows=rows, tag="full-" + name)
+    check_attention(out, lse, ro, rl, rows=rows, tag="full-%s (%d rows)" % (name, rows.size))

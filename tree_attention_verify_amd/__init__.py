@@ -370,13 +370,15 @@ def tree_attention_mla_workspace_size(B: int, R: int, Hq: int, Dc: int, Dr: int,
 
 
 def tree_attention_mla(q: torch.Tensor, latent: torch.Tensor, page_table: torch.Tensor,
-                       prefix_len: torch.Tensor, masks: torch.Tensor, W: int, Dc: int = 512,
-                       max_prefix_len: Optional[int] = None, sm_scale: float = 0.0,
+                       prefix_len: torch.Tensor, masks: torch.Tensor, W: int, Dc: int = 512, *,
+                       max_prefix_len: int, sm_scale: float = 0.0,
                        workspace: Optional[torch.Tensor] = None):
     """Tree attention over an MLA latent cache.  q bf16 [B][R][Hq][Dc + Dr];
     latent bf16 [pages][page_size][Dc + Dr]; page_table int32 [B][max_pages];
-    prefix_len int32 [B]; masks int64 (uint64 bits) [B][R].  -> (out bf16
-    [B][R][Hq][Dc], lse2 float32 [B][R][Hq])."""
+    prefix_len int32 [B]; masks int64 (uint64 bits) [B][R].  max_prefix_len
+    (a host int >= every prefix_len) sizes the workspace and the split plan;
+    it is required, as for tree_attention, so the call never reads the device.
+    -> (out bf16 [B][R][Hq][Dc], lse2 float32 [B][R][Hq])."""
     _need(q, "q", torch.bfloat16)
     B, R, Hq, Dk = q.shape
     Dr = Dk - Dc
@@ -388,8 +390,6 @@ def tree_attention_mla(q: torch.Tensor, latent: torch.Tensor, page_table: torch.
     _need(page_table, "page_table", torch.int32, dev)
     _need(prefix_len, "prefix_len", torch.int32, dev, (B,))
     _need(masks, "masks", torch.int64, dev, (B, R))
-    if max_prefix_len is None:
-        max_prefix_len = int(prefix_len.max().item()) if B > 0 else 0
     need = tree_attention_mla_workspace_size(B, R, Hq, Dc, Dr, max_prefix_len, ps)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
