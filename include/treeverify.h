@@ -155,9 +155,10 @@ size_t tree_attention_workspace_size(tav_dtype dtype, int32_t B, int32_t R, int3
  *            query cast to FP8, the window kernel the unquantised query and
  *            the window's K/V widened).  Prefix keys are scored with the
  *            query rounded to the nearest E4M3 value (ties to even,
- *            saturating at +-448), window keys with the bf16 query; values
- *            are widened exactly to bf16.  Strides count elements (bytes
- *            for FP8).
+ *            saturating at +-448), window keys with the bf16 query; keys
+ *            and values are widened exactly to bf16, so every product is
+ *            exact and sums in fp32.  Strides count elements (bytes for
+ *            FP8).
  * out        [B][R][Hq][D] in q's dtype (bf16 rounded to nearest even)
  * lse2       float [B][R][Hq] or NULL: log2 of the sum over visible keys of
  *            exp(score) (so 2^lse2 is the softmax denominator)

@@ -325,51 +325,28 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
     for (int i = tid; i < LDSB / 16; i += THREADS)
         reinterpret_cast<int4 *>(lds)[i] = make_int4(0, 0, 0, 0);
 
-    // Q^T operand in registers.  bf16 (and FP8 heads of 64 channels, with the
-    // query rounded to E4M3 and held as bf16): lane (row n = l32, half hl)
-    // holds Q[row][16 kk + 8 hl .. +8] for each k step.  FP8 heads of 128
-    // channels: the query rounded to E4M3 and packed, lane holding
-    // Q[row][64 kk + 32 hl .. +32] per 64-channel step, the byte order of the
-    // K operand (the FP8 product pairs the two operands byte by byte).
-    typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
-    bf16x8 qv[KVD ? 1 : KSTEPS];
-    i32x8 qv8[KVD ? 2 : 1];
-    if constexpr (KVD) {
+    // Q^T operand in registers, bf16: lane (row n = l32, half hl) holds 8
+    // channels of Q[row] per 16-channel k step.  Under an FP8 cache the query
+    // is rounded to E4M3 (held as bf16, which holds every E4M3 value), so the
+    // bf16 products with the widened E4M3 keys are exact and accumulate in
+    // fp32.  (The FP8 MFMAs are not used for the scores: they sum each
+    // 64-product group at about 12 bits relative to its largest product.)
+    // Steps take channels 16 kk + 8 hl .. +8, except for FP8 rows of 128
+    // channels, whose K operand lane reads whole 16-byte E4M3 chunks 4 c +
+    // 2 hl + e (c, e = 0, 1): step 4 c + 2 e + h then takes channels
+    // 16 (4 c + 2 hl + e) + 8 h .. +8, the same set for the query.
+    bf16x8 qv[KSTEPS];
+    {
         const int m = rows_base + l32;
         const bool ok = m < a.M;
         const int r = ok ? m / a.G : 0, hh = ok ? m % a.G : 0;
         const uint16_t *qrow = (const uint16_t *)a.q +
                                (((int64_t)b * a.R + r) * a.Hq + (int64_t)g * a.G + hh) * D;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int4 v4 = ok ? *(const int4 *)(qrow + 64 * kk + 32 * hl + 8 * c) : make_int4(0, 0, 0, 0);
-                typedef __attribute__((__vector_size__(8 * sizeof(uint16_t)))) uint16_t u16x8;
-                const u16x8 u = __builtin_bit_cast(u16x8, v4);
-                float f[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    f[e] = round_e4m3(bf16_bits_to_f32(u[e]));
-                // exact: every value is an E4M3 value
-                int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-                lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
-                int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
-                hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
-                qv8[kk][2 * c] = lo;
-                qv8[kk][2 * c + 1] = hi;
-            }
-            settle(qv8[kk]);
-        }
-    } else {
-        const int m = rows_base + l32;
-        const bool ok = m < a.M;
-        const int r = ok ? m / a.G : 0, hh = ok ? m % a.G : 0;
-        const uint16_t *qp = (const uint16_t *)a.q +
-                             (((int64_t)b * a.R + r) * a.Hq + (int64_t)g * a.G + hh) * D + 8 * hl;
-#pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-            int4 v4 = ok ? *(const int4 *)(qp + 16 * kk) : make_int4(0, 0, 0, 0);
+            const int ch = KVD ? 16 * (4 * (kk >> 2) + 2 * hl + ((kk >> 1) & 1)) + 8 * (kk & 1)
+                               : 16 * kk + 8 * hl;
+            int4 v4 = ok ? *(const int4 *)(qrow + ch) : make_int4(0, 0, 0, 0);
             qv[kk] = __builtin_bit_cast(bf16x8, v4);
             if constexpr (KV8)
                 qv[kk] = bf16x8_round_e4m3(qv[kk]);
@@ -599,15 +576,23 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
         // hl) reading chunks 4 kk + 2 hl + e of its key row
         f32x16 s;
         if constexpr (KVD) {
+            // E4M3 chunks widened exactly to bf16 in registers, bf16 MFMA
             const char *kr0 = Kb + krow * D;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int4 x0 = *(const int4 *)(kr0 + (((4 * kk + 2 * hl) ^ xk8s(krow)) * 16));
-                const int4 x1 = *(const int4 *)(kr0 + (((4 * kk + 2 * hl + 1) ^ xk8s(krow)) * 16));
-                const i32x8 ka = i32x8{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-                s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qv8[kk], kk ? s : f32x16{}, 0, 0, 0,
-                                                                    127, 0, 127);
-            }
+            for (int r = 0; r < 16; ++r)
+                s[r] = 0.f;
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int4 x = *(const int4 *)(kr0 + (((4 * c + 2 * hl + e) ^ xk8s(krow)) * 16));
+                    int4 lo, hi;
+                    fp8x16_to_bf16(x, lo, hi);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, lo),
+                                                                qv[4 * c + 2 * e], s, 0, 0, 0);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, hi),
+                                                                qv[4 * c + 2 * e + 1], s, 0, 0, 0);
+                }
         } else {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
@@ -909,55 +894,33 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
     for (int i = tid; i < VRING / 16; i += THREADS)
         reinterpret_cast<int4 *>(lds)[i] = make_int4(0, 0, 0, 0);
 
-    // Q^T operand.  bf16: lane (row l32, half hl) holds Q[row][16 kk + 8 hl
-    // .. +8] per 16-channel k step.  FP8: the query rounded to E4M3, lane
-    // holding Q[row][64 kk + 32 hl .. +32] per 64-channel k step, the byte
-    // order of the K operand's 32 bytes (the FP8 product pairs the bytes of
-    // the two operands position by position).
-    constexpr int QREGS = KV8 ? 2 : KSTEPS;
-    typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
-    bf16x8 qv[KV8 ? 1 : KSTEPS];
-    i32x8 qv8[KV8 ? 2 : 1];
+    // Q^T operand, bf16: lane (row l32, half hl) holds 8 channels of Q[row]
+    // per 16-channel k step, 16 kk + 8 hl .. +8.  Under an FP8 cache the
+    // query is rounded to E4M3 (held as bf16) and the E4M3 keys are widened
+    // to bf16 in registers, so the products are exact and accumulate in fp32
+    // (the FP8 MFMAs sum each 64-product group at about 12 bits relative to
+    // its largest product).  The K operand lane then reads whole 16-byte
+    // E4M3 chunks 4 c + 2 hl + e (c, e = 0, 1), and step 4 c + 2 e + h takes
+    // channels 16 (4 c + 2 hl + e) + 8 h .. +8, for the query as well.
+    bf16x8 qv[KSTEPS];
     {
         const int m = rows_base + l32;
         const bool ok = m < a.M;
         const int r = ok ? m / a.G : 0, hh = ok ? m % a.G : 0;
         const uint16_t *qrow = (const uint16_t *)a.q +
                                (((int64_t)b * a.R + r) * a.Hq + (int64_t)g * a.G + hh) * D;
-        if constexpr (KV8) {
 #pragma unroll
-            for (int kk = 0; kk < QREGS; ++kk) {
-                const uint16_t *qp = qrow + 64 * kk + 32 * hl;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int4 v4 = ok ? *(const int4 *)(qp + 8 * c) : make_int4(0, 0, 0, 0);
-                    typedef __attribute__((__vector_size__(8 * sizeof(uint16_t)))) uint16_t u16x8;
-                    const u16x8 u = __builtin_bit_cast(u16x8, v4);
-                    float f[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        f[e] = round_e4m3(bf16_bits_to_f32(u[e]));
-                    // exact: every value is an E4M3 value
-                    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-                    lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
-                    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
-                    hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
-                    qv8[kk][2 * c] = lo;
-                    qv8[kk][2 * c + 1] = hi;
-                }
-                settle(qv8[kk]);
-            }
-        } else {
-            const uint16_t *qp = qrow + 8 * hl;
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk) {
-                int4 v4 = ok ? *(const int4 *)(qp + 16 * kk) : make_int4(0, 0, 0, 0);
-                qv[kk] = __builtin_bit_cast(bf16x8, v4);
-            }
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk)
-                settle(qv[kk]);
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            const int ch = KV8 ? 16 * (4 * (kk >> 2) + 2 * hl + ((kk >> 1) & 1)) + 8 * (kk & 1)
+                               : 16 * kk + 8 * hl;
+            int4 v4 = ok ? *(const int4 *)(qrow + ch) : make_int4(0, 0, 0, 0);
+            qv[kk] = __builtin_bit_cast(bf16x8, v4);
+            if constexpr (KV8)
+                qv[kk] = bf16x8_round_e4m3(qv[kk]);
         }
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk)
+            settle(qv[kk]);
     }
     __syncthreads();
 
@@ -1118,25 +1081,27 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
         else
             return block_base(u) + KREG;
     };
-    // FP8 K operand: lane (key l32, half hl) reads chunks 4 kk + 2 hl + e of
-    // its key row, e = 0, 1: channels 64 kk + 32 hl .. +32, as the query
+    // FP8 K operand: lane (key l32, half hl) reads E4M3 chunks 4 c + 2 hl + e
+    // (channels 16 (4 c + 2 hl + e) .. +16) of its key row, c, e = 0, 1
     uint32_t koff8[2][2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int e = 0; e < 2; ++e)
             koff8[kk][e] = l32 * D + (((4 * kk + 2 * hl + e) ^ xk8(l32)) * 16);
-    typedef i32x8 KOp[KV8 ? 2 : KSTEPS];
-    typedef bf16x8 KOpB[KV8 ? 1 : KSTEPS];
-    auto load_k = [&](int u, auto &ka) {
+    auto load_k = [&](int u, bf16x8 (&ka)[KSTEPS]) {
         if constexpr (KV8) {
+            // E4M3 chunk 4 c + 2 hl + e -> bf16 steps 4 c + 2 e, 4 c + 2 e + 1
             const char *kb = lds + VRING + ((u / BPS) % F8) * SB8 + (u % BPS) * (32 * D);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int4 x0 = *(const int4 *)(kb + koff8[kk][0]);
-                const int4 x1 = *(const int4 *)(kb + koff8[kk][1]);
-                ka[kk] = i32x8{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            }
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    int4 lo, hi;
+                    fp8x16_to_bf16(*(const int4 *)(kb + koff8[c][e]), lo, hi);
+                    ka[4 * c + 2 * e] = __builtin_bit_cast(bf16x8, lo);
+                    ka[4 * c + 2 * e + 1] = __builtin_bit_cast(bf16x8, hi);
+                }
         } else {
             const char *kb = block_base(u);
 #pragma unroll
@@ -1158,21 +1123,12 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
                 va[t][cc] = __builtin_bit_cast(bf16x8, pair);
             }
     };
-    // S^T of one block: keys x rows, lane l holding row l % 32.  FP8: two
-    // E4M3 x E4M3 MFMA steps of 64 channels (format 0 = E4M3 for both
-    // operands, block scales 2^0).
+    // S^T of one block: keys x rows, lane l holding row l % 32.
     auto qk = [&](const auto &ka) {
         f32x16 acc;
-        if constexpr (KV8) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[kk], qv8[kk], kk ? acc : f32x16{},
-                                                                      0, 0, 0, 127, 0, 127);
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qv[kk], kk ? acc : f32x16{}, 0, 0, 0);
-        }
+        for (int kk = 0; kk < KSTEPS; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qv[kk], kk ? acc : f32x16{}, 0, 0, 0);
         return acc;
     };
     // bf16 weights of one block and their sum (the values the MFMA multiplies)
@@ -1283,7 +1239,7 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
     }
     if (nb > 0) {
         stage_ready(0);
-        std::conditional_t<KV8, KOp, KOpB> ka;
+        bf16x8 ka[KSTEPS];
         bf16x8 va[DT][2], pa[2], pbb[2];
         f32x16 s;
         load_k(0, ka);
