@@ -211,6 +211,38 @@ tav_status tree_attention_window_merge(const void *q, const void *k_cache, const
                                        size_t workspace_bytes, void *stream);
 
 /*
+ * tree_attention without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the split-K partials live in a fixed device
+ * array of TAV_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends.  Arguments, outputs and errors are
+ * tree_attention's, minus workspace and workspace_bytes; the call allocates
+ * nothing and launches the same kernels.
+ *   Limit: shapes whose partials (tree_attention_workspace_size) exceed
+ *   TAV_NOALLOC_SCRATCH_BYTES are refused with TAV_ERR_WORKSPACE before
+ *   anything is launched (long-context B 4, R 64, Hq 32, D 128 needs about
+ *   38 MB; B 32, R 64, Hq 64 about 135 MB and is refused).
+ *   Sharing: every call on one GPU uses that GPU's one array, which keeps
+ *   the last call's partials; calls that overlap on one GPU (other streams,
+ *   other threads) race and must be serialised by the caller.  No part of
+ *   the array needs to start at zero: each call writes every partial it
+ *   reads before reading it.
+ *   The first call on a GPU resolves the array's address there (with that
+ *   GPU made current for the lookup) and may return TAV_ERR_HIP if that
+ *   fails.
+ */
+#define TAV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+tav_status tree_attention_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                  tav_dtype dtype, int64_t stride_page, int64_t stride_head,
+                                  int64_t stride_token, int64_t num_pages,
+                                  const int32_t *page_table, int32_t max_pages,
+                                  int32_t page_size, const int32_t *prefix_len,
+                                  int32_t max_prefix_len, int32_t prefix_window,
+                                  const uint64_t *masks, int32_t W, int32_t B, int32_t R,
+                                  int32_t Hq, int32_t Hkv, int32_t D, float sm_scale,
+                                  void *out, float *lse2, void *stream);
+
+/*
  * Greedy tree verify ([MEM] "Walking the accepted path"): from the root, move
  * to the child whose draft token equals the target's argmax at the current
  * node; stop when no child matches.  Ties between children carrying the same

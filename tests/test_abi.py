@@ -130,6 +130,37 @@ def test_small_entry_points_reject(L):
     assert "prefix_len is NULL" in L.tav_last_error().decode()
 
 
+def noalloc_call(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=tav.TAV_BF16, sp=8 * 64 * 128, sh=64 * 128, st=128,
+             num_pages=100, pt=FAKE, max_pages=20, ps=64, plen=FAKE, maxp=1000, pw=0, masks=FAKE,
+             W=64, B=2, R=64, Hq=32, Hkv=8, D=128, scale=0.0, out=FAKE, lse=FAKE)
+    a.update(kw)
+    st = L.tree_attention_noalloc(a["q"], a["k"], a["v"], a["dtype"], a["sp"], a["sh"], a["st"],
+                                  a["num_pages"], a["pt"], a["max_pages"], a["ps"], a["plen"],
+                                  a["maxp"], a["pw"], a["masks"], a["W"], a["B"], a["R"], a["Hq"],
+                                  a["Hkv"], a["D"], a["scale"], a["out"], a["lse"], None)
+    return st, L.tav_last_error().decode()
+
+
+@no_gpu
+def test_noalloc_refuses_shapes_past_its_scratch(L):
+    # B 32, R 64, Hq 64, Hkv 8, P 8192: ~135 MB of partials > 64 MiB
+    st, msg = noalloc_call(L, B=32, Hq=64, maxp=8192, max_pages=8192 // 64 + 1)
+    assert st == 3, msg
+    assert "static scratch array" in msg and str(tav.NOALLOC_SCRATCH_BYTES) in msg, msg
+    assert tav.tree_attention_workspace_size(torch.bfloat16, 32, 64, 64, 8, 128, 8192, 0, 64) \
+        > tav.NOALLOC_SCRATCH_BYTES
+    # argument errors are reported as for tree_attention
+    st, msg = noalloc_call(L, R=65, D=96)
+    assert st != 0 and "R must be" in msg and "D must be" in msg, msg
+
+
+def test_noalloc_limit_matches_the_header():
+    text = open(HEADER).read()
+    assert re.search(r"#define TAV_NOALLOC_SCRATCH_BYTES \(\(size_t\)64 << 20\)", text)
+    assert tav.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
 def test_empty_batch_is_a_no_op(L):
     # B = 0 launches nothing and succeeds (no pointer is touched)
     assert L.tree_build_masks(None, 0, 8, None, None, None, None, None, None) == 0
@@ -137,6 +168,9 @@ def test_empty_batch_is_a_no_op(L):
     assert L.tree_shift_positions(None, None, 0, 8, 1, None) == 0
     st, msg = attn_call(L, B=0, q=None, k=None, v=None, pt=None, plen=None, masks=None,
                         out=None, lse=None, ws=None)
+    assert st == 0, msg
+    st, msg = noalloc_call(L, B=0, q=None, k=None, v=None, pt=None, plen=None, masks=None,
+                           out=None, lse=None)
     assert st == 0, msg
     assert L.compact_window_rows(None, 0, None, None, 0, 8, None) == 0
 

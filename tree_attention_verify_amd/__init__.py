@@ -12,7 +12,8 @@ Entry points (same names as the C ABI):
   tree_attention_workspace_size, verify_tree_greedy, compact_window_rows,
   tree_sample_gumbel, tree_sample_workspace_size, tree_beam_step,
   tree_select_candidates, tree_retrieve_links, tree_attention_mla,
-  tree_attention_mla_workspace_size, verify_tree_rejection
+  tree_attention_mla_workspace_size, verify_tree_rejection,
+  tree_attention_noalloc
 plus verify_tree_sampled (tree_sample_gumbel, then verify_tree_greedy over
 the draws).
 """
@@ -38,7 +39,7 @@ EXPORTS = ("tav_last_error", "tav_version", "tree_build_masks", "tree_shift_posi
            "tree_attention_window_merge", "verify_tree_greedy", "compact_window_rows",
            "tree_sample_workspace_size", "tree_sample_gumbel", "tree_beam_step",
            "tree_select_candidates", "tree_retrieve_links", "tree_attention_mla_workspace_size",
-           "tree_attention_mla", "verify_tree_rejection")
+           "tree_attention_mla", "verify_tree_rejection", "tree_attention_noalloc")
 
 
 class TavError(RuntimeError):
@@ -91,6 +92,8 @@ def lib() -> ctypes.CDLL:
         for f in ("tree_attention", "tree_attention_prefix", "tree_attention_window_merge"):
             getattr(L, f).argtypes = attn
             getattr(L, f).restype = ctypes.c_int
+        L.tree_attention_noalloc.argtypes = attn[:24] + [P]
+        L.tree_attention_noalloc.restype = ctypes.c_int
         L.verify_tree_greedy.argtypes = [P, P, P, I32, I32, P, P, P, P]
         L.compact_window_rows.argtypes = [ctypes.POINTER(TavRows), I32, P, P, I32, I32, P]
         L.tree_sample_workspace_size.argtypes = [I32, I32, I32]
@@ -110,7 +113,7 @@ def lib() -> ctypes.CDLL:
         for f in ("tree_build_masks", "tree_shift_positions", "tree_attention",
                   "verify_tree_greedy", "compact_window_rows", "tree_sample_gumbel",
                   "tree_beam_step", "tree_select_candidates", "tree_retrieve_links",
-                  "tree_attention_mla", "verify_tree_rejection"):
+                  "tree_attention_mla", "verify_tree_rejection", "tree_attention_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -254,6 +257,43 @@ def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                                 _ptr(masks), int(W), B, R, Hq, Hkv, D, float(sm_scale),
                                 _ptr(out), _ptr(lse2), _ptr(workspace), workspace.numel(),
                                 _stream(dev)))
+    return out, lse2
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # TAV_NOALLOC_SCRATCH_BYTES
+
+
+def tree_attention_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           page_table: torch.Tensor, prefix_len: torch.Tensor,
+                           masks: torch.Tensor, W: int, *, max_prefix_len: int, out: torch.Tensor,
+                           lse2: Optional[torch.Tensor] = None, layout: str = "HND",
+                           prefix_window: int = 0, sm_scale: float = 0.0):
+    """tree_attention with its partials in the library's fixed device array
+    (no workspace, nothing allocated here or in the library: the caller
+    passes out, and lse2 or None).  Calls that overlap on one GPU race.
+    Returns (out, lse2)."""
+    dt = _code(q.dtype, k_cache.dtype)
+    _need(q, "q", q.dtype)
+    dev = q.device
+    B, R, Hq, D = q.shape
+    _need(k_cache, "k_cache", k_cache.dtype, dev)
+    _need(v_cache, "v_cache", k_cache.dtype, dev)
+    sp, sh, st, Hkv, ps = kv_strides(k_cache, layout)
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("v_cache must have k_cache's shape")
+    _need(page_table, "page_table", torch.int32, dev)
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [B][max_pages]")
+    _need(prefix_len, "prefix_len", torch.int32, dev, (B,))
+    _need(masks, "masks", torch.int64, dev, (B, R))
+    _need(out, "out", q.dtype, dev, q.shape)
+    if lse2 is not None:
+        _need(lse2, "lse2", torch.float32, dev, (B, R, Hq))
+    _check(lib().tree_attention_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), dt, sp, sh, st,
+                                        k_cache.shape[0], _ptr(page_table), page_table.shape[1],
+                                        ps, _ptr(prefix_len), int(max_prefix_len),
+                                        int(prefix_window), _ptr(masks), int(W), B, R, Hq, Hkv, D,
+                                        float(sm_scale), _ptr(out), _ptr(lse2), _stream(dev)))
     return out, lse2
 
 

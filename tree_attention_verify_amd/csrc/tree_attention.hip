@@ -23,6 +23,7 @@
 //       keys (popcount(mask) of them, never the unseen ones) and the merge of
 //       every prefix partial with the window part into out / lse2.
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -2273,4 +2274,87 @@ extern "C" tav_status tree_attention_prefix(TAV_ATTN_PARAMS) {
 
 extern "C" tav_status tree_attention_window_merge(TAV_ATTN_PARAMS) {
     return run_phases("tree_attention_window_merge", 2, TAV_ATTN_ARGS, stream);
+}
+
+// ---------------------------------------------------------------------------
+// allocation-free variant: the partials live in a fixed device array
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// One copy per GPU the library runs on, held until the process ends.  In
+// host code `scratch` only names the symbol; its device address on each GPU
+// comes from hipGetSymbolAddress with that GPU current.
+constexpr size_t kScratchBytes = TAV_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the GPU that runs `stream` (the current
+// device for the null stream), resolved on the first call for that GPU.
+tav_status scratch_on(const char *fn, hipStream_t stream, void **ptr) {
+    int dev = -1;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        tav::set_error(fn, std::string("cannot tell the stream's device: ") +
+                               (e != hipSuccess ? hipGetErrorString(e) : "ordinal out of range"));
+        return TAV_ERR_HIP;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev)
+            e = hipSetDevice(dev);
+        void *p = nullptr;
+        if (e == hipSuccess)
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur >= 0 && cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            e = e == hipSuccess ? e2 : e;
+        }
+        if (e != hipSuccess || !p) {
+            tav::set_error(fn, std::string("cannot resolve the static scratch array: ") +
+                                   (e != hipSuccess ? hipGetErrorString(e) : "null address"));
+            return TAV_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return TAV_OK;
+}
+
+}  // namespace
+
+extern "C" tav_status tree_attention_noalloc(
+    const void *q, const void *k_cache, const void *v_cache, tav_dtype dtype, int64_t stride_page,
+    int64_t stride_head, int64_t stride_token, int64_t num_pages, const int32_t *page_table,
+    int32_t max_pages, int32_t page_size, const int32_t *prefix_len, int32_t max_prefix_len,
+    int32_t prefix_window, const uint64_t *masks, int32_t W, int32_t B, int32_t R, int32_t Hq,
+    int32_t Hkv, int32_t D, float sm_scale, void *out, float *lse2, void *stream) {
+    const char *fn = "tree_attention_noalloc";
+    tav::Checks c;
+    if (shape_ok(dtype, B, R, Hq, Hkv, D, max_prefix_len, prefix_window, page_size, &c)) {
+        const size_t need =
+            make_plan(dtype, B, R, Hq, Hkv, D, max_prefix_len, prefix_window, page_size).bytes;
+        c.need(need <= kScratchBytes, TAV_ERR_WORKSPACE,
+               "this shape needs " + tav::str((long long)need) +
+                   " bytes of partials, more than the static scratch array holds (" +
+                   tav::str((long long)kScratchBytes) +
+                   "); call tree_attention with a workspace instead");
+    }
+    if (c.status != TAV_OK)
+        return tav::finish(fn, c);
+    void *ws = nullptr;
+    if (B > 0) {
+        const tav_status st = scratch_on(fn, reinterpret_cast<hipStream_t>(stream), &ws);
+        if (st != TAV_OK)
+            return st;
+    }
+    return run_phases(fn, 3, q, k_cache, v_cache, dtype, stride_page, stride_head, stride_token,
+                      num_pages, page_table, max_pages, page_size, prefix_len, max_prefix_len,
+                      prefix_window, masks, W, B, R, Hq, Hkv, D, sm_scale, out, lse2, ws,
+                      kScratchBytes, stream);
 }
