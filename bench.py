@@ -132,6 +132,68 @@ def summarize_stats(workload, stats_dir, cmd):
     print(open(out).read())
 
 
+N_XCD, N_SIMD = 8, 1024     # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def summarize_counters(workload, dirs, cmd):
+    """profiles/<workload>_counters.md from rocprofv3 --pmc runs (one
+    directory per pass): per-dispatch averages of every counter for the
+    prefix kernel, and what they imply (cycles, MFMA utilisation, vector
+    and LDS instructions per unit of work)."""
+    wl = gen.WORKLOADS[workload]
+    kname = prefix_kernel_name(wl)
+    vals, durs = {}, []
+    for d in dirs:
+        rows = [r for r in _csv_rows(os.path.join(d, "**", "*counter_collection.csv"))
+                if kname + "<" in r["Kernel_Name"] or r["Kernel_Name"].endswith(kname)]
+        per = {}
+        for r in rows:
+            per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            durs.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        for k, v in per.items():
+            vals[k] = (sum(v) / len(v), len(v))
+    P_vis = min(wl.P, wl.prefix_window) if wl.prefix_window else wl.P
+    kvb = kv_bytes(wl, P_vis, with_window=False)
+    flops = 4.0 * wl.D * wl.Hq * wl.B * wl.R * P_vis
+    scores = flops / (4.0 * wl.D)
+    g = lambda k: vals.get(k, (float("nan"), 0))[0]
+    dur_ns = float(np.median(durs)) if durs else float("nan")
+    cyc = g("GRBM_GUI_ACTIVE") / N_XCD
+    derived = [
+        ("dispatch duration (median over passes), us", dur_ns / 1e3),
+        ("kernel cycles (GRBM_GUI_ACTIVE / 8 XCDs)", cyc),
+        ("engine clock during the dispatch, GHz", cyc / dur_ns if dur_ns else float("nan")),
+        ("MFMA busy, share of SIMD cycles (SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles))",
+         g("SQ_VALU_MFMA_BUSY_CYCLES") / (N_SIMD * cyc)),
+        ("MFMA instructions per 1024 (row, key) scores (16 = the exact work on 32x32x16 bf16)",
+         g("SQ_INSTS_MFMA") / scores * 1024),
+        ("vector ALU instructions other than MFMA, per 64 scores (one wave-wide op each)",
+         (g("SQ_INSTS_VALU") - g("SQ_INSTS_MFMA")) / scores * 64),
+        ("of which transcendental (v_exp), per 64 scores", g("SQ_INSTS_VALU_TRANS_F32") / scores * 64),
+        ("LDS instructions per KiB of prefix K/V", g("SQ_INSTS_LDS") / (kvb / 1024)),
+        ("MFMA/VALU co-execution, share of MFMA busy cycles",
+         g("SQ_VALU_MFMA_COEXEC_CYCLES") / g("SQ_VALU_MFMA_BUSY_CYCLES")),
+        ("LDS bank-conflict cycles per LDS instruction", g("SQ_LDS_BANK_CONFLICT") / g("SQ_INSTS_LDS")),
+    ]
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, "%s_counters.md" % workload)
+    with open(out, "w") as f:
+        f.write("# rocprofv3 counters of %s, workload %s\n\n" % (kname, wl.describe()))
+        f.write("Commands (one counter pass each; bench.py runs 10 steps after 2 warm-up ones):\n\n")
+        for c in cmd.split(" ;; "):
+            f.write("    %s\n" % c)
+        f.write("\nWork per launch: %.4g bytes of prefix K/V, %.4g flops, %.4g (row, key) scores.\n\n"
+                % (kvb, flops, scores))
+        f.write("| counter | per dispatch (sum over the GPU) | dispatches |\n|---|---|---|\n")
+        for k in sorted(vals):
+            f.write("| %s | %.6g | %d |\n" % (k, vals[k][0], vals[k][1]))
+        f.write("\n| derived | value |\n|---|---|\n")
+        for k, v in derived:
+            f.write("| %s | %.4g |\n" % (k, v))
+        f.write("\nKernel source sha256[:16] %s.\n" % kernel_hash())
+    print(open(out).read())
+
+
 def prefix_kernel_name(wl):
     """The split-K prefix kernel the library launches for this shape."""
     if wl.dtype != "bf16":
@@ -654,12 +716,18 @@ def main():
                     help="write profiles/<workload>_prefix_traffic.{json,md} from rocprofv3 CSVs")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_DIR", "CMD"),
                     help="write profiles/<workload>_kernel_stats.md from rocprofv3 --stats CSVs")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR_OR_CMD",
+                    help="write profiles/<workload>_counters.md from rocprofv3 --pmc passes: "
+                         "the pass directories, then the commands joined by ' ;; '")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(args.workload, *args.summarize_traffic)
         return
     if args.summarize_stats:
         summarize_stats(args.workload, *args.summarize_stats)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.workload, args.summarize_counters[:-1], args.summarize_counters[-1])
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
