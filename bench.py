@@ -680,6 +680,164 @@ def run_mla(args):
     print(json.dumps(res), flush=True)
 
 
+def _smi_sample():
+    """One amd-smi reading: (socket power W, mean GFX clock MHz), or None."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True,
+                           timeout=20)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    pw = re.findall(r"SOCKET_POWER:\s*([0-9.]+)\s*W", r.stdout)
+    clk = re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", r.stdout)
+    if not pw:
+        return None
+    return float(pw[0]), (float(np.mean([float(c) for c in clk])) if clk else float("nan"))
+
+
+def _sustained(run, seconds, per_sync=20, settle=4.0):
+    """Runs `run` back to back for `seconds`; amd-smi is read every ~2 s
+    after `settle` seconds.  -> (ms per call, [(W, MHz)])."""
+    import threading
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        if stop.wait(settle):
+            return
+        while not stop.is_set():
+            s = _smi_sample()
+            if s is not None:
+                samples.append(s)
+            if stop.wait(2.0):
+                return
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(per_sync):
+            run()
+        torch.cuda.synchronize()
+        n += per_sync
+    dt = time.perf_counter() - t0
+    stop.set()
+    th.join()
+    return dt * 1e3 / n, samples
+
+
+def run_power_model(args):
+    """Board power and engine clock, sustained, for the pieces the
+    long-context step is made of: idle; a bf16 GEMM on the MFMA (hipBLASLt
+    through torch.matmul); an HBM copy; the long64 verify step; and the same
+    step with every K/V page aliased onto 8 physical pages (the same
+    arithmetic with the K/V stream served from the caches).  Energy per
+    launch above idle follows from (W - idle W) x time; it prints one JSON
+    line and the table of profiles/long64_power_model.md."""
+    secs = args.power_seconds
+    res = {"metric": "board power model of the long-context verify step", "rows": []}
+    time.sleep(3.0)
+    idle = [s for s in (_smi_sample() for _ in range(3)) if s is not None]
+    idle_w = float(np.median([s[0] for s in idle])) if idle else float("nan")
+    res["idle_w"] = idle_w
+
+    def add(name, ms, samples, work):
+        w = float(np.median([s[0] for s in samples])) if samples else float("nan")
+        mhz = float(np.median([s[1] for s in samples])) if samples else float("nan")
+        row = {"name": name, "ms_per_call": round(ms, 4), "power_w": w, "gfx_mhz": round(mhz),
+               "energy_above_idle_mj": round((w - idle_w) * ms, 4), "samples": len(samples)}
+        row.update(work)
+        res["rows"].append(row)
+        log("%-34s %.4f ms  %6.0f W  %5.0f MHz  %.3f mJ above idle  %s"
+            % (name, ms, w, mhz, row["energy_above_idle_mj"], work))
+
+    n = 8192
+    a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+    b = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+    c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+    ms, smp = _sustained(lambda: torch.matmul(a, b, out=c), secs, per_sync=10)
+    add("bf16 GEMM 8192^3 (torch.matmul)", ms, smp,
+        {"tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1), "flops": 2.0 * n ** 3})
+    del a, b, c
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms, smp = _sustained(lambda: dst.copy_(src), secs)
+    add("HBM copy 1 GiB (read + write)", ms, smp,
+        {"hbm_gbs": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1), "bytes": 2 * COPY_BYTES})
+    del src, dst
+    torch.cuda.empty_cache()
+    wl = gen.WORKLOADS["long64"]
+    inp = gen.make_inputs(wl, args.seed, "cuda")
+    step = Step(wl, inp)
+    kvb = kv_bytes(wl, wl.P)
+    flops = 4.0 * wl.D * wl.Hq * wl.B * wl.R * wl.P
+    ms, smp = _sustained(step.run, secs)
+    add("long64 verify step", ms, smp, {"kv_gbs": round(kvb / (ms * 1e-3) / 1e9, 1),
+                                          "bytes": kvb, "flops": flops})
+    # every logical page of every request on one of 8 physical pages (the
+    # first 8 pages of request 0, all inside its prefix, so finite): the
+    # kernels do the same arithmetic while the K/V reads hit the caches
+    pages8 = inp.page_table[0, :8]
+    alias = pages8[np.arange(inp.page_table.size) % 8].reshape(inp.page_table.shape)
+    step.page_table.copy_(torch.as_tensor(alias.astype(np.int32)))
+    ms, smp = _sustained(step.run, secs)
+    add("long64 step, K/V pages aliased (cached)", ms, smp, {"flops": flops})
+    res["rows_note"] = ("energy_above_idle_mj = (median board power - idle power) x time per call")
+    print(json.dumps(res), flush=True)
+
+
+def summarize_power(json_path, cmd):
+    """profiles/long64_power_model.md from the JSON line of --power-model."""
+    d = json.loads(open(json_path).read().strip().splitlines()[-1])
+    idle = d["idle_w"]
+    rows = {r["name"]: r for r in d["rows"]}
+    gemm = next(r for r in d["rows"] if r["name"].startswith("bf16 GEMM"))
+    copy = next(r for r in d["rows"] if r["name"].startswith("HBM copy"))
+    step = next(r for r in d["rows"] if r["name"] == "long64 verify step")
+    alias = next(r for r in d["rows"] if "aliased" in r["name"])
+    pj_flop = gemm["energy_above_idle_mj"] * 1e-3 / gemm["flops"] * 1e12
+    j_gb = copy["energy_above_idle_mj"] * 1e-3 / (copy["bytes"] / 1e9)
+    flops, kvb = step["flops"], step["bytes"]
+    t_gemm = flops / (gemm["tflops"] * 1e12) * 1e6
+    t70 = kvb / (0.7 * HBM_PEAK_GBS * 1e9) * 1e6
+    out = os.path.join(PROFILES, "long64_power_model.md")
+    with open(out, "w") as f:
+        f.write("# Board power model of the long-context verify step\n\nCommand:\n\n    %s\n\n" % cmd)
+        f.write("Each row runs back to back for 10 s; `amd-smi metric -p -c` is read every ~2 s "
+                "after 4 s and the medians are shown.  Idle board power: %.0f W.  Energy above "
+                "idle per call = (power - idle) x time per call.\n\n" % idle)
+        f.write("| workload | ms per call | board W | GFX MHz | mJ above idle | rate |\n"
+                "|---|---|---|---|---|---|\n")
+        for r in d["rows"]:
+            rate = ("%.0f TFLOP/s" % r["tflops"]) if "tflops" in r else \
+                   ("%.0f GB/s" % r["hbm_gbs"]) if "hbm_gbs" in r else \
+                   ("%.0f GB/s of K/V" % r["kv_gbs"]) if "kv_gbs" in r else \
+                   ("%.0f TFLOP/s" % (r["flops"] / (r["ms_per_call"] * 1e-3) / 1e12))
+            f.write("| %s | %.4f | %.0f | %.0f | %.1f | %s |\n"
+                    % (r["name"], r["ms_per_call"], r["power_w"], r["gfx_mhz"],
+                       r["energy_above_idle_mj"], rate))
+        f.write("\nWhat bounds long64 (B 4, P 131072, N 64, Hq 32, Hkv 8, D 128, bf16: %.4g bytes "
+                "of K/V and %.4g flops per step):\n\n" % (kvb, flops))
+        f.write("- The vendor bf16 GEMM sustains %.0f TFLOP/s at the board's power cap, %.2f of the "
+                "2.5 PFLOP/s dense peak.  At that rate the step's flops alone take %.0f us; 70%% "
+                "of 8 TB/s needs the whole step in %.0f us.\n" % (gemm["tflops"],
+                                                                   gemm["tflops"] / 2500, t_gemm, t70))
+        f.write("- Energy above idle: the GEMM spends %.2f pJ per flop, the copy %.3f J per GB "
+                "moved.  The step's flops at GEMM energy plus its bytes at copy energy come to "
+                "%.0f mJ; the step measures %.0f mJ (%.0f mJ with its pages aliased onto cached "
+                "ones, at a higher clock).\n" % (pj_flop, j_gb, pj_flop * flops * 1e-9 +
+                                                  j_gb * kvb / 1e9 * 1e3,
+                                                  step["energy_above_idle_mj"],
+                                                  alias["energy_above_idle_mj"]))
+        f.write("- At the cap (%.0f W above idle) that additive estimate takes %.0f us per step, "
+                "and the step runs in %.0f us: it sits at the board's power bound.  Neither HBM "
+                "bandwidth (the copy alone streams at %.0f GB/s) nor the MFMA issue rate (the "
+                "compute alone runs at %.0f TFLOP/s) sets its time.\n"
+                % (1400 - idle, (pj_flop * flops * 1e-12 + j_gb * kvb / 1e9) / (1400 - idle) * 1e6,
+                   step["ms_per_call"] * 1e3, copy["hbm_gbs"],
+                   flops / (alias["ms_per_call"] * 1e-3) / 1e12))
+    print(open(out).read())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -712,6 +870,12 @@ def main():
     ap.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
                     help="after the timed steps, run steps back to back for SECONDS (for board "
                          "power and clock readings taken meanwhile) and report their rate")
+    ap.add_argument("--power-model", action="store_true",
+                    help="sustained board power and clock of a bf16 GEMM, an HBM copy, the long64 "
+                         "step and the long64 step over aliased (cached) pages")
+    ap.add_argument("--power-seconds", type=float, default=10.0)
+    ap.add_argument("--summarize-power", nargs=2, metavar=("JSON", "CMD"),
+                    help="write profiles/long64_power_model.md from a --power-model JSON line")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "CMD"),
                     help="write profiles/<workload>_prefix_traffic.{json,md} from rocprofv3 CSVs")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_DIR", "CMD"),
@@ -726,6 +890,9 @@ def main():
     if args.summarize_stats:
         summarize_stats(args.workload, *args.summarize_stats)
         return
+    if args.summarize_power:
+        summarize_power(*args.summarize_power)
+        return
     if args.summarize_counters:
         summarize_counters(args.workload, args.summarize_counters[:-1], args.summarize_counters[-1])
         return
@@ -734,6 +901,9 @@ def main():
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.power_model:
+        run_power_model(args)
+        return
     if args.sampled:
         run_sampled(args)
         return
