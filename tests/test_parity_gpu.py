@@ -124,6 +124,9 @@ SMALL = {
                                      kv_dtype="fp8"), [777, 100]),
     # one 8-way tensor-parallel share of long64: one kv head, 4 query heads
     "long64_tp8": (W_["long64_tp8"].with_(B=2, P=3000), [3000, 2049]),
+    # 64-channel heads with 256 folded rows (the wide-row kernel at D = 64)
+    "d64_rows256": (W_["random16"].with_(name="d64w", B=2, P=1111, N=64, Hq=8, Hkv=2, D=64,
+                                         depth_cap=8), [1111, 250]),
 }
 
 
