@@ -4,12 +4,14 @@ ABI, against the CPU fp64 oracle.
 Every decision of the walk compares fp32 sums in the kernel and fp64 sums
 in the oracle.  The path and the drafted tokens must match the oracle's,
 unless the oracle reports that one of the children's tests came within
-MARGIN (relative to the row total) of a tie; such requests must be rare.
+MARGIN (relative to the row total) of a tie, and at most MAX_WALKS_OFF
+requests per case may differ that way.
 The bonus token is a draw by inverse CDF, where a single token can hold
 less of the row than the fp32 error of a running sum over 128256 tokens, so
 it must match the oracle's or be a token whose fp64 running-sum interval
 (of the residual row at the last node) holds the draw's target within
-CDF_TOL of the row's residual total.
+CDF_TOL of the row's residual total, for at most MAX_BONUS_OFF requests per
+case.
 """
 import sys
 
@@ -25,6 +27,12 @@ pytestmark = pytest.mark.gpu
 
 MARGIN = 2e-5
 CDF_TOL = 2e-5
+# Bounds on the differences per case, set just above what the seeded cases
+# show (every walk equal, at most one bonus draw resolved differently by
+# fp32 rounding): a walk may differ only at a near tie, and at most one per
+# case; at most two bonus draws per case may differ, each within CDF_TOL.
+MAX_WALKS_OFF = 1
+MAX_BONUS_OFF = 2
 
 
 def say(*a):
@@ -58,7 +66,7 @@ def run_and_check(x, with_score=True, tag="", max_near=None):
     near = ref["margin"] < MARGIN
     bad = np.nonzero(~walk_same & ~near)[0]
     assert bad.size == 0, (tag, bad[:5], path[bad[:1]], ref["accepted_path"][bad[:1]])
-    assert (~walk_same).sum() <= (max_near if max_near is not None else max(1, B // 50)), tag
+    assert (~walk_same).sum() <= (max_near if max_near is not None else MAX_WALKS_OFF), tag
     probs_h = None
     n_cdf = 0
     for b in np.nonzero(walk_same)[0]:
@@ -88,7 +96,7 @@ def run_and_check(x, with_score=True, tag="", max_near=None):
     say(tag, "B %d N %d V %d: %d of %d walks equal (%d near a tie), %d bonus draws off by "
         "rounding, mean accept_len %.2f" % (B, N, V, int(walk_same.sum()), B, int(near.sum()),
                                             n_cdf, float(alen.mean())))
-    assert n_cdf <= max(2, B // 4), tag
+    assert n_cdf <= MAX_BONUS_OFF, tag
     # the walk is a path from the root through parent links
     for b in range(B):
         p = path[b, :alen[b]]
@@ -201,7 +209,7 @@ def run_and_check_q(x, tag=""):
     near = ref["margin"] < MARGIN
     bad = np.nonzero(~walk_same & ~near)[0]
     assert bad.size == 0, (tag, bad[:5], path[bad[:1]], ref["accepted_path"][bad[:1]])
-    assert (~walk_same).sum() <= max(1, B // 50), tag
+    assert (~walk_same).sum() <= MAX_WALKS_OFF, tag
     n_cdf = 0
     for b in np.nonzero(walk_same)[0]:
         L = int(alen[b])
@@ -220,7 +228,7 @@ def run_and_check_q(x, tag=""):
     say(tag, "q form, B %d N %d V %d: %d of %d walks equal (%d near a tie), %d bonus draws off by "
         "rounding, mean accept_len %.2f" % (B, N, V, int(walk_same.sum()), B, int(near.sum()),
                                             n_cdf, float(alen.mean())))
-    assert n_cdf <= max(2, B // 4), tag
+    assert n_cdf <= MAX_BONUS_OFF, tag
 
 
 @pytest.mark.parametrize("name", ["eagle_tiles", "random_ragged", "chain_deep", "padded_rows",

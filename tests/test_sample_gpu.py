@@ -5,8 +5,8 @@ The draw is an argmax decided in floating point.  The kernel scores in fp32
 and the oracle in fp64, so a row whose two best perturbed scores are closer
 than the fp32 error of the scores may legitimately go either way.  Every row
 must therefore either match the oracle's token, or pick a token whose oracle
-score is within TIE_TOL of the oracle's best (a near tie); and near ties must
-be rare.  Greedy rows (temperature 0) compare plain logits and are
+score is within TIE_TOL of the oracle's best (a near tie), and at most one
+row per case may be such a tie.  Greedy rows (temperature 0) compare plain logits and are
 bit-exact.  The accepted paths of the sampled verify are then bit-exact
 against the oracle's greedy walk over the same draws.
 """
@@ -83,7 +83,8 @@ def check_draws(got, s, positions, rows=None, tag=""):
             tag, b, i, g, zg, o, zmax[n, 0])
         ties += 1
     say(tag, "%d rows, %d near-tie differences" % (len(rows), ties))
-    assert ties <= max(1, len(rows) // 100)
+    # the seeded cases show none; one near tie per case is allowed
+    assert ties <= 1
     return tok
 
 

@@ -1878,19 +1878,28 @@ __global__ void __launch_bounds__(256) k_merge(MergeArgs a) {
     if (mx != -INFINITY) {
         float zs = 0.f;
         const float *op = a.ws_o + row * a.S * D + lane * VPL;
-#pragma unroll 4
-        for (int s = 0; s < a.S; ++s) {
-            const float ls = lp[s];
-            const float z = ls != -INFINITY ? fast_exp2(ls - mx) : 0.f;
-            zs += z;
-            float x[VPL];
+        // MB partials per round, their loads all in flight before the first
+        // use (with many splits the merge is bound by load latency)
+        constexpr int MB = 16;
+        for (int s0 = 0; s0 < a.S; s0 += MB) {
+            float x[MB][VPL], ls[MB];
 #pragma unroll
-            for (int i = 0; i < VPL; ++i)
-                x[i] = op[(int64_t)s * D + i];
-            if (ls != -INFINITY) {
+            for (int j = 0; j < MB; ++j) {
+                const bool in = s0 + j < a.S;
+                ls[j] = in ? lp[s0 + j] : -INFINITY;
 #pragma unroll
                 for (int i = 0; i < VPL; ++i)
-                    acc[i] = fmaf(z, x[i], acc[i]);
+                    x[j][i] = in ? op[(int64_t)(s0 + j) * D + i] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < MB; ++j) {
+                const float z = ls[j] != -INFINITY ? fast_exp2(ls[j] - mx) : 0.f;
+                zs += z;
+                if (ls[j] != -INFINITY) {
+#pragma unroll
+                    for (int i = 0; i < VPL; ++i)
+                        acc[i] = fmaf(z, x[j][i], acc[i]);
+                }
             }
         }
         const float inv = 1.f / zs;
