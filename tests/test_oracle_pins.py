@@ -686,6 +686,22 @@ def test_philox4x32_10_known_answers():
         assert oracle.philox4x32_10(h("ctr"), h("key")).tolist() == h("out")
 
 
+def test_gumbel_uniforms_of_seed_0_position_0_are_the_first_known_answer():
+    """Seed 0 is key {0, 0} and tokens 0..3 at key position 0 take counter
+    {0, 0, 0, 0}: their uniforms are the four output words of the first
+    known-answer vector, top 24 bits plus one half, over 2^24."""
+    g = load("philox4x32_kat.txt")
+    assert [int(str(x), 16) for x in g["ctr0"]] == [0, 0, 0, 0]
+    assert [int(str(x), 16) for x in g["key0"]] == [0, 0]
+    words = [int(str(x), 16) for x in g["out0"]]
+    for v in range(4):
+        assert oracle.gumbel_uniform(0, 0, v) == ((words[v] >> 8) + 0.5) / 2 ** 24
+    # written out for word 0 (0x6627e8d5): top 24 bits 0x6627e8 = 6694888
+    assert oracle.gumbel_uniform(0, 0, 0) == (6694888 + 0.5) / 16777216
+    # token 4 starts the next counter: not one of these words
+    assert oracle.gumbel_uniform(0, 0, 4) not in [((w >> 8) + 0.5) / 2 ** 24 for w in words]
+
+
 def test_gumbel_uniforms_are_uniform_on_the_open_interval():
     u = np.array([oracle.gumbel_uniform(12345, p, v) for p in range(40) for v in range(500)])
     assert (u > 0).all() and (u < 1).all()
