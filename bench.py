@@ -283,7 +283,8 @@ class Step:
         step's end (all on the step's stream)."""
         L, wl = self.L, self.wl
         B, N = wl.B, wl.N
-        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec = (lambda i: ev[i].record() if ev[i] is not None else None) if ev is not None \
+            else (lambda i: None)
         rec(0)
         if not self.lanes:
             assert L.tree_build_masks(self.parents.data_ptr(), B, N, self.prefix_len.data_ptr(),
@@ -960,7 +961,11 @@ def bench_workload(wl, args, flushed):
     log("warmup done")
 
     mk = lambda: torch.cuda.Event(enable_timing=True)
-    evs = [[mk() for _ in range(5)] for _ in range(args.steps)]
+    # flushed reps time every part of each step; back-to-back steps record
+    # only the two events around the prefix launch (the roofline's timing),
+    # so markers between the small kernels do not lengthen the step
+    evs = [[mk() for _ in range(5)] if flushed else [None, mk(), mk(), None, None]
+           for _ in range(args.steps)]
     start, end = mk(), mk()
     torch.cuda.synchronize()
     t_host = time.perf_counter()
@@ -972,9 +977,13 @@ def bench_workload(wl, args, flushed):
     end.record()
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
-    step_ms = [e[0].elapsed_time(e[4]) for e in evs]
     prefix_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    attn_ms = [e[1].elapsed_time(e[3]) for e in evs]
+    if flushed:
+        step_ms = [e[0].elapsed_time(e[4]) for e in evs]
+        attn_ms = [e[1].elapsed_time(e[3]) for e in evs]
+    else:
+        step_ms = [start.elapsed_time(end) / args.steps]
+        attn_ms = [float("nan")]
     if flushed:
         ms_step = float(np.median(step_ms))
         prefix_t = float(np.median(prefix_ms))
@@ -1031,7 +1040,8 @@ def bench_workload(wl, args, flushed):
         "attention_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "timing": {"llc_flushed": bool(flushed),
                    "flush_bytes": FLUSH_BYTES if flushed else 0,
-                   "step_ms": pct(step_ms), "tree_attention_ms": pct(attn_ms),
+                   "step_ms": pct(step_ms),
+                   "tree_attention_ms": pct(attn_ms) if flushed else None,
                    "prefix_ms": pct(prefix_ms),
                    "value_from": "median step" if flushed else
                                  "K back-to-back steps between two events"},
