@@ -377,8 +377,12 @@ tav_status tree_sample_gumbel(const void *logits, tav_dtype dtype, int64_t row_s
  * exact when the children are independent draws from q tested in an order
  * that does not depend on the drawn tokens.
  *
- * Sums are fp32 in the kernel's order, so a decision within rounding of a
- * tie may differ from an exact evaluation.
+ * Sums are fp32 in a fixed order (tiles of 256 tokens, slices of 64 tiles,
+ * the slices in order), so a decision within rounding of a tie may differ
+ * from an exact evaluation; the outcome is the same on every run.  Where
+ * fp32 rounding leaves the bonus draw's running sum short of the target at
+ * a level of its search (slice, tile, token), the last positive entry of
+ * that level is taken.
  *
  * probs        device fp32 [B][N][row_stride], V used per row: the target
  *              distribution after the node (softmax at the sampling
@@ -395,15 +399,25 @@ tav_status tree_sample_gumbel(const void *logits, tav_dtype dtype, int64_t row_s
  * accepted_path, accept_len, accepted_tokens as verify_tree_greedy; the
  *              tokens are draft[path[k + 1]] for k + 1 < accept_len and the
  *              bonus at k = accept_len - 1 (NULL to skip)
+ * workspace    device, >= verify_tree_rejection_workspace_size(B, N, V)
+ *              bytes, 256-byte aligned; owned by the caller, cleared and
+ *              used by the call (the slice totals and tile sums of the
+ *              workgroups that share a request's row passes), so calls that
+ *              may overlap need workspaces of their own
  * B >= 0; 1 <= N <= 64; 1 <= V <= 2^20
+ * The workgroups of a request wait for one another's slice totals in the
+ * workspace, each wait bounded; should one give up, the request reports
+ * accept_len -1 and a path of -1.
  */
+size_t verify_tree_rejection_workspace_size(int32_t B, int32_t N, int32_t V);
 tav_status verify_tree_rejection(const float *probs, int64_t row_stride, int32_t V,
                                  const float *draft_q, int64_t q_row_stride,
                                  const int32_t *draft_tokens, const int32_t *parents,
                                  const float *draft_score, const float *coins,
                                  const float *bonus_u, int32_t B, int32_t N,
                                  int32_t *accepted_path, int32_t *accept_len,
-                                 int32_t *accepted_tokens, void *stream);
+                                 int32_t *accepted_tokens, void *workspace,
+                                 size_t workspace_bytes, void *stream);
 
 /*
  * The same cascade over an MLA latent cache ([DTS] "One tree attention ...":

@@ -226,12 +226,13 @@ def test_sample_empty_batch_is_a_no_op(L):
 
 def rejection_call(L, **kw):
     a = dict(probs=FAKE, rs=128256, V=128256, q=None, qs=0, draft=FAKE, par=FAKE, score=None,
-             coins=FAKE, bu=FAKE, B=4, N=64, path=FAKE, alen=FAKE, tok=FAKE)
+             coins=FAKE, bu=FAKE, B=4, N=64, path=FAKE, alen=FAKE, tok=FAKE, ws=FAKE,
+             wsb=1 << 30)
     a.update(kw)
     st = L.verify_tree_rejection(a["probs"], a["rs"], a["V"], a["q"], a["qs"], a["draft"],
                                  a["par"], a["score"],
                                  a["coins"], a["bu"], a["B"], a["N"], a["path"], a["alen"],
-                                 a["tok"], None)
+                                 a["tok"], a["ws"], a["wsb"], None)
     return st, L.tav_last_error().decode()
 
 
@@ -246,6 +247,9 @@ def rejection_call(L, **kw):
     (dict(path=None), 1, ["accepted_path is NULL"]),
     (dict(q=FAKE, qs=1000), 1, ["q_row_stride must be >= V"]),
     (dict(q=FAKE + 8, qs=128258), 1, ["multiple of 4 elements", "draft_q is not 16-byte aligned"]),
+    (dict(ws=None), 3, ["workspace is NULL"]),
+    (dict(ws=FAKE + 16), 3, ["workspace is not 256-byte aligned"]),
+    (dict(wsb=1000), 3, ["workspace too small"]),
 ])
 def test_verify_tree_rejection_rejects(L, kw, status, words):
     st, msg = rejection_call(L, **kw)
@@ -256,8 +260,20 @@ def test_verify_tree_rejection_rejects(L, kw, status, words):
 
 def test_rejection_empty_batch_is_a_no_op(L):
     st, msg = rejection_call(L, B=0, probs=None, draft=None, par=None, coins=None, bu=None,
-                             path=None, alen=None, tok=None)
+                             path=None, alen=None, tok=None, ws=None, wsb=0)
     assert st == 0, msg
+
+
+def test_rejection_workspace_size(L):
+    f = L.verify_tree_rejection_workspace_size
+    # out of range: 0
+    assert f(-1, 64, 1000) == 0 and f(4, 0, 1000) == 0 and f(4, 65, 1000) == 0
+    assert f(4, 64, 0) == 0 and f(4, 64, (1 << 20) + 1) == 0
+    # grows with the batch and the vocabulary, in 256-byte units
+    a, b, c = f(4, 64, 128256), f(32, 64, 128256), f(32, 64, 1 << 20)
+    assert 0 < a < b < c and a % 256 == b % 256 == c % 256 == 0
+    # at least the per-request tile sums of a row (one float per 256 tokens)
+    assert b >= 32 * (128256 // 256) * 4
 
 
 @no_gpu

@@ -113,6 +113,11 @@ CASES = {
     "tiny_vocab": (64, 8, 3, "random", 4, 0.9),
     "padded_rows": (32, 32, 1000, "random", 1004, 0.9),
     "single_node": (16, 1, 500, "chain", None, 1.0),
+    # several workgroups per request: 782 tiles in 13 slices (the last one
+    # partial, its last tile 64 tokens), 13 workgroups per request
+    "many_slices": (2, 64, 200000, "eagle", None, 0.75),
+    # the largest vocabulary: 64 slices, 64 workgroups per request
+    "max_vocab": (2, 16, 1 << 20, "random", None, 0.9),
 }
 
 
@@ -232,7 +237,7 @@ def run_and_check_q(x, tag=""):
 
 
 @pytest.mark.parametrize("name", ["eagle_tiles", "random_ragged", "chain_deep", "padded_rows",
-                                  "one_tile"])
+                                  "one_tile", "many_slices", "max_vocab"])
 def test_rejection_against_q_parity(name):
     B, N, V, tree, rs, agree = CASES[name]
     x = gen.make_rejection_inputs(B, N, V, 41, "cuda", tree=tree, row_stride=rs, agree=agree,
@@ -278,3 +283,26 @@ def test_rejection_full_path_on_a_64_node_chain(form):
         target = float(bu[b, N - 1]) * c[b, -1]
         lo = c[b, g] - float(p[b, N - 1, g])
         assert lo <= target + CDF_TOL * c[b, -1] and c[b, g] >= target - CDF_TOL * c[b, -1]
+
+
+def test_rejection_workspace_reused_across_calls():
+    """One workspace serves calls of different shapes and both forms in a
+    row (each call clears the counters it uses): every result is bit-identical
+    to a call with a fresh workspace, and to a repeat of itself."""
+    big = tav.verify_tree_rejection_workspace_size(32, 64, 70000)
+    ws = torch.full((big,), 0xA5, dtype=torch.uint8, device="cuda")   # not zero to begin with
+    for B, N, V, seed, with_q in [(32, 64, 70000, 61, False), (8, 16, 3000, 62, True),
+                                  (32, 64, 70000, 63, True), (4, 64, 70000, 64, False)]:
+        x = gen.make_rejection_inputs(B, N, V, seed, "cuda", tree="eagle", with_q=with_q)
+        args = (x.probs, dev(x.draft), dev(x.parents), dev(x.coins, torch.float32),
+                dev(x.bonus_u, torch.float32))
+        kw = dict(draft_score=dev(x.draft_score, torch.float32),
+                  draft_q=x.draft_q if with_q else None)
+        fresh = tav.verify_tree_rejection(*args, **kw)
+        for rep in range(2):
+            got = tav.verify_tree_rejection(*args, **kw, workspace=ws)
+            torch.cuda.synchronize()
+            for k in ("accepted_path", "accept_len", "accepted_tokens"):
+                assert torch.equal(got[k], fresh[k]), (B, N, V, with_q, rep, k)
+        assert int(fresh["accept_len"].min()) >= 1
+        say("workspace reuse B %d N %d V %d q %s: identical" % (B, N, V, with_q))

@@ -13,7 +13,7 @@ Entry points (same names as the C ABI):
   tree_sample_gumbel, tree_sample_workspace_size, tree_beam_step,
   tree_select_candidates, tree_retrieve_links, tree_attention_mla,
   tree_attention_mla_workspace_size, verify_tree_rejection,
-  tree_attention_noalloc
+  verify_tree_rejection_workspace_size, tree_attention_noalloc
 plus verify_tree_sampled (tree_sample_gumbel, then verify_tree_greedy over
 the draws).
 """
@@ -39,7 +39,8 @@ EXPORTS = ("tav_last_error", "tav_version", "tree_build_masks", "tree_shift_posi
            "tree_attention_window_merge", "verify_tree_greedy", "compact_window_rows",
            "tree_sample_workspace_size", "tree_sample_gumbel", "tree_beam_step",
            "tree_select_candidates", "tree_retrieve_links", "tree_attention_mla_workspace_size",
-           "tree_attention_mla", "verify_tree_rejection", "tree_attention_noalloc")
+           "tree_attention_mla", "verify_tree_rejection", "verify_tree_rejection_workspace_size",
+           "tree_attention_noalloc")
 
 
 class TavError(RuntimeError):
@@ -108,12 +109,15 @@ def lib() -> ctypes.CDLL:
         L.tree_attention_mla.argtypes = [P, P, ctypes.c_int, I64, I64, I64, P, I32, I32, P, I32,
                                          P, I32, I32, I32, I32, I32, I32, ctypes.c_float, P, P, P,
                                          ctypes.c_size_t, P]
+        L.verify_tree_rejection_workspace_size.argtypes = [I32, I32, I32]
+        L.verify_tree_rejection_workspace_size.restype = ctypes.c_size_t
         L.verify_tree_rejection.argtypes = [P, I64, I32, P, I64, P, P, P, P, P, I32, I32, P, P, P,
-                                            P]
+                                            P, ctypes.c_size_t, P]
         for f in ("tree_build_masks", "tree_shift_positions", "tree_attention",
                   "verify_tree_greedy", "compact_window_rows", "tree_sample_gumbel",
                   "tree_beam_step", "tree_select_candidates", "tree_retrieve_links",
-                  "tree_attention_mla", "verify_tree_rejection", "tree_attention_noalloc"):
+                  "tree_attention_mla", "verify_tree_rejection", "verify_tree_rejection_workspace_size",
+           "tree_attention_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -364,13 +368,16 @@ def verify_tree_sampled(draft_tokens: torch.Tensor, logits: torch.Tensor,
 def verify_tree_rejection(probs: torch.Tensor, draft_tokens: torch.Tensor, parents: torch.Tensor,
                           coins: torch.Tensor, bonus_u: torch.Tensor,
                           draft_score: Optional[torch.Tensor] = None, tokens: bool = True,
-                          draft_q: Optional[torch.Tensor] = None):
+                          draft_q: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None):
     """Tree rejection sampling: probs float32 [B][N][V] (the target
     distribution after every node; rows may be padded to a stride of a
     multiple of 4), draft_tokens / parents int32 [B][N], coins / bonus_u
     float32 [B][N] uniform in [0, 1), draft_score float32 [B][N] or None
     (the sibling order), draft_q float32 [B][N][V] or None (the draft
-    distribution that drew each node's children: test against it).
+    distribution that drew each node's children: test against it),
+    workspace uint8 of >= verify_tree_rejection_workspace_size(B, N, V)
+    bytes or None (allocated here).
     -> dict(accepted_path, accept_len, accepted_tokens)."""
     if probs.dtype != torch.float32 or not probs.is_cuda or probs.dim() != 3 \
             or probs.stride(2) != 1 or probs.stride(0) != probs.shape[1] * probs.stride(1):
@@ -395,12 +402,20 @@ def verify_tree_rejection(probs: torch.Tensor, draft_tokens: torch.Tensor, paren
     path = torch.empty((B, N), dtype=torch.int32, device=dev)
     alen = torch.empty((B,), dtype=torch.int32, device=dev)
     tok = torch.empty((B, N), dtype=torch.int32, device=dev) if tokens else None
+    need = verify_tree_rejection_workspace_size(B, N, V)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
     _check(lib().verify_tree_rejection(_ptr(probs), probs.stride(1), V, _ptr(draft_q), qs,
                                        _ptr(draft_tokens),
                                        _ptr(parents), _ptr(draft_score), _ptr(coins),
                                        _ptr(bonus_u), B, N, _ptr(path), _ptr(alen), _ptr(tok),
-                                       _stream(dev)))
+                                       _ptr(workspace), workspace.numel(), _stream(dev)))
     return {"accepted_path": path, "accept_len": alen, "accepted_tokens": tok}
+
+
+def verify_tree_rejection_workspace_size(B: int, N: int, V: int) -> int:
+    return int(lib().verify_tree_rejection_workspace_size(B, N, V))
 
 
 def tree_attention_mla_workspace_size(B: int, R: int, Hq: int, Dc: int, Dr: int,
