@@ -749,26 +749,68 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
         }
     }
 
-    // partial (O / l, lse2) of this split and key subset
-    const int sidx = split * NKS + ks;
+    // The split's partial (O / l, lse2) of each row.  The NKS key subsets of
+    // a row block are combined here, as the merge combines partials: every
+    // wave stores its normalised O (in its MFMA layout: lane and register
+    // index name the same rows and channels in every wave) and its rows'
+    // lse2 in the free stage buffers; then wave ks combines float4 units ks,
+    // ks + NKS, ... of its row block and writes them.  The max is
+    // NaN-propagating, so a NaN subset makes the row NaN.
+    constexpr int NU = DT * 4;   // float4 units of a lane's O
+    static_assert(C::WAVES * NU * 64 * 16 <= LDSB, "key-subset partials fit the stage buffers");
+    __shared__ float cl[NRB * NKS][32];
     const float lt = pair_sum(l_run);
+    const float inv = has_keys(lt) ? 1.f / lt : 0.f;
+    __syncthreads();   // every wave is done with the stage buffers
+    float4 *cb = reinterpret_cast<float4 *>(lds);
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            cb[(w * NU + 4 * t + q4) * 64 + lane] =
+                make_float4(o[t][4 * q4] * inv, o[t][4 * q4 + 1] * inv, o[t][4 * q4 + 2] * inv,
+                            o[t][4 * q4 + 3] * inv);
+    if (hl == 0)
+        cl[w][l32] = has_keys(lt) ? m_run + __log2f(lt) : -INFINITY;
+    __syncthreads();
+    float lk[NKS], z[NKS];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NKS; ++k) {
+        lk[k] = cl[k * NRB + rbw][l32];
+        mx = (lk[k] != lk[k] || mx != mx) ? __builtin_nanf("") : fmaxf(mx, lk[k]);
+    }
+    float zs = 0.f;
+#pragma unroll
+    for (int k = 0; k < NKS; ++k) {
+        z[k] = lk[k] != -INFINITY ? fast_exp2(lk[k] - mx) : 0.f;
+        zs += z[k];
+    }
+    const bool any = mx != -INFINITY;
+    const float zinv = any ? 1.f / zs : 0.f;
     const int m = rows_base + l32;
     if (m < a.M) {
         const int r = m / a.G, hh = m % a.G;
         const int64_t row = ((int64_t)b * a.R + r) * a.Hq + (int64_t)g * a.G + hh;
-        const float inv = has_keys(lt) ? 1.f / lt : 0.f;
-        float *dst = a.ws_o + (row * a.S + sidx) * D;
+        float *dst = a.ws_o + (row * a.S + split) * D;
+        for (int u = ks; u < NU; u += NKS) {
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = ((q4 >> 1) ? D / 2 : 0) + 16 * t + 8 * (q4 & 1) + 4 * hl;
-                float4 v4 = make_float4(o[t][4 * q4] * inv, o[t][4 * q4 + 1] * inv,
-                                        o[t][4 * q4 + 2] * inv, o[t][4 * q4 + 3] * inv);
-                *(float4 *)(dst + d) = v4;
+            for (int k = 0; k < NKS; ++k) {
+                if (lk[k] != -INFINITY) {
+                    const float4 v = cb[((k * NRB + rbw) * NU + u) * 64 + lane];
+                    acc.x = fmaf(z[k], v.x, acc.x);
+                    acc.y = fmaf(z[k], v.y, acc.y);
+                    acc.z = fmaf(z[k], v.z, acc.z);
+                    acc.w = fmaf(z[k], v.w, acc.w);
+                }
             }
-        if (hl == 0)
-            a.ws_lse[row * a.S + sidx] = has_keys(lt) ? m_run + __log2f(lt) : -INFINITY;
+            const int t = u >> 2, q4 = u & 3;
+            const int d = ((q4 >> 1) ? D / 2 : 0) + 16 * t + 8 * (q4 & 1) + 4 * hl;
+            *(float4 *)(dst + d) = make_float4(acc.x * zinv, acc.y * zinv, acc.z * zinv, acc.w * zinv);
+        }
+        if (ks == 0 && hl == 0)
+            a.ws_lse[row * a.S + split] = any ? mx + __log2f(zs) : -INFINITY;
     }
 }
 
@@ -1976,7 +2018,8 @@ Plan make_plan(tav_dtype dtype, int B, int R, int Hq, int Hkv, int D, int max_pr
         }
         p.kps = kps;
         p.n_split = max_vis > 0 ? (max_vis + kps - 1) / kps : 1;
-        p.S = p.n_split * p.NKS + 1;   // the last slot holds the window partial
+        p.S = p.n_split + 1;   // one partial per split (the key subsets combined); the
+                               // last slot holds the window partial
     } else {
         p.mfma = false;
         p.NT = p.NRB = p.NKS = p.RG = 1;
