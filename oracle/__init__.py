@@ -75,8 +75,8 @@ def lib():
         L.orc_select_candidates.restype = ctypes.c_int
         L.orc_retrieve_links.argtypes = [P, I, I, P, P]
         L.orc_retrieve_links.restype = ctypes.c_int
-        L.orc_mla_attention.argtypes = [P, P, I, I64, I64, P, I, I, P, P, I, I, I, I, I, I, D,
-                                        P, I64, P, P]
+        L.orc_mla_attention.argtypes = [P, P, I, I, I64, I64, P, I, I, P, P, I, I, I, I, I, I,
+                                        D, P, I64, P, P]
         L.orc_mla_attention.restype = ctypes.c_int
         L.orc_tree_attention.argtypes = [P, P, P, I, I, I64, I64, I64, P, I, I, P, I,
                                          P, I, I, I, I, I, I, D, P, I64, P, P]
@@ -419,14 +419,17 @@ def mla_attention(q, latent, strides, page_table, page_size, prefix_len, masks, 
     """fp64 tree attention over an MLA latent cache.
 
     q: [B][R][Hq][Dc + Dr] float32 or uint16 (bf16 bits); latent: a flat
-    pool of the same dtype with (page, token) strides in elements, Dc + Dr
-    contiguous channels per token (latent part, then rotary part).  Returns
-    (out float64 [B][R][Hq][Dc], lse2 float64 [B][R][Hq]) or, for a rows
-    list, ([n][Dc], [n])."""
+    pool of the same dtype, or of uint8 E4M3 codes under a bf16 query (every
+    key is then scored with the query rounded to E4M3), with (page, token)
+    strides in elements, Dc + Dr contiguous channels per token (latent part,
+    then rotary part).  Returns (out float64 [B][R][Hq][Dc], lse2 float64
+    [B][R][Hq]) or, for a rows list, ([n][Dc], [n])."""
     q = np.ascontiguousarray(q)
     dt = _dtype_code(q)
     latent = np.ascontiguousarray(latent)
-    assert _dtype_code(latent) == dt and dt in (0, 1)
+    ldt = _dtype_code(latent)
+    assert dt in (0, 1) and (ldt == dt or (ldt == 2 and dt == 1)), \
+        "the latent pool is the query's dtype, or E4M3 under a bf16 query"
     B, R, Hq, Dk = q.shape
     assert Dk == Dc + Dr
     page_table = _c(page_table, np.int32)
@@ -442,7 +445,7 @@ def mla_attention(q, latent, strides, page_table, page_size, prefix_len, masks, 
         lse = np.empty((rows.size,), np.float64)
         rp, nr = rows, rows.size
     sp, st = (int(x) for x in strides)
-    _check(lib().orc_mla_attention(_p(q), _p(latent), dt, sp, st, _p(page_table),
+    _check(lib().orc_mla_attention(_p(q), _p(latent), dt, ldt, sp, st, _p(page_table),
                                    page_table.shape[1], int(page_size), _p(prefix_len),
                                    _p(masks), int(W), B, R, Hq, int(Dc), int(Dr),
                                    float(sm_scale), _p(rp), nr, _p(out), _p(lse)),

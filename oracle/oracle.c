@@ -864,30 +864,37 @@ int orc_retrieve_links(const int32_t *parents, int B, int N, int32_t *next_token
 /* ------------------------------------------------------------------ */
 
 /*
- * Tree attention over an MLA latent cache ([DTS] "One tree attention ...":
- * MLA runs the same cascade over its latent cache; a token's latent row is
- * read once, its kv_lora_rank (Dc) leading channels are both the key's
- * latent part and the value, and the rotary channels after them (Dr, zero
- * for GQA) add a second score product).  Every query head reads the one
- * latent row of a token:
+ * Tree attention over an MLA latent cache ([DTS] "One tree attention ...",
+ * the MLA paragraph).  The cascade is the one of orc_tree_attention; what
+ * changes is the key and value: each token stores one latent row, shared by
+ * every query head, whose first Dc channels (kv_lora_rank) enter the score
+ * against the query's first Dc channels and are also the value, and whose
+ * Dr rotary channels after them enter the score against the query's last Dr
+ * channels (Dr = 0: no rotary part):
  *   s_t = scale * (sum_{d < Dc} q[d] c_t[d] + sum_{d < Dr} q[Dc + d] r_t[d]),
  *   o = sum_t softmax(s)_t c_t  (Dc channels),  lse2 = base-2 log-sum-exp,
  * over the visible keys of the row: the committed prefix [0, P) and window
  * node j at logical position P + j for the set bits j < W of the row's mask
  * (the same visibility as orc_tree_attention).  The latent row of logical
  * position t is at page_table[b][t / ps] * stride_page + (t % ps) *
- * stride_token, Dc + Dr contiguous elements.  q is [B][R][Hq][Dc + Dr]
- * (dtype, bf16 or fp32, as the latent cache), out [B][R][Hq][Dc] fp64, lse2
- * [B][R][Hq]; or n_rows listed rows ((b*R + r)*Hq + h).  sm_scale <= 0
- * means 1/sqrt(Dc + Dr).
+ * stride_token, Dc + Dr contiguous elements.  q is [B][R][Hq][Dc + Dr] of
+ * dtype qdt (fp32 or bf16), the latent pool of dtype latdt: the same as q,
+ * or FP8 E4M3 under a bf16 query.  Under an E4M3 latent cache the absorbed
+ * query is an E4M3 value too (the page: the prologue returns it in FP8 and
+ * the window kernel widens it back exactly), so every key, prefix and
+ * window, is scored with q rounded to E4M3 (orc_e4m3_round).  out is
+ * [B][R][Hq][Dc] fp64, lse2 [B][R][Hq]; or n_rows listed rows ((b*R + r)*Hq
+ * + h).  sm_scale <= 0 means 1/sqrt(Dc + Dr).
  */
-int orc_mla_attention(const void *q, const void *latent, int dtype, int64_t stride_page,
-                      int64_t stride_token, const int32_t *page_table, int max_pages,
-                      int page_size, const int32_t *prefix_len, const uint64_t *masks, int W,
-                      int B, int R, int Hq, int Dc, int Dr, double sm_scale,
-                      const int64_t *rows, int64_t n_rows, double *out, double *lse2)
+int orc_mla_attention(const void *q, const void *latent, int qdt, int latdt,
+                      int64_t stride_page, int64_t stride_token, const int32_t *page_table,
+                      int max_pages, int page_size, const int32_t *prefix_len,
+                      const uint64_t *masks, int W, int B, int R, int Hq, int Dc, int Dr,
+                      double sm_scale, const int64_t *rows, int64_t n_rows, double *out,
+                      double *lse2)
 {
-    if (W < 0 || W > 64 || page_size <= 0 || Dc < 1 || Dr < 0 || (dtype != 0 && dtype != 1))
+    if (W < 0 || W > 64 || page_size <= 0 || Dc < 1 || Dr < 0 || (qdt != 0 && qdt != 1) ||
+        !(latdt == qdt || (latdt == 2 && qdt == 1)))
         return ORC_BAD;
     const int Dk = Dc + Dr;
     if (sm_scale <= 0.0)
@@ -918,8 +925,11 @@ int orc_mla_attention(const void *q, const void *latent, int dtype, int64_t stri
             int64_t page = page_table[(int64_t)b * max_pages + lp];
             kofs[nk++] = page * stride_page + (int64_t)(t % page_size) * stride_token;
         }
-        for (int d = 0; d < Dk; ++d)
-            qv[d] = orc_load(q, dtype, id * Dk + d);
+        for (int d = 0; d < Dk; ++d) {
+            qv[d] = orc_load(q, qdt, id * Dk + d);
+            if (latdt == 2)
+                qv[d] = orc_e4m3_round(qv[d]);
+        }
         double *o = out + n * Dc;
         for (int d = 0; d < Dc; ++d)
             o[d] = 0.0;
@@ -930,9 +940,9 @@ int orc_mla_attention(const void *q, const void *latent, int dtype, int64_t stri
             for (int t = 0; t < nk; ++t) {
                 double acc = 0.0;
                 for (int d = 0; d < Dc; ++d)          /* latent part */
-                    acc += qv[d] * orc_load(latent, dtype, kofs[t] + d);
+                    acc += qv[d] * orc_load(latent, latdt, kofs[t] + d);
                 for (int d = 0; d < Dr; ++d)          /* rotary part */
-                    acc += qv[Dc + d] * orc_load(latent, dtype, kofs[t] + Dc + d);
+                    acc += qv[Dc + d] * orc_load(latent, latdt, kofs[t] + Dc + d);
                 s[t] = sm_scale * acc;
                 if (s[t] > mx)
                     mx = s[t];
@@ -942,7 +952,7 @@ int orc_mla_attention(const void *q, const void *latent, int dtype, int64_t stri
                 double w = exp(s[t] - mx);
                 Z += w;
                 for (int d = 0; d < Dc; ++d)          /* the value is the latent part */
-                    o[d] += w * orc_load(latent, dtype, kofs[t] + d);
+                    o[d] += w * orc_load(latent, latdt, kofs[t] + d);
             }
             for (int d = 0; d < Dc; ++d)
                 o[d] /= Z;

@@ -1252,6 +1252,71 @@ def test_mla_matches_sdpa():
         np.testing.assert_allclose(l[b], rl.permute(1, 0).numpy(), atol=1e-12, rtol=0)
 
 
+def mla_sdpa(wl, inp, m, q):
+    """fp64 SDPA over the latent rows (key = the whole row, value = its Dc
+    leading channels), query q [B][R][Hq][Dk] float64; -> (out, lse2)."""
+    lat = inp.latent.double()
+    pt = torch.from_numpy(inp.page_table.astype(np.int64))
+    rows = lat[pt].reshape(wl.B, -1, wl.Dc + wl.Dr)            # [B][T][Dk] logical
+    T = rows.shape[1]
+    outs, lses = [], []
+    for b in range(wl.B):
+        P = int(inp.prefix_len[b])
+        dense = torch.zeros(wl.R, T, dtype=torch.bool)
+        dense[:, :P] = True
+        for r in range(wl.R):
+            for j in range(wl.W):
+                if (int(m[b, r]) >> j) & 1:
+                    dense[r, P + j] = True
+        seen = dense.any(0)[:, None]
+        k = torch.where(seen, rows[b], 0.0)
+        v = k[:, :wl.Dc]
+        qb = q[b].permute(1, 0, 2)                                 # [Hq][R][Dk]
+        ro = torch.nn.functional.scaled_dot_product_attention(
+            qb, k[None].expand(wl.Hq, -1, -1), v[None].expand(wl.Hq, -1, -1), attn_mask=dense[None])
+        sc = (qb @ k.T) / math.sqrt(wl.Dc + wl.Dr)
+        rl = torch.logsumexp(torch.where(dense[None], sc, -math.inf), -1) * LOG2E
+        outs.append(ro.permute(1, 0, 2).numpy())
+        lses.append(rl.permute(1, 0).numpy())
+    return np.stack(outs), np.stack(lses)
+
+
+def test_mla_fp8_latent_scores_every_key_with_the_e4m3_query():
+    """[DTS] "One tree attention ...": under an FP8 cache the absorbed query
+    is FP8 and the window kernel widens it back exactly.  The oracle over an
+    E4M3 latent cache equals fp64 SDPA on torch's float8_e4m3fn decoding of
+    the latent codes with torch's E4M3 cast of the query, for prefix and
+    window keys alike; keeping the bf16 query for the window keys (the GQA
+    reading) or for every key gives different results."""
+    wl, inp, m = mla_small(kv_dtype="fp8")
+    assert inp.latent.dtype == torch.float8_e4m3fn
+    o, l = mla_oracle(inp, m)
+    q8 = inp.q.to(torch.float8_e4m3fn).double()
+    ro, rl = mla_sdpa(wl, inp, m, q8)
+    np.testing.assert_allclose(o, ro, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(l, rl, atol=1e-12, rtol=0)
+    # the unrounded query is a different reading, by far more than rounding
+    ro2, rl2 = mla_sdpa(wl, inp, m, inp.q.double())
+    assert np.abs(rl2 - l).max() > 1e-3 and np.abs(ro2 - o).max() > 1e-3
+    # and the window keys do take the rounded query: the mixed reading
+    # (E4M3 query for prefix keys, bf16 query for window keys) differs on the
+    # rows that see window keys
+    lat = inp.latent.double()
+    pt = torch.from_numpy(inp.page_table.astype(np.int64))
+    rows = lat[pt].reshape(wl.B, -1, wl.Dc + wl.Dr)
+    worst = 0.0
+    for b in range(wl.B):
+        P = int(inp.prefix_len[b])
+        for r in range(wl.R):
+            vis = list(range(P)) + [P + j for j in range(wl.W) if (int(m[b, r]) >> j) & 1]
+            k = rows[b, vis]
+            for h in range(wl.Hq):
+                sc = torch.cat([k[:P] @ q8[b, r, h], k[P:] @ inp.q[b, r, h].double()])
+                sc = sc / math.sqrt(wl.Dc + wl.Dr)
+                worst = max(worst, abs(float(torch.logsumexp(sc, 0)) * LOG2E - float(l[b, r, h])))
+    assert worst > 1e-4, worst
+
+
 def test_mla_without_rotary_is_shared_kv_attention():
     """Dr = 0: the latent row is both key and value of a single kv head, so
     the result equals the plain tree attention with Hkv = 1 and D = Dc on a

@@ -504,6 +504,11 @@ class MlaWorkload:
     page_size: int
     depth_cap: int = 6
     dtype: str = "bf16"
+    kv_dtype: str = ""   # latent cache dtype when it differs from dtype: "fp8" (E4M3, bf16 q)
+
+    @property
+    def kv(self) -> str:
+        return self.kv_dtype or self.dtype
 
     @property
     def W(self) -> int:
@@ -517,9 +522,11 @@ class MlaWorkload:
         return dataclasses.replace(self, **kw)
 
     def describe(self) -> str:
+        dt = self.dtype if self.kv == self.dtype else "%s q, %s E4M3 latent cache" % (self.dtype,
+                                                                                       self.kv)
         return ("%s: B %d, P %d, N %d random trees (depth <= %d), Hq %d, latent %d + rotary %d, "
                 "%s, page size %d" % (self.name, self.B, self.P, self.N, self.depth_cap, self.Hq,
-                                      self.Dc, self.Dr, self.dtype, self.page_size))
+                                      self.Dc, self.Dr, dt, self.page_size))
 
 
 MLA_WORKLOADS = {
@@ -527,6 +534,9 @@ MLA_WORKLOADS = {
     "mla16": MlaWorkload("mla16", 8, 8192, 16, 16, 512, 64, 64),
     # every head of such a layer on one GPU
     "mla128": MlaWorkload("mla128", 4, 32768, 16, 128, 512, 64, 64),
+    # the same two over an FP8 E4M3 latent cache
+    "mla16_fp8": MlaWorkload("mla16_fp8", 8, 8192, 16, 16, 512, 64, 64, kv_dtype="fp8"),
+    "mla128_fp8": MlaWorkload("mla128_fp8", 4, 32768, 16, 128, 512, 64, 64, kv_dtype="fp8"),
 }
 
 
@@ -548,8 +558,9 @@ class MlaInputs:
 def make_mla_inputs(wl: MlaWorkload, seed: int, device="cpu",
                     prefix_lens: Optional[np.ndarray] = None) -> MlaInputs:
     """Seeded MLA verify inputs: random trees, the absorbed query and the
-    latent cache N(0, 1) (rounded to bf16), a shuffled page table; page 0 and
-    every slot past prefix + window hold NaN."""
+    latent cache N(0, 1) (rounded to bf16, the latent cache to E4M3 under
+    kv_dtype "fp8"), a shuffled page table; page 0 and every slot past
+    prefix + window hold NaN."""
     r_tree, _, r_pt, _ = _streams(seed + 7777, 4)
     B, N = wl.B, wl.N
     parents = np.stack([random_tree(r_tree, N, wl.depth_cap) for _ in range(B)]).astype(np.int32)
@@ -564,7 +575,7 @@ def make_mla_inputs(wl: MlaWorkload, seed: int, device="cpu",
     dev = torch.device(device)
     Dk = wl.Dc + wl.Dr
     q = torch.empty((B, N, wl.Hq, Dk), dtype=dt, device=dev)
-    lat = torch.empty((n_pages, ps, Dk), dtype=dt, device=dev)
+    lat = torch.empty((n_pages, ps, Dk), dtype=TORCH_DTYPE[wl.kv], device=dev)
     for k, t in enumerate((q, lat)):
         g = torch.Generator(device=dev)
         g.manual_seed(_torch_seed(seed + 7777, k))
