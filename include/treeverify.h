@@ -420,23 +420,29 @@ tav_status verify_tree_rejection(const float *probs, int64_t row_stride, int32_t
                                  size_t workspace_bytes, void *stream);
 
 /*
- * The same cascade over an MLA latent cache ([DTS] "One tree attention ...":
- * MLA runs the cascade over its latent cache; a token's latent row is read
- * once, its kv_lora_rank (Dc) leading channels are both the key's latent
- * part and the value, and the rotary channels after them (Dr; 0 when there
- * are none) add a second score product).  Every query head reads the one
- * latent row of a token; visibility as tree_attention (the whole prefix,
- * plus window node j at logical position P + j for the set bits j < W of
- * the row's mask).
+ * The same cascade over an MLA latent cache ([DTS] "One tree attention ...",
+ * the MLA paragraph).  Each token stores one latent row, shared by every
+ * query head: its first Dc channels (kv_lora_rank) meet the query's first Dc
+ * channels in the score and are also the value; its Dr rotary channels
+ * after them meet the query's last Dr channels (Dr = 0: no rotary part).
+ * Visibility as tree_attention (the whole prefix, plus window node j at
+ * logical position P + j for the set bits j < W of the row's mask).
  *   s_t = sm_scale * (q[:Dc] . c_t + q[Dc:] . r_t),  out = softmax(s) . c,
  *   lse2 = log2 sum_t exp(s_t)
  * q          [B][R][Hq][Dc + Dr] bf16 (the absorbed query)
  * latent     paged pool: the row of logical position t is at element
  *            page_table[b][t / page_size] * stride_page + (t % page_size) *
- *            stride_token, Dc + Dr contiguous bf16 (latent part, then the
- *            rotary part); strides in elements, rows 16-byte aligned
+ *            stride_token, Dc + Dr contiguous elements of type dtype
+ *            (latent part, then the rotary part); strides in elements,
+ *            rows 16-byte aligned
+ * dtype      TAV_BF16, or TAV_FP8_E4M3 for a cache of unscaled OCP E4M3
+ *            codes: the page hands the absorbed query over in FP8 under an
+ *            FP8 cache and the window kernel widens it back exactly, so
+ *            every key, prefix and window, is scored with q rounded to the
+ *            nearest E4M3 value (ties to even, +-448 saturation); products
+ *            are then exact, sums fp32, and the value is the widened latent
  * page_table, prefix_len, max_prefix_len, masks, W, B, R as tree_attention
- * Dc == 512; Dr in {0, 64}; dtype TAV_BF16; page_size a power of two <= 1024
+ * Dc == 512; Dr in {0, 64}; page_size a power of two <= 1024
  * sm_scale   <= 0 selects 1/sqrt(Dc + Dr)
  * out        [B][R][Hq][Dc] bf16 (round to nearest even); lse2 float
  *            [B][R][Hq] or NULL

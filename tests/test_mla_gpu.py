@@ -1,5 +1,6 @@
 """GPU parity of the MLA latent-cache cascade through the C ABI against the
-CPU fp64 oracle: out max |err| <= 1e-2, lse2 <= 1e-3 on bf16 inputs.
+CPU fp64 oracle: out max |err| <= 1e-2, lse2 <= 1e-3, with bf16 latent
+caches and with FP8 E4M3 ones (the query rounded to E4M3 for every key).
 Reduced sizes check every row (several row groups, split counts and ragged
 prefixes); the full MLA workloads, in the benchmark's launch, check sampled
 rows and that every output is finite (unseen slots hold NaN)."""
@@ -74,14 +75,17 @@ SMALL = {
 }
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
 @pytest.mark.parametrize("name", sorted(SMALL))
-def test_mla_parity_every_row(name):
+def test_mla_parity_every_row(name, kv):
     wl, pl = SMALL[name]
+    if kv == "fp8":
+        wl = wl.with_(kv_dtype="fp8")
     say("case", name, wl)
     inp = gen.make_mla_inputs(wl, 21, "cuda", prefix_lens=np.array(pl))
     m = oracle.build_masks(inp.parents)["masks"]
     out, lse = run(inp, m)
-    check(inp, m, out, lse, tag=name)
+    check(inp, m, out, lse, tag=name + " " + kv)
 
 
 @pytest.mark.parametrize("name", sorted(gen.MLA_WORKLOADS))
@@ -96,12 +100,14 @@ def test_mla_full_size_sampled_rows(name):
     check(inp, m, out, lse, rows=rows, tag=name)
 
 
-def test_mla_late_dominant_key_repeats_the_pass():
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_mla_late_dominant_key_repeats_the_pass(kv):
     # Every head's query is all ones and one late prefix key holds 3.0 in
-    # every channel: its score passes the first block's row max by far more
-    # than 64 (log2 units), so each split holding it is computed again with
-    # the exact row max as the reference; the result is still the oracle's.
-    wl = gen.MlaWorkload("m", 2, 2000, 8, 16, 512, 64, 64)
+    # every channel (both exact in E4M3): its score passes the first block's
+    # row max by far more than 64 (log2 units), so each split holding it is
+    # computed again with the exact row max as the reference; the result is
+    # still the oracle's.
+    wl = gen.MlaWorkload("m", 2, 2000, 8, 16, 512, 64, 64, kv_dtype="" if kv == "bf16" else kv)
     inp = gen.make_mla_inputs(wl, 31, "cuda", prefix_lens=np.array([2000, 1500]))
     inp.q.fill_(1.0)
     for b, t in ((0, 1900), (1, 700)):

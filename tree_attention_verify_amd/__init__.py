@@ -429,7 +429,8 @@ def tree_attention_mla(q: torch.Tensor, latent: torch.Tensor, page_table: torch.
                        max_prefix_len: int, sm_scale: float = 0.0,
                        workspace: Optional[torch.Tensor] = None):
     """Tree attention over an MLA latent cache.  q bf16 [B][R][Hq][Dc + Dr];
-    latent bf16 [pages][page_size][Dc + Dr]; page_table int32 [B][max_pages];
+    latent bf16 or float8_e4m3fn [pages][page_size][Dc + Dr] (under an E4M3
+    cache every key is scored with q rounded to E4M3); page_table int32 [B][max_pages];
     prefix_len int32 [B]; masks int64 (uint64 bits) [B][R].  max_prefix_len
     (a host int >= every prefix_len) sizes the workspace and the split plan;
     it is required, as for tree_attention, so the call never reads the device.
@@ -438,7 +439,12 @@ def tree_attention_mla(q: torch.Tensor, latent: torch.Tensor, page_table: torch.
     B, R, Hq, Dk = q.shape
     Dr = Dk - Dc
     dev = q.device
-    _need(latent, "latent", torch.bfloat16, dev)
+    if latent.dtype == torch.float8_e4m3fn:
+        _need(latent, "latent", torch.float8_e4m3fn, dev)
+        lat_code = TAV_FP8_E4M3
+    else:
+        _need(latent, "latent", torch.bfloat16, dev)
+        lat_code = TAV_BF16
     if latent.dim() != 3 or latent.shape[2] != Dk:
         raise ValueError("latent must be [pages][page_size][Dc + Dr]")
     pages, ps = latent.shape[0], latent.shape[1]
@@ -450,7 +456,7 @@ def tree_attention_mla(q: torch.Tensor, latent: torch.Tensor, page_table: torch.
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     out = torch.empty((B, R, Hq, Dc), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, R, Hq), dtype=torch.float32, device=dev)
-    _check(lib().tree_attention_mla(_ptr(q), _ptr(latent), TAV_BF16, ps * Dk, Dk, pages,
+    _check(lib().tree_attention_mla(_ptr(q), _ptr(latent), lat_code, ps * Dk, Dk, pages,
                                     _ptr(page_table), page_table.shape[1], ps, _ptr(prefix_len),
                                     int(max_prefix_len), _ptr(masks), int(W), B, R, Hq, Dc, Dr,
                                     float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),

@@ -1,12 +1,15 @@
 // tree_attention_mla: the verify cascade over an MLA latent cache, for gfx950.
 //
-// "Draft-tree speculation", section "One tree attention ...": MLA runs the
-// same cascade over its latent cache.  A token's latent row is read once:
-// its kv_lora_rank (Dc) leading channels are both the key's latent part and
-// the value, and the rotary channels after them (Dr) add a second score
-// product.  Every query head reads the one latent row, so all R x Hq query
-// rows of a request are folded into the MFMA N dimension against one K/V
-// stream.
+// "Draft-tree speculation", section "One tree attention ...", the MLA
+// paragraph: the cascade is unchanged, only the key and value differ.  Each
+// token keeps one latent row shared by all query heads: its first Dc
+// channels score against the query's first Dc channels and are also the
+// value, and its Dr rotary channels add a second dot product to the score.
+// All R x Hq query rows of a request are therefore folded into the MFMA N
+// dimension against one stream of latent rows, each read once.  Under an
+// FP8 E4M3 latent cache the query is rounded to E4M3 for every key (the
+// page's window kernel receives the FP8 query) and the rows are widened to
+// bf16 exactly.
 //
 // Kernels:
 //   k_mla_prefix<DR>  split-K prefix decode.  One workgroup of 8 waves (two
@@ -19,6 +22,8 @@
 //       (16 MFMAs).  Every score is computed once.  Latent rows stream HBM ->
 //       LDS with direct-to-LDS 16-byte loads, four stages deep; the same LDS
 //       bytes are read as the K operand and, transposed, as the V operand.
+//       FP8 rows land raw in the upper half of their stage buffer and are
+//       widened in place into the bf16 layout once the stage has landed.
 //   k_mla_window_merge<DR>  one wave per (request, row, head): the masked
 //       window keys (never the unseen ones) with lanes over channels, then
 //       the merge of the prefix partials through their base-2 LSE.
@@ -90,6 +95,47 @@ __device__ inline float mla_quad_sum(float x) {
     return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// FP8 E4M3 latent caches.  Every E4M3 value (NaN included) is a bf16 value,
+// so widening is exact: a 16-byte chunk of 16 codes becomes two bf16 chunks.
+__device__ __forceinline__ void mla_fp8x16_to_bf16(const int4 x, int4 &lo, int4 &hi) {
+    auto c0 = [](int w) {
+        return __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w, 1.0f, false));
+    };
+    auto c1 = [](int w) {
+        return __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w, 1.0f, true));
+    };
+    lo = make_int4(c0(x.x), c1(x.x), c0(x.y), c1(x.y));
+    hi = make_int4(c0(x.z), c1(x.z), c0(x.w), c1(x.w));
+}
+
+// x rounded to the nearest E4M3 value (ties to even) as fp32; magnitudes past
+// 448 give +-448, NaN stays NaN.  Above the subnormal range an E4M3 value has
+// 4 significant bits (quantum 2^(e - 3) at binary exponent e), below 2^-6 the
+// quantum is 2^-9; the scalings are exact and rint rounds ties to even.
+__device__ inline float mla_round_e4m3(float x) {
+    if (!(fabsf(x) <= 448.f))
+        return x != x ? x : copysignf(448.f, x);
+    const float a = fabsf(x);
+    int e = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;
+    e = e < -6 ? -6 : e;
+    const float up = __uint_as_float((uint32_t)(3 - e + 127) << 23);
+    const float dn = __uint_as_float((uint32_t)(e - 3 + 127) << 23);
+    return copysignf(__builtin_rintf(a * up) * dn, x);
+}
+
+// eight bf16 values (raw bits in an int4) rounded to E4M3, held as bf16
+// (exact: every E4M3 value is a bf16 value)
+__device__ inline int4 mla_bf16x8_round_e4m3(int4 v) {
+    uint32_t u[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float lo = mla_round_e4m3(__uint_as_float(u[e] << 16));
+        const float hi = mla_round_e4m3(__uint_as_float(u[e] & 0xffff0000u));
+        u[e] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+    }
+    return make_int4((int)u[0], (int)u[1], (int)u[2], (int)u[3]);
+}
+
 struct MlaArgs {
     const uint16_t *q;
     const uint16_t *lat;
@@ -120,14 +166,26 @@ struct MlaCfg {
     static constexpr int LA = (NG + 1) / 2;        // loads per stage of waves 0..3
     static constexpr int LB = NG - LA;             // and of waves 4..7
     static constexpr int PB = 64 * SK * 2;         // bf16 weights of a block: 64 rows x 32 keys
+    // FP8 E4M3 rows (DK bytes): raw stages of SK rows land in a ring of two
+    // slots in the space of the fourth stage buffer (the bf16 stages then
+    // ring over three), 64 16-byte chunks per load instruction; wave w takes
+    // instructions w, w + 8, w + 16
+    static constexpr int CH8 = DK / 16;            // 16-byte chunks per FP8 row
+    static constexpr int NCH8 = SK * CH8;          // chunks per raw stage
+    static constexpr int NL8 = NCH8 / 64;          // load instructions per raw stage
+    static constexpr int L8MAX = (NL8 + 7) / 8;    // per wave, at most
+    static constexpr int NB8 = 3;                  // bf16 stage buffers under FP8 rows
+    static constexpr int RAW8 = NB8 * SB;          // byte offset of the raw ring
     static_assert(DK % 64 == 0 && LOADS == 4 * NG && KS >= 2 * LA, "row shape");
+    static_assert(NCH8 % 64 == 0 && 2 * SK * DK <= SB && L8MAX <= 3 && KS >= 2 * L8MAX, "fp8 rows");
     static_assert(NBUF * SB + 2 * PB + kMlaPt * 4 + 3 * 2 * 64 * 4 <= 160 * 1024, "LDS");
 };
 
-template <int DR>
+template <int DR, bool KV8>
 __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
     using C = MlaCfg<DR>;
     constexpr int DK = C::DK, KS = C::KS, SK = C::SK, SB = C::SB, NBUF = C::NBUF, LA = C::LA, LB = C::LB;
+    constexpr int NB = KV8 ? C::NB8 : NBUF;   // stage buffers the bf16 stages ring over
     __shared__ __attribute__((aligned(16))) char lds[NBUF * SB];
     __shared__ __attribute__((aligned(16))) char pbuf[2 * C::PB];   // weights of blocks u, u + 1
     __shared__ int32_t pt[kMlaPt];
@@ -170,7 +228,9 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
         reinterpret_cast<int4 *>(lds)[i] = make_int4(0, 0, 0, 0);
 
     // Q^T operand of score step s: lane (g, i16) holds Q[row 16 rt + i16 of
-    // the group][32 s + 8 g .. +8]
+    // the group][32 s + 8 g .. +8]; under an FP8 latent cache the query is
+    // rounded to E4M3 (held as bf16), so every product with a widened E4M3
+    // channel is exact
     const int m = rg * 64 + rt * 16 + i16;
     const bool row_ok = m < a.M;
     bf16x8 qv[KS];
@@ -179,7 +239,9 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
         const uint16_t *qp = a.q + (((int64_t)b * a.R + r) * a.Hq + hh) * DK + 8 * g;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            const int4 v4 = row_ok ? *(const int4 *)(qp + 32 * s) : make_int4(0, 0, 0, 0);
+            int4 v4 = row_ok ? *(const int4 *)(qp + 32 * s) : make_int4(0, 0, 0, 0);
+            if constexpr (KV8)
+                v4 = mla_bf16x8_round_e4m3(v4);
             qv[s] = __builtin_bit_cast(bf16x8, v4);
         }
 #pragma unroll
@@ -219,11 +281,100 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
         if (j < nld && r.on)
             mla_dma16(r.src + 64 * j, __builtin_amdgcn_readfirstlane(r.sbase + (uint32_t)(j * SK * 128)));
     };
-    auto issue = [&](int st) {
-        const Loads r = loads_of(st);
-#pragma unroll
-        for (int j = 0; j < LA; ++j)
+    // FP8 rows: instruction x = w + 8 j (j < nld8) of a stage loads raw
+    // chunks 64 x .. 64 x + 63 (chunk q: key q / CH8, 16-byte chunk q % CH8
+    // of its row) to the raw stage, lane i at byte 16 (64 x + i); each lane
+    // looks up the page of its own key.
+    struct Loads8 {
+        int st;
+        uint32_t sbase;
+    };
+    const int nld8 = (C::NL8 - w + 7) / 8;
+    auto loads_of8 = [&](int st) {
+        Loads8 r;
+        r.st = st;
+        r.sbase = lds0 + (uint32_t)(C::RAW8 + (st & 1) * SK * DK);
+        return r;
+    };
+    // (the address is formed at issue time, and FP8 stages are issued
+    // outside the score steps, whose operands fill the registers)
+    // (the lane's chunk offsets are recomputed at every use: hoisted out of
+    // the loop they would hold a dozen registers)
+    auto opaque_lane = [&]() {
+        int l = lane;
+        mla_settle(l);
+        return l;
+    };
+    auto load_one8 = [&](const Loads8 &r, int j) {
+        if (j >= nld8)
+            return;
+        const int q = 64 * (w + 8 * j) + opaque_lane();
+        const int k = q / C::CH8, c = q - k * C::CH8;
+        const int t = lo + r.st * SK + k;
+        if (r.st < ns && t < hi) {
+            const int64_t pg = pt[(t >> a.ps_shift) - lp0];
+            mla_dma16((const uint8_t *)a.lat + pg * a.stride_page +
+                          (int64_t)(t & ps_mask) * a.stride_token + 16 * c,
+                      __builtin_amdgcn_readfirstlane(r.sbase + (uint32_t)((w + 8 * j) * 1024)));
+        }
+    };
+    using LoadsT = typename std::conditional<KV8, Loads8, Loads>::type;
+    constexpr int LMAX = KV8 ? C::L8MAX : LA;   // load instructions per stage of a wave, at most
+    auto loads_for = [&](int st) {
+        if constexpr (KV8)
+            return loads_of8(st);
+        else
+            return loads_of(st);
+    };
+    auto ld_one = [&](const LoadsT &r, int j) {
+        if constexpr (KV8)
+            load_one8(r, j);
+        else
             load_one(r, j);
+    };
+    auto issue = [&](int st) {
+        const LoadsT r = loads_for(st);
+#pragma unroll
+        for (int j = 0; j < LMAX; ++j)
+            ld_one(r, j);
+    };
+    // Stage st's raw FP8 rows widened into the bf16 layout of its stage
+    // buffer: each thread takes the chunks it loaded itself, once its own
+    // loads have landed, so no barrier is needed before; the barrier at the
+    // top of the next trip publishes the stage.  Keys past the split end (not
+    // loaded) become zeros.
+    auto convert8 = [&](int st) {
+        const char *raw = lds + C::RAW8 + (st & 1) * SK * DK;
+        char *buf = lds + (st % NB) * SB;
+#pragma unroll
+        for (int j = 0; j < C::L8MAX; ++j) {
+            if (j >= nld8)
+                break;
+            const int q = 64 * (w + 8 * j) + opaque_lane();
+            const int k = q / C::CH8, c = q - k * C::CH8;
+            int4 h[2];
+            mla_fp8x16_to_bf16(*(const int4 *)(raw + 16 * q), h[0], h[1]);
+            if (lo + st * SK + k >= hi)
+                h[0] = h[1] = make_int4(0, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int cc = 2 * c + e;   // bf16 chunk of the row
+                *(int4 *)(buf + (cc >> 3) * (SK * 128) + (k >> 3) * 1024 + (k & 7) * 128 +
+                          (((cc & 7) ^ (k & 7)) * 16)) = h[e];
+            }
+        }
+    };
+    // Wait for this wave's loads of a raw stage.  next_full: the stage after
+    // it is issued and full (not the last stage, whose keys past the split
+    // end issue no loads), so exactly its nld8 loads may still be in flight;
+    // otherwise wait for everything.
+    auto wait8 = [&](bool next_full) {
+        if (!next_full)
+            mla_wait_vmcnt<0>();
+        else if (nld8 == C::L8MAX)
+            mla_wait_vmcnt<C::L8MAX>();
+        else
+            mla_wait_vmcnt<C::L8MAX - 1>();
     };
 
     // K operand of step s (score role): lane (g, i16) reads key 16 kt + i16,
@@ -273,14 +424,14 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
     // block pst (weights in buffer pb) for this wave's 64 channels and all 64
     // rows: its operands are read first and its 16 MFMAs sit between the
     // score steps, which they do not depend on.
-    auto score = [&](int st, const Loads *ld, bool with_pv, int pst, int pb) {
-        const char *kb = lds + (st % NBUF) * SB + koff;
-        const char *kb1 = lds + (st % NBUF) * SB + (koff ^ 64u);
+    auto score = [&](int st, const LoadsT *ld, bool with_pv, int pst, int pb) {
+        const char *kb = lds + (st % NB) * SB + koff;
+        const char *kb1 = lds + (st % NB) * SB + (koff ^ 64u);
         auto kread = [&](int s) { return *(const bf16x8 *)((s & 1 ? kb1 : kb) + (s >> 1) * (SK * 128)); };
         // P^T and V^T operands of block pst, read before the score steps
         bf16x8 pr[4], vr[4];
         if (with_pv) {
-            const uint32_t vb = (uint32_t)(uintptr_t)(const MLA_LDS void *)(lds + (pst % NBUF) * SB);
+            const uint32_t vb = (uint32_t)(uintptr_t)(const MLA_LDS void *)(lds + (pst % NB) * SB);
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4)
                 pr[t4] = *(const bf16x8 *)(pbuf + pb * C::PB + t4 * 1024 + pr_off);
@@ -311,8 +462,8 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
                     k1 = kread(s + 5);
             }
             pv_step(s / 4, 1);
-            if (ld && s / 2 < LA)
-                load_one(*ld, s / 2);
+            if (ld && s / 2 < LMAX)
+                ld_one(*ld, s / 2);
             if (s + 2 < KS) {
                 sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k2, qv[s + 2], sc, 0, 0, 0);
                 if (s + 6 < KS)
@@ -325,8 +476,8 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
                     k3 = kread(s + 7);
             }
             pv_step(s / 4, 3);
-            if (ld && s / 2 + 1 < LA)
-                load_one(*ld, s / 2 + 1);
+            if (ld && s / 2 + 1 < LMAX)
+                ld_one(*ld, s / 2 + 1);
         }
         sc += sd;
         const int lim = hi - (lo + st * SK) - 16 * kt - 4 * g;
@@ -405,10 +556,26 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
             for (int t4 = 0; t4 < 4; ++t4)
                 o[ct][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
         l_part = 0.f;
-        for (int st = 0; st < NBUF - 1 && st < ns; ++st)
-            issue(st);
+        if constexpr (KV8) {
+            // raw stages 0 and 1, widened into bf16 stages 0 and 1 as they
+            // land, each slot refilled at once (stages 2 and 3)
+            issue(0);
+            issue(1);
+            wait8(1 < ns - 1);
+            if (ns > 0)
+                convert8(0);
+            issue(2);
+            wait8(2 < ns - 1);
+            if (1 < ns)
+                convert8(1);
+            issue(3);
+        } else {
+            for (int st = 0; st < NBUF - 1 && st < ns; ++st)
+                issue(st);
+        }
         if (ns > 0) {
-            wait_stage(0, ns - 1 < 2 ? ns - 1 : 2);
+            if constexpr (!KV8)
+                wait_stage(0, ns - 1 < 2 ? ns - 1 : 2);
             __syncthreads();
             const f32x4 sc = score(0, nullptr, false, 0, 0);
             float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * a.c;
@@ -422,12 +589,27 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
             weights(sc, 0, true);
         }
         for (int u = 0; u < ns; ++u) {
-            if (u + 1 < ns)
-                wait_stage(u + 1, u + 2 < ns ? 1 : 0);
+            if constexpr (!KV8) {
+                if (u + 1 < ns)
+                    wait_stage(u + 1, u + 2 < ns ? 1 : 0);
+            }
             __syncthreads();
             const bool more = u + 1 < ns;
-            const Loads ld = loads_of(u + NBUF - 1);
-            const f32x4 sc = score(more ? u + 1 : u, &ld, true, u, u & 1);
+            const LoadsT ld = loads_for(u + NBUF - 1);
+            if constexpr (KV8) {
+                // stage u + 2 is widened into the buffer of block u - 1 (free
+                // since the barrier) as this wave's loads of it land, and its
+                // raw slot is refilled with stage u + 4; the next trip's
+                // barrier publishes it
+                wait8(u + 3 < ns - 1);
+                if (u + 2 < ns)
+                    convert8(u + 2);
+                issue(u + 4);
+                // (kept apart from the score steps, whose operands fill the
+                // registers)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const f32x4 sc = score(more ? u + 1 : u, KV8 ? nullptr : &ld, true, u, u & 1);
             const float mx = mla_quad_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * a.c);
             seen = fmaxf(seen, mx);
             weights(sc, (u + 1) & 1, more);
@@ -487,7 +669,7 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
 // over the groups.  Then the merge with the n_split prefix partials (their
 // lse2 read at once, one per lane): lse2 = log2 sum_k 2^lse2_k, out = sum_k
 // 2^(lse2_k - lse2) o_k.
-template <int DR>
+template <int DR, bool KV8>
 __global__ void __launch_bounds__(256) k_mla_window_merge(MlaArgs a) {
     constexpr int DK = 512 + DR;
     const int lane = threadIdx.x & 63;
@@ -508,9 +690,25 @@ __global__ void __launch_bounds__(256) k_mla_window_merge(MlaArgs a) {
     };
     const uint16_t *qp = a.q + row * DK;
     // the query stays packed (bf16) and is widened per key: fewer registers,
-    // more waves in flight
-    const int4 qcp = *(const int4 *)(qp + 8 * lane);
-    const int4 qrp = DR > 0 && lane < DR / 8 ? *(const int4 *)(qp + 512 + 8 * lane) : make_int4(0, 0, 0, 0);
+    // more waves in flight.  Under an FP8 latent cache it is the E4M3 query
+    // (rounded, held as bf16) for window keys too.
+    int4 qcp = *(const int4 *)(qp + 8 * lane);
+    int4 qrp = DR > 0 && lane < DR / 8 ? *(const int4 *)(qp + 512 + 8 * lane) : make_int4(0, 0, 0, 0);
+    if constexpr (KV8) {
+        qcp = mla_bf16x8_round_e4m3(qcp);
+        qrp = mla_bf16x8_round_e4m3(qrp);
+    }
+    // a latent row's 8 channels of this lane as packed bf16 (FP8 rows widened)
+    auto load8 = [&](int64_t ro, int ch) {
+        if constexpr (KV8) {
+            const int2 x = *(const int2 *)((const uint8_t *)a.lat + ro + ch);
+            int4 lo, hi;
+            mla_fp8x16_to_bf16(make_int4(x.x, x.y, 0, 0), lo, hi);
+            return lo;
+        } else {
+            return *(const int4 *)(a.lat + ro + ch);
+        }
+    };
 
     uint64_t bits = a.masks[(int64_t)b * a.R + r];
     if (a.W < 64)
@@ -553,10 +751,9 @@ __global__ void __launch_bounds__(256) k_mla_window_merge(MlaArgs a) {
             if (js[i] >= 0) {
                 const int64_t ro = ((int64_t)__builtin_amdgcn_readlane((int)(myrow >> 32), js[i]) << 32) |
                                    (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)myrow, js[i]);
-                const uint16_t *kr = a.lat + ro;
-                xk[i] = *(const int4 *)(kr + 8 * lane);
+                xk[i] = load8(ro, 8 * lane);
                 if (DR > 0 && lane < DR / 8)
-                    xr[i] = *(const int4 *)(kr + 512 + 8 * lane);
+                    xr[i] = load8(ro, 512 + 8 * lane);
             }
         }
         float sj[GK];
@@ -772,14 +969,17 @@ extern "C" tav_status tree_attention_mla(const void *q, const void *latent, tav_
     c.need(Hq >= 1, TAV_ERR_INVALID_ARG, "Hq must be >= 1, got " + str(Hq));
     c.need(Dc == 512, TAV_ERR_UNSUPPORTED, "Dc (kv_lora_rank) must be 512, got " + str(Dc));
     c.need(Dr == 0 || Dr == 64, TAV_ERR_UNSUPPORTED, "Dr must be 0 or 64, got " + str(Dr));
-    c.need(dtype == TAV_BF16, TAV_ERR_UNSUPPORTED, "the MLA path takes TAV_BF16, got " + str(dtype));
+    c.need(dtype == TAV_BF16 || dtype == TAV_FP8_E4M3, TAV_ERR_UNSUPPORTED,
+           "the latent cache must be TAV_BF16 or TAV_FP8_E4M3 (bf16 query), got " + str(dtype));
+    const int64_t elem = dtype == TAV_FP8_E4M3 ? 1 : 2;
     c.need(tav::is_pow2(page_size) && page_size <= 1024, TAV_ERR_UNSUPPORTED,
            "page_size must be a power of two <= 1024, got " + str(page_size));
     c.need(max_prefix_len >= 0, TAV_ERR_INVALID_ARG, "max_prefix_len must be >= 0");
     c.need(max_pages >= 1 && (long long)max_pages * page_size >= (long long)max_prefix_len + W,
            TAV_ERR_INVALID_ARG, "max_pages * page_size must cover max_prefix_len + W");
     c.need(num_pages >= 1, TAV_ERR_INVALID_ARG, "num_pages must be >= 1");
-    c.need(stride_token >= Dc + Dr && (stride_token * 2) % 16 == 0 && (stride_page * 2) % 16 == 0,
+    c.need(stride_token >= Dc + Dr && (stride_token * elem) % 16 == 0 &&
+               (stride_page * elem) % 16 == 0,
            TAV_ERR_UNSUPPORTED,
            "latent rows must hold Dc + Dr contiguous elements at 16-byte aligned strides");
     c.need(std::isfinite(sm_scale), TAV_ERR_INVALID_ARG, "sm_scale must be finite");
@@ -802,7 +1002,7 @@ extern "C" tav_status tree_attention_mla(const void *q, const void *latent, tav_
     const MlaPlan p = mla_plan(B, R, Hq, max_prefix_len, page_size);
     MlaArgs a{};
     a.q = (const uint16_t *)q;
-    a.lat = (const uint16_t *)latent;
+    a.lat = (const uint16_t *)latent;   // byte addressed under an FP8 cache
     a.stride_page = stride_page;
     a.stride_token = stride_token;
     a.num_pages = num_pages;
@@ -829,10 +1029,15 @@ extern "C" tav_status tree_attention_mla(const void *q, const void *latent, tav_
     if (max_prefix_len > 0) {
         const long long streams = (long long)B * p.n_split;
         const unsigned grid = (unsigned)(((streams + 7) / 8) * 8 * p.RG);
-        if (Dr == 64)
-            hipLaunchKernelGGL(k_mla_prefix<64>, dim3(grid), dim3(512), 0, MS(stream), a);
+        const bool kv8 = dtype == TAV_FP8_E4M3;
+        if (Dr == 64 && kv8)
+            hipLaunchKernelGGL((k_mla_prefix<64, true>), dim3(grid), dim3(512), 0, MS(stream), a);
+        else if (Dr == 64)
+            hipLaunchKernelGGL((k_mla_prefix<64, false>), dim3(grid), dim3(512), 0, MS(stream), a);
+        else if (kv8)
+            hipLaunchKernelGGL((k_mla_prefix<0, true>), dim3(grid), dim3(512), 0, MS(stream), a);
         else
-            hipLaunchKernelGGL(k_mla_prefix<0>, dim3(grid), dim3(512), 0, MS(stream), a);
+            hipLaunchKernelGGL((k_mla_prefix<0, false>), dim3(grid), dim3(512), 0, MS(stream), a);
         tav_status st = tav::launched("tree_attention_mla");
         if (st != TAV_OK)
             return st;
@@ -840,11 +1045,14 @@ extern "C" tav_status tree_attention_mla(const void *q, const void *latent, tav_
         a.n_split = 0;
     }
     const long long rows = (long long)B * R * Hq;
-    if (Dr == 64)
-        hipLaunchKernelGGL(k_mla_window_merge<64>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
-                           MS(stream), a);
+    const dim3 wgrid((unsigned)((rows + 3) / 4));
+    if (Dr == 64 && dtype == TAV_FP8_E4M3)
+        hipLaunchKernelGGL((k_mla_window_merge<64, true>), wgrid, dim3(256), 0, MS(stream), a);
+    else if (Dr == 64)
+        hipLaunchKernelGGL((k_mla_window_merge<64, false>), wgrid, dim3(256), 0, MS(stream), a);
+    else if (dtype == TAV_FP8_E4M3)
+        hipLaunchKernelGGL((k_mla_window_merge<0, true>), wgrid, dim3(256), 0, MS(stream), a);
     else
-        hipLaunchKernelGGL(k_mla_window_merge<0>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
-                           MS(stream), a);
+        hipLaunchKernelGGL((k_mla_window_merge<0, false>), wgrid, dim3(256), 0, MS(stream), a);
     return tav::launched("tree_attention_mla");
 }
