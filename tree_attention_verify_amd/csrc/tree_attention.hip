@@ -2,24 +2,32 @@
 // LSE merge, for gfx950 (CDNA4).
 //
 // The cascade follows "Draft-tree speculation", section "One tree attention:
-// the leaf's decode for the prefix, a small kernel for the tree" (every row
-// sees the committed prefix; the 64-bit ancestor mask applies only to the
-// last W keys; the two parts are merged through their base-2 log-sum-exp)
-// and the FlashAttention cascade of "EAGLE Tree Attention candidate layout,
-// positions and visibility", section 4 (common prefix for all queries, a
-// per-query ancestor suffix, and the merge O = sum Z_k O_k / sum Z_k).
+// the leaf's decode for the prefix, a small kernel for the tree": a query
+// row attends to all of the committed prefix, its uint64 ancestor mask only
+// chooses among the W window keys, and the two partial results are combined
+// by their base-2 log-sum-exp.  "EAGLE Tree Attention candidate layout,
+// positions and visibility", section 4, describes the same split: a prefix
+// shared by every query, a suffix filtered per query, and a merge that
+// weights each part's normalised output by its softmax mass.
 //
 // Kernels:
-//   k_prefix_mfma<D, NT, NKS>  bf16.  One workgroup (4 waves) per (request,
-//       kv head, row group, split).  All R x (Hq/Hkv) query rows of a kv head
-//       are folded into the MFMA N dimension, so one pass over a K/V page
-//       serves every row and head of the group.  Pages stream HBM -> LDS with
-//       direct-to-LDS 16-byte loads, NBUF stages deep; S^T = K Q^T and
-//       O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation;
-//       softmax is online in the exp2 domain.  Writes one (O, lse2) partial
-//       per split and key subset.
+//   k_prefix_mfma<D, NRB, NKS, KV8>  bf16 (or FP8 E4M3 K/V).  One workgroup of
+//       NRB x NKS waves per (request, kv head, row group, split).  All R x
+//       (Hq/Hkv) query rows of a kv head are folded into the MFMA N
+//       dimension, so one pass over a K/V page serves every row and head of
+//       the group.  Pages stream HBM -> LDS with direct-to-LDS 16-byte loads,
+//       NBUF stages deep; S^T = K Q^T and O^T = V^T P^T run on
+//       v_mfma_f32_32x32x16_bf16 with fp32 accumulation; softmax is online in
+//       the exp2 domain.  Writes one (O, lse2) partial per split (its NKS key
+//       subsets combined in LDS).
+//   k_prefix_mfma_pipe  the software-pipelined kernel for 256 folded rows.
 //   k_prefix_f32<D>  fp32 inputs, vector ALU, one wave per (row, split).
-//   k_window_merge   one wave per (request, row, head): the masked window
+//   k_window_mfma  bf16: one tile of window keys per kv head serves all its
+//       rows on MFMA, the masks applied in-kernel; writes the window partial
+//       (or, with a single prefix partial, merges the row itself).
+//   k_merge  bf16: one wave per (request, row, head) merges every partial
+//       through its base-2 LSE into out / lse2.
+//   k_window_merge  fp32: one wave per (request, row, head): the masked window
 //       keys (popcount(mask) of them, never the unseen ones) and the merge of
 //       every prefix partial with the window part into out / lse2.
 #include <cmath>
