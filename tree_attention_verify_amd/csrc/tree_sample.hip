@@ -2,8 +2,8 @@
 //   - Gumbel-max target draws of every verify row, keyed by (request seed,
 //     the position the node predicts), walked by verify_tree_greedy;
 //   - tree rejection sampling of the draft tokens against the target rows
-//     (k_verify_rejection, and k_verify_rejection_q against the draft
-//     distribution that drew each node's children), further below.
+//     (k_verify_rejection<false>, and k_verify_rejection<true> against the
+//     draft distribution that drew each node's children), further below.
 //
 // "Draft-tree speculation", section "Sampled verify keys noise by position":
 // a verify row draws its target token by Gumbel-max keyed by (seed,
