@@ -118,6 +118,8 @@ CASES = {
     "many_slices": (2, 64, 200000, "eagle", None, 0.75),
     # the largest vocabulary: 64 slices, 64 workgroups per request
     "max_vocab": (2, 16, 1 << 20, "random", None, 0.9),
+    # 5 slices over 3 workgroups per request (members take 2, 2 and 1)
+    "uneven_slices": (100, 16, 70000, "eagle", None, 0.75),
 }
 
 
@@ -306,3 +308,40 @@ def test_rejection_workspace_reused_across_calls():
                 assert torch.equal(got[k], fresh[k]), (B, N, V, with_q, rep, k)
         assert int(fresh["accept_len"].min()) >= 1
         say("workspace reuse B %d N %d V %d q %s: identical" % (B, N, V, with_q))
+
+
+def test_rejection_replays_in_a_graph():
+    """Both forms captured in a HIP graph with a workspace bound once and
+    replayed three times (the call clears its counters with a kernel, so
+    every replay starts afresh): each replay equals the eager call."""
+    B, N, V = 32, 64, 30000
+    for with_q in (False, True):
+        x = gen.make_rejection_inputs(B, N, V, 71, "cuda", tree="eagle", with_q=with_q)
+        args = (x.probs, dev(x.draft), dev(x.parents), dev(x.coins, torch.float32),
+                dev(x.bonus_u, torch.float32))
+        kw = dict(draft_score=dev(x.draft_score, torch.float32),
+                  draft_q=x.draft_q if with_q else None)
+        ws = torch.empty(tav.verify_tree_rejection_workspace_size(B, N, V), dtype=torch.uint8,
+                         device="cuda")
+        eager = tav.verify_tree_rejection(*args, **kw, workspace=ws)
+        torch.cuda.synchronize()
+        eager = {k: v.clone() for k, v in eager.items()}
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):     # warm the capture stream first
+            tav.verify_tree_rejection(*args, **kw, workspace=ws)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            got = tav.verify_tree_rejection(*args, **kw, workspace=ws)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            for v in got.values():
+                v.fill_(-7)               # every replay must rewrite every output
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for k in eager:
+                assert torch.equal(got[k], eager[k]), (with_q, rep, k)
+        say("graph replays, q form %s: identical to the eager call" % with_q)
