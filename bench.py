@@ -7,11 +7,13 @@ Hkv 8, D 128, bf16, page size 64): tree_build_masks -> tree_attention_prefix
 (K cache, V cache and a hidden-state table) -> tree_shift_positions(-1).
 Inputs are resident in HBM before the timed region.
 
-Prints one JSON line (see the design doc for every field).  `value` is the KV
-bytes the step must read divided by the step time; the roofline object is
-for the dominant kernel (the split-K prefix), timed with HIP events on the
-stream it runs on.  `cpu_baseline` times the CPU fp64 oracle on a bounded
-sample of rows of the same workload.
+Prints one JSON line.  `value` is the KV bytes the step must read divided
+by the step time; the roofline object is for the dominant kernel (the
+split-K prefix), timed with HIP events on the stream it runs on, with the
+HBM traffic of a committed counter summary when it was taken on the current
+kernel source; `timing` holds the settle phase and the step and launch
+statistics; `cpu_baseline` times the CPU fp64 oracle on a bounded sample of
+rows of the same workload.
 """
 import argparse
 import csv
