@@ -1,6 +1,8 @@
 """GPU parity over seeded random shapes: tree_attention and the MLA cascade
 through the C ABI against the CPU fp64 oracle, every row, with the bars of
-the other parity tests (out max |err| <= 1e-2, lse2 max |err| <= 1e-3).
+the other parity tests (out max |err| <= 1e-2, lse2 max |err| <= 1e-3), and
+the integer steps of a verify round (masks, greedy walk, compaction, shift)
+bit-exact.
 
 Each case draws its shape from its own seed: head dim 64 or 128, bf16 or FP8
 E4M3 caches, 1 to 8 kv heads with 1 to 16 query heads each, 1 to 64 tree
@@ -132,3 +134,78 @@ def test_random_shape_mla(k):
                                   inp.page_table, wl.page_size, inp.prefix_len, m, wl.W, wl.Dc,
                                   wl.Dr)
     compare(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, tag)
+
+
+def as_bytes(t):
+    t = t.detach().cpu().contiguous()
+    return t.view(torch.int16).numpy().view(np.uint8) if t.dtype == torch.bfloat16 \
+        else t.view(torch.uint8).numpy()
+
+
+def step_case(k):
+    r = np.random.default_rng(9000 + k)
+    B = int(r.integers(1, 17))
+    N = int(r.integers(1, 65))
+    D = int(r.choice([64, 128]))
+    dtype, kv = [("bf16", ""), ("f32", ""), ("bf16", "fp8")][int(r.integers(0, 3))]
+    Hkv = int(r.choice([1, 2, 8]))
+    ps = int(r.choice([1, 4, 16, 64]))
+    P = int(r.integers(0, 400))
+    pl = r.integers(0, P + 1, B).astype(np.int32)
+    tree = "chain" if r.random() < 0.25 else "random"
+    layout = "NHD" if r.random() < 0.4 else "HND"
+    wl = gen.Workload("step%d" % k, B, P, N, Hkv, Hkv, D, dtype, ps, tree,
+                      depth_cap=int(r.integers(1, 10)), kv_dtype=kv)
+    hidden_words = int(r.integers(1, 200))
+    return wl, pl, layout, hidden_words
+
+
+@pytest.mark.parametrize("k", range(12))
+def test_random_shape_verify_step(k):
+    """Masks, depth and positions; the greedy walk; compaction of the K and V
+    caches and a hidden-state table; the position shift: bit-exact against
+    the oracle on a random shape (1-16 requests, 1-64 nodes, pages of 1-64
+    keys, HND or NHD pools of bf16, fp32 or FP8 rows, hidden rows of 1-199
+    words)."""
+    wl, pl, layout, hw = step_case(k)
+    tag = "step case %d: B %d N %d D %d %s/%s Hkv %d ps %d P %s %s %s hidden %d" % (
+        k, wl.B, wl.N, wl.D, wl.dtype, wl.kv, wl.Hkv, wl.page_size, pl.tolist(), layout,
+        wl.tree, hw)
+    say(tag)
+    inp = gen.make_inputs(wl, 500 + k, "cuda", layout=layout, prefix_lens=pl)
+    g = tav.tree_build_masks(dev(inp.parents), vc=dev(inp.prefix_len))
+    ref = oracle.build_masks(inp.parents, vc=inp.prefix_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(g["masks"].cpu().numpy().view(np.uint64), ref["masks"]), tag
+    for key in ("depth", "positions", "tree_error"):
+        assert np.array_equal(g[key].cpu().numpy(), ref[key]), (tag, key)
+    v = tav.verify_tree_greedy(dev(inp.draft), dev(inp.target), dev(inp.parents))
+    rv = oracle.verify_greedy(inp.draft, inp.target, inp.parents)
+    for key in ("accepted_path", "accept_len", "accepted_tokens"):
+        assert np.array_equal(v[key].cpu().numpy(), rv[key]), (tag, key)
+    hidden = torch.randint(-2**31, 2**31 - 1, (wl.B, wl.N, hw), dtype=torch.int32, device="cuda")
+    pt, pld = dev(inp.page_table), dev(inp.prefix_len)
+    tables = [tav.RowTable.paged_kv(inp.k_cache, pt, pld, layout),
+              tav.RowTable.paged_kv(inp.v_cache, pt, pld, layout),
+              tav.RowTable.dense_rows(hidden)]
+    host = []
+    for t in tables:
+        paged = t.page_table is not None
+        host.append(dict(buf=as_bytes(t.buf).copy(), page_table=inp.page_table if paged else None,
+                         prefix_len=inp.prefix_len if paged else None, page_size=t.page_size,
+                         stride_page=t.stride_page, stride_token=t.stride_token,
+                         stride_head=t.stride_head, stride_batch=t.stride_batch,
+                         n_heads=t.n_heads, row_bytes=t.row_bytes))
+    tav.compact_window_rows(tables, v["accepted_path"], v["accept_len"])
+    torch.cuda.synchronize()
+    oracle.compact_rows(host, rv["accepted_path"], rv["accept_len"])
+    for name, t, h in zip(("K", "V", "hidden"), tables, host):
+        assert np.array_equal(as_bytes(t.buf), h["buf"]), (tag, name)
+    chain = inp.prefix_len[:, None] + np.arange(wl.N, dtype=np.int32)[None]
+    p = dev(chain)
+    tav.tree_shift_positions(p, g["depth"], +1)
+    torch.cuda.synchronize()
+    assert np.array_equal(p.cpu().numpy(), oracle.shift_positions(chain, ref["depth"], +1)), tag
+    tav.tree_shift_positions(p, g["depth"], -1)
+    torch.cuda.synchronize()
+    assert np.array_equal(p.cpu().numpy(), chain), tag
