@@ -324,11 +324,19 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
     const int ks = w / NRB;    // this wave's key subset within a stage
     const int rows_base = rg * ROWS_WG + rbw * 32;
 
-    // page-table slice of this split
+    // page-table slice of this split: its entries are loaded into registers
+    // first, the query loads go out behind them, and the entries are stored
+    // to LDS after (so the stores wait for the table loads only, and the two
+    // round trips overlap)
     const int lp0 = nkeys > 0 ? (kb0 >> a.ps_shift) : 0;
     const int npt = nkeys > 0 ? ((kr.hi - 1) >> a.ps_shift) - lp0 + 1 : 0;
-    for (int i = tid; i < npt && i < kPtMax; i += THREADS)
-        pt[i] = (int32_t)clamp_page(a.page_table[(int64_t)b * a.max_pages + lp0 + i], a.num_pages);
+    constexpr int PTPT = (kPtMax + THREADS - 1) / THREADS;   // entries per thread, at most
+    int64_t ptv[PTPT];
+#pragma unroll
+    for (int j = 0; j < PTPT; ++j) {
+        const int i = tid + j * THREADS;
+        ptv[j] = i < npt && i < kPtMax ? a.page_table[(int64_t)b * a.max_pages + lp0 + i] : 0;
+    }
     // zero the stage buffers once: the last, partial stage leaves rows unloaded
     // and they must hold finite values (their softmax weight is exactly 0)
     for (int i = tid; i < LDSB / 16; i += THREADS)
@@ -357,12 +365,13 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
                                : 16 * kk + 8 * hl;
             int4 v4 = ok ? *(const int4 *)(qrow + ch) : make_int4(0, 0, 0, 0);
             qv[kk] = __builtin_bit_cast(bf16x8, v4);
-            if constexpr (KV8)
-                qv[kk] = bf16x8_round_e4m3(qv[kk]);
         }
+    }
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk)
-            settle(qv[kk]);
+    for (int j = 0; j < PTPT; ++j) {
+        const int i = tid + j * THREADS;
+        if (i < npt && i < kPtMax)
+            pt[i] = (int32_t)clamp_page(ptv[j], a.num_pages);
     }
     __syncthreads();
 
@@ -554,8 +563,25 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
         convert8(st + 1, f8);
         load8(st + 3, f8);
     };
+    // Stage 0 goes out first, then the query is made ready (the compiler's
+    // wait for it also covers the direct-to-LDS loads issued before, which
+    // it does not count: only stage 0, which the first trip needs anyway),
+    // then the rest of the prefetch.
     if constexpr (KVD) {
-        for (int st = 0; st < NBUF8 - 1 && st < ns; ++st)
+        if (ns > 0)
+            issue8d(0);
+    } else if constexpr (!KV8) {
+        if (ns > 0)
+            issue(0);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+        if constexpr (KV8)
+            qv[kk] = bf16x8_round_e4m3(qv[kk]);
+        settle(qv[kk]);
+    }
+    if constexpr (KVD) {
+        for (int st = 1; st < NBUF8 - 1 && st < ns; ++st)
             issue8d(st);
     } else if constexpr (KV8) {
         if (ns > 0) {
@@ -565,7 +591,7 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
             load8(2, f8a);
         }
     } else {
-        for (int st = 0; st < NBUF - 1 && st < ns; ++st)
+        for (int st = 1; st < NBUF - 1 && st < ns; ++st)
             issue(st);
     }
 
