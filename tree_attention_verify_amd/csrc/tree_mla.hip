@@ -22,8 +22,11 @@
 //       (16 MFMAs).  Every score is computed once.  Latent rows stream HBM ->
 //       LDS with direct-to-LDS 16-byte loads, four stages deep; the same LDS
 //       bytes are read as the K operand and, transposed, as the V operand.
-//       FP8 rows land raw in the upper half of their stage buffer and are
-//       widened in place into the bf16 layout once the stage has landed.
+//       FP8 rows land raw in a ring of two slots (in the space of the fourth
+//       stage buffer); at the end of a trip each lane takes the chunks it
+//       loaded into registers, and at the top of the next it widens them
+//       into the bf16 layout of a stage buffer (the bf16 stages ring over
+//       three) and issues the slot's next raw stage.
 //   k_mla_window_merge<DR>  one wave per (request, row, head): the masked
 //       window keys (never the unseen ones) with lanes over channels, then
 //       the merge of the prefix partials through their base-2 LSE.
@@ -168,16 +171,14 @@ struct MlaCfg {
     static constexpr int PB = 64 * SK * 2;         // bf16 weights of a block: 64 rows x 32 keys
     // FP8 E4M3 rows (DK bytes): raw stages of SK rows land in a ring of two
     // slots in the space of the fourth stage buffer (the bf16 stages then
-    // ring over three), 64 16-byte chunks per load instruction; wave w takes
-    // instructions w, w + 8, w + 16
+    // ring over three): 32 chunks of 16 bytes a row in two load instructions
+    // per wave (keys 4 w .. 4 w + 3), the rotary part's 4 chunks a row in one
+    // more for waves 0 and 1 (16 keys each)
     static constexpr int CH8 = DK / 16;            // 16-byte chunks per FP8 row
-    static constexpr int NCH8 = SK * CH8;          // chunks per raw stage
-    static constexpr int NL8 = NCH8 / 64;          // load instructions per raw stage
-    static constexpr int L8MAX = (NL8 + 7) / 8;    // per wave, at most
     static constexpr int NB8 = 3;                  // bf16 stage buffers under FP8 rows
     static constexpr int RAW8 = NB8 * SB;          // byte offset of the raw ring
     static_assert(DK % 64 == 0 && LOADS == 4 * NG && KS >= 2 * LA, "row shape");
-    static_assert(NCH8 % 64 == 0 && 2 * SK * DK <= SB && L8MAX <= 3 && KS >= 2 * L8MAX, "fp8 rows");
+    static_assert(SK == 32 && (CH8 == 32 || CH8 == 36) && 2 * SK * DK <= SB, "fp8 rows");
     static_assert(NBUF * SB + 2 * PB + kMlaPt * 4 + 3 * 2 * 64 * 4 <= 160 * 1024, "LDS");
 };
 
@@ -281,100 +282,133 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
         if (j < nld && r.on)
             mla_dma16(r.src + 64 * j, __builtin_amdgcn_readfirstlane(r.sbase + (uint32_t)(j * SK * 128)));
     };
-    // FP8 rows: instruction x = w + 8 j (j < nld8) of a stage loads raw
-    // chunks 64 x .. 64 x + 63 (chunk q: key q / CH8, 16-byte chunk q % CH8
-    // of its row) to the raw stage, lane i at byte 16 (64 x + i); each lane
-    // looks up the page of its own key.
-    struct Loads8 {
-        int st;
-        uint32_t sbase;
-    };
-    const int nld8 = (C::NL8 - w + 7) / 8;
-    auto loads_of8 = [&](int st) {
-        Loads8 r;
-        r.st = st;
-        r.sbase = lds0 + (uint32_t)(C::RAW8 + (st & 1) * SK * DK);
-        return r;
-    };
-    // (the address is formed at issue time, and FP8 stages are issued
-    // outside the score steps, whose operands fill the registers)
-    // (the lane's chunk offsets are recomputed at every use: hoisted out of
-    // the loop they would hold a dozen registers)
-    auto opaque_lane = [&]() {
-        int l = lane;
-        mla_settle(l);
-        return l;
-    };
-    auto load_one8 = [&](const Loads8 &r, int j) {
-        if (j >= nld8)
-            return;
-        const int q = 64 * (w + 8 * j) + opaque_lane();
-        const int k = q / C::CH8, c = q - k * C::CH8;
-        const int t = lo + r.st * SK + k;
-        if (r.st < ns && t < hi) {
-            const int64_t pg = pt[(t >> a.ps_shift) - lp0];
-            mla_dma16((const uint8_t *)a.lat + pg * a.stride_page +
-                          (int64_t)(t & ps_mask) * a.stride_token + 16 * c,
-                      __builtin_amdgcn_readfirstlane(r.sbase + (uint32_t)((w + 8 * j) * 1024)));
-        }
-    };
-    using LoadsT = typename std::conditional<KV8, Loads8, Loads>::type;
-    constexpr int LMAX = KV8 ? C::L8MAX : LA;   // load instructions per stage of a wave, at most
-    auto loads_for = [&](int st) {
-        if constexpr (KV8)
-            return loads_of8(st);
-        else
-            return loads_of(st);
-    };
-    auto ld_one = [&](const LoadsT &r, int j) {
-        if constexpr (KV8)
-            load_one8(r, j);
-        else
+    auto issue = [&](int st) {
+        const Loads r = loads_of(st);
+#pragma unroll
+        for (int j = 0; j < LA; ++j)
             load_one(r, j);
     };
-    auto issue = [&](int st) {
-        const LoadsT r = loads_for(st);
-#pragma unroll
-        for (int j = 0; j < LMAX; ++j)
-            ld_one(r, j);
+    // FP8 rows (DK bytes, CH8 16-byte chunks): stage st lands raw in slot st
+    // % 2 of a ring of two, by direct-to-LDS loads.  Instruction 2 w + j (j =
+    // 0, 1) of wave w carries chunks 16 j .. 16 j + 15 of keys 4 w .. 4 w + 3,
+    // lane i taking key k8 and chunk 16 j + c8; with rotary channels (four
+    // more chunks a row) instruction 16 + w of waves 0 and 1 carries chunks
+    // 32 .. 35 of keys 16 w .. 16 w + 15 (lane i: key 16 w + i / 4, chunk 32 +
+    // i % 4).  Lane i's 16 bytes land at byte 16 i of the instruction's 1 KB,
+    // and the lane widens them itself, so one page lookup serves its main
+    // loads of a stage and its chunk offsets never change.  Every eight
+    // consecutive lanes take four chunks of each of two keys whose bf16 rows
+    // have opposite parity (128-byte halves of the banks), so each 16-byte
+    // write of widened chunks lands on eight distinct bank groups.
+    constexpr int TC8 = C::CH8 - 32;
+    constexpr int NT8 = TC8 ? SK * TC8 / 64 : 0;   // tail instructions a stage
+    const bool tail8 = w < NT8;
+    const int k8 = 4 * w + (((lane >> 2) & 1) | ((lane >> 5) << 1));
+    const int c8 = (lane & 3) | (((lane >> 3) & 3) << 2);
+    const int kt8 = (16 * w + (lane >> 2)) & (SK - 1);
+    // byte offset in a bf16 stage of chunk cc of key k; widened chunk 2 c of
+    // a row goes to slot s, chunk 2 c + 1 to slot s ^ 16 (c even or odd
+    // alike), and chunks 16 further on are 4 chunk groups further
+    auto bf16_slot = [](int k, int cc) {
+        return (uint32_t)((cc >> 3) * (SK * 128) + (k >> 3) * 1024 + (k & 7) * 128 + (((cc & 7) ^ (k & 7)) * 16));
     };
-    // Stage st's raw FP8 rows widened into the bf16 layout of its stage
-    // buffer: each thread takes the chunks it loaded itself, once its own
-    // loads have landed, so no barrier is needed before; the barrier at the
-    // top of the next trip publishes the stage.  Keys past the split end (not
-    // loaded) become zeros.
-    auto convert8 = [&](int st) {
-        const char *raw = lds + C::RAW8 + (st & 1) * SK * DK;
-        char *buf = lds + (st % NB) * SB;
-#pragma unroll
-        for (int j = 0; j < C::L8MAX; ++j) {
-            if (j >= nld8)
-                break;
-            const int q = 64 * (w + 8 * j) + opaque_lane();
-            const int k = q / C::CH8, c = q - k * C::CH8;
-            int4 h[2];
-            mla_fp8x16_to_bf16(*(const int4 *)(raw + 16 * q), h[0], h[1]);
-            if (lo + st * SK + k >= hi)
-                h[0] = h[1] = make_int4(0, 0, 0, 0);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int cc = 2 * c + e;   // bf16 chunk of the row
-                *(int4 *)(buf + (cc >> 3) * (SK * 128) + (k >> 3) * 1024 + (k & 7) * 128 +
-                          (((cc & 7) ^ (k & 7)) * 16)) = h[e];
-            }
+    // A lane's fixed offsets, packed in two registers and unpacked at every
+    // use from an opaque copy: computed in the loop, or hoisted out of it one
+    // by one, they would hold a dozen registers through the score steps.
+    const uint32_t pk8a = bf16_slot(k8, 2 * c8) | ((uint32_t)k8 << 16) | ((uint32_t)c8 << 24);
+    const uint32_t pk8b = bf16_slot(kt8, 64 + 2 * (lane & 3)) | ((uint32_t)kt8 << 16);
+    struct Lane8 {
+        uint32_t wm, wt;   // bf16 slots of the main and tail chunks
+        int k, kt, c;      // main key, tail key, main chunk
+    };
+    auto lane8 = [&]() {
+        uint32_t x = pk8a, y = pk8b;
+        mla_settle(x);
+        mla_settle(y);
+        return Lane8{x & 0xffffu, y & 0xffffu, (int)((x >> 16) & 0xffu), (int)(y >> 16), (int)(x >> 24)};
+    };
+    int4 r8[3];       // this lane's raw chunks of the next stage to widen
+    int32_t pg8[2];   // pages of its keys in the next stage to load
+    // the pages of stage sp's keys (main and tail) from the page table
+    auto pages8 = [&](int sp) {
+        if (sp >= ns)
+            return;
+        const Lane8 L = lane8();
+        const int t = lo + sp * SK + L.k;
+        pg8[0] = pt[t < hi ? (t >> a.ps_shift) - lp0 : 0];
+        if (tail8) {
+            const int t2 = lo + sp * SK + L.kt;
+            pg8[1] = pt[t2 < hi ? (t2 >> a.ps_shift) - lp0 : 0];
         }
     };
-    // Wait for this wave's loads of a raw stage.  next_full: the stage after
-    // it is issued and full (not the last stage, whose keys past the split
-    // end issue no loads), so exactly its nld8 loads may still be in flight;
-    // otherwise wait for everything.
-    auto wait8 = [&](bool next_full) {
-        if (!next_full)
+    // stage st's raw loads into its slot (keys past the split end load nothing)
+    auto issue8 = [&](int st) {
+        if (st >= ns)
+            return;
+        const uint32_t rs = lds0 + (uint32_t)(C::RAW8 + (st & 1) * (SK * DK));
+        const uint8_t *lat8 = (const uint8_t *)a.lat;
+        const Lane8 L = lane8();
+        const int t = lo + st * SK + L.k;
+        if (t < hi) {
+            const uint8_t *src = lat8 + (int64_t)pg8[0] * a.stride_page + (int64_t)(t & ps_mask) * a.stride_token + 16 * L.c;
+            mla_dma16(src, __builtin_amdgcn_readfirstlane(rs + (uint32_t)(2 * w * 1024)));
+            mla_dma16(src + 256, __builtin_amdgcn_readfirstlane(rs + (uint32_t)((2 * w + 1) * 1024)));
+        }
+        if (tail8) {
+            const int t2 = lo + st * SK + L.kt;
+            if (t2 < hi)
+                mla_dma16(lat8 + (int64_t)pg8[1] * a.stride_page + (int64_t)(t2 & ps_mask) * a.stride_token +
+                              16 * (32 + (lane & 3)),
+                          __builtin_amdgcn_readfirstlane(rs + (uint32_t)((16 + w) * 1024)));
+        }
+    };
+    // Wait for this wave's loads of stage st (the stage after it is issued;
+    // when it is full, exactly its loads may stay in flight), then take this
+    // lane's raw chunks of st into registers; keys past the split end (in the
+    // last stage only) become zeros.
+    auto take8 = [&](int st) {
+        if (st + 1 < ns - 1) {
+            if (tail8)
+                mla_wait_vmcnt<NT8 ? 3 : 2>();
+            else
+                mla_wait_vmcnt<2>();
+        } else {
             mla_wait_vmcnt<0>();
-        else if (nld8 == C::L8MAX)
-            mla_wait_vmcnt<C::L8MAX>();
-        else
-            mla_wait_vmcnt<C::L8MAX - 1>();
+        }
+        if (st >= ns)
+            return;
+        const char *raw = lds + C::RAW8 + (st & 1) * (SK * DK) + 16 * lane;
+        r8[0] = *(const int4 *)(raw + 2 * w * 1024);
+        r8[1] = *(const int4 *)(raw + (2 * w + 1) * 1024);
+        if (tail8)
+            r8[2] = *(const int4 *)(raw + (16 + w) * 1024);
+        if (st == ns - 1) {
+            const Lane8 L = lane8();
+            if (lo + st * SK + L.k >= hi)
+                r8[0] = r8[1] = make_int4(0, 0, 0, 0);
+            if (tail8 && lo + st * SK + L.kt >= hi)
+                r8[2] = make_int4(0, 0, 0, 0);
+        }
+    };
+    // the taken chunks widened into the bf16 layout of stage st's buffer; the
+    // barrier at the top of the next trip publishes them
+    auto convert8 = [&](int st) {
+        char *buf = lds + (st % NB) * SB;
+        const Lane8 L = lane8();
+        const uint32_t wm8 = L.wm, wt8 = L.wt;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            int4 h0, h1;
+            mla_fp8x16_to_bf16(r8[j], h0, h1);
+            *(int4 *)(buf + wm8 + j * (4 * SK * 128)) = h0;
+            *(int4 *)(buf + (wm8 ^ 16u) + j * (4 * SK * 128)) = h1;
+        }
+        if (tail8) {
+            int4 h0, h1;
+            mla_fp8x16_to_bf16(r8[2], h0, h1);
+            *(int4 *)(buf + wt8) = h0;
+            *(int4 *)(buf + (wt8 ^ 16u)) = h1;
+        }
     };
 
     // K operand of step s (score role): lane (g, i16) reads key 16 kt + i16,
@@ -424,7 +458,7 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
     // block pst (weights in buffer pb) for this wave's 64 channels and all 64
     // rows: its operands are read first and its 16 MFMAs sit between the
     // score steps, which they do not depend on.
-    auto score = [&](int st, const LoadsT *ld, bool with_pv, int pst, int pb) {
+    auto score = [&](int st, const Loads *ld, bool with_pv, int pst, int pb) {
         const char *kb = lds + (st % NB) * SB + koff;
         const char *kb1 = lds + (st % NB) * SB + (koff ^ 64u);
         auto kread = [&](int s) { return *(const bf16x8 *)((s & 1 ? kb1 : kb) + (s >> 1) * (SK * 128)); };
@@ -462,8 +496,8 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
                     k1 = kread(s + 5);
             }
             pv_step(s / 4, 1);
-            if (ld && s / 2 < LMAX)
-                ld_one(*ld, s / 2);
+            if (ld && s / 2 < LA)
+                load_one(*ld, s / 2);
             if (s + 2 < KS) {
                 sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k2, qv[s + 2], sc, 0, 0, 0);
                 if (s + 6 < KS)
@@ -476,8 +510,8 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
                     k3 = kread(s + 7);
             }
             pv_step(s / 4, 3);
-            if (ld && s / 2 + 1 < LMAX)
-                ld_one(*ld, s / 2 + 1);
+            if (ld && s / 2 + 1 < LA)
+                load_one(*ld, s / 2 + 1);
         }
         sc += sd;
         const int lim = hi - (lo + st * SK) - 16 * kt - 4 * g;
@@ -557,18 +591,25 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
                 o[ct][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
         l_part = 0.f;
         if constexpr (KV8) {
-            // raw stages 0 and 1, widened into bf16 stages 0 and 1 as they
-            // land, each slot refilled at once (stages 2 and 3)
-            issue(0);
-            issue(1);
-            wait8(1 < ns - 1);
+            // raw stages 0 and 1 issued, each widened as it lands and its slot
+            // refilled at once (stages 2 and 3); then stage 2's chunks and
+            // stage 4's pages are taken for the first trip
+            pages8(0);
+            issue8(0);
+            pages8(1);
+            issue8(1);
+            take8(0);
+            pages8(2);
             if (ns > 0)
                 convert8(0);
-            issue(2);
-            wait8(2 < ns - 1);
+            issue8(2);
+            take8(1);
+            pages8(3);
             if (1 < ns)
                 convert8(1);
-            issue(3);
+            issue8(3);
+            take8(2);
+            pages8(4);
         } else {
             for (int st = 0; st < NBUF - 1 && st < ns; ++st)
                 issue(st);
@@ -595,16 +636,17 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
             }
             __syncthreads();
             const bool more = u + 1 < ns;
-            const LoadsT ld = loads_for(u + NBUF - 1);
+            Loads ld{};
+            if constexpr (!KV8)
+                ld = loads_of(u + NBUF - 1);
             if constexpr (KV8) {
-                // stage u + 2 is widened into the buffer of block u - 1 (free
-                // since the barrier) as this wave's loads of it land, and its
-                // raw slot is refilled with stage u + 4; the next trip's
+                // stage u + 2 (taken at the end of the last trip) is widened
+                // into the buffer of block u - 1, free since the barrier, and
+                // its raw slot is refilled with stage u + 4; the next trip's
                 // barrier publishes it
-                wait8(u + 3 < ns - 1);
                 if (u + 2 < ns)
                     convert8(u + 2);
-                issue(u + 4);
+                issue8(u + 4);
                 // (kept apart from the score steps, whose operands fill the
                 // registers)
                 __builtin_amdgcn_sched_barrier(0);
@@ -613,6 +655,11 @@ __global__ void __launch_bounds__(512, 1) k_mla_prefix(MlaArgs a) {
             const float mx = mla_quad_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * a.c);
             seen = fmaxf(seen, mx);
             weights(sc, (u + 1) & 1, more);
+            if constexpr (KV8) {
+                // for the next trip: stage u + 3's chunks, stage u + 5's pages
+                take8(u + 3);
+                pages8(u + 5);
+            }
         }
         // repeat with the exact row max (over both key tiles) when some row
         // passed mu + 64; the decision is the workgroup's: the stages are shared
