@@ -48,8 +48,8 @@ PREFIX_KERNEL = "k_prefix_mfma"
 COPY_KERNEL = "copyBuffer"
 
 
-def kernel_hash():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def kernel_hash(src=None):
+    return hashlib.sha256(open(src or KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
 def traffic_for(workload):
@@ -138,13 +138,26 @@ def summarize_stats(workload, stats_dir, cmd):
 N_XCD, N_SIMD = 8, 1024     # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 
 
-def summarize_counters(workload, dirs, cmd):
+def summarize_counters(workload, dirs, cmd, mla=False):
     """profiles/<workload>_counters.md from rocprofv3 --pmc runs (one
     directory per pass): per-dispatch averages of every counter for the
-    prefix kernel, and what they imply (cycles, MFMA utilisation, vector
-    and LDS instructions per unit of work)."""
-    wl = gen.WORKLOADS[workload]
-    kname = prefix_kernel_name(wl)
+    prefix kernel (k_mla_prefix for an MLA workload), and what they imply
+    (cycles, MFMA utilisation, vector and LDS instructions per unit of
+    work)."""
+    if mla:
+        wl = gen.MLA_WORKLOADS[workload]
+        kname, src = "k_mla_prefix", os.path.join(ROOT, "tree_attention_verify_amd", "csrc", "tree_mla.hip")
+        Dk = wl.Dc + wl.Dr
+        kvb = wl.B * wl.P * Dk * (1 if wl.kv == "fp8" else 2)
+        scores = float(wl.B * wl.R * wl.Hq * wl.P)
+        flops = scores * (2 * Dk + 2 * wl.Dc)
+        # v_mfma_f32_16x16x32_bf16 per 1024 scores: 4 tiles of 16 x 16 over Dk / 32
+        # steps, and Dc / 16 value tiles per 16 rows x 32 keys
+        mfma_note = "%d = the exact work on 16x16x32 bf16" % (4 * Dk // 32 + 2 * wl.Dc // 16)
+    else:
+        wl = gen.WORKLOADS[workload]
+        kname, src = prefix_kernel_name(wl), None
+        mfma_note = "16 = the exact work on 32x32x16 bf16"
     vals, durs = {}, []
     for d in dirs:
         rows = [r for r in _csv_rows(os.path.join(d, "**", "*counter_collection.csv"))
@@ -155,10 +168,11 @@ def summarize_counters(workload, dirs, cmd):
             durs.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
         for k, v in per.items():
             vals[k] = (sum(v) / len(v), len(v))
-    P_vis = min(wl.P, wl.prefix_window) if wl.prefix_window else wl.P
-    kvb = kv_bytes(wl, P_vis, with_window=False)
-    flops = 4.0 * wl.D * wl.Hq * wl.B * wl.R * P_vis
-    scores = flops / (4.0 * wl.D)
+    if not mla:
+        P_vis = min(wl.P, wl.prefix_window) if wl.prefix_window else wl.P
+        kvb = kv_bytes(wl, P_vis, with_window=False)
+        flops = 4.0 * wl.D * wl.Hq * wl.B * wl.R * P_vis
+        scores = flops / (4.0 * wl.D)
     g = lambda k: vals.get(k, (float("nan"), 0))[0]
     dur_ns = float(np.median(durs)) if durs else float("nan")
     cyc = g("GRBM_GUI_ACTIVE") / N_XCD
@@ -168,12 +182,14 @@ def summarize_counters(workload, dirs, cmd):
         ("engine clock during the dispatch, GHz", cyc / dur_ns if dur_ns else float("nan")),
         ("MFMA busy, share of SIMD cycles (SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles))",
          g("SQ_VALU_MFMA_BUSY_CYCLES") / (N_SIMD * cyc)),
-        ("MFMA instructions per 1024 (row, key) scores (16 = the exact work on 32x32x16 bf16)",
+        ("MFMA instructions per 1024 (row, key) scores (%s)" % mfma_note,
          g("SQ_INSTS_MFMA") / scores * 1024),
         ("vector ALU instructions other than MFMA, per 64 scores (one wave-wide op each)",
          (g("SQ_INSTS_VALU") - g("SQ_INSTS_MFMA")) / scores * 64),
         ("of which transcendental (v_exp), per 64 scores", g("SQ_INSTS_VALU_TRANS_F32") / scores * 64),
         ("LDS instructions per KiB of prefix K/V", g("SQ_INSTS_LDS") / (kvb / 1024)),
+        ("LDS busy, share of CU cycles (SQ_LDS_IDX_ACTIVE / (256 CUs x cycles))",
+         g("SQ_LDS_IDX_ACTIVE") / (N_SIMD / 4 * cyc)),
         ("MFMA/VALU co-execution, share of MFMA busy cycles",
          g("SQ_VALU_MFMA_COEXEC_CYCLES") / g("SQ_VALU_MFMA_BUSY_CYCLES")),
         ("LDS bank-conflict cycles per LDS instruction", g("SQ_LDS_BANK_CONFLICT") / g("SQ_INSTS_LDS")),
@@ -193,7 +209,7 @@ def summarize_counters(workload, dirs, cmd):
         f.write("\n| derived | value |\n|---|---|\n")
         for k, v in derived:
             f.write("| %s | %.4g |\n" % (k, v))
-        f.write("\nKernel source sha256[:16] %s.\n" % kernel_hash())
+        f.write("\nKernel source sha256[:16] %s.\n" % kernel_hash(src))
     print(open(out).read())
 
 
@@ -936,7 +952,8 @@ def main():
         summarize_power(*args.summarize_power)
         return
     if args.summarize_counters:
-        summarize_counters(args.workload, args.summarize_counters[:-1], args.summarize_counters[-1])
+        summarize_counters(args.mla or args.workload, args.summarize_counters[:-1],
+                           args.summarize_counters[-1], mla=bool(args.mla))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
