@@ -178,17 +178,25 @@ tav_status tree_attention(const void *q, const void *k_cache, const void *v_cach
 /*
  * The two phases of tree_attention as separate calls, with tree_attention's
  * arguments and contract; tree_attention is exactly tree_attention_prefix
- * followed by tree_attention_window_merge on the same stream and workspace.
- * They mirror the cascade's split ([DTS] "One tree attention ...": the
- * prefix decode, then the window part and the merge), so a caller can place
- * other work between them or time them apart.
+ * followed by tree_attention_window_merge on the same stream and workspace,
+ * and the two calls must get the same arguments.  They mirror the cascade's
+ * split ([DTS] "One tree attention ...": the prefix decode, then the window
+ * part and the merge), so a caller can place other work between them or
+ * time them apart.
  *   tree_attention_prefix        reads q, the K/V prefix pages, page_table and
  *                                prefix_len; writes the split-K prefix partials
- *                                into the workspace (masks, W, out, lse2 unused
- *                                and may be NULL / 0)
+ *                                into the workspace
  *   tree_attention_window_merge  reads the workspace partials of a preceding
  *                                tree_attention_prefix with the same arguments,
  *                                the window keys and masks; writes out and lse2
+ * Except: when the prefix runs as a single split on the kernel for more than
+ * 128 folded rows per kv head (bf16 K/V; the library picks the split count
+ * from B, Hkv and the prefix length), and out and, for W > 0, masks are
+ * given, tree_attention_prefix also attends the window keys and writes out
+ * and lse2 itself, and tree_attention_window_merge then launches nothing.
+ * The window keys are then one more stage of the prefix launch, with the
+ * same semantics (a non-finite V value reaches exactly the rows that see
+ * its key).
  */
 tav_status tree_attention_prefix(const void *q, const void *k_cache, const void *v_cache,
                                  tav_dtype dtype, int64_t stride_page, int64_t stride_head,

@@ -121,6 +121,9 @@ CASES = {
     "random16": gen.WORKLOADS["random16"].with_(B=3, P=1000),
     # FP8 E4M3 caches
     "chain8_fp8": gen.WORKLOADS["chain8_fp8"].with_(B=4, P=2000),
+    # 512 folded rows in one split: the prefix phase takes the window keys and
+    # writes the output, the window-and-merge phase launches nothing
+    "eagle64": gen.WORKLOADS["eagle64"].with_(B=2, P=300),
 }
 
 

@@ -268,6 +268,46 @@ def test_nhd_layout_and_high_mask_bits():
     check_attention(out, lse, ro, rl, tag="NHD")
 
 
+PHASE_SHAPES = {
+    # 512 folded rows, one split: the prefix launch takes the window keys and
+    # writes the output, the window-and-merge phase launches nothing
+    "pipe_one_split": gen.Workload("ph1", 2, 300, 64, 16, 2, 128, "bf16", 16, "random", depth_cap=6),
+    # 256 folded rows, several splits: prefix partials, then window and merge
+    "pipe_splits": gen.Workload("ph2", 2, 3000, 64, 32, 8, 128, "bf16", 64, "random", depth_cap=8),
+    # 64 folded rows (the small-row prefix kernel)
+    "small_rows": gen.Workload("ph3", 3, 700, 16, 32, 8, 128, "bf16", 16, "random", depth_cap=6),
+}
+
+
+@pytest.mark.parametrize("shape", sorted(PHASE_SHAPES))
+def test_phases_equal_one_call(shape):
+    # tree_attention is exactly tree_attention_prefix then
+    # tree_attention_window_merge with the same arguments: bit for bit, and
+    # both within the bars of the oracle
+    wl = PHASE_SHAPES[shape]
+    say("case", shape, wl)
+    inp = gen.make_inputs(wl, 12, "cuda")
+    m = oracle.build_masks(inp.parents)["masks"]
+    md = dev(m.view(np.int64), torch.int64)
+    out1, lse1 = run_attention(inp, md)
+    kw = dict(max_prefix_len=int(inp.prefix_len.max()), layout=inp.layout,
+              prefix_window=wl.prefix_window)
+    args = (inp.q, inp.k_cache, inp.v_cache, dev(inp.page_table), dev(inp.prefix_len), md, wl.W)
+    out2 = torch.full_like(inp.q, float("nan"))
+    lse2 = torch.full_like(lse1, float("nan"))
+    ws = torch.empty(tav.tree_attention_workspace_size(inp.q.dtype, wl.B, wl.R, wl.Hq, wl.Hkv, wl.D,
+                                                       kw["max_prefix_len"], wl.prefix_window,
+                                                       wl.page_size),
+                     dtype=torch.uint8, device="cuda")
+    tav.tree_attention(*args, **kw, out=out2, lse2=lse2, workspace=ws, phase="prefix")
+    tav.tree_attention(*args, **kw, out=out2, lse2=lse2, workspace=ws, phase="window_merge")
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16)), shape + ": out"
+    assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32)), shape + ": lse2"
+    ro, rl = oracle_attention(inp, m)
+    check_attention(out1, lse1, ro, rl, tag=shape)
+
+
 def test_nan_in_node_leaks_only_to_descendants():
     wl = gen.Workload("nan", 1, 200, 16, 8, 2, 128, "bf16", 16, "random", depth_cap=4)
     inp = gen.make_inputs(wl, 5, "cuda")

@@ -222,11 +222,16 @@ def tree_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     under a bf16 q; page_table int32 [B][max_pages];
     prefix_len int32 [B]; masks int64 [B][R] (uint64 bit patterns).
     phase: "all" (tree_attention), "prefix" (tree_attention_prefix) or
-    "window_merge" (tree_attention_window_merge; pass the workspace the
-    prefix phase filled).
+    "window_merge" (tree_attention_window_merge; pass the workspace, out
+    and lse2 of the prefix phase: with a single split the prefix phase may
+    write the output itself).
     Returns (out [B][R][Hq][D], lse2 float32 [B][R][Hq] or None)."""
     fn = {"all": "tree_attention", "prefix": "tree_attention_prefix",
           "window_merge": "tree_attention_window_merge"}[phase]
+    if phase == "window_merge" and (out is None or workspace is None or
+                                    (return_lse and lse2 is None)):
+        raise ValueError("phase='window_merge' takes the workspace, out and lse2 "
+                         "of the prefix phase")
     dt = _code(q.dtype, k_cache.dtype)
     _need(q, "q", q.dtype)
     dev = q.device

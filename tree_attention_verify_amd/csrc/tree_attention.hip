@@ -215,6 +215,13 @@ struct PrefixArgs {
     float c;  // sm_scale * log2(e): scores in the exp2 domain
     float *ws_o;
     float *ws_lse;
+    // a single split on the pipelined kernel over bf16 K/V, with the masks
+    // and output given: the split also attends the window keys under the
+    // masks and writes the output itself (no window or merge launch)
+    int32_t fuse, W;
+    const uint64_t *masks;
+    void *out;
+    float *lse2;
 };
 
 // Visible prefix range [lo, hi) of split `split` of request b.
@@ -964,12 +971,30 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
     const int nb = (nkeys + 31) / 32;
     const int rows_base = rg * ROWS_WG + w * 32;
 
-    const int lp0 = nkeys > 0 ? (kb0 >> a.ps_shift) : 0;
-    const int npt = nkeys > 0 ? ((kr.hi - 1) >> a.ps_shift) - lp0 + 1 : 0;
+    // A fused launch (one split, whose range ends at the prefix length P):
+    // the page-table slice also covers the window keys P .. P + W - 1.
+    int Pw = 0;
+    const bool wown = !KV8 && a.fuse && a.W > 0;
+    if (wown) {
+        Pw = a.prefix_len[b];
+        Pw = Pw < 0 ? 0 : (Pw > a.max_prefix_len ? a.max_prefix_len : Pw);
+    }
+    const bool any_pt = nkeys > 0 || wown;
+    const int lp0 = any_pt ? ((nkeys > 0 ? kb0 : Pw) >> a.ps_shift) : 0;
+    const int npt = any_pt ? (((wown ? Pw + a.W : kr.hi) - 1) >> a.ps_shift) - lp0 + 1 : 0;
     for (int i = tid; i < npt && i < kPtMax; i += THREADS)
         pt[i] = (int32_t)clamp_page(a.page_table[(int64_t)b * a.max_pages + lp0 + i], a.num_pages);
     for (int i = tid; i < VRING / 16; i += THREADS)
         reinterpret_cast<int4 *>(lds)[i] = make_int4(0, 0, 0, 0);
+    __shared__ uint32_t wbad[2];   // window keys 0..31, 32..63 with a non-finite V value
+    if (tid < 2)
+        wbad[tid] = 0u;
+    // the window owner's row masks, fetched with the page table
+    __shared__ uint64_t wmk[KV8 ? 1 : ROWS_WG];
+    if (wown && tid < ROWS_WG) {
+        const int mm = rg * ROWS_WG + tid;
+        wmk[tid] = mm < a.M ? a.masks[(int64_t)b * a.R + mm / a.G] : 0ull;
+    }
 
     // Q^T operand, bf16: lane (row l32, half hl) holds 8 channels of Q[row]
     // per 16-channel k step, 16 kk + 8 hl .. +8.  Under an FP8 cache the
@@ -1049,6 +1074,36 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
                     dma_load16((const uint16_t *)(vreg ? a.v : a.k) + off + chunk(i),
                                sbase + i * THREADS * 16);
                 }
+            }
+        }
+    };
+    // The window keys P .. P + W - 1 as rows 0 .. W - 1 of one more stage, in
+    // buffer ns % NBUF, which no prefix stage uses once stage ns - PF is
+    // ready: it goes out with the prefix stages when they all fit in the
+    // first PF slots, else after the main loop, before the last blocks
+    // (outside the loop, so that it adds nothing to the loop's registers).  Page per
+    // lane (the window need not start on an 8-key boundary).  Rows W .. 63
+    // keep stale stage data: their scores are masked and their V values are
+    // made finite before use.
+    auto issue_window = [&]() {
+        if (8 * w >= a.W)
+            return;
+        // (from an opaque copy of the lane index, so that nothing of this
+        // once-per-workgroup path is shared with, or hoisted into, the loop)
+        int l = lane;
+        settle(l);
+        const int j = 8 * w + (l >> 3);
+        if (j < a.W) {
+            const uint32_t sbase = lds0 + (uint32_t)((ns % NBUF) * SB) + w * 64 * 16;
+            const int t = Pw + j;
+            const int64_t off = (int64_t)pt[(t >> a.ps_shift) - lp0] * a.stride_page +
+                                (int64_t)g * a.stride_head + (int64_t)(t & ps_mask) * a.stride_token;
+#pragma unroll
+            for (int i = 0; i < LPS; ++i) {
+                const bool vreg = i * THREADS >= SK * (D / 8);
+                const int cg = (vreg ? i * THREADS - SK * (D / 8) : i * THREADS) / (SK * 8);
+                const int c = cg * 8 * 8 + ((l & 7) ^ (vreg ? yv(j, cg) : xk(j))) * 8;
+                dma_load16((const uint16_t *)(vreg ? a.v : a.k) + off + c, sbase + i * THREADS * 16);
             }
         }
     };
@@ -1313,6 +1368,8 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
     } else {
         for (int st = 0; st < PF && st < ns; ++st)
             issue(st);
+        if (wown && ns < PF)
+            issue_window();
     }
     if (nb > 0) {
         stage_ready(0);
@@ -1354,6 +1411,8 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
                 step(u, s, pa, pbb, false, ka, va);
                 step(u + 1, s, pbb, pa, true, ka, va);
             }
+            if (wown && ns >= PF)
+                issue_window();
             if (u == nb - 2) {
                 step(u, s, pa, pbb, false, ka, va);
                 pa[0] = pbb[0];
@@ -1370,25 +1429,163 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
         }
     }
 
+    // The window part (a fused launch): once the window stage has
+    // landed, its non-finite V values are set to 0 and their keys flagged;
+    // then its (at most two) 32-key blocks run as prefix blocks do, with each
+    // row's ancestor mask on the scores and the weights split into a bf16
+    // head and remainder (a row may weigh few window keys, whose rounding
+    // would not average out).  A row that sees a flagged key gets, per
+    // channel, the sum of those keys' non-finite values added to its output,
+    // which is what the exact weighted sum gives.
+    const int m = rows_base + l32;
+    uint64_t rmask = 0ull;
+    if (wown) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        char *vw = lds + (ns % NBUF) * SB + KREG;
+        for (int i = tid; i < KREG / 16; i += THREADS) {
+            const int key = (i % (SK * 8)) / 8;
+            uint4 u4 = *(const uint4 *)(vw + i * 16);
+            uint32_t x[4] = {u4.x, u4.y, u4.z, u4.w};
+            bool nf = false;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2)
+                    if (((x[e] >> (16 * h2)) & 0x7F80u) == 0x7F80u) {
+                        nf = true;
+                        x[e] &= ~(0xFFFFu << (16 * h2));
+                    }
+            if (nf) {
+                *(uint4 *)(vw + i * 16) = make_uint4(x[0], x[1], x[2], x[3]);
+                if (key < a.W)
+                    atomicOr(&wbad[key >> 5], 1u << (key & 31));
+            }
+        }
+        __syncthreads();
+        rmask = wmk[w * 32 + l32];
+        if (a.W < 64)
+            rmask &= (1ull << a.W) - 1ull;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (kb * 32 >= a.W)
+                break;
+            const int u = ns * BPS + kb;   // the window stage's blocks
+            bf16x8 ka[KSTEPS];
+            load_k(u, ka);
+            f32x16 sv = qk(ka);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int j = kb * 32 + 8 * (e >> 2) + 4 * hl + (e & 3);
+                if (!((rmask >> j) & 1ull))
+                    sv[e] = -INFINITY;
+            }
+            if (nb == 0 && kb == 0) {
+                // no prefix keys: the reference is this block's row max
+                mu = row_max(sv);
+                mu = fabsf(mu) < INFINITY ? mu : 0.f;
+            }
+            bf16x8 pb[2], pr[2];
+            float lb;
+            auto wweights = [&]() {
+                float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = fast_exp2(fmaf(sv[r], a.c, -mu));
+                    const __bf16 ph = (__bf16)p;
+                    pb[r >> 3][r & 7] = ph;
+                    pr[r >> 3][r & 7] = (__bf16)(p - (float)ph);
+                    if (r & 1)
+                        l1 += p;
+                    else
+                        l0 += p;
+                }
+                lb = l0 + l1;
+            };
+            wweights();
+            if (__ballot(!(l_run + lb <= kSumLimit))) {
+                const float mx = row_max(sv);
+                const float mnew = mx < INFINITY ? fmaxf(mu, mx) : mu;
+                const float alpha = fast_exp2(mu - mnew);
+                l_run *= alpha;
+#pragma unroll
+                for (int t = 0; t < DT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        o[t][r] *= alpha;
+                mu = mnew;
+                wweights();
+            }
+            l_run += lb;
+            bf16x8 va[DT][2];
+            load_v(u, va);
+            pv(va, pb);
+            pv(va, pr);
+        }
+    }
+
     const int sidx = split;
     const float lt = pair_sum(l_run);
-    const int m = rows_base + l32;
     if (m < a.M) {
         const int r = m / a.G, hh = m % a.G;
         const int64_t row = ((int64_t)b * a.R + r) * a.Hq + (int64_t)g * a.G + hh;
         const float inv = has_keys(lt) ? 1.f / lt : 0.f;
-        float *dst = a.ws_o + (row * a.S + sidx) * D;
+        const float lse = has_keys(lt) ? mu + __log2f(lt) : -INFINITY;
+        // lane value o[t][e] is channel chan(t, e) of row m
+        auto chan = [&](int t, int e) {
+            return ((e >> 3) ? D / 2 : 0) + 16 * t + 8 * ((e >> 2) & 1) + 4 * hl + (e & 3);
+        };
 #pragma unroll
         for (int t = 0; t < DT; ++t)
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = ((q4 >> 1) ? D / 2 : 0) + 16 * t + 8 * (q4 & 1) + 4 * hl;
-                float4 v4 = make_float4(o[t][4 * q4] * inv, o[t][4 * q4 + 1] * inv,
-                                        o[t][4 * q4 + 2] * inv, o[t][4 * q4 + 3] * inv);
-                *(float4 *)(dst + d) = v4;
+            for (int e = 0; e < 16; ++e)
+                o[t][e] *= inv;
+        uint64_t vbad = rmask & (((uint64_t)wbad[1] << 32) | wbad[0]);
+        if (wown && __ballot(vbad != 0ull)) {
+            while (vbad) {
+                const int j = __ffsll((unsigned long long)vbad) - 1;
+                vbad &= vbad - 1;
+                const int t_ = Pw + j;
+                const int64_t page =
+                    clamp_page(a.page_table[(int64_t)b * a.max_pages + (t_ >> a.ps_shift)], a.num_pages);
+                const int64_t vo = page * a.stride_page + (int64_t)g * a.stride_head +
+                                   (int64_t)(t_ & ps_mask) * a.stride_token;
+#pragma unroll
+                for (int t = 0; t < DT; ++t)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const float x = bf16_bits_to_f32(((const uint16_t *)a.v)[vo + chan(t, e)]);
+                        if (!(fabsf(x) < INFINITY))
+                            o[t][e] += x;
+                    }
             }
-        if (hl == 0)
-            a.ws_lse[row * a.S + sidx] = has_keys(lt) ? mu + __log2f(lt) : -INFINITY;
+        }
+        if (!KV8 && a.fuse) {
+            // a fused launch: this is the row's output
+            uint16_t *out = (uint16_t *)a.out + row * D;
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const uint32_t lo = f32_to_bf16_bits(o[t][4 * q4]) |
+                                        ((uint32_t)f32_to_bf16_bits(o[t][4 * q4 + 1]) << 16);
+                    const uint32_t hi = f32_to_bf16_bits(o[t][4 * q4 + 2]) |
+                                        ((uint32_t)f32_to_bf16_bits(o[t][4 * q4 + 3]) << 16);
+                    *(uint2 *)(out + chan(t, 4 * q4)) = make_uint2(lo, hi);
+                }
+            if (a.lse2 && hl == 0)
+                a.lse2[row] = lse;
+        } else {
+            float *dst = a.ws_o + (row * a.S + sidx) * D;
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    *(float4 *)(dst + chan(t, 4 * q4)) = make_float4(o[t][4 * q4], o[t][4 * q4 + 1],
+                                                                     o[t][4 * q4 + 2], o[t][4 * q4 + 3]);
+            if (hl == 0)
+                a.ws_lse[row * a.S + sidx] = lse;
+        }
     }
 }
 
@@ -2039,14 +2236,16 @@ Plan make_plan(tav_dtype dtype, int B, int R, int Hq, int Hkv, int D, int max_pr
         n = n < by_stages ? n : by_stages;
         n = n < 1 ? 1 : n;
         // keys per split: a whole number of stages whose page-table slice
-        // (kps / page_size + 2 entries at most) fits the LDS slice
+        // fits the LDS slice, also with the 8 keys below the split start that
+        // a stage may begin with and the 64 window keys a fused call appends
+        // ((kps + 72) / page_size + 2 entries at most)
         int kps;
         for (;;) {
             kps = (max_vis + n - 1) / n;
             kps = ((kps + SK - 1) / SK) * SK;
             if (kps < SK)
                 kps = SK;
-            if ((long long)kps / page_size + 2 <= kPtMax)
+            if ((long long)(kps + 72) / page_size + 2 <= kPtMax)
                 break;
             ++n;
         }
@@ -2128,6 +2327,7 @@ struct Call {
     int D;
     bool bf16;   // bf16 query and output (bf16 or FP8 K/V)
     bool kv8;    // FP8 E4M3 K/V
+    bool fused;  // the prefix launch also takes the window keys and writes the output
 };
 
 // Validates every argument (all failures are reported together) and builds
@@ -2244,6 +2444,19 @@ tav_status prepare(const char *fn, int phase, Call &call, const void *q, const v
     call.D = D;
     call.bf16 = dtype != TAV_F32;
     call.kv8 = dtype == TAV_FP8_E4M3;
+    // One split on the pipelined kernel over bf16 K/V, with the masks and
+    // the output given: the prefix launch takes the window keys too and
+    // writes the output, and the window-and-merge phase launches nothing.
+    // Both phases decide it from their (identical) arguments.
+    call.fused = dtype == TAV_BF16 && p.mfma && p.NRB == 8 && p.n_split == 1 && out != nullptr &&
+                 (W == 0 || masks != nullptr);
+    if (call.fused) {
+        a.fuse = 1;
+        a.W = W;
+        a.masks = masks;
+        a.out = out;
+        a.lse2 = lse2;
+    }
     return TAV_OK;
 }
 
@@ -2345,7 +2558,7 @@ static tav_status run_phases(const char *fn, int phase, TAV_ATTN_PARAMS) {
         if (e != TAV_OK)
             return e;
     }
-    if (phase & 2)
+    if ((phase & 2) && !call.fused)
         launch_merge(call, s);
     return tav::launched(fn);
 }
