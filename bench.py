@@ -188,12 +188,14 @@ def summarize_counters(workload, dirs, cmd, mla=False):
          (g("SQ_INSTS_VALU") - g("SQ_INSTS_MFMA")) / scores * 64),
         ("of which transcendental (v_exp), per 64 scores", g("SQ_INSTS_VALU_TRANS_F32") / scores * 64),
         ("LDS instructions per KiB of prefix K/V", g("SQ_INSTS_LDS") / (kvb / 1024)),
-        ("LDS busy, share of CU cycles (SQ_LDS_IDX_ACTIVE / (256 CUs x cycles))",
-         g("SQ_LDS_IDX_ACTIVE") / (N_SIMD / 4 * cyc)),
+
         ("MFMA/VALU co-execution, share of MFMA busy cycles",
          g("SQ_VALU_MFMA_COEXEC_CYCLES") / g("SQ_VALU_MFMA_BUSY_CYCLES")),
         ("LDS bank-conflict cycles per LDS instruction", g("SQ_LDS_BANK_CONFLICT") / g("SQ_INSTS_LDS")),
     ]
+    if "SQ_LDS_IDX_ACTIVE" in vals:
+        derived.append(("LDS busy, share of CU cycles (SQ_LDS_IDX_ACTIVE / (256 CUs x cycles))",
+                        g("SQ_LDS_IDX_ACTIVE") / (N_SIMD / 4 * cyc)))
     os.makedirs(PROFILES, exist_ok=True)
     out = os.path.join(PROFILES, "%s_counters.md" % workload)
     with open(out, "w") as f:

@@ -21,6 +21,9 @@
 //       the exp2 domain.  Writes one (O, lse2) partial per split (its NKS key
 //       subsets combined in LDS).
 //   k_prefix_mfma_pipe  the software-pipelined kernel for 256 folded rows.
+//       Run as a single split over bf16 K/V, with the masks and the output
+//       given, it also takes the window keys as one more stage and writes
+//       the output itself (no window or merge launch).
 //   k_prefix_f32<D>  fp32 inputs, vector ALU, one wave per (row, split).
 //   k_window_mfma  bf16: one tile of window keys per kv head serves all its
 //       rows on MFMA, the masks applied in-kernel; writes the window partial
