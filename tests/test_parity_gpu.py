@@ -308,6 +308,42 @@ def test_phases_equal_one_call(shape):
     check_attention(out1, lse1, ro, rl, tag=shape)
 
 
+ONE_SPLIT_CASES = {
+    # (workload, prefix lengths or None, layout): every case runs the kernel for
+    # more than 128 folded rows as one split, so its prefix launch takes the
+    # window keys and writes the output
+    "d64": (gen.Workload("os1", 2, 300, 64, 16, 2, 64, "bf16", 16, "random", depth_cap=6), None, "HND"),
+    "empty_prefix": (gen.Workload("os2", 3, 500, 40, 16, 2, 128, "bf16", 16, "random", depth_cap=5),
+                     [500, 0, 37], "HND"),
+    "sliding": (gen.Workload("os3", 2, 2000, 64, 16, 2, 128, "bf16", 64, "random", depth_cap=8,
+                             prefix_window=200), None, "HND"),
+    "pages1": (gen.Workload("os4", 1, 300, 17, 32, 4, 128, "bf16", 1, "random", depth_cap=4), None, "HND"),
+    "pages2_nhd": (gen.Workload("os5", 2, 400, 33, 16, 2, 128, "bf16", 2, "random", depth_cap=5),
+                   [400, 251], "NHD"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(ONE_SPLIT_CASES))
+def test_one_split_window_in_prefix_launch(case):
+    # the prefix phase alone writes the output (so the fused path is the one
+    # that ran), and every row matches the oracle
+    wl, lens, layout = ONE_SPLIT_CASES[case]
+    say("case", case, wl)
+    inp = gen.make_inputs(wl, 21, "cuda", layout=layout,
+                          prefix_lens=None if lens is None else np.array(lens, np.int32))
+    m = oracle.build_masks(inp.parents)["masks"]
+    md = dev(m.view(np.int64), torch.int64)
+    out = torch.full_like(inp.q, float("nan"))
+    lse = torch.full((wl.B, wl.R, wl.Hq), float("nan"), dtype=torch.float32, device="cuda")
+    tav.tree_attention(inp.q, inp.k_cache, inp.v_cache, dev(inp.page_table), dev(inp.prefix_len), md,
+                       wl.W, max_prefix_len=int(inp.prefix_len.max()), layout=layout,
+                       prefix_window=wl.prefix_window, out=out, lse2=lse, phase="prefix")
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any(), case + ": the prefix launch did not write the output"
+    ro, rl = oracle_attention(inp, m)
+    check_attention(out, lse, ro, rl, tag=case)
+
+
 def test_nan_in_node_leaks_only_to_descendants():
     wl = gen.Workload("nan", 1, 200, 16, 8, 2, 128, "bf16", 16, "random", depth_cap=4)
     inp = gen.make_inputs(wl, 5, "cuda")
