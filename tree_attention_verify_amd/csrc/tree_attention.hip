@@ -49,7 +49,7 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kPtMax = 1024;        // page-table entries one split may span
+constexpr int kPtMax = 2560;        // page-table entries one split may span
 constexpr int kLdsStageBudget = 144 * 1024;
 constexpr int kPipeStageKeys = 64;   // keys per stage of the pipelined kernel (32 or 64)
 
