@@ -79,3 +79,9 @@ def test_noalloc_matches_tree_attention_twice():
 def test_noalloc_fp8_and_small_rows():
     one_call(gen.WORKLOADS["chain8_fp8"].with_(B=4, P=2000), 73, prefix_lens=[2000, 1, 64, 1999])
     one_call(gen.WORKLOADS["worked"], 74)
+
+
+def test_noalloc_one_split_window_in_prefix_launch():
+    # 512 folded rows in one split: the prefix launch takes the window keys
+    # and writes the output itself, for both entry points
+    one_call(gen.WORKLOADS["eagle64"].with_(B=2, P=300), 75, prefix_lens=[300, 0])
