@@ -260,7 +260,7 @@ struct MfmaCfg {
     static constexpr int CH = D / 8;              // 16-byte chunks per key row
     static constexpr int ROWB = D * 2;            // bytes per key row (bf16)
     static constexpr int SB = SK * ROWB * 2;      // stage bytes, K then V
-    static constexpr int NBUF0 = kLdsStageBudget / SB;
+    static constexpr int NBUF0 = (WAVES <= 2 ? 64 * 1024 : kLdsStageBudget) / SB;   // two 2-wave workgroups share a CU
     static constexpr int NBUF = NBUF0 > 8 ? 8 : NBUF0;
     static constexpr int LPS = SB / (THREADS * 16);   // 16-byte loads per thread per stage
     static_assert(NBUF >= 2, "stage too large");
@@ -407,10 +407,15 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
     // swizzle depend only on the key modulo 16, so its 32-bit offset is fixed.
     constexpr int KPI = 64 / CH;
     constexpr int LH = LPS / 2;   // loads per region (K, then V)
-    static_assert((THREADS / CH) % (D == 128 ? 16 : 8) == 0, "swizzle period divides a load's key step");
-    const uint32_t lane_off =
-        (uint32_t)((lane / CH) * a.stride_token * 2 +
-                   (((lane % CH) ^ swz<D>((w * 64 + lane) / CH)) * 16));
+    // (with fewer threads than 16 keys' chunks, loads j of even and odd j
+    // start at keys of either parity of 8, so a lane has two offsets)
+    constexpr int NOFF = (THREADS / CH) % (D == 128 ? 16 : 8) == 0 ? 1 : 2;
+    static_assert(NOFF == 1 || (2 * THREADS / CH) % (D == 128 ? 16 : 8) == 0, "swizzle period");
+    uint32_t lane_off[NOFF];
+#pragma unroll
+    for (int jp = 0; jp < NOFF; ++jp)
+        lane_off[jp] = (uint32_t)((lane / CH) * a.stride_token * 2 +
+                                  (((lane % CH) ^ swz<D>((jp * THREADS + w * 64 + lane) / CH)) * 16));
     auto issue = [&](int st) {
         const uint32_t sbase = lds0 + (uint32_t)((st % NBUF) * SB);
         const int kst = kb0 + st * SK;
@@ -433,7 +438,7 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
                                     (int64_t)g * a.stride_head + (int64_t)(k0 & ps_mask) * a.stride_token;
                 const uint16_t *base = (const uint16_t *)(i >= LH ? a.v : a.k) + off;
                 if (in)
-                    dma_load16_s(base, lane_off, sbase + (i * THREADS + w * 64) * 16);
+                    dma_load16_s(base, lane_off[j % NOFF], sbase + (i * THREADS + w * 64) * 16);
             }
         } else {
             int64_t page[LPS];
@@ -2217,7 +2222,7 @@ Plan make_plan(tav_dtype dtype, int B, int R, int Hq, int Hkv, int D, int max_pr
         p.NT = 1;
         if (M <= 32) {
             p.NRB = 1;
-            p.NKS = 4;
+            p.NKS = dtype == TAV_BF16 ? 2 : 4;
         } else if (M <= 64) {
             p.NRB = 2;
             p.NKS = 4;
@@ -2310,6 +2315,12 @@ void launch_mfma(const Plan &p, const PrefixArgs &a, hipStream_t s) {
 
 template <int D, bool KV8>
 void launch_mfma_d(const Plan &p, const PrefixArgs &a, hipStream_t s) {
+    if constexpr (!KV8) {
+        if (p.NRB == 1 && p.NKS == 2) {
+            launch_mfma<D, 1, 2, KV8>(p, a, s);
+            return;
+        }
+    }
     if (p.NRB == 1)
         launch_mfma<D, 1, 4, KV8>(p, a, s);
     else if (p.NRB == 2)
