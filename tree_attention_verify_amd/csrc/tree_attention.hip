@@ -271,7 +271,9 @@ struct MfmaCfg {
 // Split-K paged prefix decode on MFMA.  One workgroup = WAVES waves = NRB row
 // blocks of 32 folded query rows x NKS key subsets; every wave owns 32 rows
 // and, per stage, one 32-key block.  With 8 waves a SIMD holds two waves, so
-// one wave's MFMAs overlap the other's softmax.
+// one wave's MFMAs overlap the other's softmax; a 2-wave workgroup (bf16, at
+// most 32 rows) keeps two 32 KB stages, so that two workgroups share a CU and
+// one's prologue and epilogue overlap the other's stream.
 template <int D, int NRB, int NKS, bool KV8>
 __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a) {
     using C = MfmaCfg<D, NRB, NKS>;
