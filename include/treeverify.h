@@ -189,11 +189,12 @@ tav_status tree_attention(const void *q, const void *k_cache, const void *v_cach
  *   tree_attention_window_merge  reads the workspace partials of a preceding
  *                                tree_attention_prefix with the same arguments,
  *                                the window keys and masks; writes out and lse2
- * Except: when the prefix runs as a single split on the kernel for more than
- * 128 folded rows per kv head (bf16 K/V; the library picks the split count
- * from B, Hkv and the prefix length), and out and, for W > 0, masks are
- * given, tree_attention_prefix also attends the window keys and writes out
- * and lse2 itself, and tree_attention_window_merge then launches nothing.
+ * Except: when the prefix runs as a single split over bf16 K/V with at most
+ * 32 or more than 128 folded rows per kv head (R x Hq / Hkv; the library
+ * picks the split count from B, Hkv and the prefix length), and out and,
+ * for W > 0, masks are given, tree_attention_prefix also attends the window
+ * keys and writes out and lse2 itself, and tree_attention_window_merge then
+ * launches nothing.
  * The window keys are then one more stage of the prefix launch, with the
  * same semantics (a non-finite V value reaches exactly the rows that see
  * its key).

@@ -276,6 +276,8 @@ PHASE_SHAPES = {
     "pipe_splits": gen.Workload("ph2", 2, 3000, 64, 32, 8, 128, "bf16", 64, "random", depth_cap=8),
     # 64 folded rows (the small-row prefix kernel)
     "small_rows": gen.Workload("ph3", 3, 700, 16, 32, 8, 128, "bf16", 16, "random", depth_cap=6),
+    # 32 folded rows, one split (the window in the prefix launch)
+    "rows32_one_split": gen.Workload("ph4", 2, 300, 8, 8, 2, 128, "bf16", 16, "random", depth_cap=5),
 }
 
 
@@ -320,6 +322,12 @@ ONE_SPLIT_CASES = {
     "pages1": (gen.Workload("os4", 1, 300, 17, 32, 4, 128, "bf16", 1, "random", depth_cap=4), None, "HND"),
     "pages2_nhd": (gen.Workload("os5", 2, 400, 33, 16, 2, 128, "bf16", 2, "random", depth_cap=5),
                    [400, 251], "NHD"),
+    # the kernel for at most 32 folded rows, one split
+    "rows32": (gen.Workload("os6", 2, 300, 8, 8, 2, 128, "bf16", 16, "random", depth_cap=5), None, "HND"),
+    "rows16_d64_empty": (gen.Workload("os7", 3, 400, 4, 8, 2, 64, "bf16", 2, "random", depth_cap=3),
+                         [400, 0, 9], "HND"),
+    "rows32_sliding_nhd": (gen.Workload("os8", 2, 3000, 8, 16, 4, 128, "bf16", 64, "random", depth_cap=6,
+                                        prefix_window=150), None, "NHD"),
 }
 
 
@@ -377,12 +385,15 @@ def _same_nonfinite(ours, ref, tol, tag):
         assert np.abs(ours[fin] - ref[fin]).max() <= tol, tag
 
 
-@pytest.mark.parametrize("shape", ["rows64", "rows512"])
+@pytest.mark.parametrize("shape", ["rows24", "rows64", "rows512"])
 def test_nonfinite_window_values_reach_only_rows_that_see_them(shape):
     # window K NaN at node j1, V NaN at one channel of j2, V +inf and -inf at
     # one channel of j3 and j4: a row is non-finite exactly where the exact
-    # softmax over its own visible keys is
-    if shape == "rows64":
+    # softmax over its own visible keys is (rows24 and rows512 run as one
+    # split, with the window in the prefix launch)
+    if shape == "rows24":
+        wl = gen.Workload("nfw", 1, 200, 12, 4, 2, 128, "bf16", 16, "random", depth_cap=4)
+    elif shape == "rows64":
         wl = gen.Workload("nfw", 1, 200, 16, 8, 2, 128, "bf16", 16, "random", depth_cap=4)
     else:
         wl = gen.Workload("nfw", 2, 300, 64, 16, 2, 128, "bf16", 16, "random", depth_cap=6)

@@ -19,7 +19,9 @@
 //       NBUF stages deep; S^T = K Q^T and O^T = V^T P^T run on
 //       v_mfma_f32_32x32x16_bf16 with fp32 accumulation; softmax is online in
 //       the exp2 domain.  Writes one (O, lse2) partial per split (its NKS key
-//       subsets combined in LDS).
+//       subsets combined in LDS); with one row block over bf16 K/V run as a
+//       single split, it also takes the window keys as one more stage and
+//       writes the output itself.
 //   k_prefix_mfma_pipe  the software-pipelined kernel for 256 folded rows.
 //       Run as a single split over bf16 K/V, with the masks and the output
 //       given, it also takes the window keys as one more stage and writes
@@ -336,12 +338,32 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
     const int ks = w / NRB;    // this wave's key subset within a stage
     const int rows_base = rg * ROWS_WG + rbw * 32;
 
+    // A fused launch (one row block, bf16 K/V, one split, whose range ends
+    // at the prefix length P): the window keys P .. P + W - 1 are one more
+    // stage, and the page-table slice also covers their pages.
+    constexpr bool FUSE = !KV8 && NRB == 1;
+    int Pw = 0;
+    const bool wown = FUSE && a.fuse && a.W > 0;
+    if (wown) {
+        Pw = a.prefix_len[b];
+        Pw = Pw < 0 ? 0 : (Pw > a.max_prefix_len ? a.max_prefix_len : Pw);
+    }
+    __shared__ uint32_t wbad[2];   // window keys 0..31, 32..63 with a non-finite V value
+    __shared__ uint64_t wmk[FUSE ? 32 : 1];
+    if (tid < 2)
+        wbad[tid] = 0u;
+    if (wown && tid < 32) {
+        const int mm = rows_base + tid;
+        wmk[tid] = mm < a.M ? a.masks[(int64_t)b * a.R + mm / a.G] : 0ull;
+    }
+
     // page-table slice of this split: its entries are loaded into registers
     // first, the query loads go out behind them, and the entries are stored
     // to LDS after (so the stores wait for the table loads only, and the two
     // round trips overlap)
-    const int lp0 = nkeys > 0 ? (kb0 >> a.ps_shift) : 0;
-    const int npt = nkeys > 0 ? ((kr.hi - 1) >> a.ps_shift) - lp0 + 1 : 0;
+    const bool any_pt = nkeys > 0 || wown;
+    const int lp0 = any_pt ? ((nkeys > 0 ? kb0 : Pw) >> a.ps_shift) : 0;
+    const int npt = any_pt ? (((wown ? Pw + a.W : kr.hi) - 1) >> a.ps_shift) - lp0 + 1 : 0;
     constexpr int PTPT = (kPtMax + THREADS - 1) / THREADS;   // entries per thread, at most
     int64_t ptv[PTPT];
 #pragma unroll
@@ -456,6 +478,27 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
                     dma_load16(src_base[i] + page[i] * a.stride_page +
                                    (int64_t)(t & ps_mask) * a.stride_token,
                                __builtin_amdgcn_readfirstlane(sbase + (i * THREADS + w * 64) * 16));
+            }
+        }
+    };
+
+    // The window keys P .. P + W - 1 (a fused launch) as rows 0 .. W - 1 of
+    // one more stage, in buffer ns % NBUF, which no wave reads once the stage
+    // loop is done (stage ns - NBUF, or no stage); page per lane.  It is
+    // issued after the loop: inside it, its address arithmetic spilled the
+    // loop's scalar registers.  Rows W ..
+    // SK - 1 keep stale data: their scores are masked and their V values are
+    // made finite before use.
+    auto issue_window = [&]() {
+        const uint32_t sbase = lds0 + (uint32_t)((ns % NBUF) * SB);
+#pragma unroll
+        for (int i = 0; i < LPS; ++i) {
+            const int j = ld_key[i];
+            if (j < a.W) {
+                const int t = Pw + j;
+                const int64_t page = pt[(t >> a.ps_shift) - lp0];
+                dma_load16(src_base[i] + page * a.stride_page + (int64_t)(t & ps_mask) * a.stride_token,
+                           __builtin_amdgcn_readfirstlane(sbase + (i * THREADS + w * 64) * 16));
             }
         }
     };
@@ -616,12 +659,17 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
     const int key0 = ks * 32;
     const int krow = key0 + l32;                 // K operand: key of this lane
     const int ksw = swz<D>(krow);
-    // one stage of keys: S, softmax weights and O for this wave's 32 keys
-    auto compute = [&](int it) {
+    // the row's ancestor mask over the window keys (a fused launch)
+    uint64_t rmask = 0ull;
+    // one stage of keys: S, softmax weights and O for this wave's 32 keys;
+    // win: the window stage (keys P + key0 .. of buffer ns % NBUF), masked
+    // per row, with the weights split into a bf16 head and remainder (a row
+    // may weigh few window keys, whose rounding would not average out)
+    auto compute = [&](int it, bool win) {
         const char *Kb = KVD ? lds + (it % NBUF8) * SB8 : lds + (it % NBUF) * SB;
         const char *Vb = KVD ? Kb + SK * D : Kb + SB / 2;
         const int first = kb0 + it * SK + key0;  // absolute key of this wave's block
-        if (first >= kr.hi)
+        if (win ? key0 >= a.W : first >= kr.hi)
             return;
         // S^T[key][row] = sum_d K[key][d] Q[row][d]; FP8 rows: two E4M3 x
         // E4M3 steps of 64 channels (unit block scales), lane (key l32, half
@@ -655,8 +703,16 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[kk], s, 0, 0, 0);
             }
         }
-        // keys outside the split are not visible
-        if (first < kr.lo || first + 32 > kr.hi) {
+        // keys outside the split are not visible; a window key only to the
+        // rows whose mask has its bit
+        if (win) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = key0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+                if (!((rmask >> j) & 1ull))
+                    s[r] = -INFINITY;
+            }
+        } else if (first < kr.lo || first + 32 > kr.hi) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = first + 8 * (r >> 2) + 4 * hl + (r & 3);
@@ -685,13 +741,16 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
             m_run = mnew;
         }
         const float mu = m_run == -INFINITY ? 0.f : m_run;
-        bf16x8 pb[2];
+        bf16x8 pb[2], prm[2];
         float lsum = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const float pr = fast_exp2(fmaf(s[r], a.c, -mu));
             lsum += pr;
-            pb[r >> 3][r & 7] = (__bf16)pr;
+            const __bf16 ph = (__bf16)pr;
+            pb[r >> 3][r & 7] = ph;
+            if (win)
+                prm[r >> 3][r & 7] = (__bf16)(pr - (float)ph);
         }
         l_run += lsum;
         // O^T[d][row] += sum_key V[key][d] P[row][key].  The P operand is the
@@ -752,6 +811,8 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
                 } pair{half[0], half[1]};
                 const bf16x8 va = __builtin_bit_cast(bf16x8, pair);
                 o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[cc], o[t], 0, 0, 0);
+                if (win)
+                    o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, prm[cc], o[t], 0, 0, 0);
             }
         }
     };
@@ -767,7 +828,7 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
             __syncthreads();
             if (it + NBUF8 - 1 < ns)
                 issue8d(it + NBUF8 - 1);
-            compute(it);
+            compute(it, false);
         }
     } else if constexpr (KV8) {
         // Stage it was converted in the previous trip; after the barrier no
@@ -778,10 +839,10 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
         for (int it = 0; it < ns; it += 2) {
             __syncthreads();
             advance8(it, f8b);
-            compute(it);
+            compute(it, false);
             __syncthreads();
             advance8(it + 1, f8a);
-            compute(it + 1);
+            compute(it + 1, false);
         }
     } else {
         for (int it = 0; it < ns; ++it) {
@@ -796,7 +857,45 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
             __syncthreads();  // every wave's loads of stage it landed; stage it-1 is free
             if (it + NBUF - 1 < ns)
                 issue(it + NBUF - 1);
-            compute(it);
+            compute(it, false);
+        }
+    }
+
+    // The window stage (a fused launch): once it has landed its non-finite V
+    // values are set to 0 and their keys flagged, as in the window kernel;
+    // then each wave takes its 32 window keys like a prefix block.  A row
+    // that sees a flagged key gets those keys' non-finite values added to its
+    // output below, which is what the exact weighted sum gives.
+    if constexpr (FUSE) {
+        if (wown) {
+            issue_window();
+            wait_vmcnt<0>();
+            __syncthreads();
+            char *vw = lds + (ns % NBUF) * SB + SB / 2;
+            for (int i = tid; i < SB / 32; i += THREADS) {
+                const int key = (i * 16) / ROWB;
+                uint4 u4 = *(const uint4 *)(vw + i * 16);
+                uint32_t x[4] = {u4.x, u4.y, u4.z, u4.w};
+                bool nf = false;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
+                        if (((x[e] >> (16 * h2)) & 0x7F80u) == 0x7F80u) {
+                            nf = true;
+                            x[e] &= ~(0xFFFFu << (16 * h2));
+                        }
+                if (nf) {
+                    *(uint4 *)(vw + i * 16) = make_uint4(x[0], x[1], x[2], x[3]);
+                    if (key < a.W)
+                        atomicOr(&wbad[key >> 5], 1u << (key & 31));
+                }
+            }
+            __syncthreads();
+            rmask = wmk[l32];
+            if (a.W < 64)
+                rmask &= (1ull << a.W) - 1ull;
+            compute(ns, true);
         }
     }
 
@@ -840,6 +939,8 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
     const bool any = mx != -INFINITY;
     const float zinv = any ? 1.f / zs : 0.f;
     const int m = rows_base + l32;
+    const bool fout = FUSE && a.fuse;   // the only split of a fused launch: write the output
+    uint64_t vbad = rmask & (((uint64_t)wbad[1] << 32) | wbad[0]);
     if (m < a.M) {
         const int r = m / a.G, hh = m % a.G;
         const int64_t row = ((int64_t)b * a.R + r) * a.Hq + (int64_t)g * a.G + hh;
@@ -858,10 +959,40 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
             }
             const int t = u >> 2, q4 = u & 3;
             const int d = ((q4 >> 1) ? D / 2 : 0) + 16 * t + 8 * (q4 & 1) + 4 * hl;
-            *(float4 *)(dst + d) = make_float4(acc.x * zinv, acc.y * zinv, acc.z * zinv, acc.w * zinv);
+            float res[4] = {acc.x * zinv, acc.y * zinv, acc.z * zinv, acc.w * zinv};
+            if constexpr (FUSE) {
+                // visible window keys with non-finite V values (rare): add those values
+                for (uint64_t vb = vbad; vb; vb &= vb - 1) {
+                    const int t_ = Pw + __ffsll((unsigned long long)vb) - 1;
+                    const int64_t page =
+                        clamp_page(a.page_table[(int64_t)b * a.max_pages + (t_ >> a.ps_shift)], a.num_pages);
+                    const uint16_t *vr = (const uint16_t *)a.v + page * a.stride_page +
+                                         (int64_t)g * a.stride_head + (int64_t)(t_ & ps_mask) * a.stride_token;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = bf16_bits_to_f32(vr[d + e]);
+                        if (!(fabsf(x) < INFINITY))
+                            res[e] += x;
+                    }
+                }
+            }
+            if (fout) {
+                const uint32_t lo = f32_to_bf16_bits(res[0]) | ((uint32_t)f32_to_bf16_bits(res[1]) << 16);
+                const uint32_t hi = f32_to_bf16_bits(res[2]) | ((uint32_t)f32_to_bf16_bits(res[3]) << 16);
+                *(uint2 *)((uint16_t *)a.out + row * D + d) = make_uint2(lo, hi);
+            } else {
+                *(float4 *)(dst + d) = make_float4(res[0], res[1], res[2], res[3]);
+            }
         }
-        if (ks == 0 && hl == 0)
-            a.ws_lse[row * a.S + split] = any ? mx + __log2f(zs) : -INFINITY;
+        const float lse = any ? mx + __log2f(zs) : -INFINITY;
+        if (ks == 0 && hl == 0) {
+            if (fout) {
+                if (a.lse2)
+                    a.lse2[row] = lse;
+            } else {
+                a.ws_lse[row * a.S + split] = lse;
+            }
+        }
     }
 }
 
@@ -2464,8 +2595,8 @@ tav_status prepare(const char *fn, int phase, Call &call, const void *q, const v
     // the output given: the prefix launch takes the window keys too and
     // writes the output, and the window-and-merge phase launches nothing.
     // Both phases decide it from their (identical) arguments.
-    call.fused = dtype == TAV_BF16 && p.mfma && p.NRB == 8 && p.n_split == 1 && out != nullptr &&
-                 (W == 0 || masks != nullptr);
+    call.fused = dtype == TAV_BF16 && p.mfma && (p.NRB == 8 || p.NRB == 1) && p.n_split == 1 &&
+                 out != nullptr && (W == 0 || masks != nullptr);
     if (call.fused) {
         a.fuse = 1;
         a.W = W;
