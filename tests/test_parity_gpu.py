@@ -352,6 +352,48 @@ def test_one_split_window_in_prefix_launch(case):
     check_attention(out, lse, ro, rl, tag=case)
 
 
+MANY_SPLIT_CASES = {
+    # (workload, prefix lengths, bounds on the partials per row S): one kv head,
+    # so the prefix runs many splits, and the merge shares each row among 4
+    # (16 < S <= 64) or 8 (S > 64) waves; the second request is shorter, so
+    # its last splits are empty
+    "pipe_s95": (gen.Workload("ms1", 2, 30000, 64, 4, 1, 128, "bf16", 64, "random", depth_cap=8),
+                 [30000, 17001], (65, 10**9)),
+    "pipe_s39": (gen.Workload("ms2", 2, 12000, 64, 4, 1, 128, "bf16", 64, "random", depth_cap=8),
+                 [12000, 5000], (17, 64)),
+    "rows64_d64_s80": (gen.Workload("ms3", 2, 50000, 16, 4, 1, 64, "bf16", 16, "random", depth_cap=5),
+                       [50000, 20001], (65, 10**9)),
+    "rows64_d64_s20": (gen.Workload("ms4", 2, 12000, 16, 4, 1, 64, "bf16", 16, "random", depth_cap=5),
+                       [12000, 777], (17, 64)),
+    "fp8_pipe_s39": (gen.Workload("ms5", 2, 12000, 64, 4, 1, 128, "bf16", 64, "random", depth_cap=8,
+                                  kv_dtype="fp8"), [12000, 5000], (17, 64)),
+    # more than 128 partials: each of the 8 waves takes several rounds and
+    # rescales its sums when a later round raises its max
+    "pipe_s220": (gen.Workload("ms6", 1, 70000, 64, 4, 1, 128, "bf16", 64, "random", depth_cap=8),
+                  [70000], (129, 10**9)),
+    "rows64_d64_s158": (gen.Workload("ms7", 1, 100000, 16, 4, 1, 64, "bf16", 16, "random", depth_cap=5),
+                        [100000], (129, 10**9)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(MANY_SPLIT_CASES))
+def test_many_split_merge(case):
+    wl, pl, (s_lo, s_hi) = MANY_SPLIT_CASES[case]
+    say("case", case, wl, pl)
+    inp = gen.make_inputs(wl, 21, "cuda", prefix_lens=pl)
+    # the partial count the plan gives, read back from the workspace size
+    rows = wl.B * wl.R * wl.Hq
+    nbytes = tav.tree_attention_workspace_size(inp.q.dtype, wl.B, wl.R, wl.Hq, wl.Hkv, wl.D,
+                                               int(inp.prefix_len.max()), wl.prefix_window,
+                                               wl.page_size, inp.k_cache.dtype)
+    S = nbytes // (rows * (wl.D + 1) * 4)
+    assert s_lo <= S <= s_hi, (case, S)
+    m = oracle.build_masks(inp.parents)["masks"]
+    out, lse = run_attention(inp, dev(m.view(np.int64), torch.int64))
+    ro, rl = oracle_attention(inp, m)
+    check_attention(out, lse, ro, rl, tag="%s (S %d)" % (case, S))
+
+
 def test_nan_in_node_leaks_only_to_descendants():
     wl = gen.Workload("nan", 1, 200, 16, 8, 2, 128, "bf16", 16, "random", depth_cap=4)
     inp = gen.make_inputs(wl, 5, "cuda")

@@ -30,8 +30,9 @@
 //   k_window_mfma  bf16: one tile of window keys per kv head serves all its
 //       rows on MFMA, the masks applied in-kernel; writes the window partial
 //       (or, with a single prefix partial, merges the row itself).
-//   k_merge  bf16: one wave per (request, row, head) merges every partial
-//       through its base-2 LSE into out / lse2.
+//   k_merge  bf16: one wave per (request, row, head), or 4 or 8 waves per
+//       row with many splits, merges every partial through its base-2 LSE
+//       into out / lse2.
 //   k_window_merge  fp32: one wave per (request, row, head): the masked window
 //       keys (popcount(mask) of them, never the unseen ones) and the merge of
 //       every prefix partial with the window part into out / lse2.
@@ -2262,65 +2263,117 @@ __global__ void __launch_bounds__(64 * NW) k_window_mfma(MergeArgs a) {
         a.ws_lse[row * a.S + (a.S - 1)] = lse_w;
 }
 
+__device__ inline float nan_max(float x, float y) {
+    return (x != x || y != y) ? __builtin_nanf("") : fmaxf(x, y);
+}
+
 // Merge of the S partials of a row (prefix splits and the window, bf16
-// path): one wave per (request, row, head), lanes over channels.
+// path), lanes over channels.  SPL waves share a row: wave w takes partials
+// w, w + SPL, ...; with SPL = 1 a workgroup merges four rows, otherwise one.
 // lse2 = log2 sum_k 2^lse2_k, out = sum_k 2^(lse2_k - lse2) o_k; the max is
-// NaN-propagating, so a NaN partial makes the row NaN.
-template <int D>
-__global__ void __launch_bounds__(256) k_merge(MergeArgs a) {
+// NaN-propagating, so a NaN partial makes the row NaN.  A wave loads up to
+// 16 partials per round, their values and LSEs all in flight before the
+// first use, and weighs them against the largest LSE it has seen (rescaling
+// when a later round raises it); the waves' sums then combine in LDS against
+// the row's max.  A row whose partials fit one round thus costs one load
+// round trip.
+template <int D, int SPL>
+__global__ void __launch_bounds__(256 * (SPL > 4 ? SPL / 4 : 1)) k_merge(MergeArgs a) {
     constexpr int VPL = D / 64;
+    constexpr int RPW = SPL >= 4 ? 1 : 4 / SPL;   // rows per workgroup
+    constexpr int MB = 16;
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int wv = threadIdx.x >> 6;
+    const int part = wv % SPL;
+    const int64_t row = (int64_t)blockIdx.x * RPW + wv / SPL;
+    // (with SPL > 1 the grid holds exactly one workgroup per row, so this
+    // exit never splits a workgroup before its barrier)
     if (row >= (int64_t)a.B * a.R * a.Hq)
         return;
     const float *lp = a.ws_lse + row * a.S;
-    float mx = -INFINITY;
-    for (int s0 = 0; s0 < a.S; s0 += 64) {
-        float ls = s0 + lane < a.S ? lp[s0 + lane] : -INFINITY;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float y = __shfl_xor(ls, off);
-            ls = (ls != ls || y != y) ? __builtin_nanf("") : fmaxf(ls, y);
-        }
-        mx = (ls != ls || mx != mx) ? __builtin_nanf("") : fmaxf(mx, ls);
-    }
+    const float *op = a.ws_o + row * a.S * D + lane * VPL;
     float acc[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
         acc[i] = 0.f;
-    float res_lse = -INFINITY;
-    if (mx != -INFINITY) {
-        float zs = 0.f;
-        const float *op = a.ws_o + row * a.S * D + lane * VPL;
-        // MB partials per round, their loads all in flight before the first
-        // use (with many splits the merge is bound by load latency)
-        constexpr int MB = 16;
-        for (int s0 = 0; s0 < a.S; s0 += MB) {
-            float x[MB][VPL], ls[MB];
+    float m = -INFINITY, zs = 0.f;
+    for (int s0 = part; s0 < a.S; s0 += MB * SPL) {
+        float x[MB][VPL], ls[MB];
 #pragma unroll
-            for (int j = 0; j < MB; ++j) {
-                const bool in = s0 + j < a.S;
-                ls[j] = in ? lp[s0 + j] : -INFINITY;
+        for (int j = 0; j < MB; ++j) {
+            const int sj = s0 + j * SPL;
+            const bool in = sj < a.S;
+            ls[j] = in ? lp[sj] : -INFINITY;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i)
+                x[j][i] = in ? op[(int64_t)sj * D + i] : 0.f;
+        }
+        float mn = m;
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+            mn = nan_max(mn, ls[j]);
+        if (mn != m) {   // (also when either is NaN)
+            const float sc = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+            zs *= sc;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i)
+                acc[i] *= sc;
+            m = mn;
+        }
+        if (m == -INFINITY)
+            continue;
+#pragma unroll
+        for (int j = 0; j < MB; ++j) {
+            const float z = ls[j] != -INFINITY ? fast_exp2(ls[j] - m) : 0.f;
+            zs += z;
+            if (ls[j] != -INFINITY) {
 #pragma unroll
                 for (int i = 0; i < VPL; ++i)
-                    x[j][i] = in ? op[(int64_t)(s0 + j) * D + i] : 0.f;
-            }
-#pragma unroll
-            for (int j = 0; j < MB; ++j) {
-                const float z = ls[j] != -INFINITY ? fast_exp2(ls[j] - mx) : 0.f;
-                zs += z;
-                if (ls[j] != -INFINITY) {
-#pragma unroll
-                    for (int i = 0; i < VPL; ++i)
-                        acc[i] = fmaf(z, x[j][i], acc[i]);
-                }
+                    acc[i] = fmaf(z, x[j][i], acc[i]);
             }
         }
+    }
+    if constexpr (SPL > 1) {
+        __shared__ float red[SPL][D + 2];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            red[part][lane * VPL + i] = acc[i];
+        if (lane == 0) {
+            red[part][D] = zs;
+            red[part][D + 1] = m;
+        }
+        __syncthreads();
+        if (part != 0)
+            return;
+        float mw[SPL];
+        m = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < SPL; ++w) {
+            mw[w] = red[w][D + 1];
+            m = nan_max(m, mw[w]);
+        }
+        zs = 0.f;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            acc[i] = 0.f;
+        if (m != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < SPL; ++w) {
+                const float f = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - m);
+                zs = fmaf(f, red[w][D], zs);
+#pragma unroll
+                for (int i = 0; i < VPL; ++i)
+                    acc[i] = fmaf(f, red[w][lane * VPL + i], acc[i]);
+            }
+        }
+    }
+    float res_lse = -INFINITY;
+    if (m != -INFINITY) {
         const float inv = 1.f / zs;
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
             acc[i] *= inv;
-        res_lse = mx + __log2f(zs);
+        res_lse = m + __log2f(zs);
     }
     uint16_t *dst = (uint16_t *)a.out + row * D + lane * VPL;
     if (VPL == 2)
@@ -2641,6 +2694,20 @@ void launch_window_mfma_d(const MergeArgs &m, hipStream_t s) {
         launch_window_mfma<D, 4, KV8>(m, s);
 }
 
+// The bf16 merge: one wave per row up to 16 partials (one round of loads),
+// else 4 or 8 waves per row, so that each wave's share fits one round up to
+// 128 partials.
+template <int D>
+void launch_merge_d(const MergeArgs &m, hipStream_t s) {
+    const long long rows = (long long)m.B * m.R * m.Hq;
+    if (m.S <= 16)
+        hipLaunchKernelGGL((k_merge<D, 1>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, m);
+    else if (m.S <= 64)
+        hipLaunchKernelGGL((k_merge<D, 4>), dim3((unsigned)rows), dim3(256), 0, s, m);
+    else
+        hipLaunchKernelGGL((k_merge<D, 8>), dim3((unsigned)rows), dim3(512), 0, s, m);
+}
+
 void launch_merge(const Call &c, hipStream_t s) {
     const MergeArgs &m = c.m;
     const unsigned grid = (unsigned)(((long long)m.B * m.R * m.Hq + 3) / 4);
@@ -2649,11 +2716,11 @@ void launch_merge(const Call &c, hipStream_t s) {
         if (c.D == 128) {
             c.kv8 ? launch_window_mfma_d<128, true>(m, s) : launch_window_mfma_d<128, false>(m, s);
             if (m.S > 2)
-                hipLaunchKernelGGL(k_merge<128>, dim3(grid), dim3(256), 0, s, m);
+                launch_merge_d<128>(m, s);
         } else {
             c.kv8 ? launch_window_mfma_d<64, true>(m, s) : launch_window_mfma_d<64, false>(m, s);
             if (m.S > 2)
-                hipLaunchKernelGGL(k_merge<64>, dim3(grid), dim3(256), 0, s, m);
+                launch_merge_d<64>(m, s);
         }
         return;
     }
