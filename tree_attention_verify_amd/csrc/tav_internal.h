@@ -25,11 +25,16 @@ struct Checks {
             msg += "; ";
         msg += what;
     }
-    void need(bool ok, tav_status s, const std::string &what) {
-        if (!ok)
-            fail(s, what);
-    }
 };
+
+// TAV_NEED(checks, ok, status, message...): records the failure when `ok` is
+// false.  The message is formed only then, so a call whose arguments pass
+// builds no strings (host time per call matters for small launches).
+#define TAV_NEED(chk, ok, st, ...)            \
+    do {                                      \
+        if (!(ok))                            \
+            (chk).fail((st), __VA_ARGS__);    \
+    } while (0)
 
 void set_error(const char *fn, const std::string &msg);
 void clear_error();

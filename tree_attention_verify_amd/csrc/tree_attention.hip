@@ -2474,22 +2474,23 @@ bool shape_ok(tav_dtype dtype, int B, int R, int Hq, int Hkv, int D, int max_pre
     tav::Checks local;
     tav::Checks &k = c ? *c : local;
     using tav::str;
-    k.need(dtype == TAV_F32 || dtype == TAV_BF16 || dtype == TAV_FP8_E4M3, TAV_ERR_UNSUPPORTED,
-           "dtype must be TAV_F32, TAV_BF16 or TAV_FP8_E4M3, got " + str(dtype));
-    k.need(B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
-    k.need(R >= 1 && R <= 64, TAV_ERR_INVALID_ARG, "R must be in [1, 64], got " + str(R));
-    k.need(Hq >= 1 && Hkv >= 1, TAV_ERR_INVALID_ARG,
-           "Hq and Hkv must be >= 1, got " + str(Hq) + ", " + str(Hkv));
-    k.need(Hkv >= 1 && Hq % Hkv == 0, TAV_ERR_INVALID_ARG,
-           "Hq must be a multiple of Hkv, got " + str(Hq) + " % " + str(Hkv));
-    k.need(D == 64 || D == 128, TAV_ERR_UNSUPPORTED, "D must be 64 or 128, got " + str(D));
-    k.need(max_prefix_len >= 0, TAV_ERR_INVALID_ARG,
-           "max_prefix_len must be >= 0, got " + str(max_prefix_len));
-    k.need(prefix_window >= 0, TAV_ERR_INVALID_ARG,
-           "prefix_window must be >= 0, got " + str(prefix_window));
-    k.need(tav::is_pow2(page_size) && page_size <= 1024, TAV_ERR_UNSUPPORTED,
-           "page_size must be a power of two in [1, 1024], got " + str(page_size));
-    k.need((long long)B * R * Hq <= (1LL << 30), TAV_ERR_INVALID_ARG, "B * R * Hq is too large");
+    TAV_NEED(k, dtype == TAV_F32 || dtype == TAV_BF16 || dtype == TAV_FP8_E4M3, TAV_ERR_UNSUPPORTED,
+             "dtype must be TAV_F32, TAV_BF16 or TAV_FP8_E4M3, got " + str(dtype));
+    TAV_NEED(k, B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
+    TAV_NEED(k, R >= 1 && R <= 64, TAV_ERR_INVALID_ARG, "R must be in [1, 64], got " + str(R));
+    TAV_NEED(k, Hq >= 1 && Hkv >= 1, TAV_ERR_INVALID_ARG,
+             "Hq and Hkv must be >= 1, got " + str(Hq) + ", " + str(Hkv));
+    TAV_NEED(k, Hkv >= 1 && Hq % Hkv == 0, TAV_ERR_INVALID_ARG,
+             "Hq must be a multiple of Hkv, got " + str(Hq) + " % " + str(Hkv));
+    TAV_NEED(k, D == 64 || D == 128, TAV_ERR_UNSUPPORTED, "D must be 64 or 128, got " + str(D));
+    TAV_NEED(k, max_prefix_len >= 0, TAV_ERR_INVALID_ARG,
+             "max_prefix_len must be >= 0, got " + str(max_prefix_len));
+    TAV_NEED(k, prefix_window >= 0, TAV_ERR_INVALID_ARG,
+             "prefix_window must be >= 0, got " + str(prefix_window));
+    TAV_NEED(k, tav::is_pow2(page_size) && page_size <= 1024, TAV_ERR_UNSUPPORTED,
+             "page_size must be a power of two in [1, 1024], got " + str(page_size));
+    TAV_NEED(k, (long long)B * R * Hq <= (1LL << 30), TAV_ERR_INVALID_ARG,
+             "B * R * Hq is too large");
     return k.status == TAV_OK;
 }
 
@@ -2544,39 +2545,46 @@ tav_status prepare(const char *fn, int phase, Call &call, const void *q, const v
     using tav::str;
     tav::Checks c;
     shape_ok(dtype, B, R, Hq, Hkv, D, max_prefix_len, prefix_window, page_size, &c);
-    c.need(W >= 0 && W <= 64, TAV_ERR_INVALID_ARG, "W must be in [0, 64], got " + str(W));
-    c.need(max_pages >= 1, TAV_ERR_INVALID_ARG, "max_pages must be >= 1, got " + str(max_pages));
-    c.need((long long)max_pages * page_size >= (long long)max_prefix_len + W, TAV_ERR_INVALID_ARG,
-           "max_pages * page_size (" + str((long long)max_pages * page_size) +
-               ") must cover max_prefix_len + W (" + str((long long)max_prefix_len + W) + ")");
-    c.need(num_pages >= 1, TAV_ERR_INVALID_ARG, "num_pages must be >= 1, got " + str(num_pages));
-    c.need(std::isfinite(sm_scale), TAV_ERR_INVALID_ARG, "sm_scale must be finite");
+    TAV_NEED(c, W >= 0 && W <= 64, TAV_ERR_INVALID_ARG, "W must be in [0, 64], got " + str(W));
+    TAV_NEED(c, max_pages >= 1, TAV_ERR_INVALID_ARG,
+             "max_pages must be >= 1, got " + str(max_pages));
+    TAV_NEED(c, (long long)max_pages * page_size >= (long long)max_prefix_len + W,
+             TAV_ERR_INVALID_ARG,
+             "max_pages * page_size (" + str((long long)max_pages * page_size) +
+                 ") must cover max_prefix_len + W (" + str((long long)max_prefix_len + W) + ")");
+    TAV_NEED(c, num_pages >= 1, TAV_ERR_INVALID_ARG,
+             "num_pages must be >= 1, got " + str(num_pages));
+    TAV_NEED(c, std::isfinite(sm_scale), TAV_ERR_INVALID_ARG, "sm_scale must be finite");
     const int esz = dtype == TAV_F32 ? 4 : (dtype == TAV_FP8_E4M3 ? 1 : 2);   // K/V element bytes
-    c.need(stride_page >= 0 && stride_head >= 0 && stride_token >= 0, TAV_ERR_INVALID_ARG,
-           "strides must be >= 0");
-    c.need((stride_page * esz) % 16 == 0 && (stride_head * esz) % 16 == 0 &&
-               (stride_token * esz) % 16 == 0,
-           TAV_ERR_UNSUPPORTED, "K/V strides must be multiples of 16 bytes");
-    c.need(stride_token * esz < (1LL << 27), TAV_ERR_UNSUPPORTED,
-           "stride_token must be below 2^27 bytes");
+    TAV_NEED(c, stride_page >= 0 && stride_head >= 0 && stride_token >= 0, TAV_ERR_INVALID_ARG,
+             "strides must be >= 0");
+    TAV_NEED(c, (stride_page * esz) % 16 == 0 && (stride_head * esz) % 16 == 0 &&
+                 (stride_token * esz) % 16 == 0,
+             TAV_ERR_UNSUPPORTED, "K/V strides must be multiples of 16 bytes");
+    TAV_NEED(c, stride_token * esz < (1LL << 27), TAV_ERR_UNSUPPORTED,
+             "stride_token must be below 2^27 bytes");
     if (B > 0) {
-        c.need(q && k_cache && v_cache, TAV_ERR_INVALID_ARG, "q, k_cache and v_cache must be set");
-        c.need(page_table && prefix_len, TAV_ERR_INVALID_ARG, "page_table and prefix_len must be set");
+        TAV_NEED(c, q && k_cache && v_cache, TAV_ERR_INVALID_ARG,
+                 "q, k_cache and v_cache must be set");
+        TAV_NEED(c, page_table && prefix_len, TAV_ERR_INVALID_ARG,
+                 "page_table and prefix_len must be set");
         if (phase & 2) {
-            c.need(W == 0 || masks, TAV_ERR_INVALID_ARG, "masks is NULL");
-            c.need(out, TAV_ERR_INVALID_ARG, "out is NULL");
+            TAV_NEED(c, W == 0 || masks, TAV_ERR_INVALID_ARG, "masks is NULL");
+            TAV_NEED(c, out, TAV_ERR_INVALID_ARG, "out is NULL");
         }
-        c.need(workspace, TAV_ERR_WORKSPACE, "workspace is NULL");
-        c.need((((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15) == 0,
-               TAV_ERR_UNSUPPORTED, "q, k_cache, v_cache and out must be 16-byte aligned");
-        c.need(((uintptr_t)workspace & 255) == 0, TAV_ERR_WORKSPACE,
-               "workspace must be 256-byte aligned");
+        TAV_NEED(c, workspace, TAV_ERR_WORKSPACE, "workspace is NULL");
+        const uintptr_t any_addr =
+            (uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out;
+        TAV_NEED(c, (any_addr & 15) == 0, TAV_ERR_UNSUPPORTED,
+                 "q, k_cache, v_cache and out must be 16-byte aligned");
+        TAV_NEED(c, ((uintptr_t)workspace & 255) == 0, TAV_ERR_WORKSPACE,
+                 "workspace must be 256-byte aligned");
     }
     if (c.status == TAV_OK) {
         call.p = make_plan(dtype, B, R, Hq, Hkv, D, max_prefix_len, prefix_window, page_size);
-        c.need(workspace_bytes >= call.p.bytes, TAV_ERR_WORKSPACE,
-               "workspace has " + str((long long)workspace_bytes) + " bytes, needs " +
-                   str((long long)call.p.bytes));
+        TAV_NEED(c, workspace_bytes >= call.p.bytes, TAV_ERR_WORKSPACE,
+                 "workspace has " + str((long long)workspace_bytes) + " bytes, needs " +
+                     str((long long)call.p.bytes));
     }
     if (c.status != TAV_OK)
         return tav::finish(fn, c);
@@ -2852,11 +2860,11 @@ extern "C" tav_status tree_attention_noalloc(
     if (shape_ok(dtype, B, R, Hq, Hkv, D, max_prefix_len, prefix_window, page_size, &c)) {
         const size_t need =
             make_plan(dtype, B, R, Hq, Hkv, D, max_prefix_len, prefix_window, page_size).bytes;
-        c.need(need <= kScratchBytes, TAV_ERR_WORKSPACE,
-               "this shape needs " + tav::str((long long)need) +
-                   " bytes of partials, more than the static scratch array holds (" +
-                   tav::str((long long)kScratchBytes) +
-                   "); call tree_attention with a workspace instead");
+        TAV_NEED(c, need <= kScratchBytes, TAV_ERR_WORKSPACE,
+                 "this shape needs " + tav::str((long long)need) +
+                     " bytes of partials, more than the static scratch array holds (" +
+                     tav::str((long long)kScratchBytes) +
+                     "); call tree_attention with a workspace instead");
     }
     if (c.status != TAV_OK)
         return tav::finish(fn, c);

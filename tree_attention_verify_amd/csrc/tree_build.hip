@@ -271,19 +271,21 @@ extern "C" tav_status tree_beam_step(const float *scores, const int32_t *surv_id
                                      int32_t *pool_tokens, float *next_scores, int32_t *next_idx,
                                      void *stream) {
     Checks c;
-    c.need(B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
-    c.need(n_surv >= 1 && K >= 1, TAV_ERR_INVALID_ARG,
-           "n_surv and K must be >= 1, got " + str(n_surv) + ", " + str(K));
-    c.need((long long)n_surv * K <= kMaxBeamCands, TAV_ERR_UNSUPPORTED,
-           "n_surv * K must be <= " + str(kMaxBeamCands) + ", got " + str((long long)n_surv * K));
-    c.need(pool_base >= 0 && (long long)pool_base + (long long)n_surv * K <= C, TAV_ERR_INVALID_ARG,
-           "pool entries [pool_base, pool_base + n_surv * K) must lie in [0, C)");
+    TAV_NEED(c, B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
+    TAV_NEED(c, n_surv >= 1 && K >= 1, TAV_ERR_INVALID_ARG,
+             "n_surv and K must be >= 1, got " + str(n_surv) + ", " + str(K));
+    TAV_NEED(c, (long long)n_surv * K <= kMaxBeamCands, TAV_ERR_UNSUPPORTED,
+             "n_surv * K must be <= " + str(kMaxBeamCands) + ", got " + str((long long)n_surv * K));
+    TAV_NEED(c, pool_base >= 0 && (long long)pool_base + (long long)n_surv * K <= C,
+             TAV_ERR_INVALID_ARG,
+             "pool entries [pool_base, pool_base + n_surv * K) must lie in [0, C)");
     if (B > 0) {
-        c.need(scores && surv_idx && child_p && child_tok, TAV_ERR_INVALID_ARG,
-               "scores, surv_idx, child_p and child_tok must be set");
-        c.need(pool_scores && pool_parents && pool_tokens, TAV_ERR_INVALID_ARG,
-               "pool_scores, pool_parents and pool_tokens must be set");
-        c.need(next_scores && next_idx, TAV_ERR_INVALID_ARG, "next_scores and next_idx must be set");
+        TAV_NEED(c, scores && surv_idx && child_p && child_tok, TAV_ERR_INVALID_ARG,
+                 "scores, surv_idx, child_p and child_tok must be set");
+        TAV_NEED(c, pool_scores && pool_parents && pool_tokens, TAV_ERR_INVALID_ARG,
+                 "pool_scores, pool_parents and pool_tokens must be set");
+        TAV_NEED(c, next_scores && next_idx, TAV_ERR_INVALID_ARG,
+                 "next_scores and next_idx must be set");
     }
     if (c.status != TAV_OK || B == 0)
         return tav::finish("tree_beam_step", c);
@@ -300,19 +302,19 @@ extern "C" tav_status tree_select_candidates(const float *pool_scores, const int
                                              int32_t *tokens, int32_t *selected,
                                              int32_t *tree_error, void *stream) {
     Checks c;
-    c.need(B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
-    c.need(N >= 1 && N <= 64, TAV_ERR_INVALID_ARG, "N must be in [1, 64], got " + str(N));
-    c.need(C >= N - 1 && C >= 1, TAV_ERR_INVALID_ARG,
-           "C must be >= max(1, N - 1), got " + str(C));
-    c.need(C <= kMaxPool, TAV_ERR_UNSUPPORTED,
-           "C must be <= " + str(kMaxPool) + ", got " + str(C));
-    c.need(order == 0 || order == 1, TAV_ERR_INVALID_ARG,
-           "order must be 0 (pool order) or 1 (depth first), got " + str(order));
+    TAV_NEED(c, B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
+    TAV_NEED(c, N >= 1 && N <= 64, TAV_ERR_INVALID_ARG, "N must be in [1, 64], got " + str(N));
+    TAV_NEED(c, C >= N - 1 && C >= 1, TAV_ERR_INVALID_ARG,
+             "C must be >= max(1, N - 1), got " + str(C));
+    TAV_NEED(c, C <= kMaxPool, TAV_ERR_UNSUPPORTED,
+             "C must be <= " + str(kMaxPool) + ", got " + str(C));
+    TAV_NEED(c, order == 0 || order == 1, TAV_ERR_INVALID_ARG,
+             "order must be 0 (pool order) or 1 (depth first), got " + str(order));
     if (B > 0) {
-        c.need(pool_scores && pool_parents && pool_tokens && root_tokens, TAV_ERR_INVALID_ARG,
-               "pool_scores, pool_parents, pool_tokens and root_tokens must be set");
-        c.need(parents && tokens && selected, TAV_ERR_INVALID_ARG,
-               "parents, tokens and selected must be set");
+        TAV_NEED(c, pool_scores && pool_parents && pool_tokens && root_tokens, TAV_ERR_INVALID_ARG,
+                 "pool_scores, pool_parents, pool_tokens and root_tokens must be set");
+        TAV_NEED(c, parents && tokens && selected, TAV_ERR_INVALID_ARG,
+                 "parents, tokens and selected must be set");
     }
     if (c.status != TAV_OK || B == 0)
         return tav::finish("tree_select_candidates", c);
@@ -326,11 +328,11 @@ extern "C" tav_status tree_retrieve_links(const int32_t *parents, int32_t B, int
                                           int32_t *next_token, int32_t *next_sibling,
                                           void *stream) {
     Checks c;
-    c.need(B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
-    c.need(N >= 1 && N <= 64, TAV_ERR_INVALID_ARG, "N must be in [1, 64], got " + str(N));
+    TAV_NEED(c, B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
+    TAV_NEED(c, N >= 1 && N <= 64, TAV_ERR_INVALID_ARG, "N must be in [1, 64], got " + str(N));
     if (B > 0)
-        c.need(parents && next_token && next_sibling, TAV_ERR_INVALID_ARG,
-               "parents, next_token and next_sibling must be set");
+        TAV_NEED(c, parents && next_token && next_sibling, TAV_ERR_INVALID_ARG,
+                 "parents, next_token and next_sibling must be set");
     if (c.status != TAV_OK || B == 0)
         return tav::finish("tree_retrieve_links", c);
     hipLaunchKernelGGL(k_retrieve_links, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, S(stream),

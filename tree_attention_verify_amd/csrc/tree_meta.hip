@@ -217,12 +217,12 @@ extern "C" tav_status tree_build_masks(const int32_t *parents, int32_t B, int32_
                                        const int32_t *vc, int32_t *depth, uint64_t *masks,
                                        int32_t *positions, int32_t *tree_error, void *stream) {
     Checks c;
-    c.need(B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
-    c.need(N >= 1 && N <= 64, TAV_ERR_INVALID_ARG, "N must be in [1, 64], got " + str(N));
+    TAV_NEED(c, B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
+    TAV_NEED(c, N >= 1 && N <= 64, TAV_ERR_INVALID_ARG, "N must be in [1, 64], got " + str(N));
     if (B > 0) {
-        c.need(parents, TAV_ERR_INVALID_ARG, "parents is NULL");
-        c.need(depth, TAV_ERR_INVALID_ARG, "depth is NULL");
-        c.need(masks, TAV_ERR_INVALID_ARG, "masks is NULL");
+        TAV_NEED(c, parents, TAV_ERR_INVALID_ARG, "parents is NULL");
+        TAV_NEED(c, depth, TAV_ERR_INVALID_ARG, "depth is NULL");
+        TAV_NEED(c, masks, TAV_ERR_INVALID_ARG, "masks is NULL");
     }
     if (c.status != TAV_OK || B == 0)
         return tav::finish("tree_build_masks", c);
@@ -235,13 +235,13 @@ extern "C" tav_status tree_build_masks(const int32_t *parents, int32_t B, int32_
 extern "C" tav_status tree_shift_positions(int32_t *positions, const int32_t *depth, int32_t B,
                                            int32_t N, int32_t direction, void *stream) {
     Checks c;
-    c.need(B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
-    c.need(N >= 1 && N <= 64, TAV_ERR_INVALID_ARG, "N must be in [1, 64], got " + str(N));
-    c.need(direction == 1 || direction == -1, TAV_ERR_INVALID_ARG,
-           "direction must be +1 or -1, got " + str(direction));
+    TAV_NEED(c, B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
+    TAV_NEED(c, N >= 1 && N <= 64, TAV_ERR_INVALID_ARG, "N must be in [1, 64], got " + str(N));
+    TAV_NEED(c, direction == 1 || direction == -1, TAV_ERR_INVALID_ARG,
+             "direction must be +1 or -1, got " + str(direction));
     if (B > 0) {
-        c.need(positions, TAV_ERR_INVALID_ARG, "positions is NULL");
-        c.need(depth, TAV_ERR_INVALID_ARG, "depth is NULL");
+        TAV_NEED(c, positions, TAV_ERR_INVALID_ARG, "positions is NULL");
+        TAV_NEED(c, depth, TAV_ERR_INVALID_ARG, "depth is NULL");
     }
     if (c.status != TAV_OK || B == 0)
         return tav::finish("tree_shift_positions", c);
@@ -256,14 +256,14 @@ extern "C" tav_status verify_tree_greedy(const int32_t *draft_tokens, const int3
                                          int32_t *accepted_path, int32_t *accept_len,
                                          int32_t *accepted_tokens, void *stream) {
     Checks c;
-    c.need(B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
-    c.need(N >= 1 && N <= 64, TAV_ERR_INVALID_ARG, "N must be in [1, 64], got " + str(N));
+    TAV_NEED(c, B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
+    TAV_NEED(c, N >= 1 && N <= 64, TAV_ERR_INVALID_ARG, "N must be in [1, 64], got " + str(N));
     if (B > 0) {
-        c.need(draft_tokens, TAV_ERR_INVALID_ARG, "draft_tokens is NULL");
-        c.need(target_argmax, TAV_ERR_INVALID_ARG, "target_argmax is NULL");
-        c.need(parents, TAV_ERR_INVALID_ARG, "parents is NULL");
-        c.need(accepted_path, TAV_ERR_INVALID_ARG, "accepted_path is NULL");
-        c.need(accept_len, TAV_ERR_INVALID_ARG, "accept_len is NULL");
+        TAV_NEED(c, draft_tokens, TAV_ERR_INVALID_ARG, "draft_tokens is NULL");
+        TAV_NEED(c, target_argmax, TAV_ERR_INVALID_ARG, "target_argmax is NULL");
+        TAV_NEED(c, parents, TAV_ERR_INVALID_ARG, "parents is NULL");
+        TAV_NEED(c, accepted_path, TAV_ERR_INVALID_ARG, "accepted_path is NULL");
+        TAV_NEED(c, accept_len, TAV_ERR_INVALID_ARG, "accept_len is NULL");
     }
     if (c.status != TAV_OK || B == 0)
         return tav::finish("verify_tree_greedy", c);
@@ -278,33 +278,35 @@ extern "C" tav_status compact_window_rows(const tav_rows *tables, int32_t n_tabl
                                           const int32_t *accepted_path, const int32_t *accept_len,
                                           int32_t B, int32_t N, void *stream) {
     Checks c;
-    c.need(B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
-    c.need(N >= 1 && N <= 64, TAV_ERR_INVALID_ARG, "N must be in [1, 64], got " + str(N));
-    c.need(n_tables >= 0, TAV_ERR_INVALID_ARG, "n_tables must be >= 0, got " + str(n_tables));
-    c.need(n_tables == 0 || tables, TAV_ERR_INVALID_ARG, "tables is NULL");
+    TAV_NEED(c, B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
+    TAV_NEED(c, N >= 1 && N <= 64, TAV_ERR_INVALID_ARG, "N must be in [1, 64], got " + str(N));
+    TAV_NEED(c, n_tables >= 0, TAV_ERR_INVALID_ARG, "n_tables must be >= 0, got " + str(n_tables));
+    TAV_NEED(c, n_tables == 0 || tables, TAV_ERR_INVALID_ARG, "tables is NULL");
     if (B > 0 && n_tables > 0) {
-        c.need(accepted_path, TAV_ERR_INVALID_ARG, "accepted_path is NULL");
-        c.need(accept_len, TAV_ERR_INVALID_ARG, "accept_len is NULL");
+        TAV_NEED(c, accepted_path, TAV_ERR_INVALID_ARG, "accepted_path is NULL");
+        TAV_NEED(c, accept_len, TAV_ERR_INVALID_ARG, "accept_len is NULL");
     }
     for (int i = 0; tables && i < n_tables; ++i) {
         const tav_rows &t = tables[i];
         const std::string p = "tables[" + str(i) + "].";
-        c.need(t.base, TAV_ERR_INVALID_ARG, p + "base is NULL");
-        c.need(((uintptr_t)t.base & 3) == 0, TAV_ERR_INVALID_ARG, p + "base is not 4-byte aligned");
-        c.need(t.n_heads >= 1, TAV_ERR_INVALID_ARG, p + "n_heads must be >= 1");
-        c.need(t.row_bytes > 0 && t.row_bytes % 4 == 0, TAV_ERR_INVALID_ARG,
-               p + "row_bytes must be a positive multiple of 4, got " + str(t.row_bytes));
-        c.need((long long)t.n_heads * (t.row_bytes / 4) <= (1LL << 30), TAV_ERR_INVALID_ARG,
-               p + "n_heads * row_bytes is too large");
-        c.need(t.stride_token % 4 == 0 && t.stride_head % 4 == 0 && t.stride_page % 4 == 0 &&
-                   t.stride_batch % 4 == 0,
-               TAV_ERR_INVALID_ARG, p + "strides must be multiples of 4 bytes");
+        TAV_NEED(c, t.base, TAV_ERR_INVALID_ARG, p + "base is NULL");
+        TAV_NEED(c, ((uintptr_t)t.base & 3) == 0, TAV_ERR_INVALID_ARG,
+                 p + "base is not 4-byte aligned");
+        TAV_NEED(c, t.n_heads >= 1, TAV_ERR_INVALID_ARG, p + "n_heads must be >= 1");
+        TAV_NEED(c, t.row_bytes > 0 && t.row_bytes % 4 == 0, TAV_ERR_INVALID_ARG,
+                 p + "row_bytes must be a positive multiple of 4, got " + str(t.row_bytes));
+        TAV_NEED(c, (long long)t.n_heads * (t.row_bytes / 4) <= (1LL << 30), TAV_ERR_INVALID_ARG,
+                 p + "n_heads * row_bytes is too large");
+        TAV_NEED(c, t.stride_token % 4 == 0 && t.stride_head % 4 == 0 && t.stride_page % 4 == 0 &&
+                     t.stride_batch % 4 == 0,
+                 TAV_ERR_INVALID_ARG, p + "strides must be multiples of 4 bytes");
         if (t.page_table) {
-            c.need(t.prefix_len, TAV_ERR_INVALID_ARG, p + "prefix_len is NULL for a paged table");
-            c.need(t.max_pages >= 1, TAV_ERR_INVALID_ARG, p + "max_pages must be >= 1");
-            c.need(tav::is_pow2(t.page_size) && t.page_size <= 1024, TAV_ERR_INVALID_ARG,
-                   p + "page_size must be a power of two in [1, 1024], got " + str(t.page_size));
-            c.need(t.num_pages >= 1, TAV_ERR_INVALID_ARG, p + "num_pages must be >= 1");
+            TAV_NEED(c, t.prefix_len, TAV_ERR_INVALID_ARG,
+                     p + "prefix_len is NULL for a paged table");
+            TAV_NEED(c, t.max_pages >= 1, TAV_ERR_INVALID_ARG, p + "max_pages must be >= 1");
+            TAV_NEED(c, tav::is_pow2(t.page_size) && t.page_size <= 1024, TAV_ERR_INVALID_ARG,
+                     p + "page_size must be a power of two in [1, 1024], got " + str(t.page_size));
+            TAV_NEED(c, t.num_pages >= 1, TAV_ERR_INVALID_ARG, p + "num_pages must be >= 1");
         }
     }
     if (c.status != TAV_OK || B == 0 || n_tables == 0)

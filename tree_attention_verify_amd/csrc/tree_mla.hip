@@ -1010,38 +1010,38 @@ extern "C" tav_status tree_attention_mla(const void *q, const void *latent, tav_
                                          void *out, float *lse2, void *workspace,
                                          size_t workspace_bytes, void *stream) {
     Checks c;
-    c.need(B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
-    c.need(R >= 1 && R <= 64, TAV_ERR_INVALID_ARG, "R must be in [1, 64], got " + str(R));
-    c.need(W >= 0 && W <= 64, TAV_ERR_INVALID_ARG, "W must be in [0, 64], got " + str(W));
-    c.need(Hq >= 1, TAV_ERR_INVALID_ARG, "Hq must be >= 1, got " + str(Hq));
-    c.need(Dc == 512, TAV_ERR_UNSUPPORTED, "Dc (kv_lora_rank) must be 512, got " + str(Dc));
-    c.need(Dr == 0 || Dr == 64, TAV_ERR_UNSUPPORTED, "Dr must be 0 or 64, got " + str(Dr));
-    c.need(dtype == TAV_BF16 || dtype == TAV_FP8_E4M3, TAV_ERR_UNSUPPORTED,
-           "the latent cache must be TAV_BF16 or TAV_FP8_E4M3 (bf16 query), got " + str(dtype));
+    TAV_NEED(c, B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
+    TAV_NEED(c, R >= 1 && R <= 64, TAV_ERR_INVALID_ARG, "R must be in [1, 64], got " + str(R));
+    TAV_NEED(c, W >= 0 && W <= 64, TAV_ERR_INVALID_ARG, "W must be in [0, 64], got " + str(W));
+    TAV_NEED(c, Hq >= 1, TAV_ERR_INVALID_ARG, "Hq must be >= 1, got " + str(Hq));
+    TAV_NEED(c, Dc == 512, TAV_ERR_UNSUPPORTED, "Dc (kv_lora_rank) must be 512, got " + str(Dc));
+    TAV_NEED(c, Dr == 0 || Dr == 64, TAV_ERR_UNSUPPORTED, "Dr must be 0 or 64, got " + str(Dr));
+    TAV_NEED(c, dtype == TAV_BF16 || dtype == TAV_FP8_E4M3, TAV_ERR_UNSUPPORTED,
+             "the latent cache must be TAV_BF16 or TAV_FP8_E4M3 (bf16 query), got " + str(dtype));
     const int64_t elem = dtype == TAV_FP8_E4M3 ? 1 : 2;
-    c.need(tav::is_pow2(page_size) && page_size <= 1024, TAV_ERR_UNSUPPORTED,
-           "page_size must be a power of two <= 1024, got " + str(page_size));
-    c.need(max_prefix_len >= 0, TAV_ERR_INVALID_ARG, "max_prefix_len must be >= 0");
-    c.need(max_pages >= 1 && (long long)max_pages * page_size >= (long long)max_prefix_len + W,
-           TAV_ERR_INVALID_ARG, "max_pages * page_size must cover max_prefix_len + W");
-    c.need(num_pages >= 1, TAV_ERR_INVALID_ARG, "num_pages must be >= 1");
-    c.need(stride_token >= Dc + Dr && (stride_token * elem) % 16 == 0 &&
-               (stride_page * elem) % 16 == 0,
-           TAV_ERR_UNSUPPORTED,
-           "latent rows must hold Dc + Dr contiguous elements at 16-byte aligned strides");
-    c.need(std::isfinite(sm_scale), TAV_ERR_INVALID_ARG, "sm_scale must be finite");
+    TAV_NEED(c, tav::is_pow2(page_size) && page_size <= 1024, TAV_ERR_UNSUPPORTED,
+             "page_size must be a power of two <= 1024, got " + str(page_size));
+    TAV_NEED(c, max_prefix_len >= 0, TAV_ERR_INVALID_ARG, "max_prefix_len must be >= 0");
+    TAV_NEED(c, max_pages >= 1 && (long long)max_pages * page_size >= (long long)max_prefix_len + W,
+             TAV_ERR_INVALID_ARG, "max_pages * page_size must cover max_prefix_len + W");
+    TAV_NEED(c, num_pages >= 1, TAV_ERR_INVALID_ARG, "num_pages must be >= 1");
+    TAV_NEED(c, stride_token >= Dc + Dr && (stride_token * elem) % 16 == 0 &&
+                 (stride_page * elem) % 16 == 0,
+             TAV_ERR_UNSUPPORTED,
+             "latent rows must hold Dc + Dr contiguous elements at 16-byte aligned strides");
+    TAV_NEED(c, std::isfinite(sm_scale), TAV_ERR_INVALID_ARG, "sm_scale must be finite");
     if (B > 0) {
-        c.need(q && latent && page_table && prefix_len && masks && out, TAV_ERR_INVALID_ARG,
-               "q, latent, page_table, prefix_len, masks and out must be set");
-        c.need(((uintptr_t)q & 15) == 0 && ((uintptr_t)latent & 15) == 0 && ((uintptr_t)out & 15) == 0,
-               TAV_ERR_INVALID_ARG, "q, latent and out must be 16-byte aligned");
+        TAV_NEED(c, q && latent && page_table && prefix_len && masks && out, TAV_ERR_INVALID_ARG,
+                 "q, latent, page_table, prefix_len, masks and out must be set");
+        TAV_NEED(c, (((uintptr_t)q | (uintptr_t)latent | (uintptr_t)out) & 15) == 0,
+                 TAV_ERR_INVALID_ARG, "q, latent and out must be 16-byte aligned");
         if (c.status == TAV_OK) {
             const MlaPlan p = mla_plan(B, R, Hq, max_prefix_len, page_size);
-            c.need(workspace && ((uintptr_t)workspace & 255) == 0, TAV_ERR_WORKSPACE,
-                   "workspace must be set and 256-byte aligned");
-            c.need(workspace_bytes >= p.bytes, TAV_ERR_WORKSPACE,
-                   "workspace has " + str((long long)workspace_bytes) + " bytes, needs " +
-                       str((long long)p.bytes));
+            TAV_NEED(c, workspace && ((uintptr_t)workspace & 255) == 0, TAV_ERR_WORKSPACE,
+                     "workspace must be set and 256-byte aligned");
+            TAV_NEED(c, workspace_bytes >= p.bytes, TAV_ERR_WORKSPACE,
+                     "workspace has " + str((long long)workspace_bytes) + " bytes, needs " +
+                         str((long long)p.bytes));
         }
     }
     if (c.status != TAV_OK || B == 0)

@@ -952,32 +952,34 @@ extern "C" tav_status tree_sample_gumbel(const void *logits, tav_dtype dtype, in
                                          int32_t *tokens, void *workspace, size_t workspace_bytes,
                                          void *stream) {
     Checks c;
-    c.need(B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
-    c.need(N >= 1 && N <= 64, TAV_ERR_INVALID_ARG, "N must be in [1, 64], got " + str(N));
-    c.need(V >= 1, TAV_ERR_INVALID_ARG, "V must be >= 1, got " + str(V));
-    c.need(dtype == TAV_BF16 || dtype == TAV_F32, TAV_ERR_UNSUPPORTED,
-           "logits dtype must be TAV_BF16 or TAV_F32, got " + str(dtype));
+    TAV_NEED(c, B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
+    TAV_NEED(c, N >= 1 && N <= 64, TAV_ERR_INVALID_ARG, "N must be in [1, 64], got " + str(N));
+    TAV_NEED(c, V >= 1, TAV_ERR_INVALID_ARG, "V must be >= 1, got " + str(V));
+    TAV_NEED(c, dtype == TAV_BF16 || dtype == TAV_F32, TAV_ERR_UNSUPPORTED,
+             "logits dtype must be TAV_BF16 or TAV_F32, got " + str(dtype));
     const int elem = dtype == TAV_F32 ? 4 : 2;
-    c.need(row_stride >= V, TAV_ERR_INVALID_ARG,
-           "row_stride must be >= V, got " + str(row_stride) + " < " + str(V));
-    c.need((row_stride * elem) % 16 == 0, TAV_ERR_INVALID_ARG,
-           "row_stride must span a multiple of 16 bytes, got " + str(row_stride) + " elements");
-    c.need((long long)B * N * row_stride < (1LL << 62), TAV_ERR_INVALID_ARG, "logits too large");
+    TAV_NEED(c, row_stride >= V, TAV_ERR_INVALID_ARG,
+             "row_stride must be >= V, got " + str(row_stride) + " < " + str(V));
+    TAV_NEED(c, (row_stride * elem) % 16 == 0, TAV_ERR_INVALID_ARG,
+             "row_stride must span a multiple of 16 bytes, got " + str(row_stride) + " elements");
+    TAV_NEED(c, (long long)B * N * row_stride < (1LL << 62), TAV_ERR_INVALID_ARG,
+             "logits too large");
     if (B > 0) {
-        c.need(logits, TAV_ERR_INVALID_ARG, "logits is NULL");
-        c.need(((uintptr_t)logits & 15) == 0, TAV_ERR_INVALID_ARG, "logits is not 16-byte aligned");
-        c.need(temperature, TAV_ERR_INVALID_ARG, "temperature is NULL");
-        c.need(seed, TAV_ERR_INVALID_ARG, "seed is NULL");
-        c.need(positions, TAV_ERR_INVALID_ARG, "positions is NULL");
-        c.need(tokens, TAV_ERR_INVALID_ARG, "tokens is NULL");
+        TAV_NEED(c, logits, TAV_ERR_INVALID_ARG, "logits is NULL");
+        TAV_NEED(c, ((uintptr_t)logits & 15) == 0, TAV_ERR_INVALID_ARG,
+                 "logits is not 16-byte aligned");
+        TAV_NEED(c, temperature, TAV_ERR_INVALID_ARG, "temperature is NULL");
+        TAV_NEED(c, seed, TAV_ERR_INVALID_ARG, "seed is NULL");
+        TAV_NEED(c, positions, TAV_ERR_INVALID_ARG, "positions is NULL");
+        TAV_NEED(c, tokens, TAV_ERR_INVALID_ARG, "tokens is NULL");
         if (c.status == TAV_OK) {
             const SamplePlan p = sample_plan(B, N, V);
-            c.need(workspace, TAV_ERR_WORKSPACE, "workspace is NULL");
-            c.need(((uintptr_t)workspace & 255) == 0, TAV_ERR_WORKSPACE,
-                   "workspace is not 256-byte aligned");
-            c.need(workspace_bytes >= p.bytes, TAV_ERR_WORKSPACE,
-                   "workspace too small: " + str((long long)workspace_bytes) + " < " +
-                       str((long long)p.bytes) + " bytes");
+            TAV_NEED(c, workspace, TAV_ERR_WORKSPACE, "workspace is NULL");
+            TAV_NEED(c, ((uintptr_t)workspace & 255) == 0, TAV_ERR_WORKSPACE,
+                     "workspace is not 256-byte aligned");
+            TAV_NEED(c, workspace_bytes >= p.bytes, TAV_ERR_WORKSPACE,
+                     "workspace too small: " + str((long long)workspace_bytes) + " < " +
+                         str((long long)p.bytes) + " bytes");
         }
     }
     if (c.status != TAV_OK || B == 0)
@@ -1025,40 +1027,44 @@ extern "C" tav_status verify_tree_rejection(const float *probs, int64_t row_stri
                                             int32_t *accepted_tokens, void *workspace,
                                             size_t workspace_bytes, void *stream) {
     Checks c;
-    c.need(B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
-    c.need(N >= 1 && N <= 64, TAV_ERR_INVALID_ARG, "N must be in [1, 64], got " + str(N));
-    c.need(V >= 1 && V <= kRejMaxV, TAV_ERR_INVALID_ARG,
-           "V must be in [1, " + str(kRejMaxV) + "], got " + str(V));
-    c.need(row_stride >= V, TAV_ERR_INVALID_ARG,
-           "row_stride must be >= V, got " + str(row_stride) + " < " + str(V));
-    c.need(row_stride % 4 == 0, TAV_ERR_INVALID_ARG,
-           "row_stride must be a multiple of 4 elements, got " + str(row_stride));
-    c.need((long long)B * N * row_stride < (1LL << 62), TAV_ERR_INVALID_ARG, "probs too large");
+    TAV_NEED(c, B >= 0, TAV_ERR_INVALID_ARG, "B must be >= 0, got " + str(B));
+    TAV_NEED(c, N >= 1 && N <= 64, TAV_ERR_INVALID_ARG, "N must be in [1, 64], got " + str(N));
+    TAV_NEED(c, V >= 1 && V <= kRejMaxV, TAV_ERR_INVALID_ARG,
+             "V must be in [1, " + str(kRejMaxV) + "], got " + str(V));
+    TAV_NEED(c, row_stride >= V, TAV_ERR_INVALID_ARG,
+             "row_stride must be >= V, got " + str(row_stride) + " < " + str(V));
+    TAV_NEED(c, row_stride % 4 == 0, TAV_ERR_INVALID_ARG,
+             "row_stride must be a multiple of 4 elements, got " + str(row_stride));
+    TAV_NEED(c, (long long)B * N * row_stride < (1LL << 62), TAV_ERR_INVALID_ARG,
+             "probs too large");
     if (draft_q) {
-        c.need(q_row_stride >= V, TAV_ERR_INVALID_ARG,
-               "q_row_stride must be >= V, got " + str(q_row_stride) + " < " + str(V));
-        c.need(q_row_stride % 4 == 0, TAV_ERR_INVALID_ARG,
-               "q_row_stride must be a multiple of 4 elements, got " + str(q_row_stride));
-        c.need(((uintptr_t)draft_q & 15) == 0, TAV_ERR_INVALID_ARG, "draft_q is not 16-byte aligned");
-        c.need((long long)B * N * q_row_stride < (1LL << 62), TAV_ERR_INVALID_ARG, "draft_q too large");
+        TAV_NEED(c, q_row_stride >= V, TAV_ERR_INVALID_ARG,
+                 "q_row_stride must be >= V, got " + str(q_row_stride) + " < " + str(V));
+        TAV_NEED(c, q_row_stride % 4 == 0, TAV_ERR_INVALID_ARG,
+                 "q_row_stride must be a multiple of 4 elements, got " + str(q_row_stride));
+        TAV_NEED(c, ((uintptr_t)draft_q & 15) == 0, TAV_ERR_INVALID_ARG,
+                 "draft_q is not 16-byte aligned");
+        TAV_NEED(c, (long long)B * N * q_row_stride < (1LL << 62), TAV_ERR_INVALID_ARG,
+                 "draft_q too large");
     }
     if (B > 0) {
-        c.need(probs, TAV_ERR_INVALID_ARG, "probs is NULL");
-        c.need(((uintptr_t)probs & 15) == 0, TAV_ERR_INVALID_ARG, "probs is not 16-byte aligned");
-        c.need(draft_tokens, TAV_ERR_INVALID_ARG, "draft_tokens is NULL");
-        c.need(parents, TAV_ERR_INVALID_ARG, "parents is NULL");
-        c.need(coins, TAV_ERR_INVALID_ARG, "coins is NULL");
-        c.need(bonus_u, TAV_ERR_INVALID_ARG, "bonus_u is NULL");
-        c.need(accepted_path, TAV_ERR_INVALID_ARG, "accepted_path is NULL");
-        c.need(accept_len, TAV_ERR_INVALID_ARG, "accept_len is NULL");
+        TAV_NEED(c, probs, TAV_ERR_INVALID_ARG, "probs is NULL");
+        TAV_NEED(c, ((uintptr_t)probs & 15) == 0, TAV_ERR_INVALID_ARG,
+                 "probs is not 16-byte aligned");
+        TAV_NEED(c, draft_tokens, TAV_ERR_INVALID_ARG, "draft_tokens is NULL");
+        TAV_NEED(c, parents, TAV_ERR_INVALID_ARG, "parents is NULL");
+        TAV_NEED(c, coins, TAV_ERR_INVALID_ARG, "coins is NULL");
+        TAV_NEED(c, bonus_u, TAV_ERR_INVALID_ARG, "bonus_u is NULL");
+        TAV_NEED(c, accepted_path, TAV_ERR_INVALID_ARG, "accepted_path is NULL");
+        TAV_NEED(c, accept_len, TAV_ERR_INVALID_ARG, "accept_len is NULL");
         if (c.status == TAV_OK) {
             const RejPlan p = rej_plan(B, V);
-            c.need(workspace, TAV_ERR_WORKSPACE, "workspace is NULL");
-            c.need(((uintptr_t)workspace & 255) == 0, TAV_ERR_WORKSPACE,
-                   "workspace is not 256-byte aligned");
-            c.need(workspace_bytes >= p.bytes, TAV_ERR_WORKSPACE,
-                   "workspace too small: " + str((long long)workspace_bytes) + " < " +
-                       str((long long)p.bytes) + " bytes");
+            TAV_NEED(c, workspace, TAV_ERR_WORKSPACE, "workspace is NULL");
+            TAV_NEED(c, ((uintptr_t)workspace & 255) == 0, TAV_ERR_WORKSPACE,
+                     "workspace is not 256-byte aligned");
+            TAV_NEED(c, workspace_bytes >= p.bytes, TAV_ERR_WORKSPACE,
+                     "workspace too small: " + str((long long)workspace_bytes) + " < " +
+                         str((long long)p.bytes) + " bytes");
         }
     }
     if (c.status != TAV_OK || B == 0)
