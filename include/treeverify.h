@@ -6,7 +6,8 @@
  *                        the tree from the drafter's candidate pool
  *   tree_build_masks     parents -> depth, 64-bit ancestor masks, positions
  *   tree_attention       paged prefix + masked tree window -> out, base-2 LSE
- *   tree_attention_mla   the same cascade over an MLA latent cache
+ *   tree_attention_mla   prefix + window + merge with K and V read from one
+ *                        MLA latent row per token
  *   verify_tree_greedy   draft tokens, target argmax -> accepted path
  *   tree_sample_gumbel   logits -> target draws keyed by (seed, position),
  *                        for the sampled verify
@@ -429,7 +430,7 @@ tav_status verify_tree_rejection(const float *probs, int64_t row_stride, int32_t
                                  size_t workspace_bytes, void *stream);
 
 /*
- * The same cascade over an MLA latent cache ([DTS] "One tree attention ...",
+ * Prefix, window and merge as in tree_attention, over an MLA latent cache ([DTS] "One tree attention ...",
  * the MLA paragraph).  Each token stores one latent row, shared by every
  * query head: its first Dc channels (kv_lora_rank) meet the query's first Dc
  * channels in the score and are also the value; its Dr rotary channels

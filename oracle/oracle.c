@@ -860,7 +860,7 @@ int orc_retrieve_links(const int32_t *parents, int B, int N, int32_t *next_token
 }
 
 /* ------------------------------------------------------------------ */
-/* MLA: the same cascade over a latent cache                            */
+/* MLA: prefix + window + merge, K and V both from one latent row      */
 /* ------------------------------------------------------------------ */
 
 /*

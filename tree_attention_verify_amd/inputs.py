@@ -499,7 +499,7 @@ class MlaWorkload:
     P: int
     N: int
     Hq: int
-    Dc: int          # kv_lora_rank: latent channels (the key's latent part and the value)
+    Dc: int          # kv_lora_rank: latent channels (scored against the query, and read as V)
     Dr: int          # rotary channels of the key
     page_size: int
     depth_cap: int = 6
