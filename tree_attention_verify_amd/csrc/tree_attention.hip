@@ -1005,7 +1005,14 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
 // weights of block u, then the S MFMAs of block u + 1, so the MFMA pipe
 // works while the vector ALU computes exponentials (two waves per SIMD fill
 // each other's gaps); each MFMA operand is read from LDS one phase ahead of
-// its use.
+// its use.  The stage barrier would line both waves of a SIMD up on the same
+// phase (both computing weights, then both waiting on their S chains), so
+// waves 4..7, which share the SIMDs of waves 0..3 (waves are placed on the
+// SIMDs round-robin), meet it before reading V and issuing the S chain
+// instead of after: after each barrier one wave of a SIMD computes weights
+// while the other runs its S MFMAs.  Either position is safe: a wave's reads
+// of the stage being freed (the two blocks before the current one) are
+// complete at both.
 // The softmax reference max mu is taken from the first block and raised only
 // when the running sum of weights would pass kSumLimit (rare): weights are
 // bf16 with the fp32 exponent range and accumulate in fp32, so their
@@ -1486,10 +1493,14 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);    // weights VALU
         }
         check(s, pb_cur, lb);
+        // waves 4..7 meet the stage barrier half a block before waves 0..3
+        const bool early = !KV8 && w >= 4;
+        if (early && new_stage && u + 2 < nb)
+            stage_ready((u + 2) / BPS);
         load_v(u, va);
         s = qk(ka);
         if (u + 2 < nb) {
-            if (new_stage)
+            if (new_stage && !early)
                 stage_ready((u + 2) / BPS);
             load_k(u + 2, ka);
         }
