@@ -254,7 +254,7 @@ tav_status tree_attention_noalloc(const void *q, const void *k_cache, const void
 
 /*
  * Greedy tree verify ([MEM] "Walking the accepted path"): from the root, move
- * to the child whose draft token equals the target's argmax at the current
+ * to the child whose draft token matches the target's argmax at the current
  * node; stop when no child matches.  Ties between children carrying the same
  * token go to the lowest node index.  The walk takes at most N nodes.
  *
@@ -499,8 +499,9 @@ tav_status tree_attention_mla(const void *q, const void *latent, tav_dtype dtype
  *   pool_scores float [B][C], pool_parents int32 [B][C] (-1 = root; a parent
  *              must precede its child), pool_tokens int32 [B][C]
  *   root_tokens int32 [B]
- *   order      0: nodes in pool order; 1: depth first, each node's best
- *              child first ([DTS]: the most likely path is 0, 1, 2, ...)
+ *   order      0: nodes in pool order; 1: depth-first order visiting a
+ *              node's higher-scoring child first ([DTS]: the top path is
+ *              then numbered 0, 1, 2, ...)
  *   parents, tokens int32 [B][N] out: the tree (parents[i] < i) and its
  *              tokens; selected int32 [B][N] out: each node's pool index (-1
  *              for the root)

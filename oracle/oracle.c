@@ -257,9 +257,9 @@ static void orc_softmax_row(const void *qb, int64_t qofs, const void *kb,
  * q holds dtype elements, k_cache and v_cache kv_dtype elements.  An FP8
  * cache takes a bf16 query: prefix keys are scored with the query rounded
  * to E4M3, window keys with the bf16 query itself ([DTS] "One tree
- * attention ...": the leaf's decode takes the query cast to FP8, while the
- * window kernel takes the unquantised query and widens the window's FP8
- * K/V after loading them).
+ * attention ...": the leaf's decode rounds the query to FP8, while the
+ * window part keeps the query unrounded and converts the window's FP8 keys
+ * and values once loaded).
  * rows: optional list of flat row ids ((b*R + r)*Hq + h); out/lse2 then hold
  * n_rows entries in list order.  With rows == NULL every row is computed and
  * out is [B][R][Hq][D], lse2 [B][R][Hq].
@@ -326,8 +326,8 @@ int orc_tree_attention(const void *q, const void *k_cache, const void *v_cache,
  * Plain causal attention on contiguous keys: q is [n][Hq][D], k and v are
  * [L][Hkv][D].  Query row i sits at position L - n + i and sees keys
  * t <= L - n + i, in ascending order.  Used by the pins: a chain tree must
- * equal this ([DTS] "The tree is a parameter of the chain path": a chain is
- * the tree parent[i] = i - 1), and each tree row must equal the last row of
+ * equal this ([DTS] "The tree is a parameter of the chain path": the chain
+ * is the special tree with parent[i] = i - 1), and each tree row must equal the last row of
  * this run on prefix + its own root-to-node path ([ETA] section 1,
  * L(v) = Target(prefix + path(root -> v))).
  */
@@ -706,8 +706,9 @@ int orc_beam_step(const float *scores, const int32_t *surv_idx, const float *chi
  *
  * The N - 1 best candidates by orc_cand_before are kept.  order 0 numbers
  * them by ascending pool index (the pool order); order 1 numbers the tree
- * depth first with each node's best child first ([DTS] "Tree construction
- * is deterministic": the most likely path is then 0, 1, 2, ...).  Node 0 is
+ * in depth-first order, a node's higher-scoring child before its others
+ * ([DTS] "Tree construction is deterministic": the top path is then
+ * numbered 0, 1, 2, ...).  Node 0 is
  * the root with token root_tokens[b]; parents[b][i] is the node of entry
  * i's parent; selected[b][i] is entry i's pool index (-1 for the root).
  * Every kept candidate's parent must be kept or be the root ([MEM] "a

@@ -785,8 +785,9 @@ def test_gumbel_scores_and_special_values():
 
 def test_sampled_chain_verify_accepts_matching_drafts():
     """A chain whose draft tokens are the draws of their parents' rows is
-    accepted whole ([DTS]: acceptance is the greedy tree walk over the draws,
-    accepting a child when it equals its parent's draw)."""
+    accepted whole ([DTS] "Sampled verify keys noise by position": the greedy
+    walk runs over the draws, and a child is taken when its token is its
+    parent's draw)."""
     rng = np.random.default_rng(8)
     N, V = 8, 64
     logits = rng.standard_normal((1, N, V)).astype(np.float32)
@@ -1128,8 +1129,9 @@ def test_select_candidates_against_brute_force():
 
 
 def test_depth_first_best_child_first_numbering():
-    """[DTS]: depth first, each node's best child first, so the most likely
-    path is 0, 1, 2, ...; every subtree occupies a contiguous block."""
+    """[DTS] "Tree construction is deterministic": depth-first numbering with
+    the higher-scoring child first puts the top path at 0, 1, 2, ...; every
+    subtree occupies a contiguous block."""
     rng = np.random.default_rng(10)
     for trial in range(100):
         C = int(rng.integers(8, 80))

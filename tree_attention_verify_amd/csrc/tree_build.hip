@@ -7,8 +7,8 @@
 //                      "EAGLE-2: the tree stops being a constant").
 //   k_select_tree      the N - 1 best candidates of a request's pool, the
 //                      previous bonus token prepended as node 0, numbered in
-//                      pool order or depth first with each node's best child
-//                      first; closure is checked ("Draft-tree speculation",
+//                      pool order or depth first, a node's higher-scoring
+//                      child before its others; closure is checked ("Draft-tree speculation",
 //                      "Tree construction is deterministic"; the course
 //                      chapter's organize_draft_results; "a missing parent is
 //                      rejected, never treated as a root").

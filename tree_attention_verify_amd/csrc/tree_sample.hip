@@ -6,9 +6,9 @@
 //     draft distribution that drew each node's children), further below.
 //
 // "Draft-tree speculation", section "Sampled verify keys noise by position":
-// a verify row draws its target token by Gumbel-max keyed by (seed,
-// position), where for a tree the position is the one the node predicts,
-// vc + depth + 1, never the row; acceptance is then the greedy tree walk
+// each verify row's target token is a Gumbel-max draw whose noise is
+// indexed by the request's seed and a position, for a tree the position the
+// node predicts (vc + depth + 1) rather than its row; acceptance is then the greedy tree walk
 // over the draws (verify_tree_greedy with the draws as the target tokens).
 //
 // Noise: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011) with counter
