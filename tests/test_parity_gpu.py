@@ -394,6 +394,90 @@ def test_many_split_merge(case):
     check_attention(out, lse, ro, rl, tag="%s (S %d)" % (case, S))
 
 
+# Few splits: with one prefix partial (S = 2 with the window's) the window
+# kernel merges it itself, with more the merge kernel runs.  Two requests
+# over 8 kv heads leave room for 16 splits, so P = 512 k gives k splits of
+# the 64-row kernel (four 128-key stages each) and S = k + 1.
+FEW_SPLIT_CASES = {
+    "rows64_s%d" % (k + 1): (gen.Workload("fs%d" % k, 2, 512 * k, 16, 32, 8, 128, "bf16", 16,
+                                          "random", depth_cap=6), k + 1)
+    for k in (1, 2, 3, 4, 5)
+}
+FEW_SPLIT_CASES.update({
+    "fp8_rows64_s4": (gen.Workload("fs_fp8", 2, 1536, 16, 32, 8, 128, "bf16", 16, "random",
+                                   depth_cap=6, kv_dtype="fp8"), 4),
+    "d64_rows64_s3": (gen.Workload("fs_d64", 2, 1024, 16, 32, 8, 64, "bf16", 16, "random",
+                                   depth_cap=6), 3),
+    # 256 folded rows (the pipelined kernel): 64-key stages, 3 splits
+    "rows256_s4": (gen.Workload("fs_pipe", 2, 768, 64, 32, 8, 128, "bf16", 64, "random",
+                                depth_cap=8), 4),
+})
+
+
+def _partials_per_row(inp):
+    wl = inp.wl
+    nbytes = tav.tree_attention_workspace_size(inp.q.dtype, wl.B, wl.R, wl.Hq, wl.Hkv, wl.D,
+                                               int(inp.prefix_len.max()), wl.prefix_window,
+                                               wl.page_size, inp.k_cache.dtype)
+    return nbytes // (wl.B * wl.R * wl.Hq * (wl.D + 1) * 4)
+
+
+@pytest.mark.parametrize("case", sorted(FEW_SPLIT_CASES))
+def test_few_split_merge(case):
+    wl, S_want = FEW_SPLIT_CASES[case]
+    P = wl.P
+    inp = gen.make_inputs(wl, 23, "cuda", prefix_lens=[P, P // 3 + 5])
+    S = _partials_per_row(inp)
+    say("case", case, wl, "S", S)
+    assert S == S_want, (case, S)
+    m = oracle.build_masks(inp.parents)["masks"]
+    out, lse = run_attention(inp, dev(m.view(np.int64), torch.int64))
+    ro, rl = oracle_attention(inp, m)
+    check_attention(out, lse, ro, rl, tag="%s (S %d)" % (case, S))
+
+
+@pytest.mark.parametrize("k", [2, 5])
+def test_nonfinite_prefix_values_through_the_merge(k):
+    # request 0, kv head 0: NaN in one prefix key's K, and in prefix V channel
+    # 77 one +inf and one -inf (NaN) and in channel 5 one +inf (+inf), in
+    # different splits; every row of that head sees every prefix key, so the
+    # whole head is NaN (the NaN key) -- with the K NaN left out, channel 77
+    # is NaN, channel 5 +inf and the rest finite.  The merge kernel combines
+    # the S = 3 and S = 6 partials of a row.
+    wl = FEW_SPLIT_CASES["rows64_s%d" % (k + 1)][0]
+    for with_k_nan in (False, True):
+        inp = gen.make_inputs(wl, 29, "cuda", prefix_lens=[wl.P, wl.P // 3 + 5])
+        assert _partials_per_row(inp) == k + 1
+
+        def slot(t):
+            return int(inp.page_table[0, t // wl.page_size]), t % wl.page_size
+
+        P0 = int(inp.prefix_len[0])
+        pg, sl = slot(3)
+        inp.v_cache[pg, 0, sl, 77] = float("inf")
+        pg, sl = slot(P0 - 2)
+        inp.v_cache[pg, 0, sl, 77] = float("-inf")
+        pg, sl = slot(P0 // 2)
+        inp.v_cache[pg, 0, sl, 5] = float("inf")
+        if with_k_nan:
+            pg, sl = slot(P0 // 3)
+            inp.k_cache[pg, 0, sl] = float("nan")
+        m = oracle.build_masks(inp.parents)["masks"]
+        out, lse = run_attention(inp, dev(m.view(np.int64), torch.int64))
+        ro, rl = oracle_attention(inp, m)
+        tag = "S %d, K NaN %s" % (k + 1, with_k_nan)
+        o = out.float().cpu().numpy()
+        _same_nonfinite(o, ro.reshape(out.shape), OUT_TOL, tag + " out")
+        _same_nonfinite(lse.cpu().numpy(), rl.reshape(lse.shape), LSE_TOL, tag + " lse2")
+        G = wl.Hq // wl.Hkv
+        head0 = o[0, :, :G]
+        if with_k_nan:
+            assert np.isnan(head0).all(), tag
+        else:
+            assert np.isnan(head0[..., 77]).all() and np.isposinf(head0[..., 5]).all(), tag
+        assert np.isfinite(o[1]).all() and np.isfinite(o[0, :, G:]).all(), tag
+
+
 def test_nan_in_node_leaks_only_to_descendants():
     wl = gen.Workload("nan", 1, 200, 16, 8, 2, 128, "bf16", 16, "random", depth_cap=4)
     inp = gen.make_inputs(wl, 5, "cuda")
