@@ -100,20 +100,22 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // streaming them past the caches costs less energy per byte, and the chip
 // runs this kernel at its board power limit.
 __device__ __forceinline__ void dma_load16(const void *src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
-                 :
+    int m0v;   // m0 is an output, so the compiler keeps no value of its own there
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                 : "={m0}"(m0v)
                  : "v"(src), "s"(lds_base)
-                 : "memory", "m0");
+                 : "memory");
 }
 
 // Direct-to-LDS 16-byte load with a wave-uniform 64-bit base and a per-lane
 // 32-bit byte offset; lane i's 16 bytes land at LDS byte lds_base + 16 i.
 // Completion is tracked as for dma_load16.
 __device__ __forceinline__ void dma_load16_s(const void *base, uint32_t voff, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-                 :
+    int m0v;   // m0 is an output, so the compiler keeps no value of its own there
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 : "={m0}"(m0v)
                  : "v"(voff), "s"(base), "s"(lds_base)
-                 : "memory", "m0");
+                 : "memory");
 }
 
 // 16 FP8 E4M3 values (one 16-byte chunk) -> 16 bf16 values (two chunks);

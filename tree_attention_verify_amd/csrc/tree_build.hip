@@ -34,9 +34,6 @@ constexpr int kMaxPool = 8192;          // candidates per request
 
 // Lane j's value in every lane (j wave-uniform): v_readlane, no LDS trip.
 __device__ inline int lane_val(int x, int j) { return __builtin_amdgcn_readlane(x, j); }
-__device__ inline float lane_val(float x, int j) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
-}
 __device__ inline uint64_t lane_val(uint64_t x, int j) {
     return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(x >> 32), j) << 32) |
            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, j);
@@ -52,9 +49,6 @@ __device__ inline int order_key(float s) {
 }
 __device__ inline bool before_k(int ka, int a, int kb, int b) {
     return ka > kb || (ka == kb && a < b);
-}
-__device__ inline bool before(float sa, int a, float sb, int b) {
-    return before_k(order_key(sa), a, order_key(sb), b);
 }
 
 // Rank of candidate (z, id) in an LDS array of n scores: how many come

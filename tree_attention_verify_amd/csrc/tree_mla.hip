@@ -66,10 +66,11 @@ __device__ inline uint16_t mla_bf16_bits(float f) {
 // 16 i; completion by vmcnt then a workgroup barrier (see the prefix kernel
 // of tree_attention.hip for why it is inline assembly).
 __device__ __forceinline__ void mla_dma16(const void *src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
-                 :
+    int m0v;   // m0 is an output, so the compiler keeps no value of its own there
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                 : "={m0}"(m0v)
                  : "v"(src), "s"(lds_base)
-                 : "memory", "m0");
+                 : "memory");
 }
 
 template <int N>
