@@ -114,12 +114,19 @@ def summarize_traffic(workload, fetch_dir, write_dir, cmd):
     print(json.dumps(t))
 
 
-def summarize_stats(workload, stats_dir, cmd):
+MLA_SRC = os.path.join(ROOT, "tree_attention_verify_amd", "csrc", "tree_mla.hip")
+
+
+def summarize_stats(workload, stats_dir, cmd, mla=False):
+    """profiles/<workload>_kernel_stats.md from a rocprofv3 --kernel-trace
+    --stats run (an MLA workload with mla=True)."""
     rows = _csv_rows(os.path.join(stats_dir, "**", "*kernel_stats.csv"))
     os.makedirs(PROFILES, exist_ok=True)
     out = os.path.join(PROFILES, "%s_kernel_stats.md" % workload)
+    title = ("MLA cascade, workload %s" % gen.MLA_WORKLOADS[workload].describe()) if mla \
+        else "workload %s" % workload
     with open(out, "w") as f:
-        f.write("# rocprofv3 kernel statistics, workload %s\n\nCommand:\n\n    %s\n\n" % (workload, cmd))
+        f.write("# rocprofv3 kernel statistics, %s\n\nCommand:\n\n    %s\n\n" % (title, cmd))
         f.write("| kernel | calls | average (us) | min (us) | max (us) | share |\n|---|---|---|---|---|---|\n")
         for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
             name = r["Name"]
@@ -127,11 +134,25 @@ def summarize_stats(workload, stats_dir, cmd):
             f.write("| %s | %s | %.1f | %.1f | %.1f | %.1f%% |\n" % (
                 name.replace("|", "/"), r["Calls"], float(r["AverageNs"]) / 1e3,
                 float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
-        f.write("\nThe at::native and __amd_rocclr kernels are the seeded input generation and "
-                "host-to-device copies before the timed region; the path's kernels count every "
-                "step run: the untimed settle steps (back to back for 2 s, so the board runs at "
-                "its steady clock), the warm-up and the timed steps.  Kernel source "
-                "sha256[:16] %s.\n" % kernel_hash())
+        if mla:
+            f.write("\nThe at::native and __amd_rocclr kernels are the seeded input generation and "
+                    "host-to-device copies before the timed region; the MLA kernels count every "
+                    "call: the untimed settle calls (back to back for 2 s), the warm-up and the "
+                    "timed calls.  tree_mla.hip sha256[:16] %s.\n\n" % kernel_hash(MLA_SRC))
+            f.write("k_mla_prefix is the split-K prefix over the latent rows (8 waves per 64 rows: "
+                    "each scores one 16 x 16 tile on v_mfma_f32_16x16x32_bf16 and, in the same "
+                    "pass, accumulates 64 value channels of the previous block); "
+                    "k_mla_window_merge is the masked window and the merge. Under the FP8 latent "
+                    "cache (KV8 = true) raw E4M3 rows land in a two-slot ring; at the end of a "
+                    "trip each lane takes the chunks it loaded into registers and at the top of "
+                    "the next widens them into the bf16 stage layout; the query is rounded to "
+                    "E4M3 for every key.\n")
+        else:
+            f.write("\nThe at::native and __amd_rocclr kernels are the seeded input generation and "
+                    "host-to-device copies before the timed region; the path's kernels count every "
+                    "step run: the untimed settle steps (back to back for 2 s, so the board runs at "
+                    "its steady clock), the warm-up and the timed steps.  Kernel source "
+                    "sha256[:16] %s.\n" % kernel_hash())
     print(open(out).read())
 
 
@@ -948,7 +969,7 @@ def main():
         summarize_traffic(args.workload, *args.summarize_traffic)
         return
     if args.summarize_stats:
-        summarize_stats(args.workload, *args.summarize_stats)
+        summarize_stats(args.mla or args.workload, *args.summarize_stats, mla=bool(args.mla))
         return
     if args.summarize_power:
         summarize_power(*args.summarize_power)
