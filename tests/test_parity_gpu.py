@@ -478,6 +478,40 @@ def test_nonfinite_prefix_values_through_the_merge(k):
         assert np.isfinite(o[1]).all() and np.isfinite(o[0, :, G:]).all(), tag
 
 
+# A split whose last stage is partial leaves the stage rows past its end
+# unloaded; with more stages than stage buffers those rows hold an earlier
+# stage's keys.  Their weight is exactly 0, so a +-inf V value there must not
+# turn into 0 * inf = NaN: prefix key 150 carries +inf in channel 5, the
+# stage ring brings it back into the unloaded rows of the last stage, and
+# every row of kv head 0 must still read +inf there (as the oracle does).
+STALE_ROW_CASES = {
+    # 256 folded rows (pipelined kernel, one split: window in the same launch),
+    # 64-key stages in 4 buffers, 401 keys: stage 6 reuses stage 2's buffer
+    "rows256": gen.Workload("stale256", 1, 401, 64, 32, 8, 128, "bf16", 16, "random", depth_cap=8),
+    # 64 folded rows: 128-key stages in 2 buffers, stage 3 reuses stage 1's
+    "rows64": gen.Workload("stale64", 1, 401, 16, 32, 8, 128, "bf16", 16, "random", depth_cap=6),
+    # 32 folded rows (2-wave workgroups): 64-key stages in 2 buffers
+    "rows32": gen.Workload("stale32", 1, 209, 8, 32, 8, 128, "bf16", 16, "chain"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(STALE_ROW_CASES))
+def test_inf_values_in_reused_stage_rows(case):
+    wl = STALE_ROW_CASES[case]
+    inp = gen.make_inputs(wl, 31, "cuda")
+    key = 150 if case != "rows32" else 90
+    pg = int(inp.page_table[0, key // wl.page_size])
+    inp.v_cache[pg, 0, key % wl.page_size, 5] = float("inf")
+    m = oracle.build_masks(inp.parents)["masks"]
+    out, lse = run_attention(inp, dev(m.view(np.int64), torch.int64))
+    ro, rl = oracle_attention(inp, m)
+    o = out.float().cpu().numpy()
+    _same_nonfinite(o, ro.reshape(out.shape), OUT_TOL, case + " out")
+    _same_nonfinite(lse.cpu().numpy(), rl.reshape(lse.shape), LSE_TOL, case + " lse2")
+    G = wl.Hq // wl.Hkv
+    assert np.isposinf(o[0, :, :G, 5]).all(), case
+
+
 def test_nan_in_node_leaks_only_to_descendants():
     wl = gen.Workload("nan", 1, 200, 16, 8, 2, 128, "bf16", 16, "random", depth_cap=4)
     inp = gen.make_inputs(wl, 5, "cuda")

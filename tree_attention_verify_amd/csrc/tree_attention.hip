@@ -668,7 +668,9 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
     // win: the window stage (keys P + key0 .. of buffer ns % NBUF), masked
     // per row, with the weights split into a bf16 head and remainder (a row
     // may weigh few window keys, whose rounding would not average out)
-    auto compute = [&](int it, bool win) {
+    // last: the last stage over bf16 K/V, whose rows past the split end are
+    // not loaded (see the V operand below)
+    auto compute = [&](int it, bool win, bool last) {
         const char *Kb = KVD ? lds + (it % NBUF8) * SB8 : lds + (it % NBUF) * SB;
         const char *Vb = KVD ? Kb + SK * D : Kb + SB / 2;
         const int first = kb0 + it * SK + key0;  // absolute key of this wave's block
@@ -796,6 +798,14 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
             }
             return;
         }
+        // A block of the last stage reaching past the split end has rows that
+        // were not loaded; once the stage ring has come round they hold an
+        // earlier stage's keys, whose weight here is exactly 0, and a +-inf V
+        // value among them would turn into 0 * inf = NaN: those operand
+        // elements are zeroed.  Element e of the V^T operand of chunk cc is
+        // key 16 cc + 4 hl + 8 (e / 4) + e % 4 of the block.  (The last stage
+        // runs outside the stage loop, so the loop carries none of this.)
+        const int vlim = kr.hi - first - 4 * hl;
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
             const int d0 = ((G16 & 1) ? D / 2 : 0) + 16 * t + 4 * a4;
@@ -812,7 +822,13 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
                 struct {
                     i16x4 lo, hi;
                 } pair{half[0], half[1]};
-                const bf16x8 va = __builtin_bit_cast(bf16x8, pair);
+                bf16x8 va = __builtin_bit_cast(bf16x8, pair);
+                if (last && first + 32 > kr.hi) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (16 * cc + 8 * (e >> 2) + (e & 3) >= vlim)
+                            va[e] = (__bf16)0.f;
+                }
                 o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[cc], o[t], 0, 0, 0);
                 if (win)
                     o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, prm[cc], o[t], 0, 0, 0);
@@ -831,7 +847,7 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
             __syncthreads();
             if (it + NBUF8 - 1 < ns)
                 issue8d(it + NBUF8 - 1);
-            compute(it, false);
+            compute(it, false, false);
         }
     } else if constexpr (KV8) {
         // Stage it was converted in the previous trip; after the barrier no
@@ -842,13 +858,13 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
         for (int it = 0; it < ns; it += 2) {
             __syncthreads();
             advance8(it, f8b);
-            compute(it, false);
+            compute(it, false, false);
             __syncthreads();
             advance8(it + 1, f8a);
-            compute(it + 1, false);
+            compute(it + 1, false, false);
         }
     } else {
-        for (int it = 0; it < ns; ++it) {
+        for (int it = 0; it < ns - 1; ++it) {
             // Stage `it` is complete once at most the loads of the later, full
             // stages are outstanding.  When the last (partial) stage is among
             // the outstanding ones some of its instructions may be skipped, so
@@ -860,7 +876,13 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
             __syncthreads();  // every wave's loads of stage it landed; stage it-1 is free
             if (it + NBUF - 1 < ns)
                 issue(it + NBUF - 1);
-            compute(it, false);
+            compute(it, false, false);
+        }
+        if (ns > 0) {
+            // the last stage (nothing left to issue)
+            wait_vmcnt<0>();
+            __syncthreads();
+            compute(ns - 1, false, true);
         }
     }
 
@@ -898,7 +920,7 @@ __global__ void __launch_bounds__(64 * NRB * NKS, 1) k_prefix_mfma(PrefixArgs a)
             rmask = wmk[l32];
             if (a.W < 64)
                 rmask &= (1ull << a.W) - 1ull;
-            compute(ns, true);
+            compute(ns, true, false);
         }
     }
 
@@ -1580,6 +1602,22 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
             weights(s, pbb, lb);
             check(s, pbb, lb);
             load_v(nb - 1, va);
+            // Its rows past the split end are not loaded; once the stage ring
+            // has come round they hold an earlier stage's keys, whose weight
+            // here is exactly 0, and a +-inf V value among them would turn
+            // into 0 * inf = NaN.  Element e of a V^T operand is key 16 cc +
+            // 4 hl + 8 (e / 4) + e % 4 of the block (the P operand's order).
+            {
+                const int lim = kr.hi - (kb0 + (nb - 1) * 32 + 4 * hl);
+#pragma unroll
+                for (int t = 0; t < DT; ++t)
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (16 * cc + 8 * (e >> 2) + (e & 3) >= lim)
+                                va[t][cc][e] = (__bf16)0.f;
+            }
             pv(va, pbb);
         }
     }
