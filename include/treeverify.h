@@ -151,10 +151,10 @@ size_t tree_attention_workspace_size(tav_dtype dtype, int32_t B, int32_t R, int3
  * B >= 0; 1 <= R <= 64; 0 <= W <= 64; Hq % Hkv == 0; D in {64, 128}
  * dtype      TAV_BF16 (bf16 MFMA prefix, fp32 accumulation), TAV_F32
  *            (fp32 vector-ALU path) or TAV_FP8_E4M3: an unscaled FP8 E4M3
- *            K/V cache with a bf16 query ([DTS] "One tree attention ...": an
- *            FP8 cache changes no structure; the prefix decode takes the
- *            query cast to FP8, the window kernel the unquantised query and
- *            the window's K/V widened).  Prefix keys are scored with the
+ *            K/V cache with a bf16 query ([DTS] "One tree attention ...": FP8
+ *            leaves the cascade's structure as it is; the prefix decode
+ *            rounds the query to FP8, the window part keeps it unrounded and
+ *            widens the window's keys and values).  Prefix keys are scored with the
  *            query rounded to the nearest E4M3 value (ties to even,
  *            saturating at +-448), window keys with the bf16 query; keys
  *            and values are widened exactly to bf16, so every product is

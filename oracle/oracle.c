@@ -78,8 +78,8 @@ double orc_e4m3_decode(int code)
  * NaN.  Written as a search over the 127 non-negative finite codes, whose
  * values increase with the code.  This is the cast of the query that the
  * prefix half of the cascade takes under an FP8 cache ([DTS] "One tree
- * attention ...": the leaf's decode takes the query cast to FP8, the window
- * kernel the unquantised query).
+ * attention ...": the leaf's decode rounds the query to FP8, the window
+ * part keeps it unrounded).
  */
 double orc_e4m3_round(double x)
 {
@@ -242,8 +242,8 @@ static void orc_softmax_row(const void *qb, int64_t qofs, const void *kb,
  *   - the committed prefix: logical positions t in [p_lo, P), where P =
  *     prefix_len[b] and p_lo = max(0, P - prefix_window) when
  *     prefix_window > 0, else 0 ([ETA] section 1: every row sees the
- *     committed prefix; [DTS] "One tree attention ...": a sliding-window
- *     draft layer sees the window frozen at the round's prefix end);
+ *     committed prefix; [DTS] "One tree attention ...": a draft layer with
+ *     a sliding window sees it as it stood at the end of the round's prefix);
  *   - then window node j, stored at logical position P + j, for j < W in
  *     ascending order with bit j of masks[b*R + r] set ([DTS] "One tree
  *     attention ...": the 64-bit ancestor mask covers the last W keys;
@@ -630,8 +630,8 @@ int orc_sample_gumbel(const void *logits, int dtype, int64_t row_stride, int V, 
 
 /* Candidate order of the tree construction: the higher score first, then the
  * lower candidate id; a NaN score ranks after every number ([DTS] "Tree
- * construction is deterministic": ties go to the lower candidate id, NaN
- * scores rank last).  Returns 1 when candidate a comes before b. */
+ * construction is deterministic": equal scores are ordered by candidate id,
+ * NaN after all numbers).  Returns 1 when candidate a comes before b. */
 static int orc_cand_before(float sa, int a, float sb, int b)
 {
     int na = isnan(sa), nb = isnan(sb);
@@ -644,9 +644,8 @@ static int orc_cand_before(float sa, int a, float sb, int b)
 
 /*
  * One EAGLE-2 expansion step for every request ([MEM] "EAGLE-2: the tree
- * stops being a constant": the surviving paths' cumulative scores are
- * multiplied by the new conditional probabilities and the best topk paths
- * are kept; [ETA] "candidate pool to verify rows": score_list / token_list /
+ * stops being a constant": each surviving path's cumulative score times
+ * each child's conditional probability, of which the topk best survive; [ETA] "candidate pool to verify rows": score_list / token_list /
  * parents_list, cumulative path scores).  Survivor s (score scores[b][s],
  * pool index surv_idx[b][s], -1 for the root) has K children with
  * conditional probabilities child_p[b][s][j] and tokens child_tok[b][s][j].
@@ -711,8 +710,9 @@ int orc_beam_step(const float *scores, const int32_t *surv_idx, const float *chi
  * numbered 0, 1, 2, ...).  Node 0 is
  * the root with token root_tokens[b]; parents[b][i] is the node of entry
  * i's parent; selected[b][i] is entry i's pool index (-1 for the root).
- * Every kept candidate's parent must be kept or be the root ([MEM] "a
- * missing parent must be rejected or repaired, never treated as a root"),
+ * Every kept candidate's parent must be kept or be the root ([MEM]
+ * "Building the mask, for real": a candidate whose parent was dropped is
+ * refused or fixed, never promoted to a root),
  * and must precede it in the pool (as every expansion step appends after
  * the candidates it expands);
  * otherwise tree_error[b] = 1 + the first node (in pool order) whose parent
@@ -828,8 +828,8 @@ int orc_select_candidates(const float *pool_scores, const int32_t *pool_parents,
 
 /*
  * First-child / next-sibling links of every tree ([MEM] "Flattening, and the
- * two link arrays": retrieve_next_token[p] is p's first child,
- * retrieve_next_sibling[i] is i's next sibling; [DDT] compile_ddtree_retrieve).
+ * two link arrays": retrieve_next_token[p] names the first child of p and
+ * retrieve_next_sibling[i] the sibling after i; [DDT] compile_ddtree_retrieve).
  * Children are taken in node order (with depth-first best-child-first
  * numbering, or pool order, that is the order the trees are numbered in);
  * -1 where there is none.

@@ -930,8 +930,9 @@ def test_rejection_bonus_is_the_inverse_cdf():
 
 
 def test_rejection_against_q_emits_the_target_law():
-    """[DTS] "Sampled verify keys noise by position": recursive rejection
-    sampling against the draft q that drew a node's children is exact.
+    """[DTS] "Sampled verify keys noise by position": rejection sampling over
+    a node's children, against the q they were drawn from, yields the target
+    distribution exactly.
     40000 walks: the root's three children and node 1's two are drawn
     independently from their parent's q each time and tried in index order;
     the first emitted token follows the root's target law and the second,

@@ -251,7 +251,7 @@ SamplePlan sample_plan(int B, int N, int V) {
 // finite entries, else 0), S its total and E the weight of the distinct
 // tokens already rejected there, which leave the residual; the walk ends
 // with a bonus token drawn from the residual by inverse CDF.
-// Against the draft q that drew the children: at node cur r_0 = w / S and
+// Against the drafter's q for the children: at node cur r_0 = w / S and
 // q^ = q / Q (positive finite entries); child i (token x) in the trying
 // order is accepted when coin * q^(x) < r_i(x), else r_{i+1} = max(0, r_i -
 // q^) / Z_{i+1}.  r_i(v) depends only on w(v), q(v), S, Q and Z_1 .. Z_i, so

@@ -150,8 +150,8 @@ def eagle_tree(rng, topk: int, steps: int, N: int) -> np.ndarray:
     into topk children.  Child probabilities are Dirichlet(1) per parent and a
     candidate's score is the product along its path (fp64).  The N - 1 best
     candidates by (-score, pool index) are kept, sorted by pool index, and the
-    root is prepended as node 0.  Parents precede children in pool order and a
-    child's score is below its parent's, so the kept set is closed."""
+    root is prepended as node 0.  Parents precede children in pool order and
+    scores shrink along a path, so every kept node's parent is kept too."""
     pool_parent = []   # parent pool index (-1 = root)
     pool_score = []
     frontier = [(-1, 1.0)]  # (pool index, score) of the nodes expanded next
