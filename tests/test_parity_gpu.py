@@ -512,6 +512,25 @@ def test_inf_values_in_reused_stage_rows(case):
     assert np.isposinf(o[0, :, :G, 5]).all(), case
 
 
+@pytest.mark.parametrize("case", ["rows256", "rows64", "rows32", "rows64_s3"])
+def test_inf_prefix_key(case):
+    # +inf in channel 0 of one prefix key of kv head 0: rows whose query
+    # channel 0 is positive score it +inf (the exact softmax is NaN, lse2 NaN),
+    # rows with a negative one -inf (the key weighs 0, the rest is finite)
+    wl = (STALE_ROW_CASES[case] if case in STALE_ROW_CASES
+          else FEW_SPLIT_CASES["rows64_s3"][0])
+    inp = gen.make_inputs(wl, 37, "cuda")
+    key = 100
+    pg = int(inp.page_table[0, key // wl.page_size])
+    inp.k_cache[pg, 0, key % wl.page_size, 0] = float("inf")
+    m = oracle.build_masks(inp.parents)["masks"]
+    out, lse = run_attention(inp, dev(m.view(np.int64), torch.int64))
+    ro, rl = oracle_attention(inp, m)
+    _same_nonfinite(out.float().cpu().numpy(), ro.reshape(out.shape), OUT_TOL, case + " out")
+    _same_nonfinite(lse.cpu().numpy(), rl.reshape(lse.shape), LSE_TOL, case + " lse2")
+    assert np.isnan(rl).any() and np.isfinite(rl).any(), "the plant must reach both kinds of rows"
+
+
 def test_nan_in_node_leaks_only_to_descendants():
     wl = gen.Workload("nan", 1, 200, 16, 8, 2, 128, "bf16", 16, "random", depth_cap=4)
     inp = gen.make_inputs(wl, 5, "cuda")

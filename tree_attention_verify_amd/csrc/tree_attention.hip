@@ -1723,7 +1723,9 @@ __global__ void __launch_bounds__(512, 1) k_prefix_mfma_pipe(PrefixArgs a) {
         const int r = m / a.G, hh = m % a.G;
         const int64_t row = ((int64_t)b * a.R + r) * a.Hq + (int64_t)g * a.G + hh;
         const float inv = has_keys(lt) ? 1.f / lt : 0.f;
-        const float lse = has_keys(lt) ? mu + __log2f(lt) : -INFINITY;
+        // (an infinite weight sum comes only from a +inf score, whose exact
+        // softmax, and so lse2, is NaN)
+        const float lse = !has_keys(lt) ? -INFINITY : (lt < INFINITY ? mu + __log2f(lt) : __builtin_nanf(""));
         // lane value o[t][e] is channel chan(t, e) of row m
         auto chan = [&](int t, int e) {
             return ((e >> 3) ? D / 2 : 0) + 16 * t + 8 * ((e >> 2) & 1) + 4 * hl + (e & 3);
