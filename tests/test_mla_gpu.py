@@ -160,3 +160,31 @@ def test_mla_nonfinite_window_rows_reach_only_rows_that_see_them():
     sees = lambda j: ((m.astype(np.uint64) >> np.uint64(j)) & np.uint64(1)).astype(bool)
     assert sees(j1).any() and sees(j3).any() and (~sees(j1)).any(), "the trees must reach the nodes"
     assert np.isfinite(ro).any() and not np.isfinite(ro).all()
+
+
+@pytest.mark.parametrize("P", [300, 2000])
+def test_mla_nonfinite_prefix_rows(P):
+    # request 0: +inf in latent channel 300 of one prefix key (a score of
+    # +inf or -inf by the query's sign, and an infinite value channel) and
+    # NaN in a rotary channel of another; request 1 clean.  Every row sees
+    # the whole prefix, so request 0's rows are non-finite exactly where the
+    # exact softmax is, and request 1 stays finite.  P = 2000 runs several
+    # splits (the merge combines their partials).
+    wl = gen.MlaWorkload("nfp", 2, P, 8, 8, 512, 64, 16)
+    inp = gen.make_mla_inputs(wl, 17, "cuda", prefix_lens=np.array([P, P // 2 + 3]))
+
+    def slot(t):
+        return int(inp.page_table[0, t // wl.page_size]), t % wl.page_size
+
+    pg, sl = slot(P // 3)
+    inp.latent[pg, sl, 300] = float("inf")
+    pg, sl = slot(P - 5)
+    inp.latent[pg, sl, 512 + 9] = float("nan")
+    m = oracle.build_masks(inp.parents)["masks"]
+    out, lse = run(inp, m)
+    ro, rl = oracle.mla_attention(gen.bf16_bits(inp.q), gen.bf16_bits(inp.latent), inp.strides,
+                                  inp.page_table, wl.page_size, inp.prefix_len, m, wl.W, wl.Dc, wl.Dr)
+    o = out.float().cpu().numpy().reshape(ro.shape)
+    _same_nonfinite(o, ro, OUT_TOL, "mla prefix out")
+    _same_nonfinite(lse.cpu().numpy().reshape(rl.shape), rl, LSE_TOL, "mla prefix lse2")
+    assert not np.isfinite(ro[0]).all() and np.isfinite(ro[1]).all()
