@@ -531,6 +531,32 @@ def test_inf_prefix_key(case):
     assert np.isnan(rl).any() and np.isfinite(rl).any(), "the plant must reach both kinds of rows"
 
 
+@pytest.mark.parametrize("case", ["rows256", "rows64", "rows32"])
+@pytest.mark.parametrize("what", ["k", "v"])
+def test_fp8_nan_prefix_values(case, what):
+    # FP8 E4M3 caches hold NaN but no infinities: NaN in channel 5 of one
+    # prefix key's K (every row of kv head 0 NaN) or V (channel 5 of those
+    # rows NaN); the other heads stay finite
+    wl = STALE_ROW_CASES[case].with_(kv_dtype="fp8")
+    inp = gen.make_inputs(wl, 41, "cuda")
+    key = 150 if case != "rows32" else 90
+    pg = int(inp.page_table[0, key // wl.page_size])
+    cache = inp.k_cache if what == "k" else inp.v_cache
+    cache[pg, 0, key % wl.page_size, 5] = float("nan")
+    m = oracle.build_masks(inp.parents)["masks"]
+    out, lse = run_attention(inp, dev(m.view(np.int64), torch.int64))
+    ro, rl = oracle_attention(inp, m)
+    o = out.float().cpu().numpy()
+    _same_nonfinite(o, ro.reshape(out.shape), OUT_TOL, case + " out")
+    _same_nonfinite(lse.cpu().numpy(), rl.reshape(lse.shape), LSE_TOL, case + " lse2")
+    G = wl.Hq // wl.Hkv
+    if what == "k":
+        assert np.isnan(o[0, :, :G]).all(), case
+    else:
+        assert np.isnan(o[0, :, :G, 5]).all(), case
+    assert np.isfinite(o[0, :, G:]).all(), case
+
+
 def test_nan_in_node_leaks_only_to_descendants():
     wl = gen.Workload("nan", 1, 200, 16, 8, 2, 128, "bf16", 16, "random", depth_cap=4)
     inp = gen.make_inputs(wl, 5, "cuda")
