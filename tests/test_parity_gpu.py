@@ -557,6 +557,26 @@ def test_fp8_nan_prefix_values(case, what):
     assert np.isfinite(o[0, :, G:]).all(), case
 
 
+@pytest.mark.parametrize("case", ["rows256", "rows64", "rows32", "rows64_s3"])
+def test_inf_window_key(case):
+    # +inf in channel 0 of window node 2's K: a row that sees the node and
+    # whose query channel 0 is positive scores it +inf (the exact softmax is
+    # NaN, lse2 NaN); a negative one gives -inf (the node weighs 0); rows that
+    # do not see it are untouched
+    wl = (STALE_ROW_CASES[case] if case in STALE_ROW_CASES
+          else FEW_SPLIT_CASES["rows64_s3"][0])
+    inp = gen.make_inputs(wl, 43, "cuda")
+    t = int(inp.prefix_len[0]) + 2
+    pg = int(inp.page_table[0, t // wl.page_size])
+    inp.k_cache[pg, 0, t % wl.page_size, 0] = float("inf")
+    m = oracle.build_masks(inp.parents)["masks"]
+    out, lse = run_attention(inp, dev(m.view(np.int64), torch.int64))
+    ro, rl = oracle_attention(inp, m)
+    _same_nonfinite(out.float().cpu().numpy(), ro.reshape(out.shape), OUT_TOL, case + " out")
+    _same_nonfinite(lse.cpu().numpy(), rl.reshape(lse.shape), LSE_TOL, case + " lse2")
+    assert np.isnan(rl).any() and np.isfinite(rl).any(), "the plant must reach both kinds of rows"
+
+
 def test_nan_in_node_leaks_only_to_descendants():
     wl = gen.Workload("nan", 1, 200, 16, 8, 2, 128, "bf16", 16, "random", depth_cap=4)
     inp = gen.make_inputs(wl, 5, "cuda")
